@@ -1,0 +1,29 @@
+"""fp64 CPU oracle for the routed MoE SwiGLU feed-forward layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute anything in this package: only ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with
+the HIP library (no kernels, headers, helpers, tables or pre/post-processing);
+both sides receive the same seeded inputs and nothing else.
+
+Every floating-point step here is computed in float64 with numpy, from the
+device-rounded inputs upcast exactly to float64, with no intermediate rounding.
+"""
+
+from .moe_oracle import (  # noqa: F401
+    router_logits,
+    softmax_rows,
+    topk_select,
+    gate_weights,
+    near_tie_tokens,
+    expert_permutation,
+    silu,
+    swiglu_rows,
+    shared_experts_forward,
+    combine,
+    aux_statistics,
+    layer_forward,
+    layer_backward,
+    layer_loss,
+)
+from .mx import mx_fake_quant, e4m3_round, mx_block_scale  # noqa: F401

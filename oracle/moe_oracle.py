@@ -1,0 +1,348 @@
+"""Plain float64 definition of the routed MoE SwiGLU FFN layer, forward and backward.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): the product path never
+imports this module.
+
+What the layer computes is taken from three descriptions of it:
+  * KochiLLM v1.0 model card, "Architecture": each token goes through one
+    always-on expert and through 2 of 4 routed experts whose two weights are
+    rescaled to sum to one; the loss gains 0.01 times the layer mean of the
+    balancing term 4 * sum_i f_i * p_i (a single layer here).
+  * KochiLLM v1.0 model card, "Configuration": experts are SwiGLU blocks.
+  * spark-gpt README, feature list (optional Qwen3-MoE layers): a router
+    without bias, a softmax taken in fp32, top-k choice, SwiGLU experts whose
+    gate and up weights live in one tensor, and rescaling of the chosen
+    probabilities; and its MoE paragraph: the rescaling can be turned off, the
+    balancing statistic combines integer counts (no gradient) with a
+    differentiable mean of probabilities, and the logged router metrics are
+    the smallest and largest per-expert count, their coefficient of variation,
+    the mean routing entropy and the number of experts that got no token.
+
+Readings where the pages are silent (each is also listed in the design notes):
+  * top-k is taken on the logits (after any constant router bias), ordered by
+    logit descending and, on equal logits, by lower expert index;
+  * f_e = count_e / (T * k), P_e = mean over all T tokens of the full softmax,
+    aux = E * sum_e f_e * P_e (equals 1 at perfect balance; E = 4 gives the
+    model card's "4 * sum");
+  * f_e is a hard count and carries no gradient; P_e does;
+  * shared experts have weight 1 and no gate;
+  * packed gate/up layout: W_gu[e] rows 0..I-1 are the gate rows, rows
+    I..2I-1 the up rows, each row of length d; W_d[e] is [d, I].
+
+All arrays are numpy float64 (int64 for indices).  Loops over experts are plain
+Python; every contraction is a numpy matmul (a library primitive).
+"""
+
+import numpy as np
+
+
+# ---------------------------------------------------------------- routing ---
+
+def router_logits(x, w_router, bias=None):
+    """z = x W_r^T (+ b).  spark-gpt README, Qwen3-MoE feature: the router is a
+    bias-free linear map; ``bias`` is the constant per-expert offset used only
+    to skew expert popularity in a stress workload, never trained."""
+    z = x @ w_router.T
+    if bias is not None:
+        z = z + np.asarray(bias, dtype=np.float64)[None, :]
+    return z
+
+
+def softmax_rows(z):
+    """Row softmax, max-subtracted.  spark-gpt README: fp32-softmax routing
+    (computed here in float64)."""
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def topk_select(z, k):
+    """Indices [T, k] of the k largest logits per row, in slot order: logit
+    descending, lower expert index first on equal logits (a stable sort of -z).
+    KochiLLM "Architecture" (top-2 of 4) and spark-gpt Qwen3-MoE feature (top-k)."""
+    order = np.argsort(-z, axis=1, kind="stable")
+    return order[:, :k].astype(np.int64)
+
+
+def gate_weights(p, idx, renorm):
+    """Weights of the selected experts.  With ``renorm`` the selected
+    probabilities are divided by their sum (KochiLLM "Architecture": the two
+    chosen weights are rescaled; spark-gpt MoE paragraph: the default, with a
+    flag that disables it)."""
+    sel = np.take_along_axis(p, idx, axis=1)
+    if renorm:
+        return sel / sel.sum(axis=1, keepdims=True)
+    return sel
+
+
+def near_tie_tokens(z, k, eps=1e-5):
+    """Tokens whose routing is decided by a near-tie of the logits.
+
+    Returns (set_tie, order_tie), boolean [T] masks:
+      set_tie   -- the k-th and (k+1)-th largest logits differ by less than eps
+                   (the selected *set* is ambiguous at that precision);
+      order_tie -- two adjacent selected logits differ by less than eps (the
+                   *slot order* inside the set is ambiguous).
+    """
+    srt = -np.sort(-z, axis=1)
+    E = z.shape[1]
+    if k < E:
+        set_tie = (srt[:, k - 1] - srt[:, k]) < eps
+    else:
+        set_tie = np.zeros(z.shape[0], dtype=bool)
+    if k > 1:
+        order_tie = ((srt[:, : k - 1] - srt[:, 1:k]) < eps).any(axis=1)
+    else:
+        order_tie = np.zeros(z.shape[0], dtype=bool)
+    return set_tie, order_tie
+
+
+# ------------------------------------------------------------ permutation ---
+
+def expert_permutation(idx, n_experts):
+    """Group the T*k assignments by expert.
+
+    counts[e]      number of assignments (t, j) with idx[t, j] == e
+    offsets        exclusive prefix sum of counts, length E+1
+    perm_token[r]  token of the r-th row of the expert-sorted order, the order
+                   being (expert ascending, token ascending)
+    inv[t, j]      row r at which assignment (t, j) sits in that order
+    """
+    T, k = idx.shape
+    flat = idx.reshape(-1)
+    counts = np.bincount(flat, minlength=n_experts).astype(np.int64)
+    offsets = np.zeros(n_experts + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    order = np.argsort(flat, kind="stable")          # flat position f = t*k + j
+    perm_token = (order // k).astype(np.int64)
+    inv = np.empty(T * k, dtype=np.int64)
+    inv[order] = np.arange(T * k, dtype=np.int64)
+    return counts, offsets, perm_token, inv.reshape(T, k)
+
+
+# ----------------------------------------------------------------- experts ---
+
+def silu(a):
+    """silu(a) = a * sigmoid(a) = a / (1 + exp(-a))."""
+    with np.errstate(over="ignore"):
+        return a / (1.0 + np.exp(-a))
+
+
+def _sigmoid(a):
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-a))
+
+
+def swiglu_rows(rows, w_gate_up_e, w_down_e):
+    """One SwiGLU expert on a block of rows: G = X Wg^T, U = X Wu^T,
+    H = silu(G) * U, Y = H Wd^T (no biases).  KochiLLM "Configuration"
+    (SwiGLU experts) and spark-gpt (packed SwiGLU experts: gate and up stacked
+    in one [2I, d] weight)."""
+    inter = w_down_e.shape[1]
+    g = rows @ w_gate_up_e[:inter].T
+    u = rows @ w_gate_up_e[inter:].T
+    h = silu(g) * u
+    return g, u, h, h @ w_down_e.T
+
+
+def shared_experts_forward(x, ws_gate_up, ws_down):
+    """Sum of the always-on shared experts, each applied to every token with
+    weight 1 and no gate (KochiLLM "Architecture")."""
+    y = np.zeros((x.shape[0], ws_down.shape[1]))
+    parts = []
+    for s in range(ws_gate_up.shape[0]):
+        g, u, h, ys = swiglu_rows(x, ws_gate_up[s], ws_down[s])
+        parts.append((g, u, h))
+        y += ys
+    return y, parts
+
+
+def combine(y_perm, inv, w, y_shared=None):
+    """y_t = sum_j w_tj * Y_perm[inv[t, j]] (+ shared output)."""
+    y = np.einsum("tj,tjd->td", w, y_perm[inv])
+    if y_shared is not None:
+        y = y + y_shared
+    return y
+
+
+# ---------------------------------------------------------- aux statistics ---
+
+def aux_statistics(p, counts, top_k):
+    """Load-balancing statistic and router metrics.
+
+    KochiLLM "Architecture": the term 4 * sum_i f_i * p_i for its 4 experts;
+    spark-gpt MoE paragraph: the raw balancing value plus count extremes,
+    count spread (coefficient of variation), mean routing entropy and the
+    number of idle experts.  f_e = count_e / (T k), P_e = mean_t p_te,
+    aux_raw = sum_e f_e P_e, aux = E * aux_raw.
+    """
+    T, E = p.shape
+    counts = np.asarray(counts, dtype=np.float64)
+    f = counts / (T * top_k)
+    p_mean = p.mean(axis=0)
+    aux_raw = float((f * p_mean).sum())
+    with np.errstate(divide="ignore", invalid="ignore"):
+        plogp = np.where(p > 0, p * np.log(np.where(p > 0, p, 1.0)), 0.0)
+    entropy = float((-plogp.sum(axis=1)).mean())
+    mean_c = counts.mean()
+    cv = float(counts.std() / mean_c) if mean_c > 0 else 0.0
+    return {
+        "f": f,
+        "p_mean": p_mean,
+        "aux_raw": aux_raw,
+        "aux": E * aux_raw,
+        "entropy_mean": entropy,
+        "count_min": int(counts.min()),
+        "count_max": int(counts.max()),
+        "count_cv": cv,
+        "n_unused": int((counts == 0).sum()),
+    }
+
+
+# ------------------------------------------------------------ layer passes ---
+
+def layer_forward(x, w_router, w_gate_up, w_down, *, top_k, renorm=True, bias=None,
+                  ws_gate_up=None, ws_down=None, quant=None):
+    """Full forward pass.  Returns a dict of every intermediate.
+
+    ``quant``, if given, is applied to each operand of each expert GEMM as
+    quant(array, axis) with ``axis`` the contraction axis of that GEMM (the MX
+    fake-quant mode); the router, softmax and combine are never quantised.
+    """
+    q = quant if quant is not None else (lambda a, axis: a)
+    T, d = x.shape
+    E = w_router.shape[0]
+    z = router_logits(x, w_router, bias)
+    p = softmax_rows(z)
+    idx = topk_select(z, top_k)
+    w = gate_weights(p, idx, renorm)
+    counts, offsets, perm_token, inv = expert_permutation(idx, E)
+    x_perm = x[perm_token]
+    inter = w_down.shape[2]
+    A = T * top_k
+    g = np.zeros((A, inter)); u = np.zeros((A, inter)); h = np.zeros((A, inter))
+    y_perm = np.zeros((A, d))
+    for e in range(E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r1 == r0:
+            continue
+        xr = q(x_perm[r0:r1], 1)
+        wgu = q(w_gate_up[e], 1)
+        ge = xr @ wgu[:inter].T
+        ue = xr @ wgu[inter:].T
+        he = silu(ge) * ue
+        g[r0:r1], u[r0:r1], h[r0:r1] = ge, ue, he
+        y_perm[r0:r1] = q(he, 1) @ q(w_down[e], 1).T
+    y_shared = None
+    shared = []
+    if ws_gate_up is not None and ws_gate_up.shape[0] > 0:
+        y_shared = np.zeros((T, d))
+        inter_s = ws_down.shape[2]
+        xq = q(x, 1)
+        for s in range(ws_gate_up.shape[0]):
+            wgu = q(ws_gate_up[s], 1)
+            gs = xq @ wgu[:inter_s].T
+            us = xq @ wgu[inter_s:].T
+            hs = silu(gs) * us
+            y_shared += q(hs, 1) @ q(ws_down[s], 1).T
+            shared.append((gs, us, hs))
+    y = combine(y_perm, inv, w, y_shared)
+    return dict(z=z, p=p, idx=idx, w=w, counts=counts, offsets=offsets,
+                perm_token=perm_token, inv=inv, x_perm=x_perm, g=g, u=u, h=h,
+                y_perm=y_perm, y_shared=y_shared, shared=shared, y=y,
+                x=x, w_router=w_router, w_gate_up=w_gate_up, w_down=w_down,
+                ws_gate_up=ws_gate_up, ws_down=ws_down, top_k=top_k,
+                renorm=renorm, bias=bias)
+
+
+def layer_backward(fwd, dy, *, aux_coef=0.0, quant=None):
+    """Gradients of L = <dy, y> + aux_coef * aux with respect to x and every
+    weight, by the chain rule through the forward of ``layer_forward``.
+
+    f_e is an integer count and carries no gradient; P_e does (spark-gpt MoE
+    paragraph: counts without gradient, a differentiable stand-in).
+    """
+    q = quant if quant is not None else (lambda a, axis: a)
+    x, w_r = fwd["x"], fwd["w_router"]
+    w_gate_up, w_down = fwd["w_gate_up"], fwd["w_down"]
+    p, idx, w, inv = fwd["p"], fwd["idx"], fwd["w"], fwd["inv"]
+    offsets, counts = fwd["offsets"], fwd["counts"]
+    T, d = x.shape
+    E = w_r.shape[0]
+    k = fwd["top_k"]
+    inter = w_down.shape[2]
+
+    # combine: y_t = sum_j w_tj Y_perm[inv_tj]  ->  g_tj and dY_perm
+    y_rows = fwd["y_perm"][inv]                       # [T, k, d]
+    gsc = np.einsum("td,tjd->tj", dy, y_rows)         # dL/dw_tj
+    dy_perm = np.zeros_like(fwd["y_perm"])
+    dy_perm[inv.reshape(-1)] = (w[:, :, None] * dy[:, None, :]).reshape(-1, d)
+
+    dw_gate_up = np.zeros_like(w_gate_up)
+    dw_down = np.zeros_like(w_down)
+    dx_perm = np.zeros((T * k, d))
+    for e in range(E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r1 == r0:
+            continue
+        G, U, H = fwd["g"][r0:r1], fwd["u"][r0:r1], fwd["h"][r0:r1]
+        dY = dy_perm[r0:r1]
+        dH = q(dY, 1) @ q(w_down[e], 0)
+        dw_down[e] = q(dY, 0).T @ q(H, 0)
+        sg = _sigmoid(G)
+        dG = dH * U * sg * (1.0 + G * (1.0 - sg))
+        dU = dH * silu(G)
+        dGU = np.concatenate([dG, dU], axis=1)
+        dx_perm[r0:r1] = q(dGU, 1) @ q(w_gate_up[e], 0)
+        dw_gate_up[e] = q(dGU, 0).T @ q(fwd["x_perm"][r0:r1], 0)
+
+    dx = np.zeros((T, d))
+    for j in range(k):
+        dx += dx_perm[inv[:, j]]
+
+    grads = {"dw_gate_up": dw_gate_up, "dw_down": dw_down}
+    if fwd["ws_gate_up"] is not None and fwd["ws_gate_up"].shape[0] > 0:
+        ws_gu, ws_d = fwd["ws_gate_up"], fwd["ws_down"]
+        dws_gu = np.zeros_like(ws_gu)
+        dws_d = np.zeros_like(ws_d)
+        for s, (G, U, H) in enumerate(fwd["shared"]):
+            dH = q(dy, 1) @ q(ws_d[s], 0)
+            dws_d[s] = q(dy, 0).T @ q(H, 0)
+            sg = _sigmoid(G)
+            dG = dH * U * sg * (1.0 + G * (1.0 - sg))
+            dU = dH * silu(G)
+            dGU = np.concatenate([dG, dU], axis=1)
+            dx += q(dGU, 1) @ q(ws_gu[s], 0)
+            dws_gu[s] = q(dGU, 0).T @ q(x, 0)
+        grads["dws_gate_up"] = dws_gu
+        grads["dws_down"] = dws_d
+
+    # router: gradient reaching the selected probabilities
+    p_sel = np.take_along_axis(p, idx, axis=1)
+    if fwd["renorm"]:
+        S = p_sel.sum(axis=1, keepdims=True)
+        dp_sel = (gsc - (w * gsc).sum(axis=1, keepdims=True)) / S
+    else:
+        dp_sel = gsc
+    dp = np.zeros_like(p)
+    np.put_along_axis(dp, idx, dp_sel, axis=1)
+    if aux_coef != 0.0:
+        f = np.asarray(counts, dtype=np.float64) / (T * k)
+        dp = dp + aux_coef * E * f[None, :] / T
+    dz = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    grads["dw_router"] = dz.T @ x
+    grads["dbias"] = dz.sum(axis=0)
+    dx += dz @ w_r
+    grads["dx"] = dx
+    grads["dz"] = dz
+    grads["g"] = gsc
+    grads["dy_perm"] = dy_perm
+    grads["dx_perm"] = dx_perm
+    return grads
+
+
+def layer_loss(fwd, dy, aux_coef=0.0):
+    """L = <dy, y> + aux_coef * aux  (the scalar whose gradient layer_backward
+    returns; used by the finite-difference pins)."""
+    st = aux_statistics(fwd["p"], fwd["counts"], fwd["top_k"])
+    return float((dy * fwd["y"]).sum()) + aux_coef * st["aux"]
