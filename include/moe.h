@@ -1,0 +1,237 @@
+/*
+ * moe.h -- C ABI of the routed Mixture-of-Experts SwiGLU feed-forward layer
+ * for AMD Instinct MI355X (gfx950): forward and backward on one GPU's share
+ * of a packed token batch.
+ *
+ * What the layer computes (the sources are three public pages about small-lab
+ * decoder-only LM training, cited by title and section):
+ *   - KochiLLM v1.0 model card, "Architecture": an always-on shared expert
+ *     plus the top-2 of 4 routed experts per token, the two routing weights
+ *     rescaled to sum to one, and the balancing term 4 * sum_i f_i * p_i.
+ *   - spark-gpt README, feature list (optional Qwen3-MoE layers): router
+ *     without bias, softmax in fp32, top-k, SwiGLU experts with gate and up
+ *     weights packed in one tensor, rescaling of the chosen probabilities
+ *     (optional, MoE paragraph), the balancing statistic from integer counts
+ *     and a differentiable probability mean, plus router metrics.
+ *   - KohakUwULLM README, "Key features": MXFP8 experts (e4m3 values, one
+ *     power-of-two UE8M0 scale per 32 elements).
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument is DEVICE memory unless stated otherwise.  The
+ *     caller allocates and frees all of it, including the workspace whose
+ *     size moe_workspace_bytes() returns.  The library never allocates on
+ *     the compute calls and keeps no pointer past a call.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every compute
+ *     call only enqueues work on that stream and returns; nothing
+ *     synchronises with the host and no data-dependent size leaves the GPU.
+ *   - "act" below is the plan's activation dtype (f32, f16 or bf16): x, y,
+ *     dy, dx, the router weight and the expert weights are stored in it, and
+ *     so are the saved intermediates (GU, H, Y_perm) and the weight
+ *     gradients.  Router probabilities and routing weights are always f32.
+ *     Every matrix is row-major with the last index contiguous.
+ *   - Arguments are checked on the host before anything is launched; a
+ *     negative moe_status is returned and nothing is enqueued.  A HIP launch
+ *     error is reported as MOE_ERR_HIP.  Device-side preconditions (indices
+ *     in range, each token's k experts distinct) are documented per call and
+ *     not checked on the device; kernels never write outside the buffers
+ *     the sizes describe even when they are violated.
+ *   - A plan is immutable after creation except for the optional kernel
+ *     timing probe (moe_probe_*), which is not thread-safe.  Calls on
+ *     different streams may share a plan if each uses its own workspace.
+ *   - No float atomics are used: two runs on the same inputs give bitwise
+ *     identical results.
+ */
+#ifndef MOE_FFN_MI355X_H
+#define MOE_FFN_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,        /* a required pointer is NULL */
+  MOE_ERR_INVALID = -2,     /* a size or flag is out of range */
+  MOE_ERR_UNSUPPORTED = -3, /* valid but not implemented (dtype pair, alignment) */
+  MOE_ERR_WORKSPACE = -4,   /* workspace missing or smaller than moe_workspace_bytes() */
+  MOE_ERR_HIP = -5          /* the HIP runtime reported an error */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_F16 = 1, MOE_BF16 = 2, MOE_MXFP8_E4M3 = 3 } moe_dtype;
+
+/* Layer shape.  Requirements checked by moe_plan_create():
+ *   0 <= T;  1 <= top_k <= n_experts <= 256;
+ *   d_model, d_ff (and d_ff_shared when n_shared > 0) multiples of 128;
+ *   0 <= n_shared <= 8;  act_dtype in {F32, F16, BF16};
+ *   expert_dtype == act_dtype (MXFP8 experts are reported UNSUPPORTED until built). */
+typedef struct {
+  int64_t T;              /* tokens in the packed batch (rows of x) */
+  int32_t d_model;        /* d */
+  int32_t n_experts;      /* E routed experts */
+  int32_t top_k;          /* k experts per token */
+  int32_t d_ff;           /* I, inner width of a routed expert */
+  int32_t n_shared;       /* Ns always-on shared experts (0 = none) */
+  int32_t d_ff_shared;    /* Is, inner width of a shared expert */
+  int32_t renorm;         /* 1: routing weights = chosen probs / their sum; 0: chosen probs */
+  int32_t has_router_bias;/* 1: moe_route adds a constant f32 bias[E] to the logits */
+  int32_t act_dtype;      /* moe_dtype */
+  int32_t expert_dtype;   /* moe_dtype of the expert GEMM operands */
+  float aux_coef;         /* alpha: coefficient of the balancing statistic in the loss */
+} moe_config;
+
+typedef struct moe_plan_s* moe_plan;
+
+/* Validate `cfg` and build a plan (host memory only; selects every kernel
+ * variant once).  *out is set to NULL on failure. */
+moe_status moe_plan_create(const moe_config* cfg, moe_plan* out);
+void moe_plan_destroy(moe_plan plan);
+/* Bytes of device workspace the compute calls need (same for all calls). */
+size_t moe_workspace_bytes(moe_plan plan);
+/* Static description of a status code. */
+const char* moe_status_string(moe_status status);
+/* Library version string, e.g. "moe-ffn-mi355x 0.1 gfx950". */
+const char* moe_version(void);
+
+/* ---- forward ----------------------------------------------------------- */
+
+/* Router: z = x W_r^T (+ bias); probs = softmax(z) in f32 (max-subtracted);
+ * topk_idx[t, :] = the k largest logits, ordered by logit descending and, on
+ * equal logits, by lower expert index; topk_w = the chosen probs, divided by
+ * their sum when cfg.renorm.  (spark-gpt feature list; KochiLLM
+ * "Architecture".)
+ *   x         [T, d] act          w_router [E, d] act
+ *   bias      [E] f32, required iff cfg.has_router_bias, else ignored
+ *   probs     [T, E] f32 out      topk_idx [T, k] int32 out   topk_w [T, k] f32 out */
+moe_status moe_route(moe_plan plan, const void* x, const void* w_router, const float* bias,
+                     float* probs, int32_t* topk_idx, float* topk_w, void* stream);
+
+/* Group the T*k assignments by expert, stably (expert ascending, then token
+ * ascending), and gather the token rows in that order.
+ *   topk_idx   [T, k] int32 in: values in [0, E), distinct within a row
+ *   x          [T, d] act in
+ *   counts     [E] int32 out: assignments per expert
+ *   offsets    [E+1] int32 out: exclusive prefix sum of counts (offsets[E] = T*k)
+ *   perm_token [T*k] int32 out: token of each expert-sorted row
+ *   inv_perm   [T, k] int32 out: expert-sorted row of assignment (t, j)
+ *   x_perm     [T*k, d] act out: x_perm[r] = x[perm_token[r]] */
+moe_status moe_permute(moe_plan plan, const int32_t* topk_idx, const void* x, int32_t* counts,
+                       int32_t* offsets, int32_t* perm_token, int32_t* inv_perm, void* x_perm,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Pointers of the expert FFN (shared-expert fields are ignored when n_shared == 0). */
+typedef struct {
+  const void* x_perm;      /* [T*k, d] act, rows grouped by expert */
+  const int32_t* offsets;  /* [E+1] from moe_permute */
+  const void* w_gate_up;   /* [E, 2I, d] act: rows 0..I-1 gate, I..2I-1 up */
+  const void* w_down;      /* [E, d, I] act */
+  void* gu;                /* out [T*k, 2I] act: [G | U] per row, saved for backward */
+  void* h;                 /* out [T*k, I] act: silu(G) * U */
+  void* y_perm;            /* out [T*k, d] act: H W_d^T */
+  const void* x;           /* [T, d] act (shared experts' input) */
+  const void* ws_gate_up;  /* [Ns, 2Is, d] act */
+  const void* ws_down;     /* [Ns, d, Is] act */
+  void* gu_shared;         /* out [T, 2 Ns Is] act: expert s in columns [2 s Is, 2 (s+1) Is) as [G_s | U_s] */
+  void* h_shared;          /* out [T, Ns Is] act: expert s in columns [s Is, (s+1) Is) */
+  void* y_shared;          /* out [T, d] act: sum over shared experts */
+} moe_ffn_args;
+
+/* Routed experts as grouped GEMMs over the expert segments of x_perm (gate/up
+ * GEMM with SwiGLU in its epilogue, then the down GEMM), plus the shared
+ * experts on all T rows.  No biases.  (KochiLLM "Configuration"/"Architecture";
+ * spark-gpt feature list.) */
+moe_status moe_expert_ffn(moe_plan plan, const moe_ffn_args* args, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* y[t] = sum_j topk_w[t, j] * y_perm[inv_perm[t, j]] (+ y_shared[t]), accumulated in
+ * f32 in slot order j = 0..k-1, one write per row.
+ *   y_perm [T*k, d] act; inv_perm [T, k] int32; topk_w [T, k] f32;
+ *   y_shared [T, d] act or NULL; y [T, d] act out. */
+moe_status moe_combine(moe_plan plan, const void* y_perm, const int32_t* inv_perm,
+                       const float* topk_w, const void* y_shared, void* y, void* stream);
+
+/* ---- backward ---------------------------------------------------------- */
+
+/* Tensors saved by the forward (all produced by the calls above or inputs to them). */
+typedef struct {
+  const void* x;            /* [T, d] */
+  const void* w_router;     /* [E, d] */
+  const float* probs;       /* [T, E] */
+  const int32_t* topk_idx;  /* [T, k] */
+  const float* topk_w;      /* [T, k] */
+  const int32_t* counts;    /* [E] */
+  const int32_t* offsets;   /* [E+1] */
+  const int32_t* inv_perm;  /* [T, k] */
+  const void* x_perm;       /* [T*k, d] */
+  const void* gu;           /* [T*k, 2I] */
+  const void* h;            /* [T*k, I] */
+  const void* y_perm;       /* [T*k, d] */
+  const void* w_gate_up;    /* [E, 2I, d] */
+  const void* w_down;       /* [E, d, I] */
+  const void* ws_gate_up;   /* [Ns, 2Is, d] (n_shared > 0) */
+  const void* ws_down;      /* [Ns, d, Is] */
+  const void* gu_shared;    /* [T, 2 Ns Is] */
+  const void* h_shared;     /* [T, Ns Is] */
+} moe_saved;
+
+/* Gradient outputs (act dtype unless noted).  Every weight gradient is fully
+ * written, including zeros for experts that received no token. */
+typedef struct {
+  void* dx;            /* [T, d] */
+  void* dw_router;     /* [E, d] */
+  float* dbias;        /* [E] f32: sum_t dL/dz_te, or NULL (the bias is a constant input) */
+  void* dw_gate_up;    /* [E, 2I, d] */
+  void* dw_down;       /* [E, d, I] */
+  void* dws_gate_up;   /* [Ns, 2Is, d] (n_shared > 0) */
+  void* dws_down;      /* [Ns, d, Is] */
+} moe_grads;
+
+/* Gradients of L = <dy, y> + aux_coef * aux with respect to x and every
+ * weight.  The counts f_e carry no gradient; P_e = mean_t probs[t, e] does
+ * (spark-gpt MoE paragraph).  With renorm the routing-weight gradient goes
+ * through the division by the chosen-probability sum; the softmax Jacobian
+ * is applied in f32.
+ *   dy [T, d] act in. */
+moe_status moe_backward(moe_plan plan, const moe_saved* saved, const void* dy,
+                        const moe_grads* grads, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- balancing statistic and router metrics ---------------------------- */
+
+typedef struct {
+  float aux;           /* E * sum_e f_e P_e (1 at perfect balance) */
+  float aux_raw;       /* sum_e f_e P_e */
+  float entropy_mean;  /* mean_t of -sum_e p_te ln p_te */
+  float count_cv;      /* population std / mean of counts */
+  int32_t count_min;
+  int32_t count_max;
+  int32_t n_unused;    /* experts with count 0 */
+  int32_t reserved;
+} moe_aux_scalars;
+
+/* f_e = counts[e] / (T k); P_e = mean_t probs[t, e]; and the scalars above
+ * (KochiLLM "Architecture" for the statistic; spark-gpt MoE paragraph for the
+ * metrics).  Reductions run in a fixed order.
+ *   probs [T, E] f32; counts [E] int32; f, p_mean [E] f32 out;
+ *   out: one moe_aux_scalars in DEVICE memory. */
+moe_status moe_aux_stats(moe_plan plan, const float* probs, const int32_t* counts, float* f,
+                         float* p_mean, moe_aux_scalars* out, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* ---- kernel timing probe (measurement aid) ----------------------------- */
+
+/* Record a hipEvent pair around each of the next `max_launches` launches of
+ * the kernel named `kernel` (see moe_kernel_names()) on the stream it runs
+ * on.  max_launches <= 0 disables the probe.  Creates events (host call). */
+moe_status moe_probe_enable(moe_plan plan, const char* kernel, int max_launches);
+/* Synchronise the recorded events and return the sum of their durations and
+ * how many launches were recorded; resets the probe. */
+moe_status moe_probe_read(moe_plan plan, float* total_ms, int* launches);
+/* Comma-separated names of the kernels the probe accepts. */
+const char* moe_kernel_names(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_FFN_MI355X_H */

@@ -1,0 +1,24 @@
+"""Routed Mixture-of-Experts SwiGLU FFN layer (forward + backward) for MI355X.
+
+The computation lives in libmoe.so (hand-written HIP kernels for gfx950 behind
+the C ABI of include/moe.h).  This package is its thin binding: ``_lib`` maps
+the C calls one to one; ``layer.MoELayer`` owns the buffers of one step.
+"""
+
+from ._lib import (  # noqa: F401
+    Plan,
+    MoeError,
+    lib,
+    moe_route,
+    moe_permute,
+    moe_expert_ffn,
+    moe_combine,
+    moe_backward,
+    moe_aux_stats,
+    decode_aux,
+    probe_enable,
+    probe_read,
+    kernel_names,
+    LIB_PATH,
+)
+from .layer import MoELayer  # noqa: F401

@@ -1,0 +1,511 @@
+// Host side of the C ABI: plan creation and validation, workspace layout,
+// and the launch sequence of each call.  Nothing here touches device data;
+// every size the device produces (counts, offsets) stays on the device.
+
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "moe.h"
+
+using namespace moe;
+
+static_assert(sizeof(moe_aux_scalars) == sizeof(moe::moe_aux_out), "aux struct layout");
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+const char* kKernelNames =
+    "route,permute_hist,permute_scan,permute_scatter,gemm_gate_up_swiglu,gemm_down,"
+    "gemm_gate_up_swiglu_shared,gemm_down_shared,combine,combine_bwd,router_dz,"
+    "gemm_down_dgrad_swiglu,gemm_wgrad_down,gemm_gate_up_dgrad,gemm_wgrad_gate_up,"
+    "gemm_down_dgrad_swiglu_shared,gemm_wgrad_down_shared,gemm_wgrad_gate_up_shared,"
+    "gemm_gate_up_dgrad_shared,stack_router,gemm_router_dx,gemm_wgrad_router,router_reduce,aux";
+
+}  // namespace
+
+struct moe_plan_s {
+  moe_config cfg;
+  int dt;
+  int64_t T, A;
+  int d, E, k, I, Ns, Is, Ep;
+  int nblk_hist, nblk_dz, nblk_aux, router_splits;
+  // workspace regions (byte offsets)
+  size_t o_block_counts, o_block_base, o_dy_perm, o_g, o_dzhl, o_w2, o_dgu, o_dx_perm, o_dgu_s,
+      o_dxr, o_dwr_part, o_dbias_part, o_aux_part, ws_total;
+  // timing probe
+  std::string probe_name;
+  std::vector<hipEvent_t> ev0, ev1;
+  int probe_n = 0;
+
+  ~moe_plan_s() { release_events(); }
+  void release_events() {
+    for (auto e : ev0) (void)hipEventDestroy(e);
+    for (auto e : ev1) (void)hipEventDestroy(e);
+    ev0.clear();
+    ev1.clear();
+    probe_n = 0;
+  }
+};
+
+namespace {
+
+// Records a hipEvent pair around one launch when the probe targets `name`.
+struct Probe {
+  moe_plan p;
+  hipStream_t s;
+  bool on;
+  Probe(moe_plan p_, const char* name, hipStream_t s_) : p(p_), s(s_) {
+    on = !p->probe_name.empty() && p->probe_name == name && p->probe_n < (int)p->ev0.size();
+    if (on) (void)hipEventRecord(p->ev0[p->probe_n], s);
+  }
+  ~Probe() {
+    if (on) {
+      (void)hipEventRecord(p->ev1[p->probe_n], s);
+      ++p->probe_n;
+    }
+  }
+};
+
+char* wsp(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                        \
+  do {                                       \
+    hipError_t e_ = (expr);                  \
+    if (e_ != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+moe_status check_ws(moe_plan p, void* ws, size_t ws_bytes) {
+  if (p->ws_total == 0) return MOE_OK;
+  if (!ws) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < p->ws_total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_INVALID: return "a size or flag is out of range";
+    case MOE_ERR_UNSUPPORTED: return "valid but unsupported configuration (dtype or alignment)";
+    case MOE_ERR_WORKSPACE: return "workspace missing or smaller than moe_workspace_bytes()";
+    case MOE_ERR_HIP: return "the HIP runtime reported an error";
+  }
+  return "unknown status";
+}
+
+const char* moe_version(void) { return "moe-ffn-mi355x 0.1 gfx950"; }
+
+const char* moe_kernel_names(void) { return kKernelNames; }
+
+moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
+  if (!out) return MOE_ERR_NULL;
+  *out = nullptr;
+  if (!cfg) return MOE_ERR_NULL;
+  const moe_config& c = *cfg;
+  if (c.T < 0 || c.T > (int64_t)1 << 30) return MOE_ERR_INVALID;
+  if (c.d_model <= 0 || c.d_ff <= 0) return MOE_ERR_INVALID;
+  if (c.n_experts < 1 || c.n_experts > 256) return MOE_ERR_INVALID;
+  if (c.top_k < 1 || c.top_k > c.n_experts || c.top_k > 64) return MOE_ERR_INVALID;
+  if (c.n_shared < 0 || c.n_shared > 8) return MOE_ERR_INVALID;
+  if (c.n_shared > 0 && c.d_ff_shared <= 0) return MOE_ERR_INVALID;
+  if (c.renorm != 0 && c.renorm != 1) return MOE_ERR_INVALID;
+  if (c.has_router_bias != 0 && c.has_router_bias != 1) return MOE_ERR_INVALID;
+  if (c.act_dtype < MOE_F32 || c.act_dtype > MOE_MXFP8_E4M3) return MOE_ERR_INVALID;
+  if (c.expert_dtype < MOE_F32 || c.expert_dtype > MOE_MXFP8_E4M3) return MOE_ERR_INVALID;
+  if (!(c.aux_coef == c.aux_coef)) return MOE_ERR_INVALID;  // NaN
+  if (c.act_dtype == MOE_MXFP8_E4M3) return MOE_ERR_UNSUPPORTED;
+  if (c.expert_dtype != c.act_dtype) return MOE_ERR_UNSUPPORTED;
+  if (c.d_model % 128 || c.d_ff % 128) return MOE_ERR_UNSUPPORTED;
+  if (c.n_shared > 0 && c.d_ff_shared % 128) return MOE_ERR_UNSUPPORTED;
+  const int64_t A = c.T * c.top_k;
+  if (A >= ((int64_t)1 << 31)) return MOE_ERR_INVALID;
+
+  moe_plan p = new (std::nothrow) moe_plan_s();
+  if (!p) return MOE_ERR_INVALID;
+  p->cfg = c;
+  p->dt = c.act_dtype == MOE_F32 ? DT_F32 : (c.act_dtype == MOE_F16 ? DT_F16 : DT_BF16);
+  p->T = c.T;
+  p->A = A;
+  p->d = c.d_model;
+  p->E = c.n_experts;
+  p->k = c.top_k;
+  p->I = c.d_ff;
+  p->Ns = c.n_shared;
+  p->Is = c.n_shared > 0 ? c.d_ff_shared : 0;
+  p->Ep = (c.n_experts + 63) / 64 * 64;
+  p->nblk_hist = (int)((c.T + kHistTokens - 1) / kHistTokens);
+  p->nblk_dz = router_dz_blocks(c.T);
+  p->nblk_aux = aux_blocks(c.T);
+  {
+    // split the router weight-gradient contraction over tokens so the grid fills the GPU
+    const int tiles = (2 * p->Ep / 128) * (p->d / 128);
+    int s = (int)(c.T / 2048);
+    if (s < 1) s = 1;
+    const int cap = 512 / tiles > 1 ? 512 / tiles : 1;
+    if (s > cap) s = cap;
+    if (s > 64) s = 64;
+    p->router_splits = s;
+  }
+  const size_t es = dtype_bytes(p->dt);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  p->o_block_counts = take((size_t)p->nblk_hist * p->E * 4);
+  p->o_block_base = take((size_t)p->nblk_hist * p->E * 4);
+  p->o_dy_perm = take((size_t)A * p->d * es);
+  p->o_g = take((size_t)A * 4);
+  p->o_dzhl = take((size_t)p->T * 2 * p->Ep * es);
+  p->o_w2 = take((size_t)2 * p->Ep * p->d * es);
+  p->o_dgu = take((size_t)A * 2 * p->I * es);
+  p->o_dx_perm = take((size_t)A * p->d * es);
+  p->o_dgu_s = take((size_t)p->T * 2 * p->Ns * p->Is * es);
+  p->o_dxr = take(p->Ns > 0 ? (size_t)p->T * p->d * 4 : 0);
+  p->o_dwr_part = take((size_t)p->router_splits * 2 * p->Ep * p->d * 4);
+  p->o_dbias_part = take((size_t)p->nblk_dz * p->E * 4);
+  p->o_aux_part = take((size_t)(p->nblk_aux > 0 ? p->nblk_aux : 1) * 2 * p->E * 4);
+  p->ws_total = off;
+  *out = p;
+  return MOE_OK;
+}
+
+void moe_plan_destroy(moe_plan plan) { delete plan; }
+
+size_t moe_workspace_bytes(moe_plan plan) { return plan ? plan->ws_total : 0; }
+
+// ------------------------------------------------------------------ route --
+moe_status moe_route(moe_plan p, const void* x, const void* w_router, const float* bias, float* probs,
+                     int32_t* topk_idx, float* topk_w, void* stream) {
+  if (!p) return MOE_ERR_NULL;
+  if (p->T == 0) return MOE_OK;
+  if (!x || !w_router || !probs || !topk_idx || !topk_w) return MOE_ERR_NULL;
+  if (p->cfg.has_router_bias && !bias) return MOE_ERR_NULL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RouteArgs a{x, w_router, p->cfg.has_router_bias ? bias : nullptr, probs, topk_idx, topk_w,
+              p->T, p->d, p->E, p->k, p->cfg.renorm};
+  Probe pr(p, "route", s);
+  return hip_status(launch_route(p->dt, a, s));
+}
+
+// ---------------------------------------------------------------- permute --
+moe_status moe_permute(moe_plan p, const int32_t* topk_idx, const void* x, int32_t* counts,
+                       int32_t* offsets, int32_t* perm_token, int32_t* inv_perm, void* x_perm, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (!p) return MOE_ERR_NULL;
+  if (!counts || !offsets) return MOE_ERR_NULL;
+  if (p->T > 0 && (!topk_idx || !x || !perm_token || !inv_perm || !x_perm)) return MOE_ERR_NULL;
+  moe_status st = check_ws(p, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  PermuteArgs a{topk_idx, x, counts, offsets, perm_token, inv_perm, x_perm,
+                reinterpret_cast<int32_t*>(wsp(ws, p->o_block_counts)),
+                reinterpret_cast<int32_t*>(wsp(ws, p->o_block_base)), p->T, p->d, p->E, p->k};
+  {
+    Probe pr(p, "permute_hist", s);
+    MOE_TRY(launch_permute_hist(a, s));
+  }
+  {
+    Probe pr(p, "permute_scan", s);
+    MOE_TRY(launch_permute_scan(a, s));
+  }
+  {
+    Probe pr(p, "permute_scatter", s);
+    MOE_TRY(launch_permute_scatter(p->dt, a, s));
+  }
+  return MOE_OK;
+}
+
+// ------------------------------------------------------------- expert FFN --
+moe_status moe_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, size_t ws_bytes, void* stream) {
+  if (!p || !f) return MOE_ERR_NULL;
+  (void)ws;
+  (void)ws_bytes;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p->T == 0) return MOE_OK;
+  if (!f->x_perm || !f->offsets || !f->w_gate_up || !f->w_down || !f->gu || !f->h || !f->y_perm)
+    return MOE_ERR_NULL;
+  if (p->Ns > 0 && (!f->x || !f->ws_gate_up || !f->ws_down || !f->gu_shared || !f->h_shared || !f->y_shared))
+    return MOE_ERR_NULL;
+  const int d = p->d, I = p->I;
+  {
+    RowGemmArgs a{};
+    a.P = f->x_perm; a.ldp = d;
+    a.Q = f->w_gate_up; a.ldq = d; a.q_group_stride = (int64_t)2 * I * d;
+    a.offsets = f->offsets; a.G = p->E; a.M = p->A; a.N = I; a.K = d; a.sub = I;
+    a.C = f->gu; a.ldc = 2 * I; a.C2 = f->h; a.ldc2 = I;
+    Probe pr(p, "gemm_gate_up_swiglu", s);
+    MOE_TRY(launch_row_gemm(p->dt, OP_GU_FWD, EPI_SWIGLU_FWD, a, s));
+  }
+  {
+    RowGemmArgs a{};
+    a.P = f->h; a.ldp = I;
+    a.Q = f->w_down; a.ldq = I; a.q_group_stride = (int64_t)d * I;
+    a.offsets = f->offsets; a.G = p->E; a.M = p->A; a.N = d; a.K = I; a.sub = I;
+    a.C = f->y_perm; a.ldc = d;
+    Probe pr(p, "gemm_down", s);
+    MOE_TRY(launch_row_gemm(p->dt, OP_DOWN_FWD, EPI_STORE, a, s));
+  }
+  if (p->Ns > 0) {
+    const int Is = p->Is, NI = p->Ns * p->Is;
+    {
+      RowGemmArgs a{};
+      a.P = f->x; a.ldp = d;
+      a.Q = f->ws_gate_up; a.ldq = d; a.q_group_stride = 0;
+      a.offsets = nullptr; a.G = 1; a.M = p->T; a.N = NI; a.K = d; a.sub = Is;
+      a.C = f->gu_shared; a.ldc = 2 * NI; a.C2 = f->h_shared; a.ldc2 = NI;
+      Probe pr(p, "gemm_gate_up_swiglu_shared", s);
+      MOE_TRY(launch_row_gemm(p->dt, OP_GU_FWD, EPI_SWIGLU_FWD, a, s));
+    }
+    {
+      RowGemmArgs a{};
+      a.P = f->h_shared; a.ldp = NI;
+      a.Q = f->ws_down; a.ldq = Is; a.q_group_stride = 0;
+      a.offsets = nullptr; a.G = 1; a.M = p->T; a.N = d; a.K = NI; a.sub = Is;
+      a.C = f->y_shared; a.ldc = d;
+      Probe pr(p, "gemm_down_shared", s);
+      MOE_TRY(launch_row_gemm(p->dt, OP_DOWN_FWD, EPI_STORE, a, s));
+    }
+  }
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- combine --
+moe_status moe_combine(moe_plan p, const void* y_perm, const int32_t* inv_perm, const float* topk_w,
+                       const void* y_shared, void* y, void* stream) {
+  if (!p) return MOE_ERR_NULL;
+  if (p->T == 0) return MOE_OK;
+  if (!y_perm || !inv_perm || !topk_w || !y) return MOE_ERR_NULL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  CombineArgs a{y_perm, inv_perm, topk_w, y_shared, y, p->T, p->d, p->k};
+  Probe pr(p, "combine", s);
+  return hip_status(launch_combine(p->dt, a, s));
+}
+
+// --------------------------------------------------------------- backward --
+moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const moe_grads* gr, void* ws,
+                        size_t ws_bytes, void* stream) {
+  if (!p || !sv || !gr) return MOE_ERR_NULL;
+  if (!gr->dw_router || !gr->dw_gate_up || !gr->dw_down) return MOE_ERR_NULL;
+  if (!sv->offsets) return MOE_ERR_NULL;
+  if (p->Ns > 0 && (!gr->dws_gate_up || !gr->dws_down)) return MOE_ERR_NULL;
+  if (p->T > 0) {
+    if (!dy || !gr->dx || !sv->x || !sv->w_router || !sv->probs || !sv->topk_idx || !sv->topk_w ||
+        !sv->counts || !sv->inv_perm || !sv->x_perm || !sv->gu || !sv->h || !sv->y_perm ||
+        !sv->w_gate_up || !sv->w_down)
+      return MOE_ERR_NULL;
+    if (p->Ns > 0 && (!sv->ws_gate_up || !sv->ws_down || !sv->gu_shared || !sv->h_shared))
+      return MOE_ERR_NULL;
+  } else if (!sv->w_router || !sv->w_gate_up || !sv->w_down) {
+    return MOE_ERR_NULL;
+  }
+  moe_status st = check_ws(p, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int d = p->d, I = p->I, E = p->E, k = p->k, Ep = p->Ep;
+  void* dy_perm = wsp(ws, p->o_dy_perm);
+  float* g = reinterpret_cast<float*>(wsp(ws, p->o_g));
+  void* dzhl = wsp(ws, p->o_dzhl);
+  void* w2 = wsp(ws, p->o_w2);
+  void* dgu = wsp(ws, p->o_dgu);
+  void* dx_perm = wsp(ws, p->o_dx_perm);
+  void* dgu_s = wsp(ws, p->o_dgu_s);
+  float* dxr = reinterpret_cast<float*>(wsp(ws, p->o_dxr));
+  float* dwr_part = reinterpret_cast<float*>(wsp(ws, p->o_dwr_part));
+  float* dbias_part = reinterpret_cast<float*>(wsp(ws, p->o_dbias_part));
+
+  if (p->T > 0) {
+    {
+      CombineBwdArgs a{dy, sv->y_perm, sv->inv_perm, sv->topk_w, dy_perm, g, p->T, d, k};
+      Probe pr(p, "combine_bwd", s);
+      MOE_TRY(launch_combine_bwd(p->dt, a, s));
+    }
+    {
+      RouterDzArgs a{g, sv->topk_w, sv->topk_idx, sv->probs, sv->counts, dzhl, dbias_part,
+                     p->T, E, Ep, k, p->cfg.renorm, p->cfg.aux_coef};
+      Probe pr(p, "router_dz", s);
+      MOE_TRY(launch_router_dz(p->dt, a, s));
+    }
+    {
+      RowGemmArgs a{};
+      a.P = dy_perm; a.ldp = d;
+      a.Q = sv->w_down; a.ldq = I; a.q_group_stride = (int64_t)d * I;
+      a.offsets = sv->offsets; a.G = E; a.M = p->A; a.N = I; a.K = d; a.sub = I;
+      a.C = dgu; a.ldc = 2 * I; a.aux = sv->gu; a.ldaux = 2 * I;
+      Probe pr(p, "gemm_down_dgrad_swiglu", s);
+      MOE_TRY(launch_row_gemm(p->dt, OP_DOWN_DGRAD, EPI_SWIGLU_BWD, a, s));
+    }
+  }
+  {
+    WgradArgs a{};
+    a.P = dy_perm; a.ldp = d; a.Q = sv->h; a.ldq = I;
+    a.offsets = sv->offsets; a.G = E; a.Mtok = p->A; a.M = d; a.N = I; a.splits = 1;
+    a.C = gr->dw_down; a.c_group_stride = (int64_t)d * I; a.c_split_stride = 0; a.sub = I; a.out_f32 = 0;
+    Probe pr(p, "gemm_wgrad_down", s);
+    MOE_TRY(launch_wgrad(p->dt, a, s));
+  }
+  if (p->T > 0) {
+    RowGemmArgs a{};
+    a.P = dgu; a.ldp = 2 * I;
+    a.Q = sv->w_gate_up; a.ldq = d; a.q_group_stride = (int64_t)2 * I * d;
+    a.offsets = sv->offsets; a.G = E; a.M = p->A; a.N = d; a.K = 2 * I; a.sub = I;
+    a.C = dx_perm; a.ldc = d;
+    Probe pr(p, "gemm_gate_up_dgrad", s);
+    MOE_TRY(launch_row_gemm(p->dt, OP_GU_DGRAD, EPI_STORE, a, s));
+  }
+  {
+    WgradArgs a{};
+    a.P = dgu; a.ldp = 2 * I; a.Q = sv->x_perm; a.ldq = d;
+    a.offsets = sv->offsets; a.G = E; a.Mtok = p->A; a.M = 2 * I; a.N = d; a.splits = 1;
+    a.C = gr->dw_gate_up; a.c_group_stride = (int64_t)2 * I * d; a.c_split_stride = 0; a.sub = d; a.out_f32 = 0;
+    Probe pr(p, "gemm_wgrad_gate_up", s);
+    MOE_TRY(launch_wgrad(p->dt, a, s));
+  }
+  if (p->Ns > 0) {
+    const int Is = p->Is, NI = p->Ns * p->Is;
+    if (p->T > 0) {
+      RowGemmArgs a{};
+      a.P = dy; a.ldp = d;
+      a.Q = sv->ws_down; a.ldq = Is; a.q_group_stride = 0;
+      a.offsets = nullptr; a.G = 1; a.M = p->T; a.N = NI; a.K = d; a.sub = Is;
+      a.C = dgu_s; a.ldc = 2 * NI; a.aux = sv->gu_shared; a.ldaux = 2 * NI;
+      Probe pr(p, "gemm_down_dgrad_swiglu_shared", s);
+      MOE_TRY(launch_row_gemm(p->dt, OP_DOWN_DGRAD, EPI_SWIGLU_BWD, a, s));
+    }
+    {
+      WgradArgs a{};
+      a.P = dy; a.ldp = d; a.Q = sv->h_shared; a.ldq = NI;
+      a.offsets = nullptr; a.G = 1; a.Mtok = p->T; a.M = d; a.N = NI; a.splits = 1;
+      a.C = gr->dws_down; a.c_group_stride = 0; a.c_split_stride = 0; a.sub = Is; a.out_f32 = 0;
+      Probe pr(p, "gemm_wgrad_down_shared", s);
+      MOE_TRY(launch_wgrad(p->dt, a, s));
+    }
+    {
+      WgradArgs a{};
+      a.P = dgu_s; a.ldp = 2 * NI; a.Q = sv->x; a.ldq = d;
+      a.offsets = nullptr; a.G = 1; a.Mtok = p->T; a.M = 2 * NI; a.N = d; a.splits = 1;
+      a.C = gr->dws_gate_up; a.c_group_stride = 0; a.c_split_stride = 0; a.sub = d; a.out_f32 = 0;
+      Probe pr(p, "gemm_wgrad_gate_up_shared", s);
+      MOE_TRY(launch_wgrad(p->dt, a, s));
+    }
+  }
+  {
+    Stack2Args a{sv->w_router, w2, E, Ep, d};
+    Probe pr(p, "stack_router", s);
+    MOE_TRY(launch_stack2(p->dt, a, s));
+  }
+  if (p->T > 0) {
+    RowGemmArgs a{};
+    a.P = dzhl; a.ldp = 2 * Ep;
+    a.Q = w2; a.ldq = d; a.q_group_stride = 0;
+    a.offsets = nullptr; a.G = 1; a.M = p->T; a.N = d; a.K = 2 * Ep; a.sub = d;
+    if (p->Ns > 0) {
+      a.C = dxr; a.ldc = d;
+      {
+        Probe pr(p, "gemm_router_dx", s);
+        MOE_TRY(launch_row_gemm(p->dt, OP_ROUTER_DX, EPI_STORE_F32, a, s));
+      }
+      const int NI = p->Ns * p->Is;
+      RowGemmArgs b{};
+      b.P = dgu_s; b.ldp = 2 * NI;
+      b.Q = sv->ws_gate_up; b.ldq = d; b.q_group_stride = 0;
+      b.offsets = nullptr; b.G = 1; b.M = p->T; b.N = d; b.K = 2 * NI; b.sub = d;
+      b.C = gr->dx; b.ldc = d; b.inv = sv->inv_perm; b.topk = k; b.gath = dx_perm; b.ldg = d;
+      b.aux = dxr; b.ldaux = d;
+      Probe pr(p, "gemm_gate_up_dgrad_shared", s);
+      MOE_TRY(launch_row_gemm(p->dt, OP_GU_DGRAD, EPI_UNPERMUTE, b, s));
+    } else {
+      a.C = gr->dx; a.ldc = d; a.inv = sv->inv_perm; a.topk = k; a.gath = dx_perm; a.ldg = d;
+      a.aux = nullptr;
+      Probe pr(p, "gemm_router_dx", s);
+      MOE_TRY(launch_row_gemm(p->dt, OP_ROUTER_DX, EPI_UNPERMUTE, a, s));
+    }
+  }
+  {
+    WgradArgs a{};
+    a.P = dzhl; a.ldp = 2 * Ep; a.Q = sv->x; a.ldq = d;
+    a.offsets = nullptr; a.G = 1; a.Mtok = p->T; a.M = 2 * Ep; a.N = d; a.splits = p->router_splits;
+    a.C = dwr_part; a.c_group_stride = 0; a.c_split_stride = (int64_t)2 * Ep * d; a.sub = d; a.out_f32 = 1;
+    Probe pr(p, "gemm_wgrad_router", s);
+    MOE_TRY(launch_wgrad(p->dt, a, s));
+  }
+  {
+    RouterReduceArgs a{dwr_part, p->router_splits, E, Ep, d, gr->dw_router,
+                       dbias_part, p->T > 0 ? p->nblk_dz : 0, gr->dbias};
+    Probe pr(p, "router_reduce", s);
+    MOE_TRY(launch_router_reduce(p->dt, a, s));
+  }
+  return MOE_OK;
+}
+
+// -------------------------------------------------------------- aux stats --
+moe_status moe_aux_stats(moe_plan p, const float* probs, const int32_t* counts, float* f, float* p_mean,
+                         moe_aux_scalars* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!p) return MOE_ERR_NULL;
+  if (!counts || !f || !p_mean || !out) return MOE_ERR_NULL;
+  if (p->T > 0 && !probs) return MOE_ERR_NULL;
+  moe_status st = check_ws(p, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  AuxArgs a{probs, counts, f, p_mean, out, reinterpret_cast<float*>(wsp(ws, p->o_aux_part)), p->T, p->E, p->k};
+  Probe pr(p, "aux", s);
+  return hip_status(launch_aux(a, s));
+}
+
+// ------------------------------------------------------------------ probe --
+moe_status moe_probe_enable(moe_plan p, const char* kernel, int max_launches) {
+  if (!p) return MOE_ERR_NULL;
+  p->release_events();
+  p->probe_name.clear();
+  if (max_launches <= 0) return MOE_OK;
+  if (!kernel) return MOE_ERR_NULL;
+  const std::string name(kernel);
+  // accept only names from the list
+  const std::string all = std::string(",") + kKernelNames + ",";
+  if (all.find("," + name + ",") == std::string::npos) return MOE_ERR_INVALID;
+  if (max_launches > 100000) return MOE_ERR_INVALID;
+  p->ev0.resize(max_launches);
+  p->ev1.resize(max_launches);
+  for (int i = 0; i < max_launches; ++i) {
+    if (hipEventCreate(&p->ev0[i]) != hipSuccess || hipEventCreate(&p->ev1[i]) != hipSuccess) {
+      p->ev0.resize(i);
+      p->ev1.resize(i);
+      p->release_events();
+      return MOE_ERR_HIP;
+    }
+  }
+  p->probe_name = name;
+  p->probe_n = 0;
+  return MOE_OK;
+}
+
+moe_status moe_probe_read(moe_plan p, float* total_ms, int* launches) {
+  if (!p || !total_ms || !launches) return MOE_ERR_NULL;
+  float tot = 0.0f;
+  for (int i = 0; i < p->probe_n; ++i) {
+    if (hipEventSynchronize(p->ev1[i]) != hipSuccess) return MOE_ERR_HIP;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, p->ev0[i], p->ev1[i]) != hipSuccess) return MOE_ERR_HIP;
+    tot += ms;
+  }
+  *total_ms = tot;
+  *launches = p->probe_n;
+  p->probe_n = 0;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,382 @@
+// Bandwidth-bound kernels of the layer: weighted combine and its backward,
+// the router backward (softmax Jacobian, renormalisation, balancing term),
+// the reduction of the router weight gradient, and the balancing statistic.
+// Every reduction runs in a fixed order; there are no float atomics.
+
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int NT = 256;
+
+// y[t] = sum_j w[t,j] * y_perm[inv[t,j]] (+ y_shared[t]); one wave per token,
+// 16-byte vectors along the row, f32 accumulation in slot order.
+template <typename T>
+__global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a) {
+  constexpr int VR = 16 / sizeof(T);
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * (NT / 64);
+  const int64_t rowbytes = (int64_t)a.d * sizeof(T);
+  const int nch = (int)(rowbytes / 16);
+  const char* yp = static_cast<const char*>(a.y_perm);
+  const char* ys = static_cast<const char*>(a.y_shared);
+  char* yo = static_cast<char*>(a.y);
+  for (int64_t t = (int64_t)blockIdx.x * (NT / 64) + (threadIdx.x >> 6); t < a.T; t += waves) {
+    int r_l = 0;
+    float w_l = 0.0f;
+    if (lane < a.k) {
+      r_l = a.inv[t * a.k + lane];
+      w_l = a.wts[t * a.k + lane];
+    }
+    for (int c0 = 0; c0 < nch; c0 += 64) {
+      const int c = c0 + lane;
+      const bool ok = c < nch;
+      float acc[VR];
+#pragma unroll
+      for (int i = 0; i < VR; ++i) acc[i] = 0.0f;
+      for (int j = 0; j < a.k; ++j) {
+        const int r = __shfl(r_l, j, 64);
+        const float w = __shfl(w_l, j, 64);
+        if (ok && r >= 0) {
+          Chunk<T> ch;
+          ch.raw = ld16(yp + (int64_t)r * rowbytes + (int64_t)c * 16);
+#pragma unroll
+          for (int i = 0; i < VR; ++i) acc[i] = fmaf(w, to_f32<T>(ch.e[i]), acc[i]);
+        }
+      }
+      if (ok) {
+        if (ys) {
+          Chunk<T> ch;
+          ch.raw = ld16(ys + t * rowbytes + (int64_t)c * 16);
+#pragma unroll
+          for (int i = 0; i < VR; ++i) acc[i] += to_f32<T>(ch.e[i]);
+        }
+        Chunk<T> o;
+#pragma unroll
+        for (int i = 0; i < VR; ++i) o.e[i] = from_f32<T>(acc[i]);
+        st16(yo + t * rowbytes + (int64_t)c * 16, o.raw);
+      }
+    }
+  }
+}
+
+// dY_perm[inv[t,j]] = w[t,j] * dy[t];  g[t,j] = <dy[t], y_perm[inv[t,j]]>
+template <typename T>
+__global__ void __launch_bounds__(NT) combine_bwd_kernel(CombineBwdArgs a) {
+  constexpr int VR = 16 / sizeof(T);
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * (NT / 64);
+  const int64_t rowbytes = (int64_t)a.d * sizeof(T);
+  const int nch = (int)(rowbytes / 16);
+  const char* dyb = static_cast<const char*>(a.dy);
+  const char* yp = static_cast<const char*>(a.y_perm);
+  char* dyp = static_cast<char*>(a.dy_perm);
+  for (int64_t t = (int64_t)blockIdx.x * (NT / 64) + (threadIdx.x >> 6); t < a.T; t += waves) {
+    int r_l = 0;
+    float w_l = 0.0f;
+    if (lane < a.k) {
+      r_l = a.inv[t * a.k + lane];
+      w_l = a.wts[t * a.k + lane];
+    }
+    for (int j = 0; j < a.k; ++j) {
+      const int r = __shfl(r_l, j, 64);
+      const float w = __shfl(w_l, j, 64);
+      float dot = 0.0f;
+      for (int c0 = 0; c0 < nch; c0 += 64) {
+        const int c = c0 + lane;
+        if (c < nch && r >= 0) {
+          Chunk<T> dv, yv, o;
+          dv.raw = ld16(dyb + t * rowbytes + (int64_t)c * 16);
+          yv.raw = ld16(yp + (int64_t)r * rowbytes + (int64_t)c * 16);
+#pragma unroll
+          for (int i = 0; i < VR; ++i) {
+            const float d = to_f32<T>(dv.e[i]);
+            dot = fmaf(d, to_f32<T>(yv.e[i]), dot);
+            o.e[i] = from_f32<T>(w * d);
+          }
+          st16(dyp + (int64_t)r * rowbytes + (int64_t)c * 16, o.raw);
+        }
+      }
+      dot = wave_sum(dot);
+      if (lane == 0) a.g[t * a.k + j] = dot;
+    }
+  }
+}
+
+// Router backward for one token per wave.
+//   dp_e  = (selected e = e_j) ? (renorm ? (g_j - sum_i w_i g_i) / S : g_j) : 0
+//   dp_e += aux_coef * E * f_e / T,   f_e = count_e / (T k)
+//   dz_e  = p_e * (dp_e - sum_e' p_e' dp_e')
+// dz is written as a hi/lo pair in the activation dtype (hi = round(dz),
+// lo = round(dz - hi)) so the matrix-core products that consume it keep
+// nearly f32 accuracy.  Per-block column sums of dz feed dbias.
+template <typename T>
+__global__ void __launch_bounds__(NT) router_dz_kernel(RouterDzArgs a) {
+  __shared__ float s_dp[NT / 64][256];
+  __shared__ float s_dz[NT / 64][256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float aux_scale = a.aux_coef * (float)a.E / ((float)a.T * (float)a.T * (float)a.k);
+  float bias_acc = 0.0f;
+  T* dz = static_cast<T*>(a.dz_hl);
+  const int64_t ld = 2 * (int64_t)a.Ep;
+  for (int64_t tb = (int64_t)blockIdx.x * (NT / 64); tb < a.T; tb += (int64_t)gridDim.x * (NT / 64)) {
+    const int64_t t = tb + wave;
+    const bool active = t < a.T;
+    float p[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+      p[q] = (active && e < a.E) ? a.probs[t * a.E + e] : 0.0f;
+      if (e < a.E) s_dp[wave][e] = aux_scale * (float)a.counts[e];
+    }
+    float gj = 0.0f, wj = 0.0f, pj = 0.0f;
+    int ej = -1;
+    if (active && lane < a.k) {
+      ej = a.idx[t * a.k + lane];
+      gj = a.g[t * a.k + lane];
+      wj = a.wts[t * a.k + lane];
+      if ((unsigned)ej < (unsigned)a.E) pj = a.probs[t * a.E + ej];
+      else ej = -1;
+    }
+    const float S = wave_sum(pj);
+    const float wg = wave_sum(wj * gj);
+    const float dps = a.renorm ? (gj - wg) / S : gj;
+    __syncthreads();
+    if (ej >= 0) s_dp[wave][ej] += dps;
+    __syncthreads();
+    float dot = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+      if (e < a.E) dot = fmaf(p[q], s_dp[wave][e], dot);
+    }
+    dot = wave_sum(dot);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+      float v = 0.0f;
+      if (e < a.E) v = active ? p[q] * (s_dp[wave][e] - dot) : 0.0f;
+      if (active && e < a.Ep) {
+        const T hi = from_f32<T>(v);
+        const T lo = from_f32<T>(v - to_f32<T>(hi));
+        dz[t * ld + e] = hi;
+        dz[t * ld + a.Ep + e] = lo;
+      }
+      if (e < a.E) s_dz[wave][e] = v;
+    }
+    __syncthreads();
+    if (tid < a.E) bias_acc += ((s_dz[0][tid] + s_dz[1][tid]) + s_dz[2][tid]) + s_dz[3][tid];
+    __syncthreads();
+  }
+  if (tid < a.E) a.dbias_part[(int64_t)blockIdx.x * a.E + tid] = bias_acc;
+}
+
+// w2 rows [0, E) and [Ep, Ep + E) = W_r, every other row zero.
+template <typename T>
+__global__ void __launch_bounds__(NT) stack2_kernel(Stack2Args a) {
+  const int64_t n = 2 * (int64_t)a.Ep * a.d;
+  const T* w = static_cast<const T*>(a.w);
+  T* w2 = static_cast<T*>(a.w2);
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) {
+    const int64_t row = i / a.d, col = i - row * a.d;
+    const int64_t src = row % a.Ep;
+    w2[i] = (src < a.E) ? w[src * a.d + col] : from_f32<T>(0.0f);
+  }
+}
+
+// dW_r[e][n] = sum_s part[s][e][n] + sum_s part[s][Ep + e][n];  dbias = sum over blocks.
+template <typename T>
+__global__ void __launch_bounds__(NT) router_reduce_kernel(RouterReduceArgs a) {
+  const int64_t n = (int64_t)a.E * a.d;
+  const int64_t sstride = 2 * (int64_t)a.Ep * a.d;
+  T* dw = static_cast<T*>(a.dw);
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) {
+    const int64_t e = i / a.d, col = i - e * a.d;
+    float hi = 0.0f, lo = 0.0f;
+    for (int s = 0; s < a.splits; ++s) {
+      hi += a.part[s * sstride + e * a.d + col];
+      lo += a.part[s * sstride + (a.Ep + e) * a.d + col];
+    }
+    dw[i] = from_f32<T>(hi + lo);
+  }
+  if (a.dbias && blockIdx.x == 0) {
+    for (int e = threadIdx.x; e < a.E; e += NT) {
+      float s = 0.0f;
+      for (int b = 0; b < a.nb; ++b) s += a.dbias_part[(int64_t)b * a.E + e];
+      a.dbias[e] = s;
+    }
+  }
+}
+
+// ---- balancing statistic -----------------------------------------------------
+constexpr int kAuxTokens = 256;
+
+__global__ void __launch_bounds__(NT) aux_partials_kernel(AuxArgs a) {
+  const int e = threadIdx.x;
+  if (e >= a.E) return;
+  const int64_t t0 = (int64_t)blockIdx.x * kAuxTokens;
+  int64_t t1 = t0 + kAuxTokens;
+  if (t1 > a.T) t1 = a.T;
+  float ps = 0.0f, ent = 0.0f;
+  for (int64_t t = t0; t < t1; ++t) {
+    const float p = a.probs[t * a.E + e];
+    ps += p;
+    if (p > 0.0f) ent -= p * logf(p);
+  }
+  a.part[((int64_t)blockIdx.x * 2 + 0) * a.E + e] = ps;
+  a.part[((int64_t)blockIdx.x * 2 + 1) * a.E + e] = ent;
+}
+
+__device__ double block_sum_d(double v, double* sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  __syncthreads();
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  double s = 0.0;
+  for (int w = 0; w < NT / 64; ++w) s += sh[w];
+  return s;
+}
+
+__global__ void __launch_bounds__(NT) aux_finalize_kernel(AuxArgs a, int nblk) {
+  __shared__ double sh[NT / 64];
+  const int e = threadIdx.x;
+  const bool valid = e < a.E;
+  float ps = 0.0f, ent = 0.0f;
+  if (valid) {
+    for (int b = 0; b < nblk; ++b) {
+      ps += a.part[((int64_t)b * 2 + 0) * a.E + e];
+      ent += a.part[((int64_t)b * 2 + 1) * a.E + e];
+    }
+  }
+  const double T = (double)a.T;
+  const double cnt = valid ? (double)a.counts[e] : 0.0;
+  const double f = (T > 0) ? cnt / (T * a.k) : 0.0;
+  const double P = (T > 0) ? (double)ps / T : 0.0;
+  if (valid) {
+    a.f[e] = (float)f;
+    a.p_mean[e] = (float)P;
+  }
+  const double fp = block_sum_d(valid ? f * P : 0.0, sh);
+  const double ent_sum = block_sum_d(valid ? (double)ent : 0.0, sh);
+  const double csum = block_sum_d(cnt, sh);
+  const double mean = csum / a.E;
+  const double var = block_sum_d(valid ? (cnt - mean) * (cnt - mean) : 0.0, sh) / a.E;
+  const double unused = block_sum_d(valid && cnt == 0.0 ? 1.0 : 0.0, sh);
+  // min / max
+  double mn = valid ? cnt : 1e300, mx = valid ? cnt : -1.0;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = fmin(mn, __shfl_xor(mn, o, 64));
+    mx = fmax(mx, __shfl_xor(mx, o, 64));
+  }
+  __shared__ double smn[NT / 64], smx[NT / 64];
+  const int lane = e & 63, wave = e >> 6;
+  if (lane == 0) { smn[wave] = mn; smx[wave] = mx; }
+  __syncthreads();
+  if (e == 0) {
+    for (int w = 0; w < NT / 64; ++w) { mn = fmin(mn, smn[w]); mx = fmax(mx, smx[w]); }
+    moe_aux_out* o = static_cast<moe_aux_out*>(a.out);
+    o->aux = (float)(a.E * fp);
+    o->aux_raw = (float)fp;
+    o->entropy_mean = (T > 0) ? (float)(ent_sum / T) : 0.0f;
+    o->count_cv = mean > 0 ? (float)(sqrt(var) / mean) : 0.0f;
+    o->count_min = (int32_t)mn;
+    o->count_max = (int32_t)mx;
+    o->n_unused = (int32_t)unused;
+    o->reserved = 0;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(int dt, const CombineArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  int64_t grid = (a.T + 3) / 4;
+  if (grid > 8192) grid = 8192;
+  switch (dt) {
+    case DT_BF16: hipLaunchKernelGGL(combine_kernel<__bf16>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    case DT_F16: hipLaunchKernelGGL(combine_kernel<_Float16>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    case DT_F32: hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(int dt, const CombineBwdArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  int64_t grid = (a.T + 3) / 4;
+  if (grid > 8192) grid = 8192;
+  switch (dt) {
+    case DT_BF16: hipLaunchKernelGGL(combine_bwd_kernel<__bf16>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    case DT_F16: hipLaunchKernelGGL(combine_bwd_kernel<_Float16>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    case DT_F32: hipLaunchKernelGGL(combine_bwd_kernel<float>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+int router_dz_blocks(int64_t T) {
+  int64_t g = (T + 3) / 4;
+  if (g > 512) g = 512;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+hipError_t launch_router_dz(int dt, const RouterDzArgs& a, hipStream_t s) {
+  const int grid = router_dz_blocks(a.T);
+  switch (dt) {
+    case DT_BF16: hipLaunchKernelGGL(router_dz_kernel<__bf16>, dim3(grid), dim3(NT), 0, s, a); break;
+    case DT_F16: hipLaunchKernelGGL(router_dz_kernel<_Float16>, dim3(grid), dim3(NT), 0, s, a); break;
+    case DT_F32: hipLaunchKernelGGL(router_dz_kernel<float>, dim3(grid), dim3(NT), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_stack2(int dt, const Stack2Args& a, hipStream_t s) {
+  const int64_t n = 2 * (int64_t)a.Ep * a.d;
+  int64_t grid = (n + NT - 1) / NT;
+  if (grid > 2048) grid = 2048;
+  switch (dt) {
+    case DT_BF16: hipLaunchKernelGGL(stack2_kernel<__bf16>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    case DT_F16: hipLaunchKernelGGL(stack2_kernel<_Float16>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    case DT_F32: hipLaunchKernelGGL(stack2_kernel<float>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_router_reduce(int dt, const RouterReduceArgs& a, hipStream_t s) {
+  const int64_t n = (int64_t)a.E * a.d;
+  int64_t grid = (n + NT - 1) / NT;
+  if (grid > 2048) grid = 2048;
+  if (grid < 1) grid = 1;
+  switch (dt) {
+    case DT_BF16: hipLaunchKernelGGL(router_reduce_kernel<__bf16>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    case DT_F16: hipLaunchKernelGGL(router_reduce_kernel<_Float16>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    case DT_F32: hipLaunchKernelGGL(router_reduce_kernel<float>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+int aux_blocks(int64_t T) { return (int)((T + kAuxTokens - 1) / kAuxTokens); }
+
+hipError_t launch_aux(const AuxArgs& a, hipStream_t s) {
+  const int nblk = aux_blocks(a.T);
+  if (nblk > 0) {
+    hipLaunchKernelGGL(aux_partials_kernel, dim3(nblk), dim3(NT), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(aux_finalize_kernel, dim3(1), dim3(NT), 0, s, a, nblk);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,174 @@
+// Expert histogram, prefix scan and the stable token permutation.
+//
+// The assignments (t, j) are ordered by (expert ascending, token ascending),
+// deterministically and without atomics on global memory:
+//   1. permute_hist: each block of 1024 tokens builds, in LDS, one bit per
+//      token for every expert (bit set <=> the token chose that expert).  The
+//      popcount of the bits below a token is the token's rank among the
+//      block's tokens of that expert; the full popcount is the block's count.
+//      Ranks go to inv_perm (scratch until step 3), counts to the workspace.
+//   2. permute_scan: one workgroup turns the [blocks x E] counts into
+//      counts[E], offsets[E+1] and the first output row of every
+//      (block, expert) pair.
+//   3. permute_scatter: one wave per token computes its k destination rows,
+//      writes inv_perm / perm_token, reads the token's row of x once and
+//      writes it k times (every access a full 16-byte vector, rows contiguous).
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int NT = 256;
+constexpr int WORDS = kHistTokens / 32;   // 32-bit mask words per expert per block
+
+__global__ void __launch_bounds__(NT) permute_hist(PermuteArgs a) {
+  extern __shared__ uint32_t sm[];
+  uint32_t* mask = sm;                     // [E][WORDS]
+  uint32_t* pre = sm + a.E * WORDS;        // [E][WORDS] popcount of the words before
+  const int tid = threadIdx.x;
+  const int64_t tb = (int64_t)blockIdx.x * kHistTokens;
+  for (int i = tid; i < a.E * WORDS; i += NT) mask[i] = 0u;
+  __syncthreads();
+  for (int s = 0; s < kHistTokens / NT; ++s) {
+    const int tl = tid + NT * s;
+    const int64_t t = tb + tl;
+    if (t < a.T) {
+      for (int j = 0; j < a.k; ++j) {
+        const int e = a.idx[t * a.k + j];
+        if ((unsigned)e < (unsigned)a.E) atomicOr(&mask[e * WORDS + (tl >> 5)], 1u << (tl & 31));
+      }
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < a.E; e += NT) {
+    uint32_t run = 0;
+    for (int w = 0; w < WORDS; ++w) {
+      pre[e * WORDS + w] = run;
+      run += __popc(mask[e * WORDS + w]);
+    }
+    a.block_counts[(int64_t)blockIdx.x * a.E + e] = (int32_t)run;
+  }
+  __syncthreads();
+  for (int s = 0; s < kHistTokens / NT; ++s) {
+    const int tl = tid + NT * s;
+    const int64_t t = tb + tl;
+    if (t < a.T) {
+      for (int j = 0; j < a.k; ++j) {
+        const int e = a.idx[t * a.k + j];
+        int rank = 0;
+        if ((unsigned)e < (unsigned)a.E) {
+          const int w = tl >> 5, b = tl & 31;
+          rank = (int)(pre[e * WORDS + w] + __popc(mask[e * WORDS + w] & ((1u << b) - 1u)));
+        }
+        a.inv[t * a.k + j] = rank;
+      }
+    }
+  }
+}
+
+__global__ void __launch_bounds__(NT) permute_scan(PermuteArgs a, int nblk) {
+  constexpr int ROWS = 32;
+  __shared__ int32_t tile[ROWS * NT];
+  __shared__ int32_t s_w[NT / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e = tid;
+  int run = 0;
+  for (int b0 = 0; b0 < nblk; b0 += ROWS) {
+    const int nb = (nblk - b0) < ROWS ? (nblk - b0) : ROWS;
+    for (int i = tid; i < nb * a.E; i += NT) tile[i] = a.block_counts[(int64_t)b0 * a.E + i];
+    __syncthreads();
+    if (e < a.E) {
+      for (int b = 0; b < nb; ++b) {
+        const int c = tile[b * a.E + e];
+        a.block_base[(int64_t)(b0 + b) * a.E + e] = run;
+        run += c;
+      }
+    }
+    __syncthreads();
+  }
+  const int cnt = (e < a.E) ? run : 0;
+  int incl = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) s_w[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += s_w[w];
+  incl += before;
+  const int excl = incl - cnt;
+  if (e < a.E) {
+    a.counts[e] = cnt;
+    a.offsets[e] = excl;
+    for (int b = 0; b < nblk; ++b) a.block_base[(int64_t)b * a.E + e] += excl;
+  }
+  if (e == a.E - 1) a.offsets[a.E] = incl;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(NT) permute_scatter(PermuteArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * (NT / 64);
+  const int64_t rowbytes = (int64_t)a.d * sizeof(T);
+  const int nch = (int)(rowbytes / 16);
+  const char* xb = static_cast<const char*>(a.x);
+  char* xp = static_cast<char*>(a.x_perm);
+  for (int64_t t = (int64_t)blockIdx.x * (NT / 64) + (threadIdx.x >> 6); t < a.T; t += waves) {
+    int r_mine = -1;
+    if (lane < a.k) {
+      const int e = a.idx[t * a.k + lane];
+      if ((unsigned)e < (unsigned)a.E) {
+        const int rank = a.inv[t * a.k + lane];
+        r_mine = a.block_base[(t / kHistTokens) * a.E + e] + rank;
+        a.perm_token[r_mine] = (int32_t)t;
+      }
+      a.inv[t * a.k + lane] = r_mine;
+    }
+    // every lane runs the same number of iterations so the shuffles stay convergent
+    const char* src = xb + t * rowbytes;
+    for (int c0 = 0; c0 < nch; c0 += 64) {
+      const int c = c0 + lane;
+      const bool ok = c < nch;
+      const u32x4 v = ok ? ld16(src + (int64_t)c * 16) : (u32x4){0u, 0u, 0u, 0u};
+      for (int j = 0; j < a.k; ++j) {
+        const int r = __shfl(r_mine, j, 64);
+        if (ok && r >= 0) st16(xp + (int64_t)r * rowbytes + (int64_t)c * 16, v);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_permute_hist(const PermuteArgs& a, hipStream_t s) {
+  const int64_t nblk = (a.T + kHistTokens - 1) / kHistTokens;
+  if (nblk == 0) return hipSuccess;
+  const size_t shm = (size_t)a.E * WORDS * 2 * sizeof(uint32_t);
+  hipLaunchKernelGGL(permute_hist, dim3((unsigned)nblk), dim3(NT), shm, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_scan(const PermuteArgs& a, hipStream_t s) {
+  const int nblk = (int)((a.T + kHistTokens - 1) / kHistTokens);
+  hipLaunchKernelGGL(permute_scan, dim3(1), dim3(NT), 0, s, a, nblk);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_scatter(int dt, const PermuteArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  int64_t grid = (a.T + 3) / 4;
+  if (grid > 4096) grid = 4096;
+  switch (dt) {
+    case DT_BF16: hipLaunchKernelGGL(permute_scatter<__bf16>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    case DT_F16: hipLaunchKernelGGL(permute_scatter<_Float16>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    case DT_F32: hipLaunchKernelGGL(permute_scatter<float>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,226 @@
+// Router: logits on the matrix cores, f32 softmax, top-k and renormalisation.
+//
+// spark-gpt README, feature list (Qwen3-MoE layers): softmax taken in fp32,
+// top-k over the experts, the chosen probabilities optionally rescaled to sum
+// to one (KochiLLM v1.0 model card, "Architecture").
+//
+// A wave owns 32 tokens.  The expert weights (rows of W_r, padded to a
+// multiple of 32) are the MFMA "A" operand and the token rows the "B"
+// operand, so after the K loop lane l holds the logits of token l % 32 for
+// half of the experts (e = 32 s + 8 (r/4) + 4 (l/32) + r%4); the other half
+// sits in lane l ^ 32.  Softmax and top-k then need only one cross-lane
+// exchange per reduction.  Top-k is k rounds of "largest remaining logit,
+// lower expert index on ties", which also fixes the slot order.
+
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int KB = 128;
+constexpr int LROW = KB + 16;
+
+template <typename T, int NSUB, int WAVES>
+__global__ void __launch_bounds__(WAVES * 64) route_kernel(RouteArgs a) {
+  constexpr int ES = sizeof(T);
+  constexpr int BK = KB / ES;
+  constexpr int TB = 32 * WAVES;          // tokens per workgroup
+  constexpr int EP = 32 * NSUB;           // padded experts
+  constexpr int NTH = WAVES * 64;
+  constexpr int XPT = TB * 8 / NTH;       // 16-byte chunks of the x tile per thread (= 4)
+  constexpr int WPT = EP * 8 / NTH;       // 16-byte chunks of the W tile per thread
+  static_assert(WPT >= 1, "too many waves for the expert tile");
+
+  __shared__ __attribute__((aligned(16))) char lx[TB * LROW];
+  __shared__ __attribute__((aligned(16))) char lw[EP * LROW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * TB;
+  const char* xb = static_cast<const char*>(a.x);
+  const char* wb = static_cast<const char*>(a.w);
+
+  auto load = [&](int kc, u32x4* rx, u32x4* rw) {
+#pragma unroll
+    for (int s = 0; s < XPT; ++s) {
+      const int c = tid + NTH * s, r = c >> 3, cc = c & 7;
+      rx[s] = (t0 + r < a.T) ? ld16(xb + ((t0 + r) * a.d + kc) * ES + cc * 16) : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int s = 0; s < WPT; ++s) {
+      const int c = tid + NTH * s, r = c >> 3, cc = c & 7;
+      rw[s] = (r < a.E) ? ld16(wb + ((int64_t)r * a.d + kc) * ES + cc * 16) : (u32x4){0u, 0u, 0u, 0u};
+    }
+  };
+  auto stage = [&](const u32x4* rx, const u32x4* rw) {
+#pragma unroll
+    for (int s = 0; s < XPT; ++s) {
+      const int c = tid + NTH * s;
+      st16(lx + (c >> 3) * LROW + (c & 7) * 16, rx[s]);
+    }
+#pragma unroll
+    for (int s = 0; s < WPT; ++s) {
+      const int c = tid + NTH * s;
+      st16(lw + (c >> 3) * LROW + (c & 7) * 16, rw[s]);
+    }
+  };
+
+  f32x16 acc[NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[s][r] = 0.0f;
+
+  constexpr int CH = Mma32<T>::kChunks;
+  const int nk = a.d / BK;
+  u32x4 rx[XPT], rw[WPT];
+  load(0, rx, rw);
+  stage(rx, rw);
+  __syncthreads();
+  for (int kc = 0; kc < nk; ++kc) {
+    const bool more = kc + 1 < nk;
+    if (more) load((kc + 1) * BK, rx, rw);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int kb = ks * 16 * ES + (lane >> 5) * 8 * ES;
+      u32x4 fb[CH];
+      const char* xrow = lx + (wave * 32 + (lane & 31)) * LROW + kb;
+#pragma unroll
+      for (int ch = 0; ch < CH; ++ch) fb[ch] = ld16(xrow + ch * 16);
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) {
+        u32x4 fa[CH];
+        const char* wrow = lw + (s * 32 + (lane & 31)) * LROW + kb;
+#pragma unroll
+        for (int ch = 0; ch < CH; ++ch) fa[ch] = ld16(wrow + ch * 16);
+        Mma32<T>::run(acc[s], fa, fb);
+      }
+    }
+    __syncthreads();
+    if (more) stage(rx, rw);
+    __syncthreads();
+  }
+
+  const int h = lane >> 5;
+  const int64_t t = t0 + wave * 32 + (lane & 31);
+  const bool tv = t < a.T;
+  const int E = a.E;
+
+  // logits (+ constant bias); padded experts never take part
+  float z[NSUB][16];
+  float m = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int e = s * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      float v = acc[s][r];
+      if (a.bias && e < E) v += a.bias[e];
+      z[s][r] = (e < E) ? v : -INFINITY;
+      m = fmaxf(m, z[s][r]);
+    }
+  m = fmaxf(m, __shfl_xor(m, 32, 64));
+  float sum = 0.0f;
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int e = s * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (e < E) sum += expf(z[s][r] - m);
+    }
+  sum += __shfl_xor(sum, 32, 64);
+
+  if (tv) {
+    float* prow = a.probs + t * E;
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e0 = s * 32 + 8 * q + 4 * h;
+        if (e0 >= E) continue;
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = expf(z[s][4 * q + i] - m) / sum;
+        if ((E & 3) == 0) {
+          *reinterpret_cast<f32x4*>(prow + e0) = (f32x4){p[0], p[1], p[2], p[3]};
+        } else {
+          for (int i = 0; i < 4; ++i)
+            if (e0 + i < E) prow[e0 + i] = p[i];
+        }
+      }
+  }
+
+  // top-k: k rounds of (largest remaining logit, lower index on ties)
+  uint32_t taken[NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) taken[s] = 0u;
+  float psum = 0.0f;
+  for (int j = 0; j < a.k; ++j) {
+    float bv = -INFINITY;
+    int be = -1;
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int e = s * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (e < E && !((taken[s] >> r) & 1u) && (be < 0 || z[s][r] > bv)) {
+          bv = z[s][r];
+          be = e;
+        }
+      }
+    const float pv = __shfl_xor(bv, 32, 64);
+    const int pe = __shfl_xor(be, 32, 64);
+    const bool partner = (be < 0) || (pe >= 0 && (pv > bv || (pv == bv && pe < be)));
+    const float wv = partner ? pv : bv;
+    const int we = partner ? pe : be;
+    if (!partner) {
+      const int s = we >> 5, w5 = we & 31;
+      const int r = ((w5 >> 3) << 2) | (w5 & 3);
+#pragma unroll
+      for (int ss = 0; ss < NSUB; ++ss)
+        if (ss == s) taken[ss] |= 1u << r;
+    }
+    const float pj = expf(wv - m) / sum;
+    psum += pj;
+    if (tv && h == 0) {
+      a.idx[t * a.k + j] = we;
+      a.wts[t * a.k + j] = pj;
+    }
+  }
+  if (a.renorm && tv && h == 0) {
+    for (int j = 0; j < a.k; ++j) a.wts[t * a.k + j] = a.wts[t * a.k + j] / psum;
+  }
+}
+
+template <typename T, int NSUB, int WAVES>
+hipError_t launch_route_t(const RouteArgs& a, hipStream_t s) {
+  const int64_t tb = 32 * WAVES;
+  const int64_t grid = (a.T + tb - 1) / tb;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((route_kernel<T, NSUB, WAVES>), dim3((unsigned)grid), dim3(WAVES * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_route_dt(const RouteArgs& a, hipStream_t s) {
+  const int nsub = (a.E + 31) / 32;
+  if (nsub <= 1) return launch_route_t<T, 1, 1>(a, s);
+  if (nsub <= 2) return launch_route_t<T, 2, 1>(a, s);
+  if (nsub <= 4) return launch_route_t<T, 4, 2>(a, s);
+  return launch_route_t<T, 8, 4>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_route(int dt, const RouteArgs& a, hipStream_t s) {
+  switch (dt) {
+    case DT_BF16: return launch_route_dt<__bf16>(a, s);
+    case DT_F16: return launch_route_dt<_Float16>(a, s);
+    case DT_F32: return launch_route_dt<float>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

@@ -1,0 +1,98 @@
+"""A plan plus the device buffers one fwd+bwd step of the layer needs.
+
+Allocation only (torch is the device allocator here): every step of the
+computation is one of the six C-ABI calls, issued in order on one stream with
+no host synchronisation in between.
+"""
+
+import torch
+
+from . import _lib as L
+
+
+class MoELayer:
+    def __init__(self, plan: L.Plan, device="cuda"):
+        self.plan = p = plan
+        dev = torch.device(device)
+        dt = p.dtype
+        T, d, E, k, I, A = p.T, p.d, p.E, p.k, p.I, p.T * p.k
+        z = lambda *s, dtype=dt: torch.empty(*s, dtype=dtype, device=dev)
+        self.probs = z(T, E, dtype=torch.float32)
+        self.topk_idx = z(T, k, dtype=torch.int32)
+        self.topk_w = z(T, k, dtype=torch.float32)
+        self.counts = z(E, dtype=torch.int32)
+        self.offsets = z(E + 1, dtype=torch.int32)
+        self.perm_token = z(A, dtype=torch.int32)
+        self.inv_perm = z(T, k, dtype=torch.int32)
+        self.x_perm = z(A, d)
+        self.gu = z(A, 2 * I)
+        self.h = z(A, I)
+        self.y_perm = z(A, d)
+        self.y = z(T, d)
+        if p.Ns > 0:
+            NI = p.Ns * p.Is
+            self.gu_shared = z(T, 2 * NI)
+            self.h_shared = z(T, NI)
+            self.y_shared = z(T, d)
+        else:
+            self.gu_shared = self.h_shared = self.y_shared = None
+        self.grads = {
+            "dx": z(T, d),
+            "dw_router": z(E, d),
+            "dbias": z(E, dtype=torch.float32),
+            "dw_gate_up": z(E, 2 * I, d),
+            "dw_down": z(E, d, I),
+            "dws_gate_up": z(p.Ns, 2 * p.Is, d) if p.Ns else None,
+            "dws_down": z(p.Ns, d, p.Is) if p.Ns else None,
+        }
+        self.f = z(E, dtype=torch.float32)
+        self.p_mean = z(E, dtype=torch.float32)
+        self.aux_out = torch.zeros(L.ctypes.sizeof(L.MoeAuxScalars), dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(max(p.workspace_bytes(), 256), dtype=torch.uint8, device=dev)
+        self.params = None
+
+    # -------------------------------------------------------------- forward
+    def set_params(self, x, w_router, w_gate_up, w_down, bias=None, ws_gate_up=None, ws_down=None):
+        self.params = dict(x=x, w_router=w_router, w_gate_up=w_gate_up, w_down=w_down, bias=bias,
+                           ws_gate_up=ws_gate_up, ws_down=ws_down)
+
+    def route(self, stream=None):
+        q = self.params
+        L.moe_route(self.plan, q["x"], q["w_router"], q["bias"], self.probs, self.topk_idx, self.topk_w,
+                    stream)
+
+    def dispatch_and_experts(self, stream=None):
+        q = self.params
+        L.moe_permute(self.plan, self.topk_idx, q["x"], self.counts, self.offsets, self.perm_token,
+                      self.inv_perm, self.x_perm, self.ws, stream)
+        L.moe_expert_ffn(self.plan, self.x_perm, self.offsets, q["w_gate_up"], q["w_down"], self.gu,
+                         self.h, self.y_perm, q["x"], q["ws_gate_up"], q["ws_down"], self.gu_shared,
+                         self.h_shared, self.y_shared, self.ws, stream)
+        L.moe_combine(self.plan, self.y_perm, self.inv_perm, self.topk_w, self.y_shared, self.y, stream)
+
+    def forward(self, stream=None):
+        self.route(stream)
+        self.dispatch_and_experts(stream)
+        return self.y
+
+    # ------------------------------------------------------------- backward
+    def saved(self):
+        q = self.params
+        return dict(x=q["x"], w_router=q["w_router"], probs=self.probs, topk_idx=self.topk_idx,
+                    topk_w=self.topk_w, counts=self.counts, offsets=self.offsets, inv_perm=self.inv_perm,
+                    x_perm=self.x_perm, gu=self.gu, h=self.h, y_perm=self.y_perm, w_gate_up=q["w_gate_up"],
+                    w_down=q["w_down"], ws_gate_up=q["ws_gate_up"], ws_down=q["ws_down"],
+                    gu_shared=self.gu_shared, h_shared=self.h_shared)
+
+    def backward(self, dy, stream=None):
+        L.moe_backward(self.plan, self.saved(), dy, self.grads, self.ws, stream)
+        return self.grads
+
+    def aux_stats(self, stream=None):
+        L.moe_aux_stats(self.plan, self.probs, self.counts, self.f, self.p_mean, self.aux_out, self.ws, stream)
+
+    def step(self, dy, stream=None):
+        """One full pass: route, permute, experts, combine, backward, aux statistics."""
+        self.forward(stream)
+        self.backward(dy, stream)
+        self.aux_stats(stream)

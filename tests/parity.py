@@ -1,0 +1,189 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI,
+run the fp64 oracle on the same seeded inputs, compare.
+
+Tolerances (max |gpu - oracle| <= c * RMS(oracle tensor), per tensor):
+  c = 2e-2 for bf16 / f16 storage (the layer's stated bar), c = 1e-4 for f32
+  storage (f32 MFMA products, f32 intermediates); router probabilities and
+  routing weights within 1e-6 absolute; routing indices, counts, offsets,
+  permutation and inverse permutation bit-exact, except tokens whose oracle
+  logits tie within 1e-5 (set or slot order), whose GPU choice must only be a
+  valid top-k within that margin.
+"""
+
+import sys
+
+import numpy as np
+import torch
+
+import moe_inputs as MI
+import oracle as O
+
+TIE_EPS = 1e-5
+PROB_ATOL = 1e-6
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_tol(wl):
+    return 1e-4 if wl.dtype == "f32" else 2e-2
+
+
+def plan_for(wl, has_bias):
+    from mixture_experts_ffn_wave_amd import Plan
+    return Plan(wl.T, wl.d, wl.E, wl.k, wl.I, n_shared=wl.n_shared, d_ff_shared=wl.I_shared,
+                renorm=wl.renorm, has_router_bias=has_bias, dtype=wl.torch_dtype, aux_coef=wl.aux_coef)
+
+
+def to_np(t):
+    if t is None:
+        return None
+    t = t.detach().cpu()
+    if t.dtype in (torch.int32, torch.int64):
+        return t.to(torch.int64).numpy()
+    return t.to(torch.float64).numpy()
+
+
+def gpu_run(wl, inp, routing=None):
+    """One fwd+bwd step on cuda:0.  ``routing`` (probs, idx, w as numpy) replaces
+    the router's outputs when given (then moe_route is not called)."""
+    from mixture_experts_ffn_wave_amd import MoELayer, decode_aux
+    b = inp.get("bias")
+    plan = plan_for(wl, b is not None)
+    layer = MoELayer(plan)
+    dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+    layer.set_params(dev["x"], dev["w_router"], dev["w_gate_up"], dev["w_down"],
+                     bias=(dev["bias"].float() if b is not None else None),
+                     ws_gate_up=dev.get("ws_gate_up"), ws_down=dev.get("ws_down"))
+    if routing is None:
+        layer.forward()
+    else:
+        layer.probs.copy_(torch.from_numpy(routing["p"]).to(torch.float32))
+        layer.topk_idx.copy_(torch.from_numpy(routing["idx"]).to(torch.int32))
+        layer.topk_w.copy_(torch.from_numpy(routing["w"]).to(torch.float32))
+        layer.dispatch_and_experts()
+    layer.backward(dev["dy"])
+    layer.aux_stats()
+    torch.cuda.synchronize()
+    out = {n: to_np(getattr(layer, n)) for n in
+           ["probs", "topk_idx", "topk_w", "counts", "offsets", "perm_token", "inv_perm", "x_perm", "gu",
+            "h", "y_perm", "y", "gu_shared", "h_shared", "y_shared", "f", "p_mean"]}
+    for n, t in layer.grads.items():
+        out[n] = to_np(t)
+    out["aux"] = decode_aux(layer.aux_out)
+    return out
+
+
+def oracle_inputs(inp):
+    return {k: MI.to_f64(v) for k, v in inp.items()}
+
+
+def oracle_run(wl, f64):
+    b = f64.get("bias")
+    fwd = O.layer_forward(f64["x"], f64["w_router"], f64["w_gate_up"], f64["w_down"], top_k=wl.k,
+                          renorm=wl.renorm, bias=b, ws_gate_up=f64.get("ws_gate_up"),
+                          ws_down=f64.get("ws_down"))
+    bwd = O.layer_backward(fwd, f64["dy"], aux_coef=wl.aux_coef)
+    st = O.aux_statistics(fwd["p"], fwd["counts"], wl.k)
+    return fwd, bwd, st
+
+
+def check_close(name, got, ref, c):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, f"{name}: shape {got.shape} vs {ref.shape}"
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    assert err <= c * rms + 1e-30, f"{name}: max abs err {err:.3e} > {c:g} x RMS {rms:.3e}"
+    return err, rms
+
+
+def compare_routing(wl, gpu, fwd):
+    """Returns True when the GPU chose exactly the oracle's routing for every
+    token; asserts that any difference is an allowed near-tie."""
+    z = fwd["z"]
+    k, E = wl.k, wl.E
+    assert np.max(np.abs(gpu["probs"] - fwd["p"])) <= PROB_ATOL, "router probabilities"
+    gi = gpu["topk_idx"]
+    same = np.all(gi == fwd["idx"], axis=1)
+    set_tie, order_tie = O.near_tie_tokens(z, k, TIE_EPS)
+    bad = ~same & ~(set_tie | order_tie)
+    assert not bad.any(), f"routing differs on {int(bad.sum())} non-tied tokens, e.g. {np.where(bad)[0][:5]}"
+    for t in np.where(~same)[0]:
+        sel = gi[t]
+        assert len(set(sel.tolist())) == k and sel.min() >= 0 and sel.max() < E
+        zs = z[t, sel]
+        assert np.all(np.diff(zs) <= TIE_EPS), f"token {t}: slot order not descending"
+        rest = np.setdiff1d(np.arange(E), sel)
+        if rest.size:
+            assert zs.min() >= z[t, rest].max() - TIE_EPS, f"token {t}: not a top-k"
+    if same.any():
+        assert np.max(np.abs(gpu["topk_w"][same] - fwd["w"][same])) <= PROB_ATOL, "routing weights"
+    return bool(same.all())
+
+
+def compare_downstream(wl, gpu, fwd, bwd, st):
+    c = rel_tol(wl)
+    # integer work: bit-exact
+    assert np.array_equal(gpu["counts"], fwd["counts"]), "counts"
+    assert np.array_equal(gpu["offsets"], fwd["offsets"]), "offsets"
+    assert np.array_equal(gpu["perm_token"], fwd["perm_token"]), "perm_token"
+    assert np.array_equal(gpu["inv_perm"], fwd["inv"]), "inv_perm"
+    assert np.array_equal(gpu["x_perm"], fwd["x_perm"]), "x_perm is a pure copy"
+    inter = wl.I
+    check_close("G", gpu["gu"][:, :inter], fwd["g"], c)
+    check_close("U", gpu["gu"][:, inter:], fwd["u"], c)
+    check_close("H", gpu["h"], fwd["h"], c)
+    check_close("Y_perm", gpu["y_perm"], fwd["y_perm"], c)
+    if wl.n_shared:
+        Is = wl.I_shared
+        for s, (gs, us, hs) in enumerate(fwd["shared"]):
+            check_close(f"G_shared[{s}]", gpu["gu_shared"][:, 2 * s * Is:2 * s * Is + Is], gs, c)
+            check_close(f"U_shared[{s}]", gpu["gu_shared"][:, 2 * s * Is + Is:2 * (s + 1) * Is], us, c)
+            check_close(f"H_shared[{s}]", gpu["h_shared"][:, s * Is:(s + 1) * Is], hs, c)
+        check_close("Y_shared", gpu["y_shared"], fwd["y_shared"], c)
+    check_close("y", gpu["y"], fwd["y"], c)
+    check_close("dx", gpu["dx"], bwd["dx"], c)
+    check_close("dW_router", gpu["dw_router"], bwd["dw_router"], c)
+    check_close("dbias", gpu["dbias"], bwd["dbias"], c)
+    check_close("dW_gate_up", gpu["dw_gate_up"], bwd["dw_gate_up"], c)
+    check_close("dW_down", gpu["dw_down"], bwd["dw_down"], c)
+    empty = np.where(fwd["counts"] == 0)[0]
+    for e in empty:
+        assert not np.any(gpu["dw_gate_up"][e]) and not np.any(gpu["dw_down"][e]), f"empty expert {e} grads"
+    if wl.n_shared:
+        check_close("dWs_gate_up", gpu["dws_gate_up"], bwd["dws_gate_up"], c)
+        check_close("dWs_down", gpu["dws_down"], bwd["dws_down"], c)
+    # balancing statistic and metrics
+    assert np.allclose(gpu["f"], st["f"], rtol=1e-6, atol=0), "f"
+    assert np.max(np.abs(gpu["p_mean"] - st["p_mean"])) <= PROB_ATOL, "p_mean"
+    a = gpu["aux"]
+    assert abs(a["aux"] - st["aux"]) <= 1e-5 * max(1.0, abs(st["aux"])), ("aux", a["aux"], st["aux"])
+    assert abs(a["aux_raw"] - st["aux_raw"]) <= 1e-5 * max(1.0, abs(st["aux_raw"]))
+    assert abs(a["entropy_mean"] - st["entropy_mean"]) <= 1e-5 * max(1.0, abs(st["entropy_mean"]))
+    assert abs(a["count_cv"] - st["count_cv"]) <= 1e-5 * max(1.0, abs(st["count_cv"]))
+    assert a["count_min"] == st["count_min"] and a["count_max"] == st["count_max"]
+    assert a["n_unused"] == st["n_unused"]
+
+
+def full_parity(wl, inp=None):
+    """The whole chain on the GPU against the oracle.  When a near-tie made
+    the GPU pick a different (valid) routing, the downstream calls are run a
+    second time from the oracle's routing so every later tensor is compared
+    on identical assignments."""
+    if inp is None:
+        inp = MI.make_inputs(wl)
+    f64 = oracle_inputs(inp)
+    say(f"[parity] {wl.name}: {MI.describe(wl)} -- GPU chain")
+    gpu = gpu_run(wl, inp)
+    say(f"[parity] {wl.name}: oracle")
+    fwd, bwd, st = oracle_run(wl, f64)
+    identical = compare_routing(wl, gpu, fwd)
+    if not identical:
+        say(f"[parity] {wl.name}: near-tie routing differs; rerunning downstream from the oracle routing")
+        gpu = gpu_run(wl, inp, routing={"p": fwd["p"], "idx": fwd["idx"], "w": fwd["w"]})
+    compare_downstream(wl, gpu, fwd, bwd, st)
+    return gpu, fwd, bwd, st

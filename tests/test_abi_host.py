@@ -1,0 +1,168 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched).
+
+The library must load, export every function include/moe.h declares, reject
+bad configurations with the documented status codes before launching
+anything, and size its workspace consistently.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_ffn_wave_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+MOE_OK, MOE_ERR_NULL, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4, -5
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**(moe_[a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.lib()
+    names = declared_functions()
+    assert len(names) >= 14, names
+    for n in names:
+        assert hasattr(lib, n), f"libmoe.so does not export {n}"
+    # the binding describes exactly the header's functions
+    assert sorted(L.SIGNATURES) == names
+
+
+def test_version_and_status_strings():
+    lib = L.lib()
+    assert b"gfx950" in lib.moe_version()
+    for st in (MOE_OK, MOE_ERR_NULL, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP):
+        s = lib.moe_status_string(st)
+        assert s and s != b"unknown status"
+    assert lib.moe_status_string(123) == b"unknown status"
+
+
+def test_struct_sizes_match_header_layout():
+    assert ctypes.sizeof(L.MoeConfig) == 56          # int64 + 10 int32 + float, 8-aligned
+    assert ctypes.sizeof(L.MoeAuxScalars) == 32
+    assert ctypes.sizeof(L.MoeFfnArgs) == 13 * 8
+    assert ctypes.sizeof(L.MoeSaved) == 18 * 8
+    assert ctypes.sizeof(L.MoeGrads) == 7 * 8
+
+
+def _create(**kw):
+    base = dict(T=512, d_model=256, n_experts=8, top_k=2, d_ff=128, n_shared=0, d_ff_shared=0,
+                renorm=1, has_router_bias=0, act_dtype=L.MOE_BF16, expert_dtype=L.MOE_BF16, aux_coef=0.01)
+    base.update(kw)
+    cfg = L.MoeConfig(**base)
+    h = ctypes.c_void_p()
+    st = L.lib().moe_plan_create(ctypes.byref(cfg), ctypes.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), MOE_OK),
+    (dict(T=0), MOE_OK),
+    (dict(T=-1), MOE_ERR_INVALID),
+    (dict(n_experts=0), MOE_ERR_INVALID),
+    (dict(n_experts=257, top_k=2), MOE_ERR_INVALID),
+    (dict(top_k=0), MOE_ERR_INVALID),
+    (dict(top_k=9), MOE_ERR_INVALID),                 # k > E
+    (dict(n_experts=128, top_k=65), MOE_ERR_INVALID),  # k > 64
+    (dict(d_model=200), MOE_ERR_UNSUPPORTED),
+    (dict(d_ff=96), MOE_ERR_UNSUPPORTED),
+    (dict(n_shared=1, d_ff_shared=0), MOE_ERR_INVALID),
+    (dict(n_shared=1, d_ff_shared=100), MOE_ERR_UNSUPPORTED),
+    (dict(n_shared=2, d_ff_shared=256), MOE_OK),
+    (dict(renorm=2), MOE_ERR_INVALID),
+    (dict(act_dtype=7), MOE_ERR_INVALID),
+    (dict(act_dtype=L.MOE_MXFP8_E4M3, expert_dtype=L.MOE_MXFP8_E4M3), MOE_ERR_UNSUPPORTED),
+    (dict(expert_dtype=L.MOE_F16), MOE_ERR_UNSUPPORTED),
+    (dict(aux_coef=float("nan")), MOE_ERR_INVALID),
+    (dict(act_dtype=L.MOE_F32, expert_dtype=L.MOE_F32), MOE_OK),
+    (dict(act_dtype=L.MOE_F16, expert_dtype=L.MOE_F16), MOE_OK),
+])
+def test_plan_validation(kw, status):
+    st, h = _create(**kw)
+    assert st == status
+    if st == MOE_OK:
+        assert h.value
+        L.lib().moe_plan_destroy(h)
+    else:
+        assert not h.value
+
+
+def test_plan_create_null_arguments():
+    lib = L.lib()
+    h = ctypes.c_void_p()
+    assert lib.moe_plan_create(None, ctypes.byref(h)) == MOE_ERR_NULL
+    cfg = L.MoeConfig(512, 256, 8, 2, 128, 0, 0, 1, 0, L.MOE_BF16, L.MOE_BF16, 0.01)
+    assert lib.moe_plan_create(ctypes.byref(cfg), None) == MOE_ERR_NULL
+
+
+def test_workspace_grows_with_tokens_and_width():
+    sizes = []
+    for T in (0, 512, 4096, 16384):
+        p = L.Plan(T, 512, 8, 2, 768, dtype=L.torch.bfloat16)
+        sizes.append(p.workspace_bytes())
+        p.close()
+    assert all(a <= b for a, b in zip(sizes, sizes[1:])) and sizes[-1] > sizes[0]
+    a = L.Plan(4096, 512, 8, 2, 768).workspace_bytes()
+    b = L.Plan(4096, 512, 8, 2, 1536).workspace_bytes()
+    c = L.Plan(4096, 512, 8, 2, 768, n_shared=1, d_ff_shared=768).workspace_bytes()
+    assert b > a and c > a
+    # 256-byte aligned regions
+    assert a % 256 == 0
+
+
+def test_calls_reject_bad_arguments_before_any_launch():
+    lib = L.lib()
+    p = L.Plan(512, 256, 8, 2, 128)
+    h = p.handle
+    nul = None
+    # route: NULL pointers
+    assert lib.moe_route(h, nul, nul, nul, nul, nul, nul, nul) == MOE_ERR_NULL
+    assert lib.moe_route(None, nul, nul, nul, nul, nul, nul, nul) == MOE_ERR_NULL
+    # permute: workspace missing / too small (pointers are never dereferenced on the host)
+    fake = ctypes.c_void_p(0x1000)
+    args = [h, fake, fake, fake, fake, fake, fake, fake]
+    assert lib.moe_permute(*args, nul, 0, nul) == MOE_ERR_WORKSPACE
+    assert lib.moe_permute(*args, fake, p.workspace_bytes() - 1, nul) == MOE_ERR_WORKSPACE
+    # combine / ffn / backward / aux: NULLs
+    assert lib.moe_combine(h, nul, nul, nul, nul, nul, nul) == MOE_ERR_NULL
+    assert lib.moe_expert_ffn(h, None, nul, 0, nul) == MOE_ERR_NULL
+    empty = L.MoeFfnArgs()
+    assert lib.moe_expert_ffn(h, ctypes.byref(empty), nul, 0, nul) == MOE_ERR_NULL
+    assert lib.moe_backward(h, None, nul, None, nul, 0, nul) == MOE_ERR_NULL
+    sv, gr = L.MoeSaved(), L.MoeGrads()
+    assert lib.moe_backward(h, ctypes.byref(sv), nul, ctypes.byref(gr), nul, 0, nul) == MOE_ERR_NULL
+    assert lib.moe_aux_stats(h, nul, nul, nul, nul, nul, nul, 0, nul) == MOE_ERR_NULL
+    # a plan with a bias requires the bias pointer
+    pb = L.Plan(512, 256, 8, 2, 128, has_router_bias=True)
+    assert lib.moe_route(pb.handle, fake, fake, nul, fake, fake, fake, nul) == MOE_ERR_NULL
+    pb.close()
+    p.close()
+
+
+def test_probe_rejects_unknown_kernel_names():
+    p = L.Plan(512, 256, 8, 2, 128)
+    lib = L.lib()
+    assert lib.moe_probe_enable(p.handle, b"no_such_kernel", 4) == MOE_ERR_INVALID
+    assert lib.moe_probe_enable(p.handle, b"route", 0) == MOE_OK        # disabling needs no GPU
+    names = L.kernel_names()
+    assert "gemm_gate_up_swiglu" in names and "route" in names and "combine" in names
+    ms, n = ctypes.c_float(), ctypes.c_int32()
+    assert lib.moe_probe_read(p.handle, ctypes.byref(ms), ctypes.byref(n)) == MOE_OK and n.value == 0
+    p.close()
+
+
+def test_empty_batch_route_and_combine_are_no_ops():
+    p = L.Plan(0, 256, 8, 2, 128)
+    lib = L.lib()
+    # T = 0: nothing to do, nothing launched, pointers may be NULL
+    assert lib.moe_route(p.handle, None, None, None, None, None, None, None) == MOE_OK
+    assert lib.moe_combine(p.handle, None, None, None, None, None, None) == MOE_OK
+    p.close()
