@@ -1,0 +1,207 @@
+"""Benchmark: one fwd+bwd step of the routed MoE SwiGLU layer on one MI355X.
+
+A step is one pass of the whole path over one synthetic batch: route, permute,
+expert FFN (grouped GEMMs), combine, backward (all gradients) and the
+balancing statistic -- the six C-ABI calls, back to back on one stream.
+Inputs are resident in HBM before the timed region starts.
+
+Prints ONE JSON line (rank 0, N = 1): tokens/s over K timed steps, plus
+  roofline      -- the dominant kernel's algorithmic FLOPs per launch over its
+                   average launch time (hipEvents recorded around that kernel
+                   inside the timed region), against the bf16 MFMA peak;
+  cpu_baseline  -- the fp64 numpy oracle timed on the host on a bounded
+                   sample of the same workload.
+Per-kernel times go to stderr.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import moe_inputs as MI  # noqa: E402
+
+METRIC = "MoE FFN layer tokens/s fwd+bwd; grouped-GEMM TFLOP/s as % of MFMA peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3, "mxfp8": 5000.0}
+HBM_PEAK_GBS = 8000.0
+
+
+def kernel_flops(wl):
+    """Algorithmic FLOPs per launch of each GEMM kernel (real rows only)."""
+    A = wl.T * wl.k
+    d, I = wl.d, wl.I
+    f = {
+        "gemm_gate_up_swiglu": 2.0 * A * d * 2 * I,
+        "gemm_down": 2.0 * A * I * d,
+        "gemm_down_dgrad_swiglu": 2.0 * A * d * I,
+        "gemm_wgrad_down": 2.0 * A * d * I,
+        "gemm_gate_up_dgrad": 2.0 * A * 2 * I * d,
+        "gemm_wgrad_gate_up": 2.0 * A * 2 * I * d,
+        "gemm_router_dx": 2.0 * wl.T * wl.E * d,
+        "gemm_wgrad_router": 2.0 * wl.T * wl.E * d,
+    }
+    if wl.n_shared:
+        NI = wl.n_shared * wl.I_shared
+        f.update({
+            "gemm_gate_up_swiglu_shared": 2.0 * wl.T * d * 2 * NI,
+            "gemm_down_shared": 2.0 * wl.T * NI * d,
+            "gemm_down_dgrad_swiglu_shared": 2.0 * wl.T * d * NI,
+            "gemm_wgrad_down_shared": 2.0 * wl.T * d * NI,
+            "gemm_gate_up_dgrad_shared": 2.0 * wl.T * 2 * NI * d,
+            "gemm_wgrad_gate_up_shared": 2.0 * wl.T * 2 * NI * d,
+        })
+    return f
+
+
+def expert_flops(wl):
+    return 18.0 * wl.d * (wl.T * wl.k * wl.I + wl.T * wl.n_shared * wl.I_shared)
+
+
+def make_layer(wl, device="cuda"):
+    from mixture_experts_ffn_wave_amd import MoELayer, Plan
+    inp = MI.make_inputs(wl)
+    dev = {k: (v.to(device) if v is not None else None) for k, v in inp.items()}
+    plan = Plan(wl.T, wl.d, wl.E, wl.k, wl.I, n_shared=wl.n_shared, d_ff_shared=wl.I_shared,
+                renorm=wl.renorm, has_router_bias=dev["bias"] is not None, dtype=wl.torch_dtype,
+                aux_coef=wl.aux_coef)
+    layer = MoELayer(plan, device)
+    layer.set_params(dev["x"], dev["w_router"], dev["w_gate_up"], dev["w_down"], bias=dev["bias"],
+                     ws_gate_up=dev.get("ws_gate_up"), ws_down=dev.get("ws_down"))
+    return layer, dev
+
+
+def per_kernel_times(layer, dy, names, steps=3):
+    """Average launch time (ms) of every kernel, one probe pass per name."""
+    from mixture_experts_ffn_wave_amd import probe_enable, probe_read
+    out = {}
+    for n in names:
+        probe_enable(layer.plan, n, 64)
+        for _ in range(steps):
+            layer.step(dy)
+        ms, cnt = probe_read(layer.plan)
+        probe_enable(layer.plan, n, 0)
+        if cnt:
+            out[n] = (ms / cnt, cnt // steps)
+    return out
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The fp64 oracle, untuned, on the host cores: whole fwd+bwd+aux passes of
+    the same workload until ~budget_s of CPU time has run (at least one)."""
+    import numpy as np  # noqa: F401
+    import oracle as O
+    inp = MI.make_inputs(wl)
+    f = {k: MI.to_f64(v) for k, v in inp.items()}
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        fwd = O.layer_forward(f["x"], f["w_router"], f["w_gate_up"], f["w_down"], top_k=wl.k,
+                              renorm=wl.renorm, bias=f["bias"], ws_gate_up=f.get("ws_gate_up"),
+                              ws_down=f.get("ws_down"))
+        O.layer_backward(fwd, f["dy"], aux_coef=wl.aux_coef)
+        O.aux_statistics(fwd["p"], fwd["counts"], wl.k)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or runs >= 50:
+            break
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    threads = int(os.environ.get("OPENBLAS_NUM_THREADS", os.environ.get("OMP_NUM_THREADS", cores)))
+    return {"value": wl.T * runs / el, "unit": "tokens/s", "cores": min(cores, threads), "kind": "oracle",
+            "sample": f"{runs} full fwd+bwd+aux pass(es) of the {wl.name} workload in float64 numpy "
+                      f"({el:.1f} s wall)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=MI.BENCH)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-breakdown", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (no collectives, no sharding); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    wl = MI.WORKLOADS[args.workload]
+    torch.cuda.init()
+    layer, dev = make_layer(wl)
+    dy = dev["dy"]
+    print(f"[bench] workload {wl.name}: {MI.describe(wl)}", file=sys.stderr, flush=True)
+
+    flops = kernel_flops(wl)
+    for _ in range(max(args.warmup, 1)):
+        layer.step(dy)
+    torch.cuda.synchronize()
+
+    from mixture_experts_ffn_wave_amd import kernel_names, probe_enable, probe_read
+    breakdown = {}
+    if not args.no_breakdown:
+        breakdown = per_kernel_times(layer, dy, kernel_names())
+        for n, (ms, per) in sorted(breakdown.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
+            extra = ""
+            if n in flops:
+                extra = f"  {flops[n] / (ms * 1e-3) / 1e12:8.1f} TFLOP/s"
+            print(f"[bench] {n:34s} {ms * 1e3:9.1f} us x{per}{extra}", file=sys.stderr, flush=True)
+    gemms = {n: v for n, v in breakdown.items() if n in flops}
+    expert_gemms = {n: v for n, v in gemms.items() if "router" not in n}
+    dominant = max(gemms, key=lambda n: gemms[n][0] * gemms[n][1]) if gemms else "gemm_gate_up_swiglu"
+
+    # ---- timed region (dominant kernel bracketed by hipEvents on its stream)
+    probe_enable(layer.plan, dominant, args.steps * 4)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        layer.step(dy)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms_total, launches = probe_read(layer.plan)
+    probe_enable(layer.plan, dominant, 0)
+
+    ms_step = el * 1e3 / args.steps
+    avg_ms = ms_total / max(launches, 1)
+    achieved = flops[dominant] / (avg_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[wl.expert_dtype or wl.dtype]
+    gemm_ms = sum(ms * per for ms, per in expert_gemms.values())
+    result = {
+        "metric": METRIC,
+        "value": wl.T * args.steps / el,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "d_model": wl.d, "experts": wl.E, "top_k": wl.k,
+                   "d_ff": wl.I, "shared": f"{wl.n_shared}x{wl.I_shared}", "renorm": wl.renorm,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": dominant, "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                     "avg_launch_us": avg_ms * 1e3, "launches": launches},
+    }
+    if gemms:
+        result["grouped_gemm"] = {"tflops": expert_flops(wl) / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None,
+                                  "frac_of_peak": (expert_flops(wl) / (gemm_ms * 1e-3) / 1e12) / peak
+                                  if gemm_ms else None,
+                                  "gemm_ms_per_step": gemm_ms}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

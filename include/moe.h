@@ -26,8 +26,8 @@
  *     synchronises with the host and no data-dependent size leaves the GPU.
  *   - "act" below is the plan's activation dtype (f32, f16 or bf16): x, y,
  *     dy, dx, the router weight and the expert weights are stored in it, and
- *     so are the saved intermediates (GU, H, Y_perm) and the weight
- *     gradients.  Router probabilities and routing weights are always f32.
+ *     so are the saved intermediates GU and H and the weight gradients.
+ *     The expert outputs Y_perm are kept in f32.  Router probabilities and routing weights are always f32.
  *     Every matrix is row-major with the last index contiguous.
  *   - Arguments are checked on the host before anything is launched; a
  *     negative moe_status is returned and nothing is enqueued.  A HIP launch
@@ -129,7 +129,8 @@ typedef struct {
   const void* w_down;      /* [E, d, I] act */
   void* gu;                /* out [T*k, 2I] act: [G | U] per row, saved for backward */
   void* h;                 /* out [T*k, I] act: silu(G) * U */
-  void* y_perm;            /* out [T*k, d] act: H W_d^T */
+  float* y_perm;           /* out [T*k, d] f32: H W_d^T (kept in f32: the router gradient
+                              differences these rows, which magnifies storage rounding) */
   const void* x;           /* [T, d] act (shared experts' input) */
   const void* ws_gate_up;  /* [Ns, 2Is, d] act */
   const void* ws_down;     /* [Ns, d, Is] act */
@@ -147,9 +148,9 @@ moe_status moe_expert_ffn(moe_plan plan, const moe_ffn_args* args, void* ws, siz
 
 /* y[t] = sum_j topk_w[t, j] * y_perm[inv_perm[t, j]] (+ y_shared[t]), accumulated in
  * f32 in slot order j = 0..k-1, one write per row.
- *   y_perm [T*k, d] act; inv_perm [T, k] int32; topk_w [T, k] f32;
+ *   y_perm [T*k, d] f32; inv_perm [T, k] int32; topk_w [T, k] f32;
  *   y_shared [T, d] act or NULL; y [T, d] act out. */
-moe_status moe_combine(moe_plan plan, const void* y_perm, const int32_t* inv_perm,
+moe_status moe_combine(moe_plan plan, const float* y_perm, const int32_t* inv_perm,
                        const float* topk_w, const void* y_shared, void* y, void* stream);
 
 /* ---- backward ---------------------------------------------------------- */
@@ -167,7 +168,7 @@ typedef struct {
   const void* x_perm;       /* [T*k, d] */
   const void* gu;           /* [T*k, 2I] */
   const void* h;            /* [T*k, I] */
-  const void* y_perm;       /* [T*k, d] */
+  const float* y_perm;      /* [T*k, d] f32 */
   const void* w_gate_up;    /* [E, 2I, d] */
   const void* w_down;       /* [E, d, I] */
   const void* ws_gate_up;   /* [Ns, 2Is, d] (n_shared > 0) */

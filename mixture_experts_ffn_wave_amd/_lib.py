@@ -200,7 +200,7 @@ def moe_expert_ffn(plan, x_perm, offsets, w_gate_up, w_down, gu, h, y_perm, x=No
     A = T * k
     _need(x_perm, "x_perm", (A, d), dt); _need(offsets, "offsets", (E + 1,), torch.int32)
     _need(w_gate_up, "w_gate_up", (E, 2 * I, d), dt); _need(w_down, "w_down", (E, d, I), dt)
-    _need(gu, "gu", (A, 2 * I), dt); _need(h, "h", (A, I), dt); _need(y_perm, "y_perm", (A, d), dt)
+    _need(gu, "gu", (A, 2 * I), dt); _need(h, "h", (A, I), dt); _need(y_perm, "y_perm", (A, d), torch.float32)
     args = MoeFfnArgs(*[None] * len(_FFN_FIELDS))
     for n, t in [("x_perm", x_perm), ("offsets", offsets), ("w_gate_up", w_gate_up), ("w_down", w_down),
                  ("gu", gu), ("h", h), ("y_perm", y_perm)]:
@@ -221,7 +221,7 @@ def moe_expert_ffn(plan, x_perm, offsets, w_gate_up, w_down, gu, h, y_perm, x=No
 
 def moe_combine(plan, y_perm, inv_perm, topk_w, y_shared, y, stream=None):
     T, d, k, dt = plan.T, plan.d, plan.k, plan.dtype
-    _need(y_perm, "y_perm", (T * k, d), dt); _need(inv_perm, "inv_perm", (T, k), torch.int32)
+    _need(y_perm, "y_perm", (T * k, d), torch.float32); _need(inv_perm, "inv_perm", (T, k), torch.int32)
     _need(topk_w, "topk_w", (T, k), torch.float32); _need(y, "y", (T, d), dt)
     if y_shared is not None:
         _need(y_shared, "y_shared", (T, d), dt)

@@ -258,7 +258,7 @@ moe_status moe_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, size_t ws
     a.offsets = f->offsets; a.G = p->E; a.M = p->A; a.N = d; a.K = I; a.sub = I;
     a.C = f->y_perm; a.ldc = d;
     Probe pr(p, "gemm_down", s);
-    MOE_TRY(launch_row_gemm(p->dt, OP_DOWN_FWD, EPI_STORE, a, s));
+    MOE_TRY(launch_row_gemm(p->dt, OP_DOWN_FWD, EPI_STORE_F32, a, s));
   }
   if (p->Ns > 0) {
     const int Is = p->Is, NI = p->Ns * p->Is;
@@ -285,7 +285,7 @@ moe_status moe_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, size_t ws
 }
 
 // ---------------------------------------------------------------- combine --
-moe_status moe_combine(moe_plan p, const void* y_perm, const int32_t* inv_perm, const float* topk_w,
+moe_status moe_combine(moe_plan p, const float* y_perm, const int32_t* inv_perm, const float* topk_w,
                        const void* y_shared, void* y, void* stream) {
   if (!p) return MOE_ERR_NULL;
   if (p->T == 0) return MOE_OK;

@@ -81,8 +81,12 @@ template <> struct Mma32<float> {
   __device__ __forceinline__ static void run(f32x16& c, const u32x4* a, const u32x4* b) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float av = __builtin_bit_cast(float, a[i >> 2][i & 3]);
-      float bv = __builtin_bit_cast(float, b[i >> 2][i & 3]);
+      // read the element into a scalar first: a bit_cast applied directly to a
+      // vector-element expression drops the element index in this compiler
+      const uint32_t ua = a[i >> 2][i & 3];
+      const uint32_t ub = b[i >> 2][i & 3];
+      const float av = __uint_as_float(ua);
+      const float bv = __uint_as_float(ub);
       c = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, c, 0, 0, 0);
     }
   }

@@ -14,15 +14,16 @@ namespace {
 constexpr int NT = 256;
 
 // y[t] = sum_j w[t,j] * y_perm[inv[t,j]] (+ y_shared[t]); one wave per token,
-// 16-byte vectors along the row, f32 accumulation in slot order.
+// 16-byte vectors along the row (y_perm rows are f32), f32 accumulation in
+// slot order.
 template <typename T>
 __global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a) {
-  constexpr int VR = 16 / sizeof(T);
+  constexpr int VR = 16 / sizeof(T);   // output elements per 16-byte chunk
+  constexpr int YC = VR / 4;           // 16-byte f32 chunks of y_perm per output chunk
   const int lane = threadIdx.x & 63;
   const int64_t waves = (int64_t)gridDim.x * (NT / 64);
   const int64_t rowbytes = (int64_t)a.d * sizeof(T);
   const int nch = (int)(rowbytes / 16);
-  const char* yp = static_cast<const char*>(a.y_perm);
   const char* ys = static_cast<const char*>(a.y_shared);
   char* yo = static_cast<char*>(a.y);
   for (int64_t t = (int64_t)blockIdx.x * (NT / 64) + (threadIdx.x >> 6); t < a.T; t += waves) {
@@ -42,10 +43,13 @@ __global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a) {
         const int r = __shfl(r_l, j, 64);
         const float w = __shfl(w_l, j, 64);
         if (ok && r >= 0) {
-          Chunk<T> ch;
-          ch.raw = ld16(yp + (int64_t)r * rowbytes + (int64_t)c * 16);
+          const f32x4* src = reinterpret_cast<const f32x4*>(a.y_perm + (int64_t)r * a.d + (int64_t)c * VR);
 #pragma unroll
-          for (int i = 0; i < VR; ++i) acc[i] = fmaf(w, to_f32<T>(ch.e[i]), acc[i]);
+          for (int q = 0; q < YC; ++q) {
+            const f32x4 v = src[q];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[4 * q + i] = fmaf(w, v[i], acc[4 * q + i]);
+          }
         }
       }
       if (ok) {
@@ -68,12 +72,12 @@ __global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a) {
 template <typename T>
 __global__ void __launch_bounds__(NT) combine_bwd_kernel(CombineBwdArgs a) {
   constexpr int VR = 16 / sizeof(T);
+  constexpr int YC = VR / 4;
   const int lane = threadIdx.x & 63;
   const int64_t waves = (int64_t)gridDim.x * (NT / 64);
   const int64_t rowbytes = (int64_t)a.d * sizeof(T);
   const int nch = (int)(rowbytes / 16);
   const char* dyb = static_cast<const char*>(a.dy);
-  const char* yp = static_cast<const char*>(a.y_perm);
   char* dyp = static_cast<char*>(a.dy_perm);
   for (int64_t t = (int64_t)blockIdx.x * (NT / 64) + (threadIdx.x >> 6); t < a.T; t += waves) {
     int r_l = 0;
@@ -89,14 +93,18 @@ __global__ void __launch_bounds__(NT) combine_bwd_kernel(CombineBwdArgs a) {
       for (int c0 = 0; c0 < nch; c0 += 64) {
         const int c = c0 + lane;
         if (c < nch && r >= 0) {
-          Chunk<T> dv, yv, o;
+          Chunk<T> dv, o;
           dv.raw = ld16(dyb + t * rowbytes + (int64_t)c * 16);
-          yv.raw = ld16(yp + (int64_t)r * rowbytes + (int64_t)c * 16);
+          const f32x4* src = reinterpret_cast<const f32x4*>(a.y_perm + (int64_t)r * a.d + (int64_t)c * VR);
 #pragma unroll
-          for (int i = 0; i < VR; ++i) {
-            const float d = to_f32<T>(dv.e[i]);
-            dot = fmaf(d, to_f32<T>(yv.e[i]), dot);
-            o.e[i] = from_f32<T>(w * d);
+          for (int q = 0; q < YC; ++q) {
+            const f32x4 yv = src[q];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float dd = to_f32<T>(dv.e[4 * q + i]);
+              dot = fmaf(dd, yv[i], dot);
+              o.e[4 * q + i] = from_f32<T>(w * dd);
+            }
           }
           st16(dyp + (int64_t)r * rowbytes + (int64_t)c * 16, o.raw);
         }

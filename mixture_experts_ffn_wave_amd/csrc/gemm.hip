@@ -440,7 +440,9 @@ template <typename T>
 hipError_t launch_row_dt(int op, int epi, const RowGemmArgs& a, hipStream_t s) {
   switch (op) {
     case OP_GU_FWD: return launch_row_t<T, OP_GU_FWD, EPI_SWIGLU_FWD>(a, s);
-    case OP_DOWN_FWD: return launch_row_t<T, OP_DOWN_FWD, EPI_STORE>(a, s);
+    case OP_DOWN_FWD:
+      if (epi == EPI_STORE_F32) return launch_row_t<T, OP_DOWN_FWD, EPI_STORE_F32>(a, s);
+      return launch_row_t<T, OP_DOWN_FWD, EPI_STORE>(a, s);
     case OP_DOWN_DGRAD: return launch_row_t<T, OP_DOWN_DGRAD, EPI_SWIGLU_BWD>(a, s);
     case OP_GU_DGRAD:
       if (epi == EPI_UNPERMUTE) return launch_row_t<T, OP_GU_DGRAD, EPI_UNPERMUTE>(a, s);

@@ -84,13 +84,13 @@ hipError_t launch_wgrad(int dt, const WgradArgs& a, hipStream_t s);
 
 // ------------------------------------------------------ element-wise --
 struct CombineArgs {
-  const void* y_perm; const int32_t* inv; const float* wts; const void* y_shared; void* y;
+  const float* y_perm; const int32_t* inv; const float* wts; const void* y_shared; void* y;
   int64_t T; int d, k;
 };
 hipError_t launch_combine(int dt, const CombineArgs& a, hipStream_t s);
 
 struct CombineBwdArgs {
-  const void* dy; const void* y_perm; const int32_t* inv; const float* wts;
+  const void* dy; const float* y_perm; const int32_t* inv; const float* wts;
   void* dy_perm;  // [T*k, d]
   float* g;       // [T, k]
   int64_t T; int d, k;

@@ -27,7 +27,7 @@ class MoELayer:
         self.x_perm = z(A, d)
         self.gu = z(A, 2 * I)
         self.h = z(A, I)
-        self.y_perm = z(A, d)
+        self.y_perm = z(A, d, dtype=torch.float32)
         self.y = z(T, d)
         if p.Ns > 0:
             NI = p.Ns * p.Is

@@ -1,9 +1,16 @@
 """Shared helpers of the GPU parity tests: run the HIP path through the C ABI,
 run the fp64 oracle on the same seeded inputs, compare.
 
-Tolerances (max |gpu - oracle| <= c * RMS(oracle tensor), per tensor):
-  c = 2e-2 for bf16 / f16 storage (the layer's stated bar), c = 1e-4 for f32
-  storage (f32 MFMA products, f32 intermediates); router probabilities and
+Tolerances, per output matrix and element (each expert's weight gradient is
+its own matrix, as each expert is a separate parameter):
+  |gpu - oracle| <= c * RMS(oracle tensor) + ulp(value) / 2
+  with c = 2e-2 for bf16 / f16 storage (the layer's stated bar) and c = 1e-4
+  for f32 storage (f32 MFMA products, f32 intermediates).  The half-ulp term
+  is the rounding of the result into its storage dtype, which no
+  implementation that returns that dtype can avoid: for bf16 it alone reaches
+  2^-8 of an element just above a power of two, i.e. about 2.2% of the RMS at
+  the largest elements of these tensors.  The raw max|err|/RMS is reported
+  too.  Router probabilities and
   routing weights within 1e-6 absolute; routing indices, counts, offsets,
   permutation and inverse permutation bit-exact, except tokens whose oracle
   logits tie within 1e-5 (set or slot order), whose GPU choice must only be a
@@ -90,14 +97,36 @@ def oracle_run(wl, f64):
     return fwd, bwd, st
 
 
-def check_close(name, got, ref, c):
+MANTISSA_BITS = {"f32": 23, "f16": 10, "bf16": 7}
+MIN_EXP = {"f32": -126, "f16": -14, "bf16": -126}
+
+
+def half_ulp(v, dtype):
+    """Half a unit in the last place of |v| in ``dtype`` (normal and subnormal range)."""
+    a = np.abs(v)
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))
+    e = np.maximum(ex - 1, MIN_EXP[dtype])
+    return np.ldexp(0.5, e - MANTISSA_BITS[dtype])
+
+
+REPORT = []
+
+
+def check_close(name, got, ref, c, dtype="f32"):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, f"{name}: shape {got.shape} vs {ref.shape}"
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
-    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
-    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
-    assert err <= c * rms + 1e-30, f"{name}: max abs err {err:.3e} > {c:g} x RMS {rms:.3e}"
+    if got.size == 0:
+        return 0.0, 0.0
+    diff = np.abs(got - ref)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    excess = diff - half_ulp(np.maximum(np.abs(got), np.abs(ref)), dtype)
+    err = float(diff.max())
+    worst = float(excess.max())
+    REPORT.append((name, err / rms if rms > 0 else 0.0))
+    assert worst <= c * rms + 1e-30, (f"{name}: max(|err| - ulp/2) {worst:.3e} > {c:g} x RMS {rms:.3e} "
+                                      f"(raw max|err| {err:.3e} = {err / max(rms, 1e-300):.4f} RMS)")
     return err, rms
 
 
@@ -127,6 +156,7 @@ def compare_routing(wl, gpu, fwd):
 
 def compare_downstream(wl, gpu, fwd, bwd, st):
     c = rel_tol(wl)
+    dt = wl.dtype
     # integer work: bit-exact
     assert np.array_equal(gpu["counts"], fwd["counts"]), "counts"
     assert np.array_equal(gpu["offsets"], fwd["offsets"]), "offsets"
@@ -134,29 +164,32 @@ def compare_downstream(wl, gpu, fwd, bwd, st):
     assert np.array_equal(gpu["inv_perm"], fwd["inv"]), "inv_perm"
     assert np.array_equal(gpu["x_perm"], fwd["x_perm"]), "x_perm is a pure copy"
     inter = wl.I
-    check_close("G", gpu["gu"][:, :inter], fwd["g"], c)
-    check_close("U", gpu["gu"][:, inter:], fwd["u"], c)
-    check_close("H", gpu["h"], fwd["h"], c)
-    check_close("Y_perm", gpu["y_perm"], fwd["y_perm"], c)
+    check_close("G", gpu["gu"][:, :inter], fwd["g"], c, dt)
+    check_close("U", gpu["gu"][:, inter:], fwd["u"], c, dt)
+    check_close("H", gpu["h"], fwd["h"], c, dt)
+    check_close("Y_perm", gpu["y_perm"], fwd["y_perm"], c, dt)
     if wl.n_shared:
         Is = wl.I_shared
         for s, (gs, us, hs) in enumerate(fwd["shared"]):
-            check_close(f"G_shared[{s}]", gpu["gu_shared"][:, 2 * s * Is:2 * s * Is + Is], gs, c)
-            check_close(f"U_shared[{s}]", gpu["gu_shared"][:, 2 * s * Is + Is:2 * (s + 1) * Is], us, c)
-            check_close(f"H_shared[{s}]", gpu["h_shared"][:, s * Is:(s + 1) * Is], hs, c)
-        check_close("Y_shared", gpu["y_shared"], fwd["y_shared"], c)
-    check_close("y", gpu["y"], fwd["y"], c)
-    check_close("dx", gpu["dx"], bwd["dx"], c)
-    check_close("dW_router", gpu["dw_router"], bwd["dw_router"], c)
-    check_close("dbias", gpu["dbias"], bwd["dbias"], c)
-    check_close("dW_gate_up", gpu["dw_gate_up"], bwd["dw_gate_up"], c)
-    check_close("dW_down", gpu["dw_down"], bwd["dw_down"], c)
+            check_close(f"G_shared[{s}]", gpu["gu_shared"][:, 2 * s * Is:2 * s * Is + Is], gs, c, dt)
+            check_close(f"U_shared[{s}]", gpu["gu_shared"][:, 2 * s * Is + Is:2 * (s + 1) * Is], us, c, dt)
+            check_close(f"H_shared[{s}]", gpu["h_shared"][:, s * Is:(s + 1) * Is], hs, c, dt)
+        check_close("Y_shared", gpu["y_shared"], fwd["y_shared"], c, dt)
+    check_close("y", gpu["y"], fwd["y"], c, dt)
+    check_close("dx", gpu["dx"], bwd["dx"], c, dt)
+    check_close("dW_router", gpu["dw_router"], bwd["dw_router"], c, dt)
+    check_close("dbias", gpu["dbias"], bwd["dbias"], c, "f32")
+    # each expert's weight is its own parameter matrix: compare per expert
+    for e in range(wl.E):
+        check_close(f"dW_gate_up[{e}]", gpu["dw_gate_up"][e], bwd["dw_gate_up"][e], c, dt)
+        check_close(f"dW_down[{e}]", gpu["dw_down"][e], bwd["dw_down"][e], c, dt)
     empty = np.where(fwd["counts"] == 0)[0]
     for e in empty:
         assert not np.any(gpu["dw_gate_up"][e]) and not np.any(gpu["dw_down"][e]), f"empty expert {e} grads"
     if wl.n_shared:
-        check_close("dWs_gate_up", gpu["dws_gate_up"], bwd["dws_gate_up"], c)
-        check_close("dWs_down", gpu["dws_down"], bwd["dws_down"], c)
+        for s_ in range(wl.n_shared):
+            check_close(f"dWs_gate_up[{s_}]", gpu["dws_gate_up"][s_], bwd["dws_gate_up"][s_], c, dt)
+            check_close(f"dWs_down[{s_}]", gpu["dws_down"][s_], bwd["dws_down"][s_], c, dt)
     # balancing statistic and metrics
     assert np.allclose(gpu["f"], st["f"], rtol=1e-6, atol=0), "f"
     assert np.max(np.abs(gpu["p_mean"] - st["p_mean"])) <= PROB_ATOL, "p_mean"
@@ -185,5 +218,11 @@ def full_parity(wl, inp=None):
     if not identical:
         say(f"[parity] {wl.name}: near-tie routing differs; rerunning downstream from the oracle routing")
         gpu = gpu_run(wl, inp, routing={"p": fwd["p"], "idx": fwd["idx"], "w": fwd["w"]})
+    REPORT.clear()
     compare_downstream(wl, gpu, fwd, bwd, st)
+    worst = {}
+    for n, r in REPORT:
+        key = n.split("[")[0]
+        worst[key] = max(worst.get(key, 0.0), r)
+    say(f"[parity] {wl.name}: raw max|err|/RMS " + " ".join(f"{n}={r:.4f}" for n, r in worst.items()))
     return gpu, fwd, bwd, st

@@ -13,17 +13,24 @@ pytestmark = pytest.mark.gpu
 
 W = MI.Workload
 
+# Sparse-expert cases (few tokens per expert) run in f16: their weight
+# gradients are sums of a handful of rank-1 terms, so one bf16 rounding of a
+# GEMM operand alone exceeds 2e-2 x RMS there (see the precision notes in the
+# design document); f16 exercises the same kernels with 3 more mantissa bits.
 SMALL = [
     W("t300_d128_e4k2_i128_f32", T=300, d=128, E=4, k=2, I=128, dtype="f32"),
     W("t300_d128_e4k2_i128_bf16", T=300, d=128, E=4, k=2, I=128, dtype="bf16"),
     W("t300_d128_e4k2_i128_f16_norenorm", T=300, d=128, E=4, k=2, I=128, dtype="f16", renorm=False),
-    W("t257_d256_e2k2_i128_bf16_shared1", T=257, d=256, E=2, k=2, I=128, n_shared=1, I_shared=256),
-    W("t1000_d256_e64k6_i128_bf16_shared2", T=1000, d=256, E=64, k=6, I=128, n_shared=2, I_shared=128),
-    W("t777_d128_e128k8_i128_zipf_bf16", T=777, d=128, E=128, k=8, I=128, zipf_s=1.1),
+    # k = E: the router gradient is a difference of expert outputs (cancellation), run in f16
+    W("t257_d256_e2k2_i128_f16_shared1", T=257, d=256, E=2, k=2, I=128, n_shared=1, I_shared=256, dtype="f16"),
+    W("t4096_d256_e8k2_i256_bf16_shared1", T=4096, d=256, E=8, k=2, I=256, n_shared=1, I_shared=256),
+    W("t1000_d256_e64k6_i128_f16_shared2", T=1000, d=256, E=64, k=6, I=128, n_shared=2, I_shared=128,
+      dtype="f16"),
+    W("t777_d128_e128k8_i128_zipf_f16", T=777, d=128, E=128, k=8, I=128, zipf_s=1.1, dtype="f16"),
     W("t64_d128_e1k1_i256_bf16", T=64, d=128, E=1, k=1, I=256),
     W("t2100_d384_e8k1_i256_f16_noaux", T=2100, d=384, E=8, k=1, I=256, dtype="f16", aux_coef=0.0),
     W("t513_d256_e16k4_i384_f32_shared1", T=513, d=256, E=16, k=4, I=384, n_shared=1, I_shared=128, dtype="f32"),
-    W("t1500_d256_e200k3_i128_bf16", T=1500, d=256, E=200, k=3, I=128),
+    W("t1500_d256_e200k3_i128_f16", T=1500, d=256, E=200, k=3, I=128, dtype="f16"),
 ]
 
 
@@ -48,7 +55,7 @@ def test_forced_empty_experts_write_zero_gradients():
 
 
 def test_zero_router_ties_break_to_lower_index():
-    wl = W("t256_d128_e8k3_i128_bf16_zero_router", T=256, d=128, E=8, k=3, I=128)
+    wl = W("t256_d128_e8k3_i128_f16_zero_router", T=256, d=128, E=8, k=3, I=128, dtype="f16")
     inp = MI.make_inputs(wl)
     inp["w_router"] = torch.zeros_like(inp["w_router"])
     gpu, fwd, _, st = PT.full_parity(wl, inp)
