@@ -26,7 +26,7 @@ const char* kKernelNames =
     "gemm_gate_up_swiglu_shared,gemm_down_shared,combine,combine_bwd,router_dz,"
     "gemm_down_dgrad_swiglu,gemm_wgrad_down,gemm_gate_up_dgrad,gemm_wgrad_gate_up,"
     "gemm_down_dgrad_swiglu_shared,gemm_wgrad_down_shared,gemm_wgrad_gate_up_shared,"
-    "gemm_gate_up_dgrad_shared,stack_router,gemm_router_dx,gemm_wgrad_router,router_reduce,aux";
+    "gemm_gate_up_dgrad_shared,stack_router,gemm_router_dx,unpermute,gemm_wgrad_router,router_reduce,aux";
 
 }  // namespace
 
@@ -36,9 +36,13 @@ struct moe_plan_s {
   int64_t T, A;
   int d, E, k, I, Ns, Is, Ep;
   int nblk_hist, nblk_dz, nblk_aux, router_splits;
+  // GEMM tile per call site, chosen once at plan time
+  int t_gu, t_down, t_gu_s, t_down_s, t_down_dgrad, t_gu_dgrad, t_down_dgrad_s, t_gu_dgrad_s, t_router_dx;
+  int t_wg_down, t_wg_gu, t_wg_down_s, t_wg_gu_s, t_wg_router;
   // workspace regions (byte offsets)
   size_t o_block_counts, o_block_base, o_dy_perm, o_g, o_dzhl, o_w2, o_dgu, o_dx_perm, o_dgu_s,
-      o_dxr, o_dwr_part, o_dbias_part, o_aux_part, ws_total;
+      o_dxs, o_dxr, o_dwr_part, o_dbias_part, o_aux_part, ws_total;
+  bool router_dx_gemm;     // many experts: the router part of dx goes through the matrix cores
   // timing probe
   std::string probe_name;
   std::vector<hipEvent_t> ev0, ev1;
@@ -90,6 +94,33 @@ moe_status check_ws(moe_plan p, void* ws, size_t ws_bytes) {
   return MOE_OK;
 }
 
+// Tile choice for one GEMM: 256 x 256 stages twice the FLOP per operand byte
+// of 128 x 128 but needs four times the rows per workgroup.  Estimated time =
+// rounds of workgroups over the CUs x the time of one tile, with the smaller
+// tile costed at the operand-bandwidth limit (about 0.55 of the larger one's
+// rate).  `rows_per_seg` assumes balanced segments (sizes are device-side).
+constexpr int kCUs = 256;
+double tile_cost(int tile, double segs, double rows_per_seg, int ncols, int ktot) {
+  const double mt = segs * ((rows_per_seg + tile - 1) / tile);
+  const double wgs = mt * (ncols / tile);
+  const double rounds = (wgs + kCUs - 1) / kCUs;
+  const double per_tile = (double)tile * tile * ktot / (tile == 256 ? 1.0 : 0.55);
+  return (rounds < 1 ? 1 : rounds) * per_tile;
+}
+int choose_row_tile(int dt, double segs, double rows_per_seg, int ncols, int ktot, int block_align) {
+  if (dt == DT_F32) return 128;
+  if (ncols % 256 || block_align % 256) return 128;
+  return tile_cost(256, segs, rows_per_seg, ncols, ktot) <= tile_cost(128, segs, rows_per_seg, ncols, ktot) ? 256 : 128;
+}
+int choose_wgrad_tile(int dt, double segs, int M, int N, double ktok) {
+  if (dt == DT_F32) return 128;
+  if (M % 256 || N % 256) return 128;
+  const double w256 = segs * (M / 256) * (N / 256), w128 = segs * (M / 128) * (N / 128);
+  const double c256 = ((w256 + kCUs - 1) / kCUs) * 256.0 * 256.0 * ktok;
+  const double c128 = ((w128 + kCUs - 1) / kCUs) * 128.0 * 128.0 * ktok / 0.55;
+  return c256 <= c128 ? 256 : 128;
+}
+
 }  // namespace
 
 extern "C" {
@@ -132,6 +163,7 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
   if (c.n_shared > 0 && c.d_ff_shared % 128) return MOE_ERR_UNSUPPORTED;
   const int64_t A = c.T * c.top_k;
   if (A >= ((int64_t)1 << 31)) return MOE_ERR_INVALID;
+  const int64_t A_ = A;
 
   moe_plan p = new (std::nothrow) moe_plan_s();
   if (!p) return MOE_ERR_INVALID;
@@ -150,14 +182,40 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
   p->nblk_dz = router_dz_blocks(c.T);
   p->nblk_aux = aux_blocks(c.T);
   {
-    // split the router weight-gradient contraction over tokens so the grid fills the GPU
+    // split the router weight-gradient contraction over tokens so that about
+    // 512 workgroups run, each with at least 256 tokens
     const int tiles = (2 * p->Ep / 128) * (p->d / 128);
-    int s = (int)(c.T / 2048);
-    if (s < 1) s = 1;
-    const int cap = 512 / tiles > 1 ? 512 / tiles : 1;
-    if (s > cap) s = cap;
+    int s = (512 + tiles - 1) / tiles;
+    const int by_tokens = (int)(c.T / 256);
+    if (s > by_tokens) s = by_tokens;
     if (s > 64) s = 64;
+    if (s < 1) s = 1;
     p->router_splits = s;
+  }
+  p->router_dx_gemm = p->E > kRouterDxVectorMaxE;
+  {
+    const double E = p->E, A = (double)A_, T = (double)c.T;
+    const double rps = E > 0 ? A / E : 0;               // rows per expert if balanced
+    const int d = p->d, I = p->I, NI = p->Ns * p->Is;
+    // gate/up: output columns are 2I packed, tile columns pair gate/up halves (needs I % (tile/2))
+    p->t_gu = choose_row_tile(p->dt, E, rps, 2 * I, d, 2 * I);
+    p->t_down = choose_row_tile(p->dt, E, rps, d, I, 256);
+    p->t_down_dgrad = choose_row_tile(p->dt, E, rps, I, d, I);
+    p->t_gu_dgrad = choose_row_tile(p->dt, E, rps, d, 2 * I, 256);
+    p->t_router_dx = 128;                                 // K = 2 Ep is tiny
+    p->t_wg_down = choose_wgrad_tile(p->dt, E, d, I, rps);
+    p->t_wg_gu = choose_wgrad_tile(p->dt, E, 2 * I, d, rps);
+    p->t_wg_router = 128;
+    if (p->Ns > 0) {
+      p->t_gu_s = choose_row_tile(p->dt, 1, T, 2 * NI, d, 2 * p->Is);
+      p->t_down_s = choose_row_tile(p->dt, 1, T, d, NI, 256);
+      p->t_down_dgrad_s = choose_row_tile(p->dt, 1, T, NI, d, p->Is);
+      p->t_gu_dgrad_s = choose_row_tile(p->dt, 1, T, d, 2 * NI, 256);
+      p->t_wg_down_s = (p->Is % 256 == 0) ? choose_wgrad_tile(p->dt, 1, d, NI, T) : 128;
+      p->t_wg_gu_s = choose_wgrad_tile(p->dt, 1, 2 * NI, d, T);
+    } else {
+      p->t_gu_s = p->t_down_s = p->t_down_dgrad_s = p->t_gu_dgrad_s = p->t_wg_down_s = p->t_wg_gu_s = 128;
+    }
   }
   const size_t es = dtype_bytes(p->dt);
   size_t off = 0;
@@ -171,11 +229,12 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
   p->o_dy_perm = take((size_t)A * p->d * es);
   p->o_g = take((size_t)A * 4);
   p->o_dzhl = take((size_t)p->T * 2 * p->Ep * es);
-  p->o_w2 = take((size_t)2 * p->Ep * p->d * es);
+  p->o_w2 = take(p->router_dx_gemm ? (size_t)2 * p->Ep * p->d * es : 0);
   p->o_dgu = take((size_t)A * 2 * p->I * es);
   p->o_dx_perm = take((size_t)A * p->d * es);
   p->o_dgu_s = take((size_t)p->T * 2 * p->Ns * p->Is * es);
-  p->o_dxr = take(p->Ns > 0 ? (size_t)p->T * p->d * 4 : 0);
+  p->o_dxs = take(p->Ns > 0 ? (size_t)p->T * p->d * es : 0);
+  p->o_dxr = take(p->router_dx_gemm ? (size_t)p->T * p->d * 4 : 0);
   p->o_dwr_part = take((size_t)p->router_splits * 2 * p->Ep * p->d * 4);
   p->o_dbias_part = take((size_t)p->nblk_dz * p->E * 4);
   p->o_aux_part = take((size_t)(p->nblk_aux > 0 ? p->nblk_aux : 1) * 2 * p->E * 4);
@@ -249,7 +308,7 @@ moe_status moe_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, size_t ws
     a.offsets = f->offsets; a.G = p->E; a.M = p->A; a.N = I; a.K = d; a.sub = I;
     a.C = f->gu; a.ldc = 2 * I; a.C2 = f->h; a.ldc2 = I;
     Probe pr(p, "gemm_gate_up_swiglu", s);
-    MOE_TRY(launch_row_gemm(p->dt, OP_GU_FWD, EPI_SWIGLU_FWD, a, s));
+    MOE_TRY(launch_row_gemm(p->dt, OP_GU_FWD, EPI_SWIGLU_FWD, p->t_gu, a, s));
   }
   {
     RowGemmArgs a{};
@@ -258,7 +317,7 @@ moe_status moe_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, size_t ws
     a.offsets = f->offsets; a.G = p->E; a.M = p->A; a.N = d; a.K = I; a.sub = I;
     a.C = f->y_perm; a.ldc = d;
     Probe pr(p, "gemm_down", s);
-    MOE_TRY(launch_row_gemm(p->dt, OP_DOWN_FWD, EPI_STORE_F32, a, s));
+    MOE_TRY(launch_row_gemm(p->dt, OP_DOWN_FWD, EPI_STORE_F32, p->t_down, a, s));
   }
   if (p->Ns > 0) {
     const int Is = p->Is, NI = p->Ns * p->Is;
@@ -269,7 +328,7 @@ moe_status moe_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, size_t ws
       a.offsets = nullptr; a.G = 1; a.M = p->T; a.N = NI; a.K = d; a.sub = Is;
       a.C = f->gu_shared; a.ldc = 2 * NI; a.C2 = f->h_shared; a.ldc2 = NI;
       Probe pr(p, "gemm_gate_up_swiglu_shared", s);
-      MOE_TRY(launch_row_gemm(p->dt, OP_GU_FWD, EPI_SWIGLU_FWD, a, s));
+      MOE_TRY(launch_row_gemm(p->dt, OP_GU_FWD, EPI_SWIGLU_FWD, p->t_gu_s, a, s));
     }
     {
       RowGemmArgs a{};
@@ -278,7 +337,7 @@ moe_status moe_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, size_t ws
       a.offsets = nullptr; a.G = 1; a.M = p->T; a.N = d; a.K = NI; a.sub = Is;
       a.C = f->y_shared; a.ldc = d;
       Probe pr(p, "gemm_down_shared", s);
-      MOE_TRY(launch_row_gemm(p->dt, OP_DOWN_FWD, EPI_STORE, a, s));
+      MOE_TRY(launch_row_gemm(p->dt, OP_DOWN_FWD, EPI_STORE, p->t_down_s, a, s));
     }
   }
   return MOE_OK;
@@ -324,6 +383,7 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
   void* dgu = wsp(ws, p->o_dgu);
   void* dx_perm = wsp(ws, p->o_dx_perm);
   void* dgu_s = wsp(ws, p->o_dgu_s);
+  void* dxs = wsp(ws, p->o_dxs);
   float* dxr = reinterpret_cast<float*>(wsp(ws, p->o_dxr));
   float* dwr_part = reinterpret_cast<float*>(wsp(ws, p->o_dwr_part));
   float* dbias_part = reinterpret_cast<float*>(wsp(ws, p->o_dbias_part));
@@ -347,7 +407,7 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
       a.offsets = sv->offsets; a.G = E; a.M = p->A; a.N = I; a.K = d; a.sub = I;
       a.C = dgu; a.ldc = 2 * I; a.aux = sv->gu; a.ldaux = 2 * I;
       Probe pr(p, "gemm_down_dgrad_swiglu", s);
-      MOE_TRY(launch_row_gemm(p->dt, OP_DOWN_DGRAD, EPI_SWIGLU_BWD, a, s));
+      MOE_TRY(launch_row_gemm(p->dt, OP_DOWN_DGRAD, EPI_SWIGLU_BWD, p->t_down_dgrad, a, s));
     }
   }
   {
@@ -356,7 +416,7 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
     a.offsets = sv->offsets; a.G = E; a.Mtok = p->A; a.M = d; a.N = I; a.splits = 1;
     a.C = gr->dw_down; a.c_group_stride = (int64_t)d * I; a.c_split_stride = 0; a.sub = I; a.out_f32 = 0;
     Probe pr(p, "gemm_wgrad_down", s);
-    MOE_TRY(launch_wgrad(p->dt, a, s));
+    MOE_TRY(launch_wgrad(p->dt, p->t_wg_down, a, s));
   }
   if (p->T > 0) {
     RowGemmArgs a{};
@@ -365,7 +425,7 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
     a.offsets = sv->offsets; a.G = E; a.M = p->A; a.N = d; a.K = 2 * I; a.sub = I;
     a.C = dx_perm; a.ldc = d;
     Probe pr(p, "gemm_gate_up_dgrad", s);
-    MOE_TRY(launch_row_gemm(p->dt, OP_GU_DGRAD, EPI_STORE, a, s));
+    MOE_TRY(launch_row_gemm(p->dt, OP_GU_DGRAD, EPI_STORE, p->t_gu_dgrad, a, s));
   }
   {
     WgradArgs a{};
@@ -373,7 +433,7 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
     a.offsets = sv->offsets; a.G = E; a.Mtok = p->A; a.M = 2 * I; a.N = d; a.splits = 1;
     a.C = gr->dw_gate_up; a.c_group_stride = (int64_t)2 * I * d; a.c_split_stride = 0; a.sub = d; a.out_f32 = 0;
     Probe pr(p, "gemm_wgrad_gate_up", s);
-    MOE_TRY(launch_wgrad(p->dt, a, s));
+    MOE_TRY(launch_wgrad(p->dt, p->t_wg_gu, a, s));
   }
   if (p->Ns > 0) {
     const int Is = p->Is, NI = p->Ns * p->Is;
@@ -384,7 +444,7 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
       a.offsets = nullptr; a.G = 1; a.M = p->T; a.N = NI; a.K = d; a.sub = Is;
       a.C = dgu_s; a.ldc = 2 * NI; a.aux = sv->gu_shared; a.ldaux = 2 * NI;
       Probe pr(p, "gemm_down_dgrad_swiglu_shared", s);
-      MOE_TRY(launch_row_gemm(p->dt, OP_DOWN_DGRAD, EPI_SWIGLU_BWD, a, s));
+      MOE_TRY(launch_row_gemm(p->dt, OP_DOWN_DGRAD, EPI_SWIGLU_BWD, p->t_down_dgrad_s, a, s));
     }
     {
       WgradArgs a{};
@@ -392,7 +452,7 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
       a.offsets = nullptr; a.G = 1; a.Mtok = p->T; a.M = d; a.N = NI; a.splits = 1;
       a.C = gr->dws_down; a.c_group_stride = 0; a.c_split_stride = 0; a.sub = Is; a.out_f32 = 0;
       Probe pr(p, "gemm_wgrad_down_shared", s);
-      MOE_TRY(launch_wgrad(p->dt, a, s));
+      MOE_TRY(launch_wgrad(p->dt, p->t_wg_down_s, a, s));
     }
     {
       WgradArgs a{};
@@ -400,40 +460,38 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
       a.offsets = nullptr; a.G = 1; a.Mtok = p->T; a.M = 2 * NI; a.N = d; a.splits = 1;
       a.C = gr->dws_gate_up; a.c_group_stride = 0; a.c_split_stride = 0; a.sub = d; a.out_f32 = 0;
       Probe pr(p, "gemm_wgrad_gate_up_shared", s);
-      MOE_TRY(launch_wgrad(p->dt, a, s));
+      MOE_TRY(launch_wgrad(p->dt, p->t_wg_gu_s, a, s));
     }
   }
-  {
-    Stack2Args a{sv->w_router, w2, E, Ep, d};
-    Probe pr(p, "stack_router", s);
-    MOE_TRY(launch_stack2(p->dt, a, s));
+  if (p->Ns > 0 && p->T > 0) {
+    const int NI = p->Ns * p->Is;
+    RowGemmArgs b{};
+    b.P = dgu_s; b.ldp = 2 * NI;
+    b.Q = sv->ws_gate_up; b.ldq = d; b.q_group_stride = 0;
+    b.offsets = nullptr; b.G = 1; b.M = p->T; b.N = d; b.K = 2 * NI; b.sub = d;
+    b.C = dxs; b.ldc = d;
+    Probe pr(p, "gemm_gate_up_dgrad_shared", s);
+    MOE_TRY(launch_row_gemm(p->dt, OP_GU_DGRAD, EPI_STORE, p->t_gu_dgrad_s, b, s));
   }
-  if (p->T > 0) {
+  if (p->router_dx_gemm && p->T > 0) {
+    {
+      Stack2Args a{sv->w_router, w2, E, Ep, d};
+      Probe pr(p, "stack_router", s);
+      MOE_TRY(launch_stack2(p->dt, a, s));
+    }
     RowGemmArgs a{};
     a.P = dzhl; a.ldp = 2 * Ep;
     a.Q = w2; a.ldq = d; a.q_group_stride = 0;
     a.offsets = nullptr; a.G = 1; a.M = p->T; a.N = d; a.K = 2 * Ep; a.sub = d;
-    if (p->Ns > 0) {
-      a.C = dxr; a.ldc = d;
-      {
-        Probe pr(p, "gemm_router_dx", s);
-        MOE_TRY(launch_row_gemm(p->dt, OP_ROUTER_DX, EPI_STORE_F32, a, s));
-      }
-      const int NI = p->Ns * p->Is;
-      RowGemmArgs b{};
-      b.P = dgu_s; b.ldp = 2 * NI;
-      b.Q = sv->ws_gate_up; b.ldq = d; b.q_group_stride = 0;
-      b.offsets = nullptr; b.G = 1; b.M = p->T; b.N = d; b.K = 2 * NI; b.sub = d;
-      b.C = gr->dx; b.ldc = d; b.inv = sv->inv_perm; b.topk = k; b.gath = dx_perm; b.ldg = d;
-      b.aux = dxr; b.ldaux = d;
-      Probe pr(p, "gemm_gate_up_dgrad_shared", s);
-      MOE_TRY(launch_row_gemm(p->dt, OP_GU_DGRAD, EPI_UNPERMUTE, b, s));
-    } else {
-      a.C = gr->dx; a.ldc = d; a.inv = sv->inv_perm; a.topk = k; a.gath = dx_perm; a.ldg = d;
-      a.aux = nullptr;
-      Probe pr(p, "gemm_router_dx", s);
-      MOE_TRY(launch_row_gemm(p->dt, OP_ROUTER_DX, EPI_UNPERMUTE, a, s));
-    }
+    a.C = dxr; a.ldc = d;
+    Probe pr(p, "gemm_router_dx", s);
+    MOE_TRY(launch_row_gemm(p->dt, OP_ROUTER_DX, EPI_STORE_F32, p->t_router_dx, a, s));
+  }
+  if (p->T > 0) {
+    UnpermuteArgs a{dx_perm, sv->inv_perm, p->Ns > 0 ? dxs : nullptr, p->router_dx_gemm ? dxr : nullptr,
+                    dzhl, sv->w_router, gr->dx, p->T, d, k, E, Ep};
+    Probe pr(p, "unpermute", s);
+    MOE_TRY(launch_unpermute(p->dt, a, s));
   }
   {
     WgradArgs a{};
@@ -441,7 +499,7 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
     a.offsets = nullptr; a.G = 1; a.Mtok = p->T; a.M = 2 * Ep; a.N = d; a.splits = p->router_splits;
     a.C = dwr_part; a.c_group_stride = 0; a.c_split_stride = (int64_t)2 * Ep * d; a.sub = d; a.out_f32 = 1;
     Probe pr(p, "gemm_wgrad_router", s);
-    MOE_TRY(launch_wgrad(p->dt, a, s));
+    MOE_TRY(launch_wgrad(p->dt, p->t_wg_router, a, s));
   }
   {
     RouterReduceArgs a{dwr_part, p->router_splits, E, Ep, d, gr->dw_router,

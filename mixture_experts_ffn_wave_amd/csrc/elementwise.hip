@@ -196,13 +196,37 @@ __global__ void __launch_bounds__(NT) stack2_kernel(Stack2Args a) {
   }
 }
 
-// dW_r[e][n] = sum_s part[s][e][n] + sum_s part[s][Ep + e][n];  dbias = sum over blocks.
+// Sum of v over the workgroup in a fixed order (butterfly within waves, then
+// waves in index order); every thread gets the result.
+__device__ __forceinline__ float block_sum_f(float v, float* sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  float s = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) s += sh[w];
+  return s;
+}
+
+// Blocks [0, nbw): dW_r[e][n] = sum_s part[s][e][n] + sum_s part[s][Ep + e][n].
+// Blocks [nbw, nbw + E): dbias[e] = sum over router_dz blocks of their partial.
 template <typename T>
-__global__ void __launch_bounds__(NT) router_reduce_kernel(RouterReduceArgs a) {
+__global__ void __launch_bounds__(NT) router_reduce_kernel(RouterReduceArgs a, int nbw) {
+  __shared__ float sh[NT / 64];
+  if ((int)blockIdx.x >= nbw) {
+    const int e = blockIdx.x - nbw;
+    float v = 0.0f;
+    for (int b = threadIdx.x; b < a.nb; b += NT) v += a.dbias_part[(int64_t)b * a.E + e];
+    v = block_sum_f(v, sh);
+    if (threadIdx.x == 0) a.dbias[e] = v;
+    return;
+  }
   const int64_t n = (int64_t)a.E * a.d;
   const int64_t sstride = 2 * (int64_t)a.Ep * a.d;
   T* dw = static_cast<T*>(a.dw);
-  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) {
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)nbw * NT) {
     const int64_t e = i / a.d, col = i - e * a.d;
     float hi = 0.0f, lo = 0.0f;
     for (int s = 0; s < a.splits; ++s) {
@@ -211,32 +235,118 @@ __global__ void __launch_bounds__(NT) router_reduce_kernel(RouterReduceArgs a) {
     }
     dw[i] = from_f32<T>(hi + lo);
   }
-  if (a.dbias && blockIdx.x == 0) {
-    for (int e = threadIdx.x; e < a.E; e += NT) {
-      float s = 0.0f;
-      for (int b = 0; b < a.nb; ++b) s += a.dbias_part[(int64_t)b * a.E + e];
-      a.dbias[e] = s;
+}
+
+// dx[t] = sum_j dX_perm[inv[t, j]] (+ dx_shared[t]) + router part, where the
+// router part is either sum_e dz[t, e] W_r[e] computed here (few experts) or
+// the f32 rows of a matrix-core product (dxr).  One wave per token, 16-byte
+// vectors along the row, fixed summation order.
+template <typename T>
+__global__ void __launch_bounds__(NT) unpermute_kernel(UnpermuteArgs a) {
+  constexpr int VR = 16 / sizeof(T);
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * (NT / 64);
+  const int64_t rowbytes = (int64_t)a.d * sizeof(T);
+  const int nch = (int)(rowbytes / 16);
+  const char* gp = static_cast<const char*>(a.dx_perm);
+  const char* sp = static_cast<const char*>(a.dx_shared);
+  const T* dz = static_cast<const T*>(a.dz_hl);
+  const char* wr = static_cast<const char*>(a.w_router);
+  char* out = static_cast<char*>(a.dx);
+  for (int64_t t = (int64_t)blockIdx.x * (NT / 64) + (threadIdx.x >> 6); t < a.T; t += waves) {
+    int r_l = -1;
+    if (lane < a.k) r_l = a.inv[t * a.k + lane];
+    for (int c0 = 0; c0 < nch; c0 += 64) {
+      const int c = c0 + lane;
+      const bool ok = c < nch;
+      float acc[VR];
+#pragma unroll
+      for (int i = 0; i < VR; ++i) acc[i] = 0.0f;
+      for (int j = 0; j < a.k; ++j) {
+        const int r = __shfl(r_l, j, 64);
+        if (ok && r >= 0) {
+          Chunk<T> ch;
+          ch.raw = ld16(gp + (int64_t)r * rowbytes + (int64_t)c * 16);
+#pragma unroll
+          for (int i = 0; i < VR; ++i) acc[i] += to_f32<T>(ch.e[i]);
+        }
+      }
+      if (!ok) continue;
+      if (sp) {
+        Chunk<T> ch;
+        ch.raw = ld16(sp + t * rowbytes + (int64_t)c * 16);
+#pragma unroll
+        for (int i = 0; i < VR; ++i) acc[i] += to_f32<T>(ch.e[i]);
+      }
+      if (a.dxr) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(a.dxr + t * a.d + (int64_t)c * VR);
+#pragma unroll
+        for (int q = 0; q < VR / 4; ++q) {
+          const f32x4 v = src[q];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[4 * q + i] += v[i];
+        }
+      } else {
+        float rz[VR];
+#pragma unroll
+        for (int i = 0; i < VR; ++i) rz[i] = 0.0f;
+        for (int e = 0; e < a.E; ++e) {
+          const float z = to_f32<T>(dz[t * 2 * a.Ep + e]) + to_f32<T>(dz[t * 2 * a.Ep + a.Ep + e]);
+          Chunk<T> w;
+          w.raw = ld16(wr + (int64_t)e * rowbytes + (int64_t)c * 16);
+#pragma unroll
+          for (int i = 0; i < VR; ++i) rz[i] = fmaf(z, to_f32<T>(w.e[i]), rz[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < VR; ++i) acc[i] += rz[i];
+      }
+      Chunk<T> o;
+#pragma unroll
+      for (int i = 0; i < VR; ++i) o.e[i] = from_f32<T>(acc[i]);
+      st16(out + t * rowbytes + (int64_t)c * 16, o.raw);
     }
   }
 }
 
 // ---- balancing statistic -----------------------------------------------------
+// Threads form a (token lane) x (expert) grid: EP2 = E rounded up to a power of
+// two experts per row of threads, NT / EP2 token lanes.
 constexpr int kAuxTokens = 256;
 
+__device__ __forceinline__ int pow2_at_least(int v) {
+  int p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
 __global__ void __launch_bounds__(NT) aux_partials_kernel(AuxArgs a) {
-  const int e = threadIdx.x;
-  if (e >= a.E) return;
+  __shared__ float sp[NT], se[NT];
+  const int EP2 = pow2_at_least(a.E);
+  const int TL = NT / EP2;
+  const int e = threadIdx.x % EP2, tl = threadIdx.x / EP2;
   const int64_t t0 = (int64_t)blockIdx.x * kAuxTokens;
   int64_t t1 = t0 + kAuxTokens;
   if (t1 > a.T) t1 = a.T;
   float ps = 0.0f, ent = 0.0f;
-  for (int64_t t = t0; t < t1; ++t) {
-    const float p = a.probs[t * a.E + e];
-    ps += p;
-    if (p > 0.0f) ent -= p * logf(p);
+  if (e < a.E) {
+    for (int64_t t = t0 + tl; t < t1; t += TL) {
+      const float p = a.probs[t * a.E + e];
+      ps += p;
+      if (p > 0.0f) ent -= p * logf(p);
+    }
   }
-  a.part[((int64_t)blockIdx.x * 2 + 0) * a.E + e] = ps;
-  a.part[((int64_t)blockIdx.x * 2 + 1) * a.E + e] = ent;
+  sp[threadIdx.x] = ps;
+  se[threadIdx.x] = ent;
+  __syncthreads();
+  if (tl == 0 && e < a.E) {
+    float s1 = 0.0f, s2 = 0.0f;
+    for (int l = 0; l < TL; ++l) {
+      s1 += sp[l * EP2 + e];
+      s2 += se[l * EP2 + e];
+    }
+    a.part[((int64_t)blockIdx.x * 2 + 0) * a.E + e] = s1;
+    a.part[((int64_t)blockIdx.x * 2 + 1) * a.E + e] = s2;
+  }
 }
 
 __device__ double block_sum_d(double v, double* sh) {
@@ -253,15 +363,36 @@ __device__ double block_sum_d(double v, double* sh) {
 
 __global__ void __launch_bounds__(NT) aux_finalize_kernel(AuxArgs a, int nblk) {
   __shared__ double sh[NT / 64];
+  __shared__ float cp[NT], ce[NT];
+  __shared__ float colp[256], cole[256];
+  const int EP2 = pow2_at_least(a.E);
+  const int TL = NT / EP2;
+  {
+    const int e = threadIdx.x % EP2, tl = threadIdx.x / EP2;
+    float s1 = 0.0f, s2 = 0.0f;
+    if (e < a.E) {
+      for (int b = tl; b < nblk; b += TL) {
+        s1 += a.part[((int64_t)b * 2 + 0) * a.E + e];
+        s2 += a.part[((int64_t)b * 2 + 1) * a.E + e];
+      }
+    }
+    cp[threadIdx.x] = s1;
+    ce[threadIdx.x] = s2;
+    __syncthreads();
+    if (tl == 0 && e < a.E) {
+      float t1 = 0.0f, t2 = 0.0f;
+      for (int l = 0; l < TL; ++l) {
+        t1 += cp[l * EP2 + e];
+        t2 += ce[l * EP2 + e];
+      }
+      colp[e] = t1;
+      cole[e] = t2;
+    }
+    __syncthreads();
+  }
   const int e = threadIdx.x;
   const bool valid = e < a.E;
-  float ps = 0.0f, ent = 0.0f;
-  if (valid) {
-    for (int b = 0; b < nblk; ++b) {
-      ps += a.part[((int64_t)b * 2 + 0) * a.E + e];
-      ent += a.part[((int64_t)b * 2 + 1) * a.E + e];
-    }
-  }
+  const float ps = valid ? colp[e] : 0.0f, ent = valid ? cole[e] : 0.0f;
   const double T = (double)a.T;
   const double cnt = valid ? (double)a.counts[e] : 0.0;
   const double f = (T > 0) ? cnt / (T * a.k) : 0.0;
@@ -276,7 +407,6 @@ __global__ void __launch_bounds__(NT) aux_finalize_kernel(AuxArgs a, int nblk) {
   const double mean = csum / a.E;
   const double var = block_sum_d(valid ? (cnt - mean) * (cnt - mean) : 0.0, sh) / a.E;
   const double unused = block_sum_d(valid && cnt == 0.0 ? 1.0 : 0.0, sh);
-  // min / max
   double mn = valid ? cnt : 1e300, mx = valid ? cnt : -1.0;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -362,13 +492,27 @@ hipError_t launch_stack2(int dt, const Stack2Args& a, hipStream_t s) {
 
 hipError_t launch_router_reduce(int dt, const RouterReduceArgs& a, hipStream_t s) {
   const int64_t n = (int64_t)a.E * a.d;
-  int64_t grid = (n + NT - 1) / NT;
-  if (grid > 2048) grid = 2048;
-  if (grid < 1) grid = 1;
+  int64_t nbw = (n + NT - 1) / NT;
+  if (nbw > 2048) nbw = 2048;
+  if (nbw < 1) nbw = 1;
+  const int64_t grid = nbw + (a.dbias ? a.E : 0);
   switch (dt) {
-    case DT_BF16: hipLaunchKernelGGL(router_reduce_kernel<__bf16>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
-    case DT_F16: hipLaunchKernelGGL(router_reduce_kernel<_Float16>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
-    case DT_F32: hipLaunchKernelGGL(router_reduce_kernel<float>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    case DT_BF16: hipLaunchKernelGGL(router_reduce_kernel<__bf16>, dim3((unsigned)grid), dim3(NT), 0, s, a, (int)nbw); break;
+    case DT_F16: hipLaunchKernelGGL(router_reduce_kernel<_Float16>, dim3((unsigned)grid), dim3(NT), 0, s, a, (int)nbw); break;
+    case DT_F32: hipLaunchKernelGGL(router_reduce_kernel<float>, dim3((unsigned)grid), dim3(NT), 0, s, a, (int)nbw); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_unpermute(int dt, const UnpermuteArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  int64_t grid = (a.T + 3) / 4;
+  if (grid > 8192) grid = 8192;
+  switch (dt) {
+    case DT_BF16: hipLaunchKernelGGL(unpermute_kernel<__bf16>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    case DT_F16: hipLaunchKernelGGL(unpermute_kernel<_Float16>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    case DT_F32: hipLaunchKernelGGL(unpermute_kernel<float>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

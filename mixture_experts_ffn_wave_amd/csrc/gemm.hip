@@ -1,29 +1,47 @@
-// Grouped GEMMs of the MoE layer on gfx950 matrix cores (MFMA 32x32x16 for
-// bf16/f16, 32x32x2 for f32), LDS-staged 128x128 tiles, four waves per
-// workgroup, each wave a 64x64 quadrant (2x2 MFMA tiles).
+// Grouped GEMMs of the MoE layer on gfx950 matrix cores.
 //
-// Two kernel families:
-//   row_gemm    -- output rows are token rows.  Rows come in segments (one per
+// One tile engine, two kernel families:
+//   row GEMMs   -- output rows are token rows.  Rows come in segments (one per
 //                  expert, read from the device offsets array, so the host
 //                  never learns the per-expert sizes) or as one dense segment.
 //                  Used for gate/up (+SwiGLU epilogue), down, the two dgrad
-//                  GEMMs (+SwiGLU backward / unpermute epilogues) and the
+//                  GEMMs (+SwiGLU-backward epilogue) and the
 //                  router's input gradient.
-//   wgrad_gemm  -- the contraction runs over a segment's tokens (weight
-//                  gradients); both operands are read token-major and
-//                  transposed while being staged into LDS.
+//   wgrad GEMMs -- the contraction runs over a segment's tokens (weight
+//                  gradients); both operands are token-major.
 //
-// Every workgroup works out its own tile from the offsets array (a prefix sum
-// over at most 256 segments), so no schedule buffer and no host sync is
-// needed.  Workgroup ids are remapped so that each of the 8 XCDs (which own
-// separate L2 caches; hardware hands out ids round-robin over them) receives a
-// contiguous run of tiles: neighbouring n-tiles of one m-tile share the token
-// rows, neighbouring m-tiles of one expert share its weights.
+// Tiles.  A workgroup of 4 waves (2 x 2) computes a BM x BN output tile; each
+// wave a (BM/2) x (BN/2) quadrant made of 32x32 MFMA tiles (32x32x16 for
+// bf16/f16, eight 32x32x2 steps for f32).  16-bit types use 256 x 256 tiles
+// (128 x 128 per wave: 16 accumulators of 16 registers), which stage 128
+// FLOP per byte of operand -- twice the per-CU operand bandwidth a 128 x 128
+// tile needs; the plan picks 128 x 128 where a dimension is not a multiple of
+// 256 or segments are short.  K is staged 128 bytes at a time through a
+// double-buffered LDS ring: global loads for chunk c+1 are in flight while the
+// MFMAs of chunk c run, one barrier per chunk.
+//
+// Operand layouts in LDS.  An operand whose rows are contiguous along K is
+// stored [row][k] (row stride 144 bytes: conflict-free ds_read_b128).  An
+// operand that arrives k-major (weights read transposed, token-major operands
+// of the weight gradients) is stored as it comes, [k][row] with a 64-byte row
+// pad, and turned into MFMA fragments by ds_read_b64_tr_b16: within each
+// 16-lane group, lane i receives element i%4 of the 8-byte chunks addressed by
+// lanes 4q+i/4 (q = 0..3), so pointing lane j at (k0 + j/4, r0 + 4(j%4))
+// hands lane i the four k values of row r0 + i.  (f32 operands are transposed
+// in registers instead.)
 //
 // MFMA operand roles: the weight-side tile feeds the MFMA "A" operand and the
-// token-side tile the "B" operand, so each lane ends up holding 4 consecutive
-// output columns of one token row -- an 8-byte (16-bit types) or 16-byte
-// (f32) store.
+// token-side tile the "B" operand, so each lane holds 4 consecutive output
+// columns of one token row -- one 8-byte (16-bit) or 16-byte (f32) store.
+//
+// Every workgroup works out its own tile from the offsets array (a prefix sum
+// over at most 256 segments), and workgroup ids are remapped so that each of
+// the 8 XCDs (separate L2 caches; ids are handed out round-robin over them)
+// receives a contiguous run of tiles.
+
+#include <mutex>
+#include <set>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -31,15 +49,14 @@
 namespace moe {
 namespace {
 
-constexpr int BM = 128;          // token rows (row_gemm) / output rows (wgrad) per tile
-constexpr int BN = 128;          // output columns per tile
-constexpr int KB = 128;          // bytes of k staged per LDS chunk
-constexpr int LROW = KB + 16;    // LDS row stride: 16 bytes of padding keeps ds_read_b128 conflict-free
-constexpr int NT = 256;          // threads per workgroup
+constexpr int NT = 256;          // threads per workgroup (4 waves)
+constexpr int KB = 128;          // bytes of k staged per chunk
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
 
 // Maps the hardware workgroup id onto a logical tile index in [0, R) so that
-// XCD x (= id % 8) gets logical tiles [x*Q, (x+1)*Q).  Returns -1 for ids
-// beyond the work.
+// XCD x (= id % 8) gets logical tiles [x*Q, (x+1)*Q).  Returns -1 beyond the work.
 __device__ __forceinline__ int xcd_logical(int hw, int R) {
   const int q = (R + 7) >> 3;
   const int y = hw >> 3;
@@ -48,85 +65,242 @@ __device__ __forceinline__ int xcd_logical(int hw, int R) {
   return l < R ? l : -1;
 }
 
-// Stage 4 rows x 16 bytes of a token-major source into LDS rows of k:
-// chunk i holds source row k = 4*kg + i, columns cg*VR .. cg*VR+VR-1; element
-// v of every chunk goes to LDS row cg*VR + v at k offset 4*kg.
-template <typename T>
-__device__ __forceinline__ void store_transposed(char* lds, const u32x4* c, int kg, int cg) {
-  constexpr int ES = sizeof(T);
-  constexpr int VR = 16 / ES;
-  if constexpr (ES == 2) {
+// ------------------------------------------------------------ operand tile --
+// ROWS rows of the tile; TR: the source is k-major (rows contiguous along the
+// tile's row index, one source row per k).
+template <typename T, int ROWS, bool TR>
+struct Operand {
+  static constexpr int ES = sizeof(T);
+  static constexpr int BK = KB / ES;                       // k per chunk
+  static constexpr bool HWTR = TR && ES == 2;              // transpose on the read side
+  static constexpr int STRIDE = HWTR ? ROWS * ES + 64 : KB + 16;
+  static constexpr int BYTES = HWTR ? BK * STRIDE : ROWS * STRIDE;
+  // 16-byte chunks each thread moves per K chunk
+  static constexpr int NREG = ROWS * KB / 16 / NT;         // = ROWS / 32
+  static constexpr int CH = Mma32<T>::kChunks;
+  // register-transpose path (f32): 4 k-rows x 16 bytes per thread-block
+  static constexpr int VR = 16 / ES;                       // row elements per 16 bytes
+  static constexpr int NCG = ROWS / VR;                    // column groups of a k-row
+  static constexpr int KG = BK / 4;                        // groups of 4 k-rows
+  static_assert(HWTR || !TR || NCG * KG == NT * NREG / 4, "f32 transposed tile geometry");
+
+  u32x4 r[NREG];
+
+  // -- loads, normal layout: row pointers are precomputed by the caller --
+  // chunk c = tid + NT*s holds row c/8, 16-byte column c%8
+  __device__ __forceinline__ static int nrow(int tid, int s) { return (tid + NT * s) >> 3; }
+  __device__ __forceinline__ void load_normal(const char* const (&rowp)[NREG], int64_t koff, int tid) {
 #pragma unroll
-    for (int v = 0; v < VR; ++v) {
-      const int w = v >> 1, sh = (v & 1) * 16;
-      uint32_t e0 = (c[0][w] >> sh) & 0xffffu, e1 = (c[1][w] >> sh) & 0xffffu;
-      uint32_t e2 = (c[2][w] >> sh) & 0xffffu, e3 = (c[3][w] >> sh) & 0xffffu;
-      u32x2 o = {e0 | (e1 << 16), e2 | (e3 << 16)};
-      st8(lds + (cg * VR + v) * LROW + (4 * kg) * ES, o);
-    }
-  } else {
+    for (int s = 0; s < NREG; ++s)
+      r[s] = rowp[s] ? ld16(rowp[s] + koff + (tid & 7) * 16) : (u32x4){0u, 0u, 0u, 0u};
+  }
+  __device__ __forceinline__ void stage_normal(char* lds, int tid) const {
 #pragma unroll
-    for (int v = 0; v < VR; ++v) {
-      u32x4 o = {c[0][v], c[1][v], c[2][v], c[3][v]};
-      st16(lds + (cg * VR + v) * LROW + (4 * kg) * ES, o);
+    for (int s = 0; s < NREG; ++s) {
+      const int c = tid + NT * s;
+      st16(lds + (c >> 3) * STRIDE + (c & 7) * 16, r[s]);
     }
   }
-}
 
-__device__ __forceinline__ void store_normal(char* lds, const u32x4* r, int tid) {
+  // -- loads, k-major source: element (k, row) at base + k*ldk + row*ES, k < kvalid --
+  __device__ __forceinline__ void load_kmajor(const char* base, int64_t ldk, int kvalid, int tid) {
+    if constexpr (HWTR) {
+      constexpr int CPR = ROWS * ES / 16;                  // 16-byte chunks per k-row
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int c = tid + NT * s;
-    st16(lds + (c >> 3) * LROW + (c & 7) * 16, r[s]);
+      for (int s = 0; s < NREG; ++s) {
+        const int c = tid + NT * s, k = c / CPR, cc = c % CPR;
+        r[s] = (k < kvalid) ? ld16(base + (int64_t)k * ldk + cc * 16) : (u32x4){0u, 0u, 0u, 0u};
+      }
+    } else {
+      // thread-block b covers k-rows 4*kg..4*kg+3 and row elements cg*VR..cg*VR+VR-1
+#pragma unroll
+      for (int b = 0; b < NREG / 4; ++b) {
+        const int blk = tid + NT * b, kg = blk / NCG, cg = blk % NCG;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int k = 4 * kg + i;
+          r[4 * b + i] = (k < kvalid) ? ld16(base + (int64_t)k * ldk + cg * 16) : (u32x4){0u, 0u, 0u, 0u};
+        }
+      }
+    }
   }
-}
+  __device__ __forceinline__ void stage_kmajor(char* lds, int tid) const {
+    if constexpr (HWTR) {
+      constexpr int CPR = ROWS * ES / 16;
+#pragma unroll
+      for (int s = 0; s < NREG; ++s) {
+        const int c = tid + NT * s, k = c / CPR, cc = c % CPR;
+        st16(lds + k * STRIDE + cc * 16, r[s]);
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < NREG / 4; ++b) {
+        const int blk = tid + NT * b, kg = blk / NCG, cg = blk % NCG;
+#pragma unroll
+        for (int v = 0; v < VR; ++v) {
+          // element v of each of the 4 k-rows -> LDS row cg*VR + v at k offset 4*kg
+          u32x4 o = {r[4 * b + 0][v], r[4 * b + 1][v], r[4 * b + 2][v], r[4 * b + 3][v]};
+          st16(lds + (cg * VR + v) * STRIDE + (4 * kg) * ES, o);
+        }
+      }
+    }
+  }
 
-// One LDS chunk of MFMA work: KB bytes of k for the wave's 2x2 tiles.
-// qrow[ns] / prow[ms] are the LDS rows (lane 0's) of the wave's operand tiles.
-template <typename T>
-__device__ __forceinline__ void mfma_chunk(f32x16 (&acc)[2][2], const char* lq, const char* lp,
-                                           const int (&qrow)[2], const int (&prow)[2], int lane) {
-  constexpr int ES = sizeof(T);
-  constexpr int KSTEPS = KB / ES / 16;
+  // -- MFMA fragment: rows row0 .. row0+31, k16 step ks of the chunk --
+  __device__ __forceinline__ static void frag(u32x4 (&f)[CH], const char* lds, int row0, int ks, int lane) {
+    if constexpr (HWTR) {
+      const int g = lane >> 4, i = lane & 15;
+      const int k = ks * 16 + 8 * (g >> 1) + (i >> 2);
+      const int row = row0 + 16 * (g & 1) + 4 * (i & 3);
+      const char* p = lds + k * STRIDE + row * ES;
+      const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(p));
+      const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(p + 4 * STRIDE));
+      const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+      f[0] = (u32x4){ua[0], ua[1], ub[0], ub[1]};
+    } else {
+      const char* p = lds + (row0 + (lane & 31)) * STRIDE + ks * 16 * ES + (lane >> 5) * 8 * ES;
+#pragma unroll
+      for (int ch = 0; ch < CH; ++ch) f[ch] = ld16(p + ch * 16);
+    }
+  }
+};
+
+// MFMA work of one chunk for a wave: NS weight-side subtiles (LDS rows
+// qrow[ns]) x MS token-side subtiles (LDS rows prow[ms]).
+template <typename T, typename PO, typename QO, int NS, int MS, int KSTEPS = KB / sizeof(T) / 16>
+__device__ __forceinline__ void mfma_chunk(f32x16 (&acc)[NS][MS], const char* lq, const char* lp,
+                                           const int (&qrow)[NS], const int (&prow)[MS], int lane) {
   constexpr int CH = Mma32<T>::kChunks;
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
-    const int kb = ks * 16 * ES + (lane >> 5) * 8 * ES;
-    u32x4 fa[2][CH], fb[2][CH];
+    u32x4 fa[NS][CH], fb[MS][CH];
 #pragma unroll
-    for (int ns = 0; ns < 2; ++ns) {
-      const char* base = lq + (qrow[ns] + (lane & 31)) * LROW + kb;
+    for (int ns = 0; ns < NS; ++ns) QO::frag(fa[ns], lq, qrow[ns], ks, lane);
 #pragma unroll
-      for (int ch = 0; ch < CH; ++ch) fa[ns][ch] = ld16(base + ch * 16);
-    }
+    for (int ms = 0; ms < MS; ++ms) PO::frag(fb[ms], lp, prow[ms], ks, lane);
 #pragma unroll
-    for (int ms = 0; ms < 2; ++ms) {
-      const char* base = lp + (prow[ms] + (lane & 31)) * LROW + kb;
+    for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
-      for (int ch = 0; ch < CH; ++ch) fb[ms][ch] = ld16(base + ch * 16);
-    }
-#pragma unroll
-    for (int ns = 0; ns < 2; ++ns)
-#pragma unroll
-      for (int ms = 0; ms < 2; ++ms) Mma32<T>::run(acc[ns][ms], fa[ns], fb[ms]);
+      for (int ms = 0; ms < MS; ++ms) Mma32<T>::run(acc[ns][ms], fa[ns], fb[ms]);
   }
 }
 
-// ------------------------------------------------------------ row GEMM ----
-template <typename T, int OP, int EPI>
-__global__ void __launch_bounds__(NT) row_gemm(RowGemmArgs a) {
+template <int NS, int MS>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[NS][MS]) {
+#pragma unroll
+  for (int i = 0; i < NS; ++i)
+#pragma unroll
+    for (int j = 0; j < MS; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+}
+
+
+// --------------------------------------------- direct-to-LDS operand tiles --
+// 16-bit operands go from global memory straight into LDS with
+// buffer_load_dwordx4 ... lds: lane l of an instruction lands 16 bytes at the
+// instruction's LDS base + 16 l, and offsets at or past the descriptor's record
+// count read as zero (masked rows and tokens cost no branch).  Tiles are
+// unpadded and XOR-swizzled at 16-byte granularity so the fragment reads are
+// free of bank conflicts:
+//   [row][k] tiles (128-byte rows): chunk c of row r sits at c ^ ((r >> 1) & 7)
+//   [k][row] tiles: chunk c of k-row k sits at c ^ (4 (k & 3))
+// Each wave issues ROWS/32 loads per operand per K chunk.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ void dma16(rsrc_t rs, char* lds_lane0, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_lane0, 16, voff, 0, 0, 0);
+}
+
+// Bytes of k per LDS chunk on the direct-load path and the depth of its ring:
+// 64-byte chunks, 4 stages, so loads run three chunks ahead of the MFMAs.
+constexpr int DKB = 64;
+constexpr int NSTG = 4;
+
+// vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+template <int ROWS>
+struct DmaRows {                                   // [row][k], DKB bytes per row
+  static constexpr int CPRW = DKB / 16;            // 16-byte chunks per row (4)
+  static constexpr int RPI = 1024 / DKB;           // rows per load instruction (16)
+  static constexpr int BYTES = ROWS * DKB;
+  static constexpr int NI = BYTES / 1024 / 4;      // load instructions per wave per chunk
+  __device__ __forceinline__ static int swz(int r) { return (r >> 2) & 3; }
+  __device__ __forceinline__ static int row_of(int w, int s, int lane) { return RPI * (w + 4 * s) + lane / CPRW; }
+  __device__ __forceinline__ static int gchunk(int row, int lane) { return (lane % CPRW) ^ swz(row); }
+  __device__ __forceinline__ static int lds_off(int w, int s) { return RPI * (w + 4 * s) * DKB; }
+  __device__ __forceinline__ static void frag(u32x4 (&f)[1], const char* lds, int row0, int ks, int lane) {
+    const int r = row0 + (lane & 31);
+    const int c = ks * 2 + (lane >> 5);
+    f[0] = ld16(lds + r * DKB + ((c ^ swz(r)) << 4));
+  }
+};
+
+template <int ROWS>
+struct DmaKmajor {                                 // [k][row], DKB/2 k-rows per chunk
+  static constexpr int KROWS = DKB / 2;
+  static constexpr int RB = ROWS * 2;              // bytes per k-row
+  static constexpr int CPR = RB / 16;              // 16-byte chunks per k-row
+  static constexpr int KPI = 1024 / RB;            // k-rows per load instruction
+  static constexpr int BYTES = KROWS * RB;
+  static constexpr int NI = BYTES / 1024 / 4;
+  static_assert(CPR >= 16, "swizzle needs at least 16 chunks per k-row");
+  __device__ __forceinline__ static int k_of(int w, int s, int lane) { return KPI * (w + 4 * s) + lane / CPR; }
+  __device__ __forceinline__ static int gchunk(int k, int lane) { return (lane % CPR) ^ (4 * (k & 3)); }
+  __device__ __forceinline__ static int lds_off(int w, int s) { return KPI * (w + 4 * s) * RB; }
+  __device__ __forceinline__ static void frag(u32x4 (&f)[1], const char* lds, int row0, int ks, int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    const int k = ks * 16 + 8 * (g >> 1) + (i >> 2);
+    const int row = row0 + 16 * (g & 1) + 4 * (i & 3);
+    const char* p = lds + k * RB + (((row >> 3) ^ (4 * (k & 3))) << 4) + (row & 7) * 2;
+    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(p));
+    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(p + 4 * RB));
+    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+    f[0] = (u32x4){ua[0], ua[1], ub[0], ub[1]};
+  }
+};
+
+// Barrier before chunk kc of the ring.  This wave's loads of chunk kc have
+// landed once at most the (up to NSTG-2) later chunks' loads are outstanding;
+// its LDS reads of chunk kc-1 have returned (lgkmcnt(0)); s_barrier then makes
+// both true for the whole workgroup.  __syncthreads() would add a release
+// fence that waits for every outstanding load, draining the ring.  The empty
+// asm statements keep the compiler from moving memory accesses across.
+template <int LPC>
+__device__ __forceinline__ void ring_barrier(int ahead) {
+  asm volatile("" ::: "memory");
+  if (ahead >= 2) wait_vmcnt<2 * LPC>();
+  else if (ahead == 1) wait_vmcnt<LPC>();
+  else wait_vmcnt<0>();
+  __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0), vmcnt/expcnt untouched
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// --------------------------------------------------------------- row GEMM ---
+template <typename T, int BM, int BN, int OP, int EPI>
+__device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) {
   constexpr int ES = sizeof(T);
-  constexpr int BK = KB / ES;
-  constexpr int VR = 16 / ES;
-  constexpr int NCG = BN / VR;
   constexpr bool QT = (OP == OP_DOWN_DGRAD || OP == OP_GU_DGRAD || OP == OP_ROUTER_DX);
-  constexpr int TILE_N = (OP == OP_GU_FWD) ? BN / 2 : BN;   // output (H) columns per tile
+  using PO = Operand<T, BM, false>;
+  using QO = Operand<T, BN, QT>;
+  constexpr int BK = PO::BK;
+  constexpr int TILE_N = (OP == OP_GU_FWD) ? BN / 2 : BN;    // output (H) columns per tile
+  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int MS = WTM / 32, NS = WTN / 32;
+  constexpr int STAGE = PO::BYTES + QO::BYTES;
 
-  __shared__ __attribute__((aligned(16))) char lp[BM * LROW];
-  __shared__ __attribute__((aligned(16))) char lq[BN * LROW];
-  __shared__ int s_scan[NT / 64];
-  __shared__ int s_loc[2];
-
+  constexpr int SCAN_OFF = (ES == 2) ? NSTG * (BM + BN) * DKB : 2 * STAGE;
+  int* s_scan = reinterpret_cast<int*>(smem + SCAN_OFF);      // [4] wave sums, [4..5] located tile
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_ntiles = a.N / TILE_N;
 
@@ -153,102 +327,186 @@ __global__ void __launch_bounds__(NT) row_gemm(RowGemmArgs a) {
   }
   const int start = before + incl - my_nt;
   const int logical = xcd_logical(blockIdx.x, total * n_ntiles);
-  if (logical < 0) return;                       // uniform across the workgroup
+  if (logical < 0) return;                                    // uniform across the workgroup
   const int mt = logical / n_ntiles, ntile = logical - mt * n_ntiles;
-  if (tid < a.G && mt >= start && mt < start + my_nt) { s_loc[0] = tid; s_loc[1] = mt - start; }
+  if (tid < a.G && mt >= start && mt < start + my_nt) { s_scan[4] = tid; s_scan[5] = mt - start; }
   __syncthreads();
-  const int g = s_loc[0];
+  const int g = s_scan[4];
   const int64_t seg0 = a.offsets ? a.offsets[g] : 0;
   const int64_t seg1 = a.offsets ? a.offsets[g + 1] : a.M;
-  const int64_t row0 = seg0 + (int64_t)s_loc[1] * BM;
+  const int64_t row0 = seg0 + (int64_t)s_scan[5] * BM;
   const int rows = (int)((seg1 - row0) < BM ? (seg1 - row0) : BM);
   const int n0 = ntile * TILE_N;
 
   const char* Pb = static_cast<const char*>(a.P);
   const char* Qb = static_cast<const char*>(a.Q) + (int64_t)g * a.q_group_stride * ES;
+  const int wm = wave & 1, wn = wave >> 1;
+  int qrow[NS], prow[MS];
+#pragma unroll
+  for (int ns = 0; ns < NS; ++ns) {
+    if constexpr (OP == OP_GU_FWD)
+      qrow[ns] = (ns < NS / 2) ? wn * (BN / 4) + ns * 32 : BN / 2 + wn * (BN / 4) + (ns - NS / 2) * 32;
+    else
+      qrow[ns] = wn * WTN + ns * 32;
+  }
+#pragma unroll
+  for (int ms = 0; ms < MS; ++ms) prow[ms] = wm * WTM + ms * 32;
+  f32x16 acc[NS][MS];
+  zero_acc(acc);
+  const int nk = a.K / BK;
 
-  // ---- global -> register loaders for one K chunk starting at element kc
-  auto load_p = [&](int kc, u32x4* r) {
+  if constexpr (ES == 2) {
+    // ---------------- direct-to-LDS main loop (16-bit types)
+    using PD = DmaRows<BM>;
+    using QD = std::conditional_t<QT, DmaKmajor<BN>, DmaRows<BN>>;
+    constexpr int DSTAGE = PD::BYTES + QD::BYTES;
+    constexpr int DBKE = DKB / ES;                    // k elements per chunk
+    // token rows of this tile: rows >= `rows` fall outside the descriptor and read as zero
+    const rsrc_t prs = make_rsrc(Pb + row0 * a.ldp * ES, (uint32_t)(rows * a.ldp * ES));
+    uint32_t poff[PD::NI];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int c = tid + NT * s, rr = c >> 3, cc = c & 7;
-      if (rr < rows) r[s] = ld16(Pb + ((row0 + rr) * a.ldp + kc) * ES + cc * 16);
-      else r[s] = (u32x4){0u, 0u, 0u, 0u};
+    for (int s2 = 0; s2 < PD::NI; ++s2) {
+      const int r = PD::row_of(wave, s2, lane);
+      poff[s2] = (uint32_t)(r * a.ldp * ES + PD::gchunk(r, lane) * 16);
     }
-  };
-  auto load_q = [&](int kc, u32x4* r) {
+    uint32_t qoff[QD::NI];
+    const char* qbase;
+    int64_t qldk = 0;
     if constexpr (!QT) {
+      qbase = Qb;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int c = tid + NT * s, q = c >> 3, cc = c & 7;
-        int64_t off;
+      for (int s2 = 0; s2 < QD::NI; ++s2) {
+        const int q = QD::row_of(wave, s2, lane);
+        int64_t roff;
         if constexpr (OP == OP_GU_FWD) {
-          // tile = 64 gate rows then the 64 matching up rows of one expert block
           const int blk = n0 / a.sub, r0 = n0 - blk * a.sub;
-          const int wrow = blk * 2 * a.sub + (q < 64 ? r0 + q : a.sub + r0 + (q - 64));
-          off = (int64_t)wrow * a.ldq + kc;
+          const int wrow = blk * 2 * a.sub + (q < BN / 2 ? r0 + q : a.sub + r0 + (q - BN / 2));
+          roff = (int64_t)wrow * a.ldq;
         } else {
-          // OP_DOWN_FWD: Q[n][c] = W[c / sub][n][c % sub]
-          const int blk = kc / a.sub, kk = kc - blk * a.sub;
-          off = ((int64_t)blk * a.N + (n0 + q)) * a.sub + kk;
+          roff = (int64_t)(n0 + q) * a.sub;         // OP_DOWN_FWD, block part added per chunk
         }
-        r[s] = ld16(Qb + off * ES + cc * 16);
+        qoff[s2] = (uint32_t)(roff * ES + QD::gchunk(q, lane) * 16);
       }
     } else {
-      const int kg = tid / NCG, cg = tid % NCG;
+      if constexpr (OP == OP_DOWN_DGRAD) {
+        const int blk = n0 / a.sub, c0 = n0 - blk * a.sub;
+        qbase = Qb + ((int64_t)blk * a.K * a.sub + c0) * ES;
+        qldk = (int64_t)a.sub * ES;
+      } else {
+        qbase = Qb + (int64_t)n0 * ES;
+        qldk = a.ldq * ES;
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int k = kc + 4 * kg + i;
-        int64_t off;
-        if constexpr (OP == OP_DOWN_DGRAD) {
-          // Q[c][k] = W[c / sub][k][c % sub]; a tile never straddles two blocks
-          const int blk = n0 / a.sub, c0 = n0 - blk * a.sub;
-          off = ((int64_t)blk * a.K + k) * a.sub + c0 + cg * VR;
-        } else {
-          off = (int64_t)k * a.ldq + n0 + cg * VR;
-        }
-        r[i] = ld16(Qb + off * ES);
+      for (int s2 = 0; s2 < QD::NI; ++s2) {
+        const int k = QD::k_of(wave, s2, lane);
+        qoff[s2] = (uint32_t)(k * qldk + QD::gchunk(k, lane) * 16);
       }
     }
+    auto issue = [&](int kc, char* stage) {
+#pragma unroll
+      for (int s2 = 0; s2 < PD::NI; ++s2) dma16(prs, stage + PD::lds_off(wave, s2), poff[s2] + (uint32_t)(kc * ES));
+      if constexpr (!QT) {
+        int64_t koff = (int64_t)kc * ES;
+        if constexpr (OP == OP_DOWN_FWD) {
+          const int blk = kc / a.sub, kk = kc - blk * a.sub;
+          koff = ((int64_t)blk * a.N * a.sub + kk) * ES;
+        }
+        const rsrc_t qrs = make_rsrc(qbase + koff, 0x7fffffffu);
+#pragma unroll
+        for (int s2 = 0; s2 < QD::NI; ++s2) dma16(qrs, stage + PD::BYTES + QD::lds_off(wave, s2), qoff[s2]);
+      } else {
+        const rsrc_t qrs = make_rsrc(qbase + (int64_t)kc * qldk, (uint32_t)(QD::KROWS * qldk));
+#pragma unroll
+        for (int s2 = 0; s2 < QD::NI; ++s2) dma16(qrs, stage + PD::BYTES + QD::lds_off(wave, s2), qoff[s2]);
+      }
+    };
+    constexpr int LPC = PD::NI + QD::NI;             // loads per wave per chunk
+    const int nkd = a.K / DBKE;
+#pragma unroll
+    for (int c = 0; c < NSTG - 1; ++c)
+      if (c < nkd) issue(c * DBKE, smem + c * DSTAGE);
+    for (int kc = 0; kc < nkd; ++kc) {
+      ring_barrier<LPC>(nkd - 1 - kc);                // chunk kc landed everywhere; kc-1 consumed
+      if (kc + NSTG - 1 < nkd) issue((kc + NSTG - 1) * DBKE, smem + ((kc + NSTG - 1) % NSTG) * DSTAGE);
+      const char* buf = smem + (kc % NSTG) * DSTAGE;
+      mfma_chunk<T, PD, QD, NS, MS, DKB / 32>(acc, buf + PD::BYTES, buf, qrow, prow, lane);
+    }
+  } else {
+  // ---------------- register-staged main loop (f32)
+  // ---- row pointers (normal operands) / k-major base (transposed weight)
+  const char* prowp[PO::NREG];
+#pragma unroll
+  for (int s = 0; s < PO::NREG; ++s) {
+    const int rr = PO::nrow(tid, s);
+    prowp[s] = rr < rows ? Pb + (row0 + rr) * a.ldp * ES : nullptr;
+  }
+  const char* qrowp[QO::NREG];
+  const char* qkbase = nullptr;
+  int64_t qldk = 0;
+  if constexpr (!QT) {
+#pragma unroll
+    for (int s = 0; s < QO::NREG; ++s) {
+      const int q = QO::nrow(tid, s);
+      int64_t off;
+      if constexpr (OP == OP_GU_FWD) {
+        // tile = BN/2 gate rows then the matching BN/2 up rows of one expert block
+        const int blk = n0 / a.sub, r0 = n0 - blk * a.sub;
+        const int wrow = blk * 2 * a.sub + (q < BN / 2 ? r0 + q : a.sub + r0 + (q - BN / 2));
+        off = (int64_t)wrow * a.ldq;
+      } else {
+        // OP_DOWN_FWD: Q[n][c] = W[c / sub][n][c % sub]; the block part is added per chunk
+        off = (int64_t)(n0 + q) * a.sub;
+      }
+      qrowp[s] = Qb + off * ES;
+    }
+  } else {
+    if constexpr (OP == OP_DOWN_DGRAD) {
+      // Q[c][k] = W[c / sub][k][c % sub]; a tile never straddles two blocks
+      const int blk = n0 / a.sub, c0 = n0 - blk * a.sub;
+      qkbase = Qb + ((int64_t)blk * a.K * a.sub + c0) * ES;
+      qldk = (int64_t)a.sub * ES;
+    } else {
+      qkbase = Qb + (int64_t)n0 * ES;
+      qldk = a.ldq * ES;
+    }
+  }
+  auto load = [&](int kc, PO& po, QO& qo) {
+    po.load_normal(prowp, (int64_t)kc * ES, tid);
+    if constexpr (!QT) {
+      int64_t koff = (int64_t)kc * ES;
+      if constexpr (OP == OP_DOWN_FWD) {
+        const int blk = kc / a.sub, kk = kc - blk * a.sub;
+        koff = ((int64_t)blk * a.N * a.sub + kk) * ES;
+      }
+      qo.load_normal(qrowp, koff, tid);
+    } else {
+      qo.load_kmajor(qkbase + (int64_t)kc * qldk, qldk, BK, tid);
+    }
   };
-  auto stage = [&](const u32x4* rp, const u32x4* rq) {
-    store_normal(lp, rp, tid);
-    if constexpr (!QT) store_normal(lq, rq, tid);
-    else store_transposed<T>(lq, rq, tid / NCG, tid % NCG);
+  auto stage = [&](char* buf, const PO& po, const QO& qo) {
+    po.stage_normal(buf, tid);
+    if constexpr (!QT) qo.stage_normal(buf + PO::BYTES, tid);
+    else qo.stage_kmajor(buf + PO::BYTES, tid);
   };
 
-  const int wm = wave & 1, wn = wave >> 1;
-  const int qrow[2] = {(OP == OP_GU_FWD) ? wn * 32 : wn * 64, (OP == OP_GU_FWD) ? 64 + wn * 32 : wn * 64 + 32};
-  const int prow[2] = {wm * 64, wm * 64 + 32};
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  const int nk = a.K / BK;
-  u32x4 rp[4], rq[4];
-  load_p(0, rp);
-  load_q(0, rq);
-  stage(rp, rq);
+  PO po;
+  QO qo;
+  load(0, po, qo);
+  stage(smem, po, qo);
   __syncthreads();
   for (int kc = 0; kc < nk; ++kc) {
     const bool more = kc + 1 < nk;
-    if (more) {
-      load_p((kc + 1) * BK, rp);
-      load_q((kc + 1) * BK, rq);
-    }
-    mfma_chunk<T>(acc, lq, lp, qrow, prow, lane);
-    __syncthreads();
-    if (more) stage(rp, rq);
+    if (more) load((kc + 1) * BK, po, qo);
+    const char* buf = smem + (kc & 1) * STAGE;
+    mfma_chunk<T, PO, QO, NS, MS>(acc, buf + PO::BYTES, buf, qrow, prow, lane);
+    if (more) stage(smem + ((kc + 1) & 1) * STAGE, po, qo);
     __syncthreads();
   }
+  }  // main loops
 
   // ---- epilogue: lane holds columns qrow[ns] + 8*rq + 4*(lane/32) + 0..3 of row prow[ms] + lane%32
 #pragma unroll
-  for (int ms = 0; ms < 2; ++ms) {
+  for (int ms = 0; ms < MS; ++ms) {
     const int ml = prow[ms] + (lane & 31);
     if (ml >= rows) continue;
     const int64_t row = row0 + ml;
@@ -256,23 +514,26 @@ __global__ void __launch_bounds__(NT) row_gemm(RowGemmArgs a) {
     for (int rq4 = 0; rq4 < 4; ++rq4) {
       const int nl = 8 * rq4 + 4 * (lane >> 5);
       if constexpr (EPI == EPI_SWIGLU_FWD) {
-        const int hc = n0 + wn * 32 + nl;
-        const int blk = hc / a.sub;
-        const int gcol = blk * 2 * a.sub + (hc - blk * a.sub);
-        float gv[4], uv[4], hv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          gv[i] = acc[0][ms][4 * rq4 + i];
-          uv[i] = acc[1][ms][4 * rq4 + i];
-          hv[i] = silu_f(gv[i]) * uv[i];
+        for (int j = 0; j < NS / 2; ++j) {
+          const int hc = n0 + wn * (BN / 4) + j * 32 + nl;
+          const int blk = hc / a.sub;
+          const int gcol = blk * 2 * a.sub + (hc - blk * a.sub);
+          float gv[4], uv[4], hv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            gv[i] = acc[j][ms][4 * rq4 + i];
+            uv[i] = acc[j + NS / 2][ms][4 * rq4 + i];
+            hv[i] = silu_f(gv[i]) * uv[i];
+          }
+          T* gu = static_cast<T*>(a.C) + row * a.ldc;
+          store4<T>(gu + gcol, gv[0], gv[1], gv[2], gv[3]);
+          store4<T>(gu + gcol + a.sub, uv[0], uv[1], uv[2], uv[3]);
+          store4<T>(static_cast<T*>(a.C2) + row * a.ldc2 + hc, hv[0], hv[1], hv[2], hv[3]);
         }
-        T* gu = static_cast<T*>(a.C) + row * a.ldc;
-        store4<T>(gu + gcol, gv[0], gv[1], gv[2], gv[3]);
-        store4<T>(gu + gcol + a.sub, uv[0], uv[1], uv[2], uv[3]);
-        store4<T>(static_cast<T*>(a.C2) + row * a.ldc2 + hc, hv[0], hv[1], hv[2], hv[3]);
       } else {
 #pragma unroll
-        for (int ns = 0; ns < 2; ++ns) {
+        for (int ns = 0; ns < NS; ++ns) {
           const int n = n0 + qrow[ns] + nl;
           float v[4];
 #pragma unroll
@@ -298,23 +559,6 @@ __global__ void __launch_bounds__(NT) row_gemm(RowGemmArgs a) {
             T* dgu = static_cast<T*>(a.C) + row * a.ldc;
             store4<T>(dgu + gcol, dG[0], dG[1], dG[2], dG[3]);
             store4<T>(dgu + gcol + a.sub, dU[0], dU[1], dU[2], dU[3]);
-          } else if constexpr (EPI == EPI_UNPERMUTE) {
-            // dx[t] = this product + sum_j dX_perm[inv[t, j]] (+ f32 addend)
-            for (int j = 0; j < a.topk; ++j) {
-              const int64_t r = a.inv[row * a.topk + j];
-              if (r < 0) continue;                 // only for an out-of-range routing index
-              float t4[4];
-              load4<T>(static_cast<const T*>(a.gath) + r * a.ldg + n, t4);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) v[i] += t4[i];
-            }
-            if (a.aux) {
-              float t4[4];
-              load4<float>(static_cast<const float*>(a.aux) + row * a.ldaux + n, t4);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) v[i] += t4[i];
-            }
-            store4<T>(static_cast<T*>(a.C) + row * a.ldc + n, v[0], v[1], v[2], v[3]);
           }
         }
       }
@@ -322,16 +566,16 @@ __global__ void __launch_bounds__(NT) row_gemm(RowGemmArgs a) {
   }
 }
 
-// ----------------------------------------------------------- wgrad GEMM ----
-template <typename T, int OUT_F32>
-__global__ void __launch_bounds__(NT) wgrad_gemm(WgradArgs a) {
+// ------------------------------------------------------------- wgrad GEMM ---
+template <typename T, int BM, int BN, int OUT_F32>
+__device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
   constexpr int ES = sizeof(T);
-  constexpr int BK = KB / ES;
-  constexpr int VR = 16 / ES;
-  constexpr int NCG = BN / VR;
-
-  __shared__ __attribute__((aligned(16))) char lp[BM * LROW];
-  __shared__ __attribute__((aligned(16))) char lq[BN * LROW];
+  using PO = Operand<T, BM, true>;
+  using QO = Operand<T, BN, true>;
+  constexpr int BK = PO::BK;
+  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int MS = WTM / 32, NS = WTN / 32;
+  constexpr int STAGE = PO::BYTES + QO::BYTES;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_mt = a.M / BM, n_nt = a.N / BN;
@@ -353,59 +597,89 @@ __global__ void __launch_bounds__(NT) wgrad_gemm(WgradArgs a) {
   const int nk = kend > kbeg ? (int)((kend - kbeg + BK - 1) / BK) : 0;
   const int m0 = mt * BM, n0 = nt * BN;
 
-  const char* Pb = static_cast<const char*>(a.P);
-  const char* Qb = static_cast<const char*>(a.Q);
-  const int kg = tid / NCG, cg = tid % NCG;
-  auto load = [&](int64_t kc, u32x4* rp, u32x4* rq) {
+  const char* Pb = static_cast<const char*>(a.P) + (int64_t)m0 * ES;
+  const char* Qb = static_cast<const char*>(a.Q) + (int64_t)n0 * ES;
+  const int64_t pld = a.ldp * ES, qld = a.ldq * ES;
+  const int wm = wave & 1, wn = wave >> 1;
+  int qrow[NS], prow[MS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t t = kc + 4 * kg + i;
-      if (t < kend) {
-        rp[i] = ld16(Pb + (t * a.ldp + m0 + cg * VR) * ES);
-        rq[i] = ld16(Qb + (t * a.ldq + n0 + cg * VR) * ES);
-      } else {
-        rp[i] = (u32x4){0u, 0u, 0u, 0u};
-        rq[i] = (u32x4){0u, 0u, 0u, 0u};
-      }
+  for (int ns = 0; ns < NS; ++ns) qrow[ns] = wn * WTN + ns * 32;
+#pragma unroll
+  for (int ms = 0; ms < MS; ++ms) prow[ms] = wm * WTM + ms * 32;
+  f32x16 acc[NS][MS];
+  zero_acc(acc);
+
+  if constexpr (ES == 2) {
+    using PD = DmaKmajor<BM>;
+    using QD = DmaKmajor<BN>;
+    constexpr int DSTAGE = PD::BYTES + QD::BYTES;
+    uint32_t poff[PD::NI], qoff[QD::NI];
+#pragma unroll
+    for (int s2 = 0; s2 < PD::NI; ++s2) {
+      const int k = PD::k_of(wave, s2, lane);
+      poff[s2] = (uint32_t)(k * pld + PD::gchunk(k, lane) * 16);
     }
+#pragma unroll
+    for (int s2 = 0; s2 < QD::NI; ++s2) {
+      const int k = QD::k_of(wave, s2, lane);
+      qoff[s2] = (uint32_t)(k * qld + QD::gchunk(k, lane) * 16);
+    }
+    // tokens at or past kend fall outside the per-chunk descriptors and read as zero
+    auto issue = [&](int64_t kc, char* stage) {
+      const int kvalid = (int)((kend - kc) < PD::KROWS ? (kend - kc) : PD::KROWS);
+      const rsrc_t prs = make_rsrc(Pb + kc * pld, (uint32_t)(kvalid * pld));
+      const rsrc_t qrs = make_rsrc(Qb + kc * qld, (uint32_t)(kvalid * qld));
+#pragma unroll
+      for (int s2 = 0; s2 < PD::NI; ++s2) dma16(prs, stage + PD::lds_off(wave, s2), poff[s2]);
+#pragma unroll
+      for (int s2 = 0; s2 < QD::NI; ++s2) dma16(qrs, stage + PD::BYTES + QD::lds_off(wave, s2), qoff[s2]);
+    };
+    constexpr int LPC = PD::NI + QD::NI;
+    constexpr int DBKK = PD::KROWS;                   // tokens per chunk
+    const int nkd = kend > kbeg ? (int)((kend - kbeg + DBKK - 1) / DBKK) : 0;
+#pragma unroll
+    for (int c = 0; c < NSTG - 1; ++c)
+      if (c < nkd) issue(kbeg + (int64_t)c * DBKK, smem + c * DSTAGE);
+    for (int kc = 0; kc < nkd; ++kc) {
+      ring_barrier<LPC>(nkd - 1 - kc);
+      if (kc + NSTG - 1 < nkd) issue(kbeg + (int64_t)(kc + NSTG - 1) * DBKK, smem + ((kc + NSTG - 1) % NSTG) * DSTAGE);
+      const char* buf = smem + (kc % NSTG) * DSTAGE;
+      mfma_chunk<T, PD, QD, NS, MS, DKB / 32>(acc, buf + PD::BYTES, buf, qrow, prow, lane);
+    }
+  } else {
+  auto load = [&](int64_t kc, PO& po, QO& qo) {
+    const int kvalid = (int)((kend - kc) < BK ? (kend - kc) : BK);
+    po.load_kmajor(Pb + kc * pld, pld, kvalid, tid);
+    qo.load_kmajor(Qb + kc * qld, qld, kvalid, tid);
+  };
+  auto stage = [&](char* buf, const PO& po, const QO& qo) {
+    po.stage_kmajor(buf, tid);
+    qo.stage_kmajor(buf + PO::BYTES, tid);
   };
 
-  const int wm = wave & 1, wn = wave >> 1;
-  const int qrow[2] = {wn * 64, wn * 64 + 32};
-  const int prow[2] = {wm * 64, wm * 64 + 32};
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
   if (nk > 0) {
-    u32x4 rp[4], rq[4];
-    load(kbeg, rp, rq);
-    store_transposed<T>(lp, rp, kg, cg);
-    store_transposed<T>(lq, rq, kg, cg);
+    PO po;
+    QO qo;
+    load(kbeg, po, qo);
+    stage(smem, po, qo);
     __syncthreads();
     for (int kc = 0; kc < nk; ++kc) {
       const bool more = kc + 1 < nk;
-      if (more) load(kbeg + (int64_t)(kc + 1) * BK, rp, rq);
-      mfma_chunk<T>(acc, lq, lp, qrow, prow, lane);
-      __syncthreads();
-      if (more) {
-        store_transposed<T>(lp, rp, kg, cg);
-        store_transposed<T>(lq, rq, kg, cg);
-      }
+      if (more) load(kbeg + (int64_t)(kc + 1) * BK, po, qo);
+      const char* buf = smem + (kc & 1) * STAGE;
+      mfma_chunk<T, PO, QO, NS, MS>(acc, buf + PO::BYTES, buf, qrow, prow, lane);
+      if (more) stage(smem + ((kc + 1) & 1) * STAGE, po, qo);
       __syncthreads();
     }
   }
+  }  // main loops
 
   // out[m][n] at C + g*cgs + sp*css + (n/sub)*(M*sub) + m*sub + n%sub
 #pragma unroll
-  for (int ms = 0; ms < 2; ++ms) {
+  for (int ms = 0; ms < MS; ++ms) {
     const int64_t m = m0 + prow[ms] + (lane & 31);
 #pragma unroll
-    for (int ns = 0; ns < 2; ++ns) {
+    for (int ns = 0; ns < NS; ++ns) {
 #pragma unroll
       for (int rq4 = 0; rq4 < 4; ++rq4) {
         const int n = n0 + qrow[ns] + 8 * rq4 + 4 * (lane >> 5);
@@ -421,68 +695,136 @@ __global__ void __launch_bounds__(NT) wgrad_gemm(WgradArgs a) {
   }
 }
 
-template <typename T, int OP, int EPI>
-hipError_t launch_row_t(const RowGemmArgs& a, hipStream_t s) {
-  const int tile_n = (OP == OP_GU_FWD) ? BN / 2 : BN;
-  const int64_t n_ntiles = a.N / tile_n;
-  int64_t mtiles;
-  if (a.offsets) mtiles = (a.M + (int64_t)a.G * (BM - 1)) / BM;   // >= sum_g ceil(len_g / BM)
-  else mtiles = (a.M + BM - 1) / BM;
-  int64_t grid = mtiles * n_ntiles;
-  grid = (grid + 7) / 8 * 8;
-  if (grid == 0) return hipSuccess;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((row_gemm<T, OP, EPI>), dim3((unsigned)grid), dim3(NT), 0, s, a);
-  return hipGetLastError();
-}
-
-template <typename T>
-hipError_t launch_row_dt(int op, int epi, const RowGemmArgs& a, hipStream_t s) {
-  switch (op) {
-    case OP_GU_FWD: return launch_row_t<T, OP_GU_FWD, EPI_SWIGLU_FWD>(a, s);
-    case OP_DOWN_FWD:
-      if (epi == EPI_STORE_F32) return launch_row_t<T, OP_DOWN_FWD, EPI_STORE_F32>(a, s);
-      return launch_row_t<T, OP_DOWN_FWD, EPI_STORE>(a, s);
-    case OP_DOWN_DGRAD: return launch_row_t<T, OP_DOWN_DGRAD, EPI_SWIGLU_BWD>(a, s);
-    case OP_GU_DGRAD:
-      if (epi == EPI_UNPERMUTE) return launch_row_t<T, OP_GU_DGRAD, EPI_UNPERMUTE>(a, s);
-      return launch_row_t<T, OP_GU_DGRAD, EPI_STORE>(a, s);
-    case OP_ROUTER_DX:
-      if (epi == EPI_UNPERMUTE) return launch_row_t<T, OP_ROUTER_DX, EPI_UNPERMUTE>(a, s);
-      return launch_row_t<T, OP_ROUTER_DX, EPI_STORE_F32>(a, s);
+// Dynamic LDS of one kernel: two stages of the larger operand pair, plus the
+// schedule scratch of the row GEMMs.
+template <typename T, int BM, int BN>
+constexpr size_t smem_for() {
+  if constexpr (sizeof(T) == 2) {
+    return (size_t)NSTG * (BM + BN) * DKB + 64;        // direct-load ring
+  } else {
+    constexpr int nn = Operand<T, BM, false>::BYTES + Operand<T, BN, false>::BYTES;
+    constexpr int nt = Operand<T, BM, false>::BYTES + Operand<T, BN, true>::BYTES;
+    constexpr int tt = Operand<T, BM, true>::BYTES + Operand<T, BN, true>::BYTES;
+    constexpr int m1 = nn > nt ? nn : nt;
+    constexpr int m2 = m1 > tt ? m1 : tt;
+    return 2 * (size_t)m2 + 64;
   }
-  return hipErrorInvalidValue;
-}
-
-template <typename T>
-hipError_t launch_wgrad_dt(const WgradArgs& a, hipStream_t s) {
-  int64_t grid = (int64_t)a.G * a.splits * (a.M / BM) * (a.N / BN);
-  grid = (grid + 7) / 8 * 8;
-  if (grid == 0) return hipSuccess;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  if (a.out_f32) hipLaunchKernelGGL((wgrad_gemm<T, 1>), dim3((unsigned)grid), dim3(NT), 0, s, a);
-  else hipLaunchKernelGGL((wgrad_gemm<T, 0>), dim3((unsigned)grid), dim3(NT), 0, s, a);
-  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_row_gemm(int dt, int op, int epi, const RowGemmArgs& a, hipStream_t s) {
-  switch (dt) {
-    case DT_BF16: return launch_row_dt<__bf16>(op, epi, a, s);
-    case DT_F16: return launch_row_dt<_Float16>(op, epi, a, s);
-    case DT_F32: return launch_row_dt<float>(op, epi, a, s);
+// ------------------------------------------------------- named kernels ------
+// One plainly named kernel per (operation, dtype, tile) so profiles read well.
+#define MOE_ROW_KERNEL(NAME, T, BM, BN, OP, EPI)                                           \
+  extern "C" __global__ void __launch_bounds__(NT) NAME(RowGemmArgs a) {                  \
+    extern __shared__ __attribute__((aligned(16))) char smem[];                          \
+    row_gemm_body<T, BM, BN, OP, EPI>(a, smem);                                           \
   }
-  return hipErrorInvalidValue;
+#define MOE_WGRAD_KERNEL(NAME, T, BM, BN, F32)                                             \
+  extern "C" __global__ void __launch_bounds__(NT) NAME(WgradArgs a) {                    \
+    extern __shared__ __attribute__((aligned(16))) char smem[];                          \
+    wgrad_body<T, BM, BN, F32>(a, smem);                                                  \
+  }
+
+#define MOE_KERNEL_SET(T, TN, BM, BN)                                                                      \
+  MOE_ROW_KERNEL(moe_gemm_gate_up_swiglu_##TN##_##BM##x##BN, T, BM, BN, OP_GU_FWD, EPI_SWIGLU_FWD)         \
+  MOE_ROW_KERNEL(moe_gemm_down_##TN##_##BM##x##BN, T, BM, BN, OP_DOWN_FWD, EPI_STORE)                      \
+  MOE_ROW_KERNEL(moe_gemm_down_f32out_##TN##_##BM##x##BN, T, BM, BN, OP_DOWN_FWD, EPI_STORE_F32)           \
+  MOE_ROW_KERNEL(moe_gemm_down_dgrad_swiglu_##TN##_##BM##x##BN, T, BM, BN, OP_DOWN_DGRAD, EPI_SWIGLU_BWD)  \
+  MOE_ROW_KERNEL(moe_gemm_gate_up_dgrad_##TN##_##BM##x##BN, T, BM, BN, OP_GU_DGRAD, EPI_STORE)             \
+  MOE_ROW_KERNEL(moe_gemm_router_dx_f32out_##TN##_##BM##x##BN, T, BM, BN, OP_ROUTER_DX, EPI_STORE_F32)     \
+  MOE_WGRAD_KERNEL(moe_wgrad_##TN##_##BM##x##BN, T, BM, BN, 0)                                             \
+  MOE_WGRAD_KERNEL(moe_wgrad_f32out_##TN##_##BM##x##BN, T, BM, BN, 1)
+
+MOE_KERNEL_SET(__bf16, bf16, 256, 256)
+MOE_KERNEL_SET(__bf16, bf16, 128, 128)
+MOE_KERNEL_SET(_Float16, f16, 256, 256)
+MOE_KERNEL_SET(_Float16, f16, 128, 128)
+MOE_KERNEL_SET(float, f32, 128, 128)
+
+namespace {
+
+typedef void (*RowKernel)(RowGemmArgs);
+typedef void (*WgradKernel)(WgradArgs);
+
+struct KernelSet {
+  RowKernel gu, down, down_f32, down_dgrad, gu_dgrad, router_dx_f32;
+  WgradKernel wgrad, wgrad_f32;
+  size_t lds;
+};
+
+#define MOE_KERNEL_TABLE(T, TN, BM, BN)                                                                 \
+  KernelSet{moe_gemm_gate_up_swiglu_##TN##_##BM##x##BN, moe_gemm_down_##TN##_##BM##x##BN,               \
+            moe_gemm_down_f32out_##TN##_##BM##x##BN, moe_gemm_down_dgrad_swiglu_##TN##_##BM##x##BN,     \
+            moe_gemm_gate_up_dgrad_##TN##_##BM##x##BN, moe_gemm_router_dx_f32out_##TN##_##BM##x##BN,       \
+            moe_wgrad_##TN##_##BM##x##BN, moe_wgrad_f32out_##TN##_##BM##x##BN, smem_for<T, BM, BN>()}
+
+const KernelSet* kernel_set(int dt, int tile) {
+  static const KernelSet bf16_256 = MOE_KERNEL_TABLE(__bf16, bf16, 256, 256);
+  static const KernelSet bf16_128 = MOE_KERNEL_TABLE(__bf16, bf16, 128, 128);
+  static const KernelSet f16_256 = MOE_KERNEL_TABLE(_Float16, f16, 256, 256);
+  static const KernelSet f16_128 = MOE_KERNEL_TABLE(_Float16, f16, 128, 128);
+  static const KernelSet f32_128 = MOE_KERNEL_TABLE(float, f32, 128, 128);
+  if (dt == DT_BF16) return tile == 256 ? &bf16_256 : &bf16_128;
+  if (dt == DT_F16) return tile == 256 ? &f16_256 : &f16_128;
+  if (dt == DT_F32 && tile == 128) return &f32_128;
+  return nullptr;
 }
 
-hipError_t launch_wgrad(int dt, const WgradArgs& a, hipStream_t s) {
-  switch (dt) {
-    case DT_BF16: return launch_wgrad_dt<__bf16>(a, s);
-    case DT_F16: return launch_wgrad_dt<_Float16>(a, s);
-    case DT_F32: return launch_wgrad_dt<float>(a, s);
+// More than 64 KB of dynamic LDS needs a per-kernel opt-in, done once per kernel.
+hipError_t prepare(const void* k, size_t lds) {
+  static std::mutex mu;
+  static std::set<const void*> done;
+  std::lock_guard<std::mutex> lk(mu);
+  if (done.count(k)) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e == hipSuccess) done.insert(k);
+  return e;
+}
+
+}  // namespace
+
+hipError_t launch_row_gemm(int dt, int op, int epi, int tile, const RowGemmArgs& a, hipStream_t s) {
+  const KernelSet* set = kernel_set(dt, tile);
+  if (!set) return hipErrorInvalidValue;
+  RowKernel k = nullptr;
+  switch (op) {
+    case OP_GU_FWD: k = set->gu; break;
+    case OP_DOWN_FWD: k = (epi == EPI_STORE_F32) ? set->down_f32 : set->down; break;
+    case OP_DOWN_DGRAD: k = set->down_dgrad; break;
+    case OP_GU_DGRAD: k = set->gu_dgrad; break;
+    case OP_ROUTER_DX: k = set->router_dx_f32; break;
+    default: return hipErrorInvalidValue;
   }
-  return hipErrorInvalidValue;
+  const int tile_n = (op == OP_GU_FWD) ? tile / 2 : tile;
+  if (a.N % tile_n || a.K % (KB / dtype_bytes(dt))) return hipErrorInvalidValue;
+  const int64_t n_ntiles = a.N / tile_n;
+  int64_t mtiles;
+  if (a.offsets) mtiles = (a.M + (int64_t)a.G * (tile - 1)) / tile;   // >= sum_g ceil(len_g / tile)
+  else mtiles = (a.M + tile - 1) / tile;
+  int64_t grid = mtiles * n_ntiles;
+  grid = (grid + 7) / 8 * 8;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipError_t e = prepare((const void*)k, set->lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(NT), set->lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_wgrad(int dt, int tile, const WgradArgs& a, hipStream_t s) {
+  const KernelSet* set = kernel_set(dt, tile);
+  if (!set) return hipErrorInvalidValue;
+  if (a.M % tile || a.N % tile) return hipErrorInvalidValue;
+  int64_t grid = (int64_t)a.G * a.splits * (a.M / tile) * (a.N / tile);
+  grid = (grid + 7) / 8 * 8;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  WgradKernel k = a.out_f32 ? set->wgrad_f32 : set->wgrad;
+  hipError_t e = prepare((const void*)k, set->lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(NT), set->lds, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace moe

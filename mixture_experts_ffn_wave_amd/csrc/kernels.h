@@ -46,7 +46,7 @@ hipError_t launch_permute_scatter(int dt, const PermuteArgs& a, hipStream_t s);
 // Row-grouped GEMM: output rows are token rows grouped in segments (one per
 // expert, from `offsets`), or one dense segment of M rows.
 enum RowOp { OP_GU_FWD = 0, OP_DOWN_FWD = 1, OP_DOWN_DGRAD = 2, OP_GU_DGRAD = 3, OP_ROUTER_DX = 4 };
-enum RowEpi { EPI_SWIGLU_FWD = 0, EPI_STORE = 1, EPI_SWIGLU_BWD = 2, EPI_UNPERMUTE = 3, EPI_STORE_F32 = 4 };
+enum RowEpi { EPI_SWIGLU_FWD = 0, EPI_STORE = 1, EPI_SWIGLU_BWD = 2, EPI_STORE_F32 = 4 };
 
 struct RowGemmArgs {
   const void* P; int64_t ldp;      // token-side operand [rows, K], elements
@@ -60,11 +60,10 @@ struct RowGemmArgs {
   int sub;                         // width of one shared expert (= I for routed experts)
   void* C; int64_t ldc;            // main output
   void* C2; int64_t ldc2;          // second output (H for OP_GU_FWD)
-  const void* aux; int64_t ldaux;  // saved GU (SwiGLU bwd) or f32 addend (unpermute)
-  const int32_t* inv; int topk;    // unpermute: rows of gath summed into each token
-  const void* gath; int64_t ldg;   // unpermute: dX_perm
+  const void* aux; int64_t ldaux;  // saved GU (SwiGLU backward epilogue)
 };
-hipError_t launch_row_gemm(int dt, int op, int epi, const RowGemmArgs& a, hipStream_t s);
+// tile: 256 (16-bit types only) or 128; the plan chooses it once per GEMM.
+hipError_t launch_row_gemm(int dt, int op, int epi, int tile, const RowGemmArgs& a, hipStream_t s);
 
 // Weight-gradient GEMM: out[m][n] = sum over the segment's tokens t of P[t][m] * Q[t][n].
 struct WgradArgs {
@@ -80,7 +79,7 @@ struct WgradArgs {
   int sub;
   int out_f32;                     // 1: write f32 partials, 0: write act dtype
 };
-hipError_t launch_wgrad(int dt, const WgradArgs& a, hipStream_t s);
+hipError_t launch_wgrad(int dt, int tile, const WgradArgs& a, hipStream_t s);
 
 // ------------------------------------------------------ element-wise --
 struct CombineArgs {
@@ -118,6 +117,20 @@ struct RouterReduceArgs {
   const float* dbias_part; int nb; float* dbias;  // optional
 };
 hipError_t launch_router_reduce(int dt, const RouterReduceArgs& a, hipStream_t s);
+
+// dx = gathered dX_perm rows (+ dx_shared) + router input gradient
+struct UnpermuteArgs {
+  const void* dx_perm;     // [T*k, d]
+  const int32_t* inv;      // [T, k]
+  const void* dx_shared;   // [T, d] or nullptr
+  const float* dxr;        // [T, d] f32 router part, or nullptr: computed from dz_hl and w_router
+  const void* dz_hl;       // [T, 2*Ep]
+  const void* w_router;    // [E, d]
+  void* dx;                // [T, d]
+  int64_t T; int d, k, E, Ep;
+};
+hipError_t launch_unpermute(int dt, const UnpermuteArgs& a, hipStream_t s);
+constexpr int kRouterDxVectorMaxE = 32;   // up to this many experts the router part of dx is computed inline
 
 // Mirror of moe_aux_scalars (include/moe.h); the host checks the layouts match.
 struct moe_aux_out {
