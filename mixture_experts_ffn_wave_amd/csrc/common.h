@@ -51,6 +51,35 @@ template <> __device__ __forceinline__ void load4<float>(const float* p, float* 
   out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
 }
 
+// 8 consecutive elements of T: one 16-byte access for 16-bit T, two for f32.
+template <typename T> __device__ __forceinline__ void store8(T* p, const float* v) {
+  if constexpr (sizeof(T) == 2) {
+    union { u32x4 raw; T e[8]; } u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) u.e[i] = from_f32<T>(v[i]);
+    st16(p, u.raw);
+  } else {
+    store4<float>(p, v[0], v[1], v[2], v[3]);
+    store4<float>(p + 4, v[4], v[5], v[6], v[7]);
+  }
+}
+template <typename T> __device__ __forceinline__ void unpack8(u32x4 raw, float* out) {
+  static_assert(sizeof(T) == 2, "8 elements per 16 bytes");
+  union { u32x4 raw; T e[8]; } u;
+  u.raw = raw;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out[i] = to_f32<T>(u.e[i]);
+}
+// RUN (4 or 8) consecutive elements
+template <typename T, int RUN> __device__ __forceinline__ void store_run(T* p, const float* v) {
+  if constexpr (RUN == 8) store8<T>(p, v);
+  else store4<T>(p, v[0], v[1], v[2], v[3]);
+}
+template <typename T, int RUN> __device__ __forceinline__ void load_run(const T* p, float* out) {
+  if constexpr (RUN == 8) unpack8<T>(ld16(p), out);
+  else load4<T>(p, out);
+}
+
 // ---- MFMA 32x32 step over 16 values of k -------------------------------
 // Lane l supplies operand row (l % 32) and the 8 consecutive k values starting
 // at 8 * (l / 32); `a` and `b` each hold those 8 values as raw 16-byte chunks

@@ -12,28 +12,25 @@
 //
 // Tiles.  A workgroup of 4 waves (2 x 2) computes a BM x BN output tile; each
 // wave a (BM/2) x (BN/2) quadrant made of 32x32 MFMA tiles (32x32x16 for
-// bf16/f16, eight 32x32x2 steps for f32).  16-bit types use 256 x 256 tiles
-// (128 x 128 per wave: 16 accumulators of 16 registers), which stage 128
-// FLOP per byte of operand -- twice the per-CU operand bandwidth a 128 x 128
-// tile needs; the plan picks 128 x 128 where a dimension is not a multiple of
-// 256 or segments are short.  K is staged 128 bytes at a time through a
-// double-buffered LDS ring: global loads for chunk c+1 are in flight while the
-// MFMAs of chunk c run, one barrier per chunk.
+// bf16/f16, eight 32x32x2 steps for f32).  Kernels exist for 128 x 128 and
+// (16-bit) 256 x 256 tiles; the plan picks per GEMM.
 //
-// Operand layouts in LDS.  An operand whose rows are contiguous along K is
-// stored [row][k] (row stride 144 bytes: conflict-free ds_read_b128).  An
-// operand that arrives k-major (weights read transposed, token-major operands
-// of the weight gradients) is stored as it comes, [k][row] with a 64-byte row
-// pad, and turned into MFMA fragments by ds_read_b64_tr_b16: within each
-// 16-lane group, lane i receives element i%4 of the 8-byte chunks addressed by
-// lanes 4q+i/4 (q = 0..3), so pointing lane j at (k0 + j/4, r0 + 4(j%4))
-// hands lane i the four k values of row r0 + i.  (f32 operands are transposed
-// in registers instead.)
+// 16-bit main loop.  Operands go from global memory straight into LDS
+// (buffer_load ... lds) through a 4-stage ring of 64-byte k chunks, so loads
+// run three chunks ahead of the MFMAs with one barrier per chunk.  Operands
+// whose rows are contiguous along K are stored [row][k]; operands that arrive
+// k-major (weights read transposed, both operands of the weight gradients)
+// are stored [k][row] and turned into MFMA fragments by ds_read_b64_tr_b16.
+// Both layouts are XOR-swizzled at 16-byte granularity (no padding, no bank
+// conflicts on the fragment reads).  f32 operands are staged through
+// registers into padded LDS tiles, double buffered.
 //
 // MFMA operand roles: the weight-side tile feeds the MFMA "A" operand and the
-// token-side tile the "B" operand, so each lane holds 4 consecutive output
-// columns of one token row -- one 8-byte (16-bit) or 16-byte (f32) store.
-//
+// token-side tile the "B" operand, so each lane holds output columns of one
+// token row.  On the 16-bit path the A rows are read in a permuted order that
+// leaves 8 consecutive columns in each run of 8 accumulator registers: every
+// epilogue store is 16 bytes.
+
 // Every workgroup works out its own tile from the offsets array (a prefix sum
 // over at most 256 segments), and workgroup ids are remapped so that each of
 // the 8 XCDs (separate L2 caches; ids are handed out round-robin over them)
@@ -147,7 +144,9 @@ struct Operand {
   }
 
   // -- MFMA fragment: rows row0 .. row0+31, k16 step ks of the chunk --
+  template <bool PERM>
   __device__ __forceinline__ static void frag(u32x4 (&f)[CH], const char* lds, int row0, int ks, int lane) {
+    static_assert(!PERM, "the register-staged path keeps the natural row order");
     if constexpr (HWTR) {
       const int g = lane >> 4, i = lane & 15;
       const int k = ks * 16 + 8 * (g >> 1) + (i >> 2);
@@ -165,9 +164,24 @@ struct Operand {
   }
 };
 
+// Row order of the weight-side ("A") fragments on the direct-load path: MFMA
+// row i reads tile row perm_row(i) (bits 2 and 3 of i swapped).  The 32x32
+// accumulator then holds, in registers 8t .. 8t+7 of lane l, the 8 consecutive
+// output columns 16t + 8 (l / 32) + 0..7 of token row l % 32 -- one 16-byte
+// store per 8 values instead of two 8-byte ones.
+__device__ __forceinline__ int perm_row(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+
+// Output column (within a 32-column subtile) of accumulator register r of a
+// lane in half h = lane / 32.
+template <bool PERM>
+__device__ __forceinline__ constexpr int acc_col(int r, int h) {
+  return PERM ? 16 * (r >> 3) + 8 * h + (r & 7) : 8 * (r >> 2) + 4 * h + (r & 3);
+}
+
 // MFMA work of one chunk for a wave: NS weight-side subtiles (LDS rows
 // qrow[ns]) x MS token-side subtiles (LDS rows prow[ms]).
-template <typename T, typename PO, typename QO, int NS, int MS, int KSTEPS = KB / sizeof(T) / 16>
+template <typename T, typename PO, typename QO, int NS, int MS, int KSTEPS = KB / sizeof(T) / 16,
+          bool PERM = false>
 __device__ __forceinline__ void mfma_chunk(f32x16 (&acc)[NS][MS], const char* lq, const char* lp,
                                            const int (&qrow)[NS], const int (&prow)[MS], int lane) {
   constexpr int CH = Mma32<T>::kChunks;
@@ -175,9 +189,9 @@ __device__ __forceinline__ void mfma_chunk(f32x16 (&acc)[NS][MS], const char* lq
   for (int ks = 0; ks < KSTEPS; ++ks) {
     u32x4 fa[NS][CH], fb[MS][CH];
 #pragma unroll
-    for (int ns = 0; ns < NS; ++ns) QO::frag(fa[ns], lq, qrow[ns], ks, lane);
+    for (int ns = 0; ns < NS; ++ns) QO::template frag<PERM>(fa[ns], lq, qrow[ns], ks, lane);
 #pragma unroll
-    for (int ms = 0; ms < MS; ++ms) PO::frag(fb[ms], lp, prow[ms], ks, lane);
+    for (int ms = 0; ms < MS; ++ms) PO::template frag<false>(fb[ms], lp, prow[ms], ks, lane);
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
@@ -203,9 +217,9 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[NS][MS]) {
 // count read as zero (masked rows and tokens cost no branch).  Tiles are
 // unpadded and XOR-swizzled at 16-byte granularity so the fragment reads are
 // free of bank conflicts:
-//   [row][k] tiles (128-byte rows): chunk c of row r sits at c ^ ((r >> 1) & 7)
+//   [row][k] tiles (64-byte rows): chunk c of row r sits at c ^ ((r >> 2) & 3)
 //   [k][row] tiles: chunk c of k-row k sits at c ^ (4 (k & 3))
-// Each wave issues ROWS/32 loads per operand per K chunk.
+// Each wave issues ROWS/64 loads per operand per 64-byte K chunk.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
 
@@ -238,8 +252,9 @@ struct DmaRows {                                   // [row][k], DKB bytes per ro
   __device__ __forceinline__ static int row_of(int w, int s, int lane) { return RPI * (w + 4 * s) + lane / CPRW; }
   __device__ __forceinline__ static int gchunk(int row, int lane) { return (lane % CPRW) ^ swz(row); }
   __device__ __forceinline__ static int lds_off(int w, int s) { return RPI * (w + 4 * s) * DKB; }
+  template <bool PERM>
   __device__ __forceinline__ static void frag(u32x4 (&f)[1], const char* lds, int row0, int ks, int lane) {
-    const int r = row0 + (lane & 31);
+    const int r = row0 + (PERM ? perm_row(lane & 31) : (lane & 31));
     const int c = ks * 2 + (lane >> 5);
     f[0] = ld16(lds + r * DKB + ((c ^ swz(r)) << 4));
   }
@@ -257,10 +272,13 @@ struct DmaKmajor {                                 // [k][row], DKB/2 k-rows per
   __device__ __forceinline__ static int k_of(int w, int s, int lane) { return KPI * (w + 4 * s) + lane / CPR; }
   __device__ __forceinline__ static int gchunk(int k, int lane) { return (lane % CPR) ^ (4 * (k & 3)); }
   __device__ __forceinline__ static int lds_off(int w, int s) { return KPI * (w + 4 * s) * RB; }
+  template <bool PERM>
   __device__ __forceinline__ static void frag(u32x4 (&f)[1], const char* lds, int row0, int ks, int lane) {
     const int g = lane >> 4, i = lane & 15;
     const int k = ks * 16 + 8 * (g >> 1) + (i >> 2);
-    const int row = row0 + 16 * (g & 1) + 4 * (i & 3);
+    // this lane addresses the 4-row block that MFMA rows 16 (g & 1) + 4 (i & 3) + 0..3 receive
+    const int rb = 16 * (g & 1) + 4 * (i & 3);
+    const int row = row0 + (PERM ? perm_row(rb) : rb);
     const char* p = lds + k * RB + (((row >> 3) ^ (4 * (k & 3))) << 4) + (row & 7) * 2;
     const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(p));
     const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(p + 4 * RB));
@@ -355,6 +373,38 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
   zero_acc(acc);
   const int nk = a.K / BK;
 
+  // Accumulator register layout: runs of RUN consecutive output columns, run t
+  // starting at column RSTEP*t + RUN*(lane/32) of a 32-column subtile.
+  constexpr bool PERM = (ES == 2);
+  constexpr int RUN = PERM ? 8 : 4, NRUN = 16 / RUN, RSTEP = PERM ? 16 : 8;
+  static_assert(acc_col<PERM>(RUN, 0) == RSTEP && acc_col<PERM>(0, 1) == RUN, "run layout");
+  const int h = lane >> 5;
+
+  // SwiGLU backward needs the saved G and U of each output element.  With at
+  // most 4 accumulators per wave they are loaded here, before the main loop,
+  // so that the loads' latency hides behind it (the first ring barrier, which
+  // waits for the older loads too, is where they are complete).
+  constexpr bool PRE = (EPI == EPI_SWIGLU_BWD) && PERM && MS * NS <= 4;
+  u32x4 gpre[PRE ? MS : 1][PRE ? NS : 1][NRUN], upre[PRE ? MS : 1][PRE ? NS : 1][NRUN];
+  if constexpr (PRE) {
+    const T* aux = static_cast<const T*>(a.aux);
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+      const int ml = prow[ms] + (lane & 31);
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+        for (int t = 0; t < NRUN; ++t) {
+          const int n = n0 + qrow[ns] + RSTEP * t + RUN * h;
+          const int blk = n / a.sub;
+          const int gcol = blk * 2 * a.sub + (n - blk * a.sub);
+          const T* gu = aux + (row0 + ml) * a.ldaux + gcol;
+          gpre[ms][ns][t] = (ml < rows) ? ld16(gu) : (u32x4){0u, 0u, 0u, 0u};
+          upre[ms][ns][t] = (ml < rows) ? ld16(gu + a.sub) : (u32x4){0u, 0u, 0u, 0u};
+        }
+    }
+  }
+
   if constexpr (ES == 2) {
     // ---------------- direct-to-LDS main loop (16-bit types)
     using PD = DmaRows<BM>;
@@ -429,7 +479,7 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
       ring_barrier<LPC>(nkd - 1 - kc);                // chunk kc landed everywhere; kc-1 consumed
       if (kc + NSTG - 1 < nkd) issue((kc + NSTG - 1) * DBKE, smem + ((kc + NSTG - 1) % NSTG) * DSTAGE);
       const char* buf = smem + (kc % NSTG) * DSTAGE;
-      mfma_chunk<T, PD, QD, NS, MS, DKB / 32>(acc, buf + PD::BYTES, buf, qrow, prow, lane);
+      mfma_chunk<T, PD, QD, NS, MS, DKB / 32, true>(acc, buf + PD::BYTES, buf, qrow, prow, lane);
     }
   } else {
   // ---------------- register-staged main loop (f32)
@@ -504,64 +554,70 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
   }
   }  // main loops
 
-  // ---- epilogue: lane holds columns qrow[ns] + 8*rq + 4*(lane/32) + 0..3 of row prow[ms] + lane%32
+  // ---- epilogue: accumulator [ns][ms] holds row prow[ms] + lane%32 of the tile
 #pragma unroll
   for (int ms = 0; ms < MS; ++ms) {
     const int ml = prow[ms] + (lane & 31);
     if (ml >= rows) continue;
     const int64_t row = row0 + ml;
+    if constexpr (EPI == EPI_SWIGLU_FWD) {
+      // gate subtile j pairs with up subtile j + NS/2 (same H columns)
 #pragma unroll
-    for (int rq4 = 0; rq4 < 4; ++rq4) {
-      const int nl = 8 * rq4 + 4 * (lane >> 5);
-      if constexpr (EPI == EPI_SWIGLU_FWD) {
+      for (int j = 0; j < NS / 2; ++j)
 #pragma unroll
-        for (int j = 0; j < NS / 2; ++j) {
-          const int hc = n0 + wn * (BN / 4) + j * 32 + nl;
+        for (int t = 0; t < NRUN; ++t) {
+          const int hc = n0 + wn * (BN / 4) + j * 32 + RSTEP * t + RUN * h;
           const int blk = hc / a.sub;
           const int gcol = blk * 2 * a.sub + (hc - blk * a.sub);
-          float gv[4], uv[4], hv[4];
+          float gv[RUN], uv[RUN], hv[RUN];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            gv[i] = acc[j][ms][4 * rq4 + i];
-            uv[i] = acc[j + NS / 2][ms][4 * rq4 + i];
+          for (int i = 0; i < RUN; ++i) {
+            gv[i] = acc[j][ms][RUN * t + i];
+            uv[i] = acc[j + NS / 2][ms][RUN * t + i];
             hv[i] = silu_f(gv[i]) * uv[i];
           }
           T* gu = static_cast<T*>(a.C) + row * a.ldc;
-          store4<T>(gu + gcol, gv[0], gv[1], gv[2], gv[3]);
-          store4<T>(gu + gcol + a.sub, uv[0], uv[1], uv[2], uv[3]);
-          store4<T>(static_cast<T*>(a.C2) + row * a.ldc2 + hc, hv[0], hv[1], hv[2], hv[3]);
+          store_run<T, RUN>(gu + gcol, gv);
+          store_run<T, RUN>(gu + gcol + a.sub, uv);
+          store_run<T, RUN>(static_cast<T*>(a.C2) + row * a.ldc2 + hc, hv);
         }
-      } else {
+    } else {
 #pragma unroll
-        for (int ns = 0; ns < NS; ++ns) {
-          const int n = n0 + qrow[ns] + nl;
-          float v[4];
+      for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = acc[ns][ms][4 * rq4 + i];
+        for (int t = 0; t < NRUN; ++t) {
+          const int n = n0 + qrow[ns] + RSTEP * t + RUN * h;
+          float v[RUN];
+#pragma unroll
+          for (int i = 0; i < RUN; ++i) v[i] = acc[ns][ms][RUN * t + i];
           if constexpr (EPI == EPI_STORE) {
-            store4<T>(static_cast<T*>(a.C) + row * a.ldc + n, v[0], v[1], v[2], v[3]);
+            store_run<T, RUN>(static_cast<T*>(a.C) + row * a.ldc + n, v);
           } else if constexpr (EPI == EPI_STORE_F32) {
-            store4<float>(static_cast<float*>(a.C) + row * a.ldc + n, v[0], v[1], v[2], v[3]);
+            store_run<float, RUN>(static_cast<float*>(a.C) + row * a.ldc + n, v);
           } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-            // v = dH for H column n; G, U saved in the packed [G | U] layout
+            // v = dH for H columns n..; G, U saved in the packed [G | U] layout
             const int blk = n / a.sub;
             const int gcol = blk * 2 * a.sub + (n - blk * a.sub);
-            const T* gu = static_cast<const T*>(a.aux) + row * a.ldaux;
-            float G[4], U[4], dG[4], dU[4];
-            load4<T>(gu + gcol, G);
-            load4<T>(gu + gcol + a.sub, U);
+            float G[RUN], U[RUN], dG[RUN], dU[RUN];
+            if constexpr (PRE) {
+              unpack8<T>(gpre[ms][ns][t], G);
+              unpack8<T>(upre[ms][ns][t], U);
+            } else {
+              const T* gu = static_cast<const T*>(a.aux) + row * a.ldaux;
+              load_run<T, RUN>(gu + gcol, G);
+              load_run<T, RUN>(gu + gcol + a.sub, U);
+            }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < RUN; ++i) {
               const float sg = sigmoid_f(G[i]);
               dG[i] = v[i] * U[i] * sg * (1.0f + G[i] * (1.0f - sg));
               dU[i] = v[i] * G[i] * sg;
             }
             T* dgu = static_cast<T*>(a.C) + row * a.ldc;
-            store4<T>(dgu + gcol, dG[0], dG[1], dG[2], dG[3]);
-            store4<T>(dgu + gcol + a.sub, dU[0], dU[1], dU[2], dU[3]);
+            store_run<T, RUN>(dgu + gcol, dG);
+            store_run<T, RUN>(dgu + gcol + a.sub, dU);
           }
         }
-      }
     }
   }
 }
@@ -644,7 +700,7 @@ __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
       ring_barrier<LPC>(nkd - 1 - kc);
       if (kc + NSTG - 1 < nkd) issue(kbeg + (int64_t)(kc + NSTG - 1) * DBKK, smem + ((kc + NSTG - 1) % NSTG) * DSTAGE);
       const char* buf = smem + (kc % NSTG) * DSTAGE;
-      mfma_chunk<T, PD, QD, NS, MS, DKB / 32>(acc, buf + PD::BYTES, buf, qrow, prow, lane);
+      mfma_chunk<T, PD, QD, NS, MS, DKB / 32, true>(acc, buf + PD::BYTES, buf, qrow, prow, lane);
     }
   } else {
   auto load = [&](int64_t kc, PO& po, QO& qo) {
@@ -675,28 +731,32 @@ __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
   }  // main loops
 
   // out[m][n] at C + g*cgs + sp*css + (n/sub)*(M*sub) + m*sub + n%sub
+  constexpr bool PERM = (ES == 2);
+  constexpr int RUN = PERM ? 8 : 4, NRUN = 16 / RUN, RSTEP = PERM ? 16 : 8;
+  const int h = lane >> 5;
 #pragma unroll
   for (int ms = 0; ms < MS; ++ms) {
     const int64_t m = m0 + prow[ms] + (lane & 31);
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) {
 #pragma unroll
-      for (int rq4 = 0; rq4 < 4; ++rq4) {
-        const int n = n0 + qrow[ns] + 8 * rq4 + 4 * (lane >> 5);
+      for (int t = 0; t < NRUN; ++t) {
+        const int n = n0 + qrow[ns] + RSTEP * t + RUN * h;
         const int blk = n / a.sub;
         const int64_t off = (int64_t)g * a.c_group_stride + (int64_t)sp * a.c_split_stride +
                             ((int64_t)blk * a.M + m) * a.sub + (n - blk * a.sub);
-        const float v0 = acc[ns][ms][4 * rq4 + 0], v1 = acc[ns][ms][4 * rq4 + 1];
-        const float v2 = acc[ns][ms][4 * rq4 + 2], v3 = acc[ns][ms][4 * rq4 + 3];
-        if constexpr (OUT_F32) store4<float>(static_cast<float*>(a.C) + off, v0, v1, v2, v3);
-        else store4<T>(static_cast<T*>(a.C) + off, v0, v1, v2, v3);
+        float v[RUN];
+#pragma unroll
+        for (int i = 0; i < RUN; ++i) v[i] = acc[ns][ms][RUN * t + i];
+        if constexpr (OUT_F32) store_run<float, RUN>(static_cast<float*>(a.C) + off, v);
+        else store_run<T, RUN>(static_cast<T*>(a.C) + off, v);
       }
     }
   }
 }
 
-// Dynamic LDS of one kernel: two stages of the larger operand pair, plus the
-// schedule scratch of the row GEMMs.
+// Dynamic LDS of one kernel: the 4-stage ring (16-bit) or two stages of the
+// larger operand pair (f32), plus the schedule scratch of the row GEMMs.
 template <typename T, int BM, int BN>
 constexpr size_t smem_for() {
   if constexpr (sizeof(T) == 2) {
@@ -733,8 +793,9 @@ constexpr size_t smem_for() {
   MOE_ROW_KERNEL(moe_gemm_down_dgrad_swiglu_##TN##_##BM##x##BN, T, BM, BN, OP_DOWN_DGRAD, EPI_SWIGLU_BWD)  \
   MOE_ROW_KERNEL(moe_gemm_gate_up_dgrad_##TN##_##BM##x##BN, T, BM, BN, OP_GU_DGRAD, EPI_STORE)             \
   MOE_ROW_KERNEL(moe_gemm_router_dx_f32out_##TN##_##BM##x##BN, T, BM, BN, OP_ROUTER_DX, EPI_STORE_F32)     \
-  MOE_WGRAD_KERNEL(moe_wgrad_##TN##_##BM##x##BN, T, BM, BN, 0)                                             \
-  MOE_WGRAD_KERNEL(moe_wgrad_f32out_##TN##_##BM##x##BN, T, BM, BN, 1)
+  MOE_WGRAD_KERNEL(moe_wgrad_down_##TN##_##BM##x##BN, T, BM, BN, 0)                                        \
+  MOE_WGRAD_KERNEL(moe_wgrad_gate_up_##TN##_##BM##x##BN, T, BM, BN, 0)                                     \
+  MOE_WGRAD_KERNEL(moe_wgrad_router_f32out_##TN##_##BM##x##BN, T, BM, BN, 1)
 
 MOE_KERNEL_SET(__bf16, bf16, 256, 256)
 MOE_KERNEL_SET(__bf16, bf16, 128, 128)
@@ -749,7 +810,7 @@ typedef void (*WgradKernel)(WgradArgs);
 
 struct KernelSet {
   RowKernel gu, down, down_f32, down_dgrad, gu_dgrad, router_dx_f32;
-  WgradKernel wgrad, wgrad_f32;
+  WgradKernel wgrad_down, wgrad_gate_up, wgrad_router_f32;
   size_t lds;
 };
 
@@ -757,7 +818,8 @@ struct KernelSet {
   KernelSet{moe_gemm_gate_up_swiglu_##TN##_##BM##x##BN, moe_gemm_down_##TN##_##BM##x##BN,               \
             moe_gemm_down_f32out_##TN##_##BM##x##BN, moe_gemm_down_dgrad_swiglu_##TN##_##BM##x##BN,     \
             moe_gemm_gate_up_dgrad_##TN##_##BM##x##BN, moe_gemm_router_dx_f32out_##TN##_##BM##x##BN,       \
-            moe_wgrad_##TN##_##BM##x##BN, moe_wgrad_f32out_##TN##_##BM##x##BN, smem_for<T, BM, BN>()}
+            moe_wgrad_down_##TN##_##BM##x##BN, moe_wgrad_gate_up_##TN##_##BM##x##BN,                      \
+            moe_wgrad_router_f32out_##TN##_##BM##x##BN, smem_for<T, BM, BN>()}
 
 const KernelSet* kernel_set(int dt, int tile) {
   static const KernelSet bf16_256 = MOE_KERNEL_TABLE(__bf16, bf16, 256, 256);
@@ -812,15 +874,22 @@ hipError_t launch_row_gemm(int dt, int op, int epi, int tile, const RowGemmArgs&
   return hipGetLastError();
 }
 
-hipError_t launch_wgrad(int dt, int tile, const WgradArgs& a, hipStream_t s) {
+hipError_t launch_wgrad(int dt, int op, int tile, const WgradArgs& a, hipStream_t s) {
   const KernelSet* set = kernel_set(dt, tile);
   if (!set) return hipErrorInvalidValue;
+  WgradKernel k = nullptr;
+  switch (op) {
+    case WG_DOWN: k = set->wgrad_down; break;
+    case WG_GATE_UP: k = set->wgrad_gate_up; break;
+    case WG_ROUTER: k = set->wgrad_router_f32; break;
+    default: return hipErrorInvalidValue;
+  }
+  if ((op == WG_ROUTER) != (a.out_f32 != 0)) return hipErrorInvalidValue;
   if (a.M % tile || a.N % tile) return hipErrorInvalidValue;
   int64_t grid = (int64_t)a.G * a.splits * (a.M / tile) * (a.N / tile);
   grid = (grid + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  WgradKernel k = a.out_f32 ? set->wgrad_f32 : set->wgrad;
   hipError_t e = prepare((const void*)k, set->lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(NT), set->lds, s, a);

@@ -79,7 +79,9 @@ struct WgradArgs {
   int sub;
   int out_f32;                     // 1: write f32 partials, 0: write act dtype
 };
-hipError_t launch_wgrad(int dt, int tile, const WgradArgs& a, hipStream_t s);
+// One kernel symbol per weight gradient (same tile engine) so profiles tell them apart.
+enum WgradOp { WG_DOWN = 0, WG_GATE_UP = 1, WG_ROUTER = 2 };
+hipError_t launch_wgrad(int dt, int op, int tile, const WgradArgs& a, hipStream_t s);
 
 // ------------------------------------------------------ element-wise --
 struct CombineArgs {
