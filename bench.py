@@ -8,15 +8,24 @@ Inputs are resident in HBM before the timed region starts.
 Prints ONE JSON line (rank 0, N = 1): tokens/s over K timed steps, plus
   roofline      -- the dominant kernel's algorithmic FLOPs per launch over its
                    average launch time (hipEvents recorded around that kernel
-                   inside the timed region), against the bf16 MFMA peak;
+                   inside the timed region), against the bf16 MFMA peak, and
+                   its measured HBM bytes per launch ("traffic") when a
+                   counter summary of the current kernel sources exists under
+                   profiles/ (else null);
   cpu_baseline  -- the fp64 numpy oracle timed on the host on a bounded
                    sample of the same workload.
 Per-kernel times go to stderr.
+
+--traffic-calibration runs only a plain streaming kernel of known size (an
+elementwise negation over 1 GiB of float32: 1 GiB read, 1 GiB written), the
+reference that scales the FETCH_SIZE / WRITE_SIZE counters to bytes.
 """
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -77,6 +86,61 @@ def make_layer(wl, device="cuda"):
     return layer, dev
 
 
+# probe name of a GEMM launch -> prefix of its kernel symbol (dtype and tile follow)
+KERNEL_SYMBOL = {
+    "gemm_gate_up_swiglu": "moe_gemm_gate_up_swiglu",
+    "gemm_down": "moe_gemm_down_f32out",
+    "gemm_down_dgrad_swiglu": "moe_gemm_down_dgrad_swiglu",
+    "gemm_gate_up_dgrad": "moe_gemm_gate_up_dgrad",
+    "gemm_wgrad_down": "moe_wgrad_down",
+    "gemm_wgrad_gate_up": "moe_wgrad_gate_up",
+    "gemm_router_dx": "moe_gemm_router_dx_f32out",
+    "gemm_wgrad_router": "moe_wgrad_router_f32out",
+}
+CALIBRATION_BYTES = 1 << 30
+
+
+def kernel_source_hash():
+    """sha256 over the HIP/C++ sources, in name order: counter summaries taken
+    from other sources do not describe the kernels that run now."""
+    d = os.path.join(ROOT, "mixture_experts_ffn_wave_amd", "csrc")
+    h = hashlib.sha256()
+    for n in sorted(os.listdir(d)):
+        if n.endswith((".hip", ".cpp", ".h")):
+            h.update(n.encode())
+            with open(os.path.join(d, n), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_per_launch(wl, probe_name):
+    """HBM bytes per launch of one kernel from profiles/traffic_<workload>.md,
+    or None (no summary, other sources, or no unique kernel row)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.md")
+    sym = KERNEL_SYMBOL.get(probe_name)
+    if sym is None or not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source sha256: `([0-9a-f]{64})`", text)
+    if not m or m.group(1) != kernel_source_hash():
+        return None
+    pat = re.compile(r"^\| `(" + re.escape(sym) + r"_" + wl.dtype + r"_\d+x\d+)` \|[^|]*\|[^|]*\|[^|]*\| *([0-9.]+) *\|",
+                     re.M)
+    rows = pat.findall(text)
+    return float(rows[0][1]) if len(rows) == 1 else None
+
+
+def traffic_calibration():
+    n = CALIBRATION_BYTES // 4
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "neg", "bytes_read": CALIBRATION_BYTES, "bytes_written": CALIBRATION_BYTES}),
+          flush=True)
+
+
 def per_kernel_times(layer, dy, names, steps=3):
     """Average launch time (ms) of every kernel, one probe pass per name."""
     from mixture_experts_ffn_wave_amd import probe_enable, probe_read
@@ -128,11 +192,15 @@ def main():
     ap.add_argument("--workload", default=MI.BENCH)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--traffic-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (no collectives, no sharding); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.traffic_calibration:
+        traffic_calibration()
+        return
     wl = MI.WORKLOADS[args.workload]
     torch.cuda.init()
     layer, dev = make_layer(wl)
@@ -190,7 +258,7 @@ def main():
                    "d_ff": wl.I, "shared": f"{wl.n_shared}x{wl.I_shared}", "renorm": wl.renorm,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "kernel": dominant, "achieved": achieved, "peak": peak,
-                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic_per_launch(wl, dominant),
                      "avg_launch_us": avg_ms * 1e3, "launches": launches},
     }
     if gemms:
