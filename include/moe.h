@@ -85,7 +85,11 @@ typedef struct {
 typedef struct moe_plan_s* moe_plan;
 
 /* Validate `cfg` and build a plan (host memory only; selects every kernel
- * variant once).  *out is set to NULL on failure. */
+ * variant once).  *out is set to NULL on failure.  The GEMM tile sizes may be
+ * forced for tuning with the environment variables MOE_ROW_TILE and
+ * MOE_WGRAD_TILE (128 or 256), read here; a value the shape does not allow
+ * is ignored.  Results do not depend on the tile size beyond f32 rounding
+ * order within a tile's K loop, which is the same for both sizes. */
 moe_status moe_plan_create(const moe_config* cfg, moe_plan* out);
 void moe_plan_destroy(moe_plan plan);
 /* Bytes of device workspace the compute calls need (same for all calls). */

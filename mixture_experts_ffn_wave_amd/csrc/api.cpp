@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -96,21 +97,32 @@ moe_status check_ws(moe_plan p, void* ws, size_t ws_bytes) {
 
 constexpr int kCUs = 256;
 
-// Row GEMMs use 128 x 128 tiles: two workgroups share a CU, so one's barrier
-// and epilogue stalls overlap the other's MFMAs, and on the 16384-token,
-// 8-expert bf16 layer every row GEMM ran 10-25 % faster than with 256 x 256
-// (which holds one workgroup per CU and spills accumulator registers).
-int choose_row_tile(int dt, double segs, double rows_per_seg, int ncols, int ktot, int block_align) {
-  (void)dt; (void)segs; (void)rows_per_seg; (void)ncols; (void)ktot; (void)block_align;
-  return 128;
+// Tile override for tuning and tests: MOE_ROW_TILE / MOE_WGRAD_TILE = 128 or
+// 256, read once per plan; any other value, or a shape the tile does not
+// divide, keeps the default choice.
+int env_tile(const char* name) {
+  const char* v = std::getenv(name);
+  if (!v) return 0;
+  const int t = std::atoi(v);
+  return (t == 128 || t == 256) ? t : 0;
+}
+
+// Row GEMMs: 128 x 128 tiles by default (4 waves, two workgroups per CU);
+// 256 x 256 (8 waves, one workgroup per CU) where the shape allows.
+constexpr int kRowTile = 128;
+int choose_row_tile(int dt, int ncols, int block_align, int override_tile) {
+  if (dt == DT_F32) return 128;
+  if (ncols % 256 || block_align % 256) return 128;
+  return override_tile ? override_tile : kRowTile;
 }
 // Weight-gradient GEMMs: 256 x 256 stages twice the FLOP per operand byte of
 // 128 x 128 but yields a quarter of the workgroups; estimated time = rounds of
 // workgroups over the CUs x the time of one tile, the smaller tile costed at
 // about 0.55 of the larger one's rate.
-int choose_wgrad_tile(int dt, double segs, int M, int N, double ktok) {
+int choose_wgrad_tile(int dt, double segs, int M, int N, double ktok, int override_tile) {
   if (dt == DT_F32) return 128;
   if (M % 256 || N % 256) return 128;
+  if (override_tile) return override_tile;
   const double w256 = segs * (M / 256) * (N / 256), w128 = segs * (M / 128) * (N / 128);
   const double c256 = ((w256 + kCUs - 1) / kCUs) * 256.0 * 256.0 * ktok;
   const double c128 = ((w128 + kCUs - 1) / kCUs) * 128.0 * 128.0 * ktok / 0.55;
@@ -192,23 +204,24 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
   {
     const double E = p->E, A = (double)A_, T = (double)c.T;
     const double rps = E > 0 ? A / E : 0;               // rows per expert if balanced
+    const int rt = env_tile("MOE_ROW_TILE"), wt = env_tile("MOE_WGRAD_TILE");
     const int d = p->d, I = p->I, NI = p->Ns * p->Is;
     // gate/up: output columns are 2I packed, tile columns pair gate/up halves (needs I % (tile/2))
-    p->t_gu = choose_row_tile(p->dt, E, rps, 2 * I, d, 2 * I);
-    p->t_down = choose_row_tile(p->dt, E, rps, d, I, 256);
-    p->t_down_dgrad = choose_row_tile(p->dt, E, rps, I, d, I);
-    p->t_gu_dgrad = choose_row_tile(p->dt, E, rps, d, 2 * I, 256);
+    p->t_gu = choose_row_tile(p->dt, 2 * I, 2 * I, rt);
+    p->t_down = choose_row_tile(p->dt, d, 256, rt);
+    p->t_down_dgrad = choose_row_tile(p->dt, I, I, rt);
+    p->t_gu_dgrad = choose_row_tile(p->dt, d, 256, rt);
     p->t_router_dx = 128;                                 // K = 2 Ep is tiny
-    p->t_wg_down = choose_wgrad_tile(p->dt, E, d, I, rps);
-    p->t_wg_gu = choose_wgrad_tile(p->dt, E, 2 * I, d, rps);
+    p->t_wg_down = choose_wgrad_tile(p->dt, E, d, I, rps, wt);
+    p->t_wg_gu = choose_wgrad_tile(p->dt, E, 2 * I, d, rps, wt);
     p->t_wg_router = 128;
     if (p->Ns > 0) {
-      p->t_gu_s = choose_row_tile(p->dt, 1, T, 2 * NI, d, 2 * p->Is);
-      p->t_down_s = choose_row_tile(p->dt, 1, T, d, NI, 256);
-      p->t_down_dgrad_s = choose_row_tile(p->dt, 1, T, NI, d, p->Is);
-      p->t_gu_dgrad_s = choose_row_tile(p->dt, 1, T, d, 2 * NI, 256);
-      p->t_wg_down_s = (p->Is % 256 == 0) ? choose_wgrad_tile(p->dt, 1, d, NI, T) : 128;
-      p->t_wg_gu_s = choose_wgrad_tile(p->dt, 1, 2 * NI, d, T);
+      p->t_gu_s = choose_row_tile(p->dt, 2 * NI, 2 * p->Is, rt);
+      p->t_down_s = choose_row_tile(p->dt, d, 256, rt);
+      p->t_down_dgrad_s = choose_row_tile(p->dt, NI, p->Is, rt);
+      p->t_gu_dgrad_s = choose_row_tile(p->dt, d, 256, rt);
+      p->t_wg_down_s = (p->Is % 256 == 0) ? choose_wgrad_tile(p->dt, 1, d, NI, T, wt) : 128;
+      p->t_wg_gu_s = choose_wgrad_tile(p->dt, 1, 2 * NI, d, T, wt);
     } else {
       p->t_gu_s = p->t_down_s = p->t_down_dgrad_s = p->t_gu_dgrad_s = p->t_wg_down_s = p->t_wg_gu_s = 128;
     }

@@ -46,7 +46,7 @@
 namespace moe {
 namespace {
 
-constexpr int NT = 256;          // threads per workgroup (4 waves)
+constexpr int NT = 256;          // threads of the register-staged (f32) path: 4 waves
 constexpr int KB = 128;          // bytes of k staged per chunk
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -82,6 +82,7 @@ struct Operand {
   static_assert(HWTR || !TR || NCG * KG == NT * NREG / 4, "f32 transposed tile geometry");
 
   u32x4 r[NREG];
+  static constexpr bool kRawLds = false;
 
   // -- loads, normal layout: row pointers are precomputed by the caller --
   // chunk c = tid + NT*s holds row c/8, 16-byte column c%8
@@ -178,20 +179,92 @@ __device__ __forceinline__ constexpr int acc_col(int r, int h) {
   return PERM ? 16 * (r >> 3) + 8 * h + (r & 7) : 8 * (r >> 2) + 4 * h + (r & 3);
 }
 
+// N fragments' worth of ds_read_b64_tr_b16 (two per fragment, at the given
+// LDS addresses) and the wait for them, in one assembly block: the results
+// are complete when the block ends, so no use or copy of them can be
+// scheduled before the data has arrived.
+template <int N> struct TrRead;
+#define MOE_TR8(o, a) "ds_read_b64_tr_b16 %" #o ", %" #a "\n\t"
+template <> struct TrRead<2> {
+  __device__ __forceinline__ static void run(u32x2 (&o)[4], const uint32_t (&a)[4]) {
+    asm volatile(MOE_TR8(0, 4) MOE_TR8(1, 5) MOE_TR8(2, 6) MOE_TR8(3, 7) "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]) : "memory");
+  }
+};
+template <> struct TrRead<4> {
+  __device__ __forceinline__ static void run(u32x2 (&o)[8], const uint32_t (&a)[8]) {
+    asm volatile(MOE_TR8(0, 8) MOE_TR8(1, 9) MOE_TR8(2, 10) MOE_TR8(3, 11)
+                 MOE_TR8(4, 12) MOE_TR8(5, 13) MOE_TR8(6, 14) MOE_TR8(7, 15) "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]),
+                   "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+                 : "memory");
+  }
+};
+template <> struct TrRead<6> {
+  __device__ __forceinline__ static void run(u32x2 (&o)[12], const uint32_t (&a)[12]) {
+    asm volatile(MOE_TR8(0, 12) MOE_TR8(1, 13) MOE_TR8(2, 14) MOE_TR8(3, 15)
+                 MOE_TR8(4, 16) MOE_TR8(5, 17) MOE_TR8(6, 18) MOE_TR8(7, 19)
+                 MOE_TR8(8, 20) MOE_TR8(9, 21) MOE_TR8(10, 22) MOE_TR8(11, 23) "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
+                   "=&v"(o[6]), "=&v"(o[7]), "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]),
+                   "v"(a[6]), "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11])
+                 : "memory");
+  }
+};
+#undef MOE_TR8
+
 // MFMA work of one chunk for a wave: NS weight-side subtiles (LDS rows
-// qrow[ns]) x MS token-side subtiles (LDS rows prow[ms]).
+// qrow[ns]) x MS token-side subtiles (LDS rows prow[ms]).  Fragments of
+// compiler-read layouts are read first, then those of transposed layouts in
+// one TrRead block.
 template <typename T, typename PO, typename QO, int NS, int MS, int KSTEPS = KB / sizeof(T) / 16,
           bool PERM = false>
 __device__ __forceinline__ void mfma_chunk(f32x16 (&acc)[NS][MS], const char* lq, const char* lp,
                                            const int (&qrow)[NS], const int (&prow)[MS], int lane) {
   constexpr int CH = Mma32<T>::kChunks;
+  constexpr int NRAW = (QO::kRawLds ? NS : 0) + (PO::kRawLds ? MS : 0);
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
     u32x4 fa[NS][CH], fb[MS][CH];
+    if constexpr (!PO::kRawLds) {
 #pragma unroll
-    for (int ns = 0; ns < NS; ++ns) QO::template frag<PERM>(fa[ns], lq, qrow[ns], ks, lane);
+      for (int ms = 0; ms < MS; ++ms) PO::template frag<false>(fb[ms], lp, prow[ms], ks, lane);
+    }
+    if constexpr (!QO::kRawLds) {
 #pragma unroll
-    for (int ms = 0; ms < MS; ++ms) PO::template frag<false>(fb[ms], lp, prow[ms], ks, lane);
+      for (int ns = 0; ns < NS; ++ns) QO::template frag<PERM>(fa[ns], lq, qrow[ns], ks, lane);
+    }
+    if constexpr (NRAW > 0) {
+      uint32_t addr[2 * NRAW];
+      u32x2 raw[2 * NRAW];
+      constexpr int QB = 0, PB = QO::kRawLds ? NS : 0;     // fragment slots of each operand
+      if constexpr (QO::kRawLds) {
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) QO::template frag_addr<PERM>(addr + 2 * (QB + ns), lq, qrow[ns], ks, lane);
+      }
+      if constexpr (PO::kRawLds) {
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) PO::template frag_addr<false>(addr + 2 * (PB + ms), lp, prow[ms], ks, lane);
+      }
+      TrRead<NRAW>::run(raw, addr);
+      if constexpr (QO::kRawLds) {
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) {
+          const u32x2 lo = raw[2 * (QB + ns)], hi = raw[2 * (QB + ns) + 1];
+          fa[ns][0] = (u32x4){lo[0], lo[1], hi[0], hi[1]};
+        }
+      }
+      if constexpr (PO::kRawLds) {
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) {
+          const u32x2 lo = raw[2 * (PB + ms)], hi = raw[2 * (PB + ms) + 1];
+          fb[ms][0] = (u32x4){lo[0], lo[1], hi[0], hi[1]};
+        }
+      }
+    }
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
@@ -242,16 +315,18 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-template <int ROWS>
-struct DmaRows {                                   // [row][k], DKB bytes per row
+template <int ROWS, int NW>
+struct DmaRows {                                   // [row][k], DKB bytes per row; NW waves load
   static constexpr int CPRW = DKB / 16;            // 16-byte chunks per row (4)
   static constexpr int RPI = 1024 / DKB;           // rows per load instruction (16)
   static constexpr int BYTES = ROWS * DKB;
-  static constexpr int NI = BYTES / 1024 / 4;      // load instructions per wave per chunk
+  static constexpr int NI = BYTES / 1024 / NW;     // load instructions per wave per chunk
+  static_assert(NI >= 1 && NI * 1024 * NW == BYTES, "tile rows must split evenly over the waves");
+  static constexpr bool kRawLds = false;
   __device__ __forceinline__ static int swz(int r) { return (r >> 2) & 3; }
-  __device__ __forceinline__ static int row_of(int w, int s, int lane) { return RPI * (w + 4 * s) + lane / CPRW; }
+  __device__ __forceinline__ static int row_of(int w, int s, int lane) { return RPI * (w + NW * s) + lane / CPRW; }
   __device__ __forceinline__ static int gchunk(int row, int lane) { return (lane % CPRW) ^ swz(row); }
-  __device__ __forceinline__ static int lds_off(int w, int s) { return RPI * (w + 4 * s) * DKB; }
+  __device__ __forceinline__ static int lds_off(int w, int s) { return RPI * (w + NW * s) * DKB; }
   template <bool PERM>
   __device__ __forceinline__ static void frag(u32x4 (&f)[1], const char* lds, int row0, int ks, int lane) {
     const int r = row0 + (PERM ? perm_row(lane & 31) : (lane & 31));
@@ -260,30 +335,38 @@ struct DmaRows {                                   // [row][k], DKB bytes per ro
   }
 };
 
-template <int ROWS>
-struct DmaKmajor {                                 // [k][row], DKB/2 k-rows per chunk
+template <int ROWS, int NW>
+struct DmaKmajor {                                 // [k][row], DKB/2 k-rows per chunk; NW waves load
   static constexpr int KROWS = DKB / 2;
   static constexpr int RB = ROWS * 2;              // bytes per k-row
   static constexpr int CPR = RB / 16;              // 16-byte chunks per k-row
   static constexpr int KPI = 1024 / RB;            // k-rows per load instruction
   static constexpr int BYTES = KROWS * RB;
-  static constexpr int NI = BYTES / 1024 / 4;
+  static constexpr int NI = BYTES / 1024 / NW;
+  static_assert(NI >= 1 && NI * 1024 * NW == BYTES, "tile must split evenly over the waves");
   static_assert(CPR >= 16, "swizzle needs at least 16 chunks per k-row");
-  __device__ __forceinline__ static int k_of(int w, int s, int lane) { return KPI * (w + 4 * s) + lane / CPR; }
+  // Fragments of this layout are read with ds_read_b64_tr_b16 issued as
+  // inline assembly (TrRead below), not the compiler builtin: the compiler
+  // treats the builtin as possibly reading LDS that an outstanding
+  // buffer-to-LDS load writes and waits for every such load (vmcnt(0)),
+  // which would drain the ring on every chunk.  The ring barrier already
+  // orders these reads after the loads they consume.
+  static constexpr bool kRawLds = true;
+  __device__ __forceinline__ static int k_of(int w, int s, int lane) { return KPI * (w + NW * s) + lane / CPR; }
   __device__ __forceinline__ static int gchunk(int k, int lane) { return (lane % CPR) ^ (4 * (k & 3)); }
-  __device__ __forceinline__ static int lds_off(int w, int s) { return KPI * (w + 4 * s) * RB; }
+  __device__ __forceinline__ static int lds_off(int w, int s) { return KPI * (w + NW * s) * RB; }
+  // LDS addresses of the two transposing reads (k and k + 4) that form the
+  // fragment of rows row0 .. row0+31, k16 step ks
   template <bool PERM>
-  __device__ __forceinline__ static void frag(u32x4 (&f)[1], const char* lds, int row0, int ks, int lane) {
+  __device__ __forceinline__ static void frag_addr(uint32_t* a, const char* lds, int row0, int ks, int lane) {
     const int g = lane >> 4, i = lane & 15;
     const int k = ks * 16 + 8 * (g >> 1) + (i >> 2);
     // this lane addresses the 4-row block that MFMA rows 16 (g & 1) + 4 (i & 3) + 0..3 receive
     const int rb = 16 * (g & 1) + 4 * (i & 3);
     const int row = row0 + (PERM ? perm_row(rb) : rb);
     const char* p = lds + k * RB + (((row >> 3) ^ (4 * (k & 3))) << 4) + (row & 7) * 2;
-    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(p));
-    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(p + 4 * RB));
-    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
-    f[0] = (u32x4){ua[0], ua[1], ub[0], ub[1]};
+    a[0] = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+    a[1] = a[0] + 4 * RB;
   }
 };
 
@@ -305,20 +388,22 @@ __device__ __forceinline__ void ring_barrier(int ahead) {
 }
 
 // --------------------------------------------------------------- row GEMM ---
-template <typename T, int BM, int BN, int OP, int EPI>
+template <typename T, int BM, int BN, int OP, int EPI, int WM, int WN>
 __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) {
   constexpr int ES = sizeof(T);
+  constexpr int NW = WM * WN;                                  // waves: WM along rows, WN along columns
+  static_assert(ES == 2 || NW == 4, "the register-staged path runs 4 waves");
   constexpr bool QT = (OP == OP_DOWN_DGRAD || OP == OP_GU_DGRAD || OP == OP_ROUTER_DX);
   using PO = Operand<T, BM, false>;
   using QO = Operand<T, BN, QT>;
   constexpr int BK = PO::BK;
   constexpr int TILE_N = (OP == OP_GU_FWD) ? BN / 2 : BN;    // output (H) columns per tile
-  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MS = WTM / 32, NS = WTN / 32;
   constexpr int STAGE = PO::BYTES + QO::BYTES;
 
   constexpr int SCAN_OFF = (ES == 2) ? NSTG * (BM + BN) * DKB : 2 * STAGE;
-  int* s_scan = reinterpret_cast<int*>(smem + SCAN_OFF);      // [4] wave sums, [4..5] located tile
+  int* s_scan = reinterpret_cast<int*>(smem + SCAN_OFF);      // [NW] wave sums, [NW..NW+1] located tile
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_ntiles = a.N / TILE_N;
 
@@ -338,7 +423,7 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
   __syncthreads();
   int before = 0, total = 0;
 #pragma unroll
-  for (int w = 0; w < NT / 64; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const int sw = s_scan[w];
     before += (w < wave) ? sw : 0;
     total += sw;
@@ -347,23 +432,24 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
   const int logical = xcd_logical(blockIdx.x, total * n_ntiles);
   if (logical < 0) return;                                    // uniform across the workgroup
   const int mt = logical / n_ntiles, ntile = logical - mt * n_ntiles;
-  if (tid < a.G && mt >= start && mt < start + my_nt) { s_scan[4] = tid; s_scan[5] = mt - start; }
+  if (tid < a.G && mt >= start && mt < start + my_nt) { s_scan[NW] = tid; s_scan[NW + 1] = mt - start; }
   __syncthreads();
-  const int g = s_scan[4];
+  const int g = s_scan[NW];
   const int64_t seg0 = a.offsets ? a.offsets[g] : 0;
   const int64_t seg1 = a.offsets ? a.offsets[g + 1] : a.M;
-  const int64_t row0 = seg0 + (int64_t)s_scan[5] * BM;
+  const int64_t row0 = seg0 + (int64_t)s_scan[NW + 1] * BM;
   const int rows = (int)((seg1 - row0) < BM ? (seg1 - row0) : BM);
   const int n0 = ntile * TILE_N;
 
   const char* Pb = static_cast<const char*>(a.P);
   const char* Qb = static_cast<const char*>(a.Q) + (int64_t)g * a.q_group_stride * ES;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WM, wn = wave / WM;
   int qrow[NS], prow[MS];
 #pragma unroll
   for (int ns = 0; ns < NS; ++ns) {
+    // gate/up: the wave's first NS/2 subtiles are gate rows, the rest the matching up rows
     if constexpr (OP == OP_GU_FWD)
-      qrow[ns] = (ns < NS / 2) ? wn * (BN / 4) + ns * 32 : BN / 2 + wn * (BN / 4) + (ns - NS / 2) * 32;
+      qrow[ns] = (ns < NS / 2) ? wn * (WTN / 2) + ns * 32 : BN / 2 + wn * (WTN / 2) + (ns - NS / 2) * 32;
     else
       qrow[ns] = wn * WTN + ns * 32;
   }
@@ -380,16 +466,18 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
   static_assert(acc_col<PERM>(RUN, 0) == RSTEP && acc_col<PERM>(0, 1) == RUN, "run layout");
   const int h = lane >> 5;
 
-  // SwiGLU backward needs the saved G and U of each output element.  With at
-  // most 4 accumulators per wave they are loaded here, before the main loop,
-  // so that the loads' latency hides behind it (the first ring barrier, which
-  // waits for the older loads too, is where they are complete).
-  constexpr bool PRE = (EPI == EPI_SWIGLU_BWD) && PERM && MS * NS <= 4;
-  u32x4 gpre[PRE ? MS : 1][PRE ? NS : 1][NRUN], upre[PRE ? MS : 1][PRE ? NS : 1][NRUN];
-  if constexpr (PRE) {
+  // SwiGLU backward needs the saved G and U of each output element.  Those of
+  // the first PMS row subtiles (at most 64 VGPRs' worth) are loaded here,
+  // before the main loop, so that the loads' latency hides behind it (the
+  // first ring barrier, which waits for the older loads too, is where they
+  // are complete); the rest are loaded in the epilogue.
+  constexpr int PRE_REGS_PER_MS = NS * NRUN * 8;
+  constexpr int PMS = (EPI == EPI_SWIGLU_BWD && PERM) ? (64 / PRE_REGS_PER_MS < MS ? 64 / PRE_REGS_PER_MS : MS) : 0;
+  u32x4 gpre[PMS > 0 ? PMS : 1][NS][NRUN], upre[PMS > 0 ? PMS : 1][NS][NRUN];
+  if constexpr (PMS > 0) {
     const T* aux = static_cast<const T*>(a.aux);
 #pragma unroll
-    for (int ms = 0; ms < MS; ++ms) {
+    for (int ms = 0; ms < PMS; ++ms) {
       const int ml = prow[ms] + (lane & 31);
 #pragma unroll
       for (int ns = 0; ns < NS; ++ns)
@@ -407,8 +495,8 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
 
   if constexpr (ES == 2) {
     // ---------------- direct-to-LDS main loop (16-bit types)
-    using PD = DmaRows<BM>;
-    using QD = std::conditional_t<QT, DmaKmajor<BN>, DmaRows<BN>>;
+    using PD = DmaRows<BM, NW>;
+    using QD = std::conditional_t<QT, DmaKmajor<BN, NW>, DmaRows<BN, NW>>;
     constexpr int DSTAGE = PD::BYTES + QD::BYTES;
     constexpr int DBKE = DKB / ES;                    // k elements per chunk
     // token rows of this tile: rows >= `rows` fall outside the descriptor and read as zero
@@ -566,7 +654,7 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
       for (int j = 0; j < NS / 2; ++j)
 #pragma unroll
         for (int t = 0; t < NRUN; ++t) {
-          const int hc = n0 + wn * (BN / 4) + j * 32 + RSTEP * t + RUN * h;
+          const int hc = n0 + wn * (WTN / 2) + j * 32 + RSTEP * t + RUN * h;
           const int blk = hc / a.sub;
           const int gcol = blk * 2 * a.sub + (hc - blk * a.sub);
           float gv[RUN], uv[RUN], hv[RUN];
@@ -599,9 +687,11 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
             const int blk = n / a.sub;
             const int gcol = blk * 2 * a.sub + (n - blk * a.sub);
             float G[RUN], U[RUN], dG[RUN], dU[RUN];
-            if constexpr (PRE) {
-              unpack8<T>(gpre[ms][ns][t], G);
-              unpack8<T>(upre[ms][ns][t], U);
+            if (PMS > 0 && ms < PMS) {
+              if constexpr (PMS > 0) {
+                unpack8<T>(gpre[ms < PMS ? ms : 0][ns][t], G);
+                unpack8<T>(upre[ms < PMS ? ms : 0][ns][t], U);
+              }
             } else {
               const T* gu = static_cast<const T*>(a.aux) + row * a.ldaux;
               load_run<T, RUN>(gu + gcol, G);
@@ -623,13 +713,15 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
 }
 
 // ------------------------------------------------------------- wgrad GEMM ---
-template <typename T, int BM, int BN, int OUT_F32>
+template <typename T, int BM, int BN, int OUT_F32, int WM, int WN>
 __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
   constexpr int ES = sizeof(T);
+  constexpr int NW = WM * WN;
+  static_assert(ES == 2 || NW == 4, "the register-staged path runs 4 waves");
   using PO = Operand<T, BM, true>;
   using QO = Operand<T, BN, true>;
   constexpr int BK = PO::BK;
-  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MS = WTM / 32, NS = WTN / 32;
   constexpr int STAGE = PO::BYTES + QO::BYTES;
 
@@ -656,7 +748,7 @@ __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
   const char* Pb = static_cast<const char*>(a.P) + (int64_t)m0 * ES;
   const char* Qb = static_cast<const char*>(a.Q) + (int64_t)n0 * ES;
   const int64_t pld = a.ldp * ES, qld = a.ldq * ES;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WM, wn = wave / WM;
   int qrow[NS], prow[MS];
 #pragma unroll
   for (int ns = 0; ns < NS; ++ns) qrow[ns] = wn * WTN + ns * 32;
@@ -666,8 +758,8 @@ __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
   zero_acc(acc);
 
   if constexpr (ES == 2) {
-    using PD = DmaKmajor<BM>;
-    using QD = DmaKmajor<BN>;
+    using PD = DmaKmajor<BM, NW>;
+    using QD = DmaKmajor<BN, NW>;
     constexpr int DSTAGE = PD::BYTES + QD::BYTES;
     uint32_t poff[PD::NI], qoff[QD::NI];
 #pragma unroll
@@ -775,15 +867,19 @@ constexpr size_t smem_for() {
 
 // ------------------------------------------------------- named kernels ------
 // One plainly named kernel per (operation, dtype, tile) so profiles read well.
-#define MOE_ROW_KERNEL(NAME, T, BM, BN, OP, EPI)                                           \
-  extern "C" __global__ void __launch_bounds__(NT) NAME(RowGemmArgs a) {                  \
-    extern __shared__ __attribute__((aligned(16))) char smem[];                          \
-    row_gemm_body<T, BM, BN, OP, EPI>(a, smem);                                           \
+// 128 x 128 tiles run 4 waves (2 x 2); 256 x 256 tiles run 8 waves (2 along
+// rows x 4 along columns, 128 x 64 per wave), one workgroup per CU.
+template <int BM> struct TileWaves { static constexpr int WM = 2, WN = BM == 256 ? 4 : 2, THREADS = 64 * WM * WN; };
+
+#define MOE_ROW_KERNEL(NAME, T, BM, BN, OP, EPI)                                                    \
+  extern "C" __global__ void __launch_bounds__(TileWaves<BM>::THREADS) NAME(RowGemmArgs a) {       \
+    extern __shared__ __attribute__((aligned(16))) char smem[];                                   \
+    row_gemm_body<T, BM, BN, OP, EPI, TileWaves<BM>::WM, TileWaves<BM>::WN>(a, smem);              \
   }
-#define MOE_WGRAD_KERNEL(NAME, T, BM, BN, F32)                                             \
-  extern "C" __global__ void __launch_bounds__(NT) NAME(WgradArgs a) {                    \
-    extern __shared__ __attribute__((aligned(16))) char smem[];                          \
-    wgrad_body<T, BM, BN, F32>(a, smem);                                                  \
+#define MOE_WGRAD_KERNEL(NAME, T, BM, BN, F32)                                                      \
+  extern "C" __global__ void __launch_bounds__(TileWaves<BM>::THREADS) NAME(WgradArgs a) {         \
+    extern __shared__ __attribute__((aligned(16))) char smem[];                                   \
+    wgrad_body<T, BM, BN, F32, TileWaves<BM>::WM, TileWaves<BM>::WN>(a, smem);                     \
   }
 
 #define MOE_KERNEL_SET(T, TN, BM, BN)                                                                      \
@@ -870,7 +966,8 @@ hipError_t launch_row_gemm(int dt, int op, int epi, int tile, const RowGemmArgs&
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipError_t e = prepare((const void*)k, set->lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(NT), set->lds, s, a);
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(tile == 256 ? TileWaves<256>::THREADS : TileWaves<128>::THREADS),
+                     set->lds, s, a);
   return hipGetLastError();
 }
 
@@ -892,7 +989,8 @@ hipError_t launch_wgrad(int dt, int op, int tile, const WgradArgs& a, hipStream_
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipError_t e = prepare((const void*)k, set->lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(NT), set->lds, s, a);
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(tile == 256 ? TileWaves<256>::THREADS : TileWaves<128>::THREADS),
+                     set->lds, s, a);
   return hipGetLastError();
 }
 
