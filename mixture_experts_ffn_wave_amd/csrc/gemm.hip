@@ -303,10 +303,15 @@ __device__ __forceinline__ void dma16(rsrc_t rs, char* lds_lane0, uint32_t voff)
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_lane0, 16, voff, 0, 0, 0);
 }
 
-// Bytes of k per LDS chunk on the direct-load path and the depth of its ring:
-// 64-byte chunks, 4 stages, so loads run three chunks ahead of the MFMAs.
-constexpr int DKB = 64;
-constexpr int NSTG = 4;
+// Tile configurations of the direct-load path (BM = BN):
+//   128 x 128: 4 waves (2 x 2), a 4-stage ring of 64-byte k chunks (loads run
+//              three chunks ahead), 64 KB of LDS: two workgroups per CU;
+//   256 x 256: 8 waves (2 along rows x 4 along columns, 128 x 64 per wave), a
+//              2-stage ring of 128-byte k chunks (each row's chunk is one full
+//              cache line), 128 KB of LDS: one workgroup per CU.
+template <int BM> struct TileCfg;
+template <> struct TileCfg<128> { static constexpr int WM = 2, WN = 2, DKB = 64, NSTG = 4, THREADS = 256; };
+template <> struct TileCfg<256> { static constexpr int WM = 2, WN = 4, DKB = 128, NSTG = 2, THREADS = 512; };
 
 // vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding)
 template <int N>
@@ -315,15 +320,20 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-template <int ROWS, int NW>
+template <int ROWS, int NW, int DKB>
 struct DmaRows {                                   // [row][k], DKB bytes per row; NW waves load
-  static constexpr int CPRW = DKB / 16;            // 16-byte chunks per row (4)
-  static constexpr int RPI = 1024 / DKB;           // rows per load instruction (16)
+  static constexpr int CPRW = DKB / 16;            // 16-byte chunks per row
+  static constexpr int RPI = 1024 / DKB;           // rows per load instruction
   static constexpr int BYTES = ROWS * DKB;
   static constexpr int NI = BYTES / 1024 / NW;     // load instructions per wave per chunk
   static_assert(NI >= 1 && NI * 1024 * NW == BYTES, "tile rows must split evenly over the waves");
+  static_assert(DKB == 64 || DKB == 128, "chunk width");
   static constexpr bool kRawLds = false;
-  __device__ __forceinline__ static int swz(int r) { return (r >> 2) & 3; }
+  // 64-byte rows: 4 rows fill the 256-byte bank space, rows r and r+4 differ
+  // by the swizzle; 128-byte rows: 2 rows fill it, rows 2j and 2j+1 get
+  // swizzle j (mod 8).  Either way 16 consecutive (or bit-2/3-swapped) rows
+  // read at one chunk index hit 16 different 16-byte bank groups.
+  __device__ __forceinline__ static int swz(int r) { return DKB == 64 ? (r >> 2) & 3 : (r >> 1) & 7; }
   __device__ __forceinline__ static int row_of(int w, int s, int lane) { return RPI * (w + NW * s) + lane / CPRW; }
   __device__ __forceinline__ static int gchunk(int row, int lane) { return (lane % CPRW) ^ swz(row); }
   __device__ __forceinline__ static int lds_off(int w, int s) { return RPI * (w + NW * s) * DKB; }
@@ -335,7 +345,7 @@ struct DmaRows {                                   // [row][k], DKB bytes per ro
   }
 };
 
-template <int ROWS, int NW>
+template <int ROWS, int NW, int DKB>
 struct DmaKmajor {                                 // [k][row], DKB/2 k-rows per chunk; NW waves load
   static constexpr int KROWS = DKB / 2;
   static constexpr int RB = ROWS * 2;              // bytes per k-row
@@ -376,8 +386,9 @@ struct DmaKmajor {                                 // [k][row], DKB/2 k-rows per
 // both true for the whole workgroup.  __syncthreads() would add a release
 // fence that waits for every outstanding load, draining the ring.  The empty
 // asm statements keep the compiler from moving memory accesses across.
-template <int LPC>
-__device__ __forceinline__ void ring_barrier(int ahead) {
+template <int LPC, int NSTG>
+__device__ __forceinline__ void ring_barrier(int remaining) {
+  const int ahead = remaining < NSTG - 2 ? remaining : NSTG - 2;   // chunks issued after this one
   asm volatile("" ::: "memory");
   if (ahead >= 2) wait_vmcnt<2 * LPC>();
   else if (ahead == 1) wait_vmcnt<LPC>();
@@ -402,6 +413,7 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
   constexpr int MS = WTM / 32, NS = WTN / 32;
   constexpr int STAGE = PO::BYTES + QO::BYTES;
 
+  constexpr int DKB = TileCfg<BM>::DKB, NSTG = TileCfg<BM>::NSTG;
   constexpr int SCAN_OFF = (ES == 2) ? NSTG * (BM + BN) * DKB : 2 * STAGE;
   int* s_scan = reinterpret_cast<int*>(smem + SCAN_OFF);      // [NW] wave sums, [NW..NW+1] located tile
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -467,12 +479,13 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
   const int h = lane >> 5;
 
   // SwiGLU backward needs the saved G and U of each output element.  Those of
-  // the first PMS row subtiles (at most 64 VGPRs' worth) are loaded here,
+  // the first PMS row subtiles (at most PRE_BUDGET VGPRs' worth) are loaded here,
   // before the main loop, so that the loads' latency hides behind it (the
   // first ring barrier, which waits for the older loads too, is where they
   // are complete); the rest are loaded in the epilogue.
   constexpr int PRE_REGS_PER_MS = NS * NRUN * 8;
-  constexpr int PMS = (EPI == EPI_SWIGLU_BWD && PERM) ? (64 / PRE_REGS_PER_MS < MS ? 64 / PRE_REGS_PER_MS : MS) : 0;
+  constexpr int PRE_BUDGET = NW == 4 ? 64 : 32;               // 8-wave tiles keep 128 accumulator VGPRs
+  constexpr int PMS = (EPI == EPI_SWIGLU_BWD && PERM) ? (PRE_BUDGET / PRE_REGS_PER_MS < MS ? PRE_BUDGET / PRE_REGS_PER_MS : MS) : 0;
   u32x4 gpre[PMS > 0 ? PMS : 1][NS][NRUN], upre[PMS > 0 ? PMS : 1][NS][NRUN];
   if constexpr (PMS > 0) {
     const T* aux = static_cast<const T*>(a.aux);
@@ -495,8 +508,8 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
 
   if constexpr (ES == 2) {
     // ---------------- direct-to-LDS main loop (16-bit types)
-    using PD = DmaRows<BM, NW>;
-    using QD = std::conditional_t<QT, DmaKmajor<BN, NW>, DmaRows<BN, NW>>;
+    using PD = DmaRows<BM, NW, DKB>;
+    using QD = std::conditional_t<QT, DmaKmajor<BN, NW, DKB>, DmaRows<BN, NW, DKB>>;
     constexpr int DSTAGE = PD::BYTES + QD::BYTES;
     constexpr int DBKE = DKB / ES;                    // k elements per chunk
     // token rows of this tile: rows >= `rows` fall outside the descriptor and read as zero
@@ -564,7 +577,7 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
     for (int c = 0; c < NSTG - 1; ++c)
       if (c < nkd) issue(c * DBKE, smem + c * DSTAGE);
     for (int kc = 0; kc < nkd; ++kc) {
-      ring_barrier<LPC>(nkd - 1 - kc);                // chunk kc landed everywhere; kc-1 consumed
+      ring_barrier<LPC, NSTG>(nkd - 1 - kc);          // chunk kc landed everywhere; kc-1 consumed
       if (kc + NSTG - 1 < nkd) issue((kc + NSTG - 1) * DBKE, smem + ((kc + NSTG - 1) % NSTG) * DSTAGE);
       const char* buf = smem + (kc % NSTG) * DSTAGE;
       mfma_chunk<T, PD, QD, NS, MS, DKB / 32, true>(acc, buf + PD::BYTES, buf, qrow, prow, lane);
@@ -758,8 +771,9 @@ __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
   zero_acc(acc);
 
   if constexpr (ES == 2) {
-    using PD = DmaKmajor<BM, NW>;
-    using QD = DmaKmajor<BN, NW>;
+    constexpr int DKB = TileCfg<BM>::DKB, NSTG = TileCfg<BM>::NSTG;
+    using PD = DmaKmajor<BM, NW, DKB>;
+    using QD = DmaKmajor<BN, NW, DKB>;
     constexpr int DSTAGE = PD::BYTES + QD::BYTES;
     uint32_t poff[PD::NI], qoff[QD::NI];
 #pragma unroll
@@ -789,7 +803,7 @@ __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
     for (int c = 0; c < NSTG - 1; ++c)
       if (c < nkd) issue(kbeg + (int64_t)c * DBKK, smem + c * DSTAGE);
     for (int kc = 0; kc < nkd; ++kc) {
-      ring_barrier<LPC>(nkd - 1 - kc);
+      ring_barrier<LPC, NSTG>(nkd - 1 - kc);
       if (kc + NSTG - 1 < nkd) issue(kbeg + (int64_t)(kc + NSTG - 1) * DBKK, smem + ((kc + NSTG - 1) % NSTG) * DSTAGE);
       const char* buf = smem + (kc % NSTG) * DSTAGE;
       mfma_chunk<T, PD, QD, NS, MS, DKB / 32, true>(acc, buf + PD::BYTES, buf, qrow, prow, lane);
@@ -852,7 +866,7 @@ __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
 template <typename T, int BM, int BN>
 constexpr size_t smem_for() {
   if constexpr (sizeof(T) == 2) {
-    return (size_t)NSTG * (BM + BN) * DKB + 64;        // direct-load ring
+    return (size_t)TileCfg<BM>::NSTG * (BM + BN) * TileCfg<BM>::DKB + 64;   // direct-load ring
   } else {
     constexpr int nn = Operand<T, BM, false>::BYTES + Operand<T, BN, false>::BYTES;
     constexpr int nt = Operand<T, BM, false>::BYTES + Operand<T, BN, true>::BYTES;
@@ -867,19 +881,16 @@ constexpr size_t smem_for() {
 
 // ------------------------------------------------------- named kernels ------
 // One plainly named kernel per (operation, dtype, tile) so profiles read well.
-// 128 x 128 tiles run 4 waves (2 x 2); 256 x 256 tiles run 8 waves (2 along
-// rows x 4 along columns, 128 x 64 per wave), one workgroup per CU.
-template <int BM> struct TileWaves { static constexpr int WM = 2, WN = BM == 256 ? 4 : 2, THREADS = 64 * WM * WN; };
 
 #define MOE_ROW_KERNEL(NAME, T, BM, BN, OP, EPI)                                                    \
-  extern "C" __global__ void __launch_bounds__(TileWaves<BM>::THREADS) NAME(RowGemmArgs a) {       \
+  extern "C" __global__ void __launch_bounds__(TileCfg<BM>::THREADS) NAME(RowGemmArgs a) {       \
     extern __shared__ __attribute__((aligned(16))) char smem[];                                   \
-    row_gemm_body<T, BM, BN, OP, EPI, TileWaves<BM>::WM, TileWaves<BM>::WN>(a, smem);              \
+    row_gemm_body<T, BM, BN, OP, EPI, TileCfg<BM>::WM, TileCfg<BM>::WN>(a, smem);              \
   }
 #define MOE_WGRAD_KERNEL(NAME, T, BM, BN, F32)                                                      \
-  extern "C" __global__ void __launch_bounds__(TileWaves<BM>::THREADS) NAME(WgradArgs a) {         \
+  extern "C" __global__ void __launch_bounds__(TileCfg<BM>::THREADS) NAME(WgradArgs a) {         \
     extern __shared__ __attribute__((aligned(16))) char smem[];                                   \
-    wgrad_body<T, BM, BN, F32, TileWaves<BM>::WM, TileWaves<BM>::WN>(a, smem);                     \
+    wgrad_body<T, BM, BN, F32, TileCfg<BM>::WM, TileCfg<BM>::WN>(a, smem);                     \
   }
 
 #define MOE_KERNEL_SET(T, TN, BM, BN)                                                                      \
@@ -966,7 +977,7 @@ hipError_t launch_row_gemm(int dt, int op, int epi, int tile, const RowGemmArgs&
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipError_t e = prepare((const void*)k, set->lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(tile == 256 ? TileWaves<256>::THREADS : TileWaves<128>::THREADS),
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(tile == 256 ? TileCfg<256>::THREADS : TileCfg<128>::THREADS),
                      set->lds, s, a);
   return hipGetLastError();
 }
@@ -989,7 +1000,7 @@ hipError_t launch_wgrad(int dt, int op, int tile, const WgradArgs& a, hipStream_
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipError_t e = prepare((const void*)k, set->lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(tile == 256 ? TileWaves<256>::THREADS : TileWaves<128>::THREADS),
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(tile == 256 ? TileCfg<256>::THREADS : TileCfg<128>::THREADS),
                      set->lds, s, a);
   return hipGetLastError();
 }
