@@ -27,7 +27,8 @@ const char* kKernelNames =
     "gemm_gate_up_swiglu_shared,gemm_down_shared,combine,combine_bwd,router_dz,"
     "gemm_down_dgrad_swiglu,gemm_wgrad_down,gemm_gate_up_dgrad,gemm_wgrad_gate_up,"
     "gemm_down_dgrad_swiglu_shared,gemm_wgrad_down_shared,gemm_wgrad_gate_up_shared,"
-    "gemm_gate_up_dgrad_shared,stack_router,gemm_router_dx,unpermute,gemm_wgrad_router,router_reduce,aux";
+    "gemm_gate_up_dgrad_shared,stack_router,gemm_router_dx,unpermute,gemm_wgrad_router,router_reduce,aux,"
+    "wgrad_reduce";
 
 }  // namespace
 
@@ -40,9 +41,11 @@ struct moe_plan_s {
   // GEMM tile per call site, chosen once at plan time
   int t_gu, t_down, t_gu_s, t_down_s, t_down_dgrad, t_gu_dgrad, t_down_dgrad_s, t_gu_dgrad_s, t_router_dx;
   int t_wg_down, t_wg_gu, t_wg_down_s, t_wg_gu_s, t_wg_router;
+  // split-K factor of each weight-gradient GEMM (1 = no split, no partials)
+  int sp_wg_down, sp_wg_gu, sp_wg_down_s, sp_wg_gu_s;
   // workspace regions (byte offsets)
   size_t o_block_counts, o_block_base, o_dy_perm, o_g, o_dzhl, o_w2, o_dgu, o_dx_perm, o_dgu_s,
-      o_dxs, o_dxr, o_dwr_part, o_dbias_part, o_aux_part, ws_total;
+      o_dxs, o_dxr, o_dwr_part, o_dbias_part, o_aux_part, o_wg_part, ws_total;
   bool router_dx_gemm;     // many experts: the router part of dx goes through the matrix cores
   // timing probe
   std::string probe_name;
@@ -127,6 +130,25 @@ int choose_wgrad_tile(int dt, double segs, int M, int N, double ktok, int overri
   const double c256 = ((w256 + kCUs - 1) / kCUs) * 256.0 * 256.0 * ktok;
   const double c128 = ((w128 + kCUs - 1) / kCUs) * 128.0 * 128.0 * ktok / 0.55;
   return c256 <= c128 ? 256 : 128;
+}
+
+// Split-K factor of a weight-gradient GEMM with W = G (M/tile)(N/tile) output
+// tiles.  Fewer than 384 tiles leave CUs with one workgroup or none, so the
+// token range is split until about 512 workgroups run (at most 4 ways, and
+// every split keeps at least 512 tokens per group); the f32 partials are then
+// summed in order by one extra pass.  MOE_WGRAD_SPLITS (1..8) forces a value.
+int choose_wgrad_splits(int tile, int G, int M, int N, double tokens_per_group) {
+  const char* v = std::getenv("MOE_WGRAD_SPLITS");
+  if (v) {
+    const int s = std::atoi(v);
+    if (s >= 1 && s <= 8) return s;
+  }
+  const int64_t W = (int64_t)G * (M / tile) * (N / tile);
+  if (W <= 0 || W >= 384) return 1;
+  int s = (int)(512 / W);
+  if (s > 4) s = 4;
+  while (s > 1 && tokens_per_group / s < 512) --s;
+  return s < 1 ? 1 : s;
 }
 
 }  // namespace
@@ -215,6 +237,8 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
     p->t_wg_down = choose_wgrad_tile(p->dt, E, d, I, rps, wt);
     p->t_wg_gu = choose_wgrad_tile(p->dt, E, 2 * I, d, rps, wt);
     p->t_wg_router = 128;
+    p->sp_wg_down = choose_wgrad_splits(p->t_wg_down, E, d, I, rps);
+    p->sp_wg_gu = choose_wgrad_splits(p->t_wg_gu, E, 2 * I, d, rps);
     if (p->Ns > 0) {
       p->t_gu_s = choose_row_tile(p->dt, 2 * NI, 2 * p->Is, rt);
       p->t_down_s = choose_row_tile(p->dt, d, 256, rt);
@@ -222,8 +246,11 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
       p->t_gu_dgrad_s = choose_row_tile(p->dt, d, 256, rt);
       p->t_wg_down_s = (p->Is % 256 == 0) ? choose_wgrad_tile(p->dt, 1, d, NI, T, wt) : 128;
       p->t_wg_gu_s = choose_wgrad_tile(p->dt, 1, 2 * NI, d, T, wt);
+      p->sp_wg_down_s = choose_wgrad_splits(p->t_wg_down_s, 1, d, NI, T);
+      p->sp_wg_gu_s = choose_wgrad_splits(p->t_wg_gu_s, 1, 2 * NI, d, T);
     } else {
       p->t_gu_s = p->t_down_s = p->t_down_dgrad_s = p->t_gu_dgrad_s = p->t_wg_down_s = p->t_wg_gu_s = 128;
+      p->sp_wg_down_s = p->sp_wg_gu_s = 1;
     }
   }
   const size_t es = dtype_bytes(p->dt);
@@ -247,6 +274,18 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
   p->o_dwr_part = take((size_t)p->router_splits * 2 * p->Ep * p->d * 4);
   p->o_dbias_part = take((size_t)p->nblk_dz * p->E * 4);
   p->o_aux_part = take((size_t)(p->nblk_aux > 0 ? p->nblk_aux : 1) * 2 * p->E * 4);
+  {
+    // one f32 partial buffer, reused by every split weight-gradient GEMM in turn
+    size_t part = 0;
+    auto need = [&](int sp, int64_t elems) {
+      if (sp > 1 && (size_t)sp * elems * 4 > part) part = (size_t)sp * elems * 4;
+    };
+    need(p->sp_wg_down, (int64_t)p->E * p->d * p->I);
+    need(p->sp_wg_gu, (int64_t)p->E * 2 * p->I * p->d);
+    need(p->sp_wg_down_s, (int64_t)p->d * p->Ns * p->Is);
+    need(p->sp_wg_gu_s, (int64_t)2 * p->Ns * p->Is * p->d);
+    p->o_wg_part = take(part);
+  }
   p->ws_total = off;
   *out = p;
   return MOE_OK;
@@ -255,6 +294,36 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
 void moe_plan_destroy(moe_plan plan) { delete plan; }
 
 size_t moe_workspace_bytes(moe_plan plan) { return plan ? plan->ws_total : 0; }
+
+// Weight-gradient GEMM into `out` ([G][group_elems], act dtype), split over
+// tokens `splits` ways through f32 partials when splits > 1.
+moe_status run_wgrad(moe_plan p, int op, int tile, int splits, WgradArgs a, void* out, int64_t group_elems,
+                     void* ws, const char* name, hipStream_t s) {
+  a.splits = splits;
+  a.c_group_stride = group_elems;
+  if (splits <= 1) {
+    a.C = out; a.c_split_stride = 0; a.out_f32 = 0;
+    Probe pr(p, name, s);
+    MOE_TRY(launch_wgrad(p->dt, op, tile, a, s));
+    return MOE_OK;
+  }
+  float* part = reinterpret_cast<float*>(wsp(ws, p->o_wg_part));
+  a.C = part; a.c_split_stride = (int64_t)a.G * group_elems; a.out_f32 = 1;
+  {
+    Probe pr(p, name, s);
+    MOE_TRY(launch_wgrad(p->dt, op, tile, a, s));
+  }
+  SplitReduceArgs r{part, (int64_t)a.G * group_elems, splits, out};
+  Probe pr(p, "wgrad_reduce", s);
+  MOE_TRY(launch_split_reduce(p->dt, r, s));
+  return MOE_OK;
+}
+
+#define MOE_TRY_STATUS(expr)            \
+  do {                                  \
+    moe_status st_ = (expr);            \
+    if (st_ != MOE_OK) return st_;      \
+  } while (0)
 
 // ------------------------------------------------------------------ route --
 moe_status moe_route(moe_plan p, const void* x, const void* w_router, const float* bias, float* probs,
@@ -422,10 +491,9 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
   {
     WgradArgs a{};
     a.P = dy_perm; a.ldp = d; a.Q = sv->h; a.ldq = I;
-    a.offsets = sv->offsets; a.G = E; a.Mtok = p->A; a.M = d; a.N = I; a.splits = 1;
-    a.C = gr->dw_down; a.c_group_stride = (int64_t)d * I; a.c_split_stride = 0; a.sub = I; a.out_f32 = 0;
-    Probe pr(p, "gemm_wgrad_down", s);
-    MOE_TRY(launch_wgrad(p->dt, WG_DOWN, p->t_wg_down, a, s));
+    a.offsets = sv->offsets; a.G = E; a.Mtok = p->A; a.M = d; a.N = I; a.sub = I;
+    MOE_TRY_STATUS(run_wgrad(p, WG_DOWN, p->t_wg_down, p->sp_wg_down, a, gr->dw_down, (int64_t)d * I, ws,
+                             "gemm_wgrad_down", s));
   }
   if (p->T > 0) {
     RowGemmArgs a{};
@@ -439,10 +507,9 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
   {
     WgradArgs a{};
     a.P = dgu; a.ldp = 2 * I; a.Q = sv->x_perm; a.ldq = d;
-    a.offsets = sv->offsets; a.G = E; a.Mtok = p->A; a.M = 2 * I; a.N = d; a.splits = 1;
-    a.C = gr->dw_gate_up; a.c_group_stride = (int64_t)2 * I * d; a.c_split_stride = 0; a.sub = d; a.out_f32 = 0;
-    Probe pr(p, "gemm_wgrad_gate_up", s);
-    MOE_TRY(launch_wgrad(p->dt, WG_GATE_UP, p->t_wg_gu, a, s));
+    a.offsets = sv->offsets; a.G = E; a.Mtok = p->A; a.M = 2 * I; a.N = d; a.sub = d;
+    MOE_TRY_STATUS(run_wgrad(p, WG_GATE_UP, p->t_wg_gu, p->sp_wg_gu, a, gr->dw_gate_up, (int64_t)2 * I * d, ws,
+                             "gemm_wgrad_gate_up", s));
   }
   if (p->Ns > 0) {
     const int Is = p->Is, NI = p->Ns * p->Is;
@@ -458,18 +525,16 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
     {
       WgradArgs a{};
       a.P = dy; a.ldp = d; a.Q = sv->h_shared; a.ldq = NI;
-      a.offsets = nullptr; a.G = 1; a.Mtok = p->T; a.M = d; a.N = NI; a.splits = 1;
-      a.C = gr->dws_down; a.c_group_stride = 0; a.c_split_stride = 0; a.sub = Is; a.out_f32 = 0;
-      Probe pr(p, "gemm_wgrad_down_shared", s);
-      MOE_TRY(launch_wgrad(p->dt, WG_DOWN, p->t_wg_down_s, a, s));
+      a.offsets = nullptr; a.G = 1; a.Mtok = p->T; a.M = d; a.N = NI; a.sub = Is;
+      MOE_TRY_STATUS(run_wgrad(p, WG_DOWN, p->t_wg_down_s, p->sp_wg_down_s, a, gr->dws_down, (int64_t)d * NI, ws,
+                               "gemm_wgrad_down_shared", s));
     }
     {
       WgradArgs a{};
       a.P = dgu_s; a.ldp = 2 * NI; a.Q = sv->x; a.ldq = d;
-      a.offsets = nullptr; a.G = 1; a.Mtok = p->T; a.M = 2 * NI; a.N = d; a.splits = 1;
-      a.C = gr->dws_gate_up; a.c_group_stride = 0; a.c_split_stride = 0; a.sub = d; a.out_f32 = 0;
-      Probe pr(p, "gemm_wgrad_gate_up_shared", s);
-      MOE_TRY(launch_wgrad(p->dt, WG_GATE_UP, p->t_wg_gu_s, a, s));
+      a.offsets = nullptr; a.G = 1; a.Mtok = p->T; a.M = 2 * NI; a.N = d; a.sub = d;
+      MOE_TRY_STATUS(run_wgrad(p, WG_GATE_UP, p->t_wg_gu_s, p->sp_wg_gu_s, a, gr->dws_gate_up, (int64_t)2 * NI * d,
+                               ws, "gemm_wgrad_gate_up_shared", s));
     }
   }
   if (p->Ns > 0 && p->T > 0) {

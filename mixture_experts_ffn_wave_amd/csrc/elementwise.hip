@@ -124,63 +124,81 @@ __global__ void __launch_bounds__(NT) combine_bwd_kernel(CombineBwdArgs a) {
 // nearly f32 accuracy.  Per-block column sums of dz feed dbias.
 template <typename T>
 __global__ void __launch_bounds__(NT) router_dz_kernel(RouterDzArgs a) {
-  __shared__ float s_dp[NT / 64][256];
-  __shared__ float s_dz[NT / 64][256];
+  // one wave per token; lane l holds experts l, l+64, l+128, l+192
+  __shared__ float s_bias[NT / 64][256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float aux_scale = a.aux_coef * (float)a.E / ((float)a.T * (float)a.T * (float)a.k);
-  float bias_acc = 0.0f;
+  float dp_aux[4], bias_acc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = lane + 64 * q;
+    dp_aux[q] = (e < a.E) ? aux_scale * (float)a.counts[e] : 0.0f;
+    bias_acc[q] = 0.0f;
+  }
   T* dz = static_cast<T*>(a.dz_hl);
   const int64_t ld = 2 * (int64_t)a.Ep;
-  for (int64_t tb = (int64_t)blockIdx.x * (NT / 64); tb < a.T; tb += (int64_t)gridDim.x * (NT / 64)) {
-    const int64_t t = tb + wave;
-    const bool active = t < a.T;
+  const int64_t nwaves = (int64_t)gridDim.x * (NT / 64);
+  for (int64_t t = (int64_t)blockIdx.x * (NT / 64) + wave; t < a.T; t += nwaves) {
     float p[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = lane + 64 * q;
-      p[q] = (active && e < a.E) ? a.probs[t * a.E + e] : 0.0f;
-      if (e < a.E) s_dp[wave][e] = aux_scale * (float)a.counts[e];
+      p[q] = (e < a.E) ? a.probs[t * a.E + e] : 0.0f;
     }
-    float gj = 0.0f, wj = 0.0f, pj = 0.0f;
+    float gj = 0.0f, wj = 0.0f;
     int ej = -1;
-    if (active && lane < a.k) {
+    if (lane < a.k) {
       ej = a.idx[t * a.k + lane];
       gj = a.g[t * a.k + lane];
       wj = a.wts[t * a.k + lane];
-      if ((unsigned)ej < (unsigned)a.E) pj = a.probs[t * a.E + ej];
-      else ej = -1;
+      if ((unsigned)ej >= (unsigned)a.E) ej = -1;
+    }
+    // p of this slot's expert, from the lane that holds it
+    float pj = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (64 * q < a.E) {
+        const float v = __shfl(p[q], ej & 63, 64);
+        if (ej >= 0 && (ej >> 6) == q) pj = v;
+      }
     }
     const float S = wave_sum(pj);
     const float wg = wave_sum(wj * gj);
     const float dps = a.renorm ? (gj - wg) / S : gj;
-    __syncthreads();
-    if (ej >= 0) s_dp[wave][ej] += dps;
-    __syncthreads();
+    float dp[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dp[q] = dp_aux[q];
+    // scatter the k slot gradients to the lanes that hold their experts
+    for (int j = 0; j < a.k; ++j) {
+      const int eb = __shfl(ej, j, 64);
+      const float db = __shfl(dps, j, 64);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (lane + 64 * q == eb) dp[q] += db;
+    }
     float dot = 0.0f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
-      if (e < a.E) dot = fmaf(p[q], s_dp[wave][e], dot);
-    }
+    for (int q = 0; q < 4; ++q) dot = fmaf(p[q], dp[q], dot);
     dot = wave_sum(dot);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = lane + 64 * q;
-      float v = 0.0f;
-      if (e < a.E) v = active ? p[q] * (s_dp[wave][e] - dot) : 0.0f;
-      if (active && e < a.Ep) {
+      const float v = (e < a.E) ? p[q] * (dp[q] - dot) : 0.0f;
+      if (e < a.Ep) {
         const T hi = from_f32<T>(v);
         const T lo = from_f32<T>(v - to_f32<T>(hi));
         dz[t * ld + e] = hi;
         dz[t * ld + a.Ep + e] = lo;
       }
-      if (e < a.E) s_dz[wave][e] = v;
+      bias_acc[q] += v;
     }
-    __syncthreads();
-    if (tid < a.E) bias_acc += ((s_dz[0][tid] + s_dz[1][tid]) + s_dz[2][tid]) + s_dz[3][tid];
-    __syncthreads();
   }
-  if (tid < a.E) a.dbias_part[(int64_t)blockIdx.x * a.E + tid] = bias_acc;
+  // per-block column sums of dz, waves combined in index order
+#pragma unroll
+  for (int q = 0; q < 4; ++q) s_bias[wave][lane + 64 * q] = bias_acc[q];
+  __syncthreads();
+  if (tid < a.E)
+    a.dbias_part[(int64_t)blockIdx.x * a.E + tid] = ((s_bias[0][tid] + s_bias[1][tid]) + s_bias[2][tid]) + s_bias[3][tid];
 }
 
 // w2 rows [0, E) and [Ep, Ep + E) = W_r, every other row zero.
@@ -196,44 +214,69 @@ __global__ void __launch_bounds__(NT) stack2_kernel(Stack2Args a) {
   }
 }
 
-// Sum of v over the workgroup in a fixed order (butterfly within waves, then
-// waves in index order); every thread gets the result.
-__device__ __forceinline__ float block_sum_f(float v, float* sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  v = wave_sum(v);
-  __syncthreads();
-  if (lane == 0) sh[wave] = v;
-  __syncthreads();
-  float s = 0.0f;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) s += sh[w];
-  return s;
-}
-
-// Blocks [0, nbw): dW_r[e][n] = sum_s part[s][e][n] + sum_s part[s][Ep + e][n].
-// Blocks [nbw, nbw + E): dbias[e] = sum over router_dz blocks of their partial.
+// Blocks [0, nbw): block b reduces columns 64 (b % (d/64)) .. +63 of row
+// e = b / (d/64): dW_r[e][n] = sum_s part[s][e][n] + sum_s part[s][Ep + e][n].
+// Its 16 waves each sum every 16th split (hi and lo apart), then the wave
+// partials are added in index order.  Blocks [nbw, nbw + E): dbias[e] = sum
+// over router_dz blocks of their partial.
+constexpr int kReduceThreads = 1024;
 template <typename T>
-__global__ void __launch_bounds__(NT) router_reduce_kernel(RouterReduceArgs a, int nbw) {
-  __shared__ float sh[NT / 64];
+__global__ void __launch_bounds__(kReduceThreads) router_reduce_kernel(RouterReduceArgs a, int nbw) {
+  constexpr int NWV = kReduceThreads / 64;
+  __shared__ float sh[2][NWV][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if ((int)blockIdx.x >= nbw) {
     const int e = blockIdx.x - nbw;
     float v = 0.0f;
-    for (int b = threadIdx.x; b < a.nb; b += NT) v += a.dbias_part[(int64_t)b * a.E + e];
-    v = block_sum_f(v, sh);
-    if (threadIdx.x == 0) a.dbias[e] = v;
+    for (int b = tid; b < a.nb; b += kReduceThreads) v += a.dbias_part[(int64_t)b * a.E + e];
+    v = wave_sum(v);
+    if (lane == 0) sh[0][wave][0] = v;
+    __syncthreads();
+    if (tid == 0) {
+      float s = 0.0f;
+      for (int w = 0; w < NWV; ++w) s += sh[0][w][0];
+      a.dbias[e] = s;
+    }
     return;
   }
-  const int64_t n = (int64_t)a.E * a.d;
+  const int groups = a.d / 64;
+  const int e = blockIdx.x / groups;
+  const int col = (blockIdx.x - e * groups) * 64 + lane;
   const int64_t sstride = 2 * (int64_t)a.Ep * a.d;
-  T* dw = static_cast<T*>(a.dw);
-  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)nbw * NT) {
-    const int64_t e = i / a.d, col = i - e * a.d;
-    float hi = 0.0f, lo = 0.0f;
-    for (int s = 0; s < a.splits; ++s) {
-      hi += a.part[s * sstride + e * a.d + col];
-      lo += a.part[s * sstride + (a.Ep + e) * a.d + col];
+  const float* ph = a.part + (int64_t)e * a.d + col;
+  const float* pl = a.part + (int64_t)(a.Ep + e) * a.d + col;
+  float hi = 0.0f, lo = 0.0f;
+#pragma unroll 4
+  for (int s = wave; s < a.splits; s += NWV) {
+    hi += ph[s * sstride];
+    lo += pl[s * sstride];
+  }
+  sh[0][wave][lane] = hi;
+  sh[1][wave][lane] = lo;
+  __syncthreads();
+  if (wave == 0) {
+    float h = 0.0f, l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      h += sh[0][w][lane];
+      l += sh[1][w][lane];
     }
-    dw[i] = from_f32<T>(hi + lo);
+    static_cast<T*>(a.dw)[(int64_t)e * a.d + col] = from_f32<T>(h + l);
+  }
+}
+
+// out[i] = sum_s part[s][i] over the splits in order; 4 elements per thread.
+template <typename T>
+__global__ void __launch_bounds__(NT) split_reduce_kernel(SplitReduceArgs a) {
+  const int64_t n4 = a.n / 4;
+  T* out = static_cast<T*>(a.out);
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n4; i += (int64_t)gridDim.x * NT) {
+    f32x4 acc = *reinterpret_cast<const f32x4*>(a.part + 4 * i);
+    for (int s = 1; s < a.splits; ++s) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(a.part + (int64_t)s * a.n + 4 * i);
+      acc[0] += v[0]; acc[1] += v[1]; acc[2] += v[2]; acc[3] += v[3];
+    }
+    store4<T>(out + 4 * i, acc[0], acc[1], acc[2], acc[3]);
   }
 }
 
@@ -311,7 +354,7 @@ __global__ void __launch_bounds__(NT) unpermute_kernel(UnpermuteArgs a) {
 // ---- balancing statistic -----------------------------------------------------
 // Threads form a (token lane) x (expert) grid: EP2 = E rounded up to a power of
 // two experts per row of threads, NT / EP2 token lanes.
-constexpr int kAuxTokens = 256;
+constexpr int kAuxTokens = 128;
 
 __device__ __forceinline__ int pow2_at_least(int v) {
   int p = 1;
@@ -349,20 +392,32 @@ __global__ void __launch_bounds__(NT) aux_partials_kernel(AuxArgs a) {
   }
 }
 
-__device__ double block_sum_d(double v, double* sh) {
+// Sums (fixed order: butterfly within waves, then waves in index order) of K
+// values at once; every thread gets the results.
+template <int K>
+__device__ __forceinline__ void block_sum_d(double (&v)[K], double (*sh)[NT / 64]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  for (int i = 0; i < K; ++i)
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v[i] += __shfl_xor(v[i], o, 64);
   __syncthreads();
-  if (lane == 0) sh[wave] = v;
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < K; ++i) sh[i][wave] = v[i];
+  }
   __syncthreads();
-  double s = 0.0;
-  for (int w = 0; w < NT / 64; ++w) s += sh[w];
-  return s;
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    double s = 0.0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) s += sh[i][w];
+    v[i] = s;
+  }
 }
 
 __global__ void __launch_bounds__(NT) aux_finalize_kernel(AuxArgs a, int nblk) {
-  __shared__ double sh[NT / 64];
+  __shared__ double sh[6][NT / 64];
   __shared__ float cp[NT], ce[NT];
   __shared__ float colp[256], cole[256];
   const int EP2 = pow2_at_least(a.E);
@@ -401,12 +456,8 @@ __global__ void __launch_bounds__(NT) aux_finalize_kernel(AuxArgs a, int nblk) {
     a.f[e] = (float)f;
     a.p_mean[e] = (float)P;
   }
-  const double fp = block_sum_d(valid ? f * P : 0.0, sh);
-  const double ent_sum = block_sum_d(valid ? (double)ent : 0.0, sh);
-  const double csum = block_sum_d(cnt, sh);
-  const double mean = csum / a.E;
-  const double var = block_sum_d(valid ? (cnt - mean) * (cnt - mean) : 0.0, sh) / a.E;
-  const double unused = block_sum_d(valid && cnt == 0.0 ? 1.0 : 0.0, sh);
+  // pass 1: sum f P, entropy, counts, unused; min and max of the counts
+  double v1[4] = {valid ? f * P : 0.0, valid ? (double)ent : 0.0, cnt, (valid && cnt == 0.0) ? 1.0 : 0.0};
   double mn = valid ? cnt : 1e300, mx = valid ? cnt : -1.0;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -416,17 +467,22 @@ __global__ void __launch_bounds__(NT) aux_finalize_kernel(AuxArgs a, int nblk) {
   __shared__ double smn[NT / 64], smx[NT / 64];
   const int lane = e & 63, wave = e >> 6;
   if (lane == 0) { smn[wave] = mn; smx[wave] = mx; }
-  __syncthreads();
+  block_sum_d<4>(v1, sh);          // its barriers also publish smn / smx
+  const double mean = v1[2] / a.E;
+  // pass 2: population variance of the counts about their mean
+  double v2[1] = {valid ? (cnt - mean) * (cnt - mean) : 0.0};
+  block_sum_d<1>(v2, sh + 4);
   if (e == 0) {
     for (int w = 0; w < NT / 64; ++w) { mn = fmin(mn, smn[w]); mx = fmax(mx, smx[w]); }
+    const double var = v2[0] / a.E;
     moe_aux_out* o = static_cast<moe_aux_out*>(a.out);
-    o->aux = (float)(a.E * fp);
-    o->aux_raw = (float)fp;
-    o->entropy_mean = (T > 0) ? (float)(ent_sum / T) : 0.0f;
+    o->aux = (float)(a.E * v1[0]);
+    o->aux_raw = (float)v1[0];
+    o->entropy_mean = (T > 0) ? (float)(v1[1] / T) : 0.0f;
     o->count_cv = mean > 0 ? (float)(sqrt(var) / mean) : 0.0f;
     o->count_min = (int32_t)mn;
     o->count_max = (int32_t)mx;
-    o->n_unused = (int32_t)unused;
+    o->n_unused = (int32_t)v1[3];
     o->reserved = 0;
   }
 }
@@ -461,7 +517,7 @@ hipError_t launch_combine_bwd(int dt, const CombineBwdArgs& a, hipStream_t s) {
 
 int router_dz_blocks(int64_t T) {
   int64_t g = (T + 3) / 4;
-  if (g > 512) g = 512;
+  if (g > 4096) g = 4096;
   if (g < 1) g = 1;
   return (int)g;
 }
@@ -491,15 +547,29 @@ hipError_t launch_stack2(int dt, const Stack2Args& a, hipStream_t s) {
 }
 
 hipError_t launch_router_reduce(int dt, const RouterReduceArgs& a, hipStream_t s) {
-  const int64_t n = (int64_t)a.E * a.d;
-  int64_t nbw = (n + NT - 1) / NT;
-  if (nbw > 2048) nbw = 2048;
-  if (nbw < 1) nbw = 1;
+  if (a.d % 64) return hipErrorInvalidValue;
+  const int64_t nbw = (int64_t)a.E * (a.d / 64);
   const int64_t grid = nbw + (a.dbias ? a.E : 0);
+  if (grid == 0) return hipSuccess;
   switch (dt) {
-    case DT_BF16: hipLaunchKernelGGL(router_reduce_kernel<__bf16>, dim3((unsigned)grid), dim3(NT), 0, s, a, (int)nbw); break;
-    case DT_F16: hipLaunchKernelGGL(router_reduce_kernel<_Float16>, dim3((unsigned)grid), dim3(NT), 0, s, a, (int)nbw); break;
-    case DT_F32: hipLaunchKernelGGL(router_reduce_kernel<float>, dim3((unsigned)grid), dim3(NT), 0, s, a, (int)nbw); break;
+    case DT_BF16: hipLaunchKernelGGL(router_reduce_kernel<__bf16>, dim3((unsigned)grid), dim3(kReduceThreads), 0, s, a, (int)nbw); break;
+    case DT_F16: hipLaunchKernelGGL(router_reduce_kernel<_Float16>, dim3((unsigned)grid), dim3(kReduceThreads), 0, s, a, (int)nbw); break;
+    case DT_F32: hipLaunchKernelGGL(router_reduce_kernel<float>, dim3((unsigned)grid), dim3(kReduceThreads), 0, s, a, (int)nbw); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_split_reduce(int dt, const SplitReduceArgs& a, hipStream_t s) {
+  if (a.n % 4) return hipErrorInvalidValue;
+  const int64_t n4 = a.n / 4;
+  if (n4 == 0) return hipSuccess;
+  int64_t grid = (n4 + NT - 1) / NT;
+  if (grid > 8192) grid = 8192;
+  switch (dt) {
+    case DT_BF16: hipLaunchKernelGGL(split_reduce_kernel<__bf16>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    case DT_F16: hipLaunchKernelGGL(split_reduce_kernel<_Float16>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    case DT_F32: hipLaunchKernelGGL(split_reduce_kernel<float>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -304,14 +304,20 @@ __device__ __forceinline__ void dma16(rsrc_t rs, char* lds_lane0, uint32_t voff)
 }
 
 // Tile configurations of the direct-load path (BM = BN):
-//   128 x 128: 4 waves (2 x 2), a 4-stage ring of 64-byte k chunks (loads run
-//              three chunks ahead), 64 KB of LDS: two workgroups per CU;
+//   128 x 128: 4 waves (2 x 2), a ring of 64-byte k chunks: 3 stages (48 KB,
+//              three workgroups per CU) for the row GEMMs, 4 stages (64 KB,
+//              loads three chunks ahead, two workgroups per CU) for the weight
+//              gradients, whose workgroups run long K loops;
 //   256 x 256: 8 waves (2 along rows x 4 along columns, 128 x 64 per wave), a
 //              2-stage ring of 128-byte k chunks (each row's chunk is one full
 //              cache line), 128 KB of LDS: one workgroup per CU.
-template <int BM> struct TileCfg;
-template <> struct TileCfg<128> { static constexpr int WM = 2, WN = 2, DKB = 64, NSTG = 4, THREADS = 256; };
-template <> struct TileCfg<256> { static constexpr int WM = 2, WN = 4, DKB = 128, NSTG = 2, THREADS = 512; };
+template <int BM, bool WGRAD> struct TileCfg;
+template <bool WGRAD> struct TileCfg<128, WGRAD> {
+  static constexpr int WM = 2, WN = 2, DKB = 64, NSTG = WGRAD ? 4 : 3, THREADS = 256;
+};
+template <bool WGRAD> struct TileCfg<256, WGRAD> {
+  static constexpr int WM = 2, WN = 4, DKB = 128, NSTG = 2, THREADS = 512;
+};
 
 // vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding)
 template <int N>
@@ -413,7 +419,7 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
   constexpr int MS = WTM / 32, NS = WTN / 32;
   constexpr int STAGE = PO::BYTES + QO::BYTES;
 
-  constexpr int DKB = TileCfg<BM>::DKB, NSTG = TileCfg<BM>::NSTG;
+  constexpr int DKB = TileCfg<BM, false>::DKB, NSTG = TileCfg<BM, false>::NSTG;
   constexpr int SCAN_OFF = (ES == 2) ? NSTG * (BM + BN) * DKB : 2 * STAGE;
   int* s_scan = reinterpret_cast<int*>(smem + SCAN_OFF);      // [NW] wave sums, [NW..NW+1] located tile
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -771,7 +777,7 @@ __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
   zero_acc(acc);
 
   if constexpr (ES == 2) {
-    constexpr int DKB = TileCfg<BM>::DKB, NSTG = TileCfg<BM>::NSTG;
+    constexpr int DKB = TileCfg<BM, true>::DKB, NSTG = TileCfg<BM, true>::NSTG;
     using PD = DmaKmajor<BM, NW, DKB>;
     using QD = DmaKmajor<BN, NW, DKB>;
     constexpr int DSTAGE = PD::BYTES + QD::BYTES;
@@ -863,10 +869,10 @@ __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
 
 // Dynamic LDS of one kernel: the 4-stage ring (16-bit) or two stages of the
 // larger operand pair (f32), plus the schedule scratch of the row GEMMs.
-template <typename T, int BM, int BN>
+template <typename T, int BM, int BN, bool WGRAD>
 constexpr size_t smem_for() {
   if constexpr (sizeof(T) == 2) {
-    return (size_t)TileCfg<BM>::NSTG * (BM + BN) * TileCfg<BM>::DKB + 64;   // direct-load ring
+    return (size_t)TileCfg<BM, WGRAD>::NSTG * (BM + BN) * TileCfg<BM, WGRAD>::DKB + 64;   // direct-load ring
   } else {
     constexpr int nn = Operand<T, BM, false>::BYTES + Operand<T, BN, false>::BYTES;
     constexpr int nt = Operand<T, BM, false>::BYTES + Operand<T, BN, true>::BYTES;
@@ -883,14 +889,14 @@ constexpr size_t smem_for() {
 // One plainly named kernel per (operation, dtype, tile) so profiles read well.
 
 #define MOE_ROW_KERNEL(NAME, T, BM, BN, OP, EPI)                                                    \
-  extern "C" __global__ void __launch_bounds__(TileCfg<BM>::THREADS) NAME(RowGemmArgs a) {       \
+  extern "C" __global__ void __launch_bounds__((TileCfg<BM, false>::THREADS)) NAME(RowGemmArgs a) {  \
     extern __shared__ __attribute__((aligned(16))) char smem[];                                   \
-    row_gemm_body<T, BM, BN, OP, EPI, TileCfg<BM>::WM, TileCfg<BM>::WN>(a, smem);              \
+    row_gemm_body<T, BM, BN, OP, EPI, TileCfg<BM, false>::WM, TileCfg<BM, false>::WN>(a, smem);    \
   }
 #define MOE_WGRAD_KERNEL(NAME, T, BM, BN, F32)                                                      \
-  extern "C" __global__ void __launch_bounds__(TileCfg<BM>::THREADS) NAME(WgradArgs a) {         \
+  extern "C" __global__ void __launch_bounds__((TileCfg<BM, true>::THREADS)) NAME(WgradArgs a) {    \
     extern __shared__ __attribute__((aligned(16))) char smem[];                                   \
-    wgrad_body<T, BM, BN, F32, TileCfg<BM>::WM, TileCfg<BM>::WN>(a, smem);                     \
+    wgrad_body<T, BM, BN, F32, TileCfg<BM, true>::WM, TileCfg<BM, true>::WN>(a, smem);             \
   }
 
 #define MOE_KERNEL_SET(T, TN, BM, BN)                                                                      \
@@ -902,6 +908,8 @@ constexpr size_t smem_for() {
   MOE_ROW_KERNEL(moe_gemm_router_dx_f32out_##TN##_##BM##x##BN, T, BM, BN, OP_ROUTER_DX, EPI_STORE_F32)     \
   MOE_WGRAD_KERNEL(moe_wgrad_down_##TN##_##BM##x##BN, T, BM, BN, 0)                                        \
   MOE_WGRAD_KERNEL(moe_wgrad_gate_up_##TN##_##BM##x##BN, T, BM, BN, 0)                                     \
+  MOE_WGRAD_KERNEL(moe_wgrad_down_f32out_##TN##_##BM##x##BN, T, BM, BN, 1)                                 \
+  MOE_WGRAD_KERNEL(moe_wgrad_gate_up_f32out_##TN##_##BM##x##BN, T, BM, BN, 1)                              \
   MOE_WGRAD_KERNEL(moe_wgrad_router_f32out_##TN##_##BM##x##BN, T, BM, BN, 1)
 
 MOE_KERNEL_SET(__bf16, bf16, 256, 256)
@@ -917,8 +925,8 @@ typedef void (*WgradKernel)(WgradArgs);
 
 struct KernelSet {
   RowKernel gu, down, down_f32, down_dgrad, gu_dgrad, router_dx_f32;
-  WgradKernel wgrad_down, wgrad_gate_up, wgrad_router_f32;
-  size_t lds;
+  WgradKernel wgrad_down, wgrad_gate_up, wgrad_down_f32, wgrad_gate_up_f32, wgrad_router_f32;
+  size_t lds_row, lds_wgrad;
 };
 
 #define MOE_KERNEL_TABLE(T, TN, BM, BN)                                                                 \
@@ -926,7 +934,9 @@ struct KernelSet {
             moe_gemm_down_f32out_##TN##_##BM##x##BN, moe_gemm_down_dgrad_swiglu_##TN##_##BM##x##BN,     \
             moe_gemm_gate_up_dgrad_##TN##_##BM##x##BN, moe_gemm_router_dx_f32out_##TN##_##BM##x##BN,       \
             moe_wgrad_down_##TN##_##BM##x##BN, moe_wgrad_gate_up_##TN##_##BM##x##BN,                      \
-            moe_wgrad_router_f32out_##TN##_##BM##x##BN, smem_for<T, BM, BN>()}
+            moe_wgrad_down_f32out_##TN##_##BM##x##BN, moe_wgrad_gate_up_f32out_##TN##_##BM##x##BN,        \
+            moe_wgrad_router_f32out_##TN##_##BM##x##BN, smem_for<T, BM, BN, false>(),                  \
+            smem_for<T, BM, BN, true>()}
 
 const KernelSet* kernel_set(int dt, int tile) {
   static const KernelSet bf16_256 = MOE_KERNEL_TABLE(__bf16, bf16, 256, 256);
@@ -975,10 +985,10 @@ hipError_t launch_row_gemm(int dt, int op, int epi, int tile, const RowGemmArgs&
   grid = (grid + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipError_t e = prepare((const void*)k, set->lds);
+  hipError_t e = prepare((const void*)k, set->lds_row);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(tile == 256 ? TileCfg<256>::THREADS : TileCfg<128>::THREADS),
-                     set->lds, s, a);
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(tile == 256 ? 512 : 256),
+                     set->lds_row, s, a);
   return hipGetLastError();
 }
 
@@ -987,21 +997,21 @@ hipError_t launch_wgrad(int dt, int op, int tile, const WgradArgs& a, hipStream_
   if (!set) return hipErrorInvalidValue;
   WgradKernel k = nullptr;
   switch (op) {
-    case WG_DOWN: k = set->wgrad_down; break;
-    case WG_GATE_UP: k = set->wgrad_gate_up; break;
+    case WG_DOWN: k = a.out_f32 ? set->wgrad_down_f32 : set->wgrad_down; break;
+    case WG_GATE_UP: k = a.out_f32 ? set->wgrad_gate_up_f32 : set->wgrad_gate_up; break;
     case WG_ROUTER: k = set->wgrad_router_f32; break;
     default: return hipErrorInvalidValue;
   }
-  if ((op == WG_ROUTER) != (a.out_f32 != 0)) return hipErrorInvalidValue;
+  if (op == WG_ROUTER && !a.out_f32) return hipErrorInvalidValue;
   if (a.M % tile || a.N % tile) return hipErrorInvalidValue;
   int64_t grid = (int64_t)a.G * a.splits * (a.M / tile) * (a.N / tile);
   grid = (grid + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipError_t e = prepare((const void*)k, set->lds);
+  hipError_t e = prepare((const void*)k, set->lds_wgrad);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(tile == 256 ? TileCfg<256>::THREADS : TileCfg<128>::THREADS),
-                     set->lds, s, a);
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(tile == 256 ? 512 : 256),
+                     set->lds_wgrad, s, a);
   return hipGetLastError();
 }
 

@@ -120,6 +120,15 @@ struct RouterReduceArgs {
 };
 hipError_t launch_router_reduce(int dt, const RouterReduceArgs& a, hipStream_t s);
 
+// Deterministic sum of split-K partials: out[i] = sum_s part[s * n + i] (s in
+// order), rounded once to the output dtype.
+struct SplitReduceArgs {
+  const float* part;     // [splits, n]
+  int64_t n; int splits;
+  void* out;             // [n] act
+};
+hipError_t launch_split_reduce(int dt, const SplitReduceArgs& a, hipStream_t s);
+
 // dx = gathered dX_perm rows (+ dx_shared) + router input gradient
 struct UnpermuteArgs {
   const void* dx_perm;     // [T*k, d]

@@ -55,6 +55,22 @@ def test_tile_engines_match_oracle(wl, tile, monkeypatch):
     PT.full_parity(wl)
 
 
+# Weight gradients split over tokens (f32 partials, summed in order), including
+# experts with fewer tokens than splits (empty splits write zero partials).
+SPLIT = [
+    W("t4096_d256_e8k2_i256_bf16_shared1", T=4096, d=256, E=8, k=2, I=256, n_shared=1, I_shared=256),
+    W("t1000_d256_e64k6_i128_f16_shared2", T=1000, d=256, E=64, k=6, I=128, n_shared=2, I_shared=128,
+      dtype="f16"),
+]
+
+
+@pytest.mark.parametrize("splits", [2, 3])
+@pytest.mark.parametrize("wl", SPLIT, ids=[w.name for w in SPLIT])
+def test_split_weight_gradients_match_oracle(wl, splits, monkeypatch):
+    monkeypatch.setenv("MOE_WGRAD_SPLITS", str(splits))
+    PT.full_parity(wl)
+
+
 def test_tiny_reference_workload():
     PT.full_parity(MI.WORKLOADS[MI.TINY])
 
