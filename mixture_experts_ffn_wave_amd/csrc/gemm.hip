@@ -312,11 +312,14 @@ __device__ __forceinline__ void dma16(rsrc_t rs, char* lds_lane0, uint32_t voff)
 //              2-stage ring of 128-byte k chunks (each row's chunk is one full
 //              cache line), 128 KB of LDS: one workgroup per CU.
 template <int BM, bool WGRAD> struct TileCfg;
+// WAVES_PER_EU: register budget of the row kernels (3 waves per SIMD for the
+// 3-workgroup 128 x 128 tiles: the compiler then keeps the accumulators in
+// VGPRs and stays within 168 registers).
 template <bool WGRAD> struct TileCfg<128, WGRAD> {
-  static constexpr int WM = 2, WN = 2, DKB = 64, NSTG = WGRAD ? 4 : 3, THREADS = 256;
+  static constexpr int WM = 2, WN = 2, DKB = 64, NSTG = WGRAD ? 4 : 3, THREADS = 256, WAVES_PER_EU = 3;
 };
 template <bool WGRAD> struct TileCfg<256, WGRAD> {
-  static constexpr int WM = 2, WN = 4, DKB = 128, NSTG = 2, THREADS = 512;
+  static constexpr int WM = 2, WN = 4, DKB = 128, NSTG = 2, THREADS = 512, WAVES_PER_EU = 2;
 };
 
 // vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding)
@@ -484,33 +487,39 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
   static_assert(acc_col<PERM>(RUN, 0) == RSTEP && acc_col<PERM>(0, 1) == RUN, "run layout");
   const int h = lane >> 5;
 
-  // SwiGLU backward needs the saved G and U of each output element.  Those of
-  // the first PMS row subtiles (at most PRE_BUDGET VGPRs' worth) are loaded here,
-  // before the main loop, so that the loads' latency hides behind it (the
-  // first ring barrier, which waits for the older loads too, is where they
-  // are complete); the rest are loaded in the epilogue.
-  constexpr int PRE_REGS_PER_MS = NS * NRUN * 8;
-  constexpr int PRE_BUDGET = NW == 4 ? 64 : 32;               // 8-wave tiles keep 128 accumulator VGPRs
-  constexpr int PMS = (EPI == EPI_SWIGLU_BWD && PERM) ? (PRE_BUDGET / PRE_REGS_PER_MS < MS ? PRE_BUDGET / PRE_REGS_PER_MS : MS) : 0;
-  u32x4 gpre[PMS > 0 ? PMS : 1][NS][NRUN], upre[PMS > 0 ? PMS : 1][NS][NRUN];
-  if constexpr (PMS > 0) {
+  // ---- epilogue staging geometry (16-bit path).  The epilogue runs in MS
+  // passes of SR = 32 WM rows (row subtile ms of every wave row); each pass
+  // goes through LDS so that global loads and stores move whole rows of the
+  // tile: row r of a staged array is RB bytes, 16-byte chunk c at position
+  // c ^ (r & 7) (conflict-free both for the MFMA-layout accesses, 8 rows per
+  // chunk index, and for the row-wise ones).
+  constexpr int SR = 32 * WM;
+  constexpr int NARR = EPI == EPI_SWIGLU_FWD ? 3 : (EPI == EPI_SWIGLU_BWD ? 2 : 1);
+  constexpr int RB = EPI == EPI_STORE_F32 ? BN * 4 : (EPI == EPI_SWIGLU_FWD ? BN : BN * 2);
+  constexpr int CPR = RB / 16;                              // chunks per staged row
+  constexpr int SITER = SR * CPR / (64 * NW);               // row-wise chunks per thread per array
+  static_assert(!PERM || (CPR >= 8 && SITER >= 1 && SITER * 64 * NW == SR * CPR), "staging geometry");
+  // tile row of staged row sr in pass ms
+  auto srow = [&](int sr, int ms) { return (sr / 32) * WTM + ms * 32 + (sr % 32); };
+  static_assert(!PERM || NARR * SR * RB <= NSTG * (BM + BN) * DKB, "staging fits in the ring's LDS");
+  // first packed [G | U] column of this tile's H columns n0.. (SwiGLU epilogues)
+  const int gblk = n0 / a.sub;
+  const int gcol0 = gblk * 2 * a.sub + (n0 - gblk * a.sub);
+
+  // SwiGLU backward: the saved G and U of one pass, whole rows of the tile.
+  // (Loading them before the main loop instead costs VGPRs enough to drop
+  // a workgroup per CU, which was slower.)
+  auto load_gu_rows = [&](u32x4 (&dst)[2][PERM ? SITER : 1], int ms) {
     const T* aux = static_cast<const T*>(a.aux);
 #pragma unroll
-    for (int ms = 0; ms < PMS; ++ms) {
-      const int ml = prow[ms] + (lane & 31);
-#pragma unroll
-      for (int ns = 0; ns < NS; ++ns)
-#pragma unroll
-        for (int t = 0; t < NRUN; ++t) {
-          const int n = n0 + qrow[ns] + RSTEP * t + RUN * h;
-          const int blk = n / a.sub;
-          const int gcol = blk * 2 * a.sub + (n - blk * a.sub);
-          const T* gu = aux + (row0 + ml) * a.ldaux + gcol;
-          gpre[ms][ns][t] = (ml < rows) ? ld16(gu) : (u32x4){0u, 0u, 0u, 0u};
-          upre[ms][ns][t] = (ml < rows) ? ld16(gu + a.sub) : (u32x4){0u, 0u, 0u, 0u};
-        }
+    for (int i = 0; i < SITER; ++i) {
+      const int q = tid + 64 * NW * i, sr = q / CPR, c = q % CPR;
+      const int tr = srow(sr, ms);
+      const T* src = aux + (row0 + tr) * a.ldaux + gcol0 + c * 8;
+      dst[0][i] = (tr < rows) ? ld16(src) : (u32x4){0u, 0u, 0u, 0u};
+      dst[1][i] = (tr < rows) ? ld16(src + a.sub) : (u32x4){0u, 0u, 0u, 0u};
     }
-  }
+  };
 
   if constexpr (ES == 2) {
     // ---------------- direct-to-LDS main loop (16-bit types)
@@ -661,14 +670,112 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
   }
   }  // main loops
 
-  // ---- epilogue: accumulator [ns][ms] holds row prow[ms] + lane%32 of the tile
+  if constexpr (PERM) {
+    // ---- staged epilogue (16-bit path)
+    // LDS barrier without the release fence of __syncthreads(), which would
+    // also wait for this wave's outstanding global stores
+    auto lds_barrier = [&]() {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    auto sp = [&](int arr, int sr, int c) -> char* {
+      return smem + arr * SR * RB + sr * RB + ((c ^ (sr & 7)) << 4);
+    };
+    const int sr_l = wm * 32 + (lane & 31);                   // this lane's staged row
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+      lds_barrier();                                          // ring / previous pass no longer read
+      if constexpr (EPI == EPI_SWIGLU_BWD) {
+        u32x4 cur[2][SITER];
+        load_gu_rows(cur, ms);
+#pragma unroll
+        for (int i = 0; i < SITER; ++i) {
+          const int q = tid + 64 * NW * i, sr = q / CPR, c = q % CPR;
+          st16(sp(0, sr, c), cur[0][i]);
+          st16(sp(1, sr, c), cur[1][i]);
+        }
+        lds_barrier();
+      }
+      // accumulators -> staging (MFMA layout: 8 consecutive columns per run)
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns) {
+        if constexpr (EPI == EPI_SWIGLU_FWD) {
+          if (ns >= NS / 2) continue;
+        }
+#pragma unroll
+        for (int t = 0; t < NRUN; ++t) {
+          float v[RUN];
+#pragma unroll
+          for (int i = 0; i < RUN; ++i) v[i] = acc[ns][ms][RUN * t + i];
+          if constexpr (EPI == EPI_STORE) {
+            const int c = (qrow[ns] + RSTEP * t + RUN * h) / 8;
+            store8<T>(reinterpret_cast<T*>(sp(0, sr_l, c)), v);
+          } else if constexpr (EPI == EPI_STORE_F32) {
+            const int c = (qrow[ns] + RSTEP * t + RUN * h) / 4;
+            store4<float>(reinterpret_cast<float*>(sp(0, sr_l, c)), v[0], v[1], v[2], v[3]);
+            store4<float>(reinterpret_cast<float*>(sp(0, sr_l, c + 1)), v[4], v[5], v[6], v[7]);
+          } else if constexpr (EPI == EPI_SWIGLU_FWD) {
+            // gate subtile ns pairs with up subtile ns + NS/2 (same H columns)
+            const int c = (wn * (WTN / 2) + ns * 32 + RSTEP * t + RUN * h) / 8;
+            float uv[RUN], hv[RUN];
+#pragma unroll
+            for (int i = 0; i < RUN; ++i) {
+              uv[i] = acc[ns + NS / 2][ms][RUN * t + i];
+              hv[i] = silu_f(v[i]) * uv[i];
+            }
+            store8<T>(reinterpret_cast<T*>(sp(0, sr_l, c)), v);
+            store8<T>(reinterpret_cast<T*>(sp(1, sr_l, c)), uv);
+            store8<T>(reinterpret_cast<T*>(sp(2, sr_l, c)), hv);
+          } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+            // v = dH; G, U staged at the same positions, overwritten by dG, dU
+            const int c = (qrow[ns] + RSTEP * t + RUN * h) / 8;
+            float G[RUN], U[RUN], dG[RUN], dU[RUN];
+            unpack8<T>(ld16(sp(0, sr_l, c)), G);
+            unpack8<T>(ld16(sp(1, sr_l, c)), U);
+#pragma unroll
+            for (int i = 0; i < RUN; ++i) {
+              const float sg = sigmoid_f(G[i]);
+              dG[i] = v[i] * U[i] * sg * (1.0f + G[i] * (1.0f - sg));
+              dU[i] = v[i] * G[i] * sg;
+            }
+            store8<T>(reinterpret_cast<T*>(sp(0, sr_l, c)), dG);
+            store8<T>(reinterpret_cast<T*>(sp(1, sr_l, c)), dU);
+          }
+        }
+      }
+      lds_barrier();
+      // staging -> global, whole rows
+#pragma unroll
+      for (int i = 0; i < SITER; ++i) {
+        const int q = tid + 64 * NW * i, sr = q / CPR, c = q % CPR;
+        const int tr = srow(sr, ms);
+        if (tr >= rows) continue;
+        const int64_t row = row0 + tr;
+        if constexpr (EPI == EPI_STORE) {
+          st16(static_cast<T*>(a.C) + row * a.ldc + n0 + c * 8, ld16(sp(0, sr, c)));
+        } else if constexpr (EPI == EPI_STORE_F32) {
+          st16(static_cast<float*>(a.C) + row * a.ldc + n0 + c * 4, ld16(sp(0, sr, c)));
+        } else if constexpr (EPI == EPI_SWIGLU_FWD) {
+          T* gu = static_cast<T*>(a.C) + row * a.ldc + gcol0 + c * 8;
+          st16(gu, ld16(sp(0, sr, c)));
+          st16(gu + a.sub, ld16(sp(1, sr, c)));
+          st16(static_cast<T*>(a.C2) + row * a.ldc2 + n0 + c * 8, ld16(sp(2, sr, c)));
+        } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+          T* dgu = static_cast<T*>(a.C) + row * a.ldc + gcol0 + c * 8;
+          st16(dgu, ld16(sp(0, sr, c)));
+          st16(dgu + a.sub, ld16(sp(1, sr, c)));
+        }
+      }
+    }
+  } else {
+  // ---- direct epilogue (f32 path): accumulator [ns][ms] holds row prow[ms] + lane%32
 #pragma unroll
   for (int ms = 0; ms < MS; ++ms) {
     const int ml = prow[ms] + (lane & 31);
     if (ml >= rows) continue;
     const int64_t row = row0 + ml;
     if constexpr (EPI == EPI_SWIGLU_FWD) {
-      // gate subtile j pairs with up subtile j + NS/2 (same H columns)
 #pragma unroll
       for (int j = 0; j < NS / 2; ++j)
 #pragma unroll
@@ -702,20 +809,12 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
           } else if constexpr (EPI == EPI_STORE_F32) {
             store_run<float, RUN>(static_cast<float*>(a.C) + row * a.ldc + n, v);
           } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-            // v = dH for H columns n..; G, U saved in the packed [G | U] layout
             const int blk = n / a.sub;
             const int gcol = blk * 2 * a.sub + (n - blk * a.sub);
             float G[RUN], U[RUN], dG[RUN], dU[RUN];
-            if (PMS > 0 && ms < PMS) {
-              if constexpr (PMS > 0) {
-                unpack8<T>(gpre[ms < PMS ? ms : 0][ns][t], G);
-                unpack8<T>(upre[ms < PMS ? ms : 0][ns][t], U);
-              }
-            } else {
-              const T* gu = static_cast<const T*>(a.aux) + row * a.ldaux;
-              load_run<T, RUN>(gu + gcol, G);
-              load_run<T, RUN>(gu + gcol + a.sub, U);
-            }
+            const T* gu = static_cast<const T*>(a.aux) + row * a.ldaux;
+            load_run<T, RUN>(gu + gcol, G);
+            load_run<T, RUN>(gu + gcol + a.sub, U);
 #pragma unroll
             for (int i = 0; i < RUN; ++i) {
               const float sg = sigmoid_f(G[i]);
@@ -728,6 +827,7 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
           }
         }
     }
+  }
   }
 }
 
@@ -889,7 +989,8 @@ constexpr size_t smem_for() {
 // One plainly named kernel per (operation, dtype, tile) so profiles read well.
 
 #define MOE_ROW_KERNEL(NAME, T, BM, BN, OP, EPI)                                                    \
-  extern "C" __global__ void __launch_bounds__((TileCfg<BM, false>::THREADS)) NAME(RowGemmArgs a) {  \
+  extern "C" __global__ void __launch_bounds__((TileCfg<BM, false>::THREADS))                   \
+      __attribute__((amdgpu_waves_per_eu(TileCfg<BM, false>::WAVES_PER_EU))) NAME(RowGemmArgs a) {  \
     extern __shared__ __attribute__((aligned(16))) char smem[];                                   \
     row_gemm_body<T, BM, BN, OP, EPI, TileCfg<BM, false>::WM, TileCfg<BM, false>::WN>(a, smem);    \
   }
