@@ -7,7 +7,10 @@ the HIP library (no kernels, headers, helpers, tables or pre/post-processing);
 both sides receive the same seeded inputs and nothing else.
 
 Every floating-point step here is computed in float64 with numpy, from the
-device-rounded inputs upcast exactly to float64, with no intermediate rounding.
+device-rounded inputs upcast exactly to float64.  By default nothing in
+between is rounded (the exact layer); ``layer_forward`` / ``layer_backward``
+take an optional ``store`` rounding that is applied only to the values the
+layer keeps in its storage dtype (the bf16 / f16 layer of the pages).
 """
 
 from .moe_oracle import (  # noqa: F401
@@ -27,3 +30,4 @@ from .moe_oracle import (  # noqa: F401
     layer_loss,
 )
 from .mx import mx_fake_quant, e4m3_round, mx_block_scale  # noqa: F401
+from .rounding import round_to_format  # noqa: F401

@@ -201,15 +201,29 @@ def aux_statistics(p, counts, top_k):
 
 # ------------------------------------------------------------ layer passes ---
 
+def _no_store(a, kind):
+    return a
+
+
 def layer_forward(x, w_router, w_gate_up, w_down, *, top_k, renorm=True, bias=None,
-                  ws_gate_up=None, ws_down=None, quant=None):
+                  ws_gate_up=None, ws_down=None, quant=None, store=None):
     """Full forward pass.  Returns a dict of every intermediate.
 
     ``quant``, if given, is applied to each operand of each expert GEMM as
     quant(array, axis) with ``axis`` the contraction axis of that GEMM (the MX
     fake-quant mode); the router, softmax and combine are never quantised.
+
+    ``store``, if given, is store(array, kind) and rounds the values the layer
+    keeps between its steps to their storage format: kind "act" for the gate
+    and up pre-activations G, U, the activation H and the shared experts'
+    output (the activation dtype), kind "f32" for the routed experts' output
+    rows Y_perm.  The layer is trained in that dtype (spark-gpt README:
+    BF16 grouped GEMM; KochiLLM model card: fp16 training), so this is the
+    layer those pages run; with store=None the exact layer is computed.
+    Products and sums are exact either way.
     """
     q = quant if quant is not None else (lambda a, axis: a)
+    st = store if store is not None else _no_store
     T, d = x.shape
     E = w_router.shape[0]
     z = router_logits(x, w_router, bias)
@@ -230,9 +244,9 @@ def layer_forward(x, w_router, w_gate_up, w_down, *, top_k, renorm=True, bias=No
         wgu = q(w_gate_up[e], 1)
         ge = xr @ wgu[:inter].T
         ue = xr @ wgu[inter:].T
-        he = silu(ge) * ue
-        g[r0:r1], u[r0:r1], h[r0:r1] = ge, ue, he
-        y_perm[r0:r1] = q(he, 1) @ q(w_down[e], 1).T
+        he = st(silu(ge) * ue, "act")
+        g[r0:r1], u[r0:r1], h[r0:r1] = st(ge, "act"), st(ue, "act"), he
+        y_perm[r0:r1] = st(q(he, 1) @ q(w_down[e], 1).T, "f32")
     y_shared = None
     shared = []
     if ws_gate_up is not None and ws_gate_up.shape[0] > 0:
@@ -243,16 +257,17 @@ def layer_forward(x, w_router, w_gate_up, w_down, *, top_k, renorm=True, bias=No
             wgu = q(ws_gate_up[s], 1)
             gs = xq @ wgu[:inter_s].T
             us = xq @ wgu[inter_s:].T
-            hs = silu(gs) * us
+            hs = st(silu(gs) * us, "act")
             y_shared += q(hs, 1) @ q(ws_down[s], 1).T
-            shared.append((gs, us, hs))
+            shared.append((st(gs, "act"), st(us, "act"), hs))
+        y_shared = st(y_shared, "act")
     y = combine(y_perm, inv, w, y_shared)
     return dict(z=z, p=p, idx=idx, w=w, counts=counts, offsets=offsets,
                 perm_token=perm_token, inv=inv, x_perm=x_perm, g=g, u=u, h=h,
                 y_perm=y_perm, y_shared=y_shared, shared=shared, y=y,
                 x=x, w_router=w_router, w_gate_up=w_gate_up, w_down=w_down,
                 ws_gate_up=ws_gate_up, ws_down=ws_down, top_k=top_k,
-                renorm=renorm, bias=bias)
+                renorm=renorm, bias=bias, store=store)
 
 
 def layer_backward(fwd, dy, *, aux_coef=0.0, quant=None):
@@ -261,8 +276,15 @@ def layer_backward(fwd, dy, *, aux_coef=0.0, quant=None):
 
     f_e is an integer count and carries no gradient; P_e does (spark-gpt MoE
     paragraph: counts without gradient, a differentiable stand-in).
+
+    With the forward's ``store`` rounding, the gradients the layer keeps
+    between its steps are rounded too: dY_perm, [dG | dU] and dX_perm of the
+    routed experts and the shared experts' [dG | dU] and input gradient (kind
+    "act"); the router's logit gradient dz (kind "f32").  Final outputs are
+    not rounded.
     """
     q = quant if quant is not None else (lambda a, axis: a)
+    st = fwd.get("store") or _no_store
     x, w_r = fwd["x"], fwd["w_router"]
     w_gate_up, w_down = fwd["w_gate_up"], fwd["w_down"]
     p, idx, w, inv = fwd["p"], fwd["idx"], fwd["w"], fwd["inv"]
@@ -276,7 +298,7 @@ def layer_backward(fwd, dy, *, aux_coef=0.0, quant=None):
     y_rows = fwd["y_perm"][inv]                       # [T, k, d]
     gsc = np.einsum("td,tjd->tj", dy, y_rows)         # dL/dw_tj
     dy_perm = np.zeros_like(fwd["y_perm"])
-    dy_perm[inv.reshape(-1)] = (w[:, :, None] * dy[:, None, :]).reshape(-1, d)
+    dy_perm[inv.reshape(-1)] = st((w[:, :, None] * dy[:, None, :]).reshape(-1, d), "act")
 
     dw_gate_up = np.zeros_like(w_gate_up)
     dw_down = np.zeros_like(w_down)
@@ -292,8 +314,8 @@ def layer_backward(fwd, dy, *, aux_coef=0.0, quant=None):
         sg = _sigmoid(G)
         dG = dH * U * sg * (1.0 + G * (1.0 - sg))
         dU = dH * silu(G)
-        dGU = np.concatenate([dG, dU], axis=1)
-        dx_perm[r0:r1] = q(dGU, 1) @ q(w_gate_up[e], 0)
+        dGU = st(np.concatenate([dG, dU], axis=1), "act")
+        dx_perm[r0:r1] = st(q(dGU, 1) @ q(w_gate_up[e], 0), "act")
         dw_gate_up[e] = q(dGU, 0).T @ q(fwd["x_perm"][r0:r1], 0)
 
     dx = np.zeros((T, d))
@@ -311,9 +333,11 @@ def layer_backward(fwd, dy, *, aux_coef=0.0, quant=None):
             sg = _sigmoid(G)
             dG = dH * U * sg * (1.0 + G * (1.0 - sg))
             dU = dH * silu(G)
-            dGU = np.concatenate([dG, dU], axis=1)
-            dx += q(dGU, 1) @ q(ws_gu[s], 0)
+            dGU = st(np.concatenate([dG, dU], axis=1), "act")
+            dx_s = q(dGU, 1) @ q(ws_gu[s], 0)
+            dx_shared = dx_s if s == 0 else dx_shared + dx_s
             dws_gu[s] = q(dGU, 0).T @ q(x, 0)
+        dx += st(dx_shared, "act")
         grads["dws_gate_up"] = dws_gu
         grads["dws_down"] = dws_d
 
@@ -329,7 +353,7 @@ def layer_backward(fwd, dy, *, aux_coef=0.0, quant=None):
     if aux_coef != 0.0:
         f = np.asarray(counts, dtype=np.float64) / (T * k)
         dp = dp + aux_coef * E * f[None, :] / T
-    dz = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    dz = st(p * (dp - (p * dp).sum(axis=1, keepdims=True)), "f32")
     grads["dw_router"] = dz.T @ x
     grads["dbias"] = dz.sum(axis=0)
     dx += dz @ w_r

@@ -453,3 +453,57 @@ def test_expert_shape_matches_printed_parameter_counts():
     active = nl * (s["top_k"] * per_expert + attn + norms + router) + d + emb
     assert round(total / 1e6) == gold["printed_total_params_millions"]
     assert abs(active / 1e6 - gold["printed_active_params_millions"]) < 0.05
+
+
+# ------------------------------------------------------ storage-format rounding
+
+@pytest.mark.parametrize("fmt,tdt", [("bf16", torch.bfloat16), ("f16", torch.float16)])
+def test_round_to_format_matches_library_conversion(fmt, tdt):
+    """Every float32 value, across normal, subnormal and overflowing
+    magnitudes, rounds as the library's float32 -> fmt conversion (nearest,
+    ties to even)."""
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-110, 25, 200000))).astype(np.float32)
+    ref = torch.from_numpy(x).to(tdt).to(torch.float64).numpy()
+    got = O.round_to_format(x.astype(np.float64), fmt)
+    assert np.array_equal(ref, got)
+
+
+def test_round_to_format_hand_values():
+    r = O.round_to_format
+    # bf16 keeps 8 significant bits: 1 + 2^-8 is a tie between 1 and 1 + 2^-7 -> even (1)
+    assert r(1.0 + 2.0 ** -8, "bf16") == 1.0
+    assert r(1.0 + 3 * 2.0 ** -8, "bf16") == 1.0 + 2.0 ** -6       # tie -> even mantissa
+    assert r(1.0 + 2.0 ** -8 + 2.0 ** -20, "bf16") == 1.0 + 2.0 ** -7
+    # f16: largest finite 65504; 65520 is the tie with 65536 -> overflows to inf
+    assert r(65504.0, "f16") == 65504.0 and r(65519.0, "f16") == 65504.0
+    assert np.isinf(r(65520.0, "f16"))
+    # f16 subnormals are multiples of 2^-24
+    assert r(3 * 2.0 ** -26, "f16") == 2.0 ** -24
+    assert r(2.0 ** -25, "f16") == 0.0                               # tie -> even (0)
+    assert r(0.0, "bf16") == 0.0 and r(-2.5, "f32") == -2.5
+
+
+def test_storage_rounding_lands_on_the_stated_values_only():
+    """With a bf16 store, the kept intermediates are bf16 numbers (Y_perm and
+    dz f32 numbers); an identity store reproduces the exact layer bit for bit."""
+    L = rand_layer(T=16, d=16, E=4, k=2, inter=8, n_shared=1)
+    bf = lambda a, kind: O.round_to_format(a, "f32" if kind == "f32" else "bf16")
+    rep = lambda a, fmt: np.array_equal(O.round_to_format(a, fmt), a)
+    fwd = O.layer_forward(L["x"], L["w_router"], L["w_gate_up"], L["w_down"], top_k=2, bias=None,
+                          ws_gate_up=L["ws_gate_up"], ws_down=L["ws_down"], store=bf)
+    bwd = O.layer_backward(fwd, L["dy"], aux_coef=0.01)
+    for n in ["g", "u", "h"]:
+        assert rep(fwd[n], "bf16"), n
+    assert rep(fwd["y_perm"], "f32") and rep(fwd["y_shared"], "bf16")
+    assert rep(bwd["dy_perm"], "bf16") and rep(bwd["dx_perm"], "bf16") and rep(bwd["dz"], "f32")
+    assert not rep(fwd["y"], "bf16")                                  # outputs are not rounded
+    ident = lambda a, kind: a
+    f0 = fwd_of(L, 2)
+    b0 = O.layer_backward(f0, L["dy"], aux_coef=0.01)
+    f1 = O.layer_forward(L["x"], L["w_router"], L["w_gate_up"], L["w_down"], top_k=2, bias=None,
+                         ws_gate_up=L["ws_gate_up"], ws_down=L["ws_down"], store=ident)
+    b1 = O.layer_backward(f1, L["dy"], aux_coef=0.01)
+    assert np.array_equal(f0["y"], f1["y"])
+    for n in ["dx", "dw_router", "dw_gate_up", "dw_down", "dws_gate_up", "dws_down"]:
+        assert np.array_equal(b0[n], b1[n]), n
