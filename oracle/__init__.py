@@ -11,6 +11,9 @@ device-rounded inputs upcast exactly to float64.  By default nothing in
 between is rounded (the exact layer); ``layer_forward`` / ``layer_backward``
 take an optional ``store`` rounding that is applied only to the values the
 layer keeps in its storage dtype (the bf16 / f16 layer of the pages).
+The per-expert steps the layer passes are made of (``expert_*_step``,
+``router_backward``) are exposed too, so a test can run one step of the
+oracle on the inputs a GPU step received.
 """
 
 from .moe_oracle import (  # noqa: F401
@@ -24,6 +27,11 @@ from .moe_oracle import (  # noqa: F401
     swiglu_rows,
     shared_experts_forward,
     combine,
+    expert_gate_up_step,
+    expert_down_step,
+    expert_down_backward_step,
+    expert_gate_up_backward_step,
+    router_backward,
     aux_statistics,
     layer_forward,
     layer_backward,

@@ -205,6 +205,30 @@ def _no_store(a, kind):
     return a
 
 
+def _ident_quant(a, axis):
+    return a
+
+
+def expert_gate_up_step(rows, w_gate_up_e, quant=None, store=None):
+    """G, U and H = silu(G) * U of one expert on a block of rows, each as
+    stored (``store`` kind "act"); H is formed from the unrounded G and U.
+    ``quant`` is applied to both GEMM operands along the contraction (d)."""
+    q = quant or _ident_quant
+    st = store or _no_store
+    inter = w_gate_up_e.shape[0] // 2
+    xr = q(rows, 1)
+    wgu = q(w_gate_up_e, 1)
+    g = xr @ wgu[:inter].T
+    u = xr @ wgu[inter:].T
+    return st(g, "act"), st(u, "act"), st(silu(g) * u, "act")
+
+
+def expert_down_step(h, w_down_e, quant=None):
+    """H W_d^T of one expert (unrounded), both operands quantised along I."""
+    q = quant or _ident_quant
+    return q(h, 1) @ q(w_down_e, 1).T
+
+
 def layer_forward(x, w_router, w_gate_up, w_down, *, top_k, renorm=True, bias=None,
                   ws_gate_up=None, ws_down=None, quant=None, store=None):
     """Full forward pass.  Returns a dict of every intermediate.
@@ -222,7 +246,6 @@ def layer_forward(x, w_router, w_gate_up, w_down, *, top_k, renorm=True, bias=No
     layer those pages run; with store=None the exact layer is computed.
     Products and sums are exact either way.
     """
-    q = quant if quant is not None else (lambda a, axis: a)
     st = store if store is not None else _no_store
     T, d = x.shape
     E = w_router.shape[0]
@@ -240,26 +263,16 @@ def layer_forward(x, w_router, w_gate_up, w_down, *, top_k, renorm=True, bias=No
         r0, r1 = offsets[e], offsets[e + 1]
         if r1 == r0:
             continue
-        xr = q(x_perm[r0:r1], 1)
-        wgu = q(w_gate_up[e], 1)
-        ge = xr @ wgu[:inter].T
-        ue = xr @ wgu[inter:].T
-        he = st(silu(ge) * ue, "act")
-        g[r0:r1], u[r0:r1], h[r0:r1] = st(ge, "act"), st(ue, "act"), he
-        y_perm[r0:r1] = st(q(he, 1) @ q(w_down[e], 1).T, "f32")
+        g[r0:r1], u[r0:r1], h[r0:r1] = expert_gate_up_step(x_perm[r0:r1], w_gate_up[e], quant, store)
+        y_perm[r0:r1] = st(expert_down_step(h[r0:r1], w_down[e], quant), "f32")
     y_shared = None
     shared = []
     if ws_gate_up is not None and ws_gate_up.shape[0] > 0:
         y_shared = np.zeros((T, d))
-        inter_s = ws_down.shape[2]
-        xq = q(x, 1)
         for s in range(ws_gate_up.shape[0]):
-            wgu = q(ws_gate_up[s], 1)
-            gs = xq @ wgu[:inter_s].T
-            us = xq @ wgu[inter_s:].T
-            hs = st(silu(gs) * us, "act")
-            y_shared += q(hs, 1) @ q(ws_down[s], 1).T
-            shared.append((st(gs, "act"), st(us, "act"), hs))
+            gs, us, hs = expert_gate_up_step(x, ws_gate_up[s], quant, store)
+            y_shared += expert_down_step(hs, ws_down[s], quant)
+            shared.append((gs, us, hs))
         y_shared = st(y_shared, "act")
     y = combine(y_perm, inv, w, y_shared)
     return dict(z=z, p=p, idx=idx, w=w, counts=counts, offsets=offsets,
@@ -268,6 +281,56 @@ def layer_forward(x, w_router, w_gate_up, w_down, *, top_k, renorm=True, bias=No
                 x=x, w_router=w_router, w_gate_up=w_gate_up, w_down=w_down,
                 ws_gate_up=ws_gate_up, ws_down=ws_down, top_k=top_k,
                 renorm=renorm, bias=bias, store=store)
+
+
+def expert_down_backward_step(dy_rows, g, u, h, w_down_e, quant=None, store=None):
+    """Backward of one expert's down projection and SwiGLU on a block of rows.
+    dH = dY W_d (operands quantised along d), dW_d = dY^T H (along the rows),
+    then dG = dH * U * s * (1 + G (1 - s)) with s = sigmoid(G), dU = dH *
+    silu(G).  Returns ([dG | dU] as stored, kind "act"; dW_d unrounded)."""
+    q = quant or _ident_quant
+    st = store or _no_store
+    dh = q(dy_rows, 1) @ q(w_down_e, 0)
+    dw_down = q(dy_rows, 0).T @ q(h, 0)
+    sg = _sigmoid(g)
+    dg = dh * u * sg * (1.0 + g * (1.0 - sg))
+    du = dh * silu(g)
+    return st(np.concatenate([dg, du], axis=1), "act"), dw_down
+
+
+def expert_gate_up_backward_step(dgu, rows, w_gate_up_e, quant=None):
+    """Backward of one expert's packed gate/up projection: dX = [dG | dU] W_gu
+    (operands quantised along 2I) and dW_gu = [dG | dU]^T X (along the rows),
+    both unrounded."""
+    q = quant or _ident_quant
+    return q(dgu, 1) @ q(w_gate_up_e, 0), q(dgu, 0).T @ q(rows, 0)
+
+
+def router_backward(dy, y_perm, inv, p, idx, w, renorm, counts, aux_coef=0.0, store=None):
+    """Gradient of L = <dy, y> + aux_coef * aux with respect to the router
+    logits, given the expert output rows Y_perm the combine weighted.
+
+    g_tj = <dy_t, Y_perm[inv_tj]> reaches the routing weight of slot j; with
+    renormalisation w = p_sel / S, so dL/dp_sel = (g - <w, g>) / S; the
+    balancing term adds aux_coef * E * f_e / T to every p_te (f_e is a count,
+    no gradient); the softmax Jacobian then gives dz = p * (dp - <p, dp>).
+    Returns (g [T, k], dz [T, E] as stored, kind "f32")."""
+    st = store or _no_store
+    T, E = p.shape
+    k = idx.shape[1]
+    gsc = np.einsum("td,tjd->tj", dy, y_perm[inv])
+    p_sel = np.take_along_axis(p, idx, axis=1)
+    if renorm:
+        S = p_sel.sum(axis=1, keepdims=True)
+        dp_sel = (gsc - (w * gsc).sum(axis=1, keepdims=True)) / S
+    else:
+        dp_sel = gsc
+    dp = np.zeros_like(p)
+    np.put_along_axis(dp, idx, dp_sel, axis=1)
+    if aux_coef != 0.0:
+        f = np.asarray(counts, dtype=np.float64) / (T * k)
+        dp = dp + aux_coef * E * f[None, :] / T
+    return gsc, st(p * (dp - (p * dp).sum(axis=1, keepdims=True)), "f32")
 
 
 def layer_backward(fwd, dy, *, aux_coef=0.0, quant=None):
@@ -283,7 +346,6 @@ def layer_backward(fwd, dy, *, aux_coef=0.0, quant=None):
     "act"); the router's logit gradient dz (kind "f32").  Final outputs are
     not rounded.
     """
-    q = quant if quant is not None else (lambda a, axis: a)
     st = fwd.get("store") or _no_store
     x, w_r = fwd["x"], fwd["w_router"]
     w_gate_up, w_down = fwd["w_gate_up"], fwd["w_down"]
@@ -292,11 +354,8 @@ def layer_backward(fwd, dy, *, aux_coef=0.0, quant=None):
     T, d = x.shape
     E = w_r.shape[0]
     k = fwd["top_k"]
-    inter = w_down.shape[2]
 
-    # combine: y_t = sum_j w_tj Y_perm[inv_tj]  ->  g_tj and dY_perm
-    y_rows = fwd["y_perm"][inv]                       # [T, k, d]
-    gsc = np.einsum("td,tjd->tj", dy, y_rows)         # dL/dw_tj
+    # combine: y_t = sum_j w_tj Y_perm[inv_tj]  ->  dY_perm rows w_tj dy_t
     dy_perm = np.zeros_like(fwd["y_perm"])
     dy_perm[inv.reshape(-1)] = st((w[:, :, None] * dy[:, None, :]).reshape(-1, d), "act")
 
@@ -307,16 +366,10 @@ def layer_backward(fwd, dy, *, aux_coef=0.0, quant=None):
         r0, r1 = offsets[e], offsets[e + 1]
         if r1 == r0:
             continue
-        G, U, H = fwd["g"][r0:r1], fwd["u"][r0:r1], fwd["h"][r0:r1]
-        dY = dy_perm[r0:r1]
-        dH = q(dY, 1) @ q(w_down[e], 0)
-        dw_down[e] = q(dY, 0).T @ q(H, 0)
-        sg = _sigmoid(G)
-        dG = dH * U * sg * (1.0 + G * (1.0 - sg))
-        dU = dH * silu(G)
-        dGU = st(np.concatenate([dG, dU], axis=1), "act")
-        dx_perm[r0:r1] = st(q(dGU, 1) @ q(w_gate_up[e], 0), "act")
-        dw_gate_up[e] = q(dGU, 0).T @ q(fwd["x_perm"][r0:r1], 0)
+        dgu, dw_down[e] = expert_down_backward_step(dy_perm[r0:r1], fwd["g"][r0:r1], fwd["u"][r0:r1],
+                                                    fwd["h"][r0:r1], w_down[e], quant, st)
+        dxe, dw_gate_up[e] = expert_gate_up_backward_step(dgu, fwd["x_perm"][r0:r1], w_gate_up[e], quant)
+        dx_perm[r0:r1] = st(dxe, "act")
 
     dx = np.zeros((T, d))
     for j in range(k):
@@ -328,32 +381,15 @@ def layer_backward(fwd, dy, *, aux_coef=0.0, quant=None):
         dws_gu = np.zeros_like(ws_gu)
         dws_d = np.zeros_like(ws_d)
         for s, (G, U, H) in enumerate(fwd["shared"]):
-            dH = q(dy, 1) @ q(ws_d[s], 0)
-            dws_d[s] = q(dy, 0).T @ q(H, 0)
-            sg = _sigmoid(G)
-            dG = dH * U * sg * (1.0 + G * (1.0 - sg))
-            dU = dH * silu(G)
-            dGU = st(np.concatenate([dG, dU], axis=1), "act")
-            dx_s = q(dGU, 1) @ q(ws_gu[s], 0)
+            dgu, dws_d[s] = expert_down_backward_step(dy, G, U, H, ws_d[s], quant, st)
+            dx_s, dws_gu[s] = expert_gate_up_backward_step(dgu, x, ws_gu[s], quant)
             dx_shared = dx_s if s == 0 else dx_shared + dx_s
-            dws_gu[s] = q(dGU, 0).T @ q(x, 0)
         dx += st(dx_shared, "act")
         grads["dws_gate_up"] = dws_gu
         grads["dws_down"] = dws_d
 
-    # router: gradient reaching the selected probabilities
-    p_sel = np.take_along_axis(p, idx, axis=1)
-    if fwd["renorm"]:
-        S = p_sel.sum(axis=1, keepdims=True)
-        dp_sel = (gsc - (w * gsc).sum(axis=1, keepdims=True)) / S
-    else:
-        dp_sel = gsc
-    dp = np.zeros_like(p)
-    np.put_along_axis(dp, idx, dp_sel, axis=1)
-    if aux_coef != 0.0:
-        f = np.asarray(counts, dtype=np.float64) / (T * k)
-        dp = dp + aux_coef * E * f[None, :] / T
-    dz = st(p * (dp - (p * dp).sum(axis=1, keepdims=True)), "f32")
+    # router
+    gsc, dz = router_backward(dy, fwd["y_perm"], inv, p, idx, w, fwd["renorm"], counts, aux_coef, st)
     grads["dw_router"] = dz.T @ x
     grads["dbias"] = dz.sum(axis=0)
     dx += dz @ w_r
