@@ -79,7 +79,7 @@ def make_layer(wl, device="cuda"):
     dev = {k: (v.to(device) if v is not None else None) for k, v in inp.items()}
     plan = Plan(wl.T, wl.d, wl.E, wl.k, wl.I, n_shared=wl.n_shared, d_ff_shared=wl.I_shared,
                 renorm=wl.renorm, has_router_bias=dev["bias"] is not None, dtype=wl.torch_dtype,
-                aux_coef=wl.aux_coef)
+                aux_coef=wl.aux_coef, expert_dtype=wl.expert_dtype or None)
     layer = MoELayer(plan, device)
     layer.set_params(dev["x"], dev["w_router"], dev["w_gate_up"], dev["w_down"], bias=dev["bias"],
                      ws_gate_up=dev.get("ws_gate_up"), ws_down=dev.get("ws_down"))

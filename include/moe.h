@@ -66,7 +66,14 @@ typedef enum { MOE_F32 = 0, MOE_F16 = 1, MOE_BF16 = 2, MOE_MXFP8_E4M3 = 3 } moe_
  *   0 <= T;  1 <= top_k <= n_experts <= 256;
  *   d_model, d_ff (and d_ff_shared when n_shared > 0) multiples of 128;
  *   0 <= n_shared <= 8;  act_dtype in {F32, F16, BF16};
- *   expert_dtype == act_dtype (MXFP8 experts are reported UNSUPPORTED until built). */
+ *   expert_dtype == act_dtype, or expert_dtype == MXFP8_E4M3 with act_dtype
+ *   BF16 (the MX GEMMs write bf16): then every expert GEMM (routed and shared, forward and
+ *   backward) quantises both operands to MX-fp8 along that GEMM's reduction
+ *   axis (blocks of 32; along the tokens of each expert segment for the
+ *   weight gradients) into the workspace and runs on the scaled fp8 matrix
+ *   cores; weights, activations, gradients and outputs stay in act_dtype.
+ *   The router, softmax, combine and statistics are never quantised.
+ *   (KohakUwULLM README, "Key features": MXFP8 experts.) */
 typedef struct {
   int64_t T;              /* tokens in the packed batch (rows of x) */
   int32_t d_model;        /* d */
@@ -224,6 +231,23 @@ moe_status moe_aux_stats(moe_plan plan, const float* probs, const int32_t* count
                          float* p_mean, moe_aux_scalars* out, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* ---- MX-fp8 quantisation ----------------------------------------------- */
+
+/* Quantise `rows` rows of K values (act_dtype BF16 or F16, row-major, K a
+ * multiple of 32) to MX-fp8 along the row: per block of 32 values the scale is
+ * the smallest power of two 2^x with max|v| <= 448 * 2^x (x clamped to
+ * [-127, 127]; -127 for an all-zero block), scales[r * K/32 + b] = x + 127
+ * (UE8M0), and payload[r * K + k] = v / 2^x rounded to nearest OCP e4m3 (ties
+ * to even; subnormals k * 2^-9).  The quantiser the MX expert GEMMs use, as a
+ * call of its own.  (KohakUwULLM README, "Key features": e4m3 values with one
+ * power-of-two scale per 32 elements; the choice of the scale is this
+ * library's reading: no value saturates.)
+ *   in       [rows, K] act          payload [rows, K] bytes
+ *   scales   [rows, K/32] bytes
+ * Returns MOE_ERR_NULL / MOE_ERR_INVALID before any launch on bad arguments. */
+moe_status moe_mx_quantize_rows(const void* in, int32_t act_dtype, int64_t rows, int32_t K, uint8_t* payload,
+                                uint8_t* scales, void* stream);
+
 /* ---- kernel timing probe (measurement aid) ----------------------------- */
 
 /* Record a hipEvent pair around each of the next `max_launches` launches of
@@ -235,6 +259,21 @@ moe_status moe_probe_enable(moe_plan plan, const char* kernel, int max_launches)
 moe_status moe_probe_read(moe_plan plan, float* total_ms, int* launches);
 /* Comma-separated names of the kernels the probe accepts. */
 const char* moe_kernel_names(void);
+
+/* ---- backward intermediates (inspection aid) --------------------------- */
+
+/* Byte offset and size, inside the workspace, of an intermediate that
+ * moe_backward keeps there and leaves in place when it returns (until the
+ * next call that uses the workspace), all act dtype, row-major:
+ *   "dy_perm"     [T*top_k, d_model]     gradient reaching the expert rows
+ *   "dgu"         [T*top_k, 2 d_ff]      [dG | dU] of the routed experts
+ *   "dx_perm"     [T*top_k, d_model]     input gradient of the expert rows
+ *   "dgu_shared"  [T, 2 n_shared d_ff_shared]  [dG_s | dU_s] per shared expert
+ *   "dx_shared"   [T, d_model]           input gradient of the shared experts
+ * For tests and debugging, e.g. to check each GEMM of the backward on its
+ * own inputs.  MOE_ERR_NULL for a null argument, MOE_ERR_INVALID for an
+ * unknown name or a region this plan does not have (no shared experts). */
+moe_status moe_workspace_region(moe_plan plan, const char* name, size_t* offset, size_t* bytes);
 
 #ifdef __cplusplus
 }

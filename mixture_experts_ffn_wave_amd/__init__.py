@@ -19,6 +19,8 @@ from ._lib import (  # noqa: F401
     probe_enable,
     probe_read,
     kernel_names,
+    mx_quantize_rows,
+    workspace_region,
     LIB_PATH,
 )
 from .layer import MoELayer  # noqa: F401

@@ -71,6 +71,9 @@ SIGNATURES = {
     "moe_probe_enable": (c_int32, [c_void_p, ctypes.c_char_p, c_int32]),
     "moe_probe_read": (c_int32, [c_void_p, ctypes.POINTER(c_float), ctypes.POINTER(c_int32)]),
     "moe_kernel_names": (ctypes.c_char_p, []),
+    "moe_mx_quantize_rows": (c_int32, [c_void_p, c_int32, c_int64, c_int32, c_void_p, c_void_p, c_void_p]),
+    "moe_workspace_region": (c_int32, [c_void_p, ctypes.c_char_p, ctypes.POINTER(c_size_t),
+                                       ctypes.POINTER(c_size_t)]),
 }
 
 _lib = None
@@ -138,7 +141,12 @@ class Plan:
         if dtype not in _DTYPE_CODE:
             raise ValueError(f"unsupported activation dtype {dtype}")
         code = _DTYPE_CODE[dtype]
-        ecode = code if expert_dtype is None else expert_dtype
+        if expert_dtype is None:
+            ecode = code
+        elif expert_dtype == "mxfp8":
+            ecode = MOE_MXFP8_E4M3
+        else:
+            ecode = expert_dtype
         self.cfg = MoeConfig(T, d_model, n_experts, top_k, d_ff, n_shared, d_ff_shared, int(renorm),
                              int(has_router_bias), code, ecode, aux_coef)
         self.dtype = dtype
@@ -281,5 +289,27 @@ def probe_read(plan):
     return float(ms.value), int(n.value)
 
 
+def workspace_region(plan, name):
+    """(byte offset, bytes) of a backward intermediate in the workspace
+    (moe_workspace_region)."""
+    off, nb = c_size_t(), c_size_t()
+    _check("moe_workspace_region", lib().moe_workspace_region(plan.handle, name.encode(), ctypes.byref(off),
+                                                              ctypes.byref(nb)))
+    return int(off.value), int(nb.value)
+
+
 def kernel_names():
     return lib().moe_kernel_names().decode().split(",")
+
+
+def mx_quantize_rows(x, payload, scales, stream=None):
+    """MX-fp8 quantisation of the rows of x [R, K] (bf16 or f16) into payload
+    [R, K] uint8 and scales [R, K/32] uint8 (moe_mx_quantize_rows)."""
+    if x.dim() != 2 or x.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("x must be a 2-D bf16 or f16 tensor")
+    R, K = x.shape
+    _need(x, "x", (R, K), x.dtype)
+    _need(payload, "payload", (R, K), torch.uint8)
+    _need(scales, "scales", (R, K // 32), torch.uint8)
+    _check("moe_mx_quantize_rows", lib().moe_mx_quantize_rows(
+        _ptr(x), _DTYPE_CODE[x.dtype], R, K, _ptr(payload), _ptr(scales), _stream(stream)))

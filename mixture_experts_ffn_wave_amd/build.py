@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
-SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm.hip", "elementwise.hip"]
+SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm.hip", "elementwise.hip", "mx.hip"]
 ARCH = "gfx950"
 
 

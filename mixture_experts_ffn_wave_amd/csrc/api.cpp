@@ -28,7 +28,7 @@ const char* kKernelNames =
     "gemm_down_dgrad_swiglu,gemm_wgrad_down,gemm_gate_up_dgrad,gemm_wgrad_gate_up,"
     "gemm_down_dgrad_swiglu_shared,gemm_wgrad_down_shared,gemm_wgrad_gate_up_shared,"
     "gemm_gate_up_dgrad_shared,stack_router,gemm_router_dx,unpermute,gemm_wgrad_router,router_reduce,aux,"
-    "wgrad_reduce";
+    "wgrad_reduce,mx_quantize";
 
 }  // namespace
 
@@ -47,6 +47,15 @@ struct moe_plan_s {
   size_t o_block_counts, o_block_base, o_dy_perm, o_g, o_dzhl, o_w2, o_dgu, o_dx_perm, o_dgu_s,
       o_dxs, o_dxr, o_dwr_part, o_dbias_part, o_aux_part, o_wg_part, ws_total;
   bool router_dx_gemm;     // many experts: the router part of dx goes through the matrix cores
+  // MX-fp8 experts: every expert GEMM operand is quantised into the workspace
+  // (payload at .pay, scale bytes at .sc) right before the GEMM that reads it
+  bool mx = false;
+  struct MxBuf { size_t pay = 0, sc = 0; };
+  MxBuf mx_xq, mx_hq, mx_wgu, mx_wd, mx_sxq, mx_shq, mx_swgu, mx_swd;                 // forward
+  MxBuf mx_dyq, mx_wdt, mx_dguq, mx_wgut, mx_dyt, mx_ht, mx_dgut, mx_xt;              // backward, routed
+  MxBuf mx_sdyq, mx_swdt, mx_sdguq, mx_swgut, mx_sdyt, mx_sht, mx_sdgut, mx_sxt;      // backward, shared
+  size_t o_mx_pad = 0, o_mx_seg1 = 0;  // padded expert offsets [E+1]; single-segment bounds [2] + pad [2]
+  int64_t Apad = 0, Tpad = 0;          // padded token axes of the transposed operands
   // timing probe
   std::string probe_name;
   std::vector<hipEvent_t> ev0, ev1;
@@ -171,6 +180,29 @@ const char* moe_version(void) { return "moe-ffn-mi355x 0.1 gfx950"; }
 
 const char* moe_kernel_names(void) { return kKernelNames; }
 
+moe_status moe_workspace_region(moe_plan p, const char* name, size_t* offset, size_t* bytes) {
+  if (!p || !name || !offset || !bytes) return MOE_ERR_NULL;
+  const size_t es = dtype_bytes(p->dt);
+  const std::string n(name);
+  size_t o = 0, b = 0;
+  if (n == "dy_perm") {
+    o = p->o_dy_perm; b = (size_t)p->A * p->d * es;
+  } else if (n == "dgu") {
+    o = p->o_dgu; b = (size_t)p->A * 2 * p->I * es;
+  } else if (n == "dx_perm") {
+    o = p->o_dx_perm; b = (size_t)p->A * p->d * es;
+  } else if (n == "dgu_shared" && p->Ns > 0) {
+    o = p->o_dgu_s; b = (size_t)p->T * 2 * p->Ns * p->Is * es;
+  } else if (n == "dx_shared" && p->Ns > 0) {
+    o = p->o_dxs; b = (size_t)p->T * p->d * es;
+  } else {
+    return MOE_ERR_INVALID;
+  }
+  *offset = o;
+  *bytes = b;
+  return MOE_OK;
+}
+
 moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
   if (!out) return MOE_ERR_NULL;
   *out = nullptr;
@@ -188,7 +220,9 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
   if (c.expert_dtype < MOE_F32 || c.expert_dtype > MOE_MXFP8_E4M3) return MOE_ERR_INVALID;
   if (!(c.aux_coef == c.aux_coef)) return MOE_ERR_INVALID;  // NaN
   if (c.act_dtype == MOE_MXFP8_E4M3) return MOE_ERR_UNSUPPORTED;
-  if (c.expert_dtype != c.act_dtype) return MOE_ERR_UNSUPPORTED;
+  const bool mx = c.expert_dtype == MOE_MXFP8_E4M3;
+  if (mx && c.act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;   // MX GEMMs write bf16
+  if (!mx && c.expert_dtype != c.act_dtype) return MOE_ERR_UNSUPPORTED;
   if (c.d_model % 128 || c.d_ff % 128) return MOE_ERR_UNSUPPORTED;
   if (c.n_shared > 0 && c.d_ff_shared % 128) return MOE_ERR_UNSUPPORTED;
   const int64_t A = c.T * c.top_k;
@@ -199,6 +233,7 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
   if (!p) return MOE_ERR_INVALID;
   p->cfg = c;
   p->dt = c.act_dtype == MOE_F32 ? DT_F32 : (c.act_dtype == MOE_F16 ? DT_F16 : DT_BF16);
+  p->mx = mx;
   p->T = c.T;
   p->A = A;
   p->d = c.d_model;
@@ -237,6 +272,7 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
     p->t_wg_down = choose_wgrad_tile(p->dt, E, d, I, rps, wt);
     p->t_wg_gu = choose_wgrad_tile(p->dt, E, 2 * I, d, rps, wt);
     p->t_wg_router = 128;
+    if (p->mx) p->t_gu = p->t_down = p->t_down_dgrad = p->t_gu_dgrad = p->t_wg_down = p->t_wg_gu = 128;
     p->sp_wg_down = choose_wgrad_splits(p->t_wg_down, E, d, I, rps);
     p->sp_wg_gu = choose_wgrad_splits(p->t_wg_gu, E, 2 * I, d, rps);
     if (p->Ns > 0) {
@@ -246,6 +282,7 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
       p->t_gu_dgrad_s = choose_row_tile(p->dt, d, 256, rt);
       p->t_wg_down_s = (p->Is % 256 == 0) ? choose_wgrad_tile(p->dt, 1, d, NI, T, wt) : 128;
       p->t_wg_gu_s = choose_wgrad_tile(p->dt, 1, 2 * NI, d, T, wt);
+      if (p->mx) p->t_gu_s = p->t_down_s = p->t_down_dgrad_s = p->t_gu_dgrad_s = p->t_wg_down_s = p->t_wg_gu_s = 128;
       p->sp_wg_down_s = choose_wgrad_splits(p->t_wg_down_s, 1, d, NI, T);
       p->sp_wg_gu_s = choose_wgrad_splits(p->t_wg_gu_s, 1, 2 * NI, d, T);
     } else {
@@ -286,6 +323,46 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
     need(p->sp_wg_gu_s, (int64_t)2 * p->Ns * p->Is * p->d);
     p->o_wg_part = take(part);
   }
+  if (p->mx) {
+    // MX operands: payload bytes + one scale byte per 32 (both 256-byte aligned)
+    auto mxb = [&](int64_t rows, int64_t K) {
+      moe_plan_s::MxBuf b;
+      b.pay = take((size_t)rows * K);
+      b.sc = take((size_t)rows * (K / 32));
+      return b;
+    };
+    const int64_t A = p->A, T = p->T, d = p->d, I = p->I, E = p->E, NI = (int64_t)p->Ns * p->Is;
+    p->Apad = (A + 128 * E + 127) / 128 * 128;     // >= sum over experts of their counts rounded up to 128
+    p->Tpad = (T + 127) / 128 * 128;
+    p->mx_xq = mxb(A, d);
+    p->mx_hq = mxb(A, I);
+    p->mx_wgu = mxb(E * 2 * I, d);
+    p->mx_wd = mxb(E * d, I);
+    p->mx_dyq = mxb(A, d);
+    p->mx_wdt = mxb(I, E * d);
+    p->mx_dguq = mxb(A, 2 * I);
+    p->mx_wgut = mxb(d, E * 2 * I);
+    p->mx_dyt = mxb(d, p->Apad);
+    p->mx_ht = mxb(I, p->Apad);
+    p->mx_dgut = mxb(2 * I, p->Apad);
+    p->mx_xt = mxb(d, p->Apad);
+    p->o_mx_pad = take((size_t)(E + 1) * 4);
+    p->o_mx_seg1 = take(4 * 4);
+    if (NI > 0) {
+      p->mx_sxq = mxb(T, d);
+      p->mx_shq = mxb(T, NI);
+      p->mx_swgu = mxb(2 * NI, d);
+      p->mx_swd = mxb(d, NI);
+      p->mx_sdyq = mxb(T, d);
+      p->mx_swdt = mxb(NI, d);
+      p->mx_sdguq = mxb(T, 2 * NI);
+      p->mx_swgut = mxb(d, 2 * NI);
+      p->mx_sdyt = mxb(d, p->Tpad);
+      p->mx_sht = mxb(NI, p->Tpad);
+      p->mx_sdgut = mxb(2 * NI, p->Tpad);
+      p->mx_sxt = mxb(d, p->Tpad);
+    }
+  }
   p->ws_total = off;
   *out = p;
   return MOE_OK;
@@ -298,20 +375,21 @@ size_t moe_workspace_bytes(moe_plan plan) { return plan ? plan->ws_total : 0; }
 // Weight-gradient GEMM into `out` ([G][group_elems], act dtype), split over
 // tokens `splits` ways through f32 partials when splits > 1.
 moe_status run_wgrad(moe_plan p, int op, int tile, int splits, WgradArgs a, void* out, int64_t group_elems,
-                     void* ws, const char* name, hipStream_t s) {
+                     void* ws, const char* name, hipStream_t s, int gdt = -1) {
+  if (gdt < 0) gdt = p->dt;
   a.splits = splits;
   a.c_group_stride = group_elems;
   if (splits <= 1) {
     a.C = out; a.c_split_stride = 0; a.out_f32 = 0;
     Probe pr(p, name, s);
-    MOE_TRY(launch_wgrad(p->dt, op, tile, a, s));
+    MOE_TRY(launch_wgrad(gdt, op, tile, a, s));
     return MOE_OK;
   }
   float* part = reinterpret_cast<float*>(wsp(ws, p->o_wg_part));
   a.C = part; a.c_split_stride = (int64_t)a.G * group_elems; a.out_f32 = 1;
   {
     Probe pr(p, name, s);
-    MOE_TRY(launch_wgrad(p->dt, op, tile, a, s));
+    MOE_TRY(launch_wgrad(gdt, op, tile, a, s));
   }
   SplitReduceArgs r{part, (int64_t)a.G * group_elems, splits, out};
   Probe pr(p, "wgrad_reduce", s);
@@ -324,6 +402,34 @@ moe_status run_wgrad(moe_plan p, int op, int tile, int splits, WgradArgs a, void
     moe_status st_ = (expr);            \
     if (st_ != MOE_OK) return st_;      \
   } while (0)
+
+// ---- MX-fp8 operand helpers
+struct MxOp { uint8_t* pay; uint8_t* sc; };
+MxOp mxop(void* ws, const moe_plan_s::MxBuf& b) {
+  return {reinterpret_cast<uint8_t*>(wsp(ws, b.pay)), reinterpret_cast<uint8_t*>(wsp(ws, b.sc))};
+}
+// rows operand: element (r, k) at in + (k / sub) * block_stride + r * ld_in + k % sub
+moe_status mx_rows(moe_plan p, hipStream_t s, const void* in, int64_t ld_in, int64_t block_stride, int sub,
+                   int64_t R, int K, MxOp o) {
+  MxRowsArgs a{in, ld_in, block_stride, sub, R, K, o.pay, o.sc};
+  Probe pr(p, "mx_quantize", s);
+  MOE_TRY(launch_mx_quant_rows(p->dt, a, s));
+  return MOE_OK;
+}
+// transposed operand: the token axis of in [tokens][C] becomes K
+moe_status mx_cols(moe_plan p, hipStream_t s, const void* in, int64_t ld_in, int C, const int32_t* seg,
+                   const int32_t* pad, int G, int seg_len, int64_t nblk, int64_t k0, int64_t Kpad, int64_t row0,
+                   MxOp o) {
+  MxColsArgs a{in, ld_in, C, seg, pad, G, seg_len, nblk, k0, Kpad, row0, o.pay, o.sc};
+  Probe pr(p, "mx_quantize", s);
+  MOE_TRY(launch_mx_quant_cols(p->dt, a, s));
+  return MOE_OK;
+}
+// MX row GEMM operands
+void mx_pq(RowGemmArgs& a, MxOp P, int64_t ldp, MxOp Q, int64_t ldq, int64_t q_group_stride) {
+  a.P = P.pay; a.Ps = P.sc; a.ldp = ldp;
+  a.Q = Q.pay; a.Qs = Q.sc; a.ldq = ldq; a.q_group_stride = q_group_stride;
+}
 
 // ------------------------------------------------------------------ route --
 moe_status moe_route(moe_plan p, const void* x, const void* w_router, const float* bias, float* probs,
@@ -368,16 +474,21 @@ moe_status moe_permute(moe_plan p, const int32_t* topk_idx, const void* x, int32
 }
 
 // ------------------------------------------------------------- expert FFN --
+moe_status mx_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, hipStream_t s);
+
 moe_status moe_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, size_t ws_bytes, void* stream) {
   if (!p || !f) return MOE_ERR_NULL;
-  (void)ws;
-  (void)ws_bytes;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p->T == 0) return MOE_OK;
   if (!f->x_perm || !f->offsets || !f->w_gate_up || !f->w_down || !f->gu || !f->h || !f->y_perm)
     return MOE_ERR_NULL;
   if (p->Ns > 0 && (!f->x || !f->ws_gate_up || !f->ws_down || !f->gu_shared || !f->h_shared || !f->y_shared))
     return MOE_ERR_NULL;
+  if (p->mx) {
+    moe_status st = check_ws(p, ws, ws_bytes);
+    if (st != MOE_OK) return st;
+    return mx_expert_ffn(p, f, ws, s);
+  }
   const int d = p->d, I = p->I;
   {
     RowGemmArgs a{};
@@ -421,6 +532,60 @@ moe_status moe_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, size_t ws
   return MOE_OK;
 }
 
+// MX-fp8 forward of the experts: each GEMM operand quantised along that GEMM's
+// reduction axis just before the GEMM (KohakUwULLM README, "Key features").
+moe_status mx_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, hipStream_t s) {
+  const int64_t d = p->d, I = p->I, E = p->E, A = p->A;
+  const MxOp xq = mxop(ws, p->mx_xq), hq = mxop(ws, p->mx_hq), wgu = mxop(ws, p->mx_wgu), wd = mxop(ws, p->mx_wd);
+  MOE_TRY_STATUS(mx_rows(p, s, f->x_perm, d, 0, (int)d, A, (int)d, xq));
+  MOE_TRY_STATUS(mx_rows(p, s, f->w_gate_up, d, 0, (int)d, E * 2 * I, (int)d, wgu));
+  {
+    RowGemmArgs a{};
+    mx_pq(a, xq, d, wgu, d, 2 * I * d);
+    a.offsets = f->offsets; a.G = (int)E; a.M = A; a.N = (int)I; a.K = (int)d; a.sub = (int)I;
+    a.C = f->gu; a.ldc = 2 * I; a.C2 = f->h; a.ldc2 = I;
+    Probe pr(p, "gemm_gate_up_swiglu", s);
+    MOE_TRY(launch_row_gemm(DT_MXFP8, OP_GU_FWD, EPI_SWIGLU_FWD, 128, a, s));
+  }
+  MOE_TRY_STATUS(mx_rows(p, s, f->h, I, 0, (int)I, A, (int)I, hq));
+  MOE_TRY_STATUS(mx_rows(p, s, f->w_down, I, 0, (int)I, E * d, (int)I, wd));
+  {
+    RowGemmArgs a{};
+    mx_pq(a, hq, I, wd, I, d * I);
+    a.offsets = f->offsets; a.G = (int)E; a.M = A; a.N = (int)d; a.K = (int)I; a.sub = (int)I;
+    a.C = f->y_perm; a.ldc = d;
+    Probe pr(p, "gemm_down", s);
+    MOE_TRY(launch_row_gemm(DT_MXFP8, OP_DOWN_FWD, EPI_STORE_F32, 128, a, s));
+  }
+  if (p->Ns > 0) {
+    const int64_t Is = p->Is, NI = p->Ns * p->Is, T = p->T;
+    const MxOp sxq = mxop(ws, p->mx_sxq), shq = mxop(ws, p->mx_shq), swgu = mxop(ws, p->mx_swgu),
+               swd = mxop(ws, p->mx_swd);
+    MOE_TRY_STATUS(mx_rows(p, s, f->x, d, 0, (int)d, T, (int)d, sxq));
+    MOE_TRY_STATUS(mx_rows(p, s, f->ws_gate_up, d, 0, (int)d, 2 * NI, (int)d, swgu));
+    {
+      RowGemmArgs a{};
+      mx_pq(a, sxq, d, swgu, d, 0);
+      a.offsets = nullptr; a.G = 1; a.M = T; a.N = (int)NI; a.K = (int)d; a.sub = (int)Is;
+      a.C = f->gu_shared; a.ldc = 2 * NI; a.C2 = f->h_shared; a.ldc2 = NI;
+      Probe pr(p, "gemm_gate_up_swiglu_shared", s);
+      MOE_TRY(launch_row_gemm(DT_MXFP8, OP_GU_FWD, EPI_SWIGLU_FWD, 128, a, s));
+    }
+    MOE_TRY_STATUS(mx_rows(p, s, f->h_shared, NI, 0, (int)NI, T, (int)NI, shq));
+    // shared down weights [Ns][d][Is] concatenated along K into [d][NI]
+    MOE_TRY_STATUS(mx_rows(p, s, f->ws_down, Is, d * Is, (int)Is, d, (int)NI, swd));
+    {
+      RowGemmArgs a{};
+      mx_pq(a, shq, NI, swd, NI, 0);
+      a.offsets = nullptr; a.G = 1; a.M = T; a.N = (int)d; a.K = (int)NI; a.sub = (int)Is;
+      a.C = f->y_shared; a.ldc = d;
+      Probe pr(p, "gemm_down_shared", s);
+      MOE_TRY(launch_row_gemm(DT_MXFP8, OP_DOWN_FWD, EPI_STORE, 128, a, s));
+    }
+  }
+  return MOE_OK;
+}
+
 // ---------------------------------------------------------------- combine --
 moe_status moe_combine(moe_plan p, const float* y_perm, const int32_t* inv_perm, const float* topk_w,
                        const void* y_shared, void* y, void* stream) {
@@ -434,6 +599,119 @@ moe_status moe_combine(moe_plan p, const float* y_perm, const int32_t* inv_perm,
 }
 
 // --------------------------------------------------------------- backward --
+// MX-fp8 backward of the experts (routed and shared): both dgrad GEMMs, both
+// weight gradients, each operand quantised along its GEMM's reduction axis --
+// the weight gradients' along the tokens of each expert segment.
+moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, const moe_grads* gr, void* ws,
+                               hipStream_t s, void* dy_perm, void* dgu, void* dx_perm, void* dgu_s, void* dxs) {
+  const int64_t d = p->d, I = p->I, E = p->E, A = p->A, T = p->T, Apad = p->Apad;
+  int32_t* pad = reinterpret_cast<int32_t*>(wsp(ws, p->o_mx_pad));
+  const MxOp dyq = mxop(ws, p->mx_dyq), wdt = mxop(ws, p->mx_wdt), dguq = mxop(ws, p->mx_dguq),
+             wgut = mxop(ws, p->mx_wgut), dyt = mxop(ws, p->mx_dyt), ht = mxop(ws, p->mx_ht),
+             dgut = mxop(ws, p->mx_dgut), xt = mxop(ws, p->mx_xt);
+  {
+    Probe pr(p, "mx_quantize", s);
+    MOE_TRY(launch_mx_pad_offsets(sv->offsets, pad, (int)E, 128, s));
+  }
+  if (T > 0) {
+    // dH = dY_perm W_d (reduction over d): W_d [E][d][I] transposed to [I][E d]
+    MOE_TRY_STATUS(mx_rows(p, s, dy_perm, d, 0, (int)d, A, (int)d, dyq));
+    MOE_TRY_STATUS(mx_cols(p, s, sv->w_down, I, (int)I, nullptr, nullptr, (int)E, (int)d, E * d / 32, 0, E * d, 0, wdt));
+    RowGemmArgs a{};
+    mx_pq(a, dyq, d, wdt, E * d, d);
+    a.offsets = sv->offsets; a.G = (int)E; a.M = A; a.N = (int)I; a.K = (int)d; a.sub = (int)I;
+    a.C = dgu; a.ldc = 2 * I; a.aux = sv->gu; a.ldaux = 2 * I;
+    Probe pr(p, "gemm_down_dgrad_swiglu", s);
+    MOE_TRY(launch_row_gemm(DT_MXFP8, OP_DOWN_DGRAD, EPI_SWIGLU_BWD, 128, a, s));
+  }
+  {
+    // dW_d[e] = dY_perm[seg]^T H[seg]: token axis blocked per segment
+    MOE_TRY_STATUS(mx_cols(p, s, dy_perm, d, (int)d, sv->offsets, pad, (int)E, 0, Apad / 32, 0, Apad, 0, dyt));
+    MOE_TRY_STATUS(mx_cols(p, s, sv->h, I, (int)I, sv->offsets, pad, (int)E, 0, Apad / 32, 0, Apad, 0, ht));
+    WgradArgs a{};
+    a.P = dyt.pay; a.Ps = dyt.sc; a.ldp = Apad; a.Q = ht.pay; a.Qs = ht.sc; a.ldq = Apad;
+    a.offsets = pad; a.G = (int)E; a.Mtok = Apad; a.M = (int)d; a.N = (int)I; a.sub = (int)I;
+    MOE_TRY_STATUS(run_wgrad(p, WG_DOWN, 128, p->sp_wg_down, a, gr->dw_down, d * I, ws, "gemm_wgrad_down", s,
+                             DT_MXFP8));
+  }
+  if (T > 0) {
+    // dX_perm = [dG | dU] W_gu (reduction over 2I): W_gu [E][2I][d] transposed to [d][E 2I]
+    MOE_TRY_STATUS(mx_rows(p, s, dgu, 2 * I, 0, (int)(2 * I), A, (int)(2 * I), dguq));
+    MOE_TRY_STATUS(mx_cols(p, s, sv->w_gate_up, d, (int)d, nullptr, nullptr, (int)E, (int)(2 * I), E * 2 * I / 32, 0,
+                           E * 2 * I, 0, wgut));
+    RowGemmArgs a{};
+    mx_pq(a, dguq, 2 * I, wgut, E * 2 * I, 2 * I);
+    a.offsets = sv->offsets; a.G = (int)E; a.M = A; a.N = (int)d; a.K = (int)(2 * I); a.sub = (int)I;
+    a.C = dx_perm; a.ldc = d;
+    Probe pr(p, "gemm_gate_up_dgrad", s);
+    MOE_TRY(launch_row_gemm(DT_MXFP8, OP_GU_DGRAD, EPI_STORE, 128, a, s));
+  }
+  {
+    MOE_TRY_STATUS(mx_cols(p, s, dgu, 2 * I, (int)(2 * I), sv->offsets, pad, (int)E, 0, Apad / 32, 0, Apad, 0, dgut));
+    MOE_TRY_STATUS(mx_cols(p, s, sv->x_perm, d, (int)d, sv->offsets, pad, (int)E, 0, Apad / 32, 0, Apad, 0, xt));
+    WgradArgs a{};
+    a.P = dgut.pay; a.Ps = dgut.sc; a.ldp = Apad; a.Q = xt.pay; a.Qs = xt.sc; a.ldq = Apad;
+    a.offsets = pad; a.G = (int)E; a.Mtok = Apad; a.M = (int)(2 * I); a.N = (int)d; a.sub = (int)d;
+    MOE_TRY_STATUS(run_wgrad(p, WG_GATE_UP, 128, p->sp_wg_gu, a, gr->dw_gate_up, 2 * I * d, ws,
+                             "gemm_wgrad_gate_up", s, DT_MXFP8));
+  }
+  if (p->Ns > 0) {
+    const int64_t Is = p->Is, NI = p->Ns * p->Is, Tpad = p->Tpad;
+    int32_t* seg_pad = reinterpret_cast<int32_t*>(wsp(ws, p->o_mx_seg1));   // {0, T} then {0, Tpad}
+    const MxOp sdyq = mxop(ws, p->mx_sdyq), swdt = mxop(ws, p->mx_swdt), sdguq = mxop(ws, p->mx_sdguq),
+               swgut = mxop(ws, p->mx_swgut), sdyt = mxop(ws, p->mx_sdyt), sht = mxop(ws, p->mx_sht),
+               sdgut = mxop(ws, p->mx_sdgut), sxt = mxop(ws, p->mx_sxt);
+    {
+      Probe pr(p, "mx_quantize", s);
+      MOE_TRY(launch_mx_single_segment(seg_pad, T, 128, s));
+    }
+    if (T > 0) {
+      MOE_TRY_STATUS(mx_rows(p, s, dy, d, 0, (int)d, T, (int)d, sdyq));
+      for (int sh = 0; sh < p->Ns; ++sh)   // W_sd[s] [d][Is] -> rows s Is.. of [NI][d]
+        MOE_TRY_STATUS(mx_cols(p, s, static_cast<const char*>(sv->ws_down) + (int64_t)sh * d * Is * 2, Is, (int)Is,
+                               nullptr, nullptr, 1, (int)d, d / 32, 0, d, sh * Is, swdt));
+      RowGemmArgs a{};
+      mx_pq(a, sdyq, d, swdt, d, 0);
+      a.offsets = nullptr; a.G = 1; a.M = T; a.N = (int)NI; a.K = (int)d; a.sub = (int)Is;
+      a.C = dgu_s; a.ldc = 2 * NI; a.aux = sv->gu_shared; a.ldaux = 2 * NI;
+      Probe pr(p, "gemm_down_dgrad_swiglu_shared", s);
+      MOE_TRY(launch_row_gemm(DT_MXFP8, OP_DOWN_DGRAD, EPI_SWIGLU_BWD, 128, a, s));
+    }
+    {
+      MOE_TRY_STATUS(mx_cols(p, s, dy, d, (int)d, seg_pad, seg_pad + 2, 1, 0, Tpad / 32, 0, Tpad, 0, sdyt));
+      MOE_TRY_STATUS(mx_cols(p, s, sv->h_shared, NI, (int)NI, seg_pad, seg_pad + 2, 1, 0, Tpad / 32, 0, Tpad, 0, sht));
+      WgradArgs a{};
+      a.P = sdyt.pay; a.Ps = sdyt.sc; a.ldp = Tpad; a.Q = sht.pay; a.Qs = sht.sc; a.ldq = Tpad;
+      a.offsets = seg_pad + 2; a.G = 1; a.Mtok = Tpad; a.M = (int)d; a.N = (int)NI; a.sub = (int)Is;
+      MOE_TRY_STATUS(run_wgrad(p, WG_DOWN, 128, p->sp_wg_down_s, a, gr->dws_down, d * NI, ws,
+                               "gemm_wgrad_down_shared", s, DT_MXFP8));
+    }
+    {
+      MOE_TRY_STATUS(mx_cols(p, s, dgu_s, 2 * NI, (int)(2 * NI), seg_pad, seg_pad + 2, 1, 0, Tpad / 32, 0, Tpad, 0,
+                             sdgut));
+      MOE_TRY_STATUS(mx_cols(p, s, sv->x, d, (int)d, seg_pad, seg_pad + 2, 1, 0, Tpad / 32, 0, Tpad, 0, sxt));
+      WgradArgs a{};
+      a.P = sdgut.pay; a.Ps = sdgut.sc; a.ldp = Tpad; a.Q = sxt.pay; a.Qs = sxt.sc; a.ldq = Tpad;
+      a.offsets = seg_pad + 2; a.G = 1; a.Mtok = Tpad; a.M = (int)(2 * NI); a.N = (int)d; a.sub = (int)d;
+      MOE_TRY_STATUS(run_wgrad(p, WG_GATE_UP, 128, p->sp_wg_gu_s, a, gr->dws_gate_up, 2 * NI * d, ws,
+                               "gemm_wgrad_gate_up_shared", s, DT_MXFP8));
+    }
+    if (T > 0) {
+      MOE_TRY_STATUS(mx_rows(p, s, dgu_s, 2 * NI, 0, (int)(2 * NI), T, (int)(2 * NI), sdguq));
+      for (int sh = 0; sh < p->Ns; ++sh)   // W_sgu[s] [2Is][d] -> K positions s 2Is.. of [d][2 NI]
+        MOE_TRY_STATUS(mx_cols(p, s, static_cast<const char*>(sv->ws_gate_up) + (int64_t)sh * 2 * Is * d * 2, d,
+                               (int)d, nullptr, nullptr, 1, (int)(2 * Is), 2 * Is / 32, sh * 2 * Is, 2 * NI, 0, swgut));
+      RowGemmArgs a{};
+      mx_pq(a, sdguq, 2 * NI, swgut, 2 * NI, 0);
+      a.offsets = nullptr; a.G = 1; a.M = T; a.N = (int)d; a.K = (int)(2 * NI); a.sub = (int)d;
+      a.C = dxs; a.ldc = d;
+      Probe pr(p, "gemm_gate_up_dgrad_shared", s);
+      MOE_TRY(launch_row_gemm(DT_MXFP8, OP_GU_DGRAD, EPI_STORE, 128, a, s));
+    }
+  }
+  return MOE_OK;
+}
+
 moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const moe_grads* gr, void* ws,
                         size_t ws_bytes, void* stream) {
   if (!p || !sv || !gr) return MOE_ERR_NULL;
@@ -478,7 +756,7 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
       Probe pr(p, "router_dz", s);
       MOE_TRY(launch_router_dz(p->dt, a, s));
     }
-    {
+    if (!p->mx) {
       RowGemmArgs a{};
       a.P = dy_perm; a.ldp = d;
       a.Q = sv->w_down; a.ldq = I; a.q_group_stride = (int64_t)d * I;
@@ -488,14 +766,14 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
       MOE_TRY(launch_row_gemm(p->dt, OP_DOWN_DGRAD, EPI_SWIGLU_BWD, p->t_down_dgrad, a, s));
     }
   }
-  {
+  if (!p->mx) {
     WgradArgs a{};
     a.P = dy_perm; a.ldp = d; a.Q = sv->h; a.ldq = I;
     a.offsets = sv->offsets; a.G = E; a.Mtok = p->A; a.M = d; a.N = I; a.sub = I;
     MOE_TRY_STATUS(run_wgrad(p, WG_DOWN, p->t_wg_down, p->sp_wg_down, a, gr->dw_down, (int64_t)d * I, ws,
                              "gemm_wgrad_down", s));
   }
-  if (p->T > 0) {
+  if (p->T > 0 && !p->mx) {
     RowGemmArgs a{};
     a.P = dgu; a.ldp = 2 * I;
     a.Q = sv->w_gate_up; a.ldq = d; a.q_group_stride = (int64_t)2 * I * d;
@@ -504,14 +782,14 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
     Probe pr(p, "gemm_gate_up_dgrad", s);
     MOE_TRY(launch_row_gemm(p->dt, OP_GU_DGRAD, EPI_STORE, p->t_gu_dgrad, a, s));
   }
-  {
+  if (!p->mx) {
     WgradArgs a{};
     a.P = dgu; a.ldp = 2 * I; a.Q = sv->x_perm; a.ldq = d;
     a.offsets = sv->offsets; a.G = E; a.Mtok = p->A; a.M = 2 * I; a.N = d; a.sub = d;
     MOE_TRY_STATUS(run_wgrad(p, WG_GATE_UP, p->t_wg_gu, p->sp_wg_gu, a, gr->dw_gate_up, (int64_t)2 * I * d, ws,
                              "gemm_wgrad_gate_up", s));
   }
-  if (p->Ns > 0) {
+  if (p->Ns > 0 && !p->mx) {
     const int Is = p->Is, NI = p->Ns * p->Is;
     if (p->T > 0) {
       RowGemmArgs a{};
@@ -537,7 +815,8 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
                                ws, "gemm_wgrad_gate_up_shared", s));
     }
   }
-  if (p->Ns > 0 && p->T > 0) {
+  if (p->mx) MOE_TRY_STATUS(mx_backward_experts(p, sv, dy, gr, ws, s, dy_perm, dgu, dx_perm, dgu_s, dxs));
+  if (p->Ns > 0 && p->T > 0 && !p->mx) {
     const int NI = p->Ns * p->Is;
     RowGemmArgs b{};
     b.P = dgu_s; b.ldp = 2 * NI;
@@ -599,6 +878,16 @@ moe_status moe_aux_stats(moe_plan p, const float* probs, const int32_t* counts, 
 }
 
 // ------------------------------------------------------------------ probe --
+moe_status moe_mx_quantize_rows(const void* in, int32_t act_dtype, int64_t rows, int32_t K, uint8_t* payload,
+                                uint8_t* scales, void* stream) {
+  if (rows < 0 || K <= 0 || K % 32) return MOE_ERR_INVALID;
+  if (act_dtype != MOE_BF16 && act_dtype != MOE_F16) return MOE_ERR_INVALID;
+  if (rows == 0) return MOE_OK;
+  if (!in || !payload || !scales) return MOE_ERR_NULL;
+  MxRowsArgs a{in, K, 0, K, rows, K, payload, scales};
+  return hip_status(launch_mx_quant_rows(act_dtype == MOE_F16 ? DT_F16 : DT_BF16, a, static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_probe_enable(moe_plan p, const char* kernel, int max_launches) {
   if (!p) return MOE_ERR_NULL;
   p->release_events();

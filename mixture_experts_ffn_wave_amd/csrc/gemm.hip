@@ -272,6 +272,59 @@ __device__ __forceinline__ void mfma_chunk(f32x16 (&acc)[NS][MS], const char* lq
   }
 }
 
+// ---- MX-fp8 (e4m3 payload, one power-of-two scale per 32 values of k) ----
+// v_mfma_scale_f32_32x32x64_f8f6f4 over a 64-k step (two scale blocks): lane
+// l supplies operand row l % 32, with payload bytes 0-15 from k 16 h .. +15 of
+// the first block and bytes 16-31 from the same offsets of the second block
+// (h = l / 32), and the scale byte of block h of that row; the accumulator
+// layout is that of the other 32x32 MFMAs.  Which k of a block a byte stands
+// for does not change the dot product as long as both operands agree, so only
+// the block membership of each byte and each scale matters.
+typedef int v8i __attribute__((ext_vector_type(8)));
+constexpr int MX_DKB = 128;                 // k bytes (= k values) per ring chunk: 4 scale blocks
+
+// 32 payload bytes of row r: k [64 ks + 16 h, +16) and [64 ks + 32 + 16 h, +16), from a [row][128-byte]
+// tile with the 128-byte-row swizzle of DmaRows (chunk c at c ^ ((r >> 1) & 7))
+__device__ __forceinline__ v8i mx_frag(const char* lds, int r, int ks, int h) {
+  const int c = 4 * ks + h, sw = (r >> 1) & 7;
+  const u32x4 lo = ld16(lds + r * MX_DKB + ((c ^ sw) << 4));
+  const u32x4 hi = ld16(lds + r * MX_DKB + (((c + 2) ^ sw) << 4));
+  return (v8i){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+// One 128-k chunk for a wave: weight-side rows qrow[ns] (read in perm_row
+// order, as on the 16-bit path), token-side rows prow[ms]; scale tiles are
+// [row][4 bytes] (one byte per 32-k block of the chunk).
+template <int NS, int MS>
+__device__ __forceinline__ void mfma_chunk_mx(f32x16 (&acc)[NS][MS], const char* lq, const char* lp,
+                                              const uint8_t* sq, const uint8_t* sp,
+                                              const int (&qrow)[NS], const int (&prow)[MS], int lane) {
+  const int h = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < MX_DKB / 64; ++ks) {
+    v8i fa[NS], fb[MS];
+    int sa[NS], sb[MS];
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) {
+      const int r = qrow[ns] + perm_row(lane & 31);
+      fa[ns] = mx_frag(lq, r, ks, h);
+      sa[ns] = sq[4 * r + 2 * ks + h];
+    }
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+      const int r = prow[ms] + (lane & 31);
+      fb[ms] = mx_frag(lp, r, ks, h);
+      sb[ms] = sp[4 * r + 2 * ks + h];
+    }
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms)
+        acc[ns][ms] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[ns], fb[ms], acc[ns][ms], 0, 0, 0,
+                                                                        sa[ns], 0, sb[ms]);
+  }
+}
+
 template <int NS, int MS>
 __device__ __forceinline__ void zero_acc(f32x16 (&acc)[NS][MS]) {
 #pragma unroll
@@ -298,6 +351,9 @@ constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ void dma4(rsrc_t rs, char* lds_lane0, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_lane0, 4, voff, 0, 0, 0);
 }
 __device__ __forceinline__ void dma16(rsrc_t rs, char* lds_lane0, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_lane0, 16, voff, 0, 0, 0);
@@ -408,22 +464,30 @@ __device__ __forceinline__ void ring_barrier(int remaining) {
 }
 
 // --------------------------------------------------------------- row GEMM ---
-template <typename T, int BM, int BN, int OP, int EPI, int WM, int WN>
+// MX: operands are MX-fp8 payload bytes (T = uint8_t) with scale bytes in
+// a.Ps / a.Qs, both operands K-contiguous rows (transposes are done by the
+// quantiser), outputs bf16.
+template <typename T, int BM, int BN, int OP, int EPI, int WM, int WN, bool MX = false>
 __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) {
   constexpr int ES = sizeof(T);
+  using TO = std::conditional_t<MX, __bf16, T>;               // output / saved-activation type
   constexpr int NW = WM * WN;                                  // waves: WM along rows, WN along columns
   static_assert(ES == 2 || NW == 4, "the register-staged path runs 4 waves");
-  constexpr bool QT = (OP == OP_DOWN_DGRAD || OP == OP_GU_DGRAD || OP == OP_ROUTER_DX);
-  using PO = Operand<T, BM, false>;
-  using QO = Operand<T, BN, QT>;
-  constexpr int BK = PO::BK;
+  static_assert(!MX || (ES == 1 && BM == 128 && BN == 128 && NW == 4), "MX tiles are 128 x 128, 4 waves");
+  constexpr bool QT = !MX && (OP == OP_DOWN_DGRAD || OP == OP_GU_DGRAD || OP == OP_ROUTER_DX);
+  using TOP = std::conditional_t<MX, __bf16, T>;              // (register-path operand type; unused for MX)
+  using PO = Operand<TOP, BM, false>;
+  using QO = Operand<TOP, BN, QT>;
+  constexpr int BK = MX ? MX_DKB : PO::BK;
   constexpr int TILE_N = (OP == OP_GU_FWD) ? BN / 2 : BN;    // output (H) columns per tile
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MS = WTM / 32, NS = WTN / 32;
   constexpr int STAGE = PO::BYTES + QO::BYTES;
 
-  constexpr int DKB = TileCfg<BM, false>::DKB, NSTG = TileCfg<BM, false>::NSTG;
-  constexpr int SCAN_OFF = (ES == 2) ? NSTG * (BM + BN) * DKB : 2 * STAGE;
+  constexpr int DKB = MX ? MX_DKB : TileCfg<BM, false>::DKB;
+  constexpr int NSTG = MX ? 2 : TileCfg<BM, false>::NSTG;
+  constexpr int SC_OFF = NSTG * (BM + BN) * DKB;                // MX scale tiles follow the payload ring
+  constexpr int SCAN_OFF = MX ? SC_OFF + NSTG * (BM + BN) * 4 : ((ES == 2) ? NSTG * (BM + BN) * DKB : 2 * STAGE);
   int* s_scan = reinterpret_cast<int*>(smem + SCAN_OFF);      // [NW] wave sums, [NW..NW+1] located tile
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_ntiles = a.N / TILE_N;
@@ -482,7 +546,7 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
 
   // Accumulator register layout: runs of RUN consecutive output columns, run t
   // starting at column RSTEP*t + RUN*(lane/32) of a 32-column subtile.
-  constexpr bool PERM = (ES == 2);
+  constexpr bool PERM = (ES == 2) || MX;
   constexpr int RUN = PERM ? 8 : 4, NRUN = 16 / RUN, RSTEP = PERM ? 16 : 8;
   static_assert(acc_col<PERM>(RUN, 0) == RSTEP && acc_col<PERM>(0, 1) == RUN, "run layout");
   const int h = lane >> 5;
@@ -510,18 +574,77 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
   // (Loading them before the main loop instead costs VGPRs enough to drop
   // a workgroup per CU, which was slower.)
   auto load_gu_rows = [&](u32x4 (&dst)[2][PERM ? SITER : 1], int ms) {
-    const T* aux = static_cast<const T*>(a.aux);
+    const TO* aux = static_cast<const TO*>(a.aux);
 #pragma unroll
     for (int i = 0; i < SITER; ++i) {
       const int q = tid + 64 * NW * i, sr = q / CPR, c = q % CPR;
       const int tr = srow(sr, ms);
-      const T* src = aux + (row0 + tr) * a.ldaux + gcol0 + c * 8;
+      const TO* src = aux + (row0 + tr) * a.ldaux + gcol0 + c * 8;
       dst[0][i] = (tr < rows) ? ld16(src) : (u32x4){0u, 0u, 0u, 0u};
       dst[1][i] = (tr < rows) ? ld16(src + a.sub) : (u32x4){0u, 0u, 0u, 0u};
     }
   };
 
-  if constexpr (ES == 2) {
+  if constexpr (MX) {
+    // ---------------- direct-to-LDS main loop, MX-fp8 payload + scale tiles
+    using PD = DmaRows<BM, NW, MX_DKB>;
+    using QD = DmaRows<BN, NW, MX_DKB>;
+    constexpr int DSTAGE = PD::BYTES + QD::BYTES;
+    constexpr int SSTAGE = (BM + BN) * 4;
+    const int64_t pls = a.ldp / 32, qls = a.ldq / 32;          // scale bytes per row
+    const rsrc_t prs = make_rsrc(Pb + row0 * a.ldp, (uint32_t)(rows * a.ldp));
+    uint32_t poff[PD::NI];
+#pragma unroll
+    for (int s2 = 0; s2 < PD::NI; ++s2) {
+      const int r = PD::row_of(wave, s2, lane);
+      poff[s2] = (uint32_t)(r * a.ldp + PD::gchunk(r, lane) * 16);
+    }
+    // weight-side row of tile row q
+    auto qsrc_row = [&](int q) -> int64_t {
+      if constexpr (OP == OP_GU_FWD) {
+        const int blk = n0 / a.sub, r0 = n0 - blk * a.sub;
+        return blk * 2 * a.sub + (q < BN / 2 ? r0 + q : a.sub + r0 + (q - BN / 2));
+      } else {
+        return n0 + q;
+      }
+    };
+    uint32_t qoff[QD::NI];
+#pragma unroll
+    for (int s2 = 0; s2 < QD::NI; ++s2) {
+      const int q = QD::row_of(wave, s2, lane);
+      qoff[s2] = (uint32_t)(qsrc_row(q) * a.ldq + QD::gchunk(q, lane) * 16);
+    }
+    // scale rows: wave 0/1 load P rows 0-63 / 64-127, wave 2/3 Q rows 0-63 / 64-127
+    const bool sq_side = wave >= 2;
+    const int srow_t = (wave & 1) * 64 + lane;
+    const uint8_t* qsb = a.Qs + (int64_t)g * (a.q_group_stride / 32);
+    const rsrc_t psrs = make_rsrc(a.Ps + row0 * pls, (uint32_t)(rows * pls));
+    const uint32_t soff = sq_side ? (uint32_t)(qsrc_row(srow_t) * qls) : (uint32_t)(srow_t * pls);
+    auto issue = [&](int kc, int st) {
+      char* stage = smem + st * DSTAGE;
+#pragma unroll
+      for (int s2 = 0; s2 < PD::NI; ++s2) dma16(prs, stage + PD::lds_off(wave, s2), poff[s2] + (uint32_t)kc);
+      const rsrc_t qrs = make_rsrc(Qb + kc, 0x7fffffffu);
+#pragma unroll
+      for (int s2 = 0; s2 < QD::NI; ++s2) dma16(qrs, stage + PD::BYTES + QD::lds_off(wave, s2), qoff[s2]);
+      char* sst = smem + SC_OFF + st * SSTAGE + (sq_side ? BM * 4 : 0) + (wave & 1) * 64 * 4;
+      if (sq_side) dma4(make_rsrc(qsb + kc / 32, 0x7fffffffu), sst, soff);
+      else dma4(psrs, sst, soff + (uint32_t)(kc / 32));
+    };
+    constexpr int LPC = PD::NI + QD::NI + 1;
+    const int nkd = a.K / MX_DKB;
+#pragma unroll
+    for (int c = 0; c < NSTG - 1; ++c)
+      if (c < nkd) issue(c * MX_DKB, c);
+    for (int kc = 0; kc < nkd; ++kc) {
+      ring_barrier<LPC, NSTG>(nkd - 1 - kc);
+      if (kc + NSTG - 1 < nkd) issue((kc + NSTG - 1) * MX_DKB, (kc + NSTG - 1) % NSTG);
+      const int st = kc % NSTG;
+      const char* buf = smem + st * DSTAGE;
+      const uint8_t* sbuf = reinterpret_cast<const uint8_t*>(smem + SC_OFF + st * SSTAGE);
+      mfma_chunk_mx<NS, MS>(acc, buf + PD::BYTES, buf, sbuf + BM * 4, sbuf, qrow, prow, lane);
+    }
+  } else if constexpr (ES == 2) {
     // ---------------- direct-to-LDS main loop (16-bit types)
     using PD = DmaRows<BM, NW, DKB>;
     using QD = std::conditional_t<QT, DmaKmajor<BN, NW, DKB>, DmaRows<BN, NW, DKB>>;
@@ -710,7 +833,7 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
           for (int i = 0; i < RUN; ++i) v[i] = acc[ns][ms][RUN * t + i];
           if constexpr (EPI == EPI_STORE) {
             const int c = (qrow[ns] + RSTEP * t + RUN * h) / 8;
-            store8<T>(reinterpret_cast<T*>(sp(0, sr_l, c)), v);
+            store8<TO>(reinterpret_cast<TO*>(sp(0, sr_l, c)), v);
           } else if constexpr (EPI == EPI_STORE_F32) {
             const int c = (qrow[ns] + RSTEP * t + RUN * h) / 4;
             store4<float>(reinterpret_cast<float*>(sp(0, sr_l, c)), v[0], v[1], v[2], v[3]);
@@ -724,23 +847,23 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
               uv[i] = acc[ns + NS / 2][ms][RUN * t + i];
               hv[i] = silu_f(v[i]) * uv[i];
             }
-            store8<T>(reinterpret_cast<T*>(sp(0, sr_l, c)), v);
-            store8<T>(reinterpret_cast<T*>(sp(1, sr_l, c)), uv);
-            store8<T>(reinterpret_cast<T*>(sp(2, sr_l, c)), hv);
+            store8<TO>(reinterpret_cast<TO*>(sp(0, sr_l, c)), v);
+            store8<TO>(reinterpret_cast<TO*>(sp(1, sr_l, c)), uv);
+            store8<TO>(reinterpret_cast<TO*>(sp(2, sr_l, c)), hv);
           } else if constexpr (EPI == EPI_SWIGLU_BWD) {
             // v = dH; G, U staged at the same positions, overwritten by dG, dU
             const int c = (qrow[ns] + RSTEP * t + RUN * h) / 8;
             float G[RUN], U[RUN], dG[RUN], dU[RUN];
-            unpack8<T>(ld16(sp(0, sr_l, c)), G);
-            unpack8<T>(ld16(sp(1, sr_l, c)), U);
+            unpack8<TO>(ld16(sp(0, sr_l, c)), G);
+            unpack8<TO>(ld16(sp(1, sr_l, c)), U);
 #pragma unroll
             for (int i = 0; i < RUN; ++i) {
               const float sg = sigmoid_f(G[i]);
               dG[i] = v[i] * U[i] * sg * (1.0f + G[i] * (1.0f - sg));
               dU[i] = v[i] * G[i] * sg;
             }
-            store8<T>(reinterpret_cast<T*>(sp(0, sr_l, c)), dG);
-            store8<T>(reinterpret_cast<T*>(sp(1, sr_l, c)), dU);
+            store8<TO>(reinterpret_cast<TO*>(sp(0, sr_l, c)), dG);
+            store8<TO>(reinterpret_cast<TO*>(sp(1, sr_l, c)), dU);
           }
         }
       }
@@ -753,16 +876,16 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
         if (tr >= rows) continue;
         const int64_t row = row0 + tr;
         if constexpr (EPI == EPI_STORE) {
-          st16(static_cast<T*>(a.C) + row * a.ldc + n0 + c * 8, ld16(sp(0, sr, c)));
+          st16(static_cast<TO*>(a.C) + row * a.ldc + n0 + c * 8, ld16(sp(0, sr, c)));
         } else if constexpr (EPI == EPI_STORE_F32) {
           st16(static_cast<float*>(a.C) + row * a.ldc + n0 + c * 4, ld16(sp(0, sr, c)));
         } else if constexpr (EPI == EPI_SWIGLU_FWD) {
-          T* gu = static_cast<T*>(a.C) + row * a.ldc + gcol0 + c * 8;
+          TO* gu = static_cast<TO*>(a.C) + row * a.ldc + gcol0 + c * 8;
           st16(gu, ld16(sp(0, sr, c)));
           st16(gu + a.sub, ld16(sp(1, sr, c)));
-          st16(static_cast<T*>(a.C2) + row * a.ldc2 + n0 + c * 8, ld16(sp(2, sr, c)));
+          st16(static_cast<TO*>(a.C2) + row * a.ldc2 + n0 + c * 8, ld16(sp(2, sr, c)));
         } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-          T* dgu = static_cast<T*>(a.C) + row * a.ldc + gcol0 + c * 8;
+          TO* dgu = static_cast<TO*>(a.C) + row * a.ldc + gcol0 + c * 8;
           st16(dgu, ld16(sp(0, sr, c)));
           st16(dgu + a.sub, ld16(sp(1, sr, c)));
         }
@@ -832,14 +955,21 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
 }
 
 // ------------------------------------------------------------- wgrad GEMM ---
-template <typename T, int BM, int BN, int OUT_F32, int WM, int WN>
+// MX: P is [M][Kpad] and Q [N][Kpad] MX-fp8 payload bytes (token axis
+// contiguous, segments at the padded offsets in a.offsets, each a multiple of
+// 128 tokens, zero past the segment's tokens), scales a.Ps / a.Qs; outputs bf16
+// (or f32 partials).
+template <typename T, int BM, int BN, int OUT_F32, int WM, int WN, bool MX = false>
 __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
   constexpr int ES = sizeof(T);
+  using TO = std::conditional_t<MX, __bf16, T>;
   constexpr int NW = WM * WN;
   static_assert(ES == 2 || NW == 4, "the register-staged path runs 4 waves");
-  using PO = Operand<T, BM, true>;
-  using QO = Operand<T, BN, true>;
-  constexpr int BK = PO::BK;
+  static_assert(!MX || (ES == 1 && BM == 128 && BN == 128 && NW == 4), "MX tiles are 128 x 128, 4 waves");
+  using TOP = std::conditional_t<MX, __bf16, T>;
+  using PO = Operand<TOP, BM, true>;
+  using QO = Operand<TOP, BN, true>;
+  constexpr int BK = MX ? MX_DKB : PO::BK;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MS = WTM / 32, NS = WTN / 32;
   constexpr int STAGE = PO::BYTES + QO::BYTES;
@@ -864,8 +994,8 @@ __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
   const int nk = kend > kbeg ? (int)((kend - kbeg + BK - 1) / BK) : 0;
   const int m0 = mt * BM, n0 = nt * BN;
 
-  const char* Pb = static_cast<const char*>(a.P) + (int64_t)m0 * ES;
-  const char* Qb = static_cast<const char*>(a.Q) + (int64_t)n0 * ES;
+  const char* Pb = static_cast<const char*>(a.P) + (MX ? 0 : (int64_t)m0 * ES);
+  const char* Qb = static_cast<const char*>(a.Q) + (MX ? 0 : (int64_t)n0 * ES);
   const int64_t pld = a.ldp * ES, qld = a.ldq * ES;
   const int wm = wave % WM, wn = wave / WM;
   int qrow[NS], prow[MS];
@@ -876,7 +1006,56 @@ __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
   f32x16 acc[NS][MS];
   zero_acc(acc);
 
-  if constexpr (ES == 2) {
+  if constexpr (MX) {
+    // rows m0.. of P and n0.. of Q, each K-contiguous; chunk = 128 tokens
+    constexpr int NSTG = 2;
+    using PD = DmaRows<BM, NW, MX_DKB>;
+    using QD = DmaRows<BN, NW, MX_DKB>;
+    constexpr int DSTAGE = PD::BYTES + QD::BYTES;
+    constexpr int SSTAGE = (BM + BN) * 4;
+    constexpr int SC_OFF = NSTG * DSTAGE;
+    const int64_t pls = a.ldp / 32, qls = a.ldq / 32;
+    uint32_t poff[PD::NI], qoff[QD::NI];
+#pragma unroll
+    for (int s2 = 0; s2 < PD::NI; ++s2) {
+      const int r = PD::row_of(wave, s2, lane);
+      poff[s2] = (uint32_t)(r * a.ldp + PD::gchunk(r, lane) * 16);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < QD::NI; ++s2) {
+      const int r = QD::row_of(wave, s2, lane);
+      qoff[s2] = (uint32_t)(r * a.ldq + QD::gchunk(r, lane) * 16);
+    }
+    const bool sq_side = wave >= 2;
+    const int sr = (wave & 1) * 64 + lane;
+    const uint32_t soff = sq_side ? (uint32_t)((n0 + sr) * qls) : (uint32_t)((m0 + sr) * pls);
+    const uint8_t* sbase = sq_side ? a.Qs : a.Ps;
+    const int64_t ldp = a.ldp, ldq = a.ldq;
+    auto issue = [&](int64_t kc, int st) {
+      char* stage = smem + st * DSTAGE;
+      const rsrc_t prs = make_rsrc(Pb + (int64_t)m0 * ldp + kc, 0x7fffffffu);
+      const rsrc_t qrs = make_rsrc(Qb + (int64_t)n0 * ldq + kc, 0x7fffffffu);
+#pragma unroll
+      for (int s2 = 0; s2 < PD::NI; ++s2) dma16(prs, stage + PD::lds_off(wave, s2), poff[s2]);
+#pragma unroll
+      for (int s2 = 0; s2 < QD::NI; ++s2) dma16(qrs, stage + PD::BYTES + QD::lds_off(wave, s2), qoff[s2]);
+      char* sst = smem + SC_OFF + st * SSTAGE + (sq_side ? BM * 4 : 0) + (wave & 1) * 64 * 4;
+      dma4(make_rsrc(sbase + kc / 32, 0x7fffffffu), sst, soff);
+    };
+    constexpr int LPC = PD::NI + QD::NI + 1;
+    const int nkd = nk;
+#pragma unroll
+    for (int c = 0; c < NSTG - 1; ++c)
+      if (c < nkd) issue(kbeg + (int64_t)c * MX_DKB, c);
+    for (int kc = 0; kc < nkd; ++kc) {
+      ring_barrier<LPC, NSTG>(nkd - 1 - kc);
+      if (kc + NSTG - 1 < nkd) issue(kbeg + (int64_t)(kc + NSTG - 1) * MX_DKB, (kc + NSTG - 1) % NSTG);
+      const int st = kc % NSTG;
+      const char* buf = smem + st * DSTAGE;
+      const uint8_t* sbuf = reinterpret_cast<const uint8_t*>(smem + SC_OFF + st * SSTAGE);
+      mfma_chunk_mx<NS, MS>(acc, buf + PD::BYTES, buf, sbuf + BM * 4, sbuf, qrow, prow, lane);
+    }
+  } else if constexpr (ES == 2) {
     constexpr int DKB = TileCfg<BM, true>::DKB, NSTG = TileCfg<BM, true>::NSTG;
     using PD = DmaKmajor<BM, NW, DKB>;
     using QD = DmaKmajor<BN, NW, DKB>;
@@ -943,7 +1122,7 @@ __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
   }  // main loops
 
   // out[m][n] at C + g*cgs + sp*css + (n/sub)*(M*sub) + m*sub + n%sub
-  constexpr bool PERM = (ES == 2);
+  constexpr bool PERM = (ES == 2) || MX;
   constexpr int RUN = PERM ? 8 : 4, NRUN = 16 / RUN, RSTEP = PERM ? 16 : 8;
   const int h = lane >> 5;
 #pragma unroll
@@ -961,7 +1140,7 @@ __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
 #pragma unroll
         for (int i = 0; i < RUN; ++i) v[i] = acc[ns][ms][RUN * t + i];
         if constexpr (OUT_F32) store_run<float, RUN>(static_cast<float*>(a.C) + off, v);
-        else store_run<T, RUN>(static_cast<T*>(a.C) + off, v);
+        else store_run<TO, RUN>(static_cast<TO*>(a.C) + off, v);
       }
     }
   }
@@ -1019,6 +1198,27 @@ MOE_KERNEL_SET(_Float16, f16, 256, 256)
 MOE_KERNEL_SET(_Float16, f16, 128, 128)
 MOE_KERNEL_SET(float, f32, 128, 128)
 
+// MX-fp8 expert GEMMs (128 x 128 tiles, 4 waves, 2-stage ring of 128-byte chunks)
+#define MOE_MX_ROW_KERNEL(NAME, OP, EPI)                                                              \
+  extern "C" __global__ void __launch_bounds__(256) NAME(RowGemmArgs a) {                          \
+    extern __shared__ __attribute__((aligned(16))) char smem[];                                   \
+    row_gemm_body<uint8_t, 128, 128, OP, EPI, 2, 2, true>(a, smem);                               \
+  }
+#define MOE_MX_WGRAD_KERNEL(NAME, F32)                                                                \
+  extern "C" __global__ void __launch_bounds__(256) NAME(WgradArgs a) {                            \
+    extern __shared__ __attribute__((aligned(16))) char smem[];                                   \
+    wgrad_body<uint8_t, 128, 128, F32, 2, 2, true>(a, smem);                                      \
+  }
+MOE_MX_ROW_KERNEL(moe_mx_gemm_gate_up_swiglu_128x128, OP_GU_FWD, EPI_SWIGLU_FWD)
+MOE_MX_ROW_KERNEL(moe_mx_gemm_down_128x128, OP_DOWN_FWD, EPI_STORE)
+MOE_MX_ROW_KERNEL(moe_mx_gemm_down_f32out_128x128, OP_DOWN_FWD, EPI_STORE_F32)
+MOE_MX_ROW_KERNEL(moe_mx_gemm_down_dgrad_swiglu_128x128, OP_DOWN_DGRAD, EPI_SWIGLU_BWD)
+MOE_MX_ROW_KERNEL(moe_mx_gemm_gate_up_dgrad_128x128, OP_GU_DGRAD, EPI_STORE)
+MOE_MX_WGRAD_KERNEL(moe_mx_wgrad_down_128x128, 0)
+MOE_MX_WGRAD_KERNEL(moe_mx_wgrad_gate_up_128x128, 0)
+MOE_MX_WGRAD_KERNEL(moe_mx_wgrad_down_f32out_128x128, 1)
+MOE_MX_WGRAD_KERNEL(moe_mx_wgrad_gate_up_f32out_128x128, 1)
+
 namespace {
 
 typedef void (*RowKernel)(RowGemmArgs);
@@ -1048,6 +1248,16 @@ const KernelSet* kernel_set(int dt, int tile) {
   if (dt == DT_BF16) return tile == 256 ? &bf16_256 : &bf16_128;
   if (dt == DT_F16) return tile == 256 ? &f16_256 : &f16_128;
   if (dt == DT_F32 && tile == 128) return &f32_128;
+  if (dt == DT_MXFP8 && tile == 128) {
+    constexpr size_t mx_lds = 2 * (128 + 128) * MX_DKB + 2 * (128 + 128) * 4 + 64;
+    static const KernelSet mx_128{moe_mx_gemm_gate_up_swiglu_128x128, moe_mx_gemm_down_128x128,
+                                  moe_mx_gemm_down_f32out_128x128, moe_mx_gemm_down_dgrad_swiglu_128x128,
+                                  moe_mx_gemm_gate_up_dgrad_128x128, nullptr,
+                                  moe_mx_wgrad_down_128x128, moe_mx_wgrad_gate_up_128x128,
+                                  moe_mx_wgrad_down_f32out_128x128, moe_mx_wgrad_gate_up_f32out_128x128,
+                                  nullptr, mx_lds, mx_lds};
+    return &mx_128;
+  }
   return nullptr;
 }
 
@@ -1076,6 +1286,9 @@ hipError_t launch_row_gemm(int dt, int op, int epi, int tile, const RowGemmArgs&
     case OP_ROUTER_DX: k = set->router_dx_f32; break;
     default: return hipErrorInvalidValue;
   }
+  if (!k) return hipErrorInvalidValue;
+  if (dt == DT_MXFP8 && (a.ldp % 128 || a.ldq % 128 || a.q_group_stride % 32 || !a.Ps || !a.Qs))
+    return hipErrorInvalidValue;
   const int tile_n = (op == OP_GU_FWD) ? tile / 2 : tile;
   if (a.N % tile_n || a.K % (KB / dtype_bytes(dt))) return hipErrorInvalidValue;
   const int64_t n_ntiles = a.N / tile_n;
@@ -1103,7 +1316,8 @@ hipError_t launch_wgrad(int dt, int op, int tile, const WgradArgs& a, hipStream_
     case WG_ROUTER: k = set->wgrad_router_f32; break;
     default: return hipErrorInvalidValue;
   }
-  if (op == WG_ROUTER && !a.out_f32) return hipErrorInvalidValue;
+  if (!k || (op == WG_ROUTER && !a.out_f32)) return hipErrorInvalidValue;
+  if (dt == DT_MXFP8 && (a.ldp % 128 || a.ldq % 128 || !a.offsets || !a.Ps || !a.Qs)) return hipErrorInvalidValue;
   if (a.M % tile || a.N % tile) return hipErrorInvalidValue;
   int64_t grid = (int64_t)a.G * a.splits * (a.M / tile) * (a.N / tile);
   grid = (grid + 7) / 8 * 8;

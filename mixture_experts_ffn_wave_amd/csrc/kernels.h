@@ -6,9 +6,11 @@
 
 namespace moe {
 
-enum DType { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+// DT_MXFP8: GEMM operands are MX-fp8 (e4m3 payload bytes plus one UE8M0 scale
+// byte per 32 values along K); GEMM outputs are bf16 (or f32 where stated).
+enum DType { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_MXFP8 = 3 };
 
-inline int dtype_bytes(int dt) { return dt == DT_F32 ? 4 : 2; }
+inline int dtype_bytes(int dt) { return dt == DT_F32 ? 4 : (dt == DT_MXFP8 ? 1 : 2); }
 
 // ---------------------------------------------------------------- router --
 struct RouteArgs {
@@ -61,6 +63,9 @@ struct RowGemmArgs {
   void* C; int64_t ldc;            // main output
   void* C2; int64_t ldc2;          // second output (H for OP_GU_FWD)
   const void* aux; int64_t ldaux;  // saved GU (SwiGLU backward epilogue)
+  // DT_MXFP8 only: scale bytes of P ([rows][K/32], row stride ldp/32) and of
+  // Q ([rows][K/32], row stride ldq/32, group stride q_group_stride/32)
+  const uint8_t* Ps; const uint8_t* Qs;
 };
 // tile: 256 (16-bit types only) or 128; the plan chooses it once per GEMM.
 hipError_t launch_row_gemm(int dt, int op, int epi, int tile, const RowGemmArgs& a, hipStream_t s);
@@ -78,10 +83,50 @@ struct WgradArgs {
   int64_t c_group_stride, c_split_stride;
   int sub;
   int out_f32;                     // 1: write f32 partials, 0: write act dtype
+  // DT_MXFP8 only: P is [M][Kpad] and Q is [N][Kpad] (token axis contiguous,
+  // segments at the padded offsets `offsets`, each a multiple of 128 tokens),
+  // with scale bytes Ps [M][Kpad/32], Qs [N][Kpad/32].
+  const uint8_t* Ps; const uint8_t* Qs;
 };
 // One kernel symbol per weight gradient (same tile engine) so profiles tell them apart.
 enum WgradOp { WG_DOWN = 0, WG_GATE_UP = 1, WG_ROUTER = 2 };
 hipError_t launch_wgrad(int dt, int op, int tile, const WgradArgs& a, hipStream_t s);
+
+// ------------------------------------------------- MX-fp8 quantisation --
+// e4m3 payload plus one UE8M0 scale byte (exponent + 127) per block of 32
+// values along K; the scale is the smallest power of two 2^x with
+// amax <= 448 * 2^x (x clamped to [-127, 127], -127 for an all-zero block).
+
+// Row operands: element (r, k) at in + (k / sub) * block_stride + r * ld_in + k % sub
+// (sub = K: plain rows; sub < K: K concatenates blocks of width sub).
+struct MxRowsArgs {
+  const void* in; int64_t ld_in; int64_t block_stride; int sub;
+  int64_t R; int K;
+  uint8_t* out;        // [R][K]
+  uint8_t* scales;     // [R][K/32]
+};
+hipError_t launch_mx_quant_rows(int dt, const MxRowsArgs& a, hipStream_t s);
+
+// Transposing quantiser: the token axis of in ([tokens][C], row stride ld_in)
+// becomes K.  Tokens come in G segments (seg = bounds, or fixed segments of
+// seg_len); segment g occupies K positions k0 + [pad[g], pad[g+1]) (pad =
+// padded bounds, multiples of 32, or g * seg_len); 32-blocks restart at each
+// segment start and positions past its tokens hold zeros.  Column c becomes
+// output row row0 + c.
+struct MxColsArgs {
+  const void* in; int64_t ld_in; int C;
+  const int32_t* seg; const int32_t* pad; int G; int seg_len;
+  int64_t nblk;        // grid bound: number of 32-blocks to cover (>= pad[G] / 32)
+  int64_t k0, Kpad, row0;
+  uint8_t* out;        // [rows][Kpad]
+  uint8_t* scales;     // [rows][Kpad/32]
+};
+hipError_t launch_mx_quant_cols(int dt, const MxColsArgs& a, hipStream_t s);
+
+// pad[g+1] = pad[g] + ceil((offsets[g+1] - offsets[g]) / align) * align, pad[0] = 0
+hipError_t launch_mx_pad_offsets(const int32_t* offsets, int32_t* pad, int G, int align, hipStream_t s);
+// one segment of T tokens: seg_pad = {0, T, 0, ceil(T / align) * align}
+hipError_t launch_mx_single_segment(int32_t* seg_pad, int64_t T, int align, hipStream_t s);
 
 // ------------------------------------------------------ element-wise --
 struct CombineArgs {

@@ -88,6 +88,16 @@ class MoELayer:
         L.moe_backward(self.plan, self.saved(), dy, self.grads, self.ws, stream)
         return self.grads
 
+    def backward_intermediate(self, name):
+        """View of an intermediate the last backward left in the workspace
+        ("dy_perm", "dgu", "dx_perm", "dgu_shared", "dx_shared")."""
+        p = self.plan
+        A, NI = p.T * p.k, p.Ns * p.Is
+        shape = {"dy_perm": (A, p.d), "dgu": (A, 2 * p.I), "dx_perm": (A, p.d),
+                 "dgu_shared": (p.T, 2 * NI), "dx_shared": (p.T, p.d)}[name]
+        off, nb = L.workspace_region(p, name)
+        return self.ws[off:off + nb].view(p.dtype).view(*shape)
+
     def aux_stats(self, stream=None):
         L.moe_aux_stats(self.plan, self.probs, self.counts, self.f, self.p_mean, self.aux_out, self.ws, stream)
 

@@ -48,13 +48,16 @@ def say(msg):
 
 
 def rel_tol(wl):
+    if wl.expert_dtype == "mxfp8":
+        return 6e-2
     return 1e-4 if wl.dtype == "f32" else 2e-2
 
 
 def plan_for(wl, has_bias):
     from mixture_experts_ffn_wave_amd import Plan
     return Plan(wl.T, wl.d, wl.E, wl.k, wl.I, n_shared=wl.n_shared, d_ff_shared=wl.I_shared,
-                renorm=wl.renorm, has_router_bias=has_bias, dtype=wl.torch_dtype, aux_coef=wl.aux_coef)
+                renorm=wl.renorm, has_router_bias=has_bias, dtype=wl.torch_dtype, aux_coef=wl.aux_coef,
+                expert_dtype=wl.expert_dtype or None)
 
 
 def to_np(t):
@@ -66,9 +69,11 @@ def to_np(t):
     return t.to(torch.float64).numpy()
 
 
-def gpu_run(wl, inp, routing=None):
+def gpu_run(wl, inp, routing=None, intermediates=False):
     """One fwd+bwd step on cuda:0.  ``routing`` (probs, idx, w as numpy) replaces
-    the router's outputs when given (then moe_route is not called)."""
+    the router's outputs when given (then moe_route is not called).
+    ``intermediates`` also returns what the backward left in the workspace
+    (dy_perm, dgu, dx_perm and, with shared experts, dgu_shared, dx_shared)."""
     from mixture_experts_ffn_wave_amd import MoELayer, decode_aux
     b = inp.get("bias")
     plan = plan_for(wl, b is not None)
@@ -93,6 +98,10 @@ def gpu_run(wl, inp, routing=None):
     for n, t in layer.grads.items():
         out[n] = to_np(t)
     out["aux"] = decode_aux(layer.aux_out)
+    if intermediates:
+        names = ["dy_perm", "dgu", "dx_perm"] + (["dgu_shared", "dx_shared"] if wl.n_shared else [])
+        for n in names:
+            out[n] = to_np(layer.backward_intermediate(n))
     return out
 
 
@@ -105,12 +114,12 @@ def storage_rounding(wl):
     return lambda a, kind: O.round_to_format(a, "f32" if kind == "f32" else wl.dtype)
 
 
-def oracle_run(wl, f64, store=None):
+def oracle_run(wl, f64, store=None, quant=None):
     b = f64.get("bias")
     fwd = O.layer_forward(f64["x"], f64["w_router"], f64["w_gate_up"], f64["w_down"], top_k=wl.k,
                           renorm=wl.renorm, bias=b, ws_gate_up=f64.get("ws_gate_up"),
-                          ws_down=f64.get("ws_down"), store=store)
-    bwd = O.layer_backward(fwd, f64["dy"], aux_coef=wl.aux_coef)
+                          ws_down=f64.get("ws_down"), store=store, quant=quant)
+    bwd = O.layer_backward(fwd, f64["dy"], aux_coef=wl.aux_coef, quant=quant)
     st = O.aux_statistics(fwd["p"], fwd["counts"], wl.k)
     return fwd, bwd, st
 
@@ -177,6 +186,28 @@ def compare_routing(wl, gpu, fwd):
     return bool(same.all())
 
 
+def compare_dispatch(gpu, fwd):
+    """Integer work and the gather: bit-exact."""
+    assert np.array_equal(gpu["counts"], fwd["counts"]), "counts"
+    assert np.array_equal(gpu["offsets"], fwd["offsets"]), "offsets"
+    assert np.array_equal(gpu["perm_token"], fwd["perm_token"]), "perm_token"
+    assert np.array_equal(gpu["inv_perm"], fwd["inv"]), "inv_perm"
+    assert np.array_equal(gpu["x_perm"], fwd["x_perm"]), "x_perm is a pure copy"
+
+
+def compare_stats(gpu, st):
+    """Balancing statistic and router metrics."""
+    assert np.allclose(gpu["f"], st["f"], rtol=1e-6, atol=0), "f"
+    assert np.max(np.abs(gpu["p_mean"] - st["p_mean"])) <= PROB_ATOL, "p_mean"
+    a = gpu["aux"]
+    assert abs(a["aux"] - st["aux"]) <= 1e-5 * max(1.0, abs(st["aux"])), ("aux", a["aux"], st["aux"])
+    assert abs(a["aux_raw"] - st["aux_raw"]) <= 1e-5 * max(1.0, abs(st["aux_raw"]))
+    assert abs(a["entropy_mean"] - st["entropy_mean"]) <= 1e-5 * max(1.0, abs(st["entropy_mean"]))
+    assert abs(a["count_cv"] - st["count_cv"]) <= 1e-5 * max(1.0, abs(st["count_cv"]))
+    assert a["count_min"] == st["count_min"] and a["count_max"] == st["count_max"]
+    assert a["n_unused"] == st["n_unused"]
+
+
 def compare_downstream(wl, gpu, fwd, bwd, st, rounded=False):
     """``rounded``: the reference holds its stored intermediates rounded to
     the storage format too; both sides of those comparisons then carry up to
@@ -184,12 +215,7 @@ def compare_downstream(wl, gpu, fwd, bwd, st, rounded=False):
     c = rel_tol(wl)
     dt = wl.dtype
     ku = 1.0 if rounded else 0.5
-    # integer work: bit-exact
-    assert np.array_equal(gpu["counts"], fwd["counts"]), "counts"
-    assert np.array_equal(gpu["offsets"], fwd["offsets"]), "offsets"
-    assert np.array_equal(gpu["perm_token"], fwd["perm_token"]), "perm_token"
-    assert np.array_equal(gpu["inv_perm"], fwd["inv"]), "inv_perm"
-    assert np.array_equal(gpu["x_perm"], fwd["x_perm"]), "x_perm is a pure copy"
+    compare_dispatch(gpu, fwd)
     inter = wl.I
     check_close("G", gpu["gu"][:, :inter], fwd["g"], c, dt, ku)
     check_close("U", gpu["gu"][:, inter:], fwd["u"], c, dt, ku)
@@ -222,43 +248,159 @@ def compare_downstream(wl, gpu, fwd, bwd, st, rounded=False):
         for s_ in range(wl.n_shared):
             check_close(f"dWs_gate_up[{s_}]", gpu["dws_gate_up"][s_], bwd["dws_gate_up"][s_], c, dt)
             check_close(f"dWs_down[{s_}]", gpu["dws_down"][s_], bwd["dws_down"][s_], c, dt)
-    # balancing statistic and metrics
-    assert np.allclose(gpu["f"], st["f"], rtol=1e-6, atol=0), "f"
-    assert np.max(np.abs(gpu["p_mean"] - st["p_mean"])) <= PROB_ATOL, "p_mean"
-    a = gpu["aux"]
-    assert abs(a["aux"] - st["aux"]) <= 1e-5 * max(1.0, abs(st["aux"])), ("aux", a["aux"], st["aux"])
-    assert abs(a["aux_raw"] - st["aux_raw"]) <= 1e-5 * max(1.0, abs(st["aux_raw"]))
-    assert abs(a["entropy_mean"] - st["entropy_mean"]) <= 1e-5 * max(1.0, abs(st["entropy_mean"]))
-    assert abs(a["count_cv"] - st["count_cv"]) <= 1e-5 * max(1.0, abs(st["count_cv"]))
-    assert a["count_min"] == st["count_min"] and a["count_max"] == st["count_max"]
-    assert a["n_unused"] == st["n_unused"]
+    compare_stats(gpu, st)
 
 
-def full_parity(wl, inp=None):
+def compare_mx_stepwise(wl, gpu, fwd, f64, st):
+    """An MX layer, one GEMM step at a time.  MX quantisation turns each
+    stored value into a code, and a value one storage ulp away from the
+    oracle's can land on the next code (or, at a block's largest value, on
+    the next block scale); such a step is correct for its own input, yet
+    the change travels down the chain.  So every step after the first is
+    checked on the inputs the GPU step received: the oracle's step function
+    runs on the GPU's stored G, U, H, Y_perm, dY_perm, [dG | dU], dX_perm
+    (and the shared experts' counterparts), quantising them itself."""
+    c = rel_tol(wl)
+    dt = wl.dtype
+    q = O.mx_fake_quant
+    sr = storage_rounding(wl)
+    I, E, k, d = wl.I, wl.E, wl.k, wl.d
+    off = fwd["offsets"]
+    inv = fwd["inv"]
+    compare_dispatch(gpu, fwd)
+    G, U, H = gpu["gu"][:, :I], gpu["gu"][:, I:], gpu["h"]
+    # gate/up: its inputs (x_perm, the weights) are the oracle's own
+    check_close("G", G, fwd["g"], c, dt, 1.0)
+    check_close("U", U, fwd["u"], c, dt, 1.0)
+    check_close("H", H, fwd["h"], c, dt, 1.0)
+    y_perm = np.zeros_like(gpu["y_perm"])
+    for e in range(E):
+        r0, r1 = off[e], off[e + 1]
+        if r1 > r0:
+            y_perm[r0:r1] = sr(O.expert_down_step(H[r0:r1], f64["w_down"][e], q), "f32")
+    check_close("Y_perm", gpu["y_perm"], y_perm, c, "f32", 1.0)
+    y_shared = None
+    if wl.n_shared:
+        Is = wl.I_shared
+        y_shared = np.zeros((wl.T, d))
+        for s_, (gs, us, hs) in enumerate(fwd["shared"]):
+            Gs = gpu["gu_shared"][:, 2 * s_ * Is:2 * s_ * Is + Is]
+            Us = gpu["gu_shared"][:, 2 * s_ * Is + Is:2 * (s_ + 1) * Is]
+            Hs = gpu["h_shared"][:, s_ * Is:(s_ + 1) * Is]
+            check_close(f"G_shared[{s_}]", Gs, gs, c, dt, 1.0)
+            check_close(f"U_shared[{s_}]", Us, us, c, dt, 1.0)
+            check_close(f"H_shared[{s_}]", Hs, hs, c, dt, 1.0)
+            y_shared += O.expert_down_step(Hs, f64["ws_down"][s_], q)
+        check_close("Y_shared", gpu["y_shared"], sr(y_shared, "act"), c, dt, 1.0)
+    w = gpu["topk_w"]
+    check_close("y", gpu["y"], O.combine(gpu["y_perm"], inv, w, gpu.get("y_shared")), c, dt)
+
+    # backward
+    dy = f64["dy"]
+    dy_perm = np.zeros_like(gpu["dy_perm"])
+    dy_perm[inv.reshape(-1)] = sr((w[:, :, None] * dy[:, None, :]).reshape(-1, d), "act")
+    check_close("dY_perm", gpu["dy_perm"], dy_perm, c, dt, 1.0)
+    dgu = np.zeros_like(gpu["dgu"])
+    dx_perm = np.zeros_like(gpu["dx_perm"])
+    ref_dwgu = np.zeros_like(gpu["dw_gate_up"])
+    ref_dwd = np.zeros_like(gpu["dw_down"])
+    for e in range(E):
+        r0, r1 = off[e], off[e + 1]
+        if r1 == r0:
+            continue
+        dgu[r0:r1], ref_dwd[e] = O.expert_down_backward_step(gpu["dy_perm"][r0:r1], G[r0:r1], U[r0:r1],
+                                                             H[r0:r1], f64["w_down"][e], q, sr)
+        dxe, ref_dwgu[e] = O.expert_gate_up_backward_step(gpu["dgu"][r0:r1], gpu["x_perm"][r0:r1],
+                                                          f64["w_gate_up"][e], q)
+        dx_perm[r0:r1] = sr(dxe, "act")
+    check_close("dGU", gpu["dgu"], dgu, c, dt, 1.0)
+    check_close("dX_perm", gpu["dx_perm"], dx_perm, c, dt, 1.0)
+    fl_gu = float(np.sqrt(np.mean(ref_dwgu ** 2)))
+    fl_d = float(np.sqrt(np.mean(ref_dwd ** 2)))
+    for e in range(E):
+        check_close(f"dW_gate_up[{e}]", gpu["dw_gate_up"][e], ref_dwgu[e], c, dt, rms_floor=fl_gu)
+        check_close(f"dW_down[{e}]", gpu["dw_down"][e], ref_dwd[e], c, dt, rms_floor=fl_d)
+    for e in np.where(fwd["counts"] == 0)[0]:
+        assert not np.any(gpu["dw_gate_up"][e]) and not np.any(gpu["dw_down"][e]), f"empty expert {e} grads"
+    dx = np.zeros((wl.T, d))
+    for j in range(k):
+        dx += gpu["dx_perm"][inv[:, j]]
+    if wl.n_shared:
+        Is = wl.I_shared
+        dxs = np.zeros((wl.T, d))
+        for s_ in range(wl.n_shared):
+            Gs = gpu["gu_shared"][:, 2 * s_ * Is:2 * s_ * Is + Is]
+            Us = gpu["gu_shared"][:, 2 * s_ * Is + Is:2 * (s_ + 1) * Is]
+            Hs = gpu["h_shared"][:, s_ * Is:(s_ + 1) * Is]
+            dgs, dwsd = O.expert_down_backward_step(dy, Gs, Us, Hs, f64["ws_down"][s_], q, sr)
+            check_close(f"dGU_shared[{s_}]", gpu["dgu_shared"][:, 2 * s_ * Is:2 * (s_ + 1) * Is], dgs, c, dt, 1.0)
+            check_close(f"dWs_down[{s_}]", gpu["dws_down"][s_], dwsd, c, dt)
+            dxs_s, dwsgu = O.expert_gate_up_backward_step(gpu["dgu_shared"][:, 2 * s_ * Is:2 * (s_ + 1) * Is],
+                                                          f64["x"], f64["ws_gate_up"][s_], q)
+            check_close(f"dWs_gate_up[{s_}]", gpu["dws_gate_up"][s_], dwsgu, c, dt)
+            dxs += dxs_s
+        check_close("dX_shared", gpu["dx_shared"], sr(dxs, "act"), c, dt, 1.0)
+        dx += gpu["dx_shared"]
+    # router: from the GPU's probabilities, weights and expert output rows
+    _, dz = O.router_backward(dy, gpu["y_perm"], inv, gpu["probs"], fwd["idx"], w, wl.renorm,
+                              fwd["counts"], wl.aux_coef, sr)
+    check_close("dW_router", gpu["dw_router"], dz.T @ f64["x"], c, dt)
+    check_close("dbias", gpu["dbias"], dz.sum(axis=0), c, "f32")
+    check_close("dx", gpu["dx"], dx + dz @ f64["w_router"], c, dt)
+    compare_stats(gpu, st)
+
+
+def full_parity(wl, inp=None, mx_diagnostic=True):
     """The whole chain on the GPU against the oracle.  When a near-tie made
     the GPU pick a different (valid) routing, the downstream calls are run a
     second time from the oracle's routing so every later tensor is compared
-    on identical assignments."""
+    on identical assignments.
+
+    A layer with MX-fp8 experts is compared with the oracle's layer that
+    quantises the same GEMM operands to MX-fp8 (the method's own step), with
+    bf16 storage of what it keeps between steps, one GEMM step at a time
+    (compare_mx_stepwise); ``mx_diagnostic`` also prints its distance from
+    that whole oracle layer and from the unquantised layer, for the record."""
     if inp is None:
         inp = MI.make_inputs(wl)
     f64 = oracle_inputs(inp)
     say(f"[parity] {wl.name}: {MI.describe(wl)} -- GPU chain")
-    gpu = gpu_run(wl, inp)
-    rounded = wl.dtype == "bf16"
-    say(f"[parity] {wl.name}: oracle" + (" (bf16 storage rounding)" if rounded else ""))
-    fwd, bwd, st = oracle_run(wl, f64, storage_rounding(wl) if rounded else None)
+    mx = wl.expert_dtype == "mxfp8"
+    gpu = gpu_run(wl, inp, intermediates=mx)
+    rounded = wl.dtype == "bf16" or mx
+    say(f"[parity] {wl.name}: oracle" + (" (bf16 storage rounding)" if rounded else "") +
+        (" (MX-quantised expert GEMM operands)" if mx else ""))
+    fwd, bwd, st = oracle_run(wl, f64, storage_rounding(wl) if rounded else None,
+                              quant=O.mx_fake_quant if mx else None)
     identical = compare_routing(wl, gpu, fwd)
     if not identical:
         say(f"[parity] {wl.name}: near-tie routing differs; rerunning downstream from the oracle routing")
-        gpu = gpu_run(wl, inp, routing={"p": fwd["p"], "idx": fwd["idx"], "w": fwd["w"]})
+        gpu = gpu_run(wl, inp, routing={"p": fwd["p"], "idx": fwd["idx"], "w": fwd["w"]}, intermediates=mx)
     REPORT.clear()
-    compare_downstream(wl, gpu, fwd, bwd, st, rounded=rounded)
+    if mx:
+        compare_mx_stepwise(wl, gpu, fwd, f64, st)
+    else:
+        compare_downstream(wl, gpu, fwd, bwd, st, rounded=rounded)
     worst = {}
     for n, r in REPORT:
         key = n.split("[")[0]
         worst[key] = max(worst.get(key, 0.0), r)
     say(f"[parity] {wl.name}: raw max|err|/RMS " + " ".join(f"{n}={r:.4f}" for n, r in worst.items()))
-    if rounded:
+    if mx and mx_diagnostic:
+        # distance from the oracle's whole MX layer, for the record (not asserted)
+        REPORT.clear()
+        STRICT[0] = False
+        try:
+            compare_downstream(wl, gpu, fwd, bwd, st, rounded=True)
+        finally:
+            STRICT[0] = True
+        ex = {}
+        for n, r in REPORT:
+            key = n.split("[")[0]
+            ex[key] = max(ex.get(key, 0.0), r)
+        say(f"[parity] {wl.name}: vs the whole MX oracle layer, raw max|err|/RMS " +
+            " ".join(f"{n}={r:.4f}" for n, r in ex.items()))
+    if rounded and (mx_diagnostic or not mx):
         # distance from the exact layer, for the record (not asserted)
         xf, xb, xs = oracle_run(wl, f64)
         REPORT.clear()

@@ -84,6 +84,10 @@ def _create(**kw):
     (dict(aux_coef=float("nan")), MOE_ERR_INVALID),
     (dict(act_dtype=L.MOE_F32, expert_dtype=L.MOE_F32), MOE_OK),
     (dict(act_dtype=L.MOE_F16, expert_dtype=L.MOE_F16), MOE_OK),
+    (dict(expert_dtype=L.MOE_MXFP8_E4M3), MOE_OK),                              # bf16 act, MX experts
+    (dict(act_dtype=L.MOE_F16, expert_dtype=L.MOE_MXFP8_E4M3), MOE_ERR_UNSUPPORTED),  # MX GEMMs write bf16
+    (dict(act_dtype=L.MOE_F32, expert_dtype=L.MOE_MXFP8_E4M3), MOE_ERR_UNSUPPORTED),
+    (dict(expert_dtype=L.MOE_MXFP8_E4M3, n_shared=2, d_ff_shared=256), MOE_OK),
 ])
 def test_plan_validation(kw, status):
     st, h = _create(**kw)
@@ -166,3 +170,45 @@ def test_empty_batch_route_and_combine_are_no_ops():
     assert lib.moe_route(p.handle, None, None, None, None, None, None, None) == MOE_OK
     assert lib.moe_combine(p.handle, None, None, None, None, None, None) == MOE_OK
     p.close()
+
+
+def test_mx_plan_needs_more_workspace_for_the_quantised_operands():
+    a = L.Plan(512, 256, 8, 2, 128).workspace_bytes()
+    b = L.Plan(512, 256, 8, 2, 128, expert_dtype="mxfp8").workspace_bytes()
+    assert b > a
+
+
+def test_mx_quantize_rejects_bad_arguments_before_any_launch():
+    lib = L.lib()
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.moe_mx_quantize_rows(fake, L.MOE_BF16, 4, 48, fake, fake, None) == MOE_ERR_INVALID   # K % 32
+    assert lib.moe_mx_quantize_rows(fake, L.MOE_F32, 4, 64, fake, fake, None) == MOE_ERR_INVALID    # act dtype
+    assert lib.moe_mx_quantize_rows(fake, L.MOE_BF16, -1, 64, fake, fake, None) == MOE_ERR_INVALID
+    assert lib.moe_mx_quantize_rows(None, L.MOE_BF16, 4, 64, fake, fake, None) == MOE_ERR_NULL
+    assert lib.moe_mx_quantize_rows(None, L.MOE_BF16, 0, 64, None, None, None) == MOE_OK            # nothing to do
+
+
+def test_workspace_regions_lie_inside_the_workspace_and_do_not_overlap():
+    lib = L.lib()
+    T, d, E, k, I, Ns, Is = 300, 256, 8, 2, 128, 2, 128
+    p = L.Plan(T, d, E, k, I, n_shared=Ns, d_ff_shared=Is)
+    ws = p.workspace_bytes()
+    expect = {"dy_perm": T * k * d * 2, "dgu": T * k * 2 * I * 2, "dx_perm": T * k * d * 2,
+              "dgu_shared": T * 2 * Ns * Is * 2, "dx_shared": T * d * 2}
+    spans = []
+    for name, nbytes in expect.items():
+        off, nb = L.workspace_region(p, name)
+        assert nb == nbytes, name
+        assert off % 256 == 0 and off + nb <= ws, name
+        spans.append((off, off + nb))
+    spans.sort()
+    assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:])), "regions overlap"
+    off, nb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.moe_workspace_region(p.handle, b"dz", ctypes.byref(off), ctypes.byref(nb)) == MOE_ERR_INVALID
+    assert lib.moe_workspace_region(p.handle, None, ctypes.byref(off), ctypes.byref(nb)) == MOE_ERR_NULL
+    assert lib.moe_workspace_region(None, b"dgu", ctypes.byref(off), ctypes.byref(nb)) == MOE_ERR_NULL
+    p.close()
+    q = L.Plan(T, d, E, k, I)                                  # no shared experts: no shared regions
+    assert lib.moe_workspace_region(q.handle, b"dgu_shared", ctypes.byref(off), ctypes.byref(nb)) == MOE_ERR_INVALID
+    assert lib.moe_workspace_region(q.handle, b"dgu", ctypes.byref(off), ctypes.byref(nb)) == MOE_OK
+    q.close()

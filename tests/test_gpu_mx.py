@@ -1,0 +1,74 @@
+"""GPU parity of the MX-fp8 expert path: the quantiser bit for bit against
+the oracle's MX rule, and the layer with MX experts against the oracle's
+layer that MX-quantises the same expert GEMM operands, at the MX tolerance
+(6e-2 x RMS), with the distance from the unquantised layer printed
+alongside."""
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as MI
+import oracle as O
+from tests import parity as PT
+
+pytestmark = pytest.mark.gpu
+
+W = MI.Workload
+
+
+def e4m3_value(code):
+    """Value of an OCP e4m3 byte, from the format's definition (bias 7,
+    3 mantissa bits, subnormals m * 2^-9)."""
+    code = np.asarray(code, dtype=np.int64)
+    sign = np.where(code & 0x80, -1.0, 1.0)
+    e = (code >> 3) & 15
+    m = code & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    assert not np.any((code & 0x7F) == 0x7F), "NaN code"
+    return sign * mag
+
+
+def test_mx_quantiser_matches_the_oracle_bit_for_bit():
+    from mixture_experts_ffn_wave_amd import mx_quantize_rows
+    rng = np.random.default_rng(3)
+    R, K = 64, 512
+    mag = np.exp2(rng.integers(-40, 40, size=(R, K // 32, 1)))          # a magnitude per block
+    v = (rng.standard_normal((R, K // 32, 32)) * mag).reshape(R, K)
+    v[0, :32] = 0.0                                                       # all-zero block
+    v[1, :32] = 0.0; v[1, 5] = -3.0                                       # single value
+    v[2, :32] = 448.0; v[2, 7] = -448.0                                   # amax exactly 448
+    v[3, :32] = np.linspace(-1, 1, 32) * 1e-3                             # small values, subnormal codes
+    v[4, :32] = 1.0 + np.arange(32) / 8.0                                 # e4m3 grid points and ties
+    v[5, 32:64] = np.exp2(-np.arange(32, dtype=np.float64))               # a wide range in one block
+    x = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16)
+    xc = x.cuda()
+    pay = torch.empty(R, K, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(R, K // 32, dtype=torch.uint8, device="cuda")
+    mx_quantize_rows(xc, pay, sc)
+    torch.cuda.synchronize()
+    xv = x.to(torch.float64).numpy().reshape(R, K // 32, 32)
+    ex = O.mx_block_scale(np.abs(xv).max(axis=-1))
+    assert np.array_equal(sc.cpu().numpy().astype(np.int64) - 127, ex), "scale exponents"
+    ref = O.e4m3_round(xv / np.exp2(ex)[..., None]).reshape(R, K)
+    got = e4m3_value(pay.cpu().numpy())
+    assert np.array_equal(got, ref), f"payload differs at {np.argwhere(got != ref)[:5]}"
+
+
+SMALL_MX = [
+    W("t1200_d256_e8k2_i256_mx", T=1200, d=256, E=8, k=2, I=256, expert_dtype="mxfp8"),
+    W("t900_d256_e16k4_i384_s2x128_mx", T=900, d=256, E=16, k=4, I=384, n_shared=2, I_shared=128,
+      expert_dtype="mxfp8"),
+    W("t2049_d512_e4k2_i512_s1x256_mx", T=2049, d=512, E=4, k=2, I=512, n_shared=1, I_shared=256,
+      expert_dtype="mxfp8"),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL_MX, ids=[w.name for w in SMALL_MX])
+def test_mx_layer_matches_oracle(wl):
+    PT.full_parity(wl)
+
+
+@pytest.mark.timeout(900)
+def test_mx_workload_full_size():
+    PT.full_parity(MI.WORKLOADS["t16384_d2048_e64k6_i1408_s2x1408_mxfp8"], mx_diagnostic=False)
