@@ -252,7 +252,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.dtype,
+        # expert GEMMs in MX-fp8 (e4m3 payload, f32 accumulate), the rest in the layer dtype
+        "dtype": "mxfp8_e4m3+" + wl.dtype if wl.expert_dtype == "mxfp8" else wl.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "d_model": wl.d, "experts": wl.E, "top_k": wl.k,
                    "d_ff": wl.I, "shared": f"{wl.n_shared}x{wl.I_shared}", "renorm": wl.renorm,
