@@ -109,23 +109,30 @@ moe_status check_ws(moe_plan p, void* ws, size_t ws_bytes) {
 
 constexpr int kCUs = 256;
 
-// Tile override for tuning and tests: MOE_ROW_TILE / MOE_WGRAD_TILE = 128 or
-// 256, read once per plan; any other value, or a shape the tile does not
-// divide, keeps the default choice.
-int env_tile(const char* name) {
+// Tile override for tuning and tests: MOE_ROW_TILE = 128, 256 or 128x256,
+// MOE_WGRAD_TILE = 128 or 256, read once per plan; any other value, or a
+// shape the tile does not divide, keeps the default choice.
+int env_tile(const char* name, bool wide) {
   const char* v = std::getenv(name);
   if (!v) return 0;
+  if (wide && std::strcmp(v, "128x256") == 0) return TILE_128x256;
   const int t = std::atoi(v);
   return (t == 128 || t == 256) ? t : 0;
 }
 
-// Row GEMMs: 128 x 128 tiles by default (4 waves, two workgroups per CU);
-// 256 x 256 (8 waves, one workgroup per CU) where the shape allows.
-constexpr int kRowTile = 128;
-int choose_row_tile(int dt, int ncols, int block_align, int override_tile) {
-  if (dt == DT_F32) return 128;
-  if (ncols % 256 || block_align % 256) return 128;
-  return override_tile ? override_tile : kRowTile;
+// Row GEMMs: 128 x 256 tiles (4 waves, two workgroups per CU) where they
+// divide the shape and the GEMM has at least four rounds of them (2048
+// tiles): they move a quarter less operand data per FLOP than 128 x 128, but
+// a short grid of fewer, longer tiles ends unevenly, so smaller GEMMs keep
+// 128 x 128 (three workgroups per CU).  `tiles256` = the GEMM's 128 x 256
+// tile count (an upper bound for grouped GEMMs).  256 x 256 (8 waves, one
+// workgroup per CU) only on request.
+constexpr int64_t kWideTileMin = 2048;
+int choose_row_tile(int dt, int ncols, int block_align, int64_t tiles256, int override_tile) {
+  if (dt == DT_F32) return TILE_128;
+  if (ncols % 256 || block_align % 256) return TILE_128;
+  if (override_tile) return override_tile;
+  return tiles256 >= kWideTileMin ? TILE_128x256 : TILE_128;
 }
 // Weight-gradient GEMMs: 256 x 256 stages twice the FLOP per operand byte of
 // 128 x 128 but yields a quarter of the workgroups; estimated time = rounds of
@@ -261,13 +268,14 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
   {
     const double E = p->E, A = (double)A_, T = (double)c.T;
     const double rps = E > 0 ? A / E : 0;               // rows per expert if balanced
-    const int rt = env_tile("MOE_ROW_TILE"), wt = env_tile("MOE_WGRAD_TILE");
+    const int rt = env_tile("MOE_ROW_TILE", true), wt = env_tile("MOE_WGRAD_TILE", false);
     const int d = p->d, I = p->I, NI = p->Ns * p->Is;
     // gate/up: output columns are 2I packed, tile columns pair gate/up halves (needs I % (tile/2))
-    p->t_gu = choose_row_tile(p->dt, 2 * I, 2 * I, rt);
-    p->t_down = choose_row_tile(p->dt, d, 256, rt);
-    p->t_down_dgrad = choose_row_tile(p->dt, I, I, rt);
-    p->t_gu_dgrad = choose_row_tile(p->dt, d, 256, rt);
+    const int64_t mt = (A_ + (int64_t)p->E * 127) / 128, mts = (c.T + 127) / 128;   // row tiles (bounds)
+    p->t_gu = choose_row_tile(p->dt, 2 * I, 2 * I, mt * (I / 128), rt);
+    p->t_down = choose_row_tile(p->dt, d, 256, mt * (d / 256), rt);
+    p->t_down_dgrad = choose_row_tile(p->dt, I, I, mt * (I / 256), rt);
+    p->t_gu_dgrad = choose_row_tile(p->dt, d, 256, mt * (d / 256), rt);
     p->t_router_dx = 128;                                 // K = 2 Ep is tiny
     p->t_wg_down = choose_wgrad_tile(p->dt, E, d, I, rps, wt);
     p->t_wg_gu = choose_wgrad_tile(p->dt, E, 2 * I, d, rps, wt);
@@ -276,10 +284,10 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
     p->sp_wg_down = choose_wgrad_splits(p->t_wg_down, E, d, I, rps);
     p->sp_wg_gu = choose_wgrad_splits(p->t_wg_gu, E, 2 * I, d, rps);
     if (p->Ns > 0) {
-      p->t_gu_s = choose_row_tile(p->dt, 2 * NI, 2 * p->Is, rt);
-      p->t_down_s = choose_row_tile(p->dt, d, 256, rt);
-      p->t_down_dgrad_s = choose_row_tile(p->dt, NI, p->Is, rt);
-      p->t_gu_dgrad_s = choose_row_tile(p->dt, d, 256, rt);
+      p->t_gu_s = choose_row_tile(p->dt, 2 * NI, 2 * p->Is, mts * (NI / 128), rt);
+      p->t_down_s = choose_row_tile(p->dt, d, 256, mts * (d / 256), rt);
+      p->t_down_dgrad_s = choose_row_tile(p->dt, NI, p->Is, mts * (NI / 256), rt);
+      p->t_gu_dgrad_s = choose_row_tile(p->dt, d, 256, mts * (d / 256), rt);
       p->t_wg_down_s = (p->Is % 256 == 0) ? choose_wgrad_tile(p->dt, 1, d, NI, T, wt) : 128;
       p->t_wg_gu_s = choose_wgrad_tile(p->dt, 1, 2 * NI, d, T, wt);
       if (p->mx) p->t_gu_s = p->t_down_s = p->t_down_dgrad_s = p->t_gu_dgrad_s = p->t_wg_down_s = p->t_wg_gu_s = 128;

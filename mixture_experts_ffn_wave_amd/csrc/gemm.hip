@@ -62,6 +62,20 @@ __device__ __forceinline__ int xcd_logical(int hw, int R) {
   return l < R ? l : -1;
 }
 
+// Maps the hardware workgroup id onto a logical tile index in [0, R) in
+// chunks of C consecutive tiles dealt round-robin over the XCDs: XCD x gets
+// chunks x, x + 8, x + 16, ... in that order (the grid is a multiple of 8 C
+// workgroups).  For tiles of unequal work (weight gradients of experts with
+// skewed token counts) this spreads every expert over all XCDs, where the
+// contiguous mapping above would give the busiest experts to one XCD; a chunk
+// keeps tiles that share an operand slice together.  Returns -1 beyond the
+// work.  (A grid that is a multiple of 8 C also covers xcd_logical.)
+__device__ __forceinline__ int xcd_chunked(int hw, int R, int C) {
+  const int x = hw & 7, y = hw >> 3;
+  const int l = ((y / C) * 8 + x) * C + y % C;
+  return l < R ? l : -1;
+}
+
 // ------------------------------------------------------------ operand tile --
 // ROWS rows of the tile; TR: the source is k-major (rows contiguous along the
 // tile's row index, one source row per k).
@@ -359,22 +373,29 @@ __device__ __forceinline__ void dma16(rsrc_t rs, char* lds_lane0, uint32_t voff)
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_lane0, 16, voff, 0, 0, 0);
 }
 
-// Tile configurations of the direct-load path (BM = BN):
+// Tile configurations of the direct-load path (BM x BN output tiles):
 //   128 x 128: 4 waves (2 x 2), a ring of 64-byte k chunks: 3 stages (48 KB,
 //              three workgroups per CU) for the row GEMMs, 4 stages (64 KB,
 //              loads three chunks ahead, two workgroups per CU) for the weight
 //              gradients, whose workgroups run long K loops;
+//   128 x 256: row GEMMs only, 4 waves (2 x 2, 64 x 128 per wave), 3 stages of
+//              64-byte chunks (72 KB, two workgroups per CU): a quarter less
+//              operand traffic per FLOP than 128 x 128 and twice the MFMAs
+//              per wave between barriers;
 //   256 x 256: 8 waves (2 along rows x 4 along columns, 128 x 64 per wave), a
 //              2-stage ring of 128-byte k chunks (each row's chunk is one full
 //              cache line), 128 KB of LDS: one workgroup per CU.
-template <int BM, bool WGRAD> struct TileCfg;
+template <int BM, int BN, bool WGRAD> struct TileCfg;
 // WAVES_PER_EU: register budget of the row kernels (3 waves per SIMD for the
 // 3-workgroup 128 x 128 tiles: the compiler then keeps the accumulators in
 // VGPRs and stays within 168 registers).
-template <bool WGRAD> struct TileCfg<128, WGRAD> {
+template <bool WGRAD> struct TileCfg<128, 128, WGRAD> {
   static constexpr int WM = 2, WN = 2, DKB = 64, NSTG = WGRAD ? 4 : 3, THREADS = 256, WAVES_PER_EU = 3;
 };
-template <bool WGRAD> struct TileCfg<256, WGRAD> {
+template <> struct TileCfg<128, 256, false> {
+  static constexpr int WM = 2, WN = 2, DKB = 64, NSTG = 3, THREADS = 256, WAVES_PER_EU = 2;
+};
+template <bool WGRAD> struct TileCfg<256, 256, WGRAD> {
   static constexpr int WM = 2, WN = 4, DKB = 128, NSTG = 2, THREADS = 512, WAVES_PER_EU = 2;
 };
 
@@ -484,12 +505,12 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
   constexpr int MS = WTM / 32, NS = WTN / 32;
   constexpr int STAGE = PO::BYTES + QO::BYTES;
 
-  constexpr int DKB = MX ? MX_DKB : TileCfg<BM, false>::DKB;
-  constexpr int NSTG = MX ? 2 : TileCfg<BM, false>::NSTG;
+  constexpr int DKB = MX ? MX_DKB : TileCfg<BM, BN, false>::DKB;
+  constexpr int NSTG = MX ? 2 : TileCfg<BM, BN, false>::NSTG;
   constexpr int SC_OFF = NSTG * (BM + BN) * DKB;                // MX scale tiles follow the payload ring
   constexpr int SCAN_OFF = MX ? SC_OFF + NSTG * (BM + BN) * 4 : ((ES == 2) ? NSTG * (BM + BN) * DKB : 2 * STAGE);
   int* s_scan = reinterpret_cast<int*>(smem + SCAN_OFF);      // [NW] wave sums, [NW..NW+1] located tile
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int n_ntiles = a.N / TILE_N;
 
   // ---- which (segment, m-tile, n-tile) this workgroup computes
@@ -974,9 +995,36 @@ __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
   constexpr int MS = WTM / 32, NS = WTN / 32;
   constexpr int STAGE = PO::BYTES + QO::BYTES;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int n_mt = a.M / BM, n_nt = a.N / BN;
-  const int logical = xcd_logical(blockIdx.x, a.G * a.splits * n_mt * n_nt);
+  // Tile order.  Segments of similar length: each XCD takes a contiguous run
+  // of tiles (whole experts, so an expert's operand slices are read into one
+  // L2).  Skewed segments (the longest over twice the mean): chunks of the n
+  // tiles of one (expert, split, m tile), which share its P slice, dealt
+  // round-robin over the XCDs, so the busiest experts do not all land on one
+  // XCD.  Every wave derives the same choice from the offsets.
+  bool skewed = false;
+  if (a.offsets && a.G > 1) {
+    int mx = 0, tot = 0;
+    for (int gg = lane; gg < a.G; gg += 64) {
+      const int len = a.offsets[gg + 1] - a.offsets[gg];
+      mx = len > mx ? len : mx;
+      tot += len;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const int m2 = __shfl_xor(mx, o, 64);
+      mx = m2 > mx ? m2 : mx;
+      tot += __shfl_xor(tot, o, 64);
+    }
+    // every lane holds the totals: read them as scalars, so the tile indices
+    // (and the buffer descriptors built from them) stay wave-uniform values
+    mx = __builtin_amdgcn_readfirstlane(mx);
+    tot = __builtin_amdgcn_readfirstlane(tot);
+    skewed = (int64_t)mx * a.G > 2 * (int64_t)tot;
+  }
+  const int ntiles = a.G * a.splits * n_mt * n_nt;
+  const int logical = skewed ? xcd_chunked(blockIdx.x, ntiles, n_nt) : xcd_logical(blockIdx.x, ntiles);
   if (logical < 0) return;
   int rest = logical;
   const int nt = rest % n_nt; rest /= n_nt;
@@ -1056,7 +1104,7 @@ __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
       mfma_chunk_mx<NS, MS>(acc, buf + PD::BYTES, buf, sbuf + BM * 4, sbuf, qrow, prow, lane);
     }
   } else if constexpr (ES == 2) {
-    constexpr int DKB = TileCfg<BM, true>::DKB, NSTG = TileCfg<BM, true>::NSTG;
+    constexpr int DKB = TileCfg<BM, BN, true>::DKB, NSTG = TileCfg<BM, BN, true>::NSTG;
     using PD = DmaKmajor<BM, NW, DKB>;
     using QD = DmaKmajor<BN, NW, DKB>;
     constexpr int DSTAGE = PD::BYTES + QD::BYTES;
@@ -1151,7 +1199,7 @@ __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
 template <typename T, int BM, int BN, bool WGRAD>
 constexpr size_t smem_for() {
   if constexpr (sizeof(T) == 2) {
-    return (size_t)TileCfg<BM, WGRAD>::NSTG * (BM + BN) * TileCfg<BM, WGRAD>::DKB + 64;   // direct-load ring
+    return (size_t)TileCfg<BM, BN, WGRAD>::NSTG * (BM + BN) * TileCfg<BM, BN, WGRAD>::DKB + 64;   // direct-load ring
   } else {
     constexpr int nn = Operand<T, BM, false>::BYTES + Operand<T, BN, false>::BYTES;
     constexpr int nt = Operand<T, BM, false>::BYTES + Operand<T, BN, true>::BYTES;
@@ -1168,15 +1216,15 @@ constexpr size_t smem_for() {
 // One plainly named kernel per (operation, dtype, tile) so profiles read well.
 
 #define MOE_ROW_KERNEL(NAME, T, BM, BN, OP, EPI)                                                    \
-  extern "C" __global__ void __launch_bounds__((TileCfg<BM, false>::THREADS))                   \
-      __attribute__((amdgpu_waves_per_eu(TileCfg<BM, false>::WAVES_PER_EU))) NAME(RowGemmArgs a) {  \
+  extern "C" __global__ void __launch_bounds__((TileCfg<BM, BN, false>::THREADS))                   \
+      __attribute__((amdgpu_waves_per_eu(TileCfg<BM, BN, false>::WAVES_PER_EU))) NAME(RowGemmArgs a) {  \
     extern __shared__ __attribute__((aligned(16))) char smem[];                                   \
-    row_gemm_body<T, BM, BN, OP, EPI, TileCfg<BM, false>::WM, TileCfg<BM, false>::WN>(a, smem);    \
+    row_gemm_body<T, BM, BN, OP, EPI, TileCfg<BM, BN, false>::WM, TileCfg<BM, BN, false>::WN>(a, smem);    \
   }
 #define MOE_WGRAD_KERNEL(NAME, T, BM, BN, F32)                                                      \
-  extern "C" __global__ void __launch_bounds__((TileCfg<BM, true>::THREADS)) NAME(WgradArgs a) {    \
+  extern "C" __global__ void __launch_bounds__((TileCfg<BM, BN, true>::THREADS)) NAME(WgradArgs a) {    \
     extern __shared__ __attribute__((aligned(16))) char smem[];                                   \
-    wgrad_body<T, BM, BN, F32, TileCfg<BM, true>::WM, TileCfg<BM, true>::WN>(a, smem);             \
+    wgrad_body<T, BM, BN, F32, TileCfg<BM, BN, true>::WM, TileCfg<BM, BN, true>::WN>(a, smem);             \
   }
 
 #define MOE_KERNEL_SET(T, TN, BM, BN)                                                                      \
@@ -1192,10 +1240,20 @@ constexpr size_t smem_for() {
   MOE_WGRAD_KERNEL(moe_wgrad_gate_up_f32out_##TN##_##BM##x##BN, T, BM, BN, 1)                              \
   MOE_WGRAD_KERNEL(moe_wgrad_router_f32out_##TN##_##BM##x##BN, T, BM, BN, 1)
 
+#define MOE_ROW_KERNEL_SET(T, TN, BM, BN)                                                                  \
+  MOE_ROW_KERNEL(moe_gemm_gate_up_swiglu_##TN##_##BM##x##BN, T, BM, BN, OP_GU_FWD, EPI_SWIGLU_FWD)         \
+  MOE_ROW_KERNEL(moe_gemm_down_##TN##_##BM##x##BN, T, BM, BN, OP_DOWN_FWD, EPI_STORE)                      \
+  MOE_ROW_KERNEL(moe_gemm_down_f32out_##TN##_##BM##x##BN, T, BM, BN, OP_DOWN_FWD, EPI_STORE_F32)           \
+  MOE_ROW_KERNEL(moe_gemm_down_dgrad_swiglu_##TN##_##BM##x##BN, T, BM, BN, OP_DOWN_DGRAD, EPI_SWIGLU_BWD)  \
+  MOE_ROW_KERNEL(moe_gemm_gate_up_dgrad_##TN##_##BM##x##BN, T, BM, BN, OP_GU_DGRAD, EPI_STORE)             \
+  MOE_ROW_KERNEL(moe_gemm_router_dx_f32out_##TN##_##BM##x##BN, T, BM, BN, OP_ROUTER_DX, EPI_STORE_F32)
+
 MOE_KERNEL_SET(__bf16, bf16, 256, 256)
 MOE_KERNEL_SET(__bf16, bf16, 128, 128)
+MOE_ROW_KERNEL_SET(__bf16, bf16, 128, 256)
 MOE_KERNEL_SET(_Float16, f16, 256, 256)
 MOE_KERNEL_SET(_Float16, f16, 128, 128)
+MOE_ROW_KERNEL_SET(_Float16, f16, 128, 256)
 MOE_KERNEL_SET(float, f32, 128, 128)
 
 // MX-fp8 expert GEMMs (128 x 128 tiles, 4 waves, 2-stage ring of 128-byte chunks)
@@ -1239,14 +1297,22 @@ struct KernelSet {
             moe_wgrad_router_f32out_##TN##_##BM##x##BN, smem_for<T, BM, BN, false>(),                  \
             smem_for<T, BM, BN, true>()}
 
+#define MOE_ROW_TABLE(T, TN, BM, BN)                                                                    \
+  KernelSet{moe_gemm_gate_up_swiglu_##TN##_##BM##x##BN, moe_gemm_down_##TN##_##BM##x##BN,               \
+            moe_gemm_down_f32out_##TN##_##BM##x##BN, moe_gemm_down_dgrad_swiglu_##TN##_##BM##x##BN,     \
+            moe_gemm_gate_up_dgrad_##TN##_##BM##x##BN, moe_gemm_router_dx_f32out_##TN##_##BM##x##BN,       \
+            nullptr, nullptr, nullptr, nullptr, nullptr, smem_for<T, BM, BN, false>(), 0}
+
 const KernelSet* kernel_set(int dt, int tile) {
   static const KernelSet bf16_256 = MOE_KERNEL_TABLE(__bf16, bf16, 256, 256);
   static const KernelSet bf16_128 = MOE_KERNEL_TABLE(__bf16, bf16, 128, 128);
+  static const KernelSet bf16_128x256 = MOE_ROW_TABLE(__bf16, bf16, 128, 256);
   static const KernelSet f16_256 = MOE_KERNEL_TABLE(_Float16, f16, 256, 256);
   static const KernelSet f16_128 = MOE_KERNEL_TABLE(_Float16, f16, 128, 128);
+  static const KernelSet f16_128x256 = MOE_ROW_TABLE(_Float16, f16, 128, 256);
   static const KernelSet f32_128 = MOE_KERNEL_TABLE(float, f32, 128, 128);
-  if (dt == DT_BF16) return tile == 256 ? &bf16_256 : &bf16_128;
-  if (dt == DT_F16) return tile == 256 ? &f16_256 : &f16_128;
+  if (dt == DT_BF16) return tile == TILE_256 ? &bf16_256 : (tile == TILE_128x256 ? &bf16_128x256 : &bf16_128);
+  if (dt == DT_F16) return tile == TILE_256 ? &f16_256 : (tile == TILE_128x256 ? &f16_128x256 : &f16_128);
   if (dt == DT_F32 && tile == 128) return &f32_128;
   if (dt == DT_MXFP8 && tile == 128) {
     constexpr size_t mx_lds = 2 * (128 + 128) * MX_DKB + 2 * (128 + 128) * 4 + 64;
@@ -1289,19 +1355,21 @@ hipError_t launch_row_gemm(int dt, int op, int epi, int tile, const RowGemmArgs&
   if (!k) return hipErrorInvalidValue;
   if (dt == DT_MXFP8 && (a.ldp % 128 || a.ldq % 128 || a.q_group_stride % 32 || !a.Ps || !a.Qs))
     return hipErrorInvalidValue;
-  const int tile_n = (op == OP_GU_FWD) ? tile / 2 : tile;
+  if (dt == DT_F32 && tile != TILE_128) return hipErrorInvalidValue;
+  const int bm = tile_rows(tile), bn = tile_cols(tile);
+  const int tile_n = (op == OP_GU_FWD) ? bn / 2 : bn;
   if (a.N % tile_n || a.K % (KB / dtype_bytes(dt))) return hipErrorInvalidValue;
   const int64_t n_ntiles = a.N / tile_n;
   int64_t mtiles;
-  if (a.offsets) mtiles = (a.M + (int64_t)a.G * (tile - 1)) / tile;   // >= sum_g ceil(len_g / tile)
-  else mtiles = (a.M + tile - 1) / tile;
+  if (a.offsets) mtiles = (a.M + (int64_t)a.G * (bm - 1)) / bm;   // >= sum_g ceil(len_g / bm)
+  else mtiles = (a.M + bm - 1) / bm;
   int64_t grid = mtiles * n_ntiles;
   grid = (grid + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipError_t e = prepare((const void*)k, set->lds_row);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(tile == 256 ? 512 : 256),
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(tile == TILE_256 ? 512 : 256),
                      set->lds_row, s, a);
   return hipGetLastError();
 }
@@ -1316,11 +1384,12 @@ hipError_t launch_wgrad(int dt, int op, int tile, const WgradArgs& a, hipStream_
     case WG_ROUTER: k = set->wgrad_router_f32; break;
     default: return hipErrorInvalidValue;
   }
-  if (!k || (op == WG_ROUTER && !a.out_f32)) return hipErrorInvalidValue;
+  if (!k || (op == WG_ROUTER && !a.out_f32) || (tile != TILE_128 && tile != TILE_256)) return hipErrorInvalidValue;
   if (dt == DT_MXFP8 && (a.ldp % 128 || a.ldq % 128 || !a.offsets || !a.Ps || !a.Qs)) return hipErrorInvalidValue;
   if (a.M % tile || a.N % tile) return hipErrorInvalidValue;
+  const int64_t chunk8 = 8 * (int64_t)(a.N / tile);   // whole rounds of XCD chunks (xcd_chunked)
   int64_t grid = (int64_t)a.G * a.splits * (a.M / tile) * (a.N / tile);
-  grid = (grid + 7) / 8 * 8;
+  grid = (grid + chunk8 - 1) / chunk8 * chunk8;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipError_t e = prepare((const void*)k, set->lds_wgrad);

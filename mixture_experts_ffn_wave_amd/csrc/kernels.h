@@ -67,7 +67,12 @@ struct RowGemmArgs {
   // Q ([rows][K/32], row stride ldq/32, group stride q_group_stride/32)
   const uint8_t* Ps; const uint8_t* Qs;
 };
-// tile: 256 (16-bit types only) or 128; the plan chooses it once per GEMM.
+// Output tile shapes (rows x columns): TILE_128 = 128 x 128 (every dtype),
+// TILE_256 = 256 x 256 and TILE_128x256 = 128 x 256 (16-bit types; the latter
+// for the row GEMMs only).  The plan chooses one per GEMM.
+enum TileShape { TILE_128 = 128, TILE_256 = 256, TILE_128x256 = 384 };
+inline int tile_rows(int t) { return t == TILE_256 ? 256 : 128; }
+inline int tile_cols(int t) { return t == TILE_128 ? 128 : 256; }
 hipError_t launch_row_gemm(int dt, int op, int epi, int tile, const RowGemmArgs& a, hipStream_t s);
 
 // Weight-gradient GEMM: out[m][n] = sum over the segment's tokens t of P[t][m] * Q[t][n].

@@ -30,83 +30,73 @@ __device__ __forceinline__ int mx_scale_exp(float amax) {
   return x < -127 ? -127 : (x > 127 ? 127 : x);
 }
 
-// e4m3 bits of q (|q| <= 448, so no saturation is needed)
-__device__ __forceinline__ uint32_t e4m3_bits(float q) {
-  const uint32_t sign = (__float_as_uint(q) >> 24) & 0x80u;
-  const float a = fabsf(q);
-  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);   // k 2^-9; k = 8 is 2^-6 (0x08)
-  int e;
-  frexpf(a, &e);                              // a in [2^(e-1), 2^e)
-  float mq = rintf(ldexpf(a, 4 - e));         // 3 mantissa bits: a / 2^(e-4) in [8, 16]
-  int E = e - 1;
-  if (mq >= 16.0f) { mq = 8.0f; ++E; }
-  return sign | (uint32_t)((E + 7) << 3) | ((uint32_t)mq - 8u);
+// Four scaled values (|v| * 2^-x <= 448, so nothing saturates) to four e4m3
+// bytes, lowest first, with the hardware conversion (round to nearest even,
+// e4m3 subnormals).  Scaling by 2^-x is exact: for a 16-bit input x <= 120,
+// so 2^-x is a normal f32.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d, float s) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a * s, b * s, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c * s, d * s, w, true);
+  return (uint32_t)w;
 }
 
-// quantise 32 values: 32 payload bytes + the scale byte
-__device__ __forceinline__ uint8_t mx_block(const float (&v)[32], u32x4 (&out)[2]) {
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  const int x = mx_scale_exp(amax);
-#pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) word |= e4m3_bits(ldexpf(v[4 * w + b], -x)) << (8 * b);
-    out[w >> 2][w & 3] = word;
-  }
-  return (uint8_t)(x + 127);
-}
-
+// Row operands: four lanes per 32-value block, eight values (one 16-byte
+// load) per lane, so a wave reads 1 KB and writes 512 bytes contiguously.
 template <typename T>
 __global__ void __launch_bounds__(NT) mx_quant_rows_kernel(MxRowsArgs a) {
-  const int kb_per_row = a.K / 32;
-  const int64_t nb = a.R * kb_per_row;
+  static_assert(sizeof(T) == 2, "16-bit inputs");
+  const int kq = a.K / 8;                                   // 8-value pieces per row
+  const int64_t nq = a.R * kq;                              // a multiple of 4: quads stay whole
   const T* in = static_cast<const T*>(a.in);
-  for (int64_t b = (int64_t)blockIdx.x * NT + threadIdx.x; b < nb; b += (int64_t)gridDim.x * NT) {
-    const int64_t r = b / kb_per_row;
-    const int kb = (int)(b - r * kb_per_row), k0 = kb * 32;
+  const int lane = threadIdx.x & 63;
+  for (int64_t q = (int64_t)blockIdx.x * NT + threadIdx.x; q < nq; q += (int64_t)gridDim.x * NT) {
+    const int64_t r = q / kq;
+    const int k0 = (int)(q - r * kq) * 8;
     const T* src = in + (int64_t)(k0 / a.sub) * a.block_stride + r * a.ld_in + (k0 % a.sub);
-    float v[32];
+    float v[8];
+    unpack8<T>(ld16(src), v);
+    float amax = 0.0f;
 #pragma unroll
-    for (int c = 0; c < 32 * (int)sizeof(T) / 16; ++c) {
-      Chunk<T> ch;
-      ch.raw = ld16(src + c * Chunk<T>::N);
-#pragma unroll
-      for (int i = 0; i < Chunk<T>::N; ++i) v[c * Chunk<T>::N + i] = to_f32<T>(ch.e[i]);
-    }
-    u32x4 o[2];
-    const uint8_t sc = mx_block(v, o);
-    uint8_t* dst = a.out + r * a.K + k0;
-    st16(dst, o[0]);
-    st16(dst + 16, o[1]);
-    a.scales[r * kb_per_row + kb] = sc;
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    const int x = mx_scale_exp(amax);
+    const float sc = ldexpf(1.0f, -x);
+    const u32x2 o = {e4m3x4(v[0], v[1], v[2], v[3], sc), e4m3x4(v[4], v[5], v[6], v[7], sc)};
+    st8(a.out + r * a.K + k0, o);
+    if ((lane & 3) == 0) a.scales[r * (a.K / 32) + k0 / 32] = (uint8_t)(x + 127);
   }
 }
 
-// grid: x = padded 32-block, y = column tile of NT columns
+// Transposing quantiser.  One workgroup per 128 padded K positions x 64
+// columns: wave j quantises the 32-token block j of the tile for its lane's
+// column, so the four 32-byte pieces of each output row's 128-byte span are
+// written by one workgroup.  Tiles never straddle a segment: segment starts
+// (pad) and seg_len are multiples of 128.
+constexpr int kColsTileK = 128, kColsTileC = 64;
+
 template <typename T>
 __global__ void __launch_bounds__(NT) mx_quant_cols_kernel(MxColsArgs a) {
-  const int64_t p = (int64_t)blockIdx.x * 32;           // padded K position of this block
+  const int64_t p0 = (int64_t)blockIdx.x * kColsTileK;     // padded K position of this tile
   int g;
   int64_t pstart;
   if (a.pad) {
-    if (p >= a.pad[a.G]) return;
-    int lo = 0, hi = a.G - 1;                             // last g with pad[g] <= p
+    if (p0 >= a.pad[a.G]) return;
+    int lo = 0, hi = a.G - 1;                               // last g with pad[g] <= p0
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (a.pad[mid] <= p) lo = mid; else hi = mid - 1;
+      if (a.pad[mid] <= p0) lo = mid; else hi = mid - 1;
     }
     g = lo;
     pstart = a.pad[g];
   } else {
-    g = (int)(p / a.seg_len);
+    g = (int)(p0 / a.seg_len);
     if (g >= a.G) return;
     pstart = (int64_t)g * a.seg_len;
   }
-  const int c = blockIdx.y * NT + threadIdx.x;
+  const int c = blockIdx.y * kColsTileC + (threadIdx.x & 63);
   if (c >= a.C) return;
+  const int64_t p = p0 + 32 * (threadIdx.x >> 6);
   const int64_t tstart = a.seg ? a.seg[g] : (int64_t)g * a.seg_len;
   const int64_t n = a.seg ? (int64_t)(a.seg[g + 1] - a.seg[g]) : a.seg_len;
   const int64_t t0 = p - pstart;
@@ -114,13 +104,19 @@ __global__ void __launch_bounds__(NT) mx_quant_cols_kernel(MxColsArgs a) {
   float v[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) v[i] = (t0 + i < n) ? to_f32<T>(in[(t0 + i) * a.ld_in]) : 0.0f;
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int x = mx_scale_exp(amax);
+  const float sc = ldexpf(1.0f, -x);
   u32x4 o[2];
-  const uint8_t sc = mx_block(v, o);
+#pragma unroll
+  for (int w = 0; w < 8; ++w) o[w >> 2][w & 3] = e4m3x4(v[4 * w], v[4 * w + 1], v[4 * w + 2], v[4 * w + 3], sc);
   const int64_t row = a.row0 + c, k = a.k0 + p;
   uint8_t* dst = a.out + row * a.Kpad + k;
   st16(dst, o[0]);
   st16(dst + 16, o[1]);
-  a.scales[row * (a.Kpad / 32) + k / 32] = sc;
+  a.scales[row * (a.Kpad / 32) + k / 32] = (uint8_t)(x + 127);
 }
 
 __global__ void mx_pad_offsets_kernel(const int32_t* offsets, int32_t* pad, int G, int align) {
@@ -151,9 +147,9 @@ hipError_t launch_mx_single_segment(int32_t* seg_pad, int64_t T, int align, hipS
 
 hipError_t launch_mx_quant_rows(int dt, const MxRowsArgs& a, hipStream_t s) {
   if (a.K % 32 || a.sub % 32 || a.sub <= 0) return hipErrorInvalidValue;
-  const int64_t nb = a.R * (a.K / 32);
-  if (nb == 0) return hipSuccess;
-  int64_t grid = (nb + NT - 1) / NT;
+  const int64_t nq = a.R * (a.K / 8);
+  if (nq == 0) return hipSuccess;
+  int64_t grid = (nq + NT - 1) / NT;
   if (grid > 65536) grid = 65536;
   switch (dt) {
     case DT_BF16: hipLaunchKernelGGL(mx_quant_rows_kernel<__bf16>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
@@ -164,11 +160,12 @@ hipError_t launch_mx_quant_rows(int dt, const MxRowsArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_mx_quant_cols(int dt, const MxColsArgs& a, hipStream_t s) {
-  if (a.Kpad % 128 || a.k0 % 32 || a.C <= 0) return hipErrorInvalidValue;
-  if (!a.pad && (a.seg_len % 32)) return hipErrorInvalidValue;
+  if (a.Kpad % kColsTileK || a.k0 % kColsTileK || a.C <= 0) return hipErrorInvalidValue;
+  if (!a.pad && (a.seg_len % kColsTileK)) return hipErrorInvalidValue;
   if (a.nblk <= 0) return hipSuccess;
-  if (a.nblk > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)a.nblk, (unsigned)((a.C + NT - 1) / NT));
+  const int64_t tiles = (a.nblk * 32 + kColsTileK - 1) / kColsTileK;
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)tiles, (unsigned)((a.C + kColsTileC - 1) / kColsTileC));
   switch (dt) {
     case DT_BF16: hipLaunchKernelGGL(mx_quant_cols_kernel<__bf16>, grid, dim3(NT), 0, s, a); break;
     case DT_F16: hipLaunchKernelGGL(mx_quant_cols_kernel<_Float16>, grid, dim3(NT), 0, s, a); break;

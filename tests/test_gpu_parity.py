@@ -42,19 +42,20 @@ def test_small_workloads_match_oracle(wl):
     PT.full_parity(wl)
 
 
-# Both GEMM tile engines (128 x 128 with 4 waves, 256 x 256 with 8 waves) on
-# shapes that both divide, with ragged row tails and several tiles per expert.
+# Every GEMM tile engine (128 x 128 with 4 waves, 128 x 256 with 4 waves for
+# the row GEMMs, 256 x 256 with 8 waves) on shapes that all divide, with
+# ragged row tails and several tiles per expert.
 TILED = [
     W("t3000_d512_e8k2_i512_bf16_shared1", T=3000, d=512, E=8, k=2, I=512, n_shared=1, I_shared=256),
     W("t2500_d256_e4k2_i768_f16", T=2500, d=256, E=4, k=2, I=768, dtype="f16"),
 ]
 
 
-@pytest.mark.parametrize("tile", [128, 256])
+@pytest.mark.parametrize("tile", ["128", "256", "128x256"])
 @pytest.mark.parametrize("wl", TILED, ids=[w.name for w in TILED])
 def test_tile_engines_match_oracle(wl, tile, monkeypatch):
-    monkeypatch.setenv("MOE_ROW_TILE", str(tile))
-    monkeypatch.setenv("MOE_WGRAD_TILE", str(tile))
+    monkeypatch.setenv("MOE_ROW_TILE", tile)
+    monkeypatch.setenv("MOE_WGRAD_TILE", tile if tile != "128x256" else "128")
     PT.full_parity(wl)
 
 
