@@ -28,7 +28,7 @@ const char* kKernelNames =
     "gemm_down_dgrad_swiglu,gemm_wgrad_down,gemm_gate_up_dgrad,gemm_wgrad_gate_up,"
     "gemm_down_dgrad_swiglu_shared,gemm_wgrad_down_shared,gemm_wgrad_gate_up_shared,"
     "gemm_gate_up_dgrad_shared,stack_router,gemm_router_dx,unpermute,gemm_wgrad_router,router_reduce,aux,"
-    "wgrad_reduce,mx_quantize";
+    "wgrad_reduce,mx_quantize,router_bwd_small";
 
 }  // namespace
 
@@ -47,6 +47,8 @@ struct moe_plan_s {
   size_t o_block_counts, o_block_base, o_dy_perm, o_g, o_dzhl, o_w2, o_dgu, o_dx_perm, o_dgu_s,
       o_dxs, o_dxr, o_dwr_part, o_dbias_part, o_aux_part, o_wg_part, ws_total;
   bool router_dx_gemm;     // many experts: the router part of dx goes through the matrix cores
+  bool router_small;       // few experts: dz, dW_r and dbias partials in one kernel (no dz^T x GEMM)
+  int nblk_small;          // its token blocks
   // MX-fp8 experts: every expert GEMM operand is quantised into the workspace
   // (payload at .pay, scale bytes at .sc) right before the GEMM that reads it
   bool mx = false;
@@ -265,6 +267,8 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
     p->router_splits = s;
   }
   p->router_dx_gemm = p->E > kRouterDxVectorMaxE;
+  p->router_small = p->E <= kRouterSmallMaxE && p->d <= kRouterSmallMaxD;
+  p->nblk_small = router_small_blocks(c.T);
   {
     const double E = p->E, A = (double)A_, T = (double)c.T;
     const double rps = E > 0 ? A / E : 0;               // rows per expert if balanced
@@ -316,8 +320,9 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
   p->o_dgu_s = take((size_t)p->T * 2 * p->Ns * p->Is * es);
   p->o_dxs = take(p->Ns > 0 ? (size_t)p->T * p->d * es : 0);
   p->o_dxr = take(p->router_dx_gemm ? (size_t)p->T * p->d * 4 : 0);
-  p->o_dwr_part = take((size_t)p->router_splits * 2 * p->Ep * p->d * 4);
-  p->o_dbias_part = take((size_t)p->nblk_dz * p->E * 4);
+  p->o_dwr_part = take(p->router_small ? (size_t)p->nblk_small * p->E * p->d * 4
+                                        : (size_t)p->router_splits * 2 * p->Ep * p->d * 4);
+  p->o_dbias_part = take((size_t)(p->router_small ? p->nblk_small : p->nblk_dz) * p->E * 4);
   p->o_aux_part = take((size_t)(p->nblk_aux > 0 ? p->nblk_aux : 1) * 2 * p->E * 4);
   {
     // one f32 partial buffer, reused by every split weight-gradient GEMM in turn
@@ -758,7 +763,12 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
       Probe pr(p, "combine_bwd", s);
       MOE_TRY(launch_combine_bwd(p->dt, a, s));
     }
-    {
+    if (p->router_small) {
+      RouterBwdSmallArgs a{g, sv->topk_w, sv->topk_idx, sv->probs, sv->counts, sv->x, dzhl, dwr_part, dbias_part,
+                           p->T, E, Ep, d, k, p->cfg.renorm, p->cfg.aux_coef};
+      Probe pr(p, "router_bwd_small", s);
+      MOE_TRY(launch_router_bwd_small(p->dt, a, s));
+    } else {
       RouterDzArgs a{g, sv->topk_w, sv->topk_idx, sv->probs, sv->counts, dzhl, dbias_part,
                      p->T, E, Ep, k, p->cfg.renorm, p->cfg.aux_coef};
       Probe pr(p, "router_dz", s);
@@ -854,7 +864,7 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
     Probe pr(p, "unpermute", s);
     MOE_TRY(launch_unpermute(p->dt, a, s));
   }
-  {
+  if (!p->router_small) {
     WgradArgs a{};
     a.P = dzhl; a.ldp = 2 * Ep; a.Q = sv->x; a.ldq = d;
     a.offsets = nullptr; a.G = 1; a.Mtok = p->T; a.M = 2 * Ep; a.N = d; a.splits = p->router_splits;
@@ -863,8 +873,11 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
     MOE_TRY(launch_wgrad(p->dt, WG_ROUTER, p->t_wg_router, a, s));
   }
   {
-    RouterReduceArgs a{dwr_part, p->router_splits, E, Ep, d, gr->dw_router,
-                       dbias_part, p->T > 0 ? p->nblk_dz : 0, gr->dbias};
+    const int nsm = p->T > 0 ? p->nblk_small : 0;
+    RouterReduceArgs a = p->router_small
+        ? RouterReduceArgs{dwr_part, nsm, E, E, -1, d, gr->dw_router, dbias_part, nsm, gr->dbias}
+        : RouterReduceArgs{dwr_part, p->router_splits, E, 2 * Ep, Ep, d, gr->dw_router,
+                           dbias_part, p->T > 0 ? p->nblk_dz : 0, gr->dbias};
     Probe pr(p, "router_reduce", s);
     MOE_TRY(launch_router_reduce(p->dt, a, s));
   }

@@ -201,6 +201,152 @@ __global__ void __launch_bounds__(NT) router_dz_kernel(RouterDzArgs a) {
     a.dbias_part[(int64_t)blockIdx.x * a.E + tid] = ((s_bias[0][tid] + s_bias[1][tid]) + s_bias[2][tid]) + s_bias[3][tid];
 }
 
+// Router backward for few experts, one block of kRouterSmallTokens tokens per
+// workgroup: the dz of router_dz_kernel (one thread per token), then the
+// block's partial dW_r[e][c] = sum_t dz[t][e] x[t][c] in f32 (threads over
+// 8-column pieces of x, in G token groups whose sums are added in group order
+// through LDS) and its partial dbias.  Reading x here replaces the matrix-core
+// product dz^T x and its padded [2 Ep, d] f32 partials.
+template <typename T, int EM>
+__global__ void __launch_bounds__(NT) router_bwd_small_kernel(RouterBwdSmallArgs a) {
+  constexpr int TB = kRouterSmallTokens;
+  __shared__ float s_dz[TB][EM];
+  extern __shared__ float s_red[];                // [E][d] when G > 1
+  const int tid = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * TB;
+  const int E = a.E;
+  // ---- dz, one thread per token
+  if (tid < TB) {
+    const int64_t t = t0 + tid;
+    float dzv[EM];
+#pragma unroll
+    for (int e = 0; e < EM; ++e) dzv[e] = 0.0f;
+    if (t < a.T) {
+      float p[EM], dp[EM];
+      const float aux_scale = a.aux_coef * (float)E / ((float)a.T * (float)a.T * (float)a.k);
+#pragma unroll
+      for (int e = 0; e < EM; ++e) {
+        p[e] = (e < E) ? a.probs[t * E + e] : 0.0f;
+        dp[e] = (e < E) ? aux_scale * (float)a.counts[e] : 0.0f;
+      }
+      // slot gradients; with renormalisation w = p_sel / S
+      float S = 0.0f, wg = 0.0f;
+      for (int j = 0; j < a.k; ++j) {
+        const int ej = a.idx[t * a.k + j];
+        float pj = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EM; ++e) pj = (e == ej) ? p[e] : pj;
+        S += pj;
+        wg = fmaf(a.wts[t * a.k + j], a.g[t * a.k + j], wg);
+      }
+      for (int j = 0; j < a.k; ++j) {
+        const int ej = a.idx[t * a.k + j];
+        const float gj = a.g[t * a.k + j];
+        const float dps = a.renorm ? (gj - wg) / S : gj;
+#pragma unroll
+        for (int e = 0; e < EM; ++e) dp[e] += (e == ej) ? dps : 0.0f;
+      }
+      float dot = 0.0f;
+#pragma unroll
+      for (int e = 0; e < EM; ++e) dot = fmaf(p[e], dp[e], dot);
+      T* dz = static_cast<T*>(a.dz_hl) + t * 2 * (int64_t)a.Ep;
+#pragma unroll
+      for (int e = 0; e < EM; ++e) {
+        if (e < E) {
+          const float v = p[e] * (dp[e] - dot);
+          dzv[e] = v;
+          const T hi = from_f32<T>(v);
+          dz[e] = hi;
+          dz[a.Ep + e] = from_f32<T>(v - to_f32<T>(hi));
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EM; ++e) s_dz[tid][e] = dzv[e];
+  }
+  __syncthreads();
+  // ---- partial dbias: column sums over the block's tokens, in token order
+  if (tid < E) {
+    float sacc = 0.0f;
+    for (int i = 0; i < TB; ++i) sacc += s_dz[i][tid];
+    a.dbias_part[(int64_t)blockIdx.x * E + tid] = sacc;
+  }
+  // ---- partial dW_r
+  const int nch = a.d / 8;                        // 8-column pieces of a row (<= NT)
+  const int G = NT / nch;                         // token groups
+  const int c = tid % nch, grp = tid / nch;
+  float acc[EM][8];
+#pragma unroll
+  for (int e = 0; e < EM; ++e)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[e][i] = 0.0f;
+  if (grp < G) {
+    // tokens grp, grp + G, ... in batches of 8 whose loads are all issued
+    // before any is used (rows past T read as zero, and their dz is zero)
+    constexpr int NB = 8, VPR = 8 * sizeof(T) / 16;       // 16-byte vectors per 8 values
+    const T* xb = static_cast<const T*>(a.x) + (int64_t)c * 8;
+    for (int i0 = grp; i0 < TB; i0 += NB * G) {
+      u32x4 raw[NB][VPR];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int i = i0 + u * G;
+        const bool ok = i < TB && t0 + i < a.T;
+#pragma unroll
+        for (int v = 0; v < VPR; ++v)
+          raw[u][v] = ok ? ld16(xb + (t0 + i) * a.d + v * (16 / sizeof(T))) : (u32x4){0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int i = i0 + u * G;
+        if (i >= TB) break;
+        float xv[8];
+        if constexpr (sizeof(T) == 2) {
+          unpack8<T>(raw[u][0], xv);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) xv[q] = __uint_as_float(raw[u][q >> 2][q & 3]);
+        }
+#pragma unroll
+        for (int e = 0; e < EM; ++e) {
+          const float z = s_dz[i][e];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[e][q] = fmaf(z, xv[q], acc[e][q]);
+        }
+      }
+    }
+  }
+  // groups added in order: group 0 stores, groups 1.. G-1 add in turn
+  for (int gi = 0; gi < G; ++gi) {
+    if (G > 1) __syncthreads();
+    if (grp == gi) {
+#pragma unroll
+      for (int e = 0; e < EM; ++e) {
+        if (e < E) {
+          float* r = s_red + (int64_t)e * a.d + c * 8;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) r[q] = (gi == 0 ? 0.0f : r[q]) + acc[e][q];
+        }
+      }
+    }
+  }
+  if (G > 1) __syncthreads();
+  float* out = a.dw_part + (int64_t)blockIdx.x * E * a.d;
+  if (G > 1) {
+    for (int i = tid; i < E * nch; i += NT) {
+      const float* r = s_red + (int64_t)i * 8;
+      store4<float>(out + (int64_t)i * 8, r[0], r[1], r[2], r[3]);
+      store4<float>(out + (int64_t)i * 8 + 4, r[4], r[5], r[6], r[7]);
+    }
+  } else if (grp == 0) {
+#pragma unroll
+    for (int e = 0; e < EM; ++e)
+      if (e < E) {
+        store4<float>(out + (int64_t)e * a.d + c * 8, acc[e][0], acc[e][1], acc[e][2], acc[e][3]);
+        store4<float>(out + (int64_t)e * a.d + c * 8 + 4, acc[e][4], acc[e][5], acc[e][6], acc[e][7]);
+      }
+  }
+}
+
 // w2 rows [0, E) and [Ep, Ep + E) = W_r, every other row zero.
 template <typename T>
 __global__ void __launch_bounds__(NT) stack2_kernel(Stack2Args a) {
@@ -215,7 +361,7 @@ __global__ void __launch_bounds__(NT) stack2_kernel(Stack2Args a) {
 }
 
 // Blocks [0, nbw): block b reduces columns 64 (b % (d/64)) .. +63 of row
-// e = b / (d/64): dW_r[e][n] = sum_s part[s][e][n] + sum_s part[s][Ep + e][n].
+// e = b / (d/64): dW_r[e][n] = sum_s part[s][e][n] (+ sum_s part[s][lo_row + e][n]).
 // Its 16 waves each sum every 16th split (hi and lo apart), then the wave
 // partials are added in index order.  Blocks [nbw, nbw + E): dbias[e] = sum
 // over router_dz blocks of their partial.
@@ -242,14 +388,19 @@ __global__ void __launch_bounds__(kReduceThreads) router_reduce_kernel(RouterRed
   const int groups = a.d / 64;
   const int e = blockIdx.x / groups;
   const int col = (blockIdx.x - e * groups) * 64 + lane;
-  const int64_t sstride = 2 * (int64_t)a.Ep * a.d;
+  const int64_t sstride = (int64_t)a.rows * a.d;
   const float* ph = a.part + (int64_t)e * a.d + col;
-  const float* pl = a.part + (int64_t)(a.Ep + e) * a.d + col;
+  const float* pl = a.part + (int64_t)(a.lo_row + e) * a.d + col;
   float hi = 0.0f, lo = 0.0f;
+  if (a.lo_row >= 0) {
 #pragma unroll 4
-  for (int s = wave; s < a.splits; s += NWV) {
-    hi += ph[s * sstride];
-    lo += pl[s * sstride];
+    for (int s = wave; s < a.splits; s += NWV) {
+      hi += ph[s * sstride];
+      lo += pl[s * sstride];
+    }
+  } else {
+#pragma unroll 4
+    for (int s = wave; s < a.splits; s += NWV) hi += ph[s * sstride];
   }
   sh[0][wave][lane] = hi;
   sh[1][wave][lane] = lo;
@@ -531,6 +682,31 @@ hipError_t launch_router_dz(int dt, const RouterDzArgs& a, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+int router_small_blocks(int64_t T) {
+  const int64_t g = (T + kRouterSmallTokens - 1) / kRouterSmallTokens;
+  return (int)(g < 1 ? 1 : g);
+}
+
+template <typename T>
+hipError_t launch_router_bwd_small_t(const RouterBwdSmallArgs& a, hipStream_t s) {
+  const int grid = router_small_blocks(a.T);
+  const int nch = a.d / 8, G = NT / nch;
+  const size_t shm = G > 1 ? (size_t)a.E * a.d * sizeof(float) : 0;
+  if (a.E <= 8) hipLaunchKernelGGL((router_bwd_small_kernel<T, 8>), dim3(grid), dim3(NT), shm, s, a);
+  else hipLaunchKernelGGL((router_bwd_small_kernel<T, 16>), dim3(grid), dim3(NT), shm, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_bwd_small(int dt, const RouterBwdSmallArgs& a, hipStream_t s) {
+  if (a.E < 1 || a.E > kRouterSmallMaxE || a.d % 8 || a.d > kRouterSmallMaxD || a.T <= 0) return hipErrorInvalidValue;
+  switch (dt) {
+    case DT_BF16: return launch_router_bwd_small_t<__bf16>(a, s);
+    case DT_F16: return launch_router_bwd_small_t<_Float16>(a, s);
+    case DT_F32: return launch_router_bwd_small_t<float>(a, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_stack2(int dt, const Stack2Args& a, hipStream_t s) {

@@ -26,7 +26,7 @@ struct RouteArgs {
 hipError_t launch_route(int dt, const RouteArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------- permute --
-constexpr int kHistTokens = 1024;   // tokens per histogram block
+constexpr int kHistTokens = 256;    // tokens per histogram block
 struct PermuteArgs {
   const int32_t* idx;   // [T, k]
   const void* x;        // [T, d]
@@ -162,9 +162,24 @@ struct Stack2Args {    // w2 = [W_r; W_r] padded to Ep rows each, zeros elsewher
 };
 hipError_t launch_stack2(int dt, const Stack2Args& a, hipStream_t s);
 
+// Few experts (E <= kRouterSmallMaxE, d <= kRouterSmallMaxD): one kernel takes
+// dz for a block of tokens (written as the hi/lo pair of RouterDzArgs, experts
+// e < E only), the block's partial dW_r = dz^T x in f32 and its partial dbias.
+constexpr int kRouterSmallMaxE = 16, kRouterSmallMaxD = 2048, kRouterSmallTokens = 64;
+struct RouterBwdSmallArgs {
+  const float* g; const float* wts; const int32_t* idx; const float* probs; const int32_t* counts;
+  const void* x;          // [T, d] act
+  void* dz_hl;            // [T, 2*Ep] act (entries e < E and Ep + e, e < E)
+  float* dw_part;         // [nblk, E, d]
+  float* dbias_part;      // [nblk, E]
+  int64_t T; int E, Ep, d, k, renorm; float aux_coef;
+};
+int router_small_blocks(int64_t T);
+hipError_t launch_router_bwd_small(int dt, const RouterBwdSmallArgs& a, hipStream_t s);
+
 struct RouterReduceArgs {
-  const float* part;     // [splits, 2*Ep, d]
-  int splits; int E, Ep, d;
+  const float* part;     // [splits, rows, d]: row e (+ row lo_row + e when lo_row >= 0) of each split
+  int splits; int E, rows, lo_row, d;
   void* dw;              // [E, d] act
   const float* dbias_part; int nb; float* dbias;  // optional
 };

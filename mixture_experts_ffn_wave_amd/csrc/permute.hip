@@ -2,14 +2,15 @@
 //
 // The assignments (t, j) are ordered by (expert ascending, token ascending),
 // deterministically and without atomics on global memory:
-//   1. permute_hist: each block of 1024 tokens builds, in LDS, one bit per
+//   1. permute_hist: each block of kHistTokens tokens builds, in LDS, one bit per
 //      token for every expert (bit set <=> the token chose that expert).  The
 //      popcount of the bits below a token is the token's rank among the
 //      block's tokens of that expert; the full popcount is the block's count.
 //      Ranks go to inv_perm (scratch until step 3), counts to the workspace.
 //   2. permute_scan: one workgroup turns the [blocks x E] counts into
 //      counts[E], offsets[E+1] and the first output row of every
-//      (block, expert) pair.
+//      (block, expert) pair (expert totals first, so every block's row is
+//      written once).
 //   3. permute_scatter: one wave per token computes its k destination rows,
 //      writes inv_perm / perm_token, reads the token's row of x once and
 //      writes it k times (every access a full 16-byte vector, rows contiguous).
@@ -69,26 +70,17 @@ __global__ void __launch_bounds__(NT) permute_hist(PermuteArgs a) {
 }
 
 __global__ void __launch_bounds__(NT) permute_scan(PermuteArgs a, int nblk) {
-  constexpr int ROWS = 32;
-  __shared__ int32_t tile[ROWS * NT];
+  // thread e owns expert e (E <= 256): first its total over the blocks, then
+  // the exclusive scan over experts, then one pass writing every block's
+  // first output row (no read-back of block_base)
   __shared__ int32_t s_w[NT / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int e = tid;
-  int run = 0;
-  for (int b0 = 0; b0 < nblk; b0 += ROWS) {
-    const int nb = (nblk - b0) < ROWS ? (nblk - b0) : ROWS;
-    for (int i = tid; i < nb * a.E; i += NT) tile[i] = a.block_counts[(int64_t)b0 * a.E + i];
-    __syncthreads();
-    if (e < a.E) {
-      for (int b = 0; b < nb; ++b) {
-        const int c = tile[b * a.E + e];
-        a.block_base[(int64_t)(b0 + b) * a.E + e] = run;
-        run += c;
-      }
-    }
-    __syncthreads();
+  int cnt = 0;
+  if (e < a.E) {
+#pragma unroll 8
+    for (int b = 0; b < nblk; ++b) cnt += a.block_counts[(int64_t)b * a.E + e];
   }
-  const int cnt = (e < a.E) ? run : 0;
   int incl = cnt;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -104,7 +96,13 @@ __global__ void __launch_bounds__(NT) permute_scan(PermuteArgs a, int nblk) {
   if (e < a.E) {
     a.counts[e] = cnt;
     a.offsets[e] = excl;
-    for (int b = 0; b < nblk; ++b) a.block_base[(int64_t)b * a.E + e] += excl;
+    int run = excl;
+#pragma unroll 8
+    for (int b = 0; b < nblk; ++b) {
+      const int c = a.block_counts[(int64_t)b * a.E + e];
+      a.block_base[(int64_t)b * a.E + e] = run;
+      run += c;
+    }
   }
   if (e == a.E - 1) a.offsets[a.E] = incl;
 }

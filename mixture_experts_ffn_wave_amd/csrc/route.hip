@@ -23,88 +23,13 @@ namespace {
 constexpr int KB = 128;
 constexpr int LROW = KB + 16;
 
-template <typename T, int NSUB, int WAVES>
-__global__ void __launch_bounds__(WAVES * 64) route_kernel(RouteArgs a) {
-  constexpr int ES = sizeof(T);
-  constexpr int BK = KB / ES;
-  constexpr int TB = 32 * WAVES;          // tokens per workgroup
-  constexpr int EP = 32 * NSUB;           // padded experts
-  constexpr int NTH = WAVES * 64;
-  constexpr int XPT = TB * 8 / NTH;       // 16-byte chunks of the x tile per thread (= 4)
-  constexpr int WPT = EP * 8 / NTH;       // 16-byte chunks of the W tile per thread
-  static_assert(WPT >= 1, "too many waves for the expert tile");
-
-  __shared__ __attribute__((aligned(16))) char lx[TB * LROW];
-  __shared__ __attribute__((aligned(16))) char lw[EP * LROW];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t t0 = (int64_t)blockIdx.x * TB;
-  const char* xb = static_cast<const char*>(a.x);
-  const char* wb = static_cast<const char*>(a.w);
-
-  auto load = [&](int kc, u32x4* rx, u32x4* rw) {
-#pragma unroll
-    for (int s = 0; s < XPT; ++s) {
-      const int c = tid + NTH * s, r = c >> 3, cc = c & 7;
-      rx[s] = (t0 + r < a.T) ? ld16(xb + ((t0 + r) * a.d + kc) * ES + cc * 16) : (u32x4){0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int s = 0; s < WPT; ++s) {
-      const int c = tid + NTH * s, r = c >> 3, cc = c & 7;
-      rw[s] = (r < a.E) ? ld16(wb + ((int64_t)r * a.d + kc) * ES + cc * 16) : (u32x4){0u, 0u, 0u, 0u};
-    }
-  };
-  auto stage = [&](const u32x4* rx, const u32x4* rw) {
-#pragma unroll
-    for (int s = 0; s < XPT; ++s) {
-      const int c = tid + NTH * s;
-      st16(lx + (c >> 3) * LROW + (c & 7) * 16, rx[s]);
-    }
-#pragma unroll
-    for (int s = 0; s < WPT; ++s) {
-      const int c = tid + NTH * s;
-      st16(lw + (c >> 3) * LROW + (c & 7) * 16, rw[s]);
-    }
-  };
-
-  f32x16 acc[NSUB];
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[s][r] = 0.0f;
-
-  constexpr int CH = Mma32<T>::kChunks;
-  const int nk = a.d / BK;
-  u32x4 rx[XPT], rw[WPT];
-  load(0, rx, rw);
-  stage(rx, rw);
-  __syncthreads();
-  for (int kc = 0; kc < nk; ++kc) {
-    const bool more = kc + 1 < nk;
-    if (more) load((kc + 1) * BK, rx, rw);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int kb = ks * 16 * ES + (lane >> 5) * 8 * ES;
-      u32x4 fb[CH];
-      const char* xrow = lx + (wave * 32 + (lane & 31)) * LROW + kb;
-#pragma unroll
-      for (int ch = 0; ch < CH; ++ch) fb[ch] = ld16(xrow + ch * 16);
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) {
-        u32x4 fa[CH];
-        const char* wrow = lw + (s * 32 + (lane & 31)) * LROW + kb;
-#pragma unroll
-        for (int ch = 0; ch < CH; ++ch) fa[ch] = ld16(wrow + ch * 16);
-        Mma32<T>::run(acc[s], fa, fb);
-      }
-    }
-    __syncthreads();
-    if (more) stage(rx, rw);
-    __syncthreads();
-  }
-
+// Softmax, probabilities, top-k and weights of the 32 tokens tb.. tb+31 whose
+// logits sit in acc (lane l: token tb + l % 32, experts 32 s + 8 (r/4) +
+// 4 (l/32) + r%4 in register r of acc[s]).
+template <int NSUB>
+__device__ __forceinline__ void route_epilogue(const f32x16 (&acc)[NSUB], int64_t tb, int lane, const RouteArgs& a) {
   const int h = lane >> 5;
-  const int64_t t = t0 + wave * 32 + (lane & 31);
+  const int64_t t = tb + (lane & 31);
   const bool tv = t < a.T;
   const int E = a.E;
 
@@ -192,6 +117,97 @@ __global__ void __launch_bounds__(WAVES * 64) route_kernel(RouteArgs a) {
   if (a.renorm && tv && h == 0) {
     for (int j = 0; j < a.k; ++j) a.wts[t * a.k + j] = a.wts[t * a.k + j] / psum;
   }
+}
+
+template <typename T, int NSUB, int WAVES>
+__global__ void __launch_bounds__(WAVES * 64) route_kernel(RouteArgs a) {
+  constexpr int ES = sizeof(T);
+  constexpr int BK = KB / ES;
+  constexpr int TB = 32 * WAVES;          // tokens per workgroup
+  constexpr int EP = 32 * NSUB;           // padded experts
+  constexpr int NTH = WAVES * 64;
+  constexpr int XPT = TB * 8 / NTH;       // 16-byte chunks of the x tile per thread (= 4)
+  constexpr int WPT = EP * 8 / NTH;       // 16-byte chunks of the W tile per thread
+  static_assert(WPT >= 1, "too many waves for the expert tile");
+
+  __shared__ __attribute__((aligned(16))) char lx[TB * LROW];
+  __shared__ __attribute__((aligned(16))) char lw[EP * LROW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * TB;
+  const char* xb = static_cast<const char*>(a.x);
+  const char* wb = static_cast<const char*>(a.w);
+
+  auto load = [&](int kc, u32x4* rx, u32x4* rw) {
+#pragma unroll
+    for (int s = 0; s < XPT; ++s) {
+      const int c = tid + NTH * s, r = c >> 3, cc = c & 7;
+      rx[s] = (t0 + r < a.T) ? ld16(xb + ((t0 + r) * a.d + kc) * ES + cc * 16) : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int s = 0; s < WPT; ++s) {
+      const int c = tid + NTH * s, r = c >> 3, cc = c & 7;
+      rw[s] = (r < a.E) ? ld16(wb + ((int64_t)r * a.d + kc) * ES + cc * 16) : (u32x4){0u, 0u, 0u, 0u};
+    }
+  };
+  auto stage = [&](const u32x4* rx, const u32x4* rw) {
+#pragma unroll
+    for (int s = 0; s < XPT; ++s) {
+      const int c = tid + NTH * s;
+      st16(lx + (c >> 3) * LROW + (c & 7) * 16, rx[s]);
+    }
+#pragma unroll
+    for (int s = 0; s < WPT; ++s) {
+      const int c = tid + NTH * s;
+      st16(lw + (c >> 3) * LROW + (c & 7) * 16, rw[s]);
+    }
+  };
+
+  f32x16 acc[NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[s][r] = 0.0f;
+
+  constexpr int CH = Mma32<T>::kChunks;
+  const int nk = a.d / BK;
+  // a ring of PF chunks in registers: the loads of the next PF - 1 chunks are
+  // in flight while one is staged and multiplied
+  constexpr int PF = NSUB == 1 ? 4 : 2;
+  u32x4 rx[PF][XPT], rw[PF][WPT];
+#pragma unroll
+  for (int q = 0; q < PF; ++q)
+    if (q < nk) load(q * BK, rx[q], rw[q]);
+  for (int kc0 = 0; kc0 < nk; kc0 += PF) {
+#pragma unroll
+    for (int q = 0; q < PF; ++q) {
+      const int kc = kc0 + q;
+      if (kc < nk) {
+        stage(rx[q], rw[q]);
+        __syncthreads();
+        if (kc + PF < nk) load((kc + PF) * BK, rx[q], rw[q]);
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+          const int kb = ks * 16 * ES + (lane >> 5) * 8 * ES;
+          u32x4 fb[CH];
+          const char* xrow = lx + (wave * 32 + (lane & 31)) * LROW + kb;
+#pragma unroll
+          for (int ch = 0; ch < CH; ++ch) fb[ch] = ld16(xrow + ch * 16);
+#pragma unroll
+          for (int s = 0; s < NSUB; ++s) {
+            u32x4 fa[CH];
+            const char* wrow = lw + (s * 32 + (lane & 31)) * LROW + kb;
+#pragma unroll
+            for (int ch = 0; ch < CH; ++ch) fa[ch] = ld16(wrow + ch * 16);
+            Mma32<T>::run(acc[s], fa, fb);
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+
+  route_epilogue<NSUB>(acc, t0 + wave * 32, lane, a);
 }
 
 template <typename T, int NSUB, int WAVES>
