@@ -13,7 +13,12 @@ Prints ONE JSON line (rank 0, N = 1): tokens/s over K timed steps, plus
                    counter summary of the current kernel sources exists under
                    profiles/ (else null);
   cpu_baseline  -- the fp64 numpy oracle timed on the host on a bounded
-                   sample of the same workload.
+                   sample of the same workload;
+  step_ms       -- after the timed region, per-step times (hipEvents on the
+                   stream around each step): median / p10 / p90 with the
+                   caches warm, and again with a 1 GiB scratch write before
+                   every step so that no operand is left in the 256 MB
+                   last-level cache or the L2s ("flushed").
 Per-kernel times go to stderr.
 
 --traffic-calibration runs only a plain streaming kernel of known size (an
@@ -156,6 +161,28 @@ def per_kernel_times(layer, dy, names, steps=3):
     return out
 
 
+def step_distribution(layer, dy, steps, flush_bytes=0):
+    """Per-step times in ms (hipEvents on the current stream around each step);
+    with flush_bytes, a scratch buffer of that size is written before every
+    step (outside the events) to evict the caches."""
+    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda") if flush_bytes else None
+    times = []
+    for i in range(steps):
+        if scratch is not None:
+            scratch.fill_(i & 0xFF)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        layer.step(dy)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del scratch
+    times.sort()
+    q = lambda f: times[min(len(times) - 1, int(round(f * (len(times) - 1))))]
+    return {"median": q(0.5), "p10": q(0.1), "p90": q(0.9), "steps": len(times)}
+
+
 def cpu_baseline(wl, budget_s=12.0):
     """The fp64 oracle, untuned, on the host cores: whole fwd+bwd+aux passes of
     the same workload until ~budget_s of CPU time has run (at least one)."""
@@ -267,6 +294,10 @@ def main():
                                   "frac_of_peak": (expert_flops(wl) / (gemm_ms * 1e-3) / 1e12) / peak
                                   if gemm_ms else None,
                                   "gemm_ms_per_step": gemm_ms}
+    warm = step_distribution(layer, dy, args.steps)
+    flushed = step_distribution(layer, dy, args.steps, flush_bytes=1 << 30)
+    result["step_ms"] = {"warm": warm, "flushed": flushed,
+                         "flushed_tokens_per_s": wl.T / (flushed["median"] * 1e-3)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)

@@ -128,8 +128,11 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
-__device__ __forceinline__ float sigmoid_f(float g) { return 1.0f / (1.0f + __expf(-g)); }
+// sigmoid and silu with the hardware reciprocal (v_rcp_f32, about 1 ulp)
+// instead of a correctly rounded division: their results are rounded to the
+// activation dtype next.  exp(-g) = inf gives rcp = 0, the correct limit.
+__device__ __forceinline__ float sigmoid_f(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+__device__ __forceinline__ float silu_f(float g) { return g * sigmoid_f(g); }
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 

@@ -69,14 +69,19 @@ __global__ void __launch_bounds__(NT) mx_quant_rows_kernel(MxRowsArgs a) {
 }
 
 // Transposing quantiser.  One workgroup per 128 padded K positions x 64
-// columns: wave j quantises the 32-token block j of the tile for its lane's
-// column, so the four 32-byte pieces of each output row's 128-byte span are
-// written by one workgroup.  Tiles never straddle a segment: segment starts
-// (pad) and seg_len are multiples of 128.
+// columns: the 128 token rows x 64 columns are read with 16-byte row loads
+// (eight lanes per 128-byte row piece) into LDS, then wave j quantises the
+// 32-token block j of the tile for its lane's column, reading that column
+// back from LDS (64 lanes = one 128-byte row: no bank conflicts), so the four
+// 32-byte pieces of each output row's 128-byte span are written by one
+// workgroup.  Tiles never straddle a segment: segment starts (pad) and
+// seg_len are multiples of 128.
 constexpr int kColsTileK = 128, kColsTileC = 64;
 
 template <typename T>
 __global__ void __launch_bounds__(NT) mx_quant_cols_kernel(MxColsArgs a) {
+  static_assert(sizeof(T) == 2, "16-bit inputs");
+  __shared__ __attribute__((aligned(16))) T tile[kColsTileK][kColsTileC];
   const int64_t p0 = (int64_t)blockIdx.x * kColsTileK;     // padded K position of this tile
   int g;
   int64_t pstart;
@@ -94,16 +99,30 @@ __global__ void __launch_bounds__(NT) mx_quant_cols_kernel(MxColsArgs a) {
     if (g >= a.G) return;
     pstart = (int64_t)g * a.seg_len;
   }
-  const int c = blockIdx.y * kColsTileC + (threadIdx.x & 63);
-  if (c >= a.C) return;
-  const int64_t p = p0 + 32 * (threadIdx.x >> 6);
+  const int c0 = blockIdx.y * kColsTileC;
   const int64_t tstart = a.seg ? a.seg[g] : (int64_t)g * a.seg_len;
   const int64_t n = a.seg ? (int64_t)(a.seg[g + 1] - a.seg[g]) : a.seg_len;
-  const int64_t t0 = p - pstart;
-  const T* in = static_cast<const T*>(a.in) + tstart * a.ld_in + c;
+  const int64_t tt0 = p0 - pstart;                          // first token of the tile within the segment
+  const T* in = static_cast<const T*>(a.in) + tstart * a.ld_in;
+  // ---- load: 128 rows x 8 pieces of 16 bytes; rows past the segment and
+  // columns past C read as zero
+  constexpr int PIECES = kColsTileC * (int)sizeof(T) / 16;  // 16-byte pieces per tile row (8)
+#pragma unroll
+  for (int i = 0; i < kColsTileK * PIECES / NT; ++i) {
+    const int q = threadIdx.x + NT * i, r = q / PIECES, pc = q % PIECES;
+    const int col = c0 + pc * (16 / (int)sizeof(T));
+    const int64_t t = tt0 + r;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (t < n && col < a.C) v = ld16(in + t * a.ld_in + col);
+    *reinterpret_cast<u32x4*>(&tile[r][pc * (16 / (int)sizeof(T))]) = v;
+  }
+  __syncthreads();
+  const int c = c0 + (threadIdx.x & 63);
+  if (c >= a.C) return;
+  const int j = threadIdx.x >> 6;                           // 32-token block of the tile
   float v[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = (t0 + i < n) ? to_f32<T>(in[(t0 + i) * a.ld_in]) : 0.0f;
+  for (int i = 0; i < 32; ++i) v[i] = to_f32<T>(tile[32 * j + i][threadIdx.x & 63]);
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
@@ -112,7 +131,7 @@ __global__ void __launch_bounds__(NT) mx_quant_cols_kernel(MxColsArgs a) {
   u32x4 o[2];
 #pragma unroll
   for (int w = 0; w < 8; ++w) o[w >> 2][w & 3] = e4m3x4(v[4 * w], v[4 * w + 1], v[4 * w + 2], v[4 * w + 3], sc);
-  const int64_t row = a.row0 + c, k = a.k0 + p;
+  const int64_t row = a.row0 + c, k = a.k0 + p0 + 32 * j;
   uint8_t* dst = a.out + row * a.Kpad + k;
   st16(dst, o[0]);
   st16(dst + 16, o[1]);
@@ -160,7 +179,7 @@ hipError_t launch_mx_quant_rows(int dt, const MxRowsArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_mx_quant_cols(int dt, const MxColsArgs& a, hipStream_t s) {
-  if (a.Kpad % kColsTileK || a.k0 % kColsTileK || a.C <= 0) return hipErrorInvalidValue;
+  if (a.Kpad % kColsTileK || a.k0 % kColsTileK || a.C <= 0 || a.C % 8 || a.ld_in % 8) return hipErrorInvalidValue;
   if (!a.pad && (a.seg_len % kColsTileK)) return hipErrorInvalidValue;
   if (a.nblk <= 0) return hipSuccess;
   const int64_t tiles = (a.nblk * 32 + kColsTileK - 1) / kColsTileK;
