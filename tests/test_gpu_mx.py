@@ -57,6 +57,8 @@ def test_mx_quantiser_matches_the_oracle_bit_for_bit():
 
 SMALL_MX = [
     W("t1200_d256_e8k2_i256_mx", T=1200, d=256, E=8, k=2, I=256, expert_dtype="mxfp8"),
+    # skewed segments (Zipf bias): one expert far above the mean, several below 32 tokens
+    W("t1536_d256_e32k4_i128_zipf_mx", T=1536, d=256, E=32, k=4, I=128, zipf_s=1.1, expert_dtype="mxfp8"),
     W("t900_d256_e16k4_i384_s2x128_mx", T=900, d=256, E=16, k=4, I=384, n_shared=2, I_shared=128,
       expert_dtype="mxfp8"),
     W("t2049_d512_e4k2_i512_s1x256_mx", T=2049, d=512, E=4, k=2, I=512, n_shared=1, I_shared=256,
@@ -67,6 +69,39 @@ SMALL_MX = [
 @pytest.mark.parametrize("wl", SMALL_MX, ids=[w.name for w in SMALL_MX])
 def test_mx_layer_matches_oracle(wl):
     PT.full_parity(wl)
+
+
+def test_mx_forced_empty_experts_write_zero_gradients():
+    wl = W("t700_d256_e8k2_i256_mx_bias", T=700, d=256, E=8, k=2, I=256, n_shared=1, I_shared=128,
+           expert_dtype="mxfp8")
+    inp = MI.make_inputs(wl)
+    b = torch.zeros(8, dtype=torch.float32)
+    b[[2, 6]] = -1e4          # experts 2 and 6 never chosen
+    inp["bias"] = b
+    gpu, fwd, _, st = PT.full_parity(wl, inp)
+    assert fwd["counts"][2] == 0 and fwd["counts"][6] == 0
+    for e in (2, 6):
+        assert not np.any(gpu["dw_gate_up"][e]) and not np.any(gpu["dw_down"][e])
+
+
+def test_mx_empty_batch():
+    wl = W("t0_d256_e4k2_i128_mx_shared1", T=0, d=256, E=4, k=2, I=128, n_shared=1, I_shared=128,
+           expert_dtype="mxfp8")
+    gpu = PT.gpu_run(wl, MI.make_inputs(wl))
+    assert gpu["counts"].sum() == 0
+    for key in ("dw_router", "dw_gate_up", "dw_down", "dws_gate_up", "dws_down"):
+        assert not np.any(gpu[key]), key
+
+
+def test_mx_two_runs_are_bitwise_identical():
+    wl = W("t900_d256_e16k4_i384_s2x128_mx_det", T=900, d=256, E=16, k=4, I=384, n_shared=2, I_shared=128,
+           expert_dtype="mxfp8")
+    inp = MI.make_inputs(wl)
+    a = PT.gpu_run(wl, inp, intermediates=True)
+    b = PT.gpu_run(wl, inp, intermediates=True)
+    for key, v in a.items():
+        if isinstance(v, np.ndarray):
+            assert np.array_equal(v, b[key]), key
 
 
 @pytest.mark.timeout(900)

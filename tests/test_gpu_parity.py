@@ -122,9 +122,9 @@ def test_bench_workload_full_size():
     PT.full_parity(MI.WORKLOADS[MI.BENCH])
 
 
-# The two other full-size workloads the kernels support (the MX-fp8 one is not
-# built): element by element against the oracle, which takes about a minute
-# of host time each.
+# The two other full-size 16-bit workloads (the MX-fp8 one is in
+# test_gpu_mx.py): element by element against the oracle, which takes about a
+# minute of host time each.
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["t32768_d1536_e4k2_i3072_s1x3072_f16", "t16384_d2048_e128k8_i768_zipf_bf16"])
 def test_large_workloads_full_size(name):
