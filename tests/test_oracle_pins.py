@@ -507,3 +507,61 @@ def test_storage_rounding_lands_on_the_stated_values_only():
     assert np.array_equal(f0["y"], f1["y"])
     for n in ["dx", "dw_router", "dw_gate_up", "dw_down", "dws_gate_up", "dws_down"]:
         assert np.array_equal(b0[n], b1[n]), n
+
+
+def test_expert_steps_match_torch_autograd():
+    """The per-expert steps against torch autograd of the dense SwiGLU MLP
+    y = (silu(x Wg^T) * x Wu^T) Wd^T in float64 (a textbook routine)."""
+    rng = np.random.default_rng(11)
+    n, d, inter = 7, 12, 5
+    x = rng.standard_normal((n, d))
+    w_gu = rng.standard_normal((2 * inter, d)) * 0.3
+    w_d = rng.standard_normal((d, inter)) * 0.3
+    dy = rng.standard_normal((n, d))
+    G, U, H = O.expert_gate_up_step(x, w_gu)
+    Y = O.expert_down_step(H, w_d)
+    dgu, dw_d = O.expert_down_backward_step(dy, G, U, H, w_d)
+    dx, dw_gu = O.expert_gate_up_backward_step(dgu, x, w_gu)
+
+    tx = torch.tensor(x, requires_grad=True)
+    tgu = torch.tensor(w_gu, requires_grad=True)
+    td = torch.tensor(w_d, requires_grad=True)
+    g = tx @ tgu[:inter].T
+    u = tx @ tgu[inter:].T
+    g.retain_grad(); u.retain_grad()
+    y = (torch.nn.functional.silu(g) * u) @ td.T
+    (torch.tensor(dy) * y).sum().backward()
+    assert np.allclose(Y, y.detach().numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(dgu[:, :inter], g.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(dgu[:, inter:], u.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(dw_d, td.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(dx, tx.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(dw_gu, tgu.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("renorm", [True, False])
+@pytest.mark.parametrize("aux_coef", [0.0, 0.7])
+def test_router_backward_matches_torch_autograd(renorm, aux_coef):
+    """dz of router_backward against torch autograd of
+    L = sum_tj w_tj(z) <dy_t, Y_perm[inv_tj]> + aux_coef * E * sum_e f_e P_e(z)
+    with the selection and the counts held fixed (f carries no gradient)."""
+    rng = np.random.default_rng(12)
+    T, E, k, d = 9, 6, 2, 4
+    z = rng.standard_normal((T, E))
+    idx = O.topk_select(z, k)
+    counts, _, _, inv = O.expert_permutation(idx, E)
+    y_perm = rng.standard_normal((T * k, d))
+    dy = rng.standard_normal((T, d))
+    p = O.softmax_rows(z)
+    w = O.gate_weights(p, idx, renorm)
+    _, dz = O.router_backward(dy, y_perm, inv, p, idx, w, renorm, counts, aux_coef)
+
+    tz = torch.tensor(z, requires_grad=True)
+    tp = torch.softmax(tz, dim=1)
+    sel = torch.gather(tp, 1, torch.tensor(idx))
+    tw = sel / sel.sum(dim=1, keepdim=True) if renorm else sel
+    gsc = np.einsum("td,tjd->tj", dy, y_perm[inv])
+    f = torch.tensor(counts / (T * k))
+    loss = (tw * torch.tensor(gsc)).sum() + aux_coef * E * (f * tp.mean(dim=0)).sum()
+    loss.backward()
+    assert np.allclose(dz, tz.grad.numpy(), rtol=1e-10, atol=1e-13)
