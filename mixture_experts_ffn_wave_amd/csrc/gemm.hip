@@ -228,6 +228,20 @@ template <> struct TrRead<6> {
                  : "memory");
   }
 };
+template <> struct TrRead<8> {
+  __device__ __forceinline__ static void run(u32x2 (&o)[16], const uint32_t (&a)[16]) {
+    asm volatile(MOE_TR8(0, 16) MOE_TR8(1, 17) MOE_TR8(2, 18) MOE_TR8(3, 19)
+                 MOE_TR8(4, 20) MOE_TR8(5, 21) MOE_TR8(6, 22) MOE_TR8(7, 23)
+                 MOE_TR8(8, 24) MOE_TR8(9, 25) MOE_TR8(10, 26) MOE_TR8(11, 27)
+                 MOE_TR8(12, 28) MOE_TR8(13, 29) MOE_TR8(14, 30) MOE_TR8(15, 31) "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
+                   "=&v"(o[6]), "=&v"(o[7]), "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11]),
+                   "=&v"(o[12]), "=&v"(o[13]), "=&v"(o[14]), "=&v"(o[15])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+                   "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]), "v"(a[14]), "v"(a[15])
+                 : "memory");
+  }
+};
 #undef MOE_TR8
 
 // MFMA work of one chunk for a wave: NS weight-side subtiles (LDS rows
@@ -240,6 +254,81 @@ __device__ __forceinline__ void mfma_chunk(f32x16 (&acc)[NS][MS], const char* lq
                                            const int (&qrow)[NS], const int (&prow)[MS], int lane) {
   constexpr int CH = Mma32<T>::kChunks;
   constexpr int NRAW = (QO::kRawLds ? NS : 0) + (PO::kRawLds ? MS : 0);
+  if constexpr (NRAW == 0 && PERM) {
+    // Every k step's fragments first, then the MFMAs: the k step 0 products
+    // start as soon as its fragments arrive while the later ones are read.
+    u32x4 fa[KSTEPS][NS][CH], fb[KSTEPS][MS][CH];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) PO::template frag<false>(fb[ks][ms], lp, prow[ms], ks, lane);
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns) QO::template frag<PERM>(fa[ks][ns], lq, qrow[ns], ks, lane);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) Mma32<T>::run(acc[ns][ms], fa[ks][ns], fb[ks][ms]);
+    return;
+  }
+  if constexpr (NRAW > 0 && NRAW * KSTEPS <= 8 && (NRAW * KSTEPS) % 2 == 0) {
+    // Every k step's fragments of the chunk at once: the compiler-read ones
+    // first, then all transposed reads in one block whose single wait covers
+    // both, so the chunk's MFMAs run back to back after one LDS latency.
+    u32x4 fa[KSTEPS][NS][CH], fb[KSTEPS][MS][CH];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      if constexpr (!PO::kRawLds) {
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) PO::template frag<false>(fb[ks][ms], lp, prow[ms], ks, lane);
+      }
+      if constexpr (!QO::kRawLds) {
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) QO::template frag<PERM>(fa[ks][ns], lq, qrow[ns], ks, lane);
+      }
+    }
+    constexpr int QB = 0, PB = QO::kRawLds ? NS : 0;       // fragment slots of each operand per k step
+    uint32_t addr[2 * NRAW * KSTEPS];
+    u32x2 raw[2 * NRAW * KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      uint32_t* ak = addr + 2 * NRAW * ks;
+      if constexpr (QO::kRawLds) {
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) QO::template frag_addr<PERM>(ak + 2 * (QB + ns), lq, qrow[ns], ks, lane);
+      }
+      if constexpr (PO::kRawLds) {
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) PO::template frag_addr<false>(ak + 2 * (PB + ms), lp, prow[ms], ks, lane);
+      }
+    }
+    TrRead<NRAW * KSTEPS>::run(raw, addr);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const u32x2* rk = raw + 2 * NRAW * ks;
+      if constexpr (QO::kRawLds) {
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) {
+          const u32x2 lo = rk[2 * (QB + ns)], hi = rk[2 * (QB + ns) + 1];
+          fa[ks][ns][0] = (u32x4){lo[0], lo[1], hi[0], hi[1]};
+        }
+      }
+      if constexpr (PO::kRawLds) {
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) {
+          const u32x2 lo = rk[2 * (PB + ms)], hi = rk[2 * (PB + ms) + 1];
+          fb[ks][ms][0] = (u32x4){lo[0], lo[1], hi[0], hi[1]};
+        }
+      }
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) Mma32<T>::run(acc[ns][ms], fa[ks][ns], fb[ks][ms]);
+    }
+    return;
+  }
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
     u32x4 fa[NS][CH], fb[MS][CH];
