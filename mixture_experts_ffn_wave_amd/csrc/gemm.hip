@@ -402,30 +402,34 @@ template <int NS, int MS>
 __device__ __forceinline__ void mfma_chunk_mx(f32x16 (&acc)[NS][MS], const char* lq, const char* lp,
                                               const uint8_t* sq, const uint8_t* sp,
                                               const int (&qrow)[NS], const int (&prow)[MS], int lane) {
+  constexpr int KS = MX_DKB / 64;
   const int h = lane >> 5;
+  // every k step's fragments and scales first, then the MFMAs
+  v8i fa[KS][NS], fb[KS][MS];
+  int sa[KS][NS], sb[KS][MS];
 #pragma unroll
-  for (int ks = 0; ks < MX_DKB / 64; ++ks) {
-    v8i fa[NS], fb[MS];
-    int sa[NS], sb[MS];
+  for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) {
       const int r = qrow[ns] + perm_row(lane & 31);
-      fa[ns] = mx_frag(lq, r, ks, h);
-      sa[ns] = sq[4 * r + 2 * ks + h];
+      fa[ks][ns] = mx_frag(lq, r, ks, h);
+      sa[ks][ns] = sq[4 * r + 2 * ks + h];
     }
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) {
       const int r = prow[ms] + (lane & 31);
-      fb[ms] = mx_frag(lp, r, ks, h);
-      sb[ms] = sp[4 * r + 2 * ks + h];
+      fb[ks][ms] = mx_frag(lp, r, ks, h);
+      sb[ks][ms] = sp[4 * r + 2 * ks + h];
     }
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
       for (int ms = 0; ms < MS; ++ms)
-        acc[ns][ms] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[ns], fb[ms], acc[ns][ms], 0, 0, 0,
-                                                                        sa[ns], 0, sb[ms]);
-  }
+        acc[ns][ms] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[ks][ns], fb[ks][ms], acc[ns][ms], 0, 0, 0,
+                                                                        sa[ks][ns], 0, sb[ks][ms]);
 }
 
 template <int NS, int MS>
