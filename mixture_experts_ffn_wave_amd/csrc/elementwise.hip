@@ -39,6 +39,7 @@ __global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a) {
       float acc[VR];
 #pragma unroll
       for (int i = 0; i < VR; ++i) acc[i] = 0.0f;
+#pragma unroll 4
       for (int j = 0; j < a.k; ++j) {
         const int r = __shfl(r_l, j, 64);
         const float w = __shfl(w_l, j, 64);
@@ -450,12 +451,17 @@ __global__ void __launch_bounds__(NT) unpermute_kernel(UnpermuteArgs a) {
   for (int64_t t = (int64_t)blockIdx.x * (NT / 64) + (threadIdx.x >> 6); t < a.T; t += waves) {
     int r_l = -1;
     if (lane < a.k) r_l = a.inv[t * a.k + lane];
+    // router part inline (few experts): lane e < E holds dz[t][e] = hi + lo
+    float z_l = 0.0f;
+    if (!a.dxr && lane < a.E)
+      z_l = to_f32<T>(dz[t * 2 * a.Ep + lane]) + to_f32<T>(dz[t * 2 * a.Ep + a.Ep + lane]);
     for (int c0 = 0; c0 < nch; c0 += 64) {
       const int c = c0 + lane;
       const bool ok = c < nch;
       float acc[VR];
 #pragma unroll
       for (int i = 0; i < VR; ++i) acc[i] = 0.0f;
+#pragma unroll 4
       for (int j = 0; j < a.k; ++j) {
         const int r = __shfl(r_l, j, 64);
         if (ok && r >= 0) {
@@ -465,39 +471,51 @@ __global__ void __launch_bounds__(NT) unpermute_kernel(UnpermuteArgs a) {
           for (int i = 0; i < VR; ++i) acc[i] += to_f32<T>(ch.e[i]);
         }
       }
-      if (!ok) continue;
-      if (sp) {
+      // (every lane stays in the loop: the router part below shuffles)
+      if (sp && ok) {
         Chunk<T> ch;
         ch.raw = ld16(sp + t * rowbytes + (int64_t)c * 16);
 #pragma unroll
         for (int i = 0; i < VR; ++i) acc[i] += to_f32<T>(ch.e[i]);
       }
       if (a.dxr) {
-        const f32x4* src = reinterpret_cast<const f32x4*>(a.dxr + t * a.d + (int64_t)c * VR);
+        if (ok) {
+          const f32x4* src = reinterpret_cast<const f32x4*>(a.dxr + t * a.d + (int64_t)c * VR);
 #pragma unroll
-        for (int q = 0; q < VR / 4; ++q) {
-          const f32x4 v = src[q];
+          for (int q = 0; q < VR / 4; ++q) {
+            const f32x4 v = src[q];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[4 * q + i] += v[i];
+            for (int i = 0; i < 4; ++i) acc[4 * q + i] += v[i];
+          }
         }
       } else {
         float rz[VR];
 #pragma unroll
         for (int i = 0; i < VR; ++i) rz[i] = 0.0f;
-        for (int e = 0; e < a.E; ++e) {
-          const float z = to_f32<T>(dz[t * 2 * a.Ep + e]) + to_f32<T>(dz[t * 2 * a.Ep + a.Ep + e]);
-          Chunk<T> w;
-          w.raw = ld16(wr + (int64_t)e * rowbytes + (int64_t)c * 16);
+        // experts in groups of 8 whose weight loads are issued together
+        for (int e0 = 0; e0 < a.E; e0 += 8) {
+          Chunk<T> w[8];
 #pragma unroll
-          for (int i = 0; i < VR; ++i) rz[i] = fmaf(z, to_f32<T>(w.e[i]), rz[i]);
+          for (int u = 0; u < 8; ++u)
+            if (ok && e0 + u < a.E) w[u].raw = ld16(wr + (int64_t)(e0 + u) * rowbytes + (int64_t)c * 16);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const float z = __shfl(z_l, (e0 + u) & 63, 64);
+            if (e0 + u < a.E) {
+#pragma unroll
+              for (int i = 0; i < VR; ++i) rz[i] = fmaf(z, to_f32<T>(w[u].e[i]), rz[i]);
+            }
+          }
         }
 #pragma unroll
         for (int i = 0; i < VR; ++i) acc[i] += rz[i];
       }
-      Chunk<T> o;
+      if (ok) {
+        Chunk<T> o;
 #pragma unroll
-      for (int i = 0; i < VR; ++i) o.e[i] = from_f32<T>(acc[i]);
-      st16(out + t * rowbytes + (int64_t)c * 16, o.raw);
+        for (int i = 0; i < VR; ++i) o.e[i] = from_f32<T>(acc[i]);
+        st16(out + t * rowbytes + (int64_t)c * 16, o.raw);
+      }
     }
   }
 }
