@@ -577,6 +577,17 @@ __device__ __forceinline__ void ring_barrier(int remaining) {
   asm volatile("" ::: "memory");
 }
 
+// Barrier before the last chunk when PENDING later loads (issued after that
+// chunk's, e.g. the epilogue's first G/U rows) may stay in flight.
+template <int PENDING>
+__device__ __forceinline__ void ring_barrier_last() {
+  asm volatile("" ::: "memory");
+  wait_vmcnt<PENDING>();
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // --------------------------------------------------------------- row GEMM ---
 // MX: operands are MX-fp8 payload bytes (T = uint8_t) with scale bytes in
 // a.Ps / a.Qs, both operands K-contiguous rows (transposes are done by the
@@ -685,17 +696,41 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
   const int gcol0 = gblk * 2 * a.sub + (n0 - gblk * a.sub);
 
   // SwiGLU backward: the saved G and U of one pass, whole rows of the tile.
-  // (Loading them before the main loop instead costs VGPRs enough to drop
-  // a workgroup per CU, which was slower.)
+  // Buffer loads bounded by the tile's rows (rows past them read as zero), so
+  // every lane issues exactly 2 SITER loads, which the vmcnt accounting of
+  // the prefetch below relies on.
   auto load_gu_rows = [&](u32x4 (&dst)[2][PERM ? SITER : 1], int ms) {
-    const TO* aux = static_cast<const TO*>(a.aux);
+    const rsrc_t grs = make_rsrc(static_cast<const TO*>(a.aux) + row0 * a.ldaux, (uint32_t)(rows * a.ldaux * sizeof(TO)));
 #pragma unroll
     for (int i = 0; i < SITER; ++i) {
       const int q = tid + 64 * NW * i, sr = q / CPR, c = q % CPR;
-      const int tr = srow(sr, ms);
-      const TO* src = aux + (row0 + tr) * a.ldaux + gcol0 + c * 8;
-      dst[0][i] = (tr < rows) ? ld16(src) : (u32x4){0u, 0u, 0u, 0u};
-      dst[1][i] = (tr < rows) ? ld16(src + a.sub) : (u32x4){0u, 0u, 0u, 0u};
+      const uint32_t off = (uint32_t)((srow(sr, ms) * a.ldaux + gcol0 + c * 8) * sizeof(TO));
+      dst[0][i] = __builtin_amdgcn_raw_buffer_load_b128(grs, off, 0, 0);
+      dst[1][i] = __builtin_amdgcn_raw_buffer_load_b128(grs, off + (uint32_t)(a.sub * sizeof(TO)), 0, 0);
+    }
+  };
+  // The first pass's G/U rows are loaded during the last two k chunks, where
+  // their latency hides behind MFMAs (128 x 128 tiles: 32 more VGPRs there,
+  // still three workgroups per CU); each later pass's rows are loaded while
+  // the previous pass computes.
+  constexpr bool GU_PRE = PERM && EPI == EPI_SWIGLU_BWD && BM == 128 && BN == 128;
+  u32x4 gun[2][PERM ? SITER : 1];                           // (unused unless GU_PRE)
+  // The last two chunks of a ring main loop, with the first pass's G/U loads
+  // issued after every chunk's loads (so a vmcnt of 2 SITER before the last
+  // chunk still means that chunk has landed).
+  auto gu_prefetch_tail = [&](int nkd, auto barrier, auto issue_ahead, auto compute) {
+    if (nkd >= 2) {
+      barrier(1);
+      issue_ahead(nkd - 2);
+      asm volatile("" ::: "memory");                          // G/U loads after the chunk loads
+      load_gu_rows(gun, 0);
+      compute(nkd - 2);
+    } else {
+      load_gu_rows(gun, 0);
+    }
+    if (nkd >= 1) {
+      ring_barrier_last<2 * SITER>();
+      compute(nkd - 1);
     }
   };
 
@@ -750,14 +785,22 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
 #pragma unroll
     for (int c = 0; c < NSTG - 1; ++c)
       if (c < nkd) issue(c * MX_DKB, c);
-    for (int kc = 0; kc < nkd; ++kc) {
-      ring_barrier<LPC, NSTG>(nkd - 1 - kc);
+    auto issue_ahead = [&](int kc) {
       if (kc + NSTG - 1 < nkd) issue((kc + NSTG - 1) * MX_DKB, (kc + NSTG - 1) % NSTG);
+    };
+    auto compute = [&](int kc) {
       const int st = kc % NSTG;
       const char* buf = smem + st * DSTAGE;
       const uint8_t* sbuf = reinterpret_cast<const uint8_t*>(smem + SC_OFF + st * SSTAGE);
       mfma_chunk_mx<NS, MS>(acc, buf + PD::BYTES, buf, sbuf + BM * 4, sbuf, qrow, prow, lane);
+    };
+    const int nloop = GU_PRE ? nkd - 2 : nkd;
+    for (int kc = 0; kc < nloop; ++kc) {
+      ring_barrier<LPC, NSTG>(nkd - 1 - kc);
+      issue_ahead(kc);
+      compute(kc);
     }
+    if constexpr (GU_PRE) gu_prefetch_tail(nkd, ring_barrier<LPC, NSTG>, issue_ahead, compute);
   } else if constexpr (ES == 2) {
     // ---------------- direct-to-LDS main loop (16-bit types)
     using PD = DmaRows<BM, NW, DKB>;
@@ -828,12 +871,20 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
 #pragma unroll
     for (int c = 0; c < NSTG - 1; ++c)
       if (c < nkd) issue(c * DBKE, smem + c * DSTAGE);
-    for (int kc = 0; kc < nkd; ++kc) {
-      ring_barrier<LPC, NSTG>(nkd - 1 - kc);          // chunk kc landed everywhere; kc-1 consumed
+    auto issue_ahead = [&](int kc) {
       if (kc + NSTG - 1 < nkd) issue((kc + NSTG - 1) * DBKE, smem + ((kc + NSTG - 1) % NSTG) * DSTAGE);
+    };
+    auto compute = [&](int kc) {
       const char* buf = smem + (kc % NSTG) * DSTAGE;
       mfma_chunk<T, PD, QD, NS, MS, DKB / 32, true>(acc, buf + PD::BYTES, buf, qrow, prow, lane);
+    };
+    const int nloop = GU_PRE ? nkd - 2 : nkd;
+    for (int kc = 0; kc < nloop; ++kc) {
+      ring_barrier<LPC, NSTG>(nkd - 1 - kc);          // chunk kc landed everywhere; kc-1 consumed
+      issue_ahead(kc);
+      compute(kc);
     }
+    if constexpr (GU_PRE) gu_prefetch_tail(nkd, ring_barrier<LPC, NSTG>, issue_ahead, compute);
   } else {
   // ---------------- register-staged main loop (f32)
   // ---- row pointers (normal operands) / k-major base (transposed weight)
@@ -924,13 +975,23 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
     for (int ms = 0; ms < MS; ++ms) {
       lds_barrier();                                          // ring / previous pass no longer read
       if constexpr (EPI == EPI_SWIGLU_BWD) {
-        u32x4 cur[2][SITER];
-        load_gu_rows(cur, ms);
+        if constexpr (GU_PRE) {
 #pragma unroll
-        for (int i = 0; i < SITER; ++i) {
-          const int q = tid + 64 * NW * i, sr = q / CPR, c = q % CPR;
-          st16(sp(0, sr, c), cur[0][i]);
-          st16(sp(1, sr, c), cur[1][i]);
+          for (int i = 0; i < SITER; ++i) {
+            const int q = tid + 64 * NW * i, sr = q / CPR, c = q % CPR;
+            st16(sp(0, sr, c), gun[0][i]);
+            st16(sp(1, sr, c), gun[1][i]);
+          }
+          if (ms + 1 < MS) load_gu_rows(gun, ms + 1);
+        } else {
+          u32x4 cur[2][SITER];
+          load_gu_rows(cur, ms);
+#pragma unroll
+          for (int i = 0; i < SITER; ++i) {
+            const int q = tid + 64 * NW * i, sr = q / CPR, c = q % CPR;
+            st16(sp(0, sr, c), cur[0][i]);
+            st16(sp(1, sr, c), cur[1][i]);
+          }
         }
         lds_barrier();
       }
