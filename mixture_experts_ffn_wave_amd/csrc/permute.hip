@@ -10,7 +10,7 @@
 //   2. permute_scan: one workgroup turns the [blocks x E] counts into
 //      counts[E], offsets[E+1] and the first output row of every
 //      (block, expert) pair (expert totals first, so every block's row is
-//      written once).
+//      written once; several threads per expert share its blocks).
 //   3. permute_scatter: one wave per token computes its k destination rows,
 //      writes inv_perm / perm_token, reads the token's row of x once and
 //      writes it k times (every access a full 16-byte vector, rows contiguous).
@@ -70,41 +70,59 @@ __global__ void __launch_bounds__(NT) permute_hist(PermuteArgs a) {
 }
 
 __global__ void __launch_bounds__(NT) permute_scan(PermuteArgs a, int nblk) {
-  // thread e owns expert e (E <= 256): first its total over the blocks, then
-  // the exclusive scan over experts, then one pass writing every block's
-  // first output row (no read-back of block_base)
-  __shared__ int32_t s_w[NT / 64];
+  // P threads per expert (P a power of two, P E <= NT, so one expert's
+  // threads share a wave): thread p of expert e owns a contiguous range of
+  // blocks.  Range sums, a scan over the P threads, an exclusive scan over
+  // the experts, then every thread writes its blocks' first output rows.
+  __shared__ int32_t s_tot[NT], s_w[NT / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int e = tid;
-  int cnt = 0;
-  if (e < a.E) {
-#pragma unroll 8
-    for (int b = 0; b < nblk; ++b) cnt += a.block_counts[(int64_t)b * a.E + e];
+  int P = 1;
+  while (2 * P * a.E <= NT && 2 * P <= 64) P *= 2;
+  const int e = tid / P, p = tid - e * P;
+  const bool ve = e < a.E;
+  const int per = (nblk + P - 1) / P;
+  const int b0 = p * per < nblk ? p * per : nblk;
+  const int b1 = b0 + per < nblk ? b0 + per : nblk;
+  int part = 0;
+  if (ve) {
+#pragma unroll 4
+    for (int b = b0; b < b1; ++b) part += a.block_counts[(int64_t)b * a.E + e];
   }
-  int incl = cnt;
+  int incl = part;                                  // inclusive over the expert's threads
+  for (int o = 1; o < P; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (p >= o) incl += t;
+  }
+  if (ve && p == P - 1) s_tot[e] = incl;
+  __syncthreads();
+  // exclusive scan of the expert totals: thread x < E owns expert x
+  const int cnt = tid < a.E ? s_tot[tid] : 0;
+  int ex = cnt;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
+    const int t = __shfl_up(ex, o, 64);
+    if (lane >= o) ex += t;
   }
-  if (lane == 63) s_w[wave] = incl;
+  if (lane == 63) s_w[wave] = ex;
   __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wave; ++w) before += s_w[w];
-  incl += before;
-  const int excl = incl - cnt;
-  if (e < a.E) {
-    a.counts[e] = cnt;
-    a.offsets[e] = excl;
-    int run = excl;
-#pragma unroll 8
-    for (int b = 0; b < nblk; ++b) {
+  for (int w = 0; w < wave; ++w) ex += s_w[w];
+  if (tid < a.E) {
+    a.counts[tid] = cnt;
+    a.offsets[tid] = ex - cnt;
+    if (tid == a.E - 1) a.offsets[a.E] = ex;
+  }
+  __syncthreads();                                  // s_tot reused: expert offsets
+  if (tid < a.E) s_tot[tid] = ex - cnt;
+  __syncthreads();
+  if (ve) {
+    int run = s_tot[e] + incl - part;
+#pragma unroll 4
+    for (int b = b0; b < b1; ++b) {
       const int c = a.block_counts[(int64_t)b * a.E + e];
       a.block_base[(int64_t)b * a.E + e] = run;
       run += c;
     }
   }
-  if (e == a.E - 1) a.offsets[a.E] = incl;
 }
 
 template <typename T>

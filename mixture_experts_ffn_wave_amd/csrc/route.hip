@@ -23,11 +23,24 @@ namespace {
 constexpr int KB = 128;
 constexpr int LROW = KB + 16;
 
+// The bias (zeros without one) staged in LDS at kernel start by threads
+// 0 .. 32 NSUB - 1, so that the epilogue reads it without global round trips.
+template <int NSUB>
+__device__ __forceinline__ void stage_bias(float* s_bias, const RouteArgs& a) {
+  const int i = threadIdx.x;
+  if (i < 32 * NSUB) s_bias[i] = (a.bias && i < a.E) ? a.bias[i] : 0.0f;
+}
+
 // Softmax, probabilities, top-k and weights of the 32 tokens tb.. tb+31 whose
 // logits sit in acc (lane l: token tb + l % 32, experts 32 s + 8 (r/4) +
-// 4 (l/32) + r%4 in register r of acc[s]).
+// 4 (l/32) + r%4 in register r of acc[s]); s_bias as staged by stage_bias.
+// s_wts: kWtsLds floats of LDS owned by this wave, where the chosen
+// probabilities wait for their sum when they are renormalised.
+constexpr int kWtsStride = 65;                 // 64 slots per token, odd stride: no bank conflicts
+constexpr int kWtsLds = 32 * kWtsStride;
 template <int NSUB>
-__device__ __forceinline__ void route_epilogue(const f32x16 (&acc)[NSUB], int64_t tb, int lane, const RouteArgs& a) {
+__device__ __forceinline__ void route_epilogue(const f32x16 (&acc)[NSUB], int64_t tb, int lane, const RouteArgs& a,
+                                               const float* s_bias, float* s_wts) {
   const int h = lane >> 5;
   const int64_t t = tb + (lane & 31);
   const bool tv = t < a.T;
@@ -41,9 +54,7 @@ __device__ __forceinline__ void route_epilogue(const f32x16 (&acc)[NSUB], int64_
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int e = s * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-      float v = acc[s][r];
-      if (a.bias && e < E) v += a.bias[e];
-      z[s][r] = (e < E) ? v : -INFINITY;
+      z[s][r] = (e < E) ? acc[s][r] + s_bias[e] : -INFINITY;
       m = fmaxf(m, z[s][r]);
     }
   m = fmaxf(m, __shfl_xor(m, 32, 64));
@@ -111,11 +122,12 @@ __device__ __forceinline__ void route_epilogue(const f32x16 (&acc)[NSUB], int64_
     psum += pj;
     if (tv && h == 0) {
       a.idx[t * a.k + j] = we;
-      a.wts[t * a.k + j] = pj;
+      if (a.renorm) s_wts[(lane & 31) * kWtsStride + j] = pj;
+      else a.wts[t * a.k + j] = pj;
     }
   }
   if (a.renorm && tv && h == 0) {
-    for (int j = 0; j < a.k; ++j) a.wts[t * a.k + j] = a.wts[t * a.k + j] / psum;
+    for (int j = 0; j < a.k; ++j) a.wts[t * a.k + j] = s_wts[(lane & 31) * kWtsStride + j] / psum;
   }
 }
 
@@ -130,8 +142,13 @@ __global__ void __launch_bounds__(WAVES * 64) route_kernel(RouteArgs a) {
   constexpr int WPT = EP * 8 / NTH;       // 16-byte chunks of the W tile per thread
   static_assert(WPT >= 1, "too many waves for the expert tile");
 
-  __shared__ __attribute__((aligned(16))) char lx[TB * LROW];
-  __shared__ __attribute__((aligned(16))) char lw[EP * LROW];
+  __shared__ __attribute__((aligned(16))) char lds[(TB + EP) * LROW];
+  char* lx = lds;
+  char* lw = lds + TB * LROW;
+  static_assert(WAVES * kWtsLds * 4 <= (TB + EP) * LROW, "weights scratch fits in the tiles' LDS");
+  __shared__ float s_bias[EP];
+  static_assert(EP <= NTH, "bias staged by one thread per expert");
+  stage_bias<NSUB>(s_bias, a);                // visible after the K loop's first barrier
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t t0 = (int64_t)blockIdx.x * TB;
@@ -207,7 +224,133 @@ __global__ void __launch_bounds__(WAVES * 64) route_kernel(RouteArgs a) {
     }
   }
 
-  route_epilogue<NSUB>(acc, t0 + wave * 32, lane, a);
+  __syncthreads();                            // tiles free for the weights scratch (also covers an empty K loop)
+  route_epilogue<NSUB>(acc, t0 + wave * 32, lane, a, s_bias, reinterpret_cast<float*>(lds) + wave * kWtsLds);
+}
+
+// Few experts (E <= 64): 32 tokens per workgroup of KW waves that split the K
+// range.  Wave w multiplies chunks w, w + KW, ... into accumulators of its
+// own, staged through LDS tiles of its own (no workgroup barrier inside the
+// loop); the partial logits are then added in wave order through LDS and
+// wave 0 finishes the tokens.  Four times the waves of one-wave workgroups
+// over the same tokens, so each wave's serial chain of loads and MFMAs is a
+// quarter as long.
+template <typename T, int NSUB, int KW>
+__global__ void __launch_bounds__(KW * 64) route_ksplit_kernel(RouteArgs a) {
+  constexpr int ES = sizeof(T);
+  constexpr int BK = KB / ES;
+  constexpr int EP = 32 * NSUB;
+  constexpr int XPL = 32 * 8 / 64;        // 16-byte chunks of the x tile per lane
+  constexpr int WPL = EP * 8 / 64;        // 16-byte chunks of the W tile per lane
+  constexpr int WREG = (32 + EP) * LROW;  // one wave's tiles
+  constexpr int RED = (KW - 1) * NSUB * 16 * 64 * 4;
+  static_assert(RED <= KW * WREG && kWtsLds * 4 <= KW * WREG, "partial logits and weights scratch fit in the tiles' LDS");
+  __shared__ __attribute__((aligned(16))) char lds[KW * WREG];
+  __shared__ float s_bias[EP];
+  static_assert(EP <= KW * 64, "bias staged by one thread per expert");
+  stage_bias<NSUB>(s_bias, a);
+
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  char* lx = lds + wave * WREG;
+  char* lw = lx + 32 * LROW;
+  const int64_t t0 = (int64_t)blockIdx.x * 32;
+  const char* xb = static_cast<const char*>(a.x);
+  const char* wb = static_cast<const char*>(a.w);
+
+  auto load = [&](int kc, u32x4* rx, u32x4* rw) {
+#pragma unroll
+    for (int s = 0; s < XPL; ++s) {
+      const int c = lane + 64 * s, r = c >> 3, cc = c & 7;
+      rx[s] = (t0 + r < a.T) ? ld16(xb + ((t0 + r) * a.d + kc) * ES + cc * 16) : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int s = 0; s < WPL; ++s) {
+      const int c = lane + 64 * s, r = c >> 3, cc = c & 7;
+      rw[s] = (r < a.E) ? ld16(wb + ((int64_t)r * a.d + kc) * ES + cc * 16) : (u32x4){0u, 0u, 0u, 0u};
+    }
+  };
+
+  f32x16 acc[NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[s][r] = 0.0f;
+
+  constexpr int CH = Mma32<T>::kChunks;
+  constexpr int PF = 2;
+  const int nk = a.d / BK;
+  const int nmine = wave < nk ? (nk - wave + KW - 1) / KW : 0;   // chunks wave, wave + KW, ...
+  u32x4 rx[PF][XPL], rw[PF][WPL];
+#pragma unroll
+  for (int q = 0; q < PF; ++q)
+    if (q < nmine) load((wave + KW * q) * BK, rx[q], rw[q]);
+  for (int i0 = 0; i0 < nmine; i0 += PF) {
+#pragma unroll
+    for (int q = 0; q < PF; ++q) {
+      const int i = i0 + q;
+      if (i < nmine) {
+        // LDS accesses of one wave execute in order: the tiles written here
+        // are read below, and the reads of the previous chunk came first
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int s = 0; s < XPL; ++s) {
+          const int c = lane + 64 * s;
+          st16(lx + (c >> 3) * LROW + (c & 7) * 16, rx[q][s]);
+        }
+#pragma unroll
+        for (int s = 0; s < WPL; ++s) {
+          const int c = lane + 64 * s;
+          st16(lw + (c >> 3) * LROW + (c & 7) * 16, rw[q][s]);
+        }
+        asm volatile("" ::: "memory");
+        if (i + PF < nmine) load((wave + KW * (i + PF)) * BK, rx[q], rw[q]);
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+          const int kb = ks * 16 * ES + (lane >> 5) * 8 * ES;
+          u32x4 fb[CH];
+          const char* xrow = lx + (lane & 31) * LROW + kb;
+#pragma unroll
+          for (int ch = 0; ch < CH; ++ch) fb[ch] = ld16(xrow + ch * 16);
+#pragma unroll
+          for (int s = 0; s < NSUB; ++s) {
+            u32x4 fa[CH];
+            const char* wrow = lw + (s * 32 + (lane & 31)) * LROW + kb;
+#pragma unroll
+            for (int ch = 0; ch < CH; ++ch) fa[ch] = ld16(wrow + ch * 16);
+            Mma32<T>::run(acc[s], fa, fb);
+          }
+        }
+        asm volatile("" ::: "memory");
+      }
+    }
+  }
+
+  // partial logits of waves 1.. KW-1 -> LDS; wave 0 adds them in wave order
+  float* red = reinterpret_cast<float*>(lds);
+  __syncthreads();
+  if (wave > 0) {
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[(((wave - 1) * NSUB + s) * 16 + r) * 64 + lane] = acc[s][r];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    for (int w = 1; w < KW; ++w)
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[s][r] += red[(((w - 1) * NSUB + s) * 16 + r) * 64 + lane];
+    route_epilogue<NSUB>(acc, t0, lane, a, s_bias, red);      // (partials consumed: LDS reused)
+  }
+}
+
+template <typename T, int NSUB, int KW>
+hipError_t launch_route_ksplit(const RouteArgs& a, hipStream_t s) {
+  const int64_t grid = (a.T + 31) / 32;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((route_ksplit_kernel<T, NSUB, KW>), dim3((unsigned)grid), dim3(KW * 64), 0, s, a);
+  return hipGetLastError();
 }
 
 template <typename T, int NSUB, int WAVES>
@@ -222,8 +365,8 @@ hipError_t launch_route_t(const RouteArgs& a, hipStream_t s) {
 template <typename T>
 hipError_t launch_route_dt(const RouteArgs& a, hipStream_t s) {
   const int nsub = (a.E + 31) / 32;
-  if (nsub <= 1) return launch_route_t<T, 1, 1>(a, s);
-  if (nsub <= 2) return launch_route_t<T, 2, 1>(a, s);
+  if (nsub <= 1) return launch_route_ksplit<T, 1, 4>(a, s);
+  if (nsub <= 2) return launch_route_ksplit<T, 2, 4>(a, s);
   if (nsub <= 4) return launch_route_t<T, 4, 2>(a, s);
   return launch_route_t<T, 8, 4>(a, s);
 }
