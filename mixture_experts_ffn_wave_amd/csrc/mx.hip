@@ -72,16 +72,20 @@ __global__ void __launch_bounds__(NT) mx_quant_rows_kernel(MxRowsArgs a) {
 // columns: the 128 token rows x 64 columns are read with 16-byte row loads
 // (eight lanes per 128-byte row piece) into LDS, then wave j quantises the
 // 32-token block j of the tile for its lane's column, reading that column
-// back from LDS (64 lanes = one 128-byte row: no bank conflicts), so the four
-// 32-byte pieces of each output row's 128-byte span are written by one
-// workgroup.  Tiles never straddle a segment: segment starts (pad) and
-// seg_len are multiples of 128.
+// back from LDS (64 lanes = one 128-byte row: no bank conflicts).  The
+// quantised bytes go back through LDS so that each output row's 128-byte
+// span (four blocks) leaves as eight consecutive 16-byte stores and its four
+// scale bytes as one 4-byte store.  Tiles never straddle a segment: segment
+// starts (pad) and seg_len are multiples of 128.
 constexpr int kColsTileK = 128, kColsTileC = 64;
+constexpr int kColsOutRow = kColsTileK + 16;                // staged output row (padded: no bank conflicts)
 
 template <typename T>
 __global__ void __launch_bounds__(NT) mx_quant_cols_kernel(MxColsArgs a) {
   static_assert(sizeof(T) == 2, "16-bit inputs");
   __shared__ __attribute__((aligned(16))) T tile[kColsTileK][kColsTileC];
+  __shared__ __attribute__((aligned(16))) uint8_t qout[kColsTileC][kColsOutRow];
+  __shared__ __attribute__((aligned(16))) uint8_t qsc[kColsTileC][kColsTileK / 32];
   const int64_t p0 = (int64_t)blockIdx.x * kColsTileK;     // padded K position of this tile
   int g;
   int64_t pstart;
@@ -117,25 +121,40 @@ __global__ void __launch_bounds__(NT) mx_quant_cols_kernel(MxColsArgs a) {
     *reinterpret_cast<u32x4*>(&tile[r][pc * (16 / (int)sizeof(T))]) = v;
   }
   __syncthreads();
-  const int c = c0 + (threadIdx.x & 63);
-  if (c >= a.C) return;
-  const int j = threadIdx.x >> 6;                           // 32-token block of the tile
-  float v[32];
+  // ---- quantise: wave j, block j of the tile, column lane
+  {
+    const int cl = threadIdx.x & 63;
+    const int j = threadIdx.x >> 6;                         // 32-token block of the tile
+    float v[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = to_f32<T>(tile[32 * j + i][threadIdx.x & 63]);
-  float amax = 0.0f;
+    for (int i = 0; i < 32; ++i) v[i] = to_f32<T>(tile[32 * j + i][cl]);
+    float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  const int x = mx_scale_exp(amax);
-  const float sc = ldexpf(1.0f, -x);
-  u32x4 o[2];
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    const int x = mx_scale_exp(amax);
+    const float sc = ldexpf(1.0f, -x);
+    u32x4 o[2];
 #pragma unroll
-  for (int w = 0; w < 8; ++w) o[w >> 2][w & 3] = e4m3x4(v[4 * w], v[4 * w + 1], v[4 * w + 2], v[4 * w + 3], sc);
-  const int64_t row = a.row0 + c, k = a.k0 + p0 + 32 * j;
-  uint8_t* dst = a.out + row * a.Kpad + k;
-  st16(dst, o[0]);
-  st16(dst + 16, o[1]);
-  a.scales[row * (a.Kpad / 32) + k / 32] = (uint8_t)(x + 127);
+    for (int w = 0; w < 8; ++w) o[w >> 2][w & 3] = e4m3x4(v[4 * w], v[4 * w + 1], v[4 * w + 2], v[4 * w + 3], sc);
+    *reinterpret_cast<u32x4*>(&qout[cl][32 * j]) = o[0];
+    *reinterpret_cast<u32x4*>(&qout[cl][32 * j + 16]) = o[1];
+    qsc[cl][j] = (uint8_t)(x + 127);
+  }
+  __syncthreads();
+  // ---- store: output row c0 + r gets 128 bytes at K position k0 + p0 (eight
+  // lanes per row) and four scale bytes
+  const int64_t k = a.k0 + p0;
+#pragma unroll
+  for (int i = 0; i < kColsTileC * 8 / NT; ++i) {
+    const int q = threadIdx.x + NT * i, r = q >> 3, pc = q & 7;
+    if (c0 + r < a.C)
+      st16(a.out + (a.row0 + c0 + r) * a.Kpad + k + pc * 16, *reinterpret_cast<const u32x4*>(&qout[r][pc * 16]));
+  }
+  if (threadIdx.x < kColsTileC && c0 + (int)threadIdx.x < a.C) {
+    const int r = threadIdx.x;
+    *reinterpret_cast<uint32_t*>(a.scales + (a.row0 + c0 + r) * (a.Kpad / 32) + k / 32) =
+        *reinterpret_cast<const uint32_t*>(&qsc[r][0]);
+  }
 }
 
 __global__ void mx_pad_offsets_kernel(const int32_t* offsets, int32_t* pad, int G, int align) {
