@@ -541,10 +541,21 @@ __global__ void __launch_bounds__(NT) aux_partials_kernel(AuxArgs a) {
   if (t1 > a.T) t1 = a.T;
   float ps = 0.0f, ent = 0.0f;
   if (e < a.E) {
-    for (int64_t t = t0 + tl; t < t1; t += TL) {
-      const float p = a.probs[t * a.E + e];
-      ps += p;
-      if (p > 0.0f) ent -= p * logf(p);
+    // four tokens' loads issued together, then added in token order
+    for (int64_t tb = t0 + tl; tb < t1; tb += 4 * TL) {
+      float p[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t t = tb + u * TL;
+        p[u] = t < t1 ? a.probs[t * a.E + e] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (tb + u * TL < t1) {
+          ps += p[u];
+          if (p[u] > 0.0f) ent -= p[u] * logf(p[u]);
+        }
+      }
     }
   }
   sp[threadIdx.x] = ps;

@@ -157,15 +157,27 @@ __global__ void __launch_bounds__(NT) mx_quant_cols_kernel(MxColsArgs a) {
   }
 }
 
-__global__ void mx_pad_offsets_kernel(const int32_t* offsets, int32_t* pad, int G, int align) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  int32_t acc = 0;
-  pad[0] = 0;
-  for (int g = 0; g < G; ++g) {
+// pad[0] = 0, pad[g + 1] = sum over g' <= g of len(g') rounded up to align:
+// thread g rounds its segment's length, then a scan over the segments
+// (waves in order).  G <= NT.
+__global__ void __launch_bounds__(NT) mx_pad_offsets_kernel(const int32_t* offsets, int32_t* pad, int G, int align) {
+  __shared__ int32_t s_w[NT / 64];
+  const int g = threadIdx.x, lane = g & 63, wave = g >> 6;
+  int32_t v = 0;
+  if (g < G) {
     const int32_t n = offsets[g + 1] - offsets[g];
-    acc += (n + align - 1) / align * align;
-    pad[g + 1] = acc;
+    v = (n + align - 1) / align * align;
   }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  if (lane == 63) s_w[wave] = v;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) v += s_w[w];
+  if (g == 0) pad[0] = 0;
+  if (g < G) pad[g + 1] = v;
 }
 
 __global__ void mx_single_segment_kernel(int32_t* seg_pad, int64_t T, int align) {
@@ -213,7 +225,8 @@ hipError_t launch_mx_quant_cols(int dt, const MxColsArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_mx_pad_offsets(const int32_t* offsets, int32_t* pad, int G, int align, hipStream_t s) {
-  hipLaunchKernelGGL(mx_pad_offsets_kernel, dim3(1), dim3(64), 0, s, offsets, pad, G, align);
+  if (G < 1 || G > NT) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mx_pad_offsets_kernel, dim3(1), dim3(NT), 0, s, offsets, pad, G, align);
   return hipGetLastError();
 }
 
