@@ -430,10 +430,11 @@ moe_status mx_rows(moe_plan p, hipStream_t s, const void* in, int64_t ld_in, int
   return MOE_OK;
 }
 // transposed operand: the token axis of in [tokens][C] becomes K
+// (rows: the same operand also quantised along its rows, [token rows][C])
 moe_status mx_cols(moe_plan p, hipStream_t s, const void* in, int64_t ld_in, int C, const int32_t* seg,
                    const int32_t* pad, int G, int seg_len, int64_t nblk, int64_t k0, int64_t Kpad, int64_t row0,
-                   MxOp o) {
-  MxColsArgs a{in, ld_in, C, seg, pad, G, seg_len, nblk, k0, Kpad, row0, o.pay, o.sc};
+                   MxOp o, MxOp rows = MxOp{nullptr, nullptr}) {
+  MxColsArgs a{in, ld_in, C, seg, pad, G, seg_len, nblk, k0, Kpad, row0, o.pay, o.sc, rows.pay, rows.sc};
   Probe pr(p, "mx_quantize", s);
   MOE_TRY(launch_mx_quant_cols(p->dt, a, s));
   return MOE_OK;
@@ -628,7 +629,8 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
   }
   if (T > 0) {
     // dH = dY_perm W_d (reduction over d): W_d [E][d][I] transposed to [I][E d]
-    MOE_TRY_STATUS(mx_rows(p, s, dy_perm, d, 0, (int)d, A, (int)d, dyq));
+    // dY_perm both ways in one pass: rows for this product, token blocks for dW_d
+    MOE_TRY_STATUS(mx_cols(p, s, dy_perm, d, (int)d, sv->offsets, pad, (int)E, 0, Apad / 32, 0, Apad, 0, dyt, dyq));
     MOE_TRY_STATUS(mx_cols(p, s, sv->w_down, I, (int)I, nullptr, nullptr, (int)E, (int)d, E * d / 32, 0, E * d, 0, wdt));
     RowGemmArgs a{};
     mx_pq(a, dyq, d, wdt, E * d, d);
@@ -638,8 +640,7 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
     MOE_TRY(launch_row_gemm(DT_MXFP8, OP_DOWN_DGRAD, EPI_SWIGLU_BWD, 128, a, s));
   }
   {
-    // dW_d[e] = dY_perm[seg]^T H[seg]: token axis blocked per segment
-    MOE_TRY_STATUS(mx_cols(p, s, dy_perm, d, (int)d, sv->offsets, pad, (int)E, 0, Apad / 32, 0, Apad, 0, dyt));
+    // dW_d[e] = dY_perm[seg]^T H[seg]: token axis blocked per segment (dY_perm's done above)
     MOE_TRY_STATUS(mx_cols(p, s, sv->h, I, (int)I, sv->offsets, pad, (int)E, 0, Apad / 32, 0, Apad, 0, ht));
     WgradArgs a{};
     a.P = dyt.pay; a.Ps = dyt.sc; a.ldp = Apad; a.Q = ht.pay; a.Qs = ht.sc; a.ldq = Apad;
@@ -649,7 +650,9 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
   }
   if (T > 0) {
     // dX_perm = [dG | dU] W_gu (reduction over 2I): W_gu [E][2I][d] transposed to [d][E 2I]
-    MOE_TRY_STATUS(mx_rows(p, s, dgu, 2 * I, 0, (int)(2 * I), A, (int)(2 * I), dguq));
+    // [dG | dU] both ways in one pass: rows for this product, token blocks for dW_gu
+    MOE_TRY_STATUS(mx_cols(p, s, dgu, 2 * I, (int)(2 * I), sv->offsets, pad, (int)E, 0, Apad / 32, 0, Apad, 0, dgut,
+                           dguq));
     MOE_TRY_STATUS(mx_cols(p, s, sv->w_gate_up, d, (int)d, nullptr, nullptr, (int)E, (int)(2 * I), E * 2 * I / 32, 0,
                            E * 2 * I, 0, wgut));
     RowGemmArgs a{};
@@ -660,7 +663,6 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
     MOE_TRY(launch_row_gemm(DT_MXFP8, OP_GU_DGRAD, EPI_STORE, 128, a, s));
   }
   {
-    MOE_TRY_STATUS(mx_cols(p, s, dgu, 2 * I, (int)(2 * I), sv->offsets, pad, (int)E, 0, Apad / 32, 0, Apad, 0, dgut));
     MOE_TRY_STATUS(mx_cols(p, s, sv->x_perm, d, (int)d, sv->offsets, pad, (int)E, 0, Apad / 32, 0, Apad, 0, xt));
     WgradArgs a{};
     a.P = dgut.pay; a.Ps = dgut.sc; a.ldp = Apad; a.Q = xt.pay; a.Qs = xt.sc; a.ldq = Apad;

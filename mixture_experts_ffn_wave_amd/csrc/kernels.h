@@ -125,6 +125,10 @@ struct MxColsArgs {
   int64_t k0, Kpad, row0;
   uint8_t* out;        // [rows][Kpad]
   uint8_t* scales;     // [rows][Kpad/32]
+  // optional: the same input also quantised along its rows (blocks of 32
+  // columns), [token rows][C] and [token rows][C/32]; nullptr skips it
+  uint8_t* rout = nullptr;
+  uint8_t* rscales = nullptr;
 };
 hipError_t launch_mx_quant_cols(int dt, const MxColsArgs& a, hipStream_t s);
 

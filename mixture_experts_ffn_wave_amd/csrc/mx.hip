@@ -68,24 +68,30 @@ __global__ void __launch_bounds__(NT) mx_quant_rows_kernel(MxRowsArgs a) {
   }
 }
 
-// Transposing quantiser.  One workgroup per 128 padded K positions x 64
-// columns: the 128 token rows x 64 columns are read with 16-byte row loads
-// (eight lanes per 128-byte row piece) into LDS, then wave j quantises the
-// 32-token block j of the tile for its lane's column, reading that column
-// back from LDS (64 lanes = one 128-byte row: no bank conflicts).  The
-// quantised bytes go back through LDS so that each output row's 128-byte
-// span (four blocks) leaves as eight consecutive 16-byte stores and its four
-// scale bytes as one 4-byte store.  Tiles never straddle a segment: segment
-// starts (pad) and seg_len are multiples of 128.
-constexpr int kColsTileK = 128, kColsTileC = 64;
+// Transposing quantiser.  One workgroup per 128 padded K positions x TC
+// columns (TC = 64, or 128 when the row-wise blocks are wanted too): the 128
+// token rows x TC columns are read with 16-byte row loads into LDS, then wave
+// j quantises the 32-token block j of the tile for its lane's TC / 64
+// columns, reading them back from LDS (64 lanes = one 128-byte row: no bank
+// conflicts).  The quantised bytes go back through LDS (over the input tile,
+// which is dead by then) so that each output row's 128-byte span (four
+// blocks) leaves as eight consecutive 16-byte stores and its four scale
+// bytes as one 4-byte store.  Tiles never straddle a segment: segment starts
+// (pad) and seg_len are multiples of 128.  With rout set (TC = 128), the
+// tile is also quantised along its rows (four 32-column blocks per token
+// row, whole 128-byte output spans), so an operand needed both ways is read
+// once.
+constexpr int kColsTileK = 128;
 constexpr int kColsOutRow = kColsTileK + 16;                // staged output row (padded: no bank conflicts)
 
-template <typename T>
+template <typename T, int TC>
 __global__ void __launch_bounds__(NT) mx_quant_cols_kernel(MxColsArgs a) {
   static_assert(sizeof(T) == 2, "16-bit inputs");
-  __shared__ __attribute__((aligned(16))) T tile[kColsTileK][kColsTileC];
-  __shared__ __attribute__((aligned(16))) uint8_t qout[kColsTileC][kColsOutRow];
-  __shared__ __attribute__((aligned(16))) uint8_t qsc[kColsTileC][kColsTileK / 32];
+  static_assert(TC == 64 || TC == 128, "tile width");
+  static_assert(TC * kColsOutRow <= kColsTileK * TC * (int)sizeof(T), "output staging fits");
+  __shared__ __attribute__((aligned(16))) T tile[kColsTileK][TC];
+  __shared__ __attribute__((aligned(16))) uint8_t qsc[TC][kColsTileK / 32];
+  uint8_t* qout = reinterpret_cast<uint8_t*>(&tile[0][0]);  // [TC][kColsOutRow], after the quantise reads
   const int64_t p0 = (int64_t)blockIdx.x * kColsTileK;     // padded K position of this tile
   int g;
   int64_t pstart;
@@ -103,54 +109,89 @@ __global__ void __launch_bounds__(NT) mx_quant_cols_kernel(MxColsArgs a) {
     if (g >= a.G) return;
     pstart = (int64_t)g * a.seg_len;
   }
-  const int c0 = blockIdx.y * kColsTileC;
+  const int c0 = blockIdx.y * TC;
   const int64_t tstart = a.seg ? a.seg[g] : (int64_t)g * a.seg_len;
   const int64_t n = a.seg ? (int64_t)(a.seg[g + 1] - a.seg[g]) : a.seg_len;
   const int64_t tt0 = p0 - pstart;                          // first token of the tile within the segment
   const T* in = static_cast<const T*>(a.in) + tstart * a.ld_in;
-  // ---- load: 128 rows x 8 pieces of 16 bytes; rows past the segment and
+  // ---- load: 128 rows x 16 pieces of 16 bytes; rows past the segment and
   // columns past C read as zero
-  constexpr int PIECES = kColsTileC * (int)sizeof(T) / 16;  // 16-byte pieces per tile row (8)
+  constexpr int VP = 16 / (int)sizeof(T);                   // values per piece
+  constexpr int PIECES = TC / VP;                   // pieces per tile row
 #pragma unroll
   for (int i = 0; i < kColsTileK * PIECES / NT; ++i) {
     const int q = threadIdx.x + NT * i, r = q / PIECES, pc = q % PIECES;
-    const int col = c0 + pc * (16 / (int)sizeof(T));
+    const int col = c0 + pc * VP;
     const int64_t t = tt0 + r;
     u32x4 v = {0u, 0u, 0u, 0u};
     if (t < n && col < a.C) v = ld16(in + t * a.ld_in + col);
-    *reinterpret_cast<u32x4*>(&tile[r][pc * (16 / (int)sizeof(T))]) = v;
+    *reinterpret_cast<u32x4*>(&tile[r][pc * VP]) = v;
   }
   __syncthreads();
-  // ---- quantise: wave j, block j of the tile, column lane
-  {
-    const int cl = threadIdx.x & 63;
-    const int j = threadIdx.x >> 6;                         // 32-token block of the tile
+  // ---- row-wise blocks (optional): token row r, columns c0 + 32 b ..
+  if (TC == 128 && a.rout) {
+#pragma unroll
+    for (int i = 0; i < kColsTileK * (TC / 32) / NT; ++i) {
+      const int q = threadIdx.x + NT * i, r = q >> 2, b = q & 3;
+      const int cb = c0 + 32 * b;
+      if (tt0 + r < n && cb < a.C) {
+        float v[32];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) unpack8<T>(*reinterpret_cast<const u32x4*>(&tile[r][32 * b + 8 * u]), v + 8 * u);
+        float amax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(v[e]));
+        const int x = mx_scale_exp(amax);
+        const float sc = ldexpf(1.0f, -x);
+        u32x4 o[2];
+#pragma unroll
+        for (int w = 0; w < 8; ++w) o[w >> 2][w & 3] = e4m3x4(v[4 * w], v[4 * w + 1], v[4 * w + 2], v[4 * w + 3], sc);
+        const int64_t row = tstart + tt0 + r;
+        uint8_t* dst = a.rout + row * a.C + cb;
+        st16(dst, o[0]);
+        st16(dst + 16, o[1]);
+        a.rscales[row * (a.C / 32) + cb / 32] = (uint8_t)(x + 127);
+      }
+    }
+  }
+  // ---- token blocks: wave j, block j of the tile, columns lane (+ 64)
+  constexpr int NCC = TC / 64;
+  const int j = threadIdx.x >> 6, cl = threadIdx.x & 63;
+  u32x4 o[NCC][2];
+  int xs[NCC];
+#pragma unroll
+  for (int cc = 0; cc < NCC; ++cc) {
     float v[32];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = to_f32<T>(tile[32 * j + i][cl]);
+    for (int i = 0; i < 32; ++i) v[i] = to_f32<T>(tile[32 * j + i][cl + 64 * cc]);
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
     const int x = mx_scale_exp(amax);
     const float sc = ldexpf(1.0f, -x);
-    u32x4 o[2];
 #pragma unroll
-    for (int w = 0; w < 8; ++w) o[w >> 2][w & 3] = e4m3x4(v[4 * w], v[4 * w + 1], v[4 * w + 2], v[4 * w + 3], sc);
-    *reinterpret_cast<u32x4*>(&qout[cl][32 * j]) = o[0];
-    *reinterpret_cast<u32x4*>(&qout[cl][32 * j + 16]) = o[1];
-    qsc[cl][j] = (uint8_t)(x + 127);
+    for (int w = 0; w < 8; ++w) o[cc][w >> 2][w & 3] = e4m3x4(v[4 * w], v[4 * w + 1], v[4 * w + 2], v[4 * w + 3], sc);
+    xs[cc] = x;
+  }
+  __syncthreads();                                          // input tile dead: reused for the output rows
+#pragma unroll
+  for (int cc = 0; cc < NCC; ++cc) {
+    const int r = cl + 64 * cc;
+    *reinterpret_cast<u32x4*>(qout + r * kColsOutRow + 32 * j) = o[cc][0];
+    *reinterpret_cast<u32x4*>(qout + r * kColsOutRow + 32 * j + 16) = o[cc][1];
+    qsc[r][j] = (uint8_t)(xs[cc] + 127);
   }
   __syncthreads();
   // ---- store: output row c0 + r gets 128 bytes at K position k0 + p0 (eight
   // lanes per row) and four scale bytes
   const int64_t k = a.k0 + p0;
 #pragma unroll
-  for (int i = 0; i < kColsTileC * 8 / NT; ++i) {
+  for (int i = 0; i < TC * 8 / NT; ++i) {
     const int q = threadIdx.x + NT * i, r = q >> 3, pc = q & 7;
     if (c0 + r < a.C)
-      st16(a.out + (a.row0 + c0 + r) * a.Kpad + k + pc * 16, *reinterpret_cast<const u32x4*>(&qout[r][pc * 16]));
+      st16(a.out + (a.row0 + c0 + r) * a.Kpad + k + pc * 16, *reinterpret_cast<const u32x4*>(qout + r * kColsOutRow + pc * 16));
   }
-  if (threadIdx.x < kColsTileC && c0 + (int)threadIdx.x < a.C) {
+  if (threadIdx.x < TC && c0 + (int)threadIdx.x < a.C) {
     const int r = threadIdx.x;
     *reinterpret_cast<uint32_t*>(a.scales + (a.row0 + c0 + r) * (a.Kpad / 32) + k / 32) =
         *reinterpret_cast<const uint32_t*>(&qsc[r][0]);
@@ -212,13 +253,23 @@ hipError_t launch_mx_quant_rows(int dt, const MxRowsArgs& a, hipStream_t s) {
 hipError_t launch_mx_quant_cols(int dt, const MxColsArgs& a, hipStream_t s) {
   if (a.Kpad % kColsTileK || a.k0 % kColsTileK || a.C <= 0 || a.C % 8 || a.ld_in % 8) return hipErrorInvalidValue;
   if (!a.pad && (a.seg_len % kColsTileK)) return hipErrorInvalidValue;
+  if (a.rout && (a.C % 32 || !a.rscales)) return hipErrorInvalidValue;
   if (a.nblk <= 0) return hipSuccess;
   const int64_t tiles = (a.nblk * 32 + kColsTileK - 1) / kColsTileK;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)tiles, (unsigned)((a.C + kColsTileC - 1) / kColsTileC));
+  // 128-column tiles when the row-wise blocks ride along (whole 128-byte
+  // row spans); otherwise 64 columns, which measured faster
+  const int tc = a.rout ? 128 : 64;
+  const dim3 grid((unsigned)tiles, (unsigned)((a.C + tc - 1) / tc));
   switch (dt) {
-    case DT_BF16: hipLaunchKernelGGL(mx_quant_cols_kernel<__bf16>, grid, dim3(NT), 0, s, a); break;
-    case DT_F16: hipLaunchKernelGGL(mx_quant_cols_kernel<_Float16>, grid, dim3(NT), 0, s, a); break;
+    case DT_BF16:
+      if (a.rout) hipLaunchKernelGGL((mx_quant_cols_kernel<__bf16, 128>), grid, dim3(NT), 0, s, a);
+      else hipLaunchKernelGGL((mx_quant_cols_kernel<__bf16, 64>), grid, dim3(NT), 0, s, a);
+      break;
+    case DT_F16:
+      if (a.rout) hipLaunchKernelGGL((mx_quant_cols_kernel<_Float16, 128>), grid, dim3(NT), 0, s, a);
+      else hipLaunchKernelGGL((mx_quant_cols_kernel<_Float16, 64>), grid, dim3(NT), 0, s, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
