@@ -21,6 +21,8 @@ from .moe_oracle import (  # noqa: F401
     softmax_rows,
     topk_select,
     gate_weights,
+    balanced_selection_scores,
+    balance_bias_update,
     near_tie_tokens,
     expert_permutation,
     silu,

@@ -21,6 +21,10 @@ What the layer computes is taken from three descriptions of it:
 Readings where the pages are silent (each is also listed in the design notes):
   * top-k is taken on the logits (after any constant router bias), ordered by
     logit descending and, on equal logits, by lower expert index;
+  * aux-loss-free balancing (KohakUwULLM README, "Key features": DeepSeekMoE
+    with aux-loss-free load balancing, no rule given) follows the published
+    method: top-k on probability + per-expert selection bias, weights from the
+    unbiased probabilities, bias += gamma * sign(mean load - load) per step;
   * f_e = count_e / (T * k), P_e = mean over all T tokens of the full softmax,
     aux = E * sum_e f_e * P_e (equals 1 at perfect balance; E = 4 gives the
     model card's "4 * sum");
@@ -73,6 +77,31 @@ def gate_weights(p, idx, renorm):
     if renorm:
         return sel / sel.sum(axis=1, keepdims=True)
     return sel
+
+
+def balanced_selection_scores(p, sel_bias):
+    """Scores the aux-loss-free balancing router ranks for top-k: the routing
+    probabilities plus a per-expert selection bias.  KohakUwULLM README, "Key
+    features", names DeepSeekMoE with aux-loss-free load balancing and gives
+    no rule; the reading taken is the published method (a bias added to each
+    expert's routing score for the choice of experts only, the gate weights
+    still taken from the unbiased probabilities).  Rank with topk_select;
+    weights with gate_weights on the unbiased ``p``."""
+    return p + np.asarray(sel_bias, dtype=np.float64)[None, :]
+
+
+def balance_bias_update(sel_bias, counts, T, top_k, gamma):
+    """One update of the selection bias after a step: b_e += gamma * sign(mean
+    load - count_e), mean load = T k / E, so overloaded experts lose and
+    underloaded ones gain a fixed step (the published aux-loss-free rule; see
+    balanced_selection_scores).  The bias is an f32 vector, so the addition
+    is rounded to f32 once; the sign is decided exactly in integers
+    (T k - E count_e)."""
+    b = np.asarray(sel_bias, dtype=np.float32)
+    c = np.asarray(counts, dtype=np.int64)
+    E = b.shape[0]
+    sgn = np.sign(int(T) * int(top_k) - E * c).astype(np.float32)
+    return (b + np.float32(gamma) * sgn).astype(np.float32)
 
 
 def near_tie_tokens(z, k, eps=1e-5):
@@ -230,8 +259,12 @@ def expert_down_step(h, w_down_e, quant=None):
 
 
 def layer_forward(x, w_router, w_gate_up, w_down, *, top_k, renorm=True, bias=None,
-                  ws_gate_up=None, ws_down=None, quant=None, store=None):
+                  ws_gate_up=None, ws_down=None, quant=None, store=None, sel_bias=None):
     """Full forward pass.  Returns a dict of every intermediate.
+
+    ``sel_bias`` (aux-loss-free balancing) moves the choice of experts to
+    balanced_selection_scores(p, sel_bias); the weights stay the unbiased
+    probabilities of the chosen experts.
 
     ``quant``, if given, is applied to each operand of each expert GEMM as
     quant(array, axis) with ``axis`` the contraction axis of that GEMM (the MX
@@ -251,7 +284,7 @@ def layer_forward(x, w_router, w_gate_up, w_down, *, top_k, renorm=True, bias=No
     E = w_router.shape[0]
     z = router_logits(x, w_router, bias)
     p = softmax_rows(z)
-    idx = topk_select(z, top_k)
+    idx = topk_select(z if sel_bias is None else balanced_selection_scores(p, sel_bias), top_k)
     w = gate_weights(p, idx, renorm)
     counts, offsets, perm_token, inv = expert_permutation(idx, E)
     x_perm = x[perm_token]
@@ -280,7 +313,7 @@ def layer_forward(x, w_router, w_gate_up, w_down, *, top_k, renorm=True, bias=No
                 y_perm=y_perm, y_shared=y_shared, shared=shared, y=y,
                 x=x, w_router=w_router, w_gate_up=w_gate_up, w_down=w_down,
                 ws_gate_up=ws_gate_up, ws_down=ws_down, top_k=top_k,
-                renorm=renorm, bias=bias, store=store)
+                renorm=renorm, bias=bias, store=store, sel_bias=sel_bias)
 
 
 def expert_down_backward_step(dy_rows, g, u, h, w_down_e, quant=None, store=None):

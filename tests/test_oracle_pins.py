@@ -182,8 +182,10 @@ def test_permutation_properties(E, k):
 
 # ----------------------------------------------------- forward brute force
 
-def _py_forward(L, k, renorm):
-    """The whole forward with Python loops and math.exp, no numpy algebra."""
+def _py_forward(L, k, renorm, sel_bias=None):
+    """The whole forward with Python loops and math.exp, no numpy algebra.
+    With sel_bias the experts are chosen on probability + bias (aux-loss-free
+    balancing) and weighted by the unbiased probabilities."""
     x, Wr, Wgu, Wd = L["x"].tolist(), L["w_router"].tolist(), L["w_gate_up"].tolist(), L["w_down"].tolist()
     T, d, E, inter = len(x), len(x[0]), len(Wr), len(Wd[0][0])
     b = L["bias"].tolist() if L["bias"] is not None else [0.0] * E
@@ -206,7 +208,7 @@ def _py_forward(L, k, renorm):
         ex = [math.exp(v - m) for v in z]
         s = sum(ex)
         p = [v / s for v in ex]
-        sel = _brute_topk(z, k)
+        sel = _brute_topk(z if sel_bias is None else [p[e] + sel_bias[e] for e in range(E)], k)
         wts = [p[e] for e in sel]
         if renorm:
             sw = sum(wts)
@@ -231,6 +233,67 @@ def test_forward_matches_python_loops(k, renorm, n_shared, bias):
     fwd = fwd_of(L, k, renorm)
     ref = _py_forward(L, k, renorm)
     assert np.max(np.abs(fwd["y"] - ref)) < 1e-12 * max(1.0, np.abs(ref).max())
+
+
+@pytest.mark.parametrize("k,renorm", [(2, True), (3, False)])
+def test_balanced_forward_matches_python_loops(k, renorm):
+    L = rand_layer(T=6, d=8, E=5, k=k, inter=5, seed=40 + k)
+    sb = [0.3, -0.2, 0.05, 0.0, -0.4]
+    fwd = O.layer_forward(L["x"], L["w_router"], L["w_gate_up"], L["w_down"], top_k=k, renorm=renorm,
+                          sel_bias=np.array(sb))
+    ref = _py_forward(L, k, renorm, sel_bias=sb)
+    assert np.max(np.abs(fwd["y"] - ref)) < 1e-12 * max(1.0, np.abs(ref).max())
+
+
+def test_zero_selection_bias_is_the_plain_router():
+    # ranking probabilities ranks the logits (softmax is monotone per row)
+    L = rand_layer(T=64, E=8, seed=5)
+    z = O.router_logits(L["x"], L["w_router"])
+    p = O.softmax_rows(z)
+    assert (O.topk_select(O.balanced_selection_scores(p, np.zeros(8)), 3) == O.topk_select(z, 3)).all()
+
+
+def test_large_selection_bias_forces_the_choice_not_the_weights():
+    # probabilities lie in (0, 1), so a bias of 2 puts expert 5 first for every
+    # token; its weight is still its own probability over the chosen ones
+    L = rand_layer(T=32, E=8, seed=6)
+    sb = np.zeros(8)
+    sb[5] = 2.0
+    fwd = O.layer_forward(L["x"], L["w_router"], L["w_gate_up"], L["w_down"], top_k=2, renorm=True, sel_bias=sb)
+    assert (fwd["idx"][:, 0] == 5).all()
+    p = fwd["p"]
+    for t in range(32):
+        e1 = fwd["idx"][t, 1]
+        assert e1 == max((e for e in range(8) if e != 5), key=lambda e: (p[t, e], -e))
+        assert abs(fwd["w"][t, 0] - p[t, 5] / (p[t, 5] + p[t, e1])) < 1e-15
+
+
+def test_balance_bias_update_hand_values():
+    # T k = 30 over E = 3 experts: mean load 10; loads 12, 10, 8
+    out = O.balance_bias_update([0.5, 0.0, -0.75], [12, 10, 8], T=10, top_k=3, gamma=0.25)
+    assert out.dtype == np.float32 and list(out) == [0.25, 0.0, -0.5]
+    # the bias is f32: 1 + 2^-30 rounds back to 1 (an f64 sum would not)
+    assert O.balance_bias_update([1.0, 1.0], [0, 4], T=2, top_k=2, gamma=2.0 ** -30)[0] == np.float32(1.0)
+    # a mean load that is not an integer: T k / E = 7 / 2
+    assert list(O.balance_bias_update([0.0, 0.0], [4, 3], T=7, top_k=1, gamma=1.0)) == [-1.0, 1.0]
+
+
+def test_bias_updates_balance_a_skewed_router():
+    # the purpose of the method: with fixed, strongly skewed logits, repeated
+    # updates drive the per-expert loads toward the mean without touching the
+    # gate weights' source (the unbiased probabilities)
+    rng = np.random.default_rng(7)
+    T, E, k = 2048, 8, 2
+    z = rng.standard_normal((T, E)) + np.log(1.0 / np.arange(1, E + 1) ** 1.2)[None, :]
+    p = O.softmax_rows(z)
+    b = np.zeros(E, dtype=np.float32)
+    cv = []
+    for _ in range(400):
+        idx = O.topk_select(O.balanced_selection_scores(p, b), k)
+        counts = np.bincount(idx.ravel(), minlength=E)
+        cv.append(counts.std() / counts.mean())
+        b = O.balance_bias_update(b, counts, T, k, gamma=1e-3)
+    assert cv[0] > 0.5 and max(cv[-50:]) < 0.1 * cv[0]
 
 
 def test_single_expert_top1_is_dense_swiglu_mlp():
