@@ -220,6 +220,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--traffic-calibration", action="store_true")
+    ap.add_argument("--balance-gamma", type=float, default=0.0,
+                    help="route with aux-loss-free balancing, the selection bias updated by this step "
+                         "size at the end of every step (0 = the plain router)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (no collectives, no sharding); "
@@ -231,6 +234,8 @@ def main():
     wl = MI.WORKLOADS[args.workload]
     torch.cuda.init()
     layer, dev = make_layer(wl)
+    if args.balance_gamma > 0:
+        layer.enable_balancing(gamma=args.balance_gamma)
     dy = dev["dy"]
     print(f"[bench] workload {wl.name}: {MI.describe(wl)}", file=sys.stderr, flush=True)
 
@@ -284,7 +289,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "d_model": wl.d, "experts": wl.E, "top_k": wl.k,
                    "d_ff": wl.I, "shared": f"{wl.n_shared}x{wl.I_shared}", "renorm": wl.renorm,
-                   "parallelism": "none (1 GPU)"},
+                   "parallelism": "none (1 GPU)",
+                   **({"balance_gamma": args.balance_gamma} if args.balance_gamma > 0 else {})},
         "roofline": {"bound": "mfma", "kernel": dominant, "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic_per_launch(wl, dominant),
                      "avg_launch_us": avg_ms * 1e3, "launches": launches},

@@ -119,6 +119,29 @@ const char* moe_version(void);
 moe_status moe_route(moe_plan plan, const void* x, const void* w_router, const float* bias,
                      float* probs, int32_t* topk_idx, float* topk_w, void* stream);
 
+/* Router with aux-loss-free load balancing (KohakUwULLM README, "Key
+ * features": DeepSeekMoE with aux-loss-free load balancing; the pages give no
+ * rule, so this library follows the published method).  As moe_route, except
+ * that the experts are ranked on probs[t, e] + sel_bias[e], computed in f32
+ * (descending; on equal values the lower expert index first), while topk_w
+ * still holds the unbiased probabilities of the chosen experts (divided by
+ * their sum when cfg.renorm).  The selection bias carries no gradient, and
+ * moe_backward needs nothing else: it reads the chosen indices and weights.
+ *   sel_bias  [E] f32 in (required)
+ *   other arguments as for moe_route. */
+moe_status moe_route_balanced(moe_plan plan, const void* x, const void* w_router, const float* bias,
+                              const float* sel_bias, float* probs, int32_t* topk_idx, float* topk_w,
+                              void* stream);
+
+/* The step-end update of the selection bias (same reading as above):
+ * sel_bias[e] += gamma * sign(T k - E counts[e]), i.e. a fixed step down for
+ * experts above the mean load T k / E and up for those below; the sign is
+ * decided exactly in integers and the addition rounds once in f32.
+ *   counts    [E] int32 in (the step's expert loads, e.g. from moe_permute)
+ *   sel_bias  [E] f32 in/out
+ *   gamma     >= 0 and finite, else MOE_ERR_INVALID. */
+moe_status moe_balance_update(moe_plan plan, const int32_t* counts, float* sel_bias, float gamma, void* stream);
+
 /* Group the T*k assignments by expert, stably (expert ascending, then token
  * ascending), and gather the token rows in that order.
  *   topk_idx   [T, k] int32 in: values in [0, E), distinct within a row

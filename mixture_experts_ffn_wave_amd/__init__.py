@@ -10,6 +10,8 @@ from ._lib import (  # noqa: F401
     MoeError,
     lib,
     moe_route,
+    moe_route_balanced,
+    moe_balance_update,
     moe_permute,
     moe_expert_ffn,
     moe_combine,

@@ -62,6 +62,8 @@ SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [c_int32]),
     "moe_version": (ctypes.c_char_p, []),
     "moe_route": (c_int32, [c_void_p] * 8),
+    "moe_route_balanced": (c_int32, [c_void_p] * 9),
+    "moe_balance_update": (c_int32, [c_void_p, c_void_p, c_void_p, c_float, c_void_p]),
     "moe_permute": (c_int32, [c_void_p] * 9 + [c_size_t, c_void_p]),
     "moe_expert_ffn": (c_int32, [c_void_p, ctypes.POINTER(MoeFfnArgs), c_void_p, c_size_t, c_void_p]),
     "moe_combine": (c_int32, [c_void_p] * 7),
@@ -188,6 +190,25 @@ def moe_route(plan, x, w_router, bias, probs, topk_idx, topk_w, stream=None):
     st = lib().moe_route(plan.handle, _ptr(x), _ptr(w_router), _ptr(bias) if plan.has_bias else None,
                          _ptr(probs), _ptr(topk_idx), _ptr(topk_w), _stream(stream))
     _check("moe_route", st)
+
+
+def moe_route_balanced(plan, x, w_router, bias, sel_bias, probs, topk_idx, topk_w, stream=None):
+    T, d, E, k, dt = plan.T, plan.d, plan.E, plan.k, plan.dtype
+    _need(x, "x", (T, d), dt); _need(w_router, "w_router", (E, d), dt)
+    _need(sel_bias, "sel_bias", (E,), torch.float32)
+    _need(probs, "probs", (T, E), torch.float32)
+    _need(topk_idx, "topk_idx", (T, k), torch.int32); _need(topk_w, "topk_w", (T, k), torch.float32)
+    if plan.has_bias:
+        _need(bias, "bias", (E,), torch.float32)
+    st = lib().moe_route_balanced(plan.handle, _ptr(x), _ptr(w_router), _ptr(bias) if plan.has_bias else None,
+                                  _ptr(sel_bias), _ptr(probs), _ptr(topk_idx), _ptr(topk_w), _stream(stream))
+    _check("moe_route_balanced", st)
+
+
+def moe_balance_update(plan, counts, sel_bias, gamma, stream=None):
+    _need(counts, "counts", (plan.E,), torch.int32); _need(sel_bias, "sel_bias", (plan.E,), torch.float32)
+    st = lib().moe_balance_update(plan.handle, _ptr(counts), _ptr(sel_bias), c_float(gamma), _stream(stream))
+    _check("moe_balance_update", st)
 
 
 def moe_permute(plan, topk_idx, x, counts, offsets, perm_token, inv_perm, x_perm, ws, stream=None):

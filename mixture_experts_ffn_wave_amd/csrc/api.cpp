@@ -28,7 +28,7 @@ const char* kKernelNames =
     "gemm_down_dgrad_swiglu,gemm_wgrad_down,gemm_gate_up_dgrad,gemm_wgrad_gate_up,"
     "gemm_down_dgrad_swiglu_shared,gemm_wgrad_down_shared,gemm_wgrad_gate_up_shared,"
     "gemm_gate_up_dgrad_shared,stack_router,gemm_router_dx,unpermute,gemm_wgrad_router,router_reduce,aux,"
-    "wgrad_reduce,mx_quantize,router_bwd_small";
+    "wgrad_reduce,mx_quantize,router_bwd_small,balance_update";
 
 }  // namespace
 
@@ -457,6 +457,28 @@ moe_status moe_route(moe_plan p, const void* x, const void* w_router, const floa
               p->T, p->d, p->E, p->k, p->cfg.renorm};
   Probe pr(p, "route", s);
   return hip_status(launch_route(p->dt, a, s));
+}
+
+moe_status moe_route_balanced(moe_plan p, const void* x, const void* w_router, const float* bias,
+                              const float* sel_bias, float* probs, int32_t* topk_idx, float* topk_w, void* stream) {
+  if (!p) return MOE_ERR_NULL;
+  if (p->T == 0) return MOE_OK;
+  if (!x || !w_router || !sel_bias || !probs || !topk_idx || !topk_w) return MOE_ERR_NULL;
+  if (p->cfg.has_router_bias && !bias) return MOE_ERR_NULL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RouteArgs a{x, w_router, p->cfg.has_router_bias ? bias : nullptr, probs, topk_idx, topk_w,
+              p->T, p->d, p->E, p->k, p->cfg.renorm, sel_bias};
+  Probe pr(p, "route", s);
+  return hip_status(launch_route(p->dt, a, s));
+}
+
+moe_status moe_balance_update(moe_plan p, const int32_t* counts, float* sel_bias, float gamma, void* stream) {
+  if (!p) return MOE_ERR_NULL;
+  if (!counts || !sel_bias) return MOE_ERR_NULL;
+  if (!(gamma >= 0.0f) || !(gamma < INFINITY)) return MOE_ERR_INVALID;   // also rejects NaN
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Probe pr(p, "balance_update", s);
+  return hip_status(launch_balance_update(counts, sel_bias, p->T, p->E, p->k, gamma, s));
 }
 
 // ---------------------------------------------------------------- permute --

@@ -22,8 +22,12 @@ struct RouteArgs {
   float* wts;           // [T, k]
   int64_t T;
   int d, E, k, renorm;
+  const float* sel_bias = nullptr;  // [E] or nullptr: experts chosen on probs + sel_bias (weights unbiased)
 };
 hipError_t launch_route(int dt, const RouteArgs& a, hipStream_t s);
+// sel_bias[e] += gamma * sign(T k - E counts[e]) (aux-loss-free balancing update), E <= 256
+hipError_t launch_balance_update(const int32_t* counts, float* sel_bias, int64_t T, int E, int k, float gamma,
+                                 hipStream_t s);
 
 // ------------------------------------------------------------- permute --
 constexpr int kHistTokens = 256;    // tokens per histogram block

@@ -23,24 +23,31 @@ namespace {
 constexpr int KB = 128;
 constexpr int LROW = KB + 16;
 
-// The bias (zeros without one) staged in LDS at kernel start by threads
-// 0 .. 32 NSUB - 1, so that the epilogue reads it without global round trips.
+// The logit bias and the selection bias (zeros without them) staged in LDS
+// at kernel start by threads 0 .. 32 NSUB - 1, so that the epilogue reads
+// them without global round trips.
 template <int NSUB>
-__device__ __forceinline__ void stage_bias(float* s_bias, const RouteArgs& a) {
+__device__ __forceinline__ void stage_bias(float* s_bias, float* s_sel, const RouteArgs& a) {
   const int i = threadIdx.x;
-  if (i < 32 * NSUB) s_bias[i] = (a.bias && i < a.E) ? a.bias[i] : 0.0f;
+  if (i < 32 * NSUB) {
+    s_bias[i] = (a.bias && i < a.E) ? a.bias[i] : 0.0f;
+    s_sel[i] = (a.sel_bias && i < a.E) ? a.sel_bias[i] : 0.0f;
+  }
 }
 
 // Softmax, probabilities, top-k and weights of the 32 tokens tb.. tb+31 whose
 // logits sit in acc (lane l: token tb + l % 32, experts 32 s + 8 (r/4) +
-// 4 (l/32) + r%4 in register r of acc[s]); s_bias as staged by stage_bias.
-// s_wts: kWtsLds floats of LDS owned by this wave, where the chosen
-// probabilities wait for their sum when they are renormalised.
+// 4 (l/32) + r%4 in register r of acc[s]); s_bias / s_sel as staged by
+// stage_bias.  s_wts: kWtsLds floats of LDS owned by this wave, where the
+// chosen probabilities wait for their sum when they are renormalised.
+// With a selection bias (aux-loss-free balancing, KohakUwULLM README, "Key
+// features") the experts are ranked on probability + bias instead of on the
+// logits; the weights are the unbiased probabilities either way.
 constexpr int kWtsStride = 65;                 // 64 slots per token, odd stride: no bank conflicts
 constexpr int kWtsLds = 32 * kWtsStride;
 template <int NSUB>
 __device__ __forceinline__ void route_epilogue(const f32x16 (&acc)[NSUB], int64_t tb, int lane, const RouteArgs& a,
-                                               const float* s_bias, float* s_wts) {
+                                               const float* s_bias, const float* s_sel, float* s_wts) {
   const int h = lane >> 5;
   const int64_t t = tb + (lane & 31);
   const bool tv = t < a.T;
@@ -67,6 +74,17 @@ __device__ __forceinline__ void route_epilogue(const f32x16 (&acc)[NSUB], int64_
       if (e < E) sum += expf(z[s][r] - m);
     }
   sum += __shfl_xor(sum, 32, 64);
+  const bool sel = a.sel_bias != nullptr;
+  if (sel) {
+    // z now holds the probabilities (padded experts stay -inf)
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int e = s * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (e < E) z[s][r] = expf(z[s][r] - m) / sum;
+      }
+  }
 
   if (tv) {
     float* prow = a.probs + t * E;
@@ -78,7 +96,7 @@ __device__ __forceinline__ void route_epilogue(const f32x16 (&acc)[NSUB], int64_
         if (e0 >= E) continue;
         float p[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = expf(z[s][4 * q + i] - m) / sum;
+        for (int i = 0; i < 4; ++i) p[i] = sel ? z[s][4 * q + i] : expf(z[s][4 * q + i] - m) / sum;
         if ((E & 3) == 0) {
           *reinterpret_cast<f32x4*>(prow + e0) = (f32x4){p[0], p[1], p[2], p[3]};
         } else {
@@ -94,22 +112,28 @@ __device__ __forceinline__ void route_epilogue(const f32x16 (&acc)[NSUB], int64_
   for (int s = 0; s < NSUB; ++s) taken[s] = 0u;
   float psum = 0.0f;
   for (int j = 0; j < a.k; ++j) {
-    float bv = -INFINITY;
+    float bv = -INFINITY, bp = 0.0f;               // best ranking value, and its probability (sel)
     int be = -1;
 #pragma unroll
     for (int s = 0; s < NSUB; ++s)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int e = s * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (e < E && !((taken[s] >> r) & 1u) && (be < 0 || z[s][r] > bv)) {
-          bv = z[s][r];
-          be = e;
+        if (e < E && !((taken[s] >> r) & 1u)) {
+          const float v = sel ? z[s][r] + s_sel[e] : z[s][r];
+          if (be < 0 || v > bv) {
+            bv = v;
+            bp = z[s][r];
+            be = e;
+          }
         }
       }
     const float pv = __shfl_xor(bv, 32, 64);
+    const float pp = __shfl_xor(bp, 32, 64);
     const int pe = __shfl_xor(be, 32, 64);
     const bool partner = (be < 0) || (pe >= 0 && (pv > bv || (pv == bv && pe < be)));
     const float wv = partner ? pv : bv;
+    const float wp = partner ? pp : bp;
     const int we = partner ? pe : be;
     if (!partner) {
       const int s = we >> 5, w5 = we & 31;
@@ -118,7 +142,7 @@ __device__ __forceinline__ void route_epilogue(const f32x16 (&acc)[NSUB], int64_
       for (int ss = 0; ss < NSUB; ++ss)
         if (ss == s) taken[ss] |= 1u << r;
     }
-    const float pj = expf(wv - m) / sum;
+    const float pj = sel ? wp : expf(wv - m) / sum;
     psum += pj;
     if (tv && h == 0) {
       a.idx[t * a.k + j] = we;
@@ -146,9 +170,9 @@ __global__ void __launch_bounds__(WAVES * 64) route_kernel(RouteArgs a) {
   char* lx = lds;
   char* lw = lds + TB * LROW;
   static_assert(WAVES * kWtsLds * 4 <= (TB + EP) * LROW, "weights scratch fits in the tiles' LDS");
-  __shared__ float s_bias[EP];
+  __shared__ float s_bias[EP], s_sel[EP];
   static_assert(EP <= NTH, "bias staged by one thread per expert");
-  stage_bias<NSUB>(s_bias, a);                // visible after the K loop's first barrier
+  stage_bias<NSUB>(s_bias, s_sel, a);         // visible after the K loop's first barrier
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t t0 = (int64_t)blockIdx.x * TB;
@@ -225,7 +249,7 @@ __global__ void __launch_bounds__(WAVES * 64) route_kernel(RouteArgs a) {
   }
 
   __syncthreads();                            // tiles free for the weights scratch (also covers an empty K loop)
-  route_epilogue<NSUB>(acc, t0 + wave * 32, lane, a, s_bias, reinterpret_cast<float*>(lds) + wave * kWtsLds);
+  route_epilogue<NSUB>(acc, t0 + wave * 32, lane, a, s_bias, s_sel, reinterpret_cast<float*>(lds) + wave * kWtsLds);
 }
 
 // Few experts (E <= 64): 32 tokens per workgroup of KW waves that split the K
@@ -246,9 +270,9 @@ __global__ void __launch_bounds__(KW * 64) route_ksplit_kernel(RouteArgs a) {
   constexpr int RED = (KW - 1) * NSUB * 16 * 64 * 4;
   static_assert(RED <= KW * WREG && kWtsLds * 4 <= KW * WREG, "partial logits and weights scratch fit in the tiles' LDS");
   __shared__ __attribute__((aligned(16))) char lds[KW * WREG];
-  __shared__ float s_bias[EP];
+  __shared__ float s_bias[EP], s_sel[EP];
   static_assert(EP <= KW * 64, "bias staged by one thread per expert");
-  stage_bias<NSUB>(s_bias, a);
+  stage_bias<NSUB>(s_bias, s_sel, a);
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   char* lx = lds + wave * WREG;
@@ -341,7 +365,7 @@ __global__ void __launch_bounds__(KW * 64) route_ksplit_kernel(RouteArgs a) {
       for (int s = 0; s < NSUB; ++s)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[s][r] += red[(((w - 1) * NSUB + s) * 16 + r) * 64 + lane];
-    route_epilogue<NSUB>(acc, t0, lane, a, s_bias, red);      // (partials consumed: LDS reused)
+    route_epilogue<NSUB>(acc, t0, lane, a, s_bias, s_sel, red);   // (partials consumed: LDS reused)
   }
 }
 
@@ -371,7 +395,25 @@ hipError_t launch_route_dt(const RouteArgs& a, hipStream_t s) {
   return launch_route_t<T, 8, 4>(a, s);
 }
 
+// Aux-loss-free balancing update, one thread per expert: the sign of
+// (mean load - load) decided exactly in integers, then one f32 addition.
+__global__ void __launch_bounds__(256) balance_update_kernel(const int32_t* counts, float* sel_bias, int64_t T,
+                                                             int E, int k, float gamma) {
+  const int e = threadIdx.x;
+  if (e >= E) return;
+  const int64_t diff = T * k - (int64_t)E * counts[e];
+  const float sgn = diff > 0 ? 1.0f : (diff < 0 ? -1.0f : 0.0f);
+  sel_bias[e] = sel_bias[e] + gamma * sgn;
+}
+
 }  // namespace
+
+hipError_t launch_balance_update(const int32_t* counts, float* sel_bias, int64_t T, int E, int k, float gamma,
+                                 hipStream_t s) {
+  if (E < 1 || E > 256) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(balance_update_kernel, dim3(1), dim3(256), 0, s, counts, sel_bias, T, E, k, gamma);
+  return hipGetLastError();
+}
 
 hipError_t launch_route(int dt, const RouteArgs& a, hipStream_t s) {
   switch (dt) {

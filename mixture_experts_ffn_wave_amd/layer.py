@@ -50,6 +50,21 @@ class MoELayer:
         self.aux_out = torch.zeros(L.ctypes.sizeof(L.MoeAuxScalars), dtype=torch.uint8, device=dev)
         self.ws = torch.empty(max(p.workspace_bytes(), 256), dtype=torch.uint8, device=dev)
         self.params = None
+        self.sel_bias = None      # aux-loss-free balancing: set by enable_balancing()
+        self.balance_gamma = 0.0
+
+    def enable_balancing(self, sel_bias=None, gamma=0.0):
+        """Route with a per-expert selection bias (aux-loss-free balancing):
+        zeros, or the given [E] f32 device tensor, which the layer then owns.
+        With gamma > 0, step() ends with the bias update from the step's loads."""
+        E = self.plan.E
+        self.sel_bias = sel_bias if sel_bias is not None else torch.zeros(E, dtype=torch.float32,
+                                                                          device=self.probs.device)
+        self.balance_gamma = float(gamma)
+
+    def update_balance(self, gamma, stream=None):
+        """Step-end update of the selection bias from this step's counts."""
+        L.moe_balance_update(self.plan, self.counts, self.sel_bias, gamma, stream)
 
     # -------------------------------------------------------------- forward
     def set_params(self, x, w_router, w_gate_up, w_down, bias=None, ws_gate_up=None, ws_down=None):
@@ -58,8 +73,12 @@ class MoELayer:
 
     def route(self, stream=None):
         q = self.params
-        L.moe_route(self.plan, q["x"], q["w_router"], q["bias"], self.probs, self.topk_idx, self.topk_w,
-                    stream)
+        if self.sel_bias is not None:
+            L.moe_route_balanced(self.plan, q["x"], q["w_router"], q["bias"], self.sel_bias, self.probs,
+                                 self.topk_idx, self.topk_w, stream)
+        else:
+            L.moe_route(self.plan, q["x"], q["w_router"], q["bias"], self.probs, self.topk_idx, self.topk_w,
+                        stream)
 
     def dispatch_and_experts(self, stream=None):
         q = self.params
@@ -102,7 +121,10 @@ class MoELayer:
         L.moe_aux_stats(self.plan, self.probs, self.counts, self.f, self.p_mean, self.aux_out, self.ws, stream)
 
     def step(self, dy, stream=None):
-        """One full pass: route, permute, experts, combine, backward, aux statistics."""
+        """One full pass: route, permute, experts, combine, backward, aux
+        statistics (and the balancing bias update when enabled with gamma > 0)."""
         self.forward(stream)
         self.backward(dy, stream)
         self.aux_stats(stream)
+        if self.sel_bias is not None and self.balance_gamma > 0.0:
+            self.update_balance(self.balance_gamma, stream)

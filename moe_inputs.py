@@ -101,6 +101,14 @@ def make_inputs(wl: Workload, seed=None, device="cpu"):
     return out
 
 
+def selection_bias(E, scale, seed=1):
+    """A seeded per-expert selection bias (float32 numpy [E]) for the
+    aux-loss-free balancing router: normal draws times ``scale``, a size
+    comparable to the gaps between routing probabilities (about 1/E)."""
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal(E, dtype=np.float32) * np.float32(scale)).astype(np.float32)
+
+
 def to_f64(t):
     """Exact upcast of a stored tensor to a float64 numpy array (None passes)."""
     if t is None:

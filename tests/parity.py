@@ -69,11 +69,12 @@ def to_np(t):
     return t.to(torch.float64).numpy()
 
 
-def gpu_run(wl, inp, routing=None, intermediates=False):
+def gpu_run(wl, inp, routing=None, intermediates=False, sel_bias=None):
     """One fwd+bwd step on cuda:0.  ``routing`` (probs, idx, w as numpy) replaces
     the router's outputs when given (then moe_route is not called).
     ``intermediates`` also returns what the backward left in the workspace
-    (dy_perm, dgu, dx_perm and, with shared experts, dgu_shared, dx_shared)."""
+    (dy_perm, dgu, dx_perm and, with shared experts, dgu_shared, dx_shared).
+    ``sel_bias`` (numpy [E]) routes with aux-loss-free balancing."""
     from mixture_experts_ffn_wave_amd import MoELayer, decode_aux
     b = inp.get("bias")
     plan = plan_for(wl, b is not None)
@@ -82,6 +83,8 @@ def gpu_run(wl, inp, routing=None, intermediates=False):
     layer.set_params(dev["x"], dev["w_router"], dev["w_gate_up"], dev["w_down"],
                      bias=(dev["bias"].float() if b is not None else None),
                      ws_gate_up=dev.get("ws_gate_up"), ws_down=dev.get("ws_down"))
+    if sel_bias is not None:
+        layer.enable_balancing(torch.from_numpy(np.asarray(sel_bias, dtype=np.float32)).cuda())
     if routing is None:
         layer.forward()
     else:
@@ -114,11 +117,12 @@ def storage_rounding(wl):
     return lambda a, kind: O.round_to_format(a, "f32" if kind == "f32" else wl.dtype)
 
 
-def oracle_run(wl, f64, store=None, quant=None):
+def oracle_run(wl, f64, store=None, quant=None, sel_bias=None):
     b = f64.get("bias")
     fwd = O.layer_forward(f64["x"], f64["w_router"], f64["w_gate_up"], f64["w_down"], top_k=wl.k,
                           renorm=wl.renorm, bias=b, ws_gate_up=f64.get("ws_gate_up"),
-                          ws_down=f64.get("ws_down"), store=store, quant=quant)
+                          ws_down=f64.get("ws_down"), store=store, quant=quant,
+                          sel_bias=None if sel_bias is None else np.asarray(sel_bias, dtype=np.float64))
     bwd = O.layer_backward(fwd, f64["dy"], aux_coef=wl.aux_coef, quant=quant)
     st = O.aux_statistics(fwd["p"], fwd["counts"], wl.k)
     return fwd, bwd, st
@@ -164,8 +168,9 @@ def check_close(name, got, ref, c, dtype="f32", ulps=0.5, rms_floor=0.0):
 
 def compare_routing(wl, gpu, fwd):
     """Returns True when the GPU chose exactly the oracle's routing for every
-    token; asserts that any difference is an allowed near-tie."""
-    z = fwd["z"]
+    token; asserts that any difference is an allowed near-tie.  The ranked
+    values are the logits, or probability + selection bias when balancing."""
+    z = fwd["z"] if fwd.get("sel_bias") is None else O.balanced_selection_scores(fwd["p"], fwd["sel_bias"])
     k, E = wl.k, wl.E
     assert np.max(np.abs(gpu["probs"] - fwd["p"])) <= PROB_ATOL, "router probabilities"
     gi = gpu["topk_idx"]
@@ -350,7 +355,7 @@ def compare_mx_stepwise(wl, gpu, fwd, f64, st):
     compare_stats(gpu, st)
 
 
-def full_parity(wl, inp=None, mx_diagnostic=True):
+def full_parity(wl, inp=None, mx_diagnostic=True, sel_bias=None):
     """The whole chain on the GPU against the oracle.  When a near-tie made
     the GPU pick a different (valid) routing, the downstream calls are run a
     second time from the oracle's routing so every later tensor is compared
@@ -366,12 +371,12 @@ def full_parity(wl, inp=None, mx_diagnostic=True):
     f64 = oracle_inputs(inp)
     say(f"[parity] {wl.name}: {MI.describe(wl)} -- GPU chain")
     mx = wl.expert_dtype == "mxfp8"
-    gpu = gpu_run(wl, inp, intermediates=mx)
+    gpu = gpu_run(wl, inp, intermediates=mx, sel_bias=sel_bias)
     rounded = wl.dtype == "bf16" or mx
     say(f"[parity] {wl.name}: oracle" + (" (bf16 storage rounding)" if rounded else "") +
         (" (MX-quantised expert GEMM operands)" if mx else ""))
     fwd, bwd, st = oracle_run(wl, f64, storage_rounding(wl) if rounded else None,
-                              quant=O.mx_fake_quant if mx else None)
+                              quant=O.mx_fake_quant if mx else None, sel_bias=sel_bias)
     identical = compare_routing(wl, gpu, fwd)
     if not identical:
         say(f"[parity] {wl.name}: near-tie routing differs; rerunning downstream from the oracle routing")
@@ -402,7 +407,7 @@ def full_parity(wl, inp=None, mx_diagnostic=True):
             " ".join(f"{n}={r:.4f}" for n, r in ex.items()))
     if rounded and (mx_diagnostic or not mx):
         # distance from the exact layer, for the record (not asserted)
-        xf, xb, xs = oracle_run(wl, f64)
+        xf, xb, xs = oracle_run(wl, f64, sel_bias=sel_bias)
         REPORT.clear()
         STRICT[0] = False
         try:

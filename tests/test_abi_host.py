@@ -147,7 +147,15 @@ def test_calls_reject_bad_arguments_before_any_launch():
     # a plan with a bias requires the bias pointer
     pb = L.Plan(512, 256, 8, 2, 128, has_router_bias=True)
     assert lib.moe_route(pb.handle, fake, fake, nul, fake, fake, fake, nul) == MOE_ERR_NULL
+    assert lib.moe_route_balanced(pb.handle, fake, fake, nul, fake, fake, fake, fake, nul) == MOE_ERR_NULL
     pb.close()
+    # balanced routing: the selection bias is required; the update checks gamma
+    assert lib.moe_route_balanced(h, fake, fake, nul, nul, fake, fake, fake, nul) == MOE_ERR_NULL
+    assert lib.moe_route_balanced(None, fake, fake, nul, fake, fake, fake, fake, nul) == MOE_ERR_NULL
+    assert lib.moe_balance_update(h, nul, fake, ctypes.c_float(0.01), nul) == MOE_ERR_NULL
+    assert lib.moe_balance_update(h, fake, nul, ctypes.c_float(0.01), nul) == MOE_ERR_NULL
+    for bad in (float("nan"), float("inf"), -0.5):
+        assert lib.moe_balance_update(h, fake, fake, ctypes.c_float(bad), nul) == MOE_ERR_INVALID
     p.close()
 
 
@@ -168,6 +176,7 @@ def test_empty_batch_route_and_combine_are_no_ops():
     lib = L.lib()
     # T = 0: nothing to do, nothing launched, pointers may be NULL
     assert lib.moe_route(p.handle, None, None, None, None, None, None, None) == MOE_OK
+    assert lib.moe_route_balanced(p.handle, None, None, None, None, None, None, None, None) == MOE_OK
     assert lib.moe_combine(p.handle, None, None, None, None, None, None) == MOE_OK
     p.close()
 
