@@ -35,6 +35,7 @@ from .moe_oracle import (  # noqa: F401
     expert_gate_up_backward_step,
     router_backward,
     aux_statistics,
+    real_token_counts,
     layer_forward,
     layer_backward,
     layer_loss,

@@ -196,7 +196,15 @@ def combine(y_perm, inv, w, y_shared=None):
 
 # ---------------------------------------------------------- aux statistics ---
 
-def aux_statistics(p, counts, top_k):
+def real_token_counts(idx, mask, n_experts):
+    """Assignments per expert among the real tokens (mask 1) only, and the
+    number of real tokens."""
+    m = np.asarray(mask, dtype=np.int64)
+    sel = idx[m != 0]
+    return np.bincount(sel.ravel(), minlength=n_experts).astype(np.int64), int(m.sum())
+
+
+def aux_statistics(p, counts, top_k, mask=None):
     """Load-balancing statistic and router metrics.
 
     KochiLLM "Architecture": the term 4 * sum_i f_i * p_i for its 4 experts;
@@ -204,15 +212,25 @@ def aux_statistics(p, counts, top_k):
     count spread (coefficient of variation), mean routing entropy and the
     number of idle experts.  f_e = count_e / (T k), P_e = mean_t p_te,
     aux_raw = sum_e f_e P_e, aux = E * aux_raw.
+
+    ``mask`` ([T], 1 = real token, 0 = filler): the spark-gpt MoE paragraph
+    computes the statistic over real (non-filler) tokens only; then T is the
+    number of real tokens, ``counts`` must be their assignments
+    (real_token_counts), P_e averages p over the real tokens and every
+    metric is taken over them.  No real token: every value is 0.
     """
     T, E = p.shape
+    if mask is not None:
+        m = np.asarray(mask, dtype=np.float64)
+        p = p[m != 0]
+        T = p.shape[0]
     counts = np.asarray(counts, dtype=np.float64)
-    f = counts / (T * top_k)
-    p_mean = p.mean(axis=0)
+    f = counts / (T * top_k) if T > 0 else np.zeros(E)
+    p_mean = p.mean(axis=0) if T > 0 else np.zeros(E)
     aux_raw = float((f * p_mean).sum())
     with np.errstate(divide="ignore", invalid="ignore"):
         plogp = np.where(p > 0, p * np.log(np.where(p > 0, p, 1.0)), 0.0)
-    entropy = float((-plogp.sum(axis=1)).mean())
+    entropy = float((-plogp.sum(axis=1)).mean()) if T > 0 else 0.0
     mean_c = counts.mean()
     cv = float(counts.std() / mean_c) if mean_c > 0 else 0.0
     return {
@@ -339,7 +357,7 @@ def expert_gate_up_backward_step(dgu, rows, w_gate_up_e, quant=None):
     return q(dgu, 1) @ q(w_gate_up_e, 0), q(dgu, 0).T @ q(rows, 0)
 
 
-def router_backward(dy, y_perm, inv, p, idx, w, renorm, counts, aux_coef=0.0, store=None):
+def router_backward(dy, y_perm, inv, p, idx, w, renorm, counts, aux_coef=0.0, store=None, mask=None):
     """Gradient of L = <dy, y> + aux_coef * aux with respect to the router
     logits, given the expert output rows Y_perm the combine weighted.
 
@@ -347,6 +365,9 @@ def router_backward(dy, y_perm, inv, p, idx, w, renorm, counts, aux_coef=0.0, st
     renormalisation w = p_sel / S, so dL/dp_sel = (g - <w, g>) / S; the
     balancing term adds aux_coef * E * f_e / T to every p_te (f_e is a count,
     no gradient); the softmax Jacobian then gives dz = p * (dp - <p, dp>).
+    With ``mask`` the statistic covers the real tokens only (aux_statistics):
+    ``counts`` are theirs, T is their number, and only real tokens' p_te get
+    the balancing term.
     Returns (g [T, k], dz [T, E] as stored, kind "f32")."""
     st = store or _no_store
     T, E = p.shape
@@ -361,12 +382,19 @@ def router_backward(dy, y_perm, inv, p, idx, w, renorm, counts, aux_coef=0.0, st
     dp = np.zeros_like(p)
     np.put_along_axis(dp, idx, dp_sel, axis=1)
     if aux_coef != 0.0:
-        f = np.asarray(counts, dtype=np.float64) / (T * k)
-        dp = dp + aux_coef * E * f[None, :] / T
+        if mask is None:
+            f = np.asarray(counts, dtype=np.float64) / (T * k)
+            dp = dp + aux_coef * E * f[None, :] / T
+        else:
+            m = np.asarray(mask, dtype=np.float64)
+            Tr = float(m.sum())
+            if Tr > 0:
+                f = np.asarray(counts, dtype=np.float64) / (Tr * k)
+                dp = dp + m[:, None] * (aux_coef * E * f[None, :] / Tr)
     return gsc, st(p * (dp - (p * dp).sum(axis=1, keepdims=True)), "f32")
 
 
-def layer_backward(fwd, dy, *, aux_coef=0.0, quant=None):
+def layer_backward(fwd, dy, *, aux_coef=0.0, quant=None, mask=None):
     """Gradients of L = <dy, y> + aux_coef * aux with respect to x and every
     weight, by the chain rule through the forward of ``layer_forward``.
 
@@ -421,8 +449,10 @@ def layer_backward(fwd, dy, *, aux_coef=0.0, quant=None):
         grads["dws_gate_up"] = dws_gu
         grads["dws_down"] = dws_d
 
-    # router
-    gsc, dz = router_backward(dy, fwd["y_perm"], inv, p, idx, w, fwd["renorm"], counts, aux_coef, st)
+    # router (the balancing statistic over the real tokens when masked)
+    if mask is not None:
+        counts, _ = real_token_counts(idx, mask, E)
+    gsc, dz = router_backward(dy, fwd["y_perm"], inv, p, idx, w, fwd["renorm"], counts, aux_coef, st, mask)
     grads["dw_router"] = dz.T @ x
     grads["dbias"] = dz.sum(axis=0)
     dx += dz @ w_r
@@ -434,8 +464,12 @@ def layer_backward(fwd, dy, *, aux_coef=0.0, quant=None):
     return grads
 
 
-def layer_loss(fwd, dy, aux_coef=0.0):
+def layer_loss(fwd, dy, aux_coef=0.0, mask=None):
     """L = <dy, y> + aux_coef * aux  (the scalar whose gradient layer_backward
     returns; used by the finite-difference pins)."""
-    st = aux_statistics(fwd["p"], fwd["counts"], fwd["top_k"])
+    if mask is None:
+        st = aux_statistics(fwd["p"], fwd["counts"], fwd["top_k"])
+    else:
+        rc, _ = real_token_counts(fwd["idx"], mask, fwd["p"].shape[1])
+        st = aux_statistics(fwd["p"], rc, fwd["top_k"], mask)
     return float((dy * fwd["y"]).sum()) + aux_coef * st["aux"]

@@ -421,6 +421,80 @@ def test_backward_matches_central_differences(renorm, aux_coef, n_shared):
             assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (pname, pos, fd, an)
 
 
+@pytest.mark.parametrize("renorm", [True, False])
+def test_masked_statistic_gradient_matches_central_differences(renorm):
+    # the balancing statistic over the real tokens only: its gradient (only
+    # real tokens' probabilities get the term) against finite differences of
+    # the masked loss
+    k, aux_coef = 2, 0.5
+    L = _fd_case(renorm, aux_coef, 0, seed=23)
+    T = L["x"].shape[0]
+    mask = np.ones(T, dtype=np.int64)
+    mask[1::3] = 0
+    fwd = fwd_of(L, k, renorm)
+    g = O.layer_backward(fwd, L["dy"], aux_coef=aux_coef, mask=mask)
+    rng = np.random.default_rng(1)
+    h = 1e-6
+    for pname, gname in {"x": "dx", "w_router": "dw_router"}.items():
+        arr = L[pname]
+        for fi in rng.choice(arr.size, size=min(arr.size, 48), replace=False):
+            pos = np.unravel_index(fi, arr.shape)
+            orig = arr[pos]
+            arr[pos] = orig + h
+            lp = O.layer_loss(fwd_of(L, k, renorm), L["dy"], aux_coef, mask)
+            arr[pos] = orig - h
+            lm = O.layer_loss(fwd_of(L, k, renorm), L["dy"], aux_coef, mask)
+            arr[pos] = orig
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - g[gname][pos]) <= 1e-6 * max(1.0, abs(g[gname][pos])), (pname, pos)
+
+
+def test_masked_statistic_ignores_fillers():
+    # fillers change nothing: the statistic of real tokens plus arbitrary
+    # fillers under the mask equals the plain statistic of the real tokens
+    rng = np.random.default_rng(9)
+    T, E, k = 40, 6, 2
+    p = O.softmax_rows(rng.standard_normal((T, E)) * 2)
+    idx = O.topk_select(np.log(p), k)
+    mask = (rng.random(T) < 0.6).astype(np.int64)
+    rc, Tr = O.real_token_counts(idx, mask, E)
+    assert Tr == mask.sum() and rc.sum() == Tr * k
+    ref = O.aux_statistics(p[mask == 1], np.bincount(idx[mask == 1].ravel(), minlength=E), k)
+    got = O.aux_statistics(p, rc, k, mask)
+    for key in ("aux", "aux_raw", "entropy_mean", "count_cv", "count_min", "count_max", "n_unused"):
+        assert abs(got[key] - ref[key]) < 1e-14, key
+    assert np.allclose(got["f"], ref["f"], rtol=0, atol=1e-15) and np.allclose(got["p_mean"], ref["p_mean"],
+                                                                                rtol=0, atol=1e-15)
+    # all real: the unmasked statistic; none real: all zero
+    full = O.aux_statistics(p, np.bincount(idx.ravel(), minlength=E), k)
+    allm = O.aux_statistics(p, O.real_token_counts(idx, np.ones(T), E)[0], k, np.ones(T))
+    assert abs(full["aux"] - allm["aux"]) < 1e-15
+    none = O.aux_statistics(p, np.zeros(E), k, np.zeros(T))
+    assert none["aux"] == 0.0 and none["entropy_mean"] == 0.0 and none["count_cv"] == 0.0
+
+
+def test_masked_statistic_hand_values():
+    # T = 4 tokens, 2 real (tokens 0 and 2), E = 2, k = 1
+    p = np.array([[0.75, 0.25], [0.5, 0.5], [0.25, 0.75], [1.0, 0.0]])
+    idx = np.array([[0], [0], [1], [0]])
+    mask = np.array([1, 0, 1, 0])
+    rc, Tr = O.real_token_counts(idx, mask, 2)
+    assert rc.tolist() == [1, 1] and Tr == 2
+    st = O.aux_statistics(p, rc, 1, mask)
+    # f = (1/2, 1/2), P = ((0.75+0.25)/2, (0.25+0.75)/2) = (1/2, 1/2): aux_raw = 1/2, aux = 1
+    assert st["aux_raw"] == 0.5 and st["aux"] == 1.0
+    # gradient term only on real rows: aux_coef * E * f_e / T_r = 1 * 2 * 0.5 / 2 = 0.5
+    _, dz = O.router_backward(np.zeros((4, 1)), np.zeros((4, 1)), np.arange(4).reshape(4, 1), p, idx,
+                              np.ones((4, 1)), False, rc, aux_coef=1.0, mask=mask)
+    # dp = 0.5 on both experts of a real row: dz = p * (dp - <p, dp>) = 0 there; 0 on fillers
+    assert np.all(dz == 0.0)
+    rc2 = np.array([2, 0])
+    _, dz = O.router_backward(np.zeros((4, 1)), np.zeros((4, 1)), np.arange(4).reshape(4, 1), p, idx,
+                              np.ones((4, 1)), False, rc2, aux_coef=1.0, mask=mask)
+    # dp = (1, 0) on real rows: dz = p * ((1, 0) - p_0) -> token 0: (0.75 * 0.25, -0.25 * 0.75)
+    assert np.allclose(dz[0], [0.1875, -0.1875], rtol=0, atol=1e-15) and np.all(dz[1] == 0) and np.all(dz[3] == 0)
+
+
 def test_router_gradient_invariants():
     L = _fd_case(True, 0.0, 0, seed=300)
     fwd = fwd_of(L, 2, True)
