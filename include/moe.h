@@ -209,6 +209,11 @@ typedef struct {
   const void* ws_down;      /* [Ns, d, Is] */
   const void* gu_shared;    /* [T, 2 Ns Is] */
   const void* h_shared;     /* [T, Ns Is] */
+  /* Balancing statistic over real tokens only (spark-gpt MoE paragraph):
+   * real_mask [T] int32 (0 = filler) and real_counts [E+1] from
+   * moe_aux_stats_masked of the same step; NULL real_mask = every token. */
+  const int32_t* real_mask;
+  const int32_t* real_counts;
 } moe_saved;
 
 /* Gradient outputs (act dtype unless noted).  Every weight gradient is fully
@@ -253,6 +258,21 @@ typedef struct {
 moe_status moe_aux_stats(moe_plan plan, const float* probs, const int32_t* counts, float* f,
                          float* p_mean, moe_aux_scalars* out, void* ws, size_t ws_bytes,
                          void* stream);
+
+/* The same statistic over the real tokens only, fillers (padding) left out
+ * (spark-gpt README, MoE paragraph: the statistic is computed over real,
+ * non-filler tokens).  With T_r = the number of tokens whose mask is non-zero:
+ * real_counts[e] = assignments of real tokens to e, real_counts[E] = T_r,
+ * f_e = real_counts[e] / (T_r k), P_e = the mean of probs[t, e] over real t,
+ * and every metric taken over the real tokens; T_r = 0 gives zeros.
+ * moe_backward applies the statistic's gradient to real tokens only when
+ * moe_saved.real_mask and .real_counts are set from this call.
+ *   probs [T, E] f32; topk_idx [T, k] int32; real_mask [T] int32;
+ *   f, p_mean [E] f32 out; real_counts [E+1] int32 out;
+ *   out: one moe_aux_scalars in DEVICE memory. */
+moe_status moe_aux_stats_masked(moe_plan plan, const float* probs, const int32_t* topk_idx,
+                                const int32_t* real_mask, float* f, float* p_mean, int32_t* real_counts,
+                                moe_aux_scalars* out, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- MX-fp8 quantisation ----------------------------------------------- */
 

@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     moe_combine,
     moe_backward,
     moe_aux_stats,
+    moe_aux_stats_masked,
     decode_aux,
     probe_enable,
     probe_read,

@@ -32,7 +32,7 @@ _FFN_FIELDS = ["x_perm", "offsets", "w_gate_up", "w_down", "gu", "h", "y_perm", 
                "ws_down", "gu_shared", "h_shared", "y_shared"]
 _SAVED_FIELDS = ["x", "w_router", "probs", "topk_idx", "topk_w", "counts", "offsets", "inv_perm",
                  "x_perm", "gu", "h", "y_perm", "w_gate_up", "w_down", "ws_gate_up", "ws_down",
-                 "gu_shared", "h_shared"]
+                 "gu_shared", "h_shared", "real_mask", "real_counts"]
 _GRAD_FIELDS = ["dx", "dw_router", "dbias", "dw_gate_up", "dw_down", "dws_gate_up", "dws_down"]
 
 
@@ -70,6 +70,7 @@ SIGNATURES = {
     "moe_backward": (c_int32, [c_void_p, ctypes.POINTER(MoeSaved), c_void_p, ctypes.POINTER(MoeGrads),
                                c_void_p, c_size_t, c_void_p]),
     "moe_aux_stats": (c_int32, [c_void_p] * 7 + [c_size_t, c_void_p]),
+    "moe_aux_stats_masked": (c_int32, [c_void_p] * 9 + [c_size_t, c_void_p]),
     "moe_probe_enable": (c_int32, [c_void_p, ctypes.c_char_p, c_int32]),
     "moe_probe_read": (c_int32, [c_void_p, ctypes.POINTER(c_float), ctypes.POINTER(c_int32)]),
     "moe_kernel_names": (ctypes.c_char_p, []),
@@ -291,6 +292,21 @@ def moe_aux_stats(plan, probs, counts, f, p_mean, out, ws, stream=None):
     st = lib().moe_aux_stats(plan.handle, _ptr(probs), _ptr(counts), _ptr(f), _ptr(p_mean), _ptr(out),
                              _ptr(ws), ws.numel(), _stream(stream))
     _check("moe_aux_stats", st)
+
+
+def moe_aux_stats_masked(plan, probs, topk_idx, real_mask, f, p_mean, real_counts, out, ws, stream=None):
+    """The statistic over real tokens (real_mask [T] int32, 0 = filler);
+    real_counts [E+1] int32 receives their counts and their number."""
+    T, E, k = plan.T, plan.E, plan.k
+    _need(probs, "probs", (T, E), torch.float32); _need(topk_idx, "topk_idx", (T, k), torch.int32)
+    _need(real_mask, "real_mask", (T,), torch.int32)
+    _need(f, "f", (E,), torch.float32); _need(p_mean, "p_mean", (E,), torch.float32)
+    _need(real_counts, "real_counts", (E + 1,), torch.int32)
+    _need(out, "out", (ctypes.sizeof(MoeAuxScalars),), torch.uint8)
+    st = lib().moe_aux_stats_masked(plan.handle, _ptr(probs), _ptr(topk_idx), _ptr(real_mask), _ptr(f),
+                                    _ptr(p_mean), _ptr(real_counts), _ptr(out), _ptr(ws), ws.numel(),
+                                    _stream(stream))
+    _check("moe_aux_stats_masked", st)
 
 
 def decode_aux(out_tensor):

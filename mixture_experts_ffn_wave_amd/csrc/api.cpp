@@ -323,7 +323,8 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
   p->o_dwr_part = take(p->router_small ? (size_t)p->nblk_small * p->E * p->d * 4
                                         : (size_t)p->router_splits * 2 * p->Ep * p->d * 4);
   p->o_dbias_part = take((size_t)(p->router_small ? p->nblk_small : p->nblk_dz) * p->E * 4);
-  p->o_aux_part = take((size_t)(p->nblk_aux > 0 ? p->nblk_aux : 1) * 2 * p->E * 4);
+  // f32 [nblk, 2, E] partials, then (real-token mask) int32 [nblk, E + 1]
+  p->o_aux_part = take((size_t)(p->nblk_aux > 0 ? p->nblk_aux : 1) * (3 * p->E + 1) * 4);
   {
     // one f32 partial buffer, reused by every split weight-gradient GEMM in turn
     size_t part = 0;
@@ -762,6 +763,7 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
       return MOE_ERR_NULL;
     if (p->Ns > 0 && (!sv->ws_gate_up || !sv->ws_down || !sv->gu_shared || !sv->h_shared))
       return MOE_ERR_NULL;
+    if (sv->real_mask && !sv->real_counts) return MOE_ERR_NULL;
   } else if (!sv->w_router || !sv->w_gate_up || !sv->w_down) {
     return MOE_ERR_NULL;
   }
@@ -789,12 +791,12 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
     }
     if (p->router_small) {
       RouterBwdSmallArgs a{g, sv->topk_w, sv->topk_idx, sv->probs, sv->counts, sv->x, dzhl, dwr_part, dbias_part,
-                           p->T, E, Ep, d, k, p->cfg.renorm, p->cfg.aux_coef};
+                           p->T, E, Ep, d, k, p->cfg.renorm, p->cfg.aux_coef, sv->real_mask, sv->real_counts};
       Probe pr(p, "router_bwd_small", s);
       MOE_TRY(launch_router_bwd_small(p->dt, a, s));
     } else {
       RouterDzArgs a{g, sv->topk_w, sv->topk_idx, sv->probs, sv->counts, dzhl, dbias_part,
-                     p->T, E, Ep, k, p->cfg.renorm, p->cfg.aux_coef};
+                     p->T, E, Ep, k, p->cfg.renorm, p->cfg.aux_coef, sv->real_mask, sv->real_counts};
       Probe pr(p, "router_dz", s);
       MOE_TRY(launch_router_dz(p->dt, a, s));
     }
@@ -918,6 +920,26 @@ moe_status moe_aux_stats(moe_plan p, const float* probs, const int32_t* counts, 
   if (st != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   AuxArgs a{probs, counts, f, p_mean, out, reinterpret_cast<float*>(wsp(ws, p->o_aux_part)), p->T, p->E, p->k};
+  Probe pr(p, "aux", s);
+  return hip_status(launch_aux(a, s));
+}
+
+moe_status moe_aux_stats_masked(moe_plan p, const float* probs, const int32_t* topk_idx, const int32_t* real_mask,
+                                float* f, float* p_mean, int32_t* real_counts, moe_aux_scalars* out, void* ws,
+                                size_t ws_bytes, void* stream) {
+  if (!p) return MOE_ERR_NULL;
+  if (!f || !p_mean || !real_counts || !out) return MOE_ERR_NULL;
+  if (p->T > 0 && (!probs || !topk_idx || !real_mask)) return MOE_ERR_NULL;
+  moe_status st = check_ws(p, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* part = reinterpret_cast<float*>(wsp(ws, p->o_aux_part));
+  const int nb = p->nblk_aux > 0 ? p->nblk_aux : 1;
+  AuxArgs a{probs, nullptr, f, p_mean, out, part, p->T, p->E, p->k};
+  a.mask = real_mask;
+  a.idx = topk_idx;
+  a.rcounts = real_counts;
+  a.cpart = reinterpret_cast<int32_t*>(part + (size_t)nb * 2 * p->E);
   Probe pr(p, "aux", s);
   return hip_status(launch_aux(a, s));
 }

@@ -116,9 +116,19 @@ __global__ void __launch_bounds__(NT) combine_bwd_kernel(CombineBwdArgs a) {
   }
 }
 
+// Balancing-term scale aux_coef * E / (T^2 k) (times count_e gives
+// aux_coef * E * f_e / T): over all tokens, or over the real ones (T and the
+// counts those of the real tokens; no real token, no term).
+__device__ __forceinline__ float aux_grad_scale(float aux_coef, int E, int64_t T, int k, const int32_t* mask,
+                                                const int32_t* rcounts) {
+  const float Tn = mask ? (float)rcounts[E] : (float)T;
+  return Tn > 0.0f ? aux_coef * (float)E / (Tn * Tn * (float)k) : 0.0f;
+}
+
 // Router backward for one token per wave.
 //   dp_e  = (selected e = e_j) ? (renorm ? (g_j - sum_i w_i g_i) / S : g_j) : 0
 //   dp_e += aux_coef * E * f_e / T,   f_e = count_e / (T k)
+//           (with a real-token mask: real tokens only, T and counts theirs)
 //   dz_e  = p_e * (dp_e - sum_e' p_e' dp_e')
 // dz is written as a hi/lo pair in the activation dtype (hi = round(dz),
 // lo = round(dz - hi)) so the matrix-core products that consume it keep
@@ -128,12 +138,13 @@ __global__ void __launch_bounds__(NT) router_dz_kernel(RouterDzArgs a) {
   // one wave per token; lane l holds experts l, l+64, l+128, l+192
   __shared__ float s_bias[NT / 64][256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float aux_scale = a.aux_coef * (float)a.E / ((float)a.T * (float)a.T * (float)a.k);
+  const float aux_scale = aux_grad_scale(a.aux_coef, a.E, a.T, a.k, a.mask, a.rcounts);
+  const int32_t* cnt = a.mask ? a.rcounts : a.counts;
   float dp_aux[4], bias_acc[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = lane + 64 * q;
-    dp_aux[q] = (e < a.E) ? aux_scale * (float)a.counts[e] : 0.0f;
+    dp_aux[q] = (e < a.E) ? aux_scale * (float)cnt[e] : 0.0f;
     bias_acc[q] = 0.0f;
   }
   T* dz = static_cast<T*>(a.dz_hl);
@@ -166,9 +177,10 @@ __global__ void __launch_bounds__(NT) router_dz_kernel(RouterDzArgs a) {
     const float S = wave_sum(pj);
     const float wg = wave_sum(wj * gj);
     const float dps = a.renorm ? (gj - wg) / S : gj;
+    const bool real = !a.mask || a.mask[t] != 0;       // fillers get no balancing term
     float dp[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) dp[q] = dp_aux[q];
+    for (int q = 0; q < 4; ++q) dp[q] = real ? dp_aux[q] : 0.0f;
     // scatter the k slot gradients to the lanes that hold their experts
     for (int j = 0; j < a.k; ++j) {
       const int eb = __shfl(ej, j, 64);
@@ -224,11 +236,13 @@ __global__ void __launch_bounds__(NT) router_bwd_small_kernel(RouterBwdSmallArgs
     for (int e = 0; e < EM; ++e) dzv[e] = 0.0f;
     if (t < a.T) {
       float p[EM], dp[EM];
-      const float aux_scale = a.aux_coef * (float)E / ((float)a.T * (float)a.T * (float)a.k);
+      const bool real = !a.mask || a.mask[t] != 0;     // fillers get no balancing term
+      const float aux_scale = real ? aux_grad_scale(a.aux_coef, E, a.T, a.k, a.mask, a.rcounts) : 0.0f;
+      const int32_t* cnt = a.mask ? a.rcounts : a.counts;
 #pragma unroll
       for (int e = 0; e < EM; ++e) {
         p[e] = (e < E) ? a.probs[t * E + e] : 0.0f;
-        dp[e] = (e < E) ? aux_scale * (float)a.counts[e] : 0.0f;
+        dp[e] = (e < E) ? aux_scale * (float)cnt[e] : 0.0f;
       }
       // slot gradients; with renormalisation w = p_sel / S
       float S = 0.0f, wg = 0.0f;
@@ -533,6 +547,7 @@ __device__ __forceinline__ int pow2_at_least(int v) {
 
 __global__ void __launch_bounds__(NT) aux_partials_kernel(AuxArgs a) {
   __shared__ float sp[NT], se[NT];
+  __shared__ int sc[NT], sr[NT];
   const int EP2 = pow2_at_least(a.E);
   const int TL = NT / EP2;
   const int e = threadIdx.x % EP2, tl = threadIdx.x / EP2;
@@ -540,35 +555,52 @@ __global__ void __launch_bounds__(NT) aux_partials_kernel(AuxArgs a) {
   int64_t t1 = t0 + kAuxTokens;
   if (t1 > a.T) t1 = a.T;
   float ps = 0.0f, ent = 0.0f;
+  int cnt = 0, nreal = 0;                            // (real-token mask only)
   if (e < a.E) {
     // four tokens' loads issued together, then added in token order
     for (int64_t tb = t0 + tl; tb < t1; tb += 4 * TL) {
       float p[4];
+      bool use[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int64_t t = tb + u * TL;
-        p[u] = t < t1 ? a.probs[t * a.E + e] : 0.0f;
+        use[u] = t < t1 && (!a.mask || a.mask[t] != 0);
+        p[u] = use[u] ? a.probs[t * a.E + e] : 0.0f;
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        if (tb + u * TL < t1) {
+        if (use[u]) {
           ps += p[u];
           if (p[u] > 0.0f) ent -= p[u] * logf(p[u]);
+          if (a.mask) {
+            const int64_t t = tb + u * TL;
+            for (int j = 0; j < a.k; ++j) cnt += a.idx[t * a.k + j] == e ? 1 : 0;
+            nreal += 1;
+          }
         }
       }
     }
   }
   sp[threadIdx.x] = ps;
   se[threadIdx.x] = ent;
+  sc[threadIdx.x] = cnt;
+  sr[threadIdx.x] = nreal;
   __syncthreads();
   if (tl == 0 && e < a.E) {
     float s1 = 0.0f, s2 = 0.0f;
+    int c = 0, r = 0;
     for (int l = 0; l < TL; ++l) {
       s1 += sp[l * EP2 + e];
       s2 += se[l * EP2 + e];
+      c += sc[l * EP2 + e];
+      r += sr[l * EP2 + e];
     }
     a.part[((int64_t)blockIdx.x * 2 + 0) * a.E + e] = s1;
     a.part[((int64_t)blockIdx.x * 2 + 1) * a.E + e] = s2;
+    if (a.mask) {
+      a.cpart[(int64_t)blockIdx.x * (a.E + 1) + e] = c;
+      if (e == 0) a.cpart[(int64_t)blockIdx.x * (a.E + 1) + a.E] = r;   // real tokens of the block
+    }
   }
 }
 
@@ -625,11 +657,33 @@ __global__ void __launch_bounds__(NT) aux_finalize_kernel(AuxArgs a, int nblk) {
     }
     __syncthreads();
   }
+  // real-token mask: the real tokens' counts and their number, summed over
+  // the blocks' integer partials (exact), and written out for the backward
+  __shared__ int s_real;
+  if (a.mask) {
+    const int e = threadIdx.x;
+    if (e < a.E) {
+      int c = 0;
+      for (int b = 0; b < nblk; ++b) c += a.cpart[(int64_t)b * (a.E + 1) + e];
+      a.rcounts[e] = c;
+    }
+    if (threadIdx.x < 64) {
+      int r = 0;
+      for (int b = threadIdx.x; b < nblk; b += 64) r += a.cpart[(int64_t)b * (a.E + 1) + a.E];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) r += __shfl_xor(r, o, 64);
+      if (threadIdx.x == 0) {
+        s_real = r;
+        a.rcounts[a.E] = r;
+      }
+    }
+    __syncthreads();
+  }
   const int e = threadIdx.x;
   const bool valid = e < a.E;
   const float ps = valid ? colp[e] : 0.0f, ent = valid ? cole[e] : 0.0f;
-  const double T = (double)a.T;
-  const double cnt = valid ? (double)a.counts[e] : 0.0;
+  const double T = a.mask ? (double)s_real : (double)a.T;
+  const double cnt = valid ? (double)(a.mask ? a.rcounts[e] : a.counts[e]) : 0.0;
   const double f = (T > 0) ? cnt / (T * a.k) : 0.0;
   const double P = (T > 0) ? (double)ps / T : 0.0;
   if (valid) {

@@ -161,6 +161,9 @@ struct RouterDzArgs {
   void* dz_hl;          // [T, 2*Ep] act: hi part then lo part
   float* dbias_part;    // [gridDim, E]
   int64_t T; int E, Ep, k, renorm; float aux_coef;
+  // balancing statistic over real tokens: mask [T] (0 = filler) and the real
+  // tokens' counts [E] plus their number at [E]; nullptr = every token
+  const int32_t* mask = nullptr; const int32_t* rcounts = nullptr;
 };
 int router_dz_blocks(int64_t T);
 hipError_t launch_router_dz(int dt, const RouterDzArgs& a, hipStream_t s);
@@ -181,6 +184,7 @@ struct RouterBwdSmallArgs {
   float* dw_part;         // [nblk, E, d]
   float* dbias_part;      // [nblk, E]
   int64_t T; int E, Ep, d, k, renorm; float aux_coef;
+  const int32_t* mask = nullptr; const int32_t* rcounts = nullptr;   // as in RouterDzArgs
 };
 int router_small_blocks(int64_t T);
 hipError_t launch_router_bwd_small(int dt, const RouterBwdSmallArgs& a, hipStream_t s);
@@ -226,6 +230,11 @@ struct AuxArgs {
   const float* probs; const int32_t* counts; float* f; float* p_mean; void* out;
   float* part;           // ws [nblk, 2, E]
   int64_t T; int E, k;
+  // statistic over real tokens only (mask [T], 0 = filler): counts are then
+  // taken from idx [T, k] under the mask into rcounts [E + 1] (number of real
+  // tokens at [E]), with per-block integer partials in cpart [nblk, E + 1]
+  const int32_t* mask = nullptr; const int32_t* idx = nullptr;
+  int32_t* rcounts = nullptr; int32_t* cpart = nullptr;
 };
 int aux_blocks(int64_t T);
 hipError_t launch_aux(const AuxArgs& a, hipStream_t s);

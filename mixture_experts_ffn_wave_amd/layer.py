@@ -52,6 +52,15 @@ class MoELayer:
         self.params = None
         self.sel_bias = None      # aux-loss-free balancing: set by enable_balancing()
         self.balance_gamma = 0.0
+        self.real_mask = None     # statistic over real tokens only: set by set_real_mask()
+        self.real_counts = None
+
+    def set_real_mask(self, mask):
+        """Compute the balancing statistic (and its gradient) over the tokens
+        whose mask is non-zero only: mask [T] int32 device tensor, or None."""
+        self.real_mask = mask
+        self.real_counts = (torch.empty(self.plan.E + 1, dtype=torch.int32, device=self.probs.device)
+                            if mask is not None else None)
 
     def enable_balancing(self, sel_bias=None, gamma=0.0):
         """Route with a per-expert selection bias (aux-loss-free balancing):
@@ -101,7 +110,8 @@ class MoELayer:
                     topk_w=self.topk_w, counts=self.counts, offsets=self.offsets, inv_perm=self.inv_perm,
                     x_perm=self.x_perm, gu=self.gu, h=self.h, y_perm=self.y_perm, w_gate_up=q["w_gate_up"],
                     w_down=q["w_down"], ws_gate_up=q["ws_gate_up"], ws_down=q["ws_down"],
-                    gu_shared=self.gu_shared, h_shared=self.h_shared)
+                    gu_shared=self.gu_shared, h_shared=self.h_shared, real_mask=self.real_mask,
+                    real_counts=self.real_counts)
 
     def backward(self, dy, stream=None):
         L.moe_backward(self.plan, self.saved(), dy, self.grads, self.ws, stream)
@@ -118,13 +128,24 @@ class MoELayer:
         return self.ws[off:off + nb].view(p.dtype).view(*shape)
 
     def aux_stats(self, stream=None):
-        L.moe_aux_stats(self.plan, self.probs, self.counts, self.f, self.p_mean, self.aux_out, self.ws, stream)
+        if self.real_mask is not None:
+            L.moe_aux_stats_masked(self.plan, self.probs, self.topk_idx, self.real_mask, self.f, self.p_mean,
+                                   self.real_counts, self.aux_out, self.ws, stream)
+        else:
+            L.moe_aux_stats(self.plan, self.probs, self.counts, self.f, self.p_mean, self.aux_out, self.ws,
+                            stream)
 
     def step(self, dy, stream=None):
         """One full pass: route, permute, experts, combine, backward, aux
-        statistics (and the balancing bias update when enabled with gamma > 0)."""
+        statistics (and the balancing bias update when enabled with gamma > 0).
+        With a real-token mask the statistic runs before the backward, whose
+        balancing gradient needs the real tokens' counts."""
         self.forward(stream)
-        self.backward(dy, stream)
-        self.aux_stats(stream)
+        if self.real_mask is not None:
+            self.aux_stats(stream)
+            self.backward(dy, stream)
+        else:
+            self.backward(dy, stream)
+            self.aux_stats(stream)
         if self.sel_bias is not None and self.balance_gamma > 0.0:
             self.update_balance(self.balance_gamma, stream)

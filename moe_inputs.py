@@ -109,6 +109,23 @@ def selection_bias(E, scale, seed=1):
     return (rng.standard_normal(E, dtype=np.float32) * np.float32(scale)).astype(np.float32)
 
 
+def real_token_mask(T, filler_frac=0.3, seed=2):
+    """A seeded real-token mask (int32 numpy [T], 0 = filler): runs of filler
+    tokens of random length, as padding between packed documents leaves
+    them, covering about ``filler_frac`` of the batch, plus a filler tail."""
+    rng = np.random.default_rng(seed)
+    m = np.ones(T, dtype=np.int32)
+    t = 0
+    while t < T:
+        t += int(rng.integers(16, 128))                 # a document
+        n = int(rng.integers(1, 48))                    # then its padding
+        if rng.random() < filler_frac * 2:
+            m[t:t + n] = 0
+        t += n
+    m[T - T // 16:] = 0                                 # padded tail
+    return m
+
+
 def to_f64(t):
     """Exact upcast of a stored tensor to a float64 numpy array (None passes)."""
     if t is None:

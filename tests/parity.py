@@ -69,12 +69,13 @@ def to_np(t):
     return t.to(torch.float64).numpy()
 
 
-def gpu_run(wl, inp, routing=None, intermediates=False, sel_bias=None):
+def gpu_run(wl, inp, routing=None, intermediates=False, sel_bias=None, mask=None):
     """One fwd+bwd step on cuda:0.  ``routing`` (probs, idx, w as numpy) replaces
     the router's outputs when given (then moe_route is not called).
     ``intermediates`` also returns what the backward left in the workspace
     (dy_perm, dgu, dx_perm and, with shared experts, dgu_shared, dx_shared).
-    ``sel_bias`` (numpy [E]) routes with aux-loss-free balancing."""
+    ``sel_bias`` (numpy [E]) routes with aux-loss-free balancing; ``mask``
+    (numpy [T], 0 = filler) takes the balancing statistic over real tokens."""
     from mixture_experts_ffn_wave_amd import MoELayer, decode_aux
     b = inp.get("bias")
     plan = plan_for(wl, b is not None)
@@ -85,6 +86,8 @@ def gpu_run(wl, inp, routing=None, intermediates=False, sel_bias=None):
                      ws_gate_up=dev.get("ws_gate_up"), ws_down=dev.get("ws_down"))
     if sel_bias is not None:
         layer.enable_balancing(torch.from_numpy(np.asarray(sel_bias, dtype=np.float32)).cuda())
+    if mask is not None:
+        layer.set_real_mask(torch.from_numpy(np.asarray(mask, dtype=np.int32)).cuda())
     if routing is None:
         layer.forward()
     else:
@@ -92,8 +95,12 @@ def gpu_run(wl, inp, routing=None, intermediates=False, sel_bias=None):
         layer.topk_idx.copy_(torch.from_numpy(routing["idx"]).to(torch.int32))
         layer.topk_w.copy_(torch.from_numpy(routing["w"]).to(torch.float32))
         layer.dispatch_and_experts()
-    layer.backward(dev["dy"])
-    layer.aux_stats()
+    if mask is not None:
+        layer.aux_stats()                   # the masked backward needs the real tokens' counts
+        layer.backward(dev["dy"])
+    else:
+        layer.backward(dev["dy"])
+        layer.aux_stats()
     torch.cuda.synchronize()
     out = {n: to_np(getattr(layer, n)) for n in
            ["probs", "topk_idx", "topk_w", "counts", "offsets", "perm_token", "inv_perm", "x_perm", "gu",
@@ -101,6 +108,8 @@ def gpu_run(wl, inp, routing=None, intermediates=False, sel_bias=None):
     for n, t in layer.grads.items():
         out[n] = to_np(t)
     out["aux"] = decode_aux(layer.aux_out)
+    if mask is not None:
+        out["real_counts"] = to_np(layer.real_counts)
     if intermediates:
         names = ["dy_perm", "dgu", "dx_perm"] + (["dgu_shared", "dx_shared"] if wl.n_shared else [])
         for n in names:
@@ -117,14 +126,19 @@ def storage_rounding(wl):
     return lambda a, kind: O.round_to_format(a, "f32" if kind == "f32" else wl.dtype)
 
 
-def oracle_run(wl, f64, store=None, quant=None, sel_bias=None):
+def oracle_run(wl, f64, store=None, quant=None, sel_bias=None, mask=None):
     b = f64.get("bias")
     fwd = O.layer_forward(f64["x"], f64["w_router"], f64["w_gate_up"], f64["w_down"], top_k=wl.k,
                           renorm=wl.renorm, bias=b, ws_gate_up=f64.get("ws_gate_up"),
                           ws_down=f64.get("ws_down"), store=store, quant=quant,
                           sel_bias=None if sel_bias is None else np.asarray(sel_bias, dtype=np.float64))
-    bwd = O.layer_backward(fwd, f64["dy"], aux_coef=wl.aux_coef, quant=quant)
-    st = O.aux_statistics(fwd["p"], fwd["counts"], wl.k)
+    bwd = O.layer_backward(fwd, f64["dy"], aux_coef=wl.aux_coef, quant=quant, mask=mask)
+    if mask is None:
+        st = O.aux_statistics(fwd["p"], fwd["counts"], wl.k)
+    else:
+        rc, tr = O.real_token_counts(fwd["idx"], mask, wl.E)
+        st = O.aux_statistics(fwd["p"], rc, wl.k, mask)
+        st["real_counts"] = np.concatenate([rc, [tr]])
     return fwd, bwd, st
 
 
@@ -201,7 +215,10 @@ def compare_dispatch(gpu, fwd):
 
 
 def compare_stats(gpu, st):
-    """Balancing statistic and router metrics."""
+    """Balancing statistic and router metrics (and, over real tokens, their
+    counts: integers, bit-exact)."""
+    if "real_counts" in st:
+        assert np.array_equal(gpu["real_counts"], st["real_counts"]), "real-token counts"
     assert np.allclose(gpu["f"], st["f"], rtol=1e-6, atol=0), "f"
     assert np.max(np.abs(gpu["p_mean"] - st["p_mean"])) <= PROB_ATOL, "p_mean"
     a = gpu["aux"]
@@ -355,7 +372,7 @@ def compare_mx_stepwise(wl, gpu, fwd, f64, st):
     compare_stats(gpu, st)
 
 
-def full_parity(wl, inp=None, mx_diagnostic=True, sel_bias=None):
+def full_parity(wl, inp=None, mx_diagnostic=True, sel_bias=None, mask=None):
     """The whole chain on the GPU against the oracle.  When a near-tie made
     the GPU pick a different (valid) routing, the downstream calls are run a
     second time from the oracle's routing so every later tensor is compared
@@ -371,16 +388,17 @@ def full_parity(wl, inp=None, mx_diagnostic=True, sel_bias=None):
     f64 = oracle_inputs(inp)
     say(f"[parity] {wl.name}: {MI.describe(wl)} -- GPU chain")
     mx = wl.expert_dtype == "mxfp8"
-    gpu = gpu_run(wl, inp, intermediates=mx, sel_bias=sel_bias)
+    gpu = gpu_run(wl, inp, intermediates=mx, sel_bias=sel_bias, mask=mask)
     rounded = wl.dtype == "bf16" or mx
     say(f"[parity] {wl.name}: oracle" + (" (bf16 storage rounding)" if rounded else "") +
         (" (MX-quantised expert GEMM operands)" if mx else ""))
     fwd, bwd, st = oracle_run(wl, f64, storage_rounding(wl) if rounded else None,
-                              quant=O.mx_fake_quant if mx else None, sel_bias=sel_bias)
+                              quant=O.mx_fake_quant if mx else None, sel_bias=sel_bias, mask=mask)
     identical = compare_routing(wl, gpu, fwd)
     if not identical:
         say(f"[parity] {wl.name}: near-tie routing differs; rerunning downstream from the oracle routing")
-        gpu = gpu_run(wl, inp, routing={"p": fwd["p"], "idx": fwd["idx"], "w": fwd["w"]}, intermediates=mx)
+        gpu = gpu_run(wl, inp, routing={"p": fwd["p"], "idx": fwd["idx"], "w": fwd["w"]}, intermediates=mx,
+                      mask=mask)
     REPORT.clear()
     if mx:
         compare_mx_stepwise(wl, gpu, fwd, f64, st)
@@ -407,7 +425,7 @@ def full_parity(wl, inp=None, mx_diagnostic=True, sel_bias=None):
             " ".join(f"{n}={r:.4f}" for n, r in ex.items()))
     if rounded and (mx_diagnostic or not mx):
         # distance from the exact layer, for the record (not asserted)
-        xf, xb, xs = oracle_run(wl, f64, sel_bias=sel_bias)
+        xf, xb, xs = oracle_run(wl, f64, sel_bias=sel_bias, mask=mask)
         REPORT.clear()
         STRICT[0] = False
         try:

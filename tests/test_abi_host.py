@@ -45,12 +45,27 @@ def test_version_and_status_strings():
     assert lib.moe_status_string(123) == b"unknown status"
 
 
-def test_struct_sizes_match_header_layout():
+def test_struct_sizes_match_header_layout(tmp_path):
     assert ctypes.sizeof(L.MoeConfig) == 56          # int64 + 10 int32 + float, 8-aligned
     assert ctypes.sizeof(L.MoeAuxScalars) == 32
     assert ctypes.sizeof(L.MoeFfnArgs) == 13 * 8
-    assert ctypes.sizeof(L.MoeSaved) == 18 * 8
+    assert ctypes.sizeof(L.MoeSaved) == 20 * 8
     assert ctypes.sizeof(L.MoeGrads) == 7 * 8
+    # and the C compiler's layout of the header itself
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "sizes.c"
+    src.write_text('#include <stdio.h>\n#include "moe.h"\nint main(void) { printf("%zu %zu %zu %zu %zu\\n", '
+                   'sizeof(moe_config), sizeof(moe_aux_scalars), sizeof(moe_ffn_args), sizeof(moe_saved), '
+                   'sizeof(moe_grads)); return 0; }\n')
+    exe = tmp_path / "sizes"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run([cc, "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    assert got == [ctypes.sizeof(c) for c in (L.MoeConfig, L.MoeAuxScalars, L.MoeFfnArgs, L.MoeSaved, L.MoeGrads)]
 
 
 def _create(**kw):
@@ -144,6 +159,18 @@ def test_calls_reject_bad_arguments_before_any_launch():
     sv, gr = L.MoeSaved(), L.MoeGrads()
     assert lib.moe_backward(h, ctypes.byref(sv), nul, ctypes.byref(gr), nul, 0, nul) == MOE_ERR_NULL
     assert lib.moe_aux_stats(h, nul, nul, nul, nul, nul, nul, 0, nul) == MOE_ERR_NULL
+    # masked statistic: the mask, the indices and the real-count output are required
+    assert lib.moe_aux_stats_masked(h, fake, fake, nul, fake, fake, fake, fake, fake, p.workspace_bytes(),
+                                    nul) == MOE_ERR_NULL
+    assert lib.moe_aux_stats_masked(h, fake, fake, fake, fake, fake, nul, fake, fake, p.workspace_bytes(),
+                                    nul) == MOE_ERR_NULL
+    assert lib.moe_aux_stats_masked(h, fake, fake, fake, fake, fake, fake, fake, nul, 0, nul) == MOE_ERR_WORKSPACE
+    # a saved real-token mask needs the real tokens' counts
+    svm = L.MoeSaved(*[0x1000] * len(L.MoeSaved._fields_))
+    svm.real_counts = None
+    grm = L.MoeGrads(*[0x1000] * len(L.MoeGrads._fields_))
+    assert lib.moe_backward(h, ctypes.byref(svm), fake, ctypes.byref(grm), fake, p.workspace_bytes(),
+                            nul) == MOE_ERR_NULL
     # a plan with a bias requires the bias pointer
     pb = L.Plan(512, 256, 8, 2, 128, has_router_bias=True)
     assert lib.moe_route(pb.handle, fake, fake, nul, fake, fake, fake, nul) == MOE_ERR_NULL
