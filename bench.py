@@ -223,6 +223,9 @@ def main():
     ap.add_argument("--balance-gamma", type=float, default=0.0,
                     help="route with aux-loss-free balancing, the selection bias updated by this step "
                          "size at the end of every step (0 = the plain router)")
+    ap.add_argument("--filler-frac", type=float, default=0.0,
+                    help="mark about this share of the tokens as fillers (seeded runs) and take the balancing "
+                         "statistic over the real tokens only (0 = every token real)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (no collectives, no sharding); "
@@ -236,6 +239,8 @@ def main():
     layer, dev = make_layer(wl)
     if args.balance_gamma > 0:
         layer.enable_balancing(gamma=args.balance_gamma)
+    if args.filler_frac > 0:
+        layer.set_real_mask(torch.from_numpy(MI.real_token_mask(wl.T, args.filler_frac)).to(dev["x"].device))
     dy = dev["dy"]
     print(f"[bench] workload {wl.name}: {MI.describe(wl)}", file=sys.stderr, flush=True)
 
@@ -290,7 +295,8 @@ def main():
         "config": {"workload": wl.name, "T": wl.T, "d_model": wl.d, "experts": wl.E, "top_k": wl.k,
                    "d_ff": wl.I, "shared": f"{wl.n_shared}x{wl.I_shared}", "renorm": wl.renorm,
                    "parallelism": "none (1 GPU)",
-                   **({"balance_gamma": args.balance_gamma} if args.balance_gamma > 0 else {})},
+                   **({"balance_gamma": args.balance_gamma} if args.balance_gamma > 0 else {}),
+                   **({"filler_frac": args.filler_frac} if args.filler_frac > 0 else {})},
         "roofline": {"bound": "mfma", "kernel": dominant, "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic_per_launch(wl, dominant),
                      "avg_launch_us": avg_ms * 1e3, "launches": launches},
