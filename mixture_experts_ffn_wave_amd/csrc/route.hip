@@ -4,13 +4,15 @@
 // top-k over the experts, the chosen probabilities optionally rescaled to sum
 // to one (KochiLLM v1.0 model card, "Architecture").
 //
-// A wave owns 32 tokens.  The expert weights (rows of W_r, padded to a
+// A workgroup owns 32 tokens.  The expert weights (rows of W_r, padded to a
 // multiple of 32) are the MFMA "A" operand and the token rows the "B"
-// operand, so after the K loop lane l holds the logits of token l % 32 for
-// half of the experts (e = 32 s + 8 (r/4) + 4 (l/32) + r%4); the other half
-// sits in lane l ^ 32.  Softmax and top-k then need only one cross-lane
-// exchange per reduction.  Top-k is k rounds of "largest remaining logit,
-// lower expert index on ties", which also fixes the slot order.
+// operand, so the logits of a token end up in the accumulator layout: lane l
+// holds token l % 32 for half of the experts (e = 32 s + 8 (r/4) + 4 (l/32) +
+// r%4), the other half sits in lane l ^ 32.  Softmax and top-k then need only
+// one cross-lane exchange per reduction.  Top-k is k rounds of "largest
+// remaining logit, lower expert index on ties", which also fixes the slot
+// order.  Up to 64 experts the four waves of a workgroup split the K range;
+// above, they split the experts (both kernels below).
 
 #include <math.h>
 
@@ -155,103 +157,6 @@ __device__ __forceinline__ void route_epilogue(const f32x16 (&acc)[NSUB], int64_
   }
 }
 
-template <typename T, int NSUB, int WAVES>
-__global__ void __launch_bounds__(WAVES * 64) route_kernel(RouteArgs a) {
-  constexpr int ES = sizeof(T);
-  constexpr int BK = KB / ES;
-  constexpr int TB = 32 * WAVES;          // tokens per workgroup
-  constexpr int EP = 32 * NSUB;           // padded experts
-  constexpr int NTH = WAVES * 64;
-  constexpr int XPT = TB * 8 / NTH;       // 16-byte chunks of the x tile per thread (= 4)
-  constexpr int WPT = EP * 8 / NTH;       // 16-byte chunks of the W tile per thread
-  static_assert(WPT >= 1, "too many waves for the expert tile");
-
-  __shared__ __attribute__((aligned(16))) char lds[(TB + EP) * LROW];
-  char* lx = lds;
-  char* lw = lds + TB * LROW;
-  static_assert(WAVES * kWtsLds * 4 <= (TB + EP) * LROW, "weights scratch fits in the tiles' LDS");
-  __shared__ float s_bias[EP], s_sel[EP];
-  static_assert(EP <= NTH, "bias staged by one thread per expert");
-  stage_bias<NSUB>(s_bias, s_sel, a);         // visible after the K loop's first barrier
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t t0 = (int64_t)blockIdx.x * TB;
-  const char* xb = static_cast<const char*>(a.x);
-  const char* wb = static_cast<const char*>(a.w);
-
-  auto load = [&](int kc, u32x4* rx, u32x4* rw) {
-#pragma unroll
-    for (int s = 0; s < XPT; ++s) {
-      const int c = tid + NTH * s, r = c >> 3, cc = c & 7;
-      rx[s] = (t0 + r < a.T) ? ld16(xb + ((t0 + r) * a.d + kc) * ES + cc * 16) : (u32x4){0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int s = 0; s < WPT; ++s) {
-      const int c = tid + NTH * s, r = c >> 3, cc = c & 7;
-      rw[s] = (r < a.E) ? ld16(wb + ((int64_t)r * a.d + kc) * ES + cc * 16) : (u32x4){0u, 0u, 0u, 0u};
-    }
-  };
-  auto stage = [&](const u32x4* rx, const u32x4* rw) {
-#pragma unroll
-    for (int s = 0; s < XPT; ++s) {
-      const int c = tid + NTH * s;
-      st16(lx + (c >> 3) * LROW + (c & 7) * 16, rx[s]);
-    }
-#pragma unroll
-    for (int s = 0; s < WPT; ++s) {
-      const int c = tid + NTH * s;
-      st16(lw + (c >> 3) * LROW + (c & 7) * 16, rw[s]);
-    }
-  };
-
-  f32x16 acc[NSUB];
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[s][r] = 0.0f;
-
-  constexpr int CH = Mma32<T>::kChunks;
-  const int nk = a.d / BK;
-  // a ring of PF chunks in registers: the loads of the next PF - 1 chunks are
-  // in flight while one is staged and multiplied
-  constexpr int PF = NSUB == 1 ? 4 : 2;
-  u32x4 rx[PF][XPT], rw[PF][WPT];
-#pragma unroll
-  for (int q = 0; q < PF; ++q)
-    if (q < nk) load(q * BK, rx[q], rw[q]);
-  for (int kc0 = 0; kc0 < nk; kc0 += PF) {
-#pragma unroll
-    for (int q = 0; q < PF; ++q) {
-      const int kc = kc0 + q;
-      if (kc < nk) {
-        stage(rx[q], rw[q]);
-        __syncthreads();
-        if (kc + PF < nk) load((kc + PF) * BK, rx[q], rw[q]);
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-          const int kb = ks * 16 * ES + (lane >> 5) * 8 * ES;
-          u32x4 fb[CH];
-          const char* xrow = lx + (wave * 32 + (lane & 31)) * LROW + kb;
-#pragma unroll
-          for (int ch = 0; ch < CH; ++ch) fb[ch] = ld16(xrow + ch * 16);
-#pragma unroll
-          for (int s = 0; s < NSUB; ++s) {
-            u32x4 fa[CH];
-            const char* wrow = lw + (s * 32 + (lane & 31)) * LROW + kb;
-#pragma unroll
-            for (int ch = 0; ch < CH; ++ch) fa[ch] = ld16(wrow + ch * 16);
-            Mma32<T>::run(acc[s], fa, fb);
-          }
-        }
-        __syncthreads();
-      }
-    }
-  }
-
-  __syncthreads();                            // tiles free for the weights scratch (also covers an empty K loop)
-  route_epilogue<NSUB>(acc, t0 + wave * 32, lane, a, s_bias, s_sel, reinterpret_cast<float*>(lds) + wave * kWtsLds);
-}
-
 // Few experts (E <= 64): 32 tokens per workgroup of KW waves that split the K
 // range.  Wave w multiplies chunks w, w + KW, ... into accumulators of its
 // own, staged through LDS tiles of its own (no workgroup barrier inside the
@@ -369,6 +274,122 @@ __global__ void __launch_bounds__(KW * 64) route_ksplit_kernel(RouteArgs a) {
   }
 }
 
+// Many experts (64 < E <= 256): 32 tokens per workgroup of four waves that
+// split the experts.  The x tile and the whole W tile of a K chunk are
+// staged once in LDS; wave w multiplies expert subtiles w, w + 4, ... (NSUB/4
+// of them) for the 32 tokens over the full K range.  The logits then meet in
+// LDS in the accumulator layout and wave 0 finishes the tokens.  Eight waves
+// per CU instead of two for the same tokens.
+template <typename T, int NSUB>
+__global__ void __launch_bounds__(256) route_esplit_kernel(RouteArgs a) {
+  constexpr int ES = sizeof(T);
+  constexpr int BK = KB / ES;
+  constexpr int EP = 32 * NSUB;
+  constexpr int NW = 4, SPW = NSUB / NW;           // expert subtiles per wave
+  constexpr int NTH = 64 * NW;
+  constexpr int XPT = 32 * 8 / NTH;                // 16-byte chunks of the x tile per thread (1)
+  constexpr int WPT = EP * 8 / NTH;                // 16-byte chunks of the W tile per thread
+  constexpr int TILES = (32 + EP) * LROW;
+  static_assert(NSUB % NW == 0 && XPT == 1 && WPT >= 1, "tile split");
+  static_assert(NSUB * 16 * 64 * 4 <= TILES && kWtsLds * 4 <= TILES, "logits and weights scratch fit");
+  __shared__ __attribute__((aligned(16))) char lds[TILES];
+  __shared__ float s_bias[EP], s_sel[EP];
+  stage_bias<NSUB>(s_bias, s_sel, a);              // visible after the K loop's first barrier
+  char* lx = lds;
+  char* lw = lds + 32 * LROW;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t t0 = (int64_t)blockIdx.x * 32;
+  const char* xb = static_cast<const char*>(a.x);
+  const char* wb = static_cast<const char*>(a.w);
+  auto load = [&](int kc, u32x4& rx, u32x4* rw) {
+    {
+      const int r = tid >> 3, cc = tid & 7;
+      rx = (t0 + r < a.T) ? ld16(xb + ((t0 + r) * a.d + kc) * ES + cc * 16) : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int s = 0; s < WPT; ++s) {
+      const int c = tid + NTH * s, r = c >> 3, cc = c & 7;
+      rw[s] = (r < a.E) ? ld16(wb + ((int64_t)r * a.d + kc) * ES + cc * 16) : (u32x4){0u, 0u, 0u, 0u};
+    }
+  };
+  auto stage = [&](const u32x4& rx, const u32x4* rw) {
+    st16(lx + (tid >> 3) * LROW + (tid & 7) * 16, rx);
+#pragma unroll
+    for (int s = 0; s < WPT; ++s) {
+      const int c = tid + NTH * s;
+      st16(lw + (c >> 3) * LROW + (c & 7) * 16, rw[s]);
+    }
+  };
+
+  f32x16 acc[SPW];
+#pragma unroll
+  for (int s = 0; s < SPW; ++s)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[s][r] = 0.0f;
+
+  constexpr int CH = Mma32<T>::kChunks;
+  constexpr int PF = 2;
+  const int nk = a.d / BK;
+  u32x4 rx[PF], rw[PF][WPT];
+#pragma unroll
+  for (int q = 0; q < PF; ++q)
+    if (q < nk) load(q * BK, rx[q], rw[q]);
+  for (int kc0 = 0; kc0 < nk; kc0 += PF) {
+#pragma unroll
+    for (int q = 0; q < PF; ++q) {
+      const int kc = kc0 + q;
+      if (kc < nk) {
+        stage(rx[q], rw[q]);
+        __syncthreads();
+        if (kc + PF < nk) load((kc + PF) * BK, rx[q], rw[q]);
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+          const int kb = ks * 16 * ES + (lane >> 5) * 8 * ES;
+          u32x4 fb[CH];
+          const char* xrow = lx + (lane & 31) * LROW + kb;
+#pragma unroll
+          for (int ch = 0; ch < CH; ++ch) fb[ch] = ld16(xrow + ch * 16);
+#pragma unroll
+          for (int s = 0; s < SPW; ++s) {
+            u32x4 fa[CH];
+            const char* wrow = lw + ((wave + NW * s) * 32 + (lane & 31)) * LROW + kb;
+#pragma unroll
+            for (int ch = 0; ch < CH; ++ch) fa[ch] = ld16(wrow + ch * 16);
+            Mma32<T>::run(acc[s], fa, fb);
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+
+  // every wave's subtiles -> LDS in the accumulator layout [subtile][r][lane]
+  float* red = reinterpret_cast<float*>(lds);
+  __syncthreads();                                 // (also covers an empty K loop)
+#pragma unroll
+  for (int s = 0; s < SPW; ++s)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[(((wave + NW * s) * 16) + r) * 64 + lane] = acc[s][r];
+  __syncthreads();
+  if (wave == 0) {
+    f32x16 all[NSUB];
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) all[s][r] = red[((s * 16) + r) * 64 + lane];
+    route_epilogue<NSUB>(all, t0, lane, a, s_bias, s_sel, red);   // (logits read: LDS reused)
+  }
+}
+
+template <typename T, int NSUB>
+hipError_t launch_route_esplit(const RouteArgs& a, hipStream_t s) {
+  const int64_t grid = (a.T + 31) / 32;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((route_esplit_kernel<T, NSUB>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <typename T, int NSUB, int KW>
 hipError_t launch_route_ksplit(const RouteArgs& a, hipStream_t s) {
   const int64_t grid = (a.T + 31) / 32;
@@ -377,22 +398,13 @@ hipError_t launch_route_ksplit(const RouteArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T, int NSUB, int WAVES>
-hipError_t launch_route_t(const RouteArgs& a, hipStream_t s) {
-  const int64_t tb = 32 * WAVES;
-  const int64_t grid = (a.T + tb - 1) / tb;
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((route_kernel<T, NSUB, WAVES>), dim3((unsigned)grid), dim3(WAVES * 64), 0, s, a);
-  return hipGetLastError();
-}
-
 template <typename T>
 hipError_t launch_route_dt(const RouteArgs& a, hipStream_t s) {
   const int nsub = (a.E + 31) / 32;
   if (nsub <= 1) return launch_route_ksplit<T, 1, 4>(a, s);
   if (nsub <= 2) return launch_route_ksplit<T, 2, 4>(a, s);
-  if (nsub <= 4) return launch_route_t<T, 4, 2>(a, s);
-  return launch_route_t<T, 8, 4>(a, s);
+  if (nsub <= 4) return launch_route_esplit<T, 4>(a, s);
+  return launch_route_esplit<T, 8>(a, s);
 }
 
 // Aux-loss-free balancing update, one thread per expert: the sign of
