@@ -157,6 +157,105 @@ __device__ __forceinline__ void route_epilogue(const f32x16 (&acc)[NSUB], int64_
   }
 }
 
+// The same epilogue with all four waves of a workgroup: the 32 tokens'
+// logits sit in LDS in the accumulator layout ([subtile][register][lane],
+// see route_epilogue); wave w takes tokens 8w .. 8w+7, eight lanes per token,
+// lane g of a token owning experts EPL g .. EPL g + EPL - 1.  Maxima, sums and
+// the k rounds of the top-k are butterflies over the token's eight lanes
+// (ties to the lower expert index, as before).  s_wts: kWtsLds floats of LDS
+// apart from the logits, rows indexed by token.
+template <int NSUB>
+__device__ __forceinline__ void route_epilogue_wide(const float* red, int64_t tb, int wave, int lane,
+                                                    const RouteArgs& a, const float* s_bias, const float* s_sel,
+                                                    float* s_wts) {
+  constexpr int EPL = 4 * NSUB;                   // experts per lane (32 NSUB over 8 lanes)
+  static_assert(EPL <= 32, "taken mask");
+  const int tl = wave * 8 + (lane >> 3), g = lane & 7;
+  const int64_t t = tb + tl;
+  const bool tv = t < a.T;
+  const int E = a.E;
+  const bool sel = a.sel_bias != nullptr;
+  // gather this lane's logits (+ constant bias) from the accumulator layout
+  float z[EPL];
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = g * EPL + i, sub = e >> 5, w = e & 31;
+    const int r = 4 * (w >> 3) + (w & 3), hh = (w >> 2) & 1;
+    const float v = red[((sub * 16) + r) * 64 + tl + 32 * hh];
+    z[i] = (e < E) ? v + s_bias[e] : -INFINITY;
+    m = fmaxf(m, z[i]);
+  }
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  float sum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i)
+    if (g * EPL + i < E) sum += expf(z[i] - m);
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) sum += __shfl_xor(sum, o, 64);
+  // probabilities (kept in z when a selection bias ranks on them)
+  float p[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) p[i] = (g * EPL + i < E) ? expf(z[i] - m) / sum : 0.0f;
+  if (tv) {
+    float* prow = a.probs + t * E + g * EPL;
+    if ((E & 3) == 0) {
+#pragma unroll
+      for (int q = 0; q < EPL / 4; ++q)
+        if (g * EPL + 4 * q < E)
+          *reinterpret_cast<f32x4*>(prow + 4 * q) = (f32x4){p[4 * q], p[4 * q + 1], p[4 * q + 2], p[4 * q + 3]};
+    } else {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (g * EPL + i < E) prow[i] = p[i];
+    }
+  }
+  // top-k: k rounds of (largest remaining ranking value, lower index on ties)
+  uint32_t taken = 0u;
+  float psum = 0.0f;
+  for (int j = 0; j < a.k; ++j) {
+    float bv = -INFINITY, bp = 0.0f, bz = -INFINITY;
+    int be = -1;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = g * EPL + i;
+      if (e < E && !((taken >> i) & 1u)) {
+        const float v = sel ? p[i] + s_sel[e] : z[i];
+        if (be < 0 || v > bv) {
+          bv = v;
+          bp = p[i];
+          bz = z[i];
+          be = e;
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      const float ov = __shfl_xor(bv, o, 64), op = __shfl_xor(bp, o, 64), oz = __shfl_xor(bz, o, 64);
+      const int oe = __shfl_xor(be, o, 64);
+      const bool take = (be < 0) || (oe >= 0 && (ov > bv || (ov == bv && oe < be)));
+      if (take) {
+        bv = ov;
+        bp = op;
+        bz = oz;
+        be = oe;
+      }
+    }
+    if (be >= 0 && be / EPL == g) taken |= 1u << (be - g * EPL);
+    const float pj = sel ? bp : expf(bz - m) / sum;
+    psum += pj;
+    if (tv && g == 0) {
+      a.idx[t * a.k + j] = be;
+      if (a.renorm) s_wts[tl * kWtsStride + j] = pj;
+      else a.wts[t * a.k + j] = pj;
+    }
+  }
+  if (a.renorm && tv && g == 0) {
+    for (int j = 0; j < a.k; ++j) a.wts[t * a.k + j] = s_wts[tl * kWtsStride + j] / psum;
+  }
+}
+
 // Few experts (E <= 64): 32 tokens per workgroup of KW waves that split the K
 // range.  Wave w multiplies chunks w, w + KW, ... into accumulators of its
 // own, staged through LDS tiles of its own (no workgroup barrier inside the
@@ -173,7 +272,8 @@ __global__ void __launch_bounds__(KW * 64) route_ksplit_kernel(RouteArgs a) {
   constexpr int WPL = EP * 8 / 64;        // 16-byte chunks of the W tile per lane
   constexpr int WREG = (32 + EP) * LROW;  // one wave's tiles
   constexpr int RED = (KW - 1) * NSUB * 16 * 64 * 4;
-  static_assert(RED <= KW * WREG && kWtsLds * 4 <= KW * WREG, "partial logits and weights scratch fit in the tiles' LDS");
+  static_assert(RED <= KW * WREG && (NSUB * 16 * 64 + kWtsLds) * 4 <= KW * WREG,
+                "partial logits, logits and weights scratch fit in the tiles' LDS");
   __shared__ __attribute__((aligned(16))) char lds[KW * WREG];
   __shared__ float s_bias[EP], s_sel[EP];
   static_assert(EP <= KW * 64, "bias staged by one thread per expert");
@@ -270,8 +370,17 @@ __global__ void __launch_bounds__(KW * 64) route_ksplit_kernel(RouteArgs a) {
       for (int s = 0; s < NSUB; ++s)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[s][r] += red[(((w - 1) * NSUB + s) * 16 + r) * 64 + lane];
-    route_epilogue<NSUB>(acc, t0, lane, a, s_bias, s_sel, red);   // (partials consumed: LDS reused)
   }
+  __syncthreads();                                 // every wave has read the partials
+  float* logits = red;                             // [NSUB][16][64], then the weights scratch
+  if (wave == 0) {
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) logits[((s * 16) + r) * 64 + lane] = acc[s][r];
+  }
+  __syncthreads();
+  route_epilogue_wide<NSUB>(logits, t0, wave, lane, a, s_bias, s_sel, logits + NSUB * 16 * 64);
 }
 
 // Many experts (64 < E <= 256): 32 tokens per workgroup of four waves that
@@ -291,9 +400,10 @@ __global__ void __launch_bounds__(256) route_esplit_kernel(RouteArgs a) {
   constexpr int WPT = EP * 8 / NTH;                // 16-byte chunks of the W tile per thread
   constexpr int TILES = (32 + EP) * LROW;
   static_assert(NSUB % NW == 0 && XPT == 1 && WPT >= 1, "tile split");
-  static_assert(NSUB * 16 * 64 * 4 <= TILES && kWtsLds * 4 <= TILES, "logits and weights scratch fit");
+  static_assert(NSUB * 16 * 64 * 4 <= TILES, "logits fit in the tiles' LDS");
   __shared__ __attribute__((aligned(16))) char lds[TILES];
   __shared__ float s_bias[EP], s_sel[EP];
+  __shared__ float s_wts[kWtsLds];
   stage_bias<NSUB>(s_bias, s_sel, a);              // visible after the K loop's first barrier
   char* lx = lds;
   char* lw = lds + 32 * LROW;
@@ -372,14 +482,7 @@ __global__ void __launch_bounds__(256) route_esplit_kernel(RouteArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) red[(((wave + NW * s) * 16) + r) * 64 + lane] = acc[s][r];
   __syncthreads();
-  if (wave == 0) {
-    f32x16 all[NSUB];
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) all[s][r] = red[((s * 16) + r) * 64 + lane];
-    route_epilogue<NSUB>(all, t0, lane, a, s_bias, s_sel, red);   // (logits read: LDS reused)
-  }
+  route_epilogue_wide<NSUB>(red, t0, wave, lane, a, s_bias, s_sel, s_wts);
 }
 
 template <typename T, int NSUB>
