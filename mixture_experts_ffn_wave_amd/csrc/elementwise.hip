@@ -15,8 +15,10 @@ constexpr int NT = 256;
 
 // y[t] = sum_j w[t,j] * y_perm[inv[t,j]] (+ y_shared[t]); one wave per token,
 // 16-byte vectors along the row (y_perm rows are f32), f32 accumulation in
-// slot order.
-template <typename T>
+// slot order.  Slots go in batches of KG whose row loads are all issued
+// before the first is used (a load under a per-slot branch would wait for
+// each row in turn).
+template <typename T, int KG>
 __global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a) {
   constexpr int VR = 16 / sizeof(T);   // output elements per 16-byte chunk
   constexpr int YC = VR / 4;           // 16-byte f32 chunks of y_perm per output chunk
@@ -39,17 +41,25 @@ __global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a) {
       float acc[VR];
 #pragma unroll
       for (int i = 0; i < VR; ++i) acc[i] = 0.0f;
-#pragma unroll 4
-      for (int j = 0; j < a.k; ++j) {
-        const int r = __shfl(r_l, j, 64);
-        const float w = __shfl(w_l, j, 64);
-        if (ok && r >= 0) {
-          const f32x4* src = reinterpret_cast<const f32x4*>(a.y_perm + (int64_t)r * a.d + (int64_t)c * VR);
+      for (int j0 = 0; j0 < a.k; j0 += KG) {
+        f32x4 v[KG][YC];
+        int r[KG];
 #pragma unroll
-          for (int q = 0; q < YC; ++q) {
-            const f32x4 v = src[q];
+        for (int u = 0; u < KG; ++u) {
+          r[u] = __shfl(r_l, (j0 + u) & 63, 64);
+          const bool use = ok && j0 + u < a.k && r[u] >= 0;
+          const f32x4* src = reinterpret_cast<const f32x4*>(a.y_perm + (int64_t)r[u] * a.d + (int64_t)c * VR);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[4 * q + i] = fmaf(w, v[i], acc[4 * q + i]);
+          for (int q = 0; q < YC; ++q) v[u][q] = use ? src[q] : (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+        }
+#pragma unroll
+        for (int u = 0; u < KG; ++u) {
+          const float w = __shfl(w_l, (j0 + u) & 63, 64);
+          if (j0 + u < a.k && r[u] >= 0) {                  // wave-uniform
+#pragma unroll
+            for (int q = 0; q < YC; ++q)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[4 * q + i] = fmaf(w, v[u][q][i], acc[4 * q + i]);
           }
         }
       }
@@ -69,8 +79,11 @@ __global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a) {
   }
 }
 
-// dY_perm[inv[t,j]] = w[t,j] * dy[t];  g[t,j] = <dy[t], y_perm[inv[t,j]]>
-template <typename T>
+// dY_perm[inv[t,j]] = w[t,j] * dy[t];  g[t,j] = <dy[t], y_perm[inv[t,j]]>.
+// Slots in batches of KG: the batch's y_perm rows and the dy row are loaded
+// together; each slot's dot product keeps its own order (row position, then
+// the butterfly).
+template <typename T, int KG>
 __global__ void __launch_bounds__(NT) combine_bwd_kernel(CombineBwdArgs a) {
   constexpr int VR = 16 / sizeof(T);
   constexpr int YC = VR / 4;
@@ -87,31 +100,51 @@ __global__ void __launch_bounds__(NT) combine_bwd_kernel(CombineBwdArgs a) {
       r_l = a.inv[t * a.k + lane];
       w_l = a.wts[t * a.k + lane];
     }
-    for (int j = 0; j < a.k; ++j) {
-      const int r = __shfl(r_l, j, 64);
-      const float w = __shfl(w_l, j, 64);
-      float dot = 0.0f;
+    for (int j0 = 0; j0 < a.k; j0 += KG) {
+      int r[KG];
+      float w[KG], dot[KG];
+#pragma unroll
+      for (int u = 0; u < KG; ++u) {
+        r[u] = __shfl(r_l, (j0 + u) & 63, 64);
+        w[u] = __shfl(w_l, (j0 + u) & 63, 64);
+        dot[u] = 0.0f;
+      }
       for (int c0 = 0; c0 < nch; c0 += 64) {
         const int c = c0 + lane;
-        if (c < nch && r >= 0) {
-          Chunk<T> dv, o;
-          dv.raw = ld16(dyb + t * rowbytes + (int64_t)c * 16);
-          const f32x4* src = reinterpret_cast<const f32x4*>(a.y_perm + (int64_t)r * a.d + (int64_t)c * VR);
+        const bool ok = c < nch;
+        Chunk<T> dv;
+        dv.raw = ok ? ld16(dyb + t * rowbytes + (int64_t)c * 16) : (u32x4){0u, 0u, 0u, 0u};
+        f32x4 yv[KG][YC];
 #pragma unroll
-          for (int q = 0; q < YC; ++q) {
-            const f32x4 yv = src[q];
+        for (int u = 0; u < KG; ++u) {
+          const bool use = ok && j0 + u < a.k && r[u] >= 0;
+          const f32x4* src = reinterpret_cast<const f32x4*>(a.y_perm + (int64_t)r[u] * a.d + (int64_t)c * VR);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float dd = to_f32<T>(dv.e[4 * q + i]);
-              dot = fmaf(dd, yv[i], dot);
-              o.e[4 * q + i] = from_f32<T>(w * dd);
-            }
+          for (int q = 0; q < YC; ++q) yv[u][q] = use ? src[q] : (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+        }
+#pragma unroll
+        for (int u = 0; u < KG; ++u) {
+          if (j0 + u < a.k && r[u] >= 0) {                  // wave-uniform
+            Chunk<T> o;
+#pragma unroll
+            for (int q = 0; q < YC; ++q)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float dd = to_f32<T>(dv.e[4 * q + i]);
+                dot[u] = fmaf(dd, yv[u][q][i], dot[u]);
+                o.e[4 * q + i] = from_f32<T>(w[u] * dd);
+              }
+            if (ok) st16(dyp + (int64_t)r[u] * rowbytes + (int64_t)c * 16, o.raw);
           }
-          st16(dyp + (int64_t)r * rowbytes + (int64_t)c * 16, o.raw);
         }
       }
-      dot = wave_sum(dot);
-      if (lane == 0) a.g[t * a.k + j] = dot;
+#pragma unroll
+      for (int u = 0; u < KG; ++u) {
+        if (j0 + u < a.k) {
+          const float ds = wave_sum(dot[u]);
+          if (lane == 0) a.g[t * a.k + j0 + u] = ds;
+        }
+      }
     }
   }
 }
@@ -450,7 +483,7 @@ __global__ void __launch_bounds__(NT) split_reduce_kernel(SplitReduceArgs a) {
 // router part is either sum_e dz[t, e] W_r[e] computed here (few experts) or
 // the f32 rows of a matrix-core product (dxr).  One wave per token, 16-byte
 // vectors along the row, fixed summation order.
-template <typename T>
+template <typename T, int KG>
 __global__ void __launch_bounds__(NT) unpermute_kernel(UnpermuteArgs a) {
   constexpr int VR = 16 / sizeof(T);
   const int lane = threadIdx.x & 63;
@@ -475,14 +508,22 @@ __global__ void __launch_bounds__(NT) unpermute_kernel(UnpermuteArgs a) {
       float acc[VR];
 #pragma unroll
       for (int i = 0; i < VR; ++i) acc[i] = 0.0f;
-#pragma unroll 4
-      for (int j = 0; j < a.k; ++j) {
-        const int r = __shfl(r_l, j, 64);
-        if (ok && r >= 0) {
-          Chunk<T> ch;
-          ch.raw = ld16(gp + (int64_t)r * rowbytes + (int64_t)c * 16);
+      // slots in batches of KG whose row loads are issued together
+      for (int j0 = 0; j0 < a.k; j0 += KG) {
+        Chunk<T> gv[KG];
+        int r[KG];
 #pragma unroll
-          for (int i = 0; i < VR; ++i) acc[i] += to_f32<T>(ch.e[i]);
+        for (int u = 0; u < KG; ++u) {
+          r[u] = __shfl(r_l, (j0 + u) & 63, 64);
+          const bool use = ok && j0 + u < a.k && r[u] >= 0;
+          gv[u].raw = use ? ld16(gp + (int64_t)r[u] * rowbytes + (int64_t)c * 16) : (u32x4){0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < KG; ++u) {
+          if (j0 + u < a.k && r[u] >= 0) {                  // wave-uniform
+#pragma unroll
+            for (int i = 0; i < VR; ++i) acc[i] += to_f32<T>(gv[u].e[i]);
+          }
         }
       }
       // (every lane stays in the loop: the router part below shuffles)
@@ -723,14 +764,24 @@ __global__ void __launch_bounds__(NT) aux_finalize_kernel(AuxArgs a, int nblk) {
 
 }  // namespace
 
+// Slots per batch of the gathering kernels: all k when k <= 4, else 8.
+inline int slot_batch(int k) { return k <= 2 ? 2 : (k <= 4 ? 4 : 8); }
+#define MOE_LAUNCH_SLOT_BATCH(KERN, TY)                                                   \
+  do {                                                                                    \
+    const int kg = slot_batch(a.k);                                                       \
+    if (kg == 2) hipLaunchKernelGGL((KERN<TY, 2>), dim3((unsigned)grid), dim3(NT), 0, s, a); \
+    else if (kg == 4) hipLaunchKernelGGL((KERN<TY, 4>), dim3((unsigned)grid), dim3(NT), 0, s, a); \
+    else hipLaunchKernelGGL((KERN<TY, 8>), dim3((unsigned)grid), dim3(NT), 0, s, a);     \
+  } while (0)
+
 hipError_t launch_combine(int dt, const CombineArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   int64_t grid = (a.T + 3) / 4;
   if (grid > 8192) grid = 8192;
   switch (dt) {
-    case DT_BF16: hipLaunchKernelGGL(combine_kernel<__bf16>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
-    case DT_F16: hipLaunchKernelGGL(combine_kernel<_Float16>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
-    case DT_F32: hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    case DT_BF16: MOE_LAUNCH_SLOT_BATCH(combine_kernel, __bf16); break;
+    case DT_F16: MOE_LAUNCH_SLOT_BATCH(combine_kernel, _Float16); break;
+    case DT_F32: MOE_LAUNCH_SLOT_BATCH(combine_kernel, float); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -741,9 +792,9 @@ hipError_t launch_combine_bwd(int dt, const CombineBwdArgs& a, hipStream_t s) {
   int64_t grid = (a.T + 3) / 4;
   if (grid > 8192) grid = 8192;
   switch (dt) {
-    case DT_BF16: hipLaunchKernelGGL(combine_bwd_kernel<__bf16>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
-    case DT_F16: hipLaunchKernelGGL(combine_bwd_kernel<_Float16>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
-    case DT_F32: hipLaunchKernelGGL(combine_bwd_kernel<float>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    case DT_BF16: MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, __bf16); break;
+    case DT_F16: MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, _Float16); break;
+    case DT_F32: MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, float); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -839,9 +890,9 @@ hipError_t launch_unpermute(int dt, const UnpermuteArgs& a, hipStream_t s) {
   int64_t grid = (a.T + 3) / 4;
   if (grid > 8192) grid = 8192;
   switch (dt) {
-    case DT_BF16: hipLaunchKernelGGL(unpermute_kernel<__bf16>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
-    case DT_F16: hipLaunchKernelGGL(unpermute_kernel<_Float16>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
-    case DT_F32: hipLaunchKernelGGL(unpermute_kernel<float>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    case DT_BF16: MOE_LAUNCH_SLOT_BATCH(unpermute_kernel, __bf16); break;
+    case DT_F16: MOE_LAUNCH_SLOT_BATCH(unpermute_kernel, _Float16); break;
+    case DT_F32: MOE_LAUNCH_SLOT_BATCH(unpermute_kernel, float); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
