@@ -581,10 +581,10 @@ moe_status mx_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, hipStream_
     mx_pq(a, xq, d, wgu, d, 2 * I * d);
     a.offsets = f->offsets; a.G = (int)E; a.M = A; a.N = (int)I; a.K = (int)d; a.sub = (int)I;
     a.C = f->gu; a.ldc = 2 * I; a.C2 = f->h; a.ldc2 = I;
+    a.Hq = hq.pay; a.Hs = hq.sc;                     // the epilogue also quantises H row-wise
     Probe pr(p, "gemm_gate_up_swiglu", s);
     MOE_TRY(launch_row_gemm(DT_MXFP8, OP_GU_FWD, EPI_SWIGLU_FWD, 128, a, s));
   }
-  MOE_TRY_STATUS(mx_rows(p, s, f->h, I, 0, (int)I, A, (int)I, hq));
   MOE_TRY_STATUS(mx_rows(p, s, f->w_down, I, 0, (int)I, E * d, (int)I, wd));
   {
     RowGemmArgs a{};
@@ -605,10 +605,10 @@ moe_status mx_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, hipStream_
       mx_pq(a, sxq, d, swgu, d, 0);
       a.offsets = nullptr; a.G = 1; a.M = T; a.N = (int)NI; a.K = (int)d; a.sub = (int)Is;
       a.C = f->gu_shared; a.ldc = 2 * NI; a.C2 = f->h_shared; a.ldc2 = NI;
+      a.Hq = shq.pay; a.Hs = shq.sc;                 // the epilogue also quantises H row-wise
       Probe pr(p, "gemm_gate_up_swiglu_shared", s);
       MOE_TRY(launch_row_gemm(DT_MXFP8, OP_GU_FWD, EPI_SWIGLU_FWD, 128, a, s));
     }
-    MOE_TRY_STATUS(mx_rows(p, s, f->h_shared, NI, 0, (int)NI, T, (int)NI, shq));
     // shared down weights [Ns][d][Is] concatenated along K into [d][NI]
     MOE_TRY_STATUS(mx_rows(p, s, f->ws_down, Is, d * Is, (int)Is, d, (int)NI, swd));
     {

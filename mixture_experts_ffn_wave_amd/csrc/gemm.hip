@@ -42,6 +42,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "mx_codec.h"
 
 namespace moe {
 namespace {
@@ -1058,7 +1059,27 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
           TO* gu = static_cast<TO*>(a.C) + row * a.ldc + gcol0 + c * 8;
           st16(gu, ld16(sp(0, sr, c)));
           st16(gu + a.sub, ld16(sp(1, sr, c)));
-          st16(static_cast<TO*>(a.C2) + row * a.ldc2 + n0 + c * 8, ld16(sp(2, sr, c)));
+          const u32x4 hraw = ld16(sp(2, sr, c));
+          st16(static_cast<TO*>(a.C2) + row * a.ldc2 + n0 + c * 8, hraw);
+          if constexpr (MX) {
+            // the stored H row-wise in MX-fp8 for the down projection: the
+            // four lanes of chunks 4b .. 4b+3 (one row, consecutive lanes)
+            // hold a 32-column block
+            if (a.Hq) {
+              float hv[8];
+              unpack8<TO>(hraw, hv);
+              float amax = 0.0f;
+#pragma unroll
+              for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(hv[q]));
+              amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+              amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+              const int x = mx_scale_exp(amax);
+              const float sc = ldexpf(1.0f, -x);
+              const u32x2 o = {e4m3x4(hv[0], hv[1], hv[2], hv[3], sc), e4m3x4(hv[4], hv[5], hv[6], hv[7], sc)};
+              st8(a.Hq + row * a.ldc2 + n0 + c * 8, o);
+              if ((c & 3) == 0) a.Hs[row * (a.ldc2 / 32) + (n0 + c * 8) / 32] = (uint8_t)(x + 127);
+            }
+          }
         } else if constexpr (EPI == EPI_SWIGLU_BWD) {
           TO* dgu = static_cast<TO*>(a.C) + row * a.ldc + gcol0 + c * 8;
           st16(dgu, ld16(sp(0, sr, c)));

@@ -70,6 +70,10 @@ struct RowGemmArgs {
   // DT_MXFP8 only: scale bytes of P ([rows][K/32], row stride ldp/32) and of
   // Q ([rows][K/32], row stride ldq/32, group stride q_group_stride/32)
   const uint8_t* Ps; const uint8_t* Qs;
+  // DT_MXFP8 with the SwiGLU epilogue: H also quantised along its rows
+  // (blocks of 32 columns) into Hq [rows][ldc2] and Hs [rows][ldc2/32]
+  // for the down projection; nullptr skips it
+  uint8_t* Hq; uint8_t* Hs;
 };
 // Output tile shapes (rows x columns): TILE_128 = 128 x 128 (every dtype),
 // TILE_256 = 256 x 256 and TILE_128x256 = 128 x 256 (16-bit types; the latter
@@ -96,6 +100,10 @@ struct WgradArgs {
   // segments at the padded offsets `offsets`, each a multiple of 128 tokens),
   // with scale bytes Ps [M][Kpad/32], Qs [N][Kpad/32].
   const uint8_t* Ps; const uint8_t* Qs;
+  // DT_MXFP8 with the SwiGLU epilogue: H also quantised along its rows
+  // (blocks of 32 columns) into Hq [rows][ldc2] and Hs [rows][ldc2/32]
+  // for the down projection; nullptr skips it
+  uint8_t* Hq; uint8_t* Hs;
 };
 // One kernel symbol per weight gradient (same tile engine) so profiles tell them apart.
 enum WgradOp { WG_DOWN = 0, WG_GATE_UP = 1, WG_ROUTER = 2 };

@@ -15,30 +15,12 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "mx_codec.h"
 
 namespace moe {
 namespace {
 
 constexpr int NT = 256;
-
-// smallest x with amax <= 448 * 2^x, clamped to [-127, 127]
-__device__ __forceinline__ int mx_scale_exp(float amax) {
-  if (!(amax > 0.0f)) return -127;
-  int e;
-  const float m = frexpf(amax, &e);          // amax = (2m) 2^(e-1), 2m in [1, 2); 448 = 1.75 * 2^8
-  const int x = (2.0f * m <= 1.75f) ? (e - 1) - 8 : (e - 1) - 7;
-  return x < -127 ? -127 : (x > 127 ? 127 : x);
-}
-
-// Four scaled values (|v| * 2^-x <= 448, so nothing saturates) to four e4m3
-// bytes, lowest first, with the hardware conversion (round to nearest even,
-// e4m3 subnormals).  Scaling by 2^-x is exact: for a 16-bit input x <= 120,
-// so 2^-x is a normal f32.
-__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d, float s) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a * s, b * s, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c * s, d * s, w, true);
-  return (uint32_t)w;
-}
 
 // Row operands: four lanes per 32-value block, eight values (one 16-byte
 // load) per lane, so a wave reads 1 KB and writes 512 bytes contiguously.
