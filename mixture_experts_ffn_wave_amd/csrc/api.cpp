@@ -652,13 +652,14 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
   }
   if (T > 0) {
     // dH = dY_perm W_d (reduction over d): W_d [E][d][I] transposed to [I][E d]
-    // dY_perm both ways in one pass: rows for this product, token blocks for dW_d
-    MOE_TRY_STATUS(mx_cols(p, s, dy_perm, d, (int)d, sv->offsets, pad, (int)E, 0, Apad / 32, 0, Apad, 0, dyt, dyq));
+    // dY_perm: its row-wise codes came from the combine backward; token blocks for dW_d
+    MOE_TRY_STATUS(mx_cols(p, s, dy_perm, d, (int)d, sv->offsets, pad, (int)E, 0, Apad / 32, 0, Apad, 0, dyt));
     MOE_TRY_STATUS(mx_cols(p, s, sv->w_down, I, (int)I, nullptr, nullptr, (int)E, (int)d, E * d / 32, 0, E * d, 0, wdt));
     RowGemmArgs a{};
     mx_pq(a, dyq, d, wdt, E * d, d);
     a.offsets = sv->offsets; a.G = (int)E; a.M = A; a.N = (int)I; a.K = (int)d; a.sub = (int)I;
     a.C = dgu; a.ldc = 2 * I; a.aux = sv->gu; a.ldaux = 2 * I;
+    a.Hq = dguq.pay; a.Hs = dguq.sc;                 // the epilogue also writes [dG | dU] row-wise
     Probe pr(p, "gemm_down_dgrad_swiglu", s);
     MOE_TRY(launch_row_gemm(DT_MXFP8, OP_DOWN_DGRAD, EPI_SWIGLU_BWD, 128, a, s));
   }
@@ -673,9 +674,8 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
   }
   if (T > 0) {
     // dX_perm = [dG | dU] W_gu (reduction over 2I): W_gu [E][2I][d] transposed to [d][E 2I]
-    // [dG | dU] both ways in one pass: rows for this product, token blocks for dW_gu
-    MOE_TRY_STATUS(mx_cols(p, s, dgu, 2 * I, (int)(2 * I), sv->offsets, pad, (int)E, 0, Apad / 32, 0, Apad, 0, dgut,
-                           dguq));
+    // [dG | dU]: row-wise codes from the SwiGLU-backward epilogue; token blocks for dW_gu
+    MOE_TRY_STATUS(mx_cols(p, s, dgu, 2 * I, (int)(2 * I), sv->offsets, pad, (int)E, 0, Apad / 32, 0, Apad, 0, dgut));
     MOE_TRY_STATUS(mx_cols(p, s, sv->w_gate_up, d, (int)d, nullptr, nullptr, (int)E, (int)(2 * I), E * 2 * I / 32, 0,
                            E * 2 * I, 0, wgut));
     RowGemmArgs a{};
@@ -786,6 +786,11 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
   if (p->T > 0) {
     {
       CombineBwdArgs a{dy, sv->y_perm, sv->inv_perm, sv->topk_w, dy_perm, g, p->T, d, k};
+      if (p->mx) {                                   // MX experts: dY_perm's row-wise codes too
+        const MxOp dyq = mxop(ws, p->mx_dyq);
+        a.q = dyq.pay;
+        a.qs = dyq.sc;
+      }
       Probe pr(p, "combine_bwd", s);
       MOE_TRY(launch_combine_bwd(p->dt, a, s));
     }

@@ -7,6 +7,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "mx_codec.h"
 
 namespace moe {
 namespace {
@@ -135,6 +136,26 @@ __global__ void __launch_bounds__(NT) combine_bwd_kernel(CombineBwdArgs a) {
                 o.e[4 * q + i] = from_f32<T>(w[u] * dd);
               }
             if (ok) st16(dyp + (int64_t)r[u] * rowbytes + (int64_t)c * 16, o.raw);
+            if constexpr (sizeof(T) == 2) {
+              // MX-fp8 experts: the row-wise codes of the stored values; the
+              // four lanes of chunks 4b .. 4b+3 hold one 32-value block
+              if (a.q) {
+                float ov[8];
+                unpack8<T>(o.raw, ov);
+                float amax = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(ov[i]));
+                amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+                amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+                const int x = mx_scale_exp(amax);
+                const float sc = ldexpf(1.0f, -x);
+                const u32x2 qv = {e4m3x4(ov[0], ov[1], ov[2], ov[3], sc), e4m3x4(ov[4], ov[5], ov[6], ov[7], sc)};
+                if (ok) {
+                  st8(a.q + (int64_t)r[u] * a.d + (int64_t)c * 8, qv);
+                  if ((c & 3) == 0) a.qs[(int64_t)r[u] * (a.d / 32) + c / 4] = (uint8_t)(x + 127);
+                }
+              }
+            }
           }
         }
       }

@@ -1082,8 +1082,31 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
           }
         } else if constexpr (EPI == EPI_SWIGLU_BWD) {
           TO* dgu = static_cast<TO*>(a.C) + row * a.ldc + gcol0 + c * 8;
-          st16(dgu, ld16(sp(0, sr, c)));
-          st16(dgu + a.sub, ld16(sp(1, sr, c)));
+          const u32x4 dgraw = ld16(sp(0, sr, c)), duraw = ld16(sp(1, sr, c));
+          st16(dgu, dgraw);
+          st16(dgu + a.sub, duraw);
+          if constexpr (MX) {
+            // [dG | dU] row-wise in MX-fp8 for the gate/up dgrad: four
+            // consecutive lanes hold a 32-column block of each half
+            if (a.Hq) {
+#pragma unroll
+              for (int half = 0; half < 2; ++half) {
+                float v8[8];
+                unpack8<TO>(half ? duraw : dgraw, v8);
+                float amax = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v8[q]));
+                amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+                amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+                const int x = mx_scale_exp(amax);
+                const float sc = ldexpf(1.0f, -x);
+                const u32x2 o = {e4m3x4(v8[0], v8[1], v8[2], v8[3], sc), e4m3x4(v8[4], v8[5], v8[6], v8[7], sc)};
+                const int64_t col = gcol0 + c * 8 + half * a.sub;
+                st8(a.Hq + row * a.ldc + col, o);
+                if ((c & 3) == 0) a.Hs[row * (a.ldc / 32) + col / 32] = (uint8_t)(x + 127);
+              }
+            }
+          }
         }
       }
     }

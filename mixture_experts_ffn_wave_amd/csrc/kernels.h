@@ -70,9 +70,10 @@ struct RowGemmArgs {
   // DT_MXFP8 only: scale bytes of P ([rows][K/32], row stride ldp/32) and of
   // Q ([rows][K/32], row stride ldq/32, group stride q_group_stride/32)
   const uint8_t* Ps; const uint8_t* Qs;
-  // DT_MXFP8 with the SwiGLU epilogue: H also quantised along its rows
-  // (blocks of 32 columns) into Hq [rows][ldc2] and Hs [rows][ldc2/32]
-  // for the down projection; nullptr skips it
+  // DT_MXFP8 with a SwiGLU epilogue, quantised along the rows (blocks of 32
+  // columns) for the next GEMM; nullptr skips it.  Forward: H into Hq
+  // [rows][ldc2], Hs [rows][ldc2/32].  Backward: [dG | dU] into Hq
+  // [rows][ldc], Hs [rows][ldc/32].
   uint8_t* Hq; uint8_t* Hs;
 };
 // Output tile shapes (rows x columns): TILE_128 = 128 x 128 (every dtype),
@@ -100,9 +101,10 @@ struct WgradArgs {
   // segments at the padded offsets `offsets`, each a multiple of 128 tokens),
   // with scale bytes Ps [M][Kpad/32], Qs [N][Kpad/32].
   const uint8_t* Ps; const uint8_t* Qs;
-  // DT_MXFP8 with the SwiGLU epilogue: H also quantised along its rows
-  // (blocks of 32 columns) into Hq [rows][ldc2] and Hs [rows][ldc2/32]
-  // for the down projection; nullptr skips it
+  // DT_MXFP8 with a SwiGLU epilogue, quantised along the rows (blocks of 32
+  // columns) for the next GEMM; nullptr skips it.  Forward: H into Hq
+  // [rows][ldc2], Hs [rows][ldc2/32].  Backward: [dG | dU] into Hq
+  // [rows][ldc], Hs [rows][ldc/32].
   uint8_t* Hq; uint8_t* Hs;
 };
 // One kernel symbol per weight gradient (same tile engine) so profiles tell them apart.
@@ -161,6 +163,9 @@ struct CombineBwdArgs {
   void* dy_perm;  // [T*k, d]
   float* g;       // [T, k]
   int64_t T; int d, k;
+  // MX-fp8 experts (16-bit layer): dY_perm also quantised along its rows
+  // (blocks of 32) into q [T*k, d] and qs [T*k, d/32]; nullptr skips it
+  uint8_t* q = nullptr; uint8_t* qs = nullptr;
 };
 hipError_t launch_combine_bwd(int dt, const CombineBwdArgs& a, hipStream_t s);
 
