@@ -431,11 +431,10 @@ moe_status mx_rows(moe_plan p, hipStream_t s, const void* in, int64_t ld_in, int
   return MOE_OK;
 }
 // transposed operand: the token axis of in [tokens][C] becomes K
-// (rows: the same operand also quantised along its rows, [token rows][C])
 moe_status mx_cols(moe_plan p, hipStream_t s, const void* in, int64_t ld_in, int C, const int32_t* seg,
                    const int32_t* pad, int G, int seg_len, int64_t nblk, int64_t k0, int64_t Kpad, int64_t row0,
-                   MxOp o, MxOp rows = MxOp{nullptr, nullptr}) {
-  MxColsArgs a{in, ld_in, C, seg, pad, G, seg_len, nblk, k0, Kpad, row0, o.pay, o.sc, rows.pay, rows.sc};
+                   MxOp o) {
+  MxColsArgs a{in, ld_in, C, seg, pad, G, seg_len, nblk, k0, Kpad, row0, o.pay, o.sc};
   Probe pr(p, "mx_quantize", s);
   MOE_TRY(launch_mx_quant_cols(p->dt, a, s));
   return MOE_OK;

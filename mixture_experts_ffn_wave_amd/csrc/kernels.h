@@ -101,11 +101,6 @@ struct WgradArgs {
   // segments at the padded offsets `offsets`, each a multiple of 128 tokens),
   // with scale bytes Ps [M][Kpad/32], Qs [N][Kpad/32].
   const uint8_t* Ps; const uint8_t* Qs;
-  // DT_MXFP8 with a SwiGLU epilogue, quantised along the rows (blocks of 32
-  // columns) for the next GEMM; nullptr skips it.  Forward: H into Hq
-  // [rows][ldc2], Hs [rows][ldc2/32].  Backward: [dG | dU] into Hq
-  // [rows][ldc], Hs [rows][ldc/32].
-  uint8_t* Hq; uint8_t* Hs;
 };
 // One kernel symbol per weight gradient (same tile engine) so profiles tell them apart.
 enum WgradOp { WG_DOWN = 0, WG_GATE_UP = 1, WG_ROUTER = 2 };
@@ -139,10 +134,6 @@ struct MxColsArgs {
   int64_t k0, Kpad, row0;
   uint8_t* out;        // [rows][Kpad]
   uint8_t* scales;     // [rows][Kpad/32]
-  // optional: the same input also quantised along its rows (blocks of 32
-  // columns), [token rows][C] and [token rows][C/32]; nullptr skips it
-  uint8_t* rout = nullptr;
-  uint8_t* rscales = nullptr;
 };
 hipError_t launch_mx_quant_cols(int dt, const MxColsArgs& a, hipStream_t s);
 

@@ -59,10 +59,7 @@ __global__ void __launch_bounds__(NT) mx_quant_rows_kernel(MxRowsArgs a) {
 // which is dead by then) so that each output row's 128-byte span (four
 // blocks) leaves as eight consecutive 16-byte stores and its four scale
 // bytes as one 4-byte store.  Tiles never straddle a segment: segment starts
-// (pad) and seg_len are multiples of 128.  With rout set (TC = 128), the
-// tile is also quantised along its rows (four 32-column blocks per token
-// row, whole 128-byte output spans), so an operand needed both ways is read
-// once.
+// (pad) and seg_len are multiples of 128.
 constexpr int kColsTileK = 128;
 constexpr int kColsOutRow = kColsTileK + 16;                // staged output row (padded: no bank conflicts)
 
@@ -110,32 +107,6 @@ __global__ void __launch_bounds__(NT) mx_quant_cols_kernel(MxColsArgs a) {
     *reinterpret_cast<u32x4*>(&tile[r][pc * VP]) = v;
   }
   __syncthreads();
-  // ---- row-wise blocks (optional): token row r, columns c0 + 32 b ..
-  if (TC == 128 && a.rout) {
-#pragma unroll
-    for (int i = 0; i < kColsTileK * (TC / 32) / NT; ++i) {
-      const int q = threadIdx.x + NT * i, r = q >> 2, b = q & 3;
-      const int cb = c0 + 32 * b;
-      if (tt0 + r < n && cb < a.C) {
-        float v[32];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) unpack8<T>(*reinterpret_cast<const u32x4*>(&tile[r][32 * b + 8 * u]), v + 8 * u);
-        float amax = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(v[e]));
-        const int x = mx_scale_exp(amax);
-        const float sc = ldexpf(1.0f, -x);
-        u32x4 o[2];
-#pragma unroll
-        for (int w = 0; w < 8; ++w) o[w >> 2][w & 3] = e4m3x4(v[4 * w], v[4 * w + 1], v[4 * w + 2], v[4 * w + 3], sc);
-        const int64_t row = tstart + tt0 + r;
-        uint8_t* dst = a.rout + row * a.C + cb;
-        st16(dst, o[0]);
-        st16(dst + 16, o[1]);
-        a.rscales[row * (a.C / 32) + cb / 32] = (uint8_t)(x + 127);
-      }
-    }
-  }
   // ---- token blocks: wave j, block j of the tile, columns lane (+ 64)
   constexpr int NCC = TC / 64;
   const int j = threadIdx.x >> 6, cl = threadIdx.x & 63;
@@ -235,23 +206,14 @@ hipError_t launch_mx_quant_rows(int dt, const MxRowsArgs& a, hipStream_t s) {
 hipError_t launch_mx_quant_cols(int dt, const MxColsArgs& a, hipStream_t s) {
   if (a.Kpad % kColsTileK || a.k0 % kColsTileK || a.C <= 0 || a.C % 8 || a.ld_in % 8) return hipErrorInvalidValue;
   if (!a.pad && (a.seg_len % kColsTileK)) return hipErrorInvalidValue;
-  if (a.rout && (a.C % 32 || !a.rscales)) return hipErrorInvalidValue;
   if (a.nblk <= 0) return hipSuccess;
   const int64_t tiles = (a.nblk * 32 + kColsTileK - 1) / kColsTileK;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  // 128-column tiles when the row-wise blocks ride along (whole 128-byte
-  // row spans); otherwise 64 columns, which measured faster
-  const int tc = a.rout ? 128 : 64;
+  constexpr int tc = 64;                                    // 64-column tiles measured faster than 128
   const dim3 grid((unsigned)tiles, (unsigned)((a.C + tc - 1) / tc));
   switch (dt) {
-    case DT_BF16:
-      if (a.rout) hipLaunchKernelGGL((mx_quant_cols_kernel<__bf16, 128>), grid, dim3(NT), 0, s, a);
-      else hipLaunchKernelGGL((mx_quant_cols_kernel<__bf16, 64>), grid, dim3(NT), 0, s, a);
-      break;
-    case DT_F16:
-      if (a.rout) hipLaunchKernelGGL((mx_quant_cols_kernel<_Float16, 128>), grid, dim3(NT), 0, s, a);
-      else hipLaunchKernelGGL((mx_quant_cols_kernel<_Float16, 64>), grid, dim3(NT), 0, s, a);
-      break;
+    case DT_BF16: hipLaunchKernelGGL((mx_quant_cols_kernel<__bf16, tc>), grid, dim3(NT), 0, s, a); break;
+    case DT_F16: hipLaunchKernelGGL((mx_quant_cols_kernel<_Float16, tc>), grid, dim3(NT), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
