@@ -194,61 +194,24 @@ __device__ __forceinline__ constexpr int acc_col(int r, int h) {
   return PERM ? 16 * (r >> 3) + 8 * h + (r & 7) : 8 * (r >> 2) + 4 * h + (r & 3);
 }
 
-// N fragments' worth of ds_read_b64_tr_b16 (two per fragment, at the given
-// LDS addresses) and the wait for them, in one assembly block: the results
-// are complete when the block ends, so no use or copy of them can be
-// scheduled before the data has arrived.
-template <int N> struct TrRead;
-#define MOE_TR8(o, a) "ds_read_b64_tr_b16 %" #o ", %" #a "\n\t"
-template <> struct TrRead<2> {
-  __device__ __forceinline__ static void run(u32x2 (&o)[4], const uint32_t (&a)[4]) {
-    asm volatile(MOE_TR8(0, 4) MOE_TR8(1, 5) MOE_TR8(2, 6) MOE_TR8(3, 7) "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
-                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]) : "memory");
+// Transposing fragment reads (ds_read_b64_tr_b16) through the builtin: the
+// compiler tracks each read and waits only for those an MFMA consumes.  The
+// buffer-to-LDS loads are inline assembly (dma4 / dma16 below), so the
+// compiler does not see them as LDS writes still in flight and adds no
+// vmcnt(0) before these reads; the ring barrier orders them instead.
+template <int M>
+__device__ __forceinline__ void tr_read(u32x2 (&o)[M], const uint32_t (&a)[M]) {
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(uintptr_t)a[i]);
+    o[i] = __builtin_bit_cast(u32x2, v);
   }
-};
-template <> struct TrRead<4> {
-  __device__ __forceinline__ static void run(u32x2 (&o)[8], const uint32_t (&a)[8]) {
-    asm volatile(MOE_TR8(0, 8) MOE_TR8(1, 9) MOE_TR8(2, 10) MOE_TR8(3, 11)
-                 MOE_TR8(4, 12) MOE_TR8(5, 13) MOE_TR8(6, 14) MOE_TR8(7, 15) "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]),
-                   "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
-                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
-                 : "memory");
-  }
-};
-template <> struct TrRead<6> {
-  __device__ __forceinline__ static void run(u32x2 (&o)[12], const uint32_t (&a)[12]) {
-    asm volatile(MOE_TR8(0, 12) MOE_TR8(1, 13) MOE_TR8(2, 14) MOE_TR8(3, 15)
-                 MOE_TR8(4, 16) MOE_TR8(5, 17) MOE_TR8(6, 18) MOE_TR8(7, 19)
-                 MOE_TR8(8, 20) MOE_TR8(9, 21) MOE_TR8(10, 22) MOE_TR8(11, 23) "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
-                   "=&v"(o[6]), "=&v"(o[7]), "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11])
-                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]),
-                   "v"(a[6]), "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11])
-                 : "memory");
-  }
-};
-template <> struct TrRead<8> {
-  __device__ __forceinline__ static void run(u32x2 (&o)[16], const uint32_t (&a)[16]) {
-    asm volatile(MOE_TR8(0, 16) MOE_TR8(1, 17) MOE_TR8(2, 18) MOE_TR8(3, 19)
-                 MOE_TR8(4, 20) MOE_TR8(5, 21) MOE_TR8(6, 22) MOE_TR8(7, 23)
-                 MOE_TR8(8, 24) MOE_TR8(9, 25) MOE_TR8(10, 26) MOE_TR8(11, 27)
-                 MOE_TR8(12, 28) MOE_TR8(13, 29) MOE_TR8(14, 30) MOE_TR8(15, 31) "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
-                   "=&v"(o[6]), "=&v"(o[7]), "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11]),
-                   "=&v"(o[12]), "=&v"(o[13]), "=&v"(o[14]), "=&v"(o[15])
-                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
-                   "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]), "v"(a[14]), "v"(a[15])
-                 : "memory");
-  }
-};
-#undef MOE_TR8
+}
 
 // MFMA work of one chunk for a wave: NS weight-side subtiles (LDS rows
 // qrow[ns]) x MS token-side subtiles (LDS rows prow[ms]).  Fragments of
-// compiler-read layouts are read first, then those of transposed layouts in
-// one TrRead block.
+// plain layouts are ordinary LDS loads; those of transposed layouts go
+// through tr_read.
 template <typename T, typename PO, typename QO, int NS, int MS, int KSTEPS = KB / sizeof(T) / 16,
           bool PERM = false>
 __device__ __forceinline__ void mfma_chunk(f32x16 (&acc)[NS][MS], const char* lq, const char* lp,
@@ -275,9 +238,8 @@ __device__ __forceinline__ void mfma_chunk(f32x16 (&acc)[NS][MS], const char* lq
     return;
   }
   if constexpr (NRAW > 0 && NRAW * KSTEPS <= 8 && (NRAW * KSTEPS) % 2 == 0) {
-    // Every k step's fragments of the chunk at once: the compiler-read ones
-    // first, then all transposed reads in one block whose single wait covers
-    // both, so the chunk's MFMAs run back to back after one LDS latency.
+    // Every k step's fragments of the chunk at once, plain ones first, then
+    // the transposed ones; each MFMA waits only for its own fragments.
     u32x4 fa[KSTEPS][NS][CH], fb[KSTEPS][MS][CH];
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -305,7 +267,13 @@ __device__ __forceinline__ void mfma_chunk(f32x16 (&acc)[NS][MS], const char* lq
         for (int ms = 0; ms < MS; ++ms) PO::template frag_addr<false>(ak + 2 * (PB + ms), lp, prow[ms], ks, lane);
       }
     }
-    TrRead<NRAW * KSTEPS>::run(raw, addr);
+    tr_read(raw, addr);
+    // every read of the chunk issues before the first MFMA; the MFMAs then
+    // run at raised wave priority so a wave that has its fragments keeps the
+    // matrix unit while the other waves on the SIMD issue their reads
+    __builtin_amdgcn_sched_group_barrier(0x100, 64, 0);    // DS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 64, 0);    // then MFMAs
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       const u32x2* rk = raw + 2 * NRAW * ks;
@@ -328,6 +296,7 @@ __device__ __forceinline__ void mfma_chunk(f32x16 (&acc)[NS][MS], const char* lq
 #pragma unroll
         for (int ms = 0; ms < MS; ++ms) Mma32<T>::run(acc[ns][ms], fa[ks][ns], fb[ks][ms]);
     }
+    __builtin_amdgcn_s_setprio(0);
     return;
   }
 #pragma unroll
@@ -353,7 +322,7 @@ __device__ __forceinline__ void mfma_chunk(f32x16 (&acc)[NS][MS], const char* lq
 #pragma unroll
         for (int ms = 0; ms < MS; ++ms) PO::template frag_addr<false>(addr + 2 * (PB + ms), lp, prow[ms], ks, lane);
       }
-      TrRead<NRAW>::run(raw, addr);
+      tr_read(raw, addr);
       if constexpr (QO::kRawLds) {
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns) {
@@ -460,11 +429,17 @@ constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
+// The LDS base goes in M0 (set by the compiler from the "{m0}" operand; the
+// s_nop covers the M0-write-to-LDS-DMA hazard).  The "memory" clobber keeps
+// LDS accesses from moving across; completion is tracked by the explicit
+// vmcnt waits of the ring barriers.
 __device__ __forceinline__ void dma4(rsrc_t rs, char* lds_lane0, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_lane0, 4, voff, 0, 0, 0);
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_lane0;
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(m0) : "memory");
 }
 __device__ __forceinline__ void dma16(rsrc_t rs, char* lds_lane0, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_lane0, 16, voff, 0, 0, 0);
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_lane0;
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(m0) : "memory");
 }
 
 // Tile configurations of the direct-load path (BM x BN output tiles):
@@ -535,12 +510,7 @@ struct DmaKmajor {                                 // [k][row], DKB/2 k-rows per
   static constexpr int NI = BYTES / 1024 / NW;
   static_assert(NI >= 1 && NI * 1024 * NW == BYTES, "tile must split evenly over the waves");
   static_assert(CPR >= 16, "swizzle needs at least 16 chunks per k-row");
-  // Fragments of this layout are read with ds_read_b64_tr_b16 issued as
-  // inline assembly (TrRead below), not the compiler builtin: the compiler
-  // treats the builtin as possibly reading LDS that an outstanding
-  // buffer-to-LDS load writes and waits for every such load (vmcnt(0)),
-  // which would drain the ring on every chunk.  The ring barrier already
-  // orders these reads after the loads they consume.
+  // Fragments of this layout are read with ds_read_b64_tr_b16 (tr_read).
   static constexpr bool kRawLds = true;
   __device__ __forceinline__ static int k_of(int w, int s, int lane) { return KPI * (w + NW * s) + lane / CPR; }
   __device__ __forceinline__ static int gchunk(int k, int lane) { return (lane % CPR) ^ (4 * (k & 3)); }
