@@ -502,9 +502,12 @@ __global__ void __launch_bounds__(NT) split_reduce_kernel(SplitReduceArgs a) {
 
 // dx[t] = sum_j dX_perm[inv[t, j]] (+ dx_shared[t]) + router part, where the
 // router part is either sum_e dz[t, e] W_r[e] computed here (few experts) or
-// the f32 rows of a matrix-core product (dxr).  One wave per token, 16-byte
-// vectors along the row, fixed summation order.
-template <typename T, int KG>
+// the f32 rows of a matrix-core product (dxr).  16-byte vectors along the row,
+// fixed summation order.  A wave takes TW tokens per pass (TW = 2 when a row
+// is at most 64 vectors and k <= 32): token u's slot indices and router
+// gradients sit in lanes 32 u + j, all TW tokens' row gathers issue together
+// and the router weight vectors are loaded once for both.
+template <typename T, int KG, int TW>
 __global__ void __launch_bounds__(NT) unpermute_kernel(UnpermuteArgs a) {
   constexpr int VR = 16 / sizeof(T);
   const int lane = threadIdx.x & 63;
@@ -516,81 +519,108 @@ __global__ void __launch_bounds__(NT) unpermute_kernel(UnpermuteArgs a) {
   const T* dz = static_cast<const T*>(a.dz_hl);
   const char* wr = static_cast<const char*>(a.w_router);
   char* out = static_cast<char*>(a.dx);
-  for (int64_t t = (int64_t)blockIdx.x * (NT / 64) + (threadIdx.x >> 6); t < a.T; t += waves) {
+  const int sub = TW > 1 ? lane >> 5 : 0, sl = TW > 1 ? lane & 31 : lane;   // token of this lane's slot / expert
+  for (int64_t tb = ((int64_t)blockIdx.x * (NT / 64) + (threadIdx.x >> 6)) * TW; tb < a.T; tb += waves * TW) {
+    int64_t t[TW];
+    bool tv[TW];
+#pragma unroll
+    for (int u = 0; u < TW; ++u) {
+      t[u] = tb + u;
+      tv[u] = t[u] < a.T;                                 // wave-uniform
+    }
+    const int64_t tm = tb + sub;
     int r_l = -1;
-    if (lane < a.k) r_l = a.inv[t * a.k + lane];
-    // router part inline (few experts): lane e < E holds dz[t][e] = hi + lo
+    if (sl < a.k && tm < a.T) r_l = a.inv[tm * a.k + sl];
+    // router part inline (few experts): lane 32 u + e holds dz[t_u][e] = hi + lo
     float z_l = 0.0f;
-    if (!a.dxr && lane < a.E)
-      z_l = to_f32<T>(dz[t * 2 * a.Ep + lane]) + to_f32<T>(dz[t * 2 * a.Ep + a.Ep + lane]);
+    if (!a.dxr && sl < a.E && tm < a.T)
+      z_l = to_f32<T>(dz[tm * 2 * a.Ep + sl]) + to_f32<T>(dz[tm * 2 * a.Ep + a.Ep + sl]);
     for (int c0 = 0; c0 < nch; c0 += 64) {
       const int c = c0 + lane;
       const bool ok = c < nch;
-      float acc[VR];
+      float acc[TW][VR];
 #pragma unroll
-      for (int i = 0; i < VR; ++i) acc[i] = 0.0f;
-      // slots in batches of KG whose row loads are issued together
+      for (int u = 0; u < TW; ++u)
+#pragma unroll
+        for (int i = 0; i < VR; ++i) acc[u][i] = 0.0f;
+      // slots in batches of KG (per token) whose row loads are issued together
       for (int j0 = 0; j0 < a.k; j0 += KG) {
-        Chunk<T> gv[KG];
-        int r[KG];
+        Chunk<T> gv[TW][KG];
+        int r[TW][KG];
 #pragma unroll
-        for (int u = 0; u < KG; ++u) {
-          r[u] = __shfl(r_l, (j0 + u) & 63, 64);
-          const bool use = ok && j0 + u < a.k && r[u] >= 0;
-          gv[u].raw = use ? ld16(gp + (int64_t)r[u] * rowbytes + (int64_t)c * 16) : (u32x4){0u, 0u, 0u, 0u};
-        }
+        for (int u = 0; u < TW; ++u)
 #pragma unroll
-        for (int u = 0; u < KG; ++u) {
-          if (j0 + u < a.k && r[u] >= 0) {                  // wave-uniform
-#pragma unroll
-            for (int i = 0; i < VR; ++i) acc[i] += to_f32<T>(gv[u].e[i]);
+          for (int q = 0; q < KG; ++q) {
+            r[u][q] = __shfl(r_l, (32 * u + j0 + q) & 63, 64);
+            const bool use = ok && tv[u] && j0 + q < a.k && r[u][q] >= 0;
+            gv[u][q].raw = use ? ld16(gp + (int64_t)r[u][q] * rowbytes + (int64_t)c * 16) : (u32x4){0u, 0u, 0u, 0u};
           }
-        }
+#pragma unroll
+        for (int u = 0; u < TW; ++u)
+#pragma unroll
+          for (int q = 0; q < KG; ++q) {
+            if (j0 + q < a.k && r[u][q] >= 0) {            // wave-uniform
+#pragma unroll
+              for (int i = 0; i < VR; ++i) acc[u][i] += to_f32<T>(gv[u][q].e[i]);
+            }
+          }
       }
       // (every lane stays in the loop: the router part below shuffles)
-      if (sp && ok) {
-        Chunk<T> ch;
-        ch.raw = ld16(sp + t * rowbytes + (int64_t)c * 16);
 #pragma unroll
-        for (int i = 0; i < VR; ++i) acc[i] += to_f32<T>(ch.e[i]);
-      }
-      if (a.dxr) {
-        if (ok) {
-          const f32x4* src = reinterpret_cast<const f32x4*>(a.dxr + t * a.d + (int64_t)c * VR);
+      for (int u = 0; u < TW; ++u) {
+        if (sp && ok && tv[u]) {
+          Chunk<T> ch;
+          ch.raw = ld16(sp + t[u] * rowbytes + (int64_t)c * 16);
+#pragma unroll
+          for (int i = 0; i < VR; ++i) acc[u][i] += to_f32<T>(ch.e[i]);
+        }
+        if (a.dxr && ok && tv[u]) {
+          const f32x4* src = reinterpret_cast<const f32x4*>(a.dxr + t[u] * a.d + (int64_t)c * VR);
 #pragma unroll
           for (int q = 0; q < VR / 4; ++q) {
             const f32x4 v = src[q];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[4 * q + i] += v[i];
+            for (int i = 0; i < 4; ++i) acc[u][4 * q + i] += v[i];
           }
         }
-      } else {
-        float rz[VR];
+      }
+      if (!a.dxr) {
+        float rz[TW][VR];
 #pragma unroll
-        for (int i = 0; i < VR; ++i) rz[i] = 0.0f;
+        for (int u = 0; u < TW; ++u)
+#pragma unroll
+          for (int i = 0; i < VR; ++i) rz[u][i] = 0.0f;
         // experts in groups of 8 whose weight loads are issued together
         for (int e0 = 0; e0 < a.E; e0 += 8) {
           Chunk<T> w[8];
 #pragma unroll
-          for (int u = 0; u < 8; ++u)
-            if (ok && e0 + u < a.E) w[u].raw = ld16(wr + (int64_t)(e0 + u) * rowbytes + (int64_t)c * 16);
+          for (int q = 0; q < 8; ++q)
+            if (ok && e0 + q < a.E) w[q].raw = ld16(wr + (int64_t)(e0 + q) * rowbytes + (int64_t)c * 16);
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const float z = __shfl(z_l, (e0 + u) & 63, 64);
-            if (e0 + u < a.E) {
+          for (int q = 0; q < 8; ++q) {
 #pragma unroll
-              for (int i = 0; i < VR; ++i) rz[i] = fmaf(z, to_f32<T>(w[u].e[i]), rz[i]);
+            for (int u = 0; u < TW; ++u) {
+              const float z = __shfl(z_l, (32 * u + e0 + q) & 63, 64);
+              if (e0 + q < a.E) {
+#pragma unroll
+                for (int i = 0; i < VR; ++i) rz[u][i] = fmaf(z, to_f32<T>(w[q].e[i]), rz[u][i]);
+              }
             }
           }
         }
 #pragma unroll
-        for (int i = 0; i < VR; ++i) acc[i] += rz[i];
-      }
-      if (ok) {
-        Chunk<T> o;
+        for (int u = 0; u < TW; ++u)
 #pragma unroll
-        for (int i = 0; i < VR; ++i) o.e[i] = from_f32<T>(acc[i]);
-        st16(out + t * rowbytes + (int64_t)c * 16, o.raw);
+          for (int i = 0; i < VR; ++i) acc[u][i] += rz[u][i];
+      }
+#pragma unroll
+      for (int u = 0; u < TW; ++u) {
+        if (ok && tv[u]) {
+          Chunk<T> o;
+#pragma unroll
+          for (int i = 0; i < VR; ++i) o.e[i] = from_f32<T>(acc[u][i]);
+          st16(out + t[u] * rowbytes + (int64_t)c * 16, o.raw);
+        }
       }
     }
   }
@@ -787,12 +817,12 @@ __global__ void __launch_bounds__(NT) aux_finalize_kernel(AuxArgs a, int nblk) {
 
 // Slots per batch of the gathering kernels: all k when k <= 4, else 8.
 inline int slot_batch(int k) { return k <= 2 ? 2 : (k <= 4 ? 4 : 8); }
-#define MOE_LAUNCH_SLOT_BATCH(KERN, TY)                                                   \
-  do {                                                                                    \
-    const int kg = slot_batch(a.k);                                                       \
-    if (kg == 2) hipLaunchKernelGGL((KERN<TY, 2>), dim3((unsigned)grid), dim3(NT), 0, s, a); \
-    else if (kg == 4) hipLaunchKernelGGL((KERN<TY, 4>), dim3((unsigned)grid), dim3(NT), 0, s, a); \
-    else hipLaunchKernelGGL((KERN<TY, 8>), dim3((unsigned)grid), dim3(NT), 0, s, a);     \
+#define MOE_LAUNCH_SLOT_BATCH(KERN, TY, ...)                                                         \
+  do {                                                                                               \
+    const int kg = slot_batch(a.k);                                                                  \
+    if (kg == 2) hipLaunchKernelGGL((KERN<TY, 2 __VA_OPT__(, ) __VA_ARGS__>), dim3((unsigned)grid), dim3(NT), 0, s, a); \
+    else if (kg == 4) hipLaunchKernelGGL((KERN<TY, 4 __VA_OPT__(, ) __VA_ARGS__>), dim3((unsigned)grid), dim3(NT), 0, s, a); \
+    else hipLaunchKernelGGL((KERN<TY, 8 __VA_OPT__(, ) __VA_ARGS__>), dim3((unsigned)grid), dim3(NT), 0, s, a); \
   } while (0)
 
 hipError_t launch_combine(int dt, const CombineArgs& a, hipStream_t s) {
@@ -906,17 +936,25 @@ hipError_t launch_split_reduce(int dt, const SplitReduceArgs& a, hipStream_t s) 
   return hipGetLastError();
 }
 
-hipError_t launch_unpermute(int dt, const UnpermuteArgs& a, hipStream_t s) {
-  if (a.T == 0) return hipSuccess;
-  int64_t grid = (a.T + 3) / 4;
+template <int TW>
+hipError_t launch_unpermute_tw(int dt, const UnpermuteArgs& a, hipStream_t s) {
+  int64_t grid = (a.T + 4 * TW - 1) / (4 * TW);
   if (grid > 8192) grid = 8192;
   switch (dt) {
-    case DT_BF16: MOE_LAUNCH_SLOT_BATCH(unpermute_kernel, __bf16); break;
-    case DT_F16: MOE_LAUNCH_SLOT_BATCH(unpermute_kernel, _Float16); break;
-    case DT_F32: MOE_LAUNCH_SLOT_BATCH(unpermute_kernel, float); break;
+    case DT_BF16: MOE_LAUNCH_SLOT_BATCH(unpermute_kernel, __bf16, TW); break;
+    case DT_F16: MOE_LAUNCH_SLOT_BATCH(unpermute_kernel, _Float16, TW); break;
+    case DT_F32: MOE_LAUNCH_SLOT_BATCH(unpermute_kernel, float, TW); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_unpermute(int dt, const UnpermuteArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  // two tokens per wave pass when a row is one pass of the wave and the slot
+  // indices / router gradients of a token fit in half a wave
+  const bool pair = (int64_t)a.d * dtype_bytes(dt) <= 64 * 16 && a.k <= 32 && (a.dxr || a.E <= 32);
+  return pair ? launch_unpermute_tw<2>(dt, a, s) : launch_unpermute_tw<1>(dt, a, s);
 }
 
 int aux_blocks(int64_t T) { return (int)((T + kAuxTokens - 1) / kAuxTokens); }

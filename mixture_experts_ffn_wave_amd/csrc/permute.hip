@@ -11,9 +11,10 @@
 //      counts[E], offsets[E+1] and the first output row of every
 //      (block, expert) pair (expert totals first, so every block's row is
 //      written once; several threads per expert share its blocks).
-//   3. permute_scatter: one wave per token computes its k destination rows,
-//      writes inv_perm / perm_token, reads the token's row of x once and
-//      writes it k times (every access a full 16-byte vector, rows contiguous).
+//   3. permute_scatter: a wave takes one token (or two, for rows of at most
+//      1 KB) per pass, computes its k destination rows, writes inv_perm /
+//      perm_token, reads the token's row of x once and writes it k times
+//      (every access a full 16-byte vector, rows contiguous).
 
 #include "common.h"
 #include "kernels.h"
@@ -125,7 +126,10 @@ __global__ void __launch_bounds__(NT) permute_scan(PermuteArgs a, int nblk) {
   }
 }
 
-template <typename T>
+// TW tokens per wave pass (TW = 2 when a row is at most 64 vectors and
+// k <= 32): token u's slots sit in lanes 32 u + j, and all TW rows are loaded
+// before any is stored.
+template <typename T, int TW>
 __global__ void __launch_bounds__(NT) permute_scatter(PermuteArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t waves = (int64_t)gridDim.x * (NT / 64);
@@ -133,27 +137,33 @@ __global__ void __launch_bounds__(NT) permute_scatter(PermuteArgs a) {
   const int nch = (int)(rowbytes / 16);
   const char* xb = static_cast<const char*>(a.x);
   char* xp = static_cast<char*>(a.x_perm);
-  for (int64_t t = (int64_t)blockIdx.x * (NT / 64) + (threadIdx.x >> 6); t < a.T; t += waves) {
+  const int sub = TW > 1 ? lane >> 5 : 0, sl = TW > 1 ? lane & 31 : lane;
+  for (int64_t tb = ((int64_t)blockIdx.x * (NT / 64) + (threadIdx.x >> 6)) * TW; tb < a.T; tb += waves * TW) {
+    const int64_t tm = tb + sub;
     int r_mine = -1;
-    if (lane < a.k) {
-      const int e = a.idx[t * a.k + lane];
+    if (sl < a.k && tm < a.T) {
+      const int e = a.idx[tm * a.k + sl];
       if ((unsigned)e < (unsigned)a.E) {
-        const int rank = a.inv[t * a.k + lane];
-        r_mine = a.block_base[(t / kHistTokens) * a.E + e] + rank;
-        a.perm_token[r_mine] = (int32_t)t;
+        const int rank = a.inv[tm * a.k + sl];
+        r_mine = a.block_base[(tm / kHistTokens) * a.E + e] + rank;
+        a.perm_token[r_mine] = (int32_t)tm;
       }
-      a.inv[t * a.k + lane] = r_mine;
+      a.inv[tm * a.k + sl] = r_mine;
     }
     // every lane runs the same number of iterations so the shuffles stay convergent
-    const char* src = xb + t * rowbytes;
     for (int c0 = 0; c0 < nch; c0 += 64) {
       const int c = c0 + lane;
       const bool ok = c < nch;
-      const u32x4 v = ok ? ld16(src + (int64_t)c * 16) : (u32x4){0u, 0u, 0u, 0u};
-      for (int j = 0; j < a.k; ++j) {
-        const int r = __shfl(r_mine, j, 64);
-        if (ok && r >= 0) st16(xp + (int64_t)r * rowbytes + (int64_t)c * 16, v);
-      }
+      u32x4 v[TW];
+#pragma unroll
+      for (int u = 0; u < TW; ++u)
+        v[u] = ok && tb + u < a.T ? ld16(xb + (tb + u) * rowbytes + (int64_t)c * 16) : (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int u = 0; u < TW; ++u)
+        for (int j = 0; j < a.k; ++j) {
+          const int r = __shfl(r_mine, (32 * u + j) & 63, 64);
+          if (ok && r >= 0) st16(xp + (int64_t)r * rowbytes + (int64_t)c * 16, v[u]);
+        }
     }
   }
 }
@@ -174,17 +184,23 @@ hipError_t launch_permute_scan(const PermuteArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_permute_scatter(int dt, const PermuteArgs& a, hipStream_t s) {
-  if (a.T == 0) return hipSuccess;
-  int64_t grid = (a.T + 3) / 4;
+template <int TW>
+hipError_t launch_permute_scatter_tw(int dt, const PermuteArgs& a, hipStream_t s) {
+  int64_t grid = (a.T + 4 * TW - 1) / (4 * TW);
   if (grid > 4096) grid = 4096;
   switch (dt) {
-    case DT_BF16: hipLaunchKernelGGL(permute_scatter<__bf16>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
-    case DT_F16: hipLaunchKernelGGL(permute_scatter<_Float16>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
-    case DT_F32: hipLaunchKernelGGL(permute_scatter<float>, dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    case DT_BF16: hipLaunchKernelGGL((permute_scatter<__bf16, TW>), dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    case DT_F16: hipLaunchKernelGGL((permute_scatter<_Float16, TW>), dim3((unsigned)grid), dim3(NT), 0, s, a); break;
+    case DT_F32: hipLaunchKernelGGL((permute_scatter<float, TW>), dim3((unsigned)grid), dim3(NT), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_permute_scatter(int dt, const PermuteArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  const bool pair = (int64_t)a.d * dtype_bytes(dt) <= 64 * 16 && a.k <= 32;
+  return pair ? launch_permute_scatter_tw<2>(dt, a, s) : launch_permute_scatter_tw<1>(dt, a, s);
 }
 
 }  // namespace moe
