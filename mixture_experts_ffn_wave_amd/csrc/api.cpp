@@ -703,7 +703,7 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
       MOE_TRY(launch_mx_single_segment(seg_pad, T, 128, s));
     }
     if (T > 0) {
-      MOE_TRY_STATUS(mx_rows(p, s, dy, d, 0, (int)d, T, (int)d, sdyq));
+      // dY's row-wise codes (sdyq) came from the combine backward
       for (int sh = 0; sh < p->Ns; ++sh)   // W_sd[s] [d][Is] -> rows s Is.. of [NI][d]
         MOE_TRY_STATUS(mx_cols(p, s, static_cast<const char*>(sv->ws_down) + (int64_t)sh * d * Is * 2, Is, (int)Is,
                                nullptr, nullptr, 1, (int)d, d / 32, 0, d, sh * Is, swdt));
@@ -711,6 +711,7 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
       mx_pq(a, sdyq, d, swdt, d, 0);
       a.offsets = nullptr; a.G = 1; a.M = T; a.N = (int)NI; a.K = (int)d; a.sub = (int)Is;
       a.C = dgu_s; a.ldc = 2 * NI; a.aux = sv->gu_shared; a.ldaux = 2 * NI;
+      a.Hq = sdguq.pay; a.Hs = sdguq.sc;             // the epilogue also writes [dG | dU] row-wise
       Probe pr(p, "gemm_down_dgrad_swiglu_shared", s);
       MOE_TRY(launch_row_gemm(DT_MXFP8, OP_DOWN_DGRAD, EPI_SWIGLU_BWD, 128, a, s));
     }
@@ -734,7 +735,6 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
                                "gemm_wgrad_gate_up_shared", s, DT_MXFP8));
     }
     if (T > 0) {
-      MOE_TRY_STATUS(mx_rows(p, s, dgu_s, 2 * NI, 0, (int)(2 * NI), T, (int)(2 * NI), sdguq));
       for (int sh = 0; sh < p->Ns; ++sh)   // W_sgu[s] [2Is][d] -> K positions s 2Is.. of [d][2 NI]
         MOE_TRY_STATUS(mx_cols(p, s, static_cast<const char*>(sv->ws_gate_up) + (int64_t)sh * 2 * Is * d * 2, d,
                                (int)d, nullptr, nullptr, 1, (int)(2 * Is), 2 * Is / 32, sh * 2 * Is, 2 * NI, 0, swgut));
@@ -789,6 +789,11 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
         const MxOp dyq = mxop(ws, p->mx_dyq);
         a.q = dyq.pay;
         a.qs = dyq.sc;
+        if (p->Ns > 0) {                             // and dY's, for the shared experts
+          const MxOp sdyq = mxop(ws, p->mx_sdyq);
+          a.dq = sdyq.pay;
+          a.dqs = sdyq.sc;
+        }
       }
       Probe pr(p, "combine_bwd", s);
       MOE_TRY(launch_combine_bwd(p->dt, a, s));

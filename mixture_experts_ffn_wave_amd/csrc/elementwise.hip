@@ -84,6 +84,28 @@ __global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a) {
 // Slots in batches of KG: the batch's y_perm rows and the dy row are loaded
 // together; each slot's dot product keeps its own order (row position, then
 // the butterfly).
+// MX-fp8 row-wise codes of one 16-byte chunk c (8 values) of a row: the four
+// lanes holding chunks 4b .. 4b+3 (consecutive lanes) form a 32-value block,
+// whose maximum they exchange; the lane of chunk 4b writes the scale byte.
+// Every lane of the wave calls this (the exchange is a shuffle).
+template <typename T>
+__device__ __forceinline__ void mx_row_codes(u32x4 raw, bool ok, uint8_t* q, uint8_t* qs, int c) {
+  float v[8];
+  unpack8<T>(raw, v);
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  const int x = mx_scale_exp(amax);
+  const float sc = ldexpf(1.0f, -x);
+  const u32x2 o = {e4m3x4(v[0], v[1], v[2], v[3], sc), e4m3x4(v[4], v[5], v[6], v[7], sc)};
+  if (ok) {
+    st8(q, o);
+    if ((c & 3) == 0) *qs = (uint8_t)(x + 127);
+  }
+}
+
 template <typename T, int KG>
 __global__ void __launch_bounds__(NT) combine_bwd_kernel(CombineBwdArgs a) {
   constexpr int VR = 16 / sizeof(T);
@@ -115,6 +137,9 @@ __global__ void __launch_bounds__(NT) combine_bwd_kernel(CombineBwdArgs a) {
         const bool ok = c < nch;
         Chunk<T> dv;
         dv.raw = ok ? ld16(dyb + t * rowbytes + (int64_t)c * 16) : (u32x4){0u, 0u, 0u, 0u};
+        if constexpr (sizeof(T) == 2) {
+          if (a.dq && j0 == 0) mx_row_codes<T>(dv.raw, ok, a.dq + t * a.d + (int64_t)c * 8, a.dqs + t * (a.d / 32) + c / 4, c);
+        }
         f32x4 yv[KG][YC];
 #pragma unroll
         for (int u = 0; u < KG; ++u) {
@@ -139,22 +164,9 @@ __global__ void __launch_bounds__(NT) combine_bwd_kernel(CombineBwdArgs a) {
             if constexpr (sizeof(T) == 2) {
               // MX-fp8 experts: the row-wise codes of the stored values; the
               // four lanes of chunks 4b .. 4b+3 hold one 32-value block
-              if (a.q) {
-                float ov[8];
-                unpack8<T>(o.raw, ov);
-                float amax = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(ov[i]));
-                amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-                amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-                const int x = mx_scale_exp(amax);
-                const float sc = ldexpf(1.0f, -x);
-                const u32x2 qv = {e4m3x4(ov[0], ov[1], ov[2], ov[3], sc), e4m3x4(ov[4], ov[5], ov[6], ov[7], sc)};
-                if (ok) {
-                  st8(a.q + (int64_t)r[u] * a.d + (int64_t)c * 8, qv);
-                  if ((c & 3) == 0) a.qs[(int64_t)r[u] * (a.d / 32) + c / 4] = (uint8_t)(x + 127);
-                }
-              }
+              if (a.q)
+                mx_row_codes<T>(o.raw, ok, a.q + (int64_t)r[u] * a.d + (int64_t)c * 8,
+                                a.qs + (int64_t)r[u] * (a.d / 32) + c / 4, c);
             }
           }
         }

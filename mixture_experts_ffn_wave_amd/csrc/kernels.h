@@ -157,6 +157,8 @@ struct CombineBwdArgs {
   // MX-fp8 experts (16-bit layer): dY_perm also quantised along its rows
   // (blocks of 32) into q [T*k, d] and qs [T*k, d/32]; nullptr skips it
   uint8_t* q = nullptr; uint8_t* qs = nullptr;
+  // and dY itself (the shared experts' output gradient) into dq [T, d], dqs [T, d/32]
+  uint8_t* dq = nullptr; uint8_t* dqs = nullptr;
 };
 hipError_t launch_combine_bwd(int dt, const CombineBwdArgs& a, hipStream_t s);
 
