@@ -228,7 +228,7 @@ def main():
                          "statistic over the real tokens only (0 = every token real)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (no collectives, no sharding); "
+        print("bench.py: the MoE layer path runs on one GPU only (no collectives, no sharding); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.traffic_calibration:
