@@ -171,6 +171,11 @@ typedef struct {
   void* gu_shared;         /* out [T, 2 Ns Is] act: expert s in columns [2 s Is, 2 (s+1) Is) as [G_s | U_s] */
   void* h_shared;          /* out [T, Ns Is] act: expert s in columns [s Is, (s+1) Is) */
   void* y_shared;          /* out [T, d] act: sum over shared experts */
+  /* Optional, MX-fp8 plans: perm_token [T*k] from moe_permute.  Given it,
+   * the gate/up GEMM gathers its rows on load from x quantised once per
+   * token (x must then be set) instead of quantising the T*k rows of x_perm;
+   * x_perm is not read.  NULL keeps the x_perm path.  Ignored otherwise. */
+  const int32_t* perm_token;
 } moe_ffn_args;
 
 /* Routed experts as grouped GEMMs over the expert segments of x_perm (gate/up
@@ -214,6 +219,10 @@ typedef struct {
    * moe_aux_stats_masked of the same step; NULL real_mask = every token. */
   const int32_t* real_mask;
   const int32_t* real_counts;
+  /* Optional, MX-fp8 plans: perm_token [T*k]; the weight gradient of the
+   * gate/up projection then gathers x's rows by it instead of reading
+   * x_perm (which may then be NULL).  Ignored otherwise. */
+  const int32_t* perm_token;
 } moe_saved;
 
 /* Gradient outputs (act dtype unless noted).  Every weight gradient is fully

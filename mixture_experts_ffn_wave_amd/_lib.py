@@ -29,10 +29,10 @@ class MoeConfig(ctypes.Structure):
 
 
 _FFN_FIELDS = ["x_perm", "offsets", "w_gate_up", "w_down", "gu", "h", "y_perm", "x", "ws_gate_up",
-               "ws_down", "gu_shared", "h_shared", "y_shared"]
+               "ws_down", "gu_shared", "h_shared", "y_shared", "perm_token"]
 _SAVED_FIELDS = ["x", "w_router", "probs", "topk_idx", "topk_w", "counts", "offsets", "inv_perm",
                  "x_perm", "gu", "h", "y_perm", "w_gate_up", "w_down", "ws_gate_up", "ws_down",
-                 "gu_shared", "h_shared", "real_mask", "real_counts"]
+                 "gu_shared", "h_shared", "real_mask", "real_counts", "perm_token"]
 _GRAD_FIELDS = ["dx", "dw_router", "dbias", "dw_gate_up", "dw_down", "dws_gate_up", "dws_down"]
 
 
@@ -153,6 +153,7 @@ class Plan:
         self.cfg = MoeConfig(T, d_model, n_experts, top_k, d_ff, n_shared, d_ff_shared, int(renorm),
                              int(has_router_bias), code, ecode, aux_coef)
         self.dtype = dtype
+        self.mx = ecode == MOE_MXFP8_E4M3                  # MX-fp8 experts
         self.T, self.d, self.E, self.k, self.I = T, d_model, n_experts, top_k, d_ff
         self.Ns, self.Is = n_shared, (d_ff_shared if n_shared else 0)
         self.renorm, self.has_bias, self.aux_coef = bool(renorm), bool(has_router_bias), aux_coef
@@ -225,7 +226,8 @@ def moe_permute(plan, topk_idx, x, counts, offsets, perm_token, inv_perm, x_perm
 
 
 def moe_expert_ffn(plan, x_perm, offsets, w_gate_up, w_down, gu, h, y_perm, x=None, ws_gate_up=None,
-                   ws_down=None, gu_shared=None, h_shared=None, y_shared=None, ws=None, stream=None):
+                   ws_down=None, gu_shared=None, h_shared=None, y_shared=None, ws=None, stream=None,
+                   perm_token=None):
     T, d, E, k, I, dt = plan.T, plan.d, plan.E, plan.k, plan.I, plan.dtype
     A = T * k
     _need(x_perm, "x_perm", (A, d), dt); _need(offsets, "offsets", (E + 1,), torch.int32)
@@ -244,6 +246,11 @@ def moe_expert_ffn(plan, x_perm, offsets, w_gate_up, w_down, gu, h, y_perm, x=No
         for n, t in [("x", x), ("ws_gate_up", ws_gate_up), ("ws_down", ws_down), ("gu_shared", gu_shared),
                      ("h_shared", h_shared), ("y_shared", y_shared)]:
             setattr(args, n, t.data_ptr())
+    if perm_token is not None:
+        _need(perm_token, "perm_token", (A,), torch.int32)
+        _need(x, "x", (T, d), dt)
+        args.perm_token = perm_token.data_ptr()
+        args.x = x.data_ptr()
     st = lib().moe_expert_ffn(plan.handle, ctypes.byref(args), _ptr(ws), ws.numel() if ws is not None else 0,
                               _stream(stream))
     _check("moe_expert_ffn", st)

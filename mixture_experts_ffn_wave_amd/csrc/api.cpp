@@ -433,8 +433,8 @@ moe_status mx_rows(moe_plan p, hipStream_t s, const void* in, int64_t ld_in, int
 // transposed operand: the token axis of in [tokens][C] becomes K
 moe_status mx_cols(moe_plan p, hipStream_t s, const void* in, int64_t ld_in, int C, const int32_t* seg,
                    const int32_t* pad, int G, int seg_len, int64_t nblk, int64_t k0, int64_t Kpad, int64_t row0,
-                   MxOp o) {
-  MxColsArgs a{in, ld_in, C, seg, pad, G, seg_len, nblk, k0, Kpad, row0, o.pay, o.sc};
+                   MxOp o, const int32_t* gather = nullptr) {
+  MxColsArgs a{in, ld_in, C, seg, pad, G, seg_len, nblk, k0, Kpad, row0, o.pay, o.sc, gather};
   Probe pr(p, "mx_quantize", s);
   MOE_TRY(launch_mx_quant_cols(p->dt, a, s));
   return MOE_OK;
@@ -516,8 +516,11 @@ moe_status moe_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, size_t ws
   if (!p || !f) return MOE_ERR_NULL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p->T == 0) return MOE_OK;
-  if (!f->x_perm || !f->offsets || !f->w_gate_up || !f->w_down || !f->gu || !f->h || !f->y_perm)
+  const bool gather = p->mx && f->perm_token;       // MX: token rows gathered from x on load
+  if ((!gather && !f->x_perm) || !f->offsets || !f->w_gate_up || !f->w_down || !f->gu || !f->h || !f->y_perm)
     return MOE_ERR_NULL;
+  if (gather && !f->x) return MOE_ERR_NULL;
+  if (gather && p->T * p->d >= (int64_t)1 << 31) return MOE_ERR_INVALID;   // 32-bit gather offsets
   if (p->Ns > 0 && (!f->x || !f->ws_gate_up || !f->ws_down || !f->gu_shared || !f->h_shared || !f->y_shared))
     return MOE_ERR_NULL;
   if (p->mx) {
@@ -573,11 +576,18 @@ moe_status moe_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, size_t ws
 moe_status mx_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, hipStream_t s) {
   const int64_t d = p->d, I = p->I, E = p->E, A = p->A;
   const MxOp xq = mxop(ws, p->mx_xq), hq = mxop(ws, p->mx_hq), wgu = mxop(ws, p->mx_wgu), wd = mxop(ws, p->mx_wd);
-  MOE_TRY_STATUS(mx_rows(p, s, f->x_perm, d, 0, (int)d, A, (int)d, xq));
+  // token rows: x quantised once per token and gathered by perm_token on load
+  // (into the shared experts' buffer when there are shared experts, which
+  // read the same codes), else the T*k rows of x_perm
+  const bool gather = f->perm_token != nullptr;
+  const MxOp xrows = (gather && p->Ns > 0) ? mxop(ws, p->mx_sxq) : xq;
+  if (gather) MOE_TRY_STATUS(mx_rows(p, s, f->x, d, 0, (int)d, p->T, (int)d, xrows));
+  else MOE_TRY_STATUS(mx_rows(p, s, f->x_perm, d, 0, (int)d, A, (int)d, xq));
   MOE_TRY_STATUS(mx_rows(p, s, f->w_gate_up, d, 0, (int)d, E * 2 * I, (int)d, wgu));
   {
     RowGemmArgs a{};
-    mx_pq(a, xq, d, wgu, d, 2 * I * d);
+    mx_pq(a, xrows, d, wgu, d, 2 * I * d);
+    if (gather) { a.gather = f->perm_token; a.p_rows = p->T; }
     a.offsets = f->offsets; a.G = (int)E; a.M = A; a.N = (int)I; a.K = (int)d; a.sub = (int)I;
     a.C = f->gu; a.ldc = 2 * I; a.C2 = f->h; a.ldc2 = I;
     a.Hq = hq.pay; a.Hs = hq.sc;                     // the epilogue also quantises H row-wise
@@ -597,7 +607,7 @@ moe_status mx_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, hipStream_
     const int64_t Is = p->Is, NI = p->Ns * p->Is, T = p->T;
     const MxOp sxq = mxop(ws, p->mx_sxq), shq = mxop(ws, p->mx_shq), swgu = mxop(ws, p->mx_swgu),
                swd = mxop(ws, p->mx_swd);
-    MOE_TRY_STATUS(mx_rows(p, s, f->x, d, 0, (int)d, T, (int)d, sxq));
+    if (!gather) MOE_TRY_STATUS(mx_rows(p, s, f->x, d, 0, (int)d, T, (int)d, sxq));
     MOE_TRY_STATUS(mx_rows(p, s, f->ws_gate_up, d, 0, (int)d, 2 * NI, (int)d, swgu));
     {
       RowGemmArgs a{};
@@ -685,7 +695,11 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
     MOE_TRY(launch_row_gemm(DT_MXFP8, OP_GU_DGRAD, EPI_STORE, 128, a, s));
   }
   {
-    MOE_TRY_STATUS(mx_cols(p, s, sv->x_perm, d, (int)d, sv->offsets, pad, (int)E, 0, Apad / 32, 0, Apad, 0, xt));
+    if (sv->perm_token)                        // x's rows gathered by perm_token (x_perm not read)
+      MOE_TRY_STATUS(mx_cols(p, s, sv->x, d, (int)d, sv->offsets, pad, (int)E, 0, Apad / 32, 0, Apad, 0, xt,
+                             sv->perm_token));
+    else
+      MOE_TRY_STATUS(mx_cols(p, s, sv->x_perm, d, (int)d, sv->offsets, pad, (int)E, 0, Apad / 32, 0, Apad, 0, xt));
     WgradArgs a{};
     a.P = dgut.pay; a.Ps = dgut.sc; a.ldp = Apad; a.Q = xt.pay; a.Qs = xt.sc; a.ldq = Apad;
     a.offsets = pad; a.G = (int)E; a.Mtok = Apad; a.M = (int)(2 * I); a.N = (int)d; a.sub = (int)d;
@@ -757,7 +771,8 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
   if (p->Ns > 0 && (!gr->dws_gate_up || !gr->dws_down)) return MOE_ERR_NULL;
   if (p->T > 0) {
     if (!dy || !gr->dx || !sv->x || !sv->w_router || !sv->probs || !sv->topk_idx || !sv->topk_w ||
-        !sv->counts || !sv->inv_perm || !sv->x_perm || !sv->gu || !sv->h || !sv->y_perm ||
+        !sv->counts || !sv->inv_perm || (!sv->x_perm && !(p->mx && sv->perm_token)) || !sv->gu || !sv->h ||
+        !sv->y_perm ||
         !sv->w_gate_up || !sv->w_down)
       return MOE_ERR_NULL;
     if (p->Ns > 0 && (!sv->ws_gate_up || !sv->ws_down || !sv->gu_shared || !sv->h_shared))

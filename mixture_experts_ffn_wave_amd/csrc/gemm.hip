@@ -712,12 +712,19 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
     constexpr int DSTAGE = PD::BYTES + QD::BYTES;
     constexpr int SSTAGE = (BM + BN) * 4;
     const int64_t pls = a.ldp / 32, qls = a.ldq / 32;          // scale bytes per row
-    const rsrc_t prs = make_rsrc(Pb + row0 * a.ldp, (uint32_t)(rows * a.ldp));
+    // token rows: this tile's rows of P, or rows of P picked by a.gather (then
+    // the descriptor spans all of P and rows past the tile read past its end)
+    const bool gat = a.gather != nullptr;
+    const rsrc_t prs = gat ? make_rsrc(Pb, (uint32_t)(a.p_rows * a.ldp))
+                           : make_rsrc(Pb + row0 * a.ldp, (uint32_t)(rows * a.ldp));
+    auto prow_src = [&](int r) -> int64_t {
+      return gat ? (r < rows ? (int64_t)a.gather[row0 + r] : a.p_rows) : (int64_t)r;
+    };
     uint32_t poff[PD::NI];
 #pragma unroll
     for (int s2 = 0; s2 < PD::NI; ++s2) {
       const int r = PD::row_of(wave, s2, lane);
-      poff[s2] = (uint32_t)(r * a.ldp + PD::gchunk(r, lane) * 16);
+      poff[s2] = (uint32_t)(prow_src(r) * a.ldp + PD::gchunk(r, lane) * 16);
     }
     // weight-side row of tile row q
     auto qsrc_row = [&](int q) -> int64_t {
@@ -738,8 +745,9 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
     const bool sq_side = wave >= 2;
     const int srow_t = (wave & 1) * 64 + lane;
     const uint8_t* qsb = a.Qs + (int64_t)g * (a.q_group_stride / 32);
-    const rsrc_t psrs = make_rsrc(a.Ps + row0 * pls, (uint32_t)(rows * pls));
-    const uint32_t soff = sq_side ? (uint32_t)(qsrc_row(srow_t) * qls) : (uint32_t)(srow_t * pls);
+    const rsrc_t psrs = gat ? make_rsrc(a.Ps, (uint32_t)(a.p_rows * pls))
+                            : make_rsrc(a.Ps + row0 * pls, (uint32_t)(rows * pls));
+    const uint32_t soff = sq_side ? (uint32_t)(qsrc_row(srow_t) * qls) : (uint32_t)(prow_src(srow_t) * pls);
     auto issue = [&](int kc, int st) {
       char* stage = smem + st * DSTAGE;
 #pragma unroll

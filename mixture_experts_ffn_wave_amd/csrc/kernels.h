@@ -75,6 +75,9 @@ struct RowGemmArgs {
   // [rows][ldc2], Hs [rows][ldc2/32].  Backward: [dG | dU] into Hq
   // [rows][ldc], Hs [rows][ldc/32].
   uint8_t* Hq; uint8_t* Hs;
+  // DT_MXFP8, optional: token-side row r is row gather[r] of P (and of Ps),
+  // P holding p_rows rows (p_rows * ldp < 2^31); nullptr reads row r itself
+  const int32_t* gather; int64_t p_rows;
 };
 // Output tile shapes (rows x columns): TILE_128 = 128 x 128 (every dtype),
 // TILE_256 = 256 x 256 and TILE_128x256 = 128 x 256 (16-bit types; the latter
@@ -134,6 +137,9 @@ struct MxColsArgs {
   int64_t k0, Kpad, row0;
   uint8_t* out;        // [rows][Kpad]
   uint8_t* scales;     // [rows][Kpad/32]
+  // optional: token t of a segment is row gather[seg start + t] of in
+  // (rows of x picked by perm_token instead of the rows of x_perm)
+  const int32_t* gather = nullptr;
 };
 hipError_t launch_mx_quant_cols(int dt, const MxColsArgs& a, hipStream_t s);
 

@@ -92,7 +92,7 @@ __global__ void __launch_bounds__(NT) mx_quant_cols_kernel(MxColsArgs a) {
   const int64_t tstart = a.seg ? a.seg[g] : (int64_t)g * a.seg_len;
   const int64_t n = a.seg ? (int64_t)(a.seg[g + 1] - a.seg[g]) : a.seg_len;
   const int64_t tt0 = p0 - pstart;                          // first token of the tile within the segment
-  const T* in = static_cast<const T*>(a.in) + tstart * a.ld_in;
+  const T* in = static_cast<const T*>(a.in) + (a.gather ? 0 : tstart * a.ld_in);
   // ---- load: 128 rows x 16 pieces of 16 bytes; rows past the segment and
   // columns past C read as zero
   constexpr int VP = 16 / (int)sizeof(T);                   // values per piece
@@ -103,7 +103,7 @@ __global__ void __launch_bounds__(NT) mx_quant_cols_kernel(MxColsArgs a) {
     const int col = c0 + pc * VP;
     const int64_t t = tt0 + r;
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (t < n && col < a.C) v = ld16(in + t * a.ld_in + col);
+    if (t < n && col < a.C) v = ld16(in + (a.gather ? (int64_t)a.gather[tstart + t] : t) * a.ld_in + col);
     *reinterpret_cast<u32x4*>(&tile[r][pc * VP]) = v;
   }
   __syncthreads();

@@ -23,6 +23,9 @@ class MoELayer:
         self.counts = z(E, dtype=torch.int32)
         self.offsets = z(E + 1, dtype=torch.int32)
         self.perm_token = z(A, dtype=torch.int32)
+        # MX experts: the gate/up GEMM and its weight gradient gather x's rows
+        # by perm_token instead of reading x_perm (False: the x_perm path)
+        self.mx_gather = plan.mx
         self.inv_perm = z(T, k, dtype=torch.int32)
         self.x_perm = z(A, d)
         self.gu = z(A, 2 * I)
@@ -95,7 +98,8 @@ class MoELayer:
                       self.inv_perm, self.x_perm, self.ws, stream)
         L.moe_expert_ffn(self.plan, self.x_perm, self.offsets, q["w_gate_up"], q["w_down"], self.gu,
                          self.h, self.y_perm, q["x"], q["ws_gate_up"], q["ws_down"], self.gu_shared,
-                         self.h_shared, self.y_shared, self.ws, stream)
+                         self.h_shared, self.y_shared, self.ws, stream,
+                         perm_token=self.perm_token if self.mx_gather else None)
         L.moe_combine(self.plan, self.y_perm, self.inv_perm, self.topk_w, self.y_shared, self.y, stream)
 
     def forward(self, stream=None):
@@ -111,7 +115,7 @@ class MoELayer:
                     x_perm=self.x_perm, gu=self.gu, h=self.h, y_perm=self.y_perm, w_gate_up=q["w_gate_up"],
                     w_down=q["w_down"], ws_gate_up=q["ws_gate_up"], ws_down=q["ws_down"],
                     gu_shared=self.gu_shared, h_shared=self.h_shared, real_mask=self.real_mask,
-                    real_counts=self.real_counts)
+                    real_counts=self.real_counts, perm_token=self.perm_token if self.mx_gather else None)
 
     def backward(self, dy, stream=None):
         L.moe_backward(self.plan, self.saved(), dy, self.grads, self.ws, stream)

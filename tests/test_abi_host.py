@@ -48,8 +48,8 @@ def test_version_and_status_strings():
 def test_struct_sizes_match_header_layout(tmp_path):
     assert ctypes.sizeof(L.MoeConfig) == 56          # int64 + 10 int32 + float, 8-aligned
     assert ctypes.sizeof(L.MoeAuxScalars) == 32
-    assert ctypes.sizeof(L.MoeFfnArgs) == 13 * 8
-    assert ctypes.sizeof(L.MoeSaved) == 20 * 8
+    assert ctypes.sizeof(L.MoeFfnArgs) == 14 * 8
+    assert ctypes.sizeof(L.MoeSaved) == 21 * 8
     assert ctypes.sizeof(L.MoeGrads) == 7 * 8
     # and the C compiler's layout of the header itself
     import shutil

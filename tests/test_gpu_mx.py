@@ -104,6 +104,32 @@ def test_mx_two_runs_are_bitwise_identical():
             assert np.array_equal(v, b[key]), key
 
 
+def test_mx_gather_on_load_equals_the_x_perm_path():
+    """The gate/up GEMM reading x's codes through perm_token, and the weight
+    gradient gathering x's rows, quantise the same values as the x_perm path
+    (x_perm[r] = x[perm_token[r]]), so every output is bitwise the same."""
+    wl = W("t700_d256_e8k3_i256_s1x128_mx_gather", T=700, d=256, E=8, k=3, I=256, n_shared=1, I_shared=128,
+           expert_dtype="mxfp8")
+    inp = MI.make_inputs(wl)
+    from mixture_experts_ffn_wave_amd import MoELayer
+    dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+    outs = []
+    for gather in (True, False):
+        layer = MoELayer(PT.plan_for(wl, inp.get("bias") is not None))
+        layer.mx_gather = gather
+        layer.set_params(dev["x"], dev["w_router"], dev["w_gate_up"], dev["w_down"],
+                         bias=(dev["bias"].float() if inp.get("bias") is not None else None),
+                         ws_gate_up=dev.get("ws_gate_up"), ws_down=dev.get("ws_down"))
+        layer.forward()
+        layer.backward(dev["dy"])
+        torch.cuda.synchronize()
+        o = {n: getattr(layer, n).clone() for n in ("gu", "h", "y_perm", "y", "gu_shared", "h_shared", "y_shared")}
+        o.update({n: t.clone() for n, t in layer.grads.items() if t is not None})
+        outs.append(o)
+    for key, v in outs[0].items():
+        assert torch.equal(v, outs[1][key]), key
+
+
 @pytest.mark.timeout(900)
 def test_mx_workload_full_size():
     PT.full_parity(MI.WORKLOADS["t16384_d2048_e64k6_i1408_s2x1408_mxfp8"], mx_diagnostic=False)
