@@ -150,7 +150,9 @@ moe_status moe_balance_update(moe_plan plan, const int32_t* counts, float* sel_b
  *   offsets    [E+1] int32 out: exclusive prefix sum of counts (offsets[E] = T*k)
  *   perm_token [T*k] int32 out: token of each expert-sorted row
  *   inv_perm   [T, k] int32 out: expert-sorted row of assignment (t, j)
- *   x_perm     [T*k, d] act out: x_perm[r] = x[perm_token[r]] */
+ *   x_perm     [T*k, d] act out: x_perm[r] = x[perm_token[r]]; or NULL (then x may be
+ *              NULL too): only the indices are produced, for MX-fp8 plans whose
+ *              expert GEMMs gather x's rows by perm_token */
 moe_status moe_permute(moe_plan plan, const int32_t* topk_idx, const void* x, int32_t* counts,
                        int32_t* offsets, int32_t* perm_token, int32_t* inv_perm, void* x_perm,
                        void* ws, size_t ws_bytes, void* stream);

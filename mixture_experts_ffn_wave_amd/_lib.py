@@ -218,7 +218,8 @@ def moe_permute(plan, topk_idx, x, counts, offsets, perm_token, inv_perm, x_perm
     _need(topk_idx, "topk_idx", (T, k), torch.int32); _need(x, "x", (T, d), dt)
     _need(counts, "counts", (E,), torch.int32); _need(offsets, "offsets", (E + 1,), torch.int32)
     _need(perm_token, "perm_token", (T * k,), torch.int32); _need(inv_perm, "inv_perm", (T, k), torch.int32)
-    _need(x_perm, "x_perm", (T * k, d), dt)
+    if x_perm is not None:                     # None: indices only (MX experts gathering on load)
+        _need(x_perm, "x_perm", (T * k, d), dt)
     st = lib().moe_permute(plan.handle, _ptr(topk_idx), _ptr(x), _ptr(counts), _ptr(offsets),
                            _ptr(perm_token), _ptr(inv_perm), _ptr(x_perm), _ptr(ws), ws.numel(),
                            _stream(stream))

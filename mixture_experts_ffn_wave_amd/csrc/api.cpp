@@ -487,7 +487,7 @@ moe_status moe_permute(moe_plan p, const int32_t* topk_idx, const void* x, int32
                        size_t ws_bytes, void* stream) {
   if (!p) return MOE_ERR_NULL;
   if (!counts || !offsets) return MOE_ERR_NULL;
-  if (p->T > 0 && (!topk_idx || !x || !perm_token || !inv_perm || !x_perm)) return MOE_ERR_NULL;
+  if (p->T > 0 && (!topk_idx || !perm_token || !inv_perm || (x_perm && !x))) return MOE_ERR_NULL;
   moe_status st = check_ws(p, ws, ws_bytes);
   if (st != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -106,7 +106,7 @@ __device__ __forceinline__ void mx_row_codes(u32x4 raw, bool ok, uint8_t* q, uin
   }
 }
 
-template <typename T, int KG>
+template <typename T, int KG, bool MXQ>
 __global__ void __launch_bounds__(NT) combine_bwd_kernel(CombineBwdArgs a) {
   constexpr int VR = 16 / sizeof(T);
   constexpr int YC = VR / 4;
@@ -137,7 +137,7 @@ __global__ void __launch_bounds__(NT) combine_bwd_kernel(CombineBwdArgs a) {
         const bool ok = c < nch;
         Chunk<T> dv;
         dv.raw = ok ? ld16(dyb + t * rowbytes + (int64_t)c * 16) : (u32x4){0u, 0u, 0u, 0u};
-        if constexpr (sizeof(T) == 2) {
+        if constexpr (MXQ && sizeof(T) == 2) {
           if (a.dq && j0 == 0) mx_row_codes<T>(dv.raw, ok, a.dq + t * a.d + (int64_t)c * 8, a.dqs + t * (a.d / 32) + c / 4, c);
         }
         f32x4 yv[KG][YC];
@@ -161,7 +161,7 @@ __global__ void __launch_bounds__(NT) combine_bwd_kernel(CombineBwdArgs a) {
                 o.e[4 * q + i] = from_f32<T>(w[u] * dd);
               }
             if (ok) st16(dyp + (int64_t)r[u] * rowbytes + (int64_t)c * 16, o.raw);
-            if constexpr (sizeof(T) == 2) {
+            if constexpr (MXQ && sizeof(T) == 2) {
               // MX-fp8 experts: the row-wise codes of the stored values; the
               // four lanes of chunks 4b .. 4b+3 hold one 32-value block
               if (a.q)
@@ -855,9 +855,17 @@ hipError_t launch_combine_bwd(int dt, const CombineBwdArgs& a, hipStream_t s) {
   int64_t grid = (a.T + 3) / 4;
   if (grid > 8192) grid = 8192;
   switch (dt) {
-    case DT_BF16: MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, __bf16); break;
-    case DT_F16: MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, _Float16); break;
-    case DT_F32: MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, float); break;
+    // the MX row-code writes are a separate instantiation, so the plain
+    // kernel carries none of their code
+    case DT_BF16:
+      if (a.q || a.dq) MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, __bf16, true);
+      else MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, __bf16, false);
+      break;
+    case DT_F16:
+      if (a.q || a.dq) MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, _Float16, true);
+      else MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, _Float16, false);
+      break;
+    case DT_F32: MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, float, false); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -150,6 +150,7 @@ __global__ void __launch_bounds__(NT) permute_scatter(PermuteArgs a) {
       }
       a.inv[tm * a.k + sl] = r_mine;
     }
+    if (!xp) continue;                                    // indices only (no row gather)
     // every lane runs the same number of iterations so the shuffles stay convergent
     for (int c0 = 0; c0 < nch; c0 += 64) {
       const int c = c0 + lane;

@@ -26,6 +26,9 @@ class MoELayer:
         # MX experts: the gate/up GEMM and its weight gradient gather x's rows
         # by perm_token instead of reading x_perm (False: the x_perm path)
         self.mx_gather = plan.mx
+        # x_perm is written only when something reads it: the non-MX experts,
+        # the x_perm path, or a caller that inspects it (write_x_perm = True)
+        self.write_x_perm = False
         self.inv_perm = z(T, k, dtype=torch.int32)
         self.x_perm = z(A, d)
         self.gu = z(A, 2 * I)
@@ -94,8 +97,9 @@ class MoELayer:
 
     def dispatch_and_experts(self, stream=None):
         q = self.params
+        xp = self.x_perm if (self.write_x_perm or not self.mx_gather) else None
         L.moe_permute(self.plan, self.topk_idx, q["x"], self.counts, self.offsets, self.perm_token,
-                      self.inv_perm, self.x_perm, self.ws, stream)
+                      self.inv_perm, xp, self.ws, stream)
         L.moe_expert_ffn(self.plan, self.x_perm, self.offsets, q["w_gate_up"], q["w_down"], self.gu,
                          self.h, self.y_perm, q["x"], q["ws_gate_up"], q["ws_down"], self.gu_shared,
                          self.h_shared, self.y_shared, self.ws, stream,
