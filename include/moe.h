@@ -324,9 +324,36 @@ const char* moe_kernel_names(void);
  *   "dx_perm"     [T*top_k, d_model]     input gradient of the expert rows
  *   "dgu_shared"  [T, 2 n_shared d_ff_shared]  [dG_s | dU_s] per shared expert
  *   "dx_shared"   [T, d_model]           input gradient of the shared experts
+ * Plans with MX-fp8 experts also expose the quantised operand of every
+ * expert GEMM, each as "<name>" (e4m3 payload bytes, [rows][K]) and
+ * "<name>.scales" (UE8M0 bytes = exponent + 127, [rows][K/32]), blocks of 32
+ * along K; A = T*top_k, Apad = the expert segments' token counts rounded up
+ * to multiples of 128 and summed (plus headroom), Tpad = T rounded up to 128,
+ * NI = n_shared * d_ff_shared:
+ *   row operands (K = the contraction of the GEMM reading them)
+ *   "mx_xq"   [A][d]       x_perm (x_perm path) or x's T rows (gather path,
+ *                          routed experts only)
+ *   "mx_hq"   [A][d_ff]    H (written by the gate/up epilogue)
+ *   "mx_dyq"  [A][d]       dY_perm (written by the combine backward)
+ *   "mx_dguq" [A][2 d_ff]  [dG | dU] (written by the SwiGLU-backward epilogue)
+ *   "mx_wgu"  [E 2 d_ff][d]   "mx_wd" [E d][d_ff]   expert weights
+ *   "mx_wdt"  [d_ff][E d]     "mx_wgut" [d][E 2 d_ff]  weights along d / 2 d_ff
+ *   token-axis operands of the weight gradients ([C][Apad]; expert e's tokens
+ *   at K positions mx_pad[e] .. mx_pad[e] + count_e, blocks of 32 restarting
+ *   at mx_pad[e], zeros up to mx_pad[e+1])
+ *   "mx_dyt" [d][Apad]  "mx_ht" [d_ff][Apad]  "mx_dgut" [2 d_ff][Apad]  "mx_xt" [d][Apad]
+ *   "mx_pad" [E+1] int32, the padded segment starts
+ *   shared experts (n_shared > 0): "mx_sxq" [T][d] (x, also read by the routed
+ *   experts on the gather path), "mx_shq" [T][NI], "mx_sdyq" [T][d] (dY),
+ *   "mx_sdguq" [T][2 NI], "mx_swgu" [2 NI][d], "mx_swd" [d][NI],
+ *   "mx_swdt" [NI][d], "mx_swgut" [d][2 NI], and token-axis (one segment of
+ *   T tokens, zeros up to Tpad) "mx_sdyt" [d][Tpad], "mx_sht" [NI][Tpad],
+ *   "mx_sdgut" [2 NI][Tpad], "mx_sxt" [d][Tpad].
+ * Each holds what the last call that wrote it left there.
  * For tests and debugging, e.g. to check each GEMM of the backward on its
  * own inputs.  MOE_ERR_NULL for a null argument, MOE_ERR_INVALID for an
- * unknown name or a region this plan does not have (no shared experts). */
+ * unknown name or a region this plan does not have (no shared experts, not
+ * an MX plan). */
 moe_status moe_workspace_region(moe_plan plan, const char* name, size_t* offset, size_t* bytes);
 
 #ifdef __cplusplus

@@ -204,6 +204,34 @@ moe_status moe_workspace_region(moe_plan p, const char* name, size_t* offset, si
     o = p->o_dgu_s; b = (size_t)p->T * 2 * p->Ns * p->Is * es;
   } else if (n == "dx_shared" && p->Ns > 0) {
     o = p->o_dxs; b = (size_t)p->T * p->d * es;
+  } else if (p->mx && n == "mx_pad") {
+    o = p->o_mx_pad; b = (size_t)(p->E + 1) * 4;
+  } else if (p->mx && n.rfind("mx_", 0) == 0) {
+    // MX operand codes: "<buffer>" is the e4m3 payload, "<buffer>.scales" its scale bytes
+    const bool sc = n.size() > 7 && n.compare(n.size() - 7, 7, ".scales") == 0;
+    const std::string base = sc ? n.substr(0, n.size() - 7) : n;
+    const int64_t A = p->A, T = p->T, d = p->d, I = p->I, E = p->E, NI = (int64_t)p->Ns * p->Is;
+    struct Entry { const char* name; const moe_plan_s::MxBuf* buf; int64_t rows, K; bool shared; };
+    const Entry tab[] = {
+        {"mx_xq", &p->mx_xq, A, d, false},       {"mx_hq", &p->mx_hq, A, I, false},
+        {"mx_wgu", &p->mx_wgu, E * 2 * I, d, false}, {"mx_wd", &p->mx_wd, E * d, I, false},
+        {"mx_dyq", &p->mx_dyq, A, d, false},     {"mx_wdt", &p->mx_wdt, I, E * d, false},
+        {"mx_dguq", &p->mx_dguq, A, 2 * I, false}, {"mx_wgut", &p->mx_wgut, d, E * 2 * I, false},
+        {"mx_dyt", &p->mx_dyt, d, p->Apad, false}, {"mx_ht", &p->mx_ht, I, p->Apad, false},
+        {"mx_dgut", &p->mx_dgut, 2 * I, p->Apad, false}, {"mx_xt", &p->mx_xt, d, p->Apad, false},
+        {"mx_sxq", &p->mx_sxq, T, d, true},      {"mx_shq", &p->mx_shq, T, NI, true},
+        {"mx_swgu", &p->mx_swgu, 2 * NI, d, true}, {"mx_swd", &p->mx_swd, d, NI, true},
+        {"mx_sdyq", &p->mx_sdyq, T, d, true},    {"mx_swdt", &p->mx_swdt, NI, d, true},
+        {"mx_sdguq", &p->mx_sdguq, T, 2 * NI, true}, {"mx_swgut", &p->mx_swgut, d, 2 * NI, true},
+        {"mx_sdyt", &p->mx_sdyt, d, p->Tpad, true}, {"mx_sht", &p->mx_sht, NI, p->Tpad, true},
+        {"mx_sdgut", &p->mx_sdgut, 2 * NI, p->Tpad, true}, {"mx_sxt", &p->mx_sxt, d, p->Tpad, true},
+    };
+    const Entry* hit = nullptr;
+    for (const Entry& t : tab)
+      if (base == t.name) hit = &t;
+    if (!hit || (hit->shared && p->Ns == 0)) return MOE_ERR_INVALID;
+    o = sc ? hit->buf->sc : hit->buf->pay;
+    b = (size_t)hit->rows * (sc ? hit->K / 32 : hit->K);
   } else {
     return MOE_ERR_INVALID;
   }
