@@ -5,20 +5,25 @@ expert FFN (grouped GEMMs), combine, backward (all gradients) and the
 balancing statistic -- the six C-ABI calls, back to back on one stream.
 Inputs are resident in HBM before the timed region starts.
 
-Prints ONE JSON line (rank 0, N = 1): tokens/s over K timed steps, plus
+The default workload is the largest single-GPU one: 32768 tokens, d_model
+1536, 4 routed experts top-2 plus one shared expert, SwiGLU width 3072, f16.
+
+Prints ONE JSON line (rank 0, N = 1).  The timed region is K steps, each after
+a 1 GiB scratch write that evicts the 256 MB last-level cache and the L2s (so
+no operand is left on chip), with hipEvents on the stream around every step;
+``value`` = T / the median of those per-step times (tokens/s) and
+``ms_per_step`` that median.  Plus
   roofline      -- the dominant kernel's algorithmic FLOPs per launch over its
                    average launch time (hipEvents recorded around that kernel
-                   inside the timed region), against the bf16 MFMA peak, and
-                   its measured HBM bytes per launch ("traffic") when a
-                   counter summary of the current kernel sources exists under
-                   profiles/ (else null);
+                   inside the timed region), against the MFMA peak of its
+                   dtype, and its measured HBM bytes per launch ("traffic")
+                   when a counter summary of the current kernel sources exists
+                   under profiles/ (else null);
   cpu_baseline  -- the fp64 numpy oracle timed on the host on a bounded
-                   sample of the same workload;
-  step_ms       -- after the timed region, per-step times (hipEvents on the
-                   stream around each step): median / p10 / p90 with the
-                   caches warm, and again with a 1 GiB scratch write before
-                   every step so that no operand is left in the 256 MB
-                   last-level cache or the L2s ("flushed").
+                   sample of the same workload, with the BLAS library, its
+                   threads and a single-thread pass of the tiny workload;
+  step_ms       -- the flushed per-step distribution (median / p10 / p90) and,
+                   after the timed region, the same with the caches warm.
 Per-kernel times go to stderr.
 
 --traffic-calibration runs only a plain streaming kernel of known size (an
@@ -94,7 +99,7 @@ def make_layer(wl, device="cuda"):
 # probe name of a GEMM launch -> prefix of its kernel symbol (dtype and tile follow)
 KERNEL_SYMBOL = {
     "gemm_gate_up_swiglu": "moe_gemm_gate_up_swiglu",
-    "gemm_down": "moe_gemm_down_f32out",
+    "gemm_down": "moe_gemm_down",
     "gemm_down_dgrad_swiglu": "moe_gemm_down_dgrad_swiglu",
     "gemm_gate_up_dgrad": "moe_gemm_gate_up_dgrad",
     "gemm_wgrad_down": "moe_wgrad_down",
@@ -183,20 +188,29 @@ def step_distribution(layer, dy, steps, flush_bytes=0):
     return {"median": q(0.5), "p10": q(0.1), "p90": q(0.9), "steps": len(times)}
 
 
-def cpu_baseline(wl, budget_s=12.0):
-    """The fp64 oracle, untuned, on the host cores: whole fwd+bwd+aux passes of
-    the same workload until ~budget_s of CPU time has run (at least one)."""
-    import numpy as np  # noqa: F401
+def _oracle_pass(O, wl, f):
+    fwd = O.layer_forward(f["x"], f["w_router"], f["w_gate_up"], f["w_down"], top_k=wl.k, renorm=wl.renorm,
+                          bias=f["bias"], ws_gate_up=f.get("ws_gate_up"), ws_down=f.get("ws_down"))
+    O.layer_backward(fwd, f["dy"], aux_coef=wl.aux_coef)
+    O.aux_statistics(fwd["p"], fwd["counts"], wl.k)
+
+
+def cpu_baseline(wl, budget_s=12.0, sample_tokens=2048):
+    """The fp64 oracle, untuned, on the host cores, on a bounded sample of the
+    workload: whole fwd+bwd+aux passes over the first ``sample_tokens`` tokens
+    of the same synthetic batch (same d, experts, k, inner widths, shared
+    experts and router bias; the routing is the sample's own) until ~budget_s
+    have run, reported as tokens/s.  Also the BLAS library and its thread
+    count, and one pass of the tiny f32 workload on one BLAS thread."""
     import oracle as O
+    from threadpoolctl import threadpool_info, threadpool_limits
     inp = MI.make_inputs(wl)
-    f = {k: MI.to_f64(v) for k, v in inp.items()}
+    Ts = min(wl.T, sample_tokens)
+    f = {k: (MI.to_f64(v[:Ts]) if k in ("x", "dy") else MI.to_f64(v)) for k, v in inp.items()}
+    swl = wl.with_(T=Ts)
     runs, t0 = 0, time.perf_counter()
     while True:
-        fwd = O.layer_forward(f["x"], f["w_router"], f["w_gate_up"], f["w_down"], top_k=wl.k,
-                              renorm=wl.renorm, bias=f["bias"], ws_gate_up=f.get("ws_gate_up"),
-                              ws_down=f.get("ws_down"))
-        O.layer_backward(fwd, f["dy"], aux_coef=wl.aux_coef)
-        O.aux_statistics(fwd["p"], fwd["counts"], wl.k)
+        _oracle_pass(O, swl, f)
         runs += 1
         el = time.perf_counter() - t0
         if el >= budget_s or runs >= 50:
@@ -205,10 +219,20 @@ def cpu_baseline(wl, budget_s=12.0):
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
-    threads = int(os.environ.get("OPENBLAS_NUM_THREADS", os.environ.get("OMP_NUM_THREADS", cores)))
-    return {"value": wl.T * runs / el, "unit": "tokens/s", "cores": min(cores, threads), "kind": "oracle",
-            "sample": f"{runs} full fwd+bwd+aux pass(es) of the {wl.name} workload in float64 numpy "
-                      f"({el:.1f} s wall)"}
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    threads = blas[0]["num_threads"] if blas else 1
+    vendor = f"{blas[0]['internal_api']} {blas[0].get('version', '')}".strip() if blas else "none"
+    tiny = MI.WORKLOADS[MI.TINY]
+    ft = {k: MI.to_f64(v) for k, v in MI.make_inputs(tiny).items()}
+    with threadpool_limits(limits=1, user_api="blas"):
+        t1 = time.perf_counter()
+        _oracle_pass(O, tiny, ft)
+        tiny_s = time.perf_counter() - t1
+    return {"value": Ts * runs / el, "unit": "tokens/s", "cores": min(cores, threads), "kind": "oracle",
+            "sample": f"{runs} fwd+bwd+aux pass(es) of the first {Ts} of {wl.T} tokens of the {wl.name} "
+                      f"workload in float64 numpy ({el:.1f} s wall)",
+            "blas": vendor, "blas_threads": threads, "host_cores": cores,
+            "single_core_tiny_s": tiny_s, "single_core_tiny_workload": tiny.name}
 
 
 def main():
@@ -216,7 +240,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=MI.BENCH)
+    ap.add_argument("--workload", default=MI.LARGEST)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--traffic-calibration", action="store_true")
@@ -262,25 +286,40 @@ def main():
     expert_gemms = {n: v for n, v in gemms.items() if "router" not in n}
     dominant = max(gemms, key=lambda n: gemms[n][0] * gemms[n][1]) if gemms else "gemm_gate_up_swiglu"
 
-    # ---- timed region (dominant kernel bracketed by hipEvents on its stream)
+    # ---- timed region: K steps, each after a 1 GiB scratch write that evicts
+    # the 256 MB last-level cache and the L2s, so no operand is left on chip;
+    # per-step hipEvents on the stream around each step, and the dominant
+    # kernel's launches bracketed by hipEvents on the stream it runs on
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     probe_enable(layer.plan, dominant, args.steps * 4)
     torch.cuda.synchronize()
+    times = []
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        scratch.fill_(i & 0xFF)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
         layer.step(dy)
+        e1.record()
+        times.append((e0, e1))
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     ms_total, launches = probe_read(layer.plan)
     probe_enable(layer.plan, dominant, 0)
+    del scratch
+    step_ms = sorted(a.elapsed_time(b) for a, b in times)
+    q = lambda f: step_ms[min(len(step_ms) - 1, int(round(f * (len(step_ms) - 1))))]
+    flushed = {"median": q(0.5), "p10": q(0.1), "p90": q(0.9), "steps": len(step_ms)}
 
-    ms_step = el * 1e3 / args.steps
+    ms_step = flushed["median"]
     avg_ms = ms_total / max(launches, 1)
     achieved = flops[dominant] / (avg_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.expert_dtype or wl.dtype]
     gemm_ms = sum(ms * per for ms, per in expert_gemms.values())
     result = {
         "metric": METRIC,
-        "value": wl.T * args.steps / el,
+        "value": wl.T / (ms_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -307,9 +346,8 @@ def main():
                                   if gemm_ms else None,
                                   "gemm_ms_per_step": gemm_ms}
     warm = step_distribution(layer, dy, args.steps)
-    flushed = step_distribution(layer, dy, args.steps, flush_bytes=1 << 30)
-    result["step_ms"] = {"warm": warm, "flushed": flushed,
-                         "flushed_tokens_per_s": wl.T / (flushed["median"] * 1e-3)}
+    result["step_ms"] = {"flushed": flushed, "warm": warm, "timed_region_s": el,
+                         "warm_tokens_per_s": wl.T / (warm["median"] * 1e-3)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)

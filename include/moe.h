@@ -26,8 +26,14 @@
  *     synchronises with the host and no data-dependent size leaves the GPU.
  *   - "act" below is the plan's activation dtype (f32, f16 or bf16): x, y,
  *     dy, dx, the router weight and the expert weights are stored in it, and
- *     so are the saved intermediates GU and H and the weight gradients.
- *     The expert outputs Y_perm are kept in f32.  Router probabilities and routing weights are always f32.
+ *     so are H and the weight gradients.  A bf16 layer with bf16 experts keeps
+ *     three intermediates in f32: the saved gate/up pre-activations GU, the
+ *     expert outputs Y_perm and (in the workspace) the experts' input-gradient
+ *     rows; rounded to bf16 they alone move y, dx and the router gradient by
+ *     2-3 % of their RMS at 16k tokens x top-8.  f16 and f32 layers keep them
+ *     in act.  With MX-fp8 experts GU is bf16 and Y_perm f32 (the
+ *     routing-weight gradient is taken from Y_perm there).  Router
+ *     probabilities and routing weights are always f32.
  *     Every matrix is row-major with the last index contiguous.
  *   - Arguments are checked on the host before anything is launched; a
  *     negative moe_status is returned and nothing is enqueued.  A HIP launch
@@ -163,14 +169,14 @@ typedef struct {
   const int32_t* offsets;  /* [E+1] from moe_permute */
   const void* w_gate_up;   /* [E, 2I, d] act: rows 0..I-1 gate, I..2I-1 up */
   const void* w_down;      /* [E, d, I] act */
-  void* gu;                /* out [T*k, 2I] act: [G | U] per row, saved for backward */
+  void* gu;                /* out [T*k, 2I]: [G | U] per row, saved for backward; f32 for a
+                              bf16 layer with bf16 experts, bf16 for MX-fp8 experts, else act */
   void* h;                 /* out [T*k, I] act: silu(G) * U */
-  float* y_perm;           /* out [T*k, d] f32: H W_d^T (kept in f32: the router gradient
-                              differences these rows, which magnifies storage rounding) */
+  void* y_perm;            /* out [T*k, d]: H W_d^T; f32 for a bf16 layer or MX-fp8 experts, else act */
   const void* x;           /* [T, d] act (shared experts' input) */
   const void* ws_gate_up;  /* [Ns, 2Is, d] act */
   const void* ws_down;     /* [Ns, d, Is] act */
-  void* gu_shared;         /* out [T, 2 Ns Is] act: expert s in columns [2 s Is, 2 (s+1) Is) as [G_s | U_s] */
+  void* gu_shared;         /* out [T, 2 Ns Is], dtype as gu: expert s in columns [2 s Is, 2 (s+1) Is) as [G_s | U_s] */
   void* h_shared;          /* out [T, Ns Is] act: expert s in columns [s Is, (s+1) Is) */
   void* y_shared;          /* out [T, d] act: sum over shared experts */
   /* Optional, MX-fp8 plans: perm_token [T*k] from moe_permute.  Given it,
@@ -189,9 +195,9 @@ moe_status moe_expert_ffn(moe_plan plan, const moe_ffn_args* args, void* ws, siz
 
 /* y[t] = sum_j topk_w[t, j] * y_perm[inv_perm[t, j]] (+ y_shared[t]), accumulated in
  * f32 in slot order j = 0..k-1, one write per row.
- *   y_perm [T*k, d] f32; inv_perm [T, k] int32; topk_w [T, k] f32;
+ *   y_perm [T*k, d], dtype as in moe_ffn_args; inv_perm [T, k] int32; topk_w [T, k] f32;
  *   y_shared [T, d] act or NULL; y [T, d] act out. */
-moe_status moe_combine(moe_plan plan, const float* y_perm, const int32_t* inv_perm,
+moe_status moe_combine(moe_plan plan, const void* y_perm, const int32_t* inv_perm,
                        const float* topk_w, const void* y_shared, void* y, void* stream);
 
 /* ---- backward ---------------------------------------------------------- */
@@ -207,9 +213,9 @@ typedef struct {
   const int32_t* offsets;   /* [E+1] */
   const int32_t* inv_perm;  /* [T, k] */
   const void* x_perm;       /* [T*k, d] */
-  const void* gu;           /* [T*k, 2I] */
+  const void* gu;           /* [T*k, 2I], dtype as in moe_ffn_args */
   const void* h;            /* [T*k, I] */
-  const float* y_perm;      /* [T*k, d] f32 */
+  const void* y_perm;       /* [T*k, d], dtype as in moe_ffn_args (read for MX-fp8 experts only) */
   const void* w_gate_up;    /* [E, 2I, d] */
   const void* w_down;       /* [E, d, I] */
   const void* ws_gate_up;   /* [Ns, 2Is, d] (n_shared > 0) */
@@ -221,9 +227,11 @@ typedef struct {
    * moe_aux_stats_masked of the same step; NULL real_mask = every token. */
   const int32_t* real_mask;
   const int32_t* real_counts;
-  /* Optional, MX-fp8 plans: perm_token [T*k]; the weight gradient of the
-   * gate/up projection then gathers x's rows by it instead of reading
-   * x_perm (which may then be NULL).  Ignored otherwise. */
+  /* perm_token [T*k] from moe_permute.  Required unless the experts are
+   * MX-fp8: the down projection's input gradient reads dy's rows through
+   * it.  Optional for MX-fp8 plans: given it, the weight gradient of the
+   * gate/up projection gathers x's rows by it instead of reading x_perm
+   * (which may then be NULL). */
   const int32_t* perm_token;
 } moe_saved;
 
@@ -243,8 +251,18 @@ typedef struct {
  * weight.  The counts f_e carry no gradient; P_e = mean_t probs[t, e] does
  * (spark-gpt MoE paragraph).  With renorm the routing-weight gradient goes
  * through the division by the chosen-probability sum; the softmax Jacobian
- * is applied in f32.
- *   dy [T, d] act in. */
+ * is applied in f32.  The routing-weight gradient g[t, j] = <dy_t, Y_perm
+ * row> is formed as <dy_t W_d, H> from the saved G, U (so Y_perm is not
+ * read), except with MX-fp8 experts, whose g is <dy_t, Y_perm row>.
+ * Rounding of the expert weight gradients' operands (bf16 / f32 layers): the
+ * down weight gradient pairs dy's own rows with w H formed in f32 and rounded
+ * once; with fewer than 128 rows per expert on average (bf16), both expert
+ * weight gradients also add the products of the operands' rounding
+ * remainders (one more GEMM pass each), since a gradient element summed over
+ * a handful of rows shows a single bf16 rounding undamped.
+ *   dy [T, d] act in.
+ * Plans with 16-bit or f32 experts need T * d_model * (element bytes) < 2^31
+ * (moe_plan_create returns MOE_ERR_UNSUPPORTED otherwise). */
 moe_status moe_backward(moe_plan plan, const moe_saved* saved, const void* dy,
                         const moe_grads* grads, void* ws, size_t ws_bytes, void* stream);
 
@@ -318,8 +336,17 @@ const char* moe_kernel_names(void);
 
 /* Byte offset and size, inside the workspace, of an intermediate that
  * moe_backward keeps there and leaves in place when it returns (until the
- * next call that uses the workspace), all act dtype, row-major:
- *   "dy_perm"     [T*top_k, d_model]     gradient reaching the expert rows
+ * next call that uses the workspace), row-major, act dtype except dx_perm and
+ * dx_shared, which are f32 in a bf16 layer with bf16 experts:
+ *   "dy_perm"     [T*top_k, d_model]     gradient reaching the expert rows:
+ *                 w dy (f16 layers, MX-fp8 experts) or dy itself (bf16 and
+ *                 f32 layers, whose routing weight sits in "wh")
+ *   "wh"          [T*top_k, d_ff]        bf16 / f32 layers: the routing weight
+ *                 times H = silu(G) U formed from the saved G, U, the down
+ *                 weight gradient's other operand
+ *   "dgu_lo", "wh_lo"  (bf16 plans whose experts see fewer than 128 rows on
+ *                 average) the rounding remainders v - bf16(v) of "dgu" and
+ *                 "wh", in bf16, which the expert weight gradients add
  *   "dgu"         [T*top_k, 2 d_ff]      [dG | dU] of the routed experts
  *   "dx_perm"     [T*top_k, d_model]     input gradient of the expert rows
  *   "dgu_shared"  [T, 2 n_shared d_ff_shared]  [dG_s | dU_s] per shared expert

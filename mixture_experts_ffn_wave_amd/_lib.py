@@ -157,6 +157,13 @@ class Plan:
         self.T, self.d, self.E, self.k, self.I = T, d_model, n_experts, top_k, d_ff
         self.Ns, self.Is = n_shared, (d_ff_shared if n_shared else 0)
         self.renorm, self.has_bias, self.aux_coef = bool(renorm), bool(has_router_bias), aux_coef
+        # storage of the saved [G | U], of Y_perm and of the experts' input
+        # gradient rows (include/moe.h): f32 in a bf16 layer with bf16 experts
+        if self.mx:
+            self.gu_dtype, self.y_perm_dtype, self.dx_rows_dtype = torch.bfloat16, torch.float32, dtype
+        else:
+            wide = torch.float32 if dtype == torch.bfloat16 else dtype
+            self.gu_dtype = self.y_perm_dtype = self.dx_rows_dtype = wide
         h = c_void_p()
         _check("moe_plan_create", lib().moe_plan_create(ctypes.byref(self.cfg), ctypes.byref(h)))
         self._h = h
@@ -231,18 +238,21 @@ def moe_expert_ffn(plan, x_perm, offsets, w_gate_up, w_down, gu, h, y_perm, x=No
                    perm_token=None):
     T, d, E, k, I, dt = plan.T, plan.d, plan.E, plan.k, plan.I, plan.dtype
     A = T * k
-    _need(x_perm, "x_perm", (A, d), dt); _need(offsets, "offsets", (E + 1,), torch.int32)
+    if x_perm is not None or perm_token is None:   # x_perm may be omitted when MX experts gather on load
+        _need(x_perm, "x_perm", (A, d), dt)
+    _need(offsets, "offsets", (E + 1,), torch.int32)
     _need(w_gate_up, "w_gate_up", (E, 2 * I, d), dt); _need(w_down, "w_down", (E, d, I), dt)
-    _need(gu, "gu", (A, 2 * I), dt); _need(h, "h", (A, I), dt); _need(y_perm, "y_perm", (A, d), torch.float32)
+    _need(gu, "gu", (A, 2 * I), plan.gu_dtype); _need(h, "h", (A, I), dt)
+    _need(y_perm, "y_perm", (A, d), plan.y_perm_dtype)
     args = MoeFfnArgs(*[None] * len(_FFN_FIELDS))
     for n, t in [("x_perm", x_perm), ("offsets", offsets), ("w_gate_up", w_gate_up), ("w_down", w_down),
                  ("gu", gu), ("h", h), ("y_perm", y_perm)]:
-        setattr(args, n, t.data_ptr())
+        setattr(args, n, t.data_ptr() if t is not None else None)
     if plan.Ns > 0:
         Ns, Is = plan.Ns, plan.Is
         _need(x, "x", (T, d), dt); _need(ws_gate_up, "ws_gate_up", (Ns, 2 * Is, d), dt)
         _need(ws_down, "ws_down", (Ns, d, Is), dt)
-        _need(gu_shared, "gu_shared", (T, 2 * Ns * Is), dt); _need(h_shared, "h_shared", (T, Ns * Is), dt)
+        _need(gu_shared, "gu_shared", (T, 2 * Ns * Is), plan.gu_dtype); _need(h_shared, "h_shared", (T, Ns * Is), dt)
         _need(y_shared, "y_shared", (T, d), dt)
         for n, t in [("x", x), ("ws_gate_up", ws_gate_up), ("ws_down", ws_down), ("gu_shared", gu_shared),
                      ("h_shared", h_shared), ("y_shared", y_shared)]:
@@ -259,7 +269,7 @@ def moe_expert_ffn(plan, x_perm, offsets, w_gate_up, w_down, gu, h, y_perm, x=No
 
 def moe_combine(plan, y_perm, inv_perm, topk_w, y_shared, y, stream=None):
     T, d, k, dt = plan.T, plan.d, plan.k, plan.dtype
-    _need(y_perm, "y_perm", (T * k, d), torch.float32); _need(inv_perm, "inv_perm", (T, k), torch.int32)
+    _need(y_perm, "y_perm", (T * k, d), plan.y_perm_dtype); _need(inv_perm, "inv_perm", (T, k), torch.int32)
     _need(topk_w, "topk_w", (T, k), torch.float32); _need(y, "y", (T, d), dt)
     if y_shared is not None:
         _need(y_shared, "y_shared", (T, d), dt)

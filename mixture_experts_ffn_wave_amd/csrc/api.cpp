@@ -45,7 +45,14 @@ struct moe_plan_s {
   int sp_wg_down, sp_wg_gu, sp_wg_down_s, sp_wg_gu_s;
   // workspace regions (byte offsets)
   size_t o_block_counts, o_block_base, o_dy_perm, o_g, o_dzhl, o_w2, o_dgu, o_dx_perm, o_dgu_s,
-      o_dxs, o_dxr, o_dwr_part, o_dbias_part, o_aux_part, o_wg_part, ws_total;
+      o_dxs, o_dxr, o_dwr_part, o_dbias_part, o_aux_part, o_wg_part, o_wsorted, o_gpart, o_wh, o_dgu_lo,
+      o_wh_lo, ws_total;
+  // bf16 experts seeing few tokens each: the expert weight gradients add the
+  // products of the rounding remainders of [dG | dU] and of w H (see run_wgrad)
+  bool comp = false;
+  // partial sums of the routing-weight gradient per expert-sorted row (the
+  // down dgrad's waves along its columns), 16-bit and f32 expert plans
+  int gparts = 0;
   bool router_dx_gemm;     // many experts: the router part of dx goes through the matrix cores
   bool router_small;       // few experts: dz, dW_r and dbias partials in one kernel (no dz^T x GEMM)
   int nblk_small;          // its token blocks
@@ -72,6 +79,11 @@ struct moe_plan_s {
     probe_n = 0;
   }
 };
+
+// bf16 and f32 experts: the down dgrad writes w H rows (the routing weight
+// times H in f32, rounded once) for the down weight gradient, and dY_perm
+// holds plain copies of dy's rows; f16 experts keep dY_perm = w dy and read H
+static bool wh_rows(const moe_plan_s* p) { return !p->mx && p->dt != DT_F16; }
 
 namespace {
 
@@ -110,30 +122,38 @@ moe_status check_ws(moe_plan p, void* ws, size_t ws_bytes) {
 }
 
 constexpr int kCUs = 256;
+// mean rows per expert below which a bf16 plan adds the remainder terms to
+// the expert weight gradients (moe_plan_s::comp)
+constexpr int kCompTokens = 128;
 
-// Tile override for tuning and tests: MOE_ROW_TILE = 128, 256 or 128x256,
-// MOE_WGRAD_TILE = 128 or 256, read once per plan; any other value, or a
-// shape the tile does not divide, keeps the default choice.
+// Tile override for tuning and tests: MOE_ROW_TILE = 128, 256, 128x256 or
+// 256pp, MOE_WGRAD_TILE = 128, 256 or 256pp, read once per plan; any other
+// value, or a shape the tile does not divide, keeps the default choice.
 int env_tile(const char* name, bool wide) {
   const char* v = std::getenv(name);
   if (!v) return 0;
   if (wide && std::strcmp(v, "128x256") == 0) return TILE_128x256;
+  if (std::strcmp(v, "256pp") == 0) return TILE_256PP;
   const int t = std::atoi(v);
   return (t == 128 || t == 256) ? t : 0;
 }
 
-// Row GEMMs: 128 x 256 tiles (4 waves, two workgroups per CU) where they
-// divide the shape and the GEMM has at least four rounds of them (2048
-// tiles): they move a quarter less operand data per FLOP than 128 x 128, but
-// a short grid of fewer, longer tiles ends unevenly, so smaller GEMMs keep
-// 128 x 128 (three workgroups per CU).  `tiles256` = the GEMM's 128 x 256
-// tile count (an upper bound for grouped GEMMs).  256 x 256 (8 waves, one
-// workgroup per CU) only on request.
+// Row GEMMs: 256 x 256 ping-pong tiles (8 waves, one workgroup per CU) where
+// they divide the shape and the GEMM has at least kPPTileMin of them (whole
+// rounds over the 256 CUs, so the last round is a small share); otherwise
+// 128 x 256 tiles (4 waves, two workgroups per CU) with at least four rounds
+// of them (2048 tiles): they move a quarter less operand data per FLOP than
+// 128 x 128, but a short grid of fewer, longer tiles ends unevenly, so
+// smaller GEMMs keep 128 x 128 (three workgroups per CU).  `tiles256` = the
+// GEMM's 128 x 256 tile count (an upper bound for grouped GEMMs).  The
+// 8-wave 256 x 256 tile without ping-pong only on request.
 constexpr int64_t kWideTileMin = 2048;
+constexpr int64_t kPPTileMin = 1024;
 int choose_row_tile(int dt, int ncols, int block_align, int64_t tiles256, int override_tile) {
   if (dt == DT_F32) return TILE_128;
   if (ncols % 256 || block_align % 256) return TILE_128;
   if (override_tile) return override_tile;
+  if (tiles256 / 2 >= kPPTileMin) return TILE_256PP;
   return tiles256 >= kWideTileMin ? TILE_128x256 : TILE_128;
 }
 // Weight-gradient GEMMs: 256 x 256 stages twice the FLOP per operand byte of
@@ -150,23 +170,43 @@ int choose_wgrad_tile(int dt, double segs, int M, int N, double ktok, int overri
   return c256 <= c128 ? 256 : 128;
 }
 
-// Split-K factor of a weight-gradient GEMM with W = G (M/tile)(N/tile) output
-// tiles.  Fewer than 384 tiles leave CUs with one workgroup or none, so the
-// token range is split until about 512 workgroups run (at most 4 ways, and
-// every split keeps at least 512 tokens per group); the f32 partials are then
-// summed in order by one extra pass.  MOE_WGRAD_SPLITS (1..8) forces a value.
+// Split-K factor of a weight-gradient GEMM with W = G (M/bt)(N/bt) output
+// tiles (bt = 128 or 256).  The f32 partials of a split are summed in order by
+// one extra pass; every split keeps at least 512 tokens per group.
+//   128 x 128 tiles (several workgroups per CU): fewer than 384 tiles leave
+//   CUs with one workgroup or none, so the token range is split until about
+//   512 workgroups run (at most 4 ways);
+//   256 x 256 tiles (one workgroup per CU): the split s (up to 8) minimises
+//   rounds(W s over the CUs) / s times the time of one unsplit tile, plus the
+//   partials' traffic (s W 256^2 f32 written and read back), the tile time
+//   taken at ~6.5 TFLOP/s per CU and the traffic at ~5 TB/s.
+// MOE_WGRAD_SPLITS (1..8) forces a value.
 int choose_wgrad_splits(int tile, int G, int M, int N, double tokens_per_group) {
   const char* v = std::getenv("MOE_WGRAD_SPLITS");
   if (v) {
     const int s = std::atoi(v);
     if (s >= 1 && s <= 8) return s;
   }
-  const int64_t W = (int64_t)G * (M / tile) * (N / tile);
-  if (W <= 0 || W >= 384) return 1;
-  int s = (int)(512 / W);
-  if (s > 4) s = 4;
-  while (s > 1 && tokens_per_group / s < 512) --s;
-  return s < 1 ? 1 : s;
+  const int bt = tile_rows(tile);
+  const int64_t W = (int64_t)G * (M / bt) * (N / bt);
+  if (W <= 0) return 1;
+  if (bt == 128) {
+    if (W >= 384) return 1;
+    int s = (int)(512 / W);
+    if (s > 4) s = 4;
+    while (s > 1 && tokens_per_group / s < 512) --s;
+    return s < 1 ? 1 : s;
+  }
+  const double tile_s = 2.0 * bt * bt * tokens_per_group / 6.5e12;
+  int best = 1;
+  double best_t = 1e30;
+  for (int s = 1; s <= 8; ++s) {
+    if (s > 1 && tokens_per_group / s < 512) break;
+    const double rounds = (double)((W * s + kCUs - 1) / kCUs);
+    const double t = rounds * tile_s / s + (s > 1 ? 2.0 * s * (double)W * bt * bt * 4 / 5e12 : 0.0);
+    if (t < best_t) { best_t = t; best = s; }
+  }
+  return best;
 }
 
 }  // namespace
@@ -198,12 +238,18 @@ moe_status moe_workspace_region(moe_plan p, const char* name, size_t* offset, si
     o = p->o_dy_perm; b = (size_t)p->A * p->d * es;
   } else if (n == "dgu") {
     o = p->o_dgu; b = (size_t)p->A * 2 * p->I * es;
+  } else if (n == "wh" && wh_rows(p)) {
+    o = p->o_wh; b = (size_t)p->A * p->I * es;
+  } else if (n == "dgu_lo" && p->comp) {
+    o = p->o_dgu_lo; b = (size_t)p->A * 2 * p->I * es;
+  } else if (n == "wh_lo" && p->comp) {
+    o = p->o_wh_lo; b = (size_t)p->A * p->I * es;
   } else if (n == "dx_perm") {
-    o = p->o_dx_perm; b = (size_t)p->A * p->d * es;
+    o = p->o_dx_perm; b = (size_t)p->A * p->d * (f32_intermediates(p->dt, p->mx) ? 4 : es);
   } else if (n == "dgu_shared" && p->Ns > 0) {
     o = p->o_dgu_s; b = (size_t)p->T * 2 * p->Ns * p->Is * es;
   } else if (n == "dx_shared" && p->Ns > 0) {
-    o = p->o_dxs; b = (size_t)p->T * p->d * es;
+    o = p->o_dxs; b = (size_t)p->T * p->d * (f32_intermediates(p->dt, p->mx) ? 4 : es);
   } else if (p->mx && n == "mx_pad") {
     o = p->o_mx_pad; b = (size_t)(p->E + 1) * 4;
   } else if (p->mx && n.rfind("mx_", 0) == 0) {
@@ -264,6 +310,8 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
   if (c.n_shared > 0 && c.d_ff_shared % 128) return MOE_ERR_UNSUPPORTED;
   const int64_t A = c.T * c.top_k;
   if (A >= ((int64_t)1 << 31)) return MOE_ERR_INVALID;
+  // the down dgrad of 16-bit / f32 experts gathers dy's rows with 32-bit byte offsets
+  if (!mx && c.T * c.d_model * (c.act_dtype == MOE_F32 ? 4 : 2) >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
   const int64_t A_ = A;
 
   moe_plan p = new (std::nothrow) moe_plan_s();
@@ -340,13 +388,34 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
   p->o_block_counts = take((size_t)p->nblk_hist * p->E * 4);
   p->o_block_base = take((size_t)p->nblk_hist * p->E * 4);
   p->o_dy_perm = take((size_t)A * p->d * es);
-  p->o_g = take((size_t)A * 4);
+  p->o_g = take(p->mx ? (size_t)A * 4 : 0);
+  if (!p->mx) {
+    // waves along the columns of the down dgrad's tile: BN / WN columns each
+    const int wcols = p->t_down_dgrad == TILE_128x256 ? 128 : 64;   // 128 x 128, 256 x 256, 256 x 256 pp: 64
+    p->gparts = p->I / wcols;
+  }
+  p->o_wsorted = take(p->mx ? 0 : (size_t)A * 4);
+  p->o_gpart = take(p->mx ? 0 : (size_t)A * p->gparts * 4);
   p->o_dzhl = take((size_t)p->T * 2 * p->Ep * es);
   p->o_w2 = take(p->router_dx_gemm ? (size_t)2 * p->Ep * p->d * es : 0);
   p->o_dgu = take((size_t)A * 2 * p->I * es);
-  p->o_dx_perm = take((size_t)A * p->d * es);
+  // w H rows, the down weight gradient's operand (bf16 and f32 experts)
+  p->o_wh = take(wh_rows(p) ? (size_t)A * p->I * es : 0);
+  {
+    // fewer than kCompTokens rows per expert on average (bf16): a weight
+    // gradient element then sums a handful of products, and one bf16
+    // rounding of an operand shows in it undamped
+    p->comp = p->dt == DT_BF16 && !p->mx && A > 0 && A < (int64_t)kCompTokens * p->E;
+    const char* v = std::getenv("MOE_WGRAD_COMP");
+    if (v && p->dt == DT_BF16 && !p->mx) p->comp = std::atoi(v) != 0;
+  }
+  p->o_dgu_lo = take(p->comp ? (size_t)A * 2 * p->I * es : 0);
+  p->o_wh_lo = take(p->comp ? (size_t)A * p->I * es : 0);
+  // input-gradient rows of the experts, f32 in a bf16 layer (f32_intermediates)
+  const size_t xs = f32_intermediates(p->dt, p->mx) ? 4 : es;
+  p->o_dx_perm = take((size_t)A * p->d * xs);
   p->o_dgu_s = take((size_t)p->T * 2 * p->Ns * p->Is * es);
-  p->o_dxs = take(p->Ns > 0 ? (size_t)p->T * p->d * es : 0);
+  p->o_dxs = take(p->Ns > 0 ? (size_t)p->T * p->d * xs : 0);
   p->o_dxr = take(p->router_dx_gemm ? (size_t)p->T * p->d * 4 : 0);
   p->o_dwr_part = take(p->router_small ? (size_t)p->nblk_small * p->E * p->d * 4
                                         : (size_t)p->router_splits * 2 * p->Ep * p->d * 4);
@@ -359,8 +428,9 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
     auto need = [&](int sp, int64_t elems) {
       if (sp > 1 && (size_t)sp * elems * 4 > part) part = (size_t)sp * elems * 4;
     };
-    need(p->sp_wg_down, (int64_t)p->E * p->d * p->I);
-    need(p->sp_wg_gu, (int64_t)p->E * 2 * p->I * p->d);
+    const int cf = p->comp ? 2 : 1;                   // rounded values' and remainders' partials
+    need(cf * p->sp_wg_down, (int64_t)p->E * p->d * p->I);
+    need(cf * p->sp_wg_gu, (int64_t)p->E * 2 * p->I * p->d);
     need(p->sp_wg_down_s, (int64_t)p->d * p->Ns * p->Is);
     need(p->sp_wg_gu_s, (int64_t)2 * p->Ns * p->Is * p->d);
     p->o_wg_part = take(part);
@@ -416,11 +486,38 @@ size_t moe_workspace_bytes(moe_plan plan) { return plan ? plan->ws_total : 0; }
 
 // Weight-gradient GEMM into `out` ([G][group_elems], act dtype), split over
 // tokens `splits` ways through f32 partials when splits > 1.
+// lo_p / lo_q (optional, one of them): the rounding remainders of P or Q in
+// the same layout.  The GEMM then runs twice, on (P, Q) and on (lo_p, Q) or
+// (P, lo_q), into consecutive f32 partial slots, and the reduce adds all
+// slots in order: the weight gradient of operands carrying about twice the
+// dtype's mantissa bits.
 moe_status run_wgrad(moe_plan p, int op, int tile, int splits, WgradArgs a, void* out, int64_t group_elems,
-                     void* ws, const char* name, hipStream_t s, int gdt = -1) {
+                     void* ws, const char* name, hipStream_t s, int gdt = -1, const void* lo_p = nullptr,
+                     const void* lo_q = nullptr) {
   if (gdt < 0) gdt = p->dt;
   a.splits = splits;
   a.c_group_stride = group_elems;
+  if (lo_p || lo_q) {
+    float* part = reinterpret_cast<float*>(wsp(ws, p->o_wg_part));
+    const int64_t slot = (int64_t)a.G * group_elems;
+    a.C = part; a.c_split_stride = slot; a.out_f32 = 1;
+    {
+      Probe pr(p, name, s);
+      MOE_TRY(launch_wgrad(gdt, op, tile, a, s));
+    }
+    WgradArgs b = a;
+    if (lo_p) b.P = lo_p;
+    else b.Q = lo_q;
+    b.C = part + splits * slot;
+    {
+      Probe pr(p, name, s);
+      MOE_TRY(launch_wgrad(gdt, op, tile, b, s));
+    }
+    SplitReduceArgs r{part, slot, 2 * splits, out};
+    Probe pr(p, "wgrad_reduce", s);
+    MOE_TRY(launch_split_reduce(p->dt, r, s));
+    return MOE_OK;
+  }
   if (splits <= 1) {
     a.C = out; a.c_split_stride = 0; a.out_f32 = 0;
     Probe pr(p, name, s);
@@ -571,9 +668,10 @@ moe_status moe_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, size_t ws
     a.P = f->h; a.ldp = I;
     a.Q = f->w_down; a.ldq = I; a.q_group_stride = (int64_t)d * I;
     a.offsets = f->offsets; a.G = p->E; a.M = p->A; a.N = d; a.K = I; a.sub = I;
-    a.C = f->y_perm; a.ldc = d;
+    a.C = f->y_perm; a.ldc = d;                       // Y_perm: f32 in a bf16 layer, else the activation dtype
     Probe pr(p, "gemm_down", s);
-    MOE_TRY(launch_row_gemm(p->dt, OP_DOWN_FWD, EPI_STORE_F32, p->t_down, a, s));
+    MOE_TRY(launch_row_gemm(p->dt, OP_DOWN_FWD, f32_intermediates(p->dt, p->mx) ? EPI_STORE_F32 : EPI_STORE,
+                            p->t_down, a, s));
   }
   if (p->Ns > 0) {
     const int Is = p->Is, NI = p->Ns * p->Is;
@@ -661,13 +759,14 @@ moe_status mx_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, hipStream_
 }
 
 // ---------------------------------------------------------------- combine --
-moe_status moe_combine(moe_plan p, const float* y_perm, const int32_t* inv_perm, const float* topk_w,
+moe_status moe_combine(moe_plan p, const void* y_perm, const int32_t* inv_perm, const float* topk_w,
                        const void* y_shared, void* y, void* stream) {
   if (!p) return MOE_ERR_NULL;
   if (p->T == 0) return MOE_OK;
   if (!y_perm || !inv_perm || !topk_w || !y) return MOE_ERR_NULL;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  CombineArgs a{y_perm, inv_perm, topk_w, y_shared, y, p->T, p->d, p->k};
+  CombineArgs a{y_perm, inv_perm, topk_w, y_shared, y, p->T, p->d, p->k,
+                p->mx || p->dt == DT_F32 || f32_intermediates(p->dt, p->mx)};
   Probe pr(p, "combine", s);
   return hip_status(launch_combine(p->dt, a, s));
 }
@@ -800,6 +899,7 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
   if (p->T > 0) {
     if (!dy || !gr->dx || !sv->x || !sv->w_router || !sv->probs || !sv->topk_idx || !sv->topk_w ||
         !sv->counts || !sv->inv_perm || (!sv->x_perm && !(p->mx && sv->perm_token)) || !sv->gu || !sv->h ||
+        (!p->mx && !sv->perm_token) ||
         !sv->y_perm ||
         !sv->w_gate_up || !sv->w_down)
       return MOE_ERR_NULL;
@@ -825,9 +925,21 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
   float* dwr_part = reinterpret_cast<float*>(wsp(ws, p->o_dwr_part));
   float* dbias_part = reinterpret_cast<float*>(wsp(ws, p->o_dbias_part));
 
+  float* wsorted = reinterpret_cast<float*>(wsp(ws, p->o_wsorted));
+  float* gpart = reinterpret_cast<float*>(wsp(ws, p->o_gpart));
+  void* wh = wsp(ws, p->o_wh);
+  void* dgu_lo = wsp(ws, p->o_dgu_lo);
+  void* wh_lo = wsp(ws, p->o_wh_lo);
   if (p->T > 0) {
     {
-      CombineBwdArgs a{dy, sv->y_perm, sv->inv_perm, sv->topk_w, dy_perm, g, p->T, d, k};
+      // dY_perm = w dy at each assignment's row; MX-fp8 experts also take the
+      // routing-weight gradient g = <dy, Y_perm> here (their Y_perm is the
+      // quantised forward's), the others the per-row weights (the down
+      // dgrad forms g from dy W_d and the saved G, U)
+      CombineBwdArgs a{dy, static_cast<const float*>(sv->y_perm), sv->inv_perm, sv->topk_w, dy_perm,
+                       p->mx ? g : nullptr, p->T, d, k};
+      if (!p->mx) a.wsorted = wsorted;
+      if (wh_rows(p)) a.copy = 1;                    // the routing weight goes on the H side
       if (p->mx) {                                   // MX experts: dY_perm's row-wise codes too
         const MxOp dyq = mxop(ws, p->mx_dyq);
         a.q = dyq.pay;
@@ -841,49 +953,60 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
       Probe pr(p, "combine_bwd", s);
       MOE_TRY(launch_combine_bwd(p->dt, a, s));
     }
+    if (!p->mx) {
+      // dH = w (dy W_d) on dy's rows gathered by perm_token, the SwiGLU
+      // backward, and the partial row sums of (dy W_d) * H for g
+      RowGemmArgs a{};
+      a.P = dy; a.ldp = d; a.gather = sv->perm_token; a.p_rows = p->T;
+      a.Q = sv->w_down; a.ldq = I; a.q_group_stride = (int64_t)d * I;
+      a.offsets = sv->offsets; a.G = E; a.M = p->A; a.N = I; a.K = d; a.sub = I;
+      a.C = dgu; a.ldc = 2 * I; a.aux = sv->gu; a.ldaux = 2 * I;
+      a.wrow = wsorted; a.gpart = gpart; a.gparts = p->gparts;
+      if (wh_rows(p)) { a.C2 = wh; a.ldc2 = I; }      // w H, the down weight gradient's operand
+      if (p->comp) { a.C_lo = dgu_lo; a.C2_lo = wh_lo; }
+      Probe pr(p, "gemm_down_dgrad_swiglu", s);
+      MOE_TRY(launch_row_gemm(p->dt, OP_DOWN_DGRAD, EPI_SWIGLU_BWD, p->t_down_dgrad, a, s));
+    }
+    const float* gp = p->mx ? nullptr : gpart;
     if (p->router_small) {
       RouterBwdSmallArgs a{g, sv->topk_w, sv->topk_idx, sv->probs, sv->counts, sv->x, dzhl, dwr_part, dbias_part,
                            p->T, E, Ep, d, k, p->cfg.renorm, p->cfg.aux_coef, sv->real_mask, sv->real_counts};
+      a.gpart = gp; a.inv = sv->inv_perm; a.gparts = p->gparts;
       Probe pr(p, "router_bwd_small", s);
       MOE_TRY(launch_router_bwd_small(p->dt, a, s));
     } else {
       RouterDzArgs a{g, sv->topk_w, sv->topk_idx, sv->probs, sv->counts, dzhl, dbias_part,
                      p->T, E, Ep, k, p->cfg.renorm, p->cfg.aux_coef, sv->real_mask, sv->real_counts};
+      a.gpart = gp; a.inv = sv->inv_perm; a.gparts = p->gparts;
       Probe pr(p, "router_dz", s);
       MOE_TRY(launch_router_dz(p->dt, a, s));
     }
-    if (!p->mx) {
-      RowGemmArgs a{};
-      a.P = dy_perm; a.ldp = d;
-      a.Q = sv->w_down; a.ldq = I; a.q_group_stride = (int64_t)d * I;
-      a.offsets = sv->offsets; a.G = E; a.M = p->A; a.N = I; a.K = d; a.sub = I;
-      a.C = dgu; a.ldc = 2 * I; a.aux = sv->gu; a.ldaux = 2 * I;
-      Probe pr(p, "gemm_down_dgrad_swiglu", s);
-      MOE_TRY(launch_row_gemm(p->dt, OP_DOWN_DGRAD, EPI_SWIGLU_BWD, p->t_down_dgrad, a, s));
-    }
   }
   if (!p->mx) {
+    // dW_d[e] = sum over the expert's rows of dy[t] (w H)[r]: dy is the
+    // caller's own values, w H is rounded once (f16: (w dy)[r] H[r])
     WgradArgs a{};
-    a.P = dy_perm; a.ldp = d; a.Q = sv->h; a.ldq = I;
+    a.P = dy_perm; a.ldp = d; a.Q = wh_rows(p) ? wh : sv->h; a.ldq = I;
     a.offsets = sv->offsets; a.G = E; a.Mtok = p->A; a.M = d; a.N = I; a.sub = I;
     MOE_TRY_STATUS(run_wgrad(p, WG_DOWN, p->t_wg_down, p->sp_wg_down, a, gr->dw_down, (int64_t)d * I, ws,
-                             "gemm_wgrad_down", s));
+                             "gemm_wgrad_down", s, -1, nullptr, p->comp ? wh_lo : nullptr));
   }
   if (p->T > 0 && !p->mx) {
     RowGemmArgs a{};
     a.P = dgu; a.ldp = 2 * I;
     a.Q = sv->w_gate_up; a.ldq = d; a.q_group_stride = (int64_t)2 * I * d;
     a.offsets = sv->offsets; a.G = E; a.M = p->A; a.N = d; a.K = 2 * I; a.sub = I;
-    a.C = dx_perm; a.ldc = d;
+    a.C = dx_perm; a.ldc = d;                         // f32 rows in a bf16 layer
     Probe pr(p, "gemm_gate_up_dgrad", s);
-    MOE_TRY(launch_row_gemm(p->dt, OP_GU_DGRAD, EPI_STORE, p->t_gu_dgrad, a, s));
+    MOE_TRY(launch_row_gemm(p->dt, OP_GU_DGRAD, f32_intermediates(p->dt, p->mx) ? EPI_STORE_F32 : EPI_STORE,
+                            p->t_gu_dgrad, a, s));
   }
   if (!p->mx) {
     WgradArgs a{};
     a.P = dgu; a.ldp = 2 * I; a.Q = sv->x_perm; a.ldq = d;
     a.offsets = sv->offsets; a.G = E; a.Mtok = p->A; a.M = 2 * I; a.N = d; a.sub = d;
     MOE_TRY_STATUS(run_wgrad(p, WG_GATE_UP, p->t_wg_gu, p->sp_wg_gu, a, gr->dw_gate_up, (int64_t)2 * I * d, ws,
-                             "gemm_wgrad_gate_up", s));
+                             "gemm_wgrad_gate_up", s, -1, p->comp ? dgu_lo : nullptr));
   }
   if (p->Ns > 0 && !p->mx) {
     const int Is = p->Is, NI = p->Ns * p->Is;
@@ -918,9 +1041,10 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
     b.P = dgu_s; b.ldp = 2 * NI;
     b.Q = sv->ws_gate_up; b.ldq = d; b.q_group_stride = 0;
     b.offsets = nullptr; b.G = 1; b.M = p->T; b.N = d; b.K = 2 * NI; b.sub = d;
-    b.C = dxs; b.ldc = d;
+    b.C = dxs; b.ldc = d;                             // f32 rows in a bf16 layer
     Probe pr(p, "gemm_gate_up_dgrad_shared", s);
-    MOE_TRY(launch_row_gemm(p->dt, OP_GU_DGRAD, EPI_STORE, p->t_gu_dgrad_s, b, s));
+    MOE_TRY(launch_row_gemm(p->dt, OP_GU_DGRAD, f32_intermediates(p->dt, p->mx) ? EPI_STORE_F32 : EPI_STORE,
+                            p->t_gu_dgrad_s, b, s));
   }
   if (p->router_dx_gemm && p->T > 0) {
     {
@@ -939,6 +1063,7 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
   if (p->T > 0) {
     UnpermuteArgs a{dx_perm, sv->inv_perm, p->Ns > 0 ? dxs : nullptr, p->router_dx_gemm ? dxr : nullptr,
                     dzhl, sv->w_router, gr->dx, p->T, d, k, E, Ep};
+    a.src_f32 = f32_intermediates(p->dt, p->mx) ? 1 : 0;
     Probe pr(p, "unpermute", s);
     MOE_TRY(launch_unpermute(p->dt, a, s));
   }

@@ -19,10 +19,11 @@ constexpr int NT = 256;
 // slot order.  Slots go in batches of KG whose row loads are all issued
 // before the first is used (a load under a per-slot branch would wait for
 // each row in turn).
-template <typename T, int KG>
+template <typename T, int KG, typename YT>
 __global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a) {
   constexpr int VR = 16 / sizeof(T);   // output elements per 16-byte chunk
-  constexpr int YC = VR / 4;           // 16-byte f32 chunks of y_perm per output chunk
+  constexpr int YC = VR * sizeof(YT) / 16;   // 16-byte chunks of y_perm per output chunk
+  const YT* yperm = static_cast<const YT*>(a.y_perm);
   const int lane = threadIdx.x & 63;
   const int64_t waves = (int64_t)gridDim.x * (NT / 64);
   const int64_t rowbytes = (int64_t)a.d * sizeof(T);
@@ -43,24 +44,28 @@ __global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a) {
 #pragma unroll
       for (int i = 0; i < VR; ++i) acc[i] = 0.0f;
       for (int j0 = 0; j0 < a.k; j0 += KG) {
-        f32x4 v[KG][YC];
+        u32x4 v[KG][YC];
         int r[KG];
 #pragma unroll
         for (int u = 0; u < KG; ++u) {
           r[u] = __shfl(r_l, (j0 + u) & 63, 64);
           const bool use = ok && j0 + u < a.k && r[u] >= 0;
-          const f32x4* src = reinterpret_cast<const f32x4*>(a.y_perm + (int64_t)r[u] * a.d + (int64_t)c * VR);
+          const u32x4* src = reinterpret_cast<const u32x4*>(yperm + (int64_t)r[u] * a.d + (int64_t)c * VR);
 #pragma unroll
-          for (int q = 0; q < YC; ++q) v[u][q] = use ? src[q] : (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+          for (int q = 0; q < YC; ++q) v[u][q] = use ? src[q] : (u32x4){0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int u = 0; u < KG; ++u) {
           const float w = __shfl(w_l, (j0 + u) & 63, 64);
           if (j0 + u < a.k && r[u] >= 0) {                  // wave-uniform
 #pragma unroll
-            for (int q = 0; q < YC; ++q)
+            for (int q = 0; q < YC; ++q) {
+              Chunk<YT> yc;
+              yc.raw = v[u][q];
 #pragma unroll
-              for (int i = 0; i < 4; ++i) acc[4 * q + i] = fmaf(w, v[u][q][i], acc[4 * q + i]);
+              for (int i = 0; i < Chunk<YT>::N; ++i)
+                acc[Chunk<YT>::N * q + i] = fmaf(w, to_f32<YT>(yc.e[i]), acc[Chunk<YT>::N * q + i]);
+            }
           }
         }
       }
@@ -106,7 +111,7 @@ __device__ __forceinline__ void mx_row_codes(u32x4 raw, bool ok, uint8_t* q, uin
   }
 }
 
-template <typename T, int KG, bool MXQ>
+template <typename T, int KG, bool MXQ, bool GD>
 __global__ void __launch_bounds__(NT) combine_bwd_kernel(CombineBwdArgs a) {
   constexpr int VR = 16 / sizeof(T);
   constexpr int YC = VR / 4;
@@ -143,7 +148,7 @@ __global__ void __launch_bounds__(NT) combine_bwd_kernel(CombineBwdArgs a) {
         f32x4 yv[KG][YC];
 #pragma unroll
         for (int u = 0; u < KG; ++u) {
-          const bool use = ok && j0 + u < a.k && r[u] >= 0;
+          const bool use = GD && ok && j0 + u < a.k && r[u] >= 0;
           const f32x4* src = reinterpret_cast<const f32x4*>(a.y_perm + (int64_t)r[u] * a.d + (int64_t)c * VR);
 #pragma unroll
           for (int q = 0; q < YC; ++q) yv[u][q] = use ? src[q] : (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
@@ -157,8 +162,8 @@ __global__ void __launch_bounds__(NT) combine_bwd_kernel(CombineBwdArgs a) {
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const float dd = to_f32<T>(dv.e[4 * q + i]);
-                dot[u] = fmaf(dd, yv[u][q][i], dot[u]);
-                o.e[4 * q + i] = from_f32<T>(w[u] * dd);
+                if constexpr (GD) dot[u] = fmaf(dd, yv[u][q][i], dot[u]);
+                o.e[4 * q + i] = a.copy ? dv.e[4 * q + i] : from_f32<T>(w[u] * dd);
               }
             if (ok) st16(dyp + (int64_t)r[u] * rowbytes + (int64_t)c * 16, o.raw);
             if constexpr (MXQ && sizeof(T) == 2) {
@@ -174,12 +179,27 @@ __global__ void __launch_bounds__(NT) combine_bwd_kernel(CombineBwdArgs a) {
 #pragma unroll
       for (int u = 0; u < KG; ++u) {
         if (j0 + u < a.k) {
-          const float ds = wave_sum(dot[u]);
-          if (lane == 0) a.g[t * a.k + j0 + u] = ds;
+          if constexpr (GD) {
+            const float ds = wave_sum(dot[u]);
+            if (lane == 0) a.g[t * a.k + j0 + u] = ds;
+          } else {
+            if (lane == 0 && r[u] >= 0) a.wsorted[r[u]] = w[u];
+          }
         }
       }
     }
   }
+}
+
+// Routing-weight gradient of assignment (t, j) = flat index tj: g[tj], or
+// the sum of the expert-sorted row's partials in index order.
+__device__ __forceinline__ float slot_g(const float* g, const float* gpart, const int32_t* inv, int gparts,
+                                        int64_t tj) {
+  if (!gpart) return g[tj];
+  const float* p = gpart + (int64_t)inv[tj] * gparts;
+  float s = 0.0f;
+  for (int i = 0; i < gparts; ++i) s += p[i];
+  return s;
 }
 
 // Balancing-term scale aux_coef * E / (T^2 k) (times count_e gives
@@ -227,7 +247,7 @@ __global__ void __launch_bounds__(NT) router_dz_kernel(RouterDzArgs a) {
     int ej = -1;
     if (lane < a.k) {
       ej = a.idx[t * a.k + lane];
-      gj = a.g[t * a.k + lane];
+      gj = slot_g(a.g, a.gpart, a.inv, a.gparts, t * a.k + lane);
       wj = a.wts[t * a.k + lane];
       if ((unsigned)ej >= (unsigned)a.E) ej = -1;
     }
@@ -318,11 +338,11 @@ __global__ void __launch_bounds__(NT) router_bwd_small_kernel(RouterBwdSmallArgs
 #pragma unroll
         for (int e = 0; e < EM; ++e) pj = (e == ej) ? p[e] : pj;
         S += pj;
-        wg = fmaf(a.wts[t * a.k + j], a.g[t * a.k + j], wg);
+        wg = fmaf(a.wts[t * a.k + j], slot_g(a.g, a.gpart, a.inv, a.gparts, t * a.k + j), wg);
       }
       for (int j = 0; j < a.k; ++j) {
         const int ej = a.idx[t * a.k + j];
-        const float gj = a.g[t * a.k + j];
+        const float gj = slot_g(a.g, a.gpart, a.inv, a.gparts, t * a.k + j);
         const float dps = a.renorm ? (gj - wg) / S : gj;
 #pragma unroll
         for (int e = 0; e < EM; ++e) dp[e] += (e == ej) ? dps : 0.0f;
@@ -519,12 +539,15 @@ __global__ void __launch_bounds__(NT) split_reduce_kernel(SplitReduceArgs a) {
 // is at most 64 vectors and k <= 32): token u's slot indices and router
 // gradients sit in lanes 32 u + j, all TW tokens' row gathers issue together
 // and the router weight vectors are loaded once for both.
-template <typename T, int KG, int TW>
+template <typename T, int KG, int TW, typename PT>
 __global__ void __launch_bounds__(NT) unpermute_kernel(UnpermuteArgs a) {
   constexpr int VR = 16 / sizeof(T);
+  constexpr int PC = VR * (int)sizeof(PT) / 16;           // 16-byte pieces of dX_perm per output chunk
+  constexpr int PV = 16 / (int)sizeof(PT);                 // dX_perm values per piece
   const int lane = threadIdx.x & 63;
   const int64_t waves = (int64_t)gridDim.x * (NT / 64);
   const int64_t rowbytes = (int64_t)a.d * sizeof(T);
+  const int64_t prowbytes = (int64_t)a.d * sizeof(PT);    // rows of dX_perm and dx_shared
   const int nch = (int)(rowbytes / 16);
   const char* gp = static_cast<const char*>(a.dx_perm);
   const char* sp = static_cast<const char*>(a.dx_shared);
@@ -557,7 +580,7 @@ __global__ void __launch_bounds__(NT) unpermute_kernel(UnpermuteArgs a) {
         for (int i = 0; i < VR; ++i) acc[u][i] = 0.0f;
       // slots in batches of KG (per token) whose row loads are issued together
       for (int j0 = 0; j0 < a.k; j0 += KG) {
-        Chunk<T> gv[TW][KG];
+        Chunk<PT> gv[TW][KG][PC];
         int r[TW][KG];
 #pragma unroll
         for (int u = 0; u < TW; ++u)
@@ -565,7 +588,10 @@ __global__ void __launch_bounds__(NT) unpermute_kernel(UnpermuteArgs a) {
           for (int q = 0; q < KG; ++q) {
             r[u][q] = __shfl(r_l, (32 * u + j0 + q) & 63, 64);
             const bool use = ok && tv[u] && j0 + q < a.k && r[u][q] >= 0;
-            gv[u][q].raw = use ? ld16(gp + (int64_t)r[u][q] * rowbytes + (int64_t)c * 16) : (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int pc = 0; pc < PC; ++pc)
+              gv[u][q][pc].raw = use ? ld16(gp + (int64_t)r[u][q] * prowbytes + ((int64_t)c * PC + pc) * 16)
+                                     : (u32x4){0u, 0u, 0u, 0u};
           }
 #pragma unroll
         for (int u = 0; u < TW; ++u)
@@ -573,7 +599,7 @@ __global__ void __launch_bounds__(NT) unpermute_kernel(UnpermuteArgs a) {
           for (int q = 0; q < KG; ++q) {
             if (j0 + q < a.k && r[u][q] >= 0) {            // wave-uniform
 #pragma unroll
-              for (int i = 0; i < VR; ++i) acc[u][i] += to_f32<T>(gv[u][q].e[i]);
+              for (int i = 0; i < VR; ++i) acc[u][i] += to_f32<PT>(gv[u][q][i / PV].e[i % PV]);
             }
           }
       }
@@ -581,10 +607,11 @@ __global__ void __launch_bounds__(NT) unpermute_kernel(UnpermuteArgs a) {
 #pragma unroll
       for (int u = 0; u < TW; ++u) {
         if (sp && ok && tv[u]) {
-          Chunk<T> ch;
-          ch.raw = ld16(sp + t[u] * rowbytes + (int64_t)c * 16);
+          Chunk<PT> ch[PC];
 #pragma unroll
-          for (int i = 0; i < VR; ++i) acc[u][i] += to_f32<T>(ch.e[i]);
+          for (int pc = 0; pc < PC; ++pc) ch[pc].raw = ld16(sp + t[u] * prowbytes + ((int64_t)c * PC + pc) * 16);
+#pragma unroll
+          for (int i = 0; i < VR; ++i) acc[u][i] += to_f32<PT>(ch[i / PV].e[i % PV]);
         }
         if (a.dxr && ok && tv[u]) {
           const f32x4* src = reinterpret_cast<const f32x4*>(a.dxr + t[u] * a.d + (int64_t)c * VR);
@@ -842,9 +869,15 @@ hipError_t launch_combine(int dt, const CombineArgs& a, hipStream_t s) {
   int64_t grid = (a.T + 3) / 4;
   if (grid > 8192) grid = 8192;
   switch (dt) {
-    case DT_BF16: MOE_LAUNCH_SLOT_BATCH(combine_kernel, __bf16); break;
-    case DT_F16: MOE_LAUNCH_SLOT_BATCH(combine_kernel, _Float16); break;
-    case DT_F32: MOE_LAUNCH_SLOT_BATCH(combine_kernel, float); break;
+    case DT_BF16:
+      if (a.y_f32) MOE_LAUNCH_SLOT_BATCH(combine_kernel, __bf16, float);
+      else MOE_LAUNCH_SLOT_BATCH(combine_kernel, __bf16, __bf16);
+      break;
+    case DT_F16:
+      if (a.y_f32) MOE_LAUNCH_SLOT_BATCH(combine_kernel, _Float16, float);
+      else MOE_LAUNCH_SLOT_BATCH(combine_kernel, _Float16, _Float16);
+      break;
+    case DT_F32: MOE_LAUNCH_SLOT_BATCH(combine_kernel, float, float); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -857,15 +890,21 @@ hipError_t launch_combine_bwd(int dt, const CombineBwdArgs& a, hipStream_t s) {
   switch (dt) {
     // the MX row-code writes are a separate instantiation, so the plain
     // kernel carries none of their code
+    // g from y_perm (MX-fp8 experts) or the per-row weights (the down dgrad
+    // then forms g); the MX row-code writes are a separate instantiation
     case DT_BF16:
-      if (a.q || a.dq) MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, __bf16, true);
-      else MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, __bf16, false);
+      if (a.q || a.dq) MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, __bf16, true, true);
+      else if (a.g) MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, __bf16, false, true);
+      else MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, __bf16, false, false);
       break;
     case DT_F16:
-      if (a.q || a.dq) MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, _Float16, true);
-      else MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, _Float16, false);
+      if (a.g) MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, _Float16, false, true);
+      else MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, _Float16, false, false);
       break;
-    case DT_F32: MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, float, false); break;
+    case DT_F32:
+      if (a.g) MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, float, false, true);
+      else MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, float, false, false);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -961,9 +1000,12 @@ hipError_t launch_unpermute_tw(int dt, const UnpermuteArgs& a, hipStream_t s) {
   int64_t grid = (a.T + 4 * TW - 1) / (4 * TW);
   if (grid > 8192) grid = 8192;
   switch (dt) {
-    case DT_BF16: MOE_LAUNCH_SLOT_BATCH(unpermute_kernel, __bf16, TW); break;
-    case DT_F16: MOE_LAUNCH_SLOT_BATCH(unpermute_kernel, _Float16, TW); break;
-    case DT_F32: MOE_LAUNCH_SLOT_BATCH(unpermute_kernel, float, TW); break;
+    case DT_BF16:
+      if (a.src_f32) MOE_LAUNCH_SLOT_BATCH(unpermute_kernel, __bf16, TW, float);
+      else MOE_LAUNCH_SLOT_BATCH(unpermute_kernel, __bf16, TW, __bf16);
+      break;
+    case DT_F16: MOE_LAUNCH_SLOT_BATCH(unpermute_kernel, _Float16, TW, _Float16); break;
+    case DT_F32: MOE_LAUNCH_SLOT_BATCH(unpermute_kernel, float, TW, float); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -345,6 +345,57 @@ __device__ __forceinline__ void mfma_chunk(f32x16 (&acc)[NS][MS], const char* lq
   }
 }
 
+// Fragments of one ring chunk, every k step, into registers (the ping-pong
+// loop reads them in one phase and multiplies them in the next): weight-side
+// rows qrow[ns] (in perm_row order), token-side rows prow[ms].
+template <typename PO, typename QO, int NS, int MS, int KSTEPS>
+__device__ __forceinline__ void read_chunk_frags(u32x4 (&fa)[KSTEPS][NS], u32x4 (&fb)[KSTEPS][MS], const char* lq,
+                                                 const char* lp, const int (&qrow)[NS], const int (&prow)[MS],
+                                                 int lane) {
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+      if constexpr (PO::kRawLds) {
+        uint32_t ad[2];
+        u32x2 raw[2];
+        PO::template frag_addr<false>(ad, lp, prow[ms], ks, lane);
+        tr_read(raw, ad);
+        fb[ks][ms] = (u32x4){raw[0][0], raw[0][1], raw[1][0], raw[1][1]};
+      } else {
+        u32x4 f[1];
+        PO::template frag<false>(f, lp, prow[ms], ks, lane);
+        fb[ks][ms] = f[0];
+      }
+    }
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) {
+      if constexpr (QO::kRawLds) {
+        uint32_t ad[2];
+        u32x2 raw[2];
+        QO::template frag_addr<true>(ad, lq, qrow[ns], ks, lane);
+        tr_read(raw, ad);
+        fa[ks][ns] = (u32x4){raw[0][0], raw[0][1], raw[1][0], raw[1][1]};
+      } else {
+        u32x4 f[1];
+        QO::template frag<true>(f, lq, qrow[ns], ks, lane);
+        fa[ks][ns] = f[0];
+      }
+    }
+  }
+}
+
+template <typename T, int NS, int MS, int KSTEPS>
+__device__ __forceinline__ void mfma_chunk_frags(f32x16 (&acc)[NS][MS], const u32x4 (&fa)[KSTEPS][NS],
+                                                 const u32x4 (&fb)[KSTEPS][MS]) {
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) Mma32<T>::run(acc[ns][ms], &fa[ks][ns], &fb[ks][ms]);
+}
+
 // ---- MX-fp8 (e4m3 payload, one power-of-two scale per 32 values of k) ----
 // v_mfma_scale_f32_32x32x64_f8f6f4 over a 64-k step (two scale blocks): lane
 // l supplies operand row l % 32, with payload bytes 0-15 from k 16 h .. +15 of
@@ -454,7 +505,15 @@ __device__ __forceinline__ void dma16(rsrc_t rs, char* lds_lane0, uint32_t voff)
 //   256 x 256: 8 waves (2 along rows x 4 along columns, 128 x 64 per wave), a
 //              2-stage ring of 128-byte k chunks (each row's chunk is one full
 //              cache line), 128 KB of LDS: one workgroup per CU.
-template <int BM, int BN, bool WGRAD> struct TileCfg;
+//   256 x 256 ping-pong (PP): 8 waves, waves w and w + 4 on one SIMD, a
+//              4-stage ring of 64-byte k chunks (128 KB, one workgroup per
+//              CU); group w / 4 computes rows 128 (w / 4) .. (128 x 64 per
+//              wave).  Each phase one group multiplies a chunk from fragments
+//              already in its registers while the other reads the next
+//              chunk's fragments and issues its half of the global loads;
+//              a barrier ends every phase, so one wave per SIMD issues
+//              MFMAs back to back while its partner waits on memory.
+template <int BM, int BN, bool WGRAD, bool PP = false> struct TileCfg;
 // WAVES_PER_EU: register budget of the row kernels (3 waves per SIMD for the
 // 3-workgroup 128 x 128 tiles: the compiler then keeps the accumulators in
 // VGPRs and stays within 168 registers).
@@ -466,6 +525,9 @@ template <> struct TileCfg<128, 256, false> {
 };
 template <bool WGRAD> struct TileCfg<256, 256, WGRAD> {
   static constexpr int WM = 2, WN = 4, DKB = 128, NSTG = 2, THREADS = 512, WAVES_PER_EU = 2;
+};
+template <bool WGRAD> struct TileCfg<256, 256, WGRAD, true> {
+  static constexpr int WM = 2, WN = 4, DKB = 64, NSTG = 4, THREADS = 512, WAVES_PER_EU = 2;
 };
 
 // vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding)
@@ -563,10 +625,16 @@ __device__ __forceinline__ void ring_barrier_last() {
 // MX: operands are MX-fp8 payload bytes (T = uint8_t) with scale bytes in
 // a.Ps / a.Qs, both operands K-contiguous rows (transposes are done by the
 // quantiser), outputs bf16.
-template <typename T, int BM, int BN, int OP, int EPI, int WM, int WN, bool MX = false>
+// LO (SwiGLU backward, 16-bit): also write the rounding remainders of
+// [dG | dU] and of the w H rows to a.C_lo / a.C2_lo.
+template <typename T, int BM, int BN, int OP, int EPI, int WM, int WN, bool MX = false, bool PP = false,
+          bool LO = false>
 __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) {
   constexpr int ES = sizeof(T);
   using TO = std::conditional_t<MX, __bf16, T>;               // output / saved-activation type
+  // saved [G | U]: f32 for a bf16 layer (kernels.h, gu_dtype), else TO
+  constexpr bool GUF32 = !MX && std::is_same_v<T, __bf16>;
+  using TG = std::conditional_t<GUF32, float, TO>;
   constexpr int NW = WM * WN;                                  // waves: WM along rows, WN along columns
   static_assert(ES == 2 || NW == 4, "the register-staged path runs 4 waves");
   static_assert(!MX || (ES == 1 && BM == 128 && BN == 128 && NW == 4), "MX tiles are 128 x 128, 4 waves");
@@ -580,8 +648,9 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
   constexpr int MS = WTM / 32, NS = WTN / 32;
   constexpr int STAGE = PO::BYTES + QO::BYTES;
 
-  constexpr int DKB = MX ? MX_DKB : TileCfg<BM, BN, false>::DKB;
-  constexpr int NSTG = MX ? 2 : TileCfg<BM, BN, false>::NSTG;
+  static_assert(!PP || (ES == 2 && BM == 256 && BN == 256 && WM == 2 && WN == 4), "ping-pong tile");
+  constexpr int DKB = MX ? MX_DKB : TileCfg<BM, BN, false, PP>::DKB;
+  constexpr int NSTG = MX ? 2 : TileCfg<BM, BN, false, PP>::NSTG;
   constexpr int SC_OFF = NSTG * (BM + BN) * DKB;                // MX scale tiles follow the payload ring
   constexpr int SCAN_OFF = MX ? SC_OFF + NSTG * (BM + BN) * 4 : ((ES == 2) ? NSTG * (BM + BN) * DKB : 2 * STAGE);
   int* s_scan = reinterpret_cast<int*>(smem + SCAN_OFF);      // [NW] wave sums, [NW..NW+1] located tile
@@ -624,7 +693,8 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
 
   const char* Pb = static_cast<const char*>(a.P);
   const char* Qb = static_cast<const char*>(a.Q) + (int64_t)g * a.q_group_stride * ES;
-  const int wm = wave % WM, wn = wave / WM;
+  // ping-pong: group wave / 4 owns a row half, its four waves (one per SIMD) the column quarters
+  const int wm = PP ? wave / WN : wave % WM, wn = PP ? wave % WN : wave / WM;
   int qrow[NS], prow[MS];
 #pragma unroll
   for (int ns = 0; ns < NS; ++ns) {
@@ -654,8 +724,13 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
   // c ^ (r & 7) (conflict-free both for the MFMA-layout accesses, 8 rows per
   // chunk index, and for the row-wise ones).
   constexpr int SR = 32 * WM;
-  constexpr int NARR = EPI == EPI_SWIGLU_FWD ? 3 : (EPI == EPI_SWIGLU_BWD ? 2 : 1);
   constexpr int RB = EPI == EPI_STORE_F32 ? BN * 4 : (EPI == EPI_SWIGLU_FWD ? BN : BN * 2);
+  // SwiGLU backward: the w H rows (C2) go through a third staged array where
+  // it fits in the ring's LDS, else straight from registers
+  // (bf16 and f32 layers; an f16 layer's down weight gradient reads w dy and H)
+  constexpr bool WH = EPI == EPI_SWIGLU_BWD && !MX && !std::is_same_v<T, _Float16>;
+  constexpr bool WH_STAGED = WH && 3 * 32 * WM * RB <= NSTG * (BM + BN) * DKB;
+  constexpr int NARR = (EPI == EPI_SWIGLU_FWD || WH_STAGED) ? 3 : (EPI == EPI_SWIGLU_BWD ? 2 : 1);
   constexpr int CPR = RB / 16;                              // chunks per staged row
   constexpr int SITER = SR * CPR / (64 * NW);               // row-wise chunks per thread per array
   static_assert(!PERM || (CPR >= 8 && SITER >= 1 && SITER * 64 * NW == SR * CPR), "staging geometry");
@@ -684,7 +759,7 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
   // their latency hides behind MFMAs (128 x 128 tiles: 32 more VGPRs there,
   // still three workgroups per CU); each later pass's rows are loaded while
   // the previous pass computes.
-  constexpr bool GU_PRE = PERM && EPI == EPI_SWIGLU_BWD && BM == 128 && BN == 128;
+  constexpr bool GU_PRE = PERM && !GUF32 && EPI == EPI_SWIGLU_BWD && BM == 128 && BN == 128;
   u32x4 gun[2][PERM ? SITER : 1];                           // (unused unless GU_PRE)
   // The last two chunks of a ring main loop, with the first pass's G/U loads
   // issued after every chunk's loads (so a vmcnt of 2 SITER before the last
@@ -780,19 +855,151 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
       compute(kc);
     }
     if constexpr (GU_PRE) gu_prefetch_tail(nkd, ring_barrier<LPC, NSTG>, issue_ahead, compute);
+  } else if constexpr (ES == 2 && PP) {
+    // ---------------- ping-pong main loop (16-bit, 256 x 256, 8 waves)
+    // Group 0 (waves 0-3) streams the token-side tile, group 1 (waves 4-7) the
+    // weight-side tile, each half of a chunk issued by four waves.  Every wave
+    // runs the same straight line per chunk c: a memory phase (read chunk c's
+    // fragments into registers, issue its half of chunk c + NSTG - 1 into the
+    // slot of chunk c - 1, wait for its own loads of chunk c + 1) and a
+    // compute phase (the chunk's MFMAs from registers), a barrier after each.
+    // Group 1 starts one barrier late and group 0 ends with one more, so the
+    // two groups are a phase apart: while one wave of a SIMD issues MFMAs, its
+    // partner waits on memory.  (s_barrier pairs the k-th arrival of every
+    // wave, wherever in the program it is.)  Chunk c is read by group 0 in the
+    // phase after barrier 2c + 1 and by group 1 after barrier 2c + 2; each
+    // wave's memory phase for chunk c - 1 ends before barrier 2c + 1 with its
+    // own loads of chunk c landed, so that barrier makes chunk c readable, and
+    // the slot of chunk c - 1 is rewritten only after both groups' reads of
+    // it have returned (lgkmcnt(0) before their barriers).
+    constexpr int NWL = 4;                           // waves loading each half
+    using PD = DmaRows<BM, NWL, DKB>;
+    using QD = std::conditional_t<QT, DmaKmajor<BN, NWL, DKB>, DmaRows<BN, NWL, DKB>>;
+    static_assert(PD::NI == QD::NI, "both halves issue the same number of loads per wave");
+    constexpr int DSTAGE = PD::BYTES + QD::BYTES;
+    constexpr int DBKE = DKB / ES;                    // k elements per chunk
+    constexpr int KSTEPS = DKB / 32;
+    constexpr int LPH = PD::NI;                       // loads per wave per chunk half
+    const int grp = wave >> 2, wq = wave & 3;
+    const bool gat = a.gather != nullptr;
+    const rsrc_t prs = gat ? make_rsrc(Pb, (uint32_t)(a.p_rows * a.ldp * ES))
+                           : make_rsrc(Pb + row0 * a.ldp * ES, (uint32_t)(rows * a.ldp * ES));
+    uint32_t off[LPH];
+    const char* qbase = Qb;
+    int64_t qldk = 0;
+    if (grp == 0) {
+#pragma unroll
+      for (int s2 = 0; s2 < LPH; ++s2) {
+        const int r = PD::row_of(wq, s2, lane);
+        const int64_t src = gat ? (r < rows ? (int64_t)a.gather[row0 + r] : a.p_rows) : (int64_t)r;
+        off[s2] = (uint32_t)(src * a.ldp * ES + PD::gchunk(r, lane) * 16);
+      }
+    } else {
+      if constexpr (!QT) {
+#pragma unroll
+        for (int s2 = 0; s2 < LPH; ++s2) {
+          const int q = QD::row_of(wq, s2, lane);
+          int64_t roff;
+          if constexpr (OP == OP_GU_FWD) {
+            const int blk = n0 / a.sub, r0 = n0 - blk * a.sub;
+            const int wrow = blk * 2 * a.sub + (q < BN / 2 ? r0 + q : a.sub + r0 + (q - BN / 2));
+            roff = (int64_t)wrow * a.ldq;
+          } else {
+            roff = (int64_t)(n0 + q) * a.sub;         // OP_DOWN_FWD, block part added per chunk
+          }
+          off[s2] = (uint32_t)(roff * ES + QD::gchunk(q, lane) * 16);
+        }
+      } else {
+        if constexpr (OP == OP_DOWN_DGRAD) {
+          const int blk = n0 / a.sub, c0 = n0 - blk * a.sub;
+          qbase = Qb + ((int64_t)blk * a.K * a.sub + c0) * ES;
+          qldk = (int64_t)a.sub * ES;
+        } else {
+          qbase = Qb + (int64_t)n0 * ES;
+          qldk = a.ldq * ES;
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < LPH; ++s2) {
+          const int k = QD::k_of(wq, s2, lane);
+          off[s2] = (uint32_t)(k * qldk + QD::gchunk(k, lane) * 16);
+        }
+      }
+    }
+    // this wave's half of chunk c (group 0: token rows, group 1: weight rows)
+    auto issue_half = [&](int c) {
+      char* stage = smem + (c % NSTG) * DSTAGE;
+      const int kc = c * DBKE;
+      if (grp == 0) {
+#pragma unroll
+        for (int s2 = 0; s2 < LPH; ++s2) dma16(prs, stage + PD::lds_off(wq, s2), off[s2] + (uint32_t)(kc * ES));
+      } else if constexpr (!QT) {
+        int64_t koff = (int64_t)kc * ES;
+        if constexpr (OP == OP_DOWN_FWD) {
+          const int blk = kc / a.sub, kk = kc - blk * a.sub;
+          koff = ((int64_t)blk * a.N * a.sub + kk) * ES;
+        }
+        const rsrc_t qrs = make_rsrc(qbase + koff, 0x7fffffffu);
+#pragma unroll
+        for (int s2 = 0; s2 < LPH; ++s2) dma16(qrs, stage + PD::BYTES + QD::lds_off(wq, s2), off[s2]);
+      } else {
+        const rsrc_t qrs = make_rsrc(qbase + (int64_t)kc * qldk, (uint32_t)(QD::KROWS * qldk));
+#pragma unroll
+        for (int s2 = 0; s2 < LPH; ++s2) dma16(qrs, stage + PD::BYTES + QD::lds_off(wq, s2), off[s2]);
+      }
+    };
+    // wait until this wave's loads of chunk c have landed (later chunks of its half may be in flight)
+    auto wait_chunk = [&](int c, int nkd) {
+      const int later = (nkd - 1 - c) < NSTG - 2 ? (nkd - 1 - c) : NSTG - 2;
+      asm volatile("" ::: "memory");
+      if (later >= 2) wait_vmcnt<2 * LPH>();
+      else if (later == 1) wait_vmcnt<LPH>();
+      else wait_vmcnt<0>();
+    };
+    auto phase_barrier = [&]() {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    static_assert(NSTG - 2 <= 2, "wait_chunk covers at most two later chunks");
+    const int nkd = a.K / DBKE;
+#pragma unroll
+    for (int c = 0; c < NSTG - 1; ++c)
+      if (c < nkd) issue_half(c);
+    if (nkd > 0) wait_chunk(0, nkd);
+    phase_barrier();
+    if (grp == 1) phase_barrier();                  // one phase behind group 0
+    u32x4 fa[KSTEPS][NS], fb[KSTEPS][MS];
+    for (int c = 0; c < nkd; ++c) {
+      const char* buf = smem + (c % NSTG) * DSTAGE;
+      read_chunk_frags<PD, QD, NS, MS, KSTEPS>(fa, fb, buf + PD::BYTES, buf, qrow, prow, lane);
+      if (c + NSTG - 1 < nkd) issue_half(c + NSTG - 1);
+      __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0): fragments in registers, slot read
+      if (c + 1 < nkd) wait_chunk(c + 1, nkd);
+      phase_barrier();
+      __builtin_amdgcn_s_setprio(1);
+      mfma_chunk_frags<T, NS, MS, KSTEPS>(acc, fa, fb);
+      __builtin_amdgcn_s_setprio(0);
+      phase_barrier();
+    }
+    if (grp == 0) phase_barrier();                  // as many barriers as group 1
   } else if constexpr (ES == 2) {
     // ---------------- direct-to-LDS main loop (16-bit types)
     using PD = DmaRows<BM, NW, DKB>;
     using QD = std::conditional_t<QT, DmaKmajor<BN, NW, DKB>, DmaRows<BN, NW, DKB>>;
     constexpr int DSTAGE = PD::BYTES + QD::BYTES;
     constexpr int DBKE = DKB / ES;                    // k elements per chunk
-    // token rows of this tile: rows >= `rows` fall outside the descriptor and read as zero
-    const rsrc_t prs = make_rsrc(Pb + row0 * a.ldp * ES, (uint32_t)(rows * a.ldp * ES));
+    // token rows of this tile: rows >= `rows` fall outside the descriptor and
+    // read as zero; gathered rows (a.gather) are addressed in all of P, rows
+    // past the tile pointing one row past its end
+    const bool gat = a.gather != nullptr;
+    const rsrc_t prs = gat ? make_rsrc(Pb, (uint32_t)(a.p_rows * a.ldp * ES))
+                           : make_rsrc(Pb + row0 * a.ldp * ES, (uint32_t)(rows * a.ldp * ES));
     uint32_t poff[PD::NI];
 #pragma unroll
     for (int s2 = 0; s2 < PD::NI; ++s2) {
       const int r = PD::row_of(wave, s2, lane);
-      poff[s2] = (uint32_t)(r * a.ldp * ES + PD::gchunk(r, lane) * 16);
+      const int64_t src = gat ? (r < rows ? (int64_t)a.gather[row0 + r] : a.p_rows) : (int64_t)r;
+      poff[s2] = (uint32_t)(src * a.ldp * ES + PD::gchunk(r, lane) * 16);
     }
     uint32_t qoff[QD::NI];
     const char* qbase;
@@ -871,7 +1078,8 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
 #pragma unroll
   for (int s = 0; s < PO::NREG; ++s) {
     const int rr = PO::nrow(tid, s);
-    prowp[s] = rr < rows ? Pb + (row0 + rr) * a.ldp * ES : nullptr;
+    const int64_t src = rr < rows ? (a.gather ? (int64_t)a.gather[row0 + rr] : row0 + rr) : 0;
+    prowp[s] = rr < rows ? Pb + src * a.ldp * ES : nullptr;
   }
   const char* qrowp[QO::NREG];
   const char* qkbase = nullptr;
@@ -953,7 +1161,16 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) {
       lds_barrier();                                          // ring / previous pass no longer read
+      // this lane's tile row in the pass (MFMA layout) and, for the SwiGLU
+      // backward of routed experts, its routing weight and g partial
+      const int tr_l = prow[ms] + (lane & 31);
+      float wrow_l = 1.0f;
+      // partial sums of (P Q) * H per column subtile and run, added in order after the loop
+      float gpiece[EPI == EPI_SWIGLU_BWD ? NS : 1][EPI == EPI_SWIGLU_BWD ? NRUN : 1];
       if constexpr (EPI == EPI_SWIGLU_BWD) {
+        if (a.wrow && tr_l < rows) wrow_l = a.wrow[row0 + tr_l];
+      }
+      if constexpr (EPI == EPI_SWIGLU_BWD && !GUF32) {
         if constexpr (GU_PRE) {
 #pragma unroll
           for (int i = 0; i < SITER; ++i) {
@@ -974,11 +1191,38 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
         }
         lds_barrier();
       }
+      // f32 G, U of the SwiGLU backward: this lane's row pieces of column
+      // subtile ns, loaded one subtile ahead of the one being computed
+      constexpr bool GU_DIRECT = GUF32 && EPI == EPI_SWIGLU_BWD;
+      float gub[2][GU_DIRECT ? NRUN : 1][2][RUN];
+      auto load_gu_f32 = [&](float (&dst)[GU_DIRECT ? NRUN : 1][2][RUN], int ns) {
+        if constexpr (GU_DIRECT) {
+#pragma unroll
+          for (int t = 0; t < NRUN; ++t) {
+            const int c = (qrow[ns] + RSTEP * t + RUN * h) / 8;
+            const float* gp = static_cast<const float*>(a.aux) + (row0 + (tr_l < rows ? tr_l : 0)) * a.ldaux +
+                              gcol0 + c * 8;
+            load4<float>(gp, dst[t][0]);
+            load4<float>(gp + 4, dst[t][0] + 4);
+            load4<float>(gp + a.sub, dst[t][1]);
+            load4<float>(gp + a.sub + 4, dst[t][1] + 4);
+          }
+        }
+      };
+      if constexpr (GU_DIRECT) load_gu_f32(gub[0], 0);
       // accumulators -> staging (MFMA layout: 8 consecutive columns per run)
 #pragma unroll
       for (int ns = 0; ns < NS; ++ns) {
         if constexpr (EPI == EPI_SWIGLU_FWD) {
           if (ns >= NS / 2) continue;
+        }
+        if constexpr (EPI == EPI_SWIGLU_BWD) {
+          // one column subtile at a time: its G/U reads (LDS or, f32, global
+          // one subtile ahead) are not hoisted above the previous subtile
+          asm volatile("" ::: "memory");
+          if constexpr (GU_DIRECT) {
+            if (ns + 1 < NS) load_gu_f32(gub[(ns + 1) & 1], ns + 1);
+          }
         }
 #pragma unroll
         for (int t = 0; t < NRUN; ++t) {
@@ -1001,24 +1245,95 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
               uv[i] = acc[ns + NS / 2][ms][RUN * t + i];
               hv[i] = silu_f(v[i]) * uv[i];
             }
-            store8<TO>(reinterpret_cast<TO*>(sp(0, sr_l, c)), v);
-            store8<TO>(reinterpret_cast<TO*>(sp(1, sr_l, c)), uv);
+            if constexpr (GUF32) {
+              // G and U in f32 straight from the accumulators (lanes l and
+              // l + 32 write the two halves of a 64-byte row piece)
+              if (tr_l < rows) {
+                float* gp = reinterpret_cast<float*>(a.C) + (row0 + tr_l) * a.ldc + gcol0 + c * 8;
+                store4<float>(gp, v[0], v[1], v[2], v[3]);
+                store4<float>(gp + 4, v[4], v[5], v[6], v[7]);
+                store4<float>(gp + a.sub, uv[0], uv[1], uv[2], uv[3]);
+                store4<float>(gp + a.sub + 4, uv[4], uv[5], uv[6], uv[7]);
+              }
+            } else {
+              store8<TO>(reinterpret_cast<TO*>(sp(0, sr_l, c)), v);
+              store8<TO>(reinterpret_cast<TO*>(sp(1, sr_l, c)), uv);
+            }
             store8<TO>(reinterpret_cast<TO*>(sp(2, sr_l, c)), hv);
           } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-            // v = dH; G, U staged at the same positions, overwritten by dG, dU
+            // v = (P Q) row piece, dH = wrow * v; G, U staged at the same
+            // positions (f32 G, U: loaded here), overwritten by dG, dU
             const int c = (qrow[ns] + RSTEP * t + RUN * h) / 8;
-            float G[RUN], U[RUN], dG[RUN], dU[RUN];
-            unpack8<TO>(ld16(sp(0, sr_l, c)), G);
-            unpack8<TO>(ld16(sp(1, sr_l, c)), U);
+            float G[RUN], U[RUN];
+            if constexpr (GUF32) {
+#pragma unroll
+              for (int i = 0; i < RUN; ++i) {
+                G[i] = gub[ns & 1][t][0][i];
+                U[i] = gub[ns & 1][t][1][i];
+              }
+            } else {
+              unpack8<TO>(ld16(sp(0, sr_l, c)), G);
+              unpack8<TO>(ld16(sp(1, sr_l, c)), U);
+            }
+            // dG, dU with the routing weight applied last (it does not
+            // depend on G, U: applied first, the products would be formed
+            // early and held); then w H, formed after dG, dU are stored
+            float gl = 0.0f, dG[RUN], dU[RUN];
 #pragma unroll
             for (int i = 0; i < RUN; ++i) {
               const float sg = sigmoid_f(G[i]);
-              dG[i] = v[i] * U[i] * sg * (1.0f + G[i] * (1.0f - sg));
-              dU[i] = v[i] * G[i] * sg;
+              const float dU0 = v[i] * G[i] * sg;
+              const float dG0 = v[i] * U[i] * sg * (1.0f + G[i] * (1.0f - sg));
+              gl = fmaf(dU0, U[i], gl);
+              dG[i] = wrow_l * dG0;
+              dU[i] = wrow_l * dU0;
             }
+            gpiece[ns][t] = gl;
             store8<TO>(reinterpret_cast<TO*>(sp(0, sr_l, c)), dG);
             store8<TO>(reinterpret_cast<TO*>(sp(1, sr_l, c)), dU);
+            if constexpr (LO) {
+              // rounding remainders of dG, dU, straight from registers
+              if (tr_l < rows) {
+                TO* dst = static_cast<TO*>(a.C_lo) + (row0 + tr_l) * a.ldc + gcol0 + c * 8;
+#pragma unroll
+                for (int i = 0; i < RUN; ++i) {
+                  dG[i] -= to_f32<TO>(from_f32<TO>(dG[i]));
+                  dU[i] -= to_f32<TO>(from_f32<TO>(dU[i]));
+                }
+                store8<TO>(dst, dG);
+                store8<TO>(dst + a.sub, dU);
+              }
+            }
+            if constexpr (WH) {
+              if (a.C2) {
+                asm volatile("" ::: "memory");
+                float wh[RUN];
+#pragma unroll
+                for (int i = 0; i < RUN; ++i) wh[i] = wrow_l * (silu_f(G[i]) * U[i]);
+                if constexpr (WH_STAGED) store8<TO>(reinterpret_cast<TO*>(sp(2, sr_l, c)), wh);
+                else if (tr_l < rows) store8<TO>(static_cast<TO*>(a.C2) + (row0 + tr_l) * a.ldc2 + n0 + c * 8, wh);
+                if constexpr (LO) {
+                  if (tr_l < rows) {
+#pragma unroll
+                    for (int i = 0; i < RUN; ++i) wh[i] -= to_f32<TO>(from_f32<TO>(wh[i]));
+                    store8<TO>(static_cast<TO*>(a.C2_lo) + (row0 + tr_l) * a.ldc2 + n0 + c * 8, wh);
+                  }
+                }
+              }
+            }
           }
+        }
+      }
+      if constexpr (EPI == EPI_SWIGLU_BWD) {
+        if (a.gpart) {
+          float gacc = 0.0f;
+#pragma unroll
+          for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+            for (int t = 0; t < NRUN; ++t) gacc += gpiece[ns][t];
+          // lanes l and l + 32 hold the two column halves of row l % 32
+          const float gs = gacc + __shfl_xor(gacc, 32, 64);
+          if (h == 0 && tr_l < rows) a.gpart[(row0 + tr_l) * a.gparts + (n0 / BN) * WN + wn] = gs;
         }
       }
       lds_barrier();
@@ -1034,9 +1349,11 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
         } else if constexpr (EPI == EPI_STORE_F32) {
           st16(static_cast<float*>(a.C) + row * a.ldc + n0 + c * 4, ld16(sp(0, sr, c)));
         } else if constexpr (EPI == EPI_SWIGLU_FWD) {
-          TO* gu = static_cast<TO*>(a.C) + row * a.ldc + gcol0 + c * 8;
-          st16(gu, ld16(sp(0, sr, c)));
-          st16(gu + a.sub, ld16(sp(1, sr, c)));
+          if constexpr (!GUF32) {
+            TO* gu = static_cast<TO*>(a.C) + row * a.ldc + gcol0 + c * 8;
+            st16(gu, ld16(sp(0, sr, c)));
+            st16(gu + a.sub, ld16(sp(1, sr, c)));
+          }
           const u32x4 hraw = ld16(sp(2, sr, c));
           st16(static_cast<TO*>(a.C2) + row * a.ldc2 + n0 + c * 8, hraw);
           if constexpr (MX) {
@@ -1063,6 +1380,9 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
           const u32x4 dgraw = ld16(sp(0, sr, c)), duraw = ld16(sp(1, sr, c));
           st16(dgu, dgraw);
           st16(dgu + a.sub, duraw);
+          if constexpr (WH_STAGED) {
+            if (a.C2) st16(static_cast<TO*>(a.C2) + row * a.ldc2 + n0 + c * 8, ld16(sp(2, sr, c)));
+          }
           if constexpr (MX) {
             // [dG | dU] row-wise in MX-fp8 for the gate/up dgrad: four
             // consecutive lanes hold a 32-column block of each half
@@ -1093,8 +1413,50 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
 #pragma unroll
   for (int ms = 0; ms < MS; ++ms) {
     const int ml = prow[ms] + (lane & 31);
-    if (ml >= rows) continue;
-    const int64_t row = row0 + ml;
+    const bool live = ml < rows;
+    const int64_t row = row0 + (live ? ml : 0);
+    if constexpr (EPI == EPI_SWIGLU_BWD) {
+      // routed experts: dH = wrow * (P Q) and the partial row sums of
+      // (P Q) * H over this wave's columns (lanes l, l + 32 share a row)
+      const float wr = (a.wrow && live) ? a.wrow[row] : 1.0f;
+      float gacc = 0.0f;
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+        for (int t = 0; t < NRUN; ++t) {
+          const int n = n0 + qrow[ns] + RSTEP * t + RUN * h;
+          const int blk = n / a.sub;
+          const int gcol = blk * 2 * a.sub + (n - blk * a.sub);
+          float G[RUN], U[RUN], dG[RUN], dU[RUN], wh[RUN];
+          const T* gu = static_cast<const T*>(a.aux) + row * a.ldaux;
+          load_run<T, RUN>(gu + gcol, G);
+          load_run<T, RUN>(gu + gcol + a.sub, U);
+#pragma unroll
+          for (int i = 0; i < RUN; ++i) {
+            const float vv = acc[ns][ms][RUN * t + i];
+            const float sg = sigmoid_f(G[i]);
+            const float gs = G[i] * sg;
+            const float dU0 = vv * gs;
+            const float dG0 = vv * U[i] * sg * (1.0f + G[i] * (1.0f - sg));
+            gacc = fmaf(dU0, U[i], gacc);
+            dG[i] = wr * dG0;
+            dU[i] = wr * dU0;
+            wh[i] = wr * (gs * U[i]);
+          }
+          if (live) {
+            T* dgu = static_cast<T*>(a.C) + row * a.ldc;
+            store_run<T, RUN>(dgu + gcol, dG);
+            store_run<T, RUN>(dgu + gcol + a.sub, dU);
+            if (a.C2) store_run<T, RUN>(static_cast<T*>(a.C2) + row * a.ldc2 + n, wh);
+          }
+        }
+      if (a.gpart) {
+        const float gs = gacc + __shfl_xor(gacc, 32, 64);
+        if (h == 0 && live) a.gpart[row * a.gparts + (n0 / BN) * WN + wn] = gs;
+      }
+      continue;
+    }
+    if (!live) continue;
     if constexpr (EPI == EPI_SWIGLU_FWD) {
 #pragma unroll
       for (int j = 0; j < NS / 2; ++j)
@@ -1128,22 +1490,6 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
             store_run<T, RUN>(static_cast<T*>(a.C) + row * a.ldc + n, v);
           } else if constexpr (EPI == EPI_STORE_F32) {
             store_run<float, RUN>(static_cast<float*>(a.C) + row * a.ldc + n, v);
-          } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-            const int blk = n / a.sub;
-            const int gcol = blk * 2 * a.sub + (n - blk * a.sub);
-            float G[RUN], U[RUN], dG[RUN], dU[RUN];
-            const T* gu = static_cast<const T*>(a.aux) + row * a.ldaux;
-            load_run<T, RUN>(gu + gcol, G);
-            load_run<T, RUN>(gu + gcol + a.sub, U);
-#pragma unroll
-            for (int i = 0; i < RUN; ++i) {
-              const float sg = sigmoid_f(G[i]);
-              dG[i] = v[i] * U[i] * sg * (1.0f + G[i] * (1.0f - sg));
-              dU[i] = v[i] * G[i] * sg;
-            }
-            T* dgu = static_cast<T*>(a.C) + row * a.ldc;
-            store_run<T, RUN>(dgu + gcol, dG);
-            store_run<T, RUN>(dgu + gcol + a.sub, dU);
           }
         }
     }
@@ -1156,9 +1502,10 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
 // contiguous, segments at the padded offsets in a.offsets, each a multiple of
 // 128 tokens, zero past the segment's tokens), scales a.Ps / a.Qs; outputs bf16
 // (or f32 partials).
-template <typename T, int BM, int BN, int OUT_F32, int WM, int WN, bool MX = false>
+template <typename T, int BM, int BN, int OUT_F32, int WM, int WN, bool MX = false, bool PP = false>
 __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
   constexpr int ES = sizeof(T);
+  static_assert(!PP || (ES == 2 && BM == 256 && BN == 256 && WM == 2 && WN == 4), "ping-pong tile");
   using TO = std::conditional_t<MX, __bf16, T>;
   constexpr int NW = WM * WN;
   static_assert(ES == 2 || NW == 4, "the register-staged path runs 4 waves");
@@ -1221,7 +1568,8 @@ __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
   const char* Pb = static_cast<const char*>(a.P) + (MX ? 0 : (int64_t)m0 * ES);
   const char* Qb = static_cast<const char*>(a.Q) + (MX ? 0 : (int64_t)n0 * ES);
   const int64_t pld = a.ldp * ES, qld = a.ldq * ES;
-  const int wm = wave % WM, wn = wave / WM;
+  // ping-pong: group wave / 4 owns a row half, its four waves (one per SIMD) the column quarters
+  const int wm = PP ? wave / WN : wave % WM, wn = PP ? wave % WN : wave / WM;
   int qrow[NS], prow[MS];
 #pragma unroll
   for (int ns = 0; ns < NS; ++ns) qrow[ns] = wn * WTN + ns * 32;
@@ -1279,6 +1627,70 @@ __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
       const uint8_t* sbuf = reinterpret_cast<const uint8_t*>(smem + SC_OFF + st * SSTAGE);
       mfma_chunk_mx<NS, MS>(acc, buf + PD::BYTES, buf, sbuf + BM * 4, sbuf, qrow, prow, lane);
     }
+  } else if constexpr (ES == 2 && PP) {
+    // ---------------- ping-pong main loop (see the row GEMM's): group 0
+    // streams P's token chunks, group 1 Q's; chunk = 32 tokens of the split
+    constexpr int DKB = TileCfg<BM, BN, true, true>::DKB, NSTG = TileCfg<BM, BN, true, true>::NSTG;
+    constexpr int NWL = 4;
+    using PD = DmaKmajor<BM, NWL, DKB>;
+    using QD = DmaKmajor<BN, NWL, DKB>;
+    static_assert(PD::NI == QD::NI, "both halves issue the same number of loads per wave");
+    constexpr int DSTAGE = PD::BYTES + QD::BYTES;
+    constexpr int KSTEPS = DKB / 32;
+    constexpr int LPH = PD::NI;
+    constexpr int DBKK = PD::KROWS;                   // tokens per chunk
+    const int grp = wave >> 2, wq = wave & 3;
+    const char* base = grp == 0 ? Pb : Qb;
+    const int64_t ld = grp == 0 ? pld : qld;
+    uint32_t off[LPH];
+#pragma unroll
+    for (int s2 = 0; s2 < LPH; ++s2) {
+      const int k = PD::k_of(wq, s2, lane);          // (both halves have the same k-row geometry)
+      off[s2] = (uint32_t)(k * ld + PD::gchunk(k, lane) * 16);
+    }
+    // this wave's half of chunk c; tokens at or past kend read as zero
+    auto issue_half = [&](int c) {
+      char* stage = smem + (c % NSTG) * DSTAGE + (grp == 0 ? 0 : PD::BYTES);
+      const int64_t kc = kbeg + (int64_t)c * DBKK;
+      const int kvalid = (int)((kend - kc) < DBKK ? (kend - kc) : DBKK);
+      const rsrc_t rs = make_rsrc(base + kc * ld, (uint32_t)(kvalid * ld));
+#pragma unroll
+      for (int s2 = 0; s2 < LPH; ++s2) dma16(rs, stage + PD::lds_off(wq, s2), off[s2]);
+    };
+    auto wait_chunk = [&](int c, int nkd) {
+      const int later = (nkd - 1 - c) < NSTG - 2 ? (nkd - 1 - c) : NSTG - 2;
+      asm volatile("" ::: "memory");
+      if (later >= 2) wait_vmcnt<2 * LPH>();
+      else if (later == 1) wait_vmcnt<LPH>();
+      else wait_vmcnt<0>();
+    };
+    auto phase_barrier = [&]() {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    static_assert(NSTG - 2 <= 2, "wait_chunk covers at most two later chunks");
+    const int nkd = kend > kbeg ? (int)((kend - kbeg + DBKK - 1) / DBKK) : 0;
+#pragma unroll
+    for (int c = 0; c < NSTG - 1; ++c)
+      if (c < nkd) issue_half(c);
+    if (nkd > 0) wait_chunk(0, nkd);
+    phase_barrier();
+    if (grp == 1) phase_barrier();                  // one phase behind group 0
+    u32x4 fa[KSTEPS][NS], fb[KSTEPS][MS];
+    for (int c = 0; c < nkd; ++c) {
+      const char* buf = smem + (c % NSTG) * DSTAGE;
+      read_chunk_frags<PD, QD, NS, MS, KSTEPS>(fa, fb, buf + PD::BYTES, buf, qrow, prow, lane);
+      if (c + NSTG - 1 < nkd) issue_half(c + NSTG - 1);
+      __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0): fragments in registers, slot read
+      if (c + 1 < nkd) wait_chunk(c + 1, nkd);
+      phase_barrier();
+      __builtin_amdgcn_s_setprio(1);
+      mfma_chunk_frags<T, NS, MS, KSTEPS>(acc, fa, fb);
+      __builtin_amdgcn_s_setprio(0);
+      phase_barrier();
+    }
+    if (grp == 0) phase_barrier();                  // as many barriers as group 1
   } else if constexpr (ES == 2) {
     constexpr int DKB = TileCfg<BM, BN, true>::DKB, NSTG = TileCfg<BM, BN, true>::NSTG;
     using PD = DmaKmajor<BM, NW, DKB>;
@@ -1372,10 +1784,11 @@ __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
 
 // Dynamic LDS of one kernel: the 4-stage ring (16-bit) or two stages of the
 // larger operand pair (f32), plus the schedule scratch of the row GEMMs.
-template <typename T, int BM, int BN, bool WGRAD>
+template <typename T, int BM, int BN, bool WGRAD, bool PP = false>
 constexpr size_t smem_for() {
   if constexpr (sizeof(T) == 2) {
-    return (size_t)TileCfg<BM, BN, WGRAD>::NSTG * (BM + BN) * TileCfg<BM, BN, WGRAD>::DKB + 64;   // direct-load ring
+    using C = TileCfg<BM, BN, WGRAD, PP>;
+    return (size_t)C::NSTG * (BM + BN) * C::DKB + 64;   // direct-load ring
   } else {
     constexpr int nn = Operand<T, BM, false>::BYTES + Operand<T, BN, false>::BYTES;
     constexpr int nt = Operand<T, BM, false>::BYTES + Operand<T, BN, true>::BYTES;
@@ -1409,6 +1822,7 @@ constexpr size_t smem_for() {
   MOE_ROW_KERNEL(moe_gemm_down_f32out_##TN##_##BM##x##BN, T, BM, BN, OP_DOWN_FWD, EPI_STORE_F32)           \
   MOE_ROW_KERNEL(moe_gemm_down_dgrad_swiglu_##TN##_##BM##x##BN, T, BM, BN, OP_DOWN_DGRAD, EPI_SWIGLU_BWD)  \
   MOE_ROW_KERNEL(moe_gemm_gate_up_dgrad_##TN##_##BM##x##BN, T, BM, BN, OP_GU_DGRAD, EPI_STORE)             \
+  MOE_ROW_KERNEL(moe_gemm_gate_up_dgrad_f32out_##TN##_##BM##x##BN, T, BM, BN, OP_GU_DGRAD, EPI_STORE_F32)  \
   MOE_ROW_KERNEL(moe_gemm_router_dx_f32out_##TN##_##BM##x##BN, T, BM, BN, OP_ROUTER_DX, EPI_STORE_F32)     \
   MOE_WGRAD_KERNEL(moe_wgrad_down_##TN##_##BM##x##BN, T, BM, BN, 0)                                        \
   MOE_WGRAD_KERNEL(moe_wgrad_gate_up_##TN##_##BM##x##BN, T, BM, BN, 0)                                     \
@@ -1422,9 +1836,57 @@ constexpr size_t smem_for() {
   MOE_ROW_KERNEL(moe_gemm_down_f32out_##TN##_##BM##x##BN, T, BM, BN, OP_DOWN_FWD, EPI_STORE_F32)           \
   MOE_ROW_KERNEL(moe_gemm_down_dgrad_swiglu_##TN##_##BM##x##BN, T, BM, BN, OP_DOWN_DGRAD, EPI_SWIGLU_BWD)  \
   MOE_ROW_KERNEL(moe_gemm_gate_up_dgrad_##TN##_##BM##x##BN, T, BM, BN, OP_GU_DGRAD, EPI_STORE)             \
+  MOE_ROW_KERNEL(moe_gemm_gate_up_dgrad_f32out_##TN##_##BM##x##BN, T, BM, BN, OP_GU_DGRAD, EPI_STORE_F32)  \
   MOE_ROW_KERNEL(moe_gemm_router_dx_f32out_##TN##_##BM##x##BN, T, BM, BN, OP_ROUTER_DX, EPI_STORE_F32)
 
+// 256 x 256 ping-pong row GEMMs (8 waves, two per SIMD)
+#define MOE_ROW_KERNEL_PP(NAME, T, OP, EPI)                                                         \
+  extern "C" __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))          \
+      NAME(RowGemmArgs a) {                                                                          \
+    extern __shared__ __attribute__((aligned(16))) char smem[];                                     \
+    row_gemm_body<T, 256, 256, OP, EPI, 2, 4, false, true>(a, smem);                                \
+  }
+#define MOE_WGRAD_KERNEL_PP(NAME, T, F32)                                                           \
+  extern "C" __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))          \
+      NAME(WgradArgs a) {                                                                            \
+    extern __shared__ __attribute__((aligned(16))) char smem[];                                     \
+    wgrad_body<T, 256, 256, F32, 2, 4, false, true>(a, smem);                                       \
+  }
+#define MOE_ROW_KERNEL_SET_PP(T, TN)                                                                       \
+  MOE_ROW_KERNEL_PP(moe_gemm_gate_up_swiglu_##TN##_256x256pp, T, OP_GU_FWD, EPI_SWIGLU_FWD)                \
+  MOE_ROW_KERNEL_PP(moe_gemm_down_##TN##_256x256pp, T, OP_DOWN_FWD, EPI_STORE)                             \
+  MOE_ROW_KERNEL_PP(moe_gemm_down_f32out_##TN##_256x256pp, T, OP_DOWN_FWD, EPI_STORE_F32)                  \
+  MOE_ROW_KERNEL_PP(moe_gemm_down_dgrad_swiglu_##TN##_256x256pp, T, OP_DOWN_DGRAD, EPI_SWIGLU_BWD)         \
+  MOE_ROW_KERNEL_PP(moe_gemm_gate_up_dgrad_##TN##_256x256pp, T, OP_GU_DGRAD, EPI_STORE)                    \
+  MOE_ROW_KERNEL_PP(moe_gemm_gate_up_dgrad_f32out_##TN##_256x256pp, T, OP_GU_DGRAD, EPI_STORE_F32)         \
+  MOE_ROW_KERNEL_PP(moe_gemm_router_dx_f32out_##TN##_256x256pp, T, OP_ROUTER_DX, EPI_STORE_F32)         \
+  MOE_WGRAD_KERNEL_PP(moe_wgrad_down_##TN##_256x256pp, T, 0)                                               \
+  MOE_WGRAD_KERNEL_PP(moe_wgrad_gate_up_##TN##_256x256pp, T, 0)                                            \
+  MOE_WGRAD_KERNEL_PP(moe_wgrad_down_f32out_##TN##_256x256pp, T, 1)                                        \
+  MOE_WGRAD_KERNEL_PP(moe_wgrad_gate_up_f32out_##TN##_256x256pp, T, 1)                                     \
+  MOE_WGRAD_KERNEL_PP(moe_wgrad_router_f32out_##TN##_256x256pp, T, 1)
+
+// the down dgrad with the rounding remainders (bf16 plans with few rows per expert)
+#define MOE_DGRAD_LO_KERNEL(BM, BN)                                                                 \
+  extern "C" __global__ void __launch_bounds__((TileCfg<BM, BN, false>::THREADS))                   \
+      __attribute__((amdgpu_waves_per_eu(TileCfg<BM, BN, false>::WAVES_PER_EU)))                    \
+      moe_gemm_down_dgrad_swiglu_lo_bf16_##BM##x##BN(RowGemmArgs a) {                                \
+    extern __shared__ __attribute__((aligned(16))) char smem[];                                   \
+    row_gemm_body<__bf16, BM, BN, OP_DOWN_DGRAD, EPI_SWIGLU_BWD, TileCfg<BM, BN, false>::WM,        \
+                  TileCfg<BM, BN, false>::WN, false, false, true>(a, smem);                         \
+  }
+MOE_DGRAD_LO_KERNEL(128, 128)
+MOE_DGRAD_LO_KERNEL(128, 256)
+MOE_DGRAD_LO_KERNEL(256, 256)
+extern "C" __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+    moe_gemm_down_dgrad_swiglu_lo_bf16_256x256pp(RowGemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  row_gemm_body<__bf16, 256, 256, OP_DOWN_DGRAD, EPI_SWIGLU_BWD, 2, 4, false, true, true>(a, smem);
+}
+
 MOE_KERNEL_SET(__bf16, bf16, 256, 256)
+MOE_ROW_KERNEL_SET_PP(__bf16, bf16)
+MOE_ROW_KERNEL_SET_PP(_Float16, f16)
 MOE_KERNEL_SET(__bf16, bf16, 128, 128)
 MOE_ROW_KERNEL_SET(__bf16, bf16, 128, 256)
 MOE_KERNEL_SET(_Float16, f16, 256, 256)
@@ -1459,34 +1921,51 @@ typedef void (*RowKernel)(RowGemmArgs);
 typedef void (*WgradKernel)(WgradArgs);
 
 struct KernelSet {
-  RowKernel gu, down, down_f32, down_dgrad, gu_dgrad, router_dx_f32;
+  RowKernel gu, down, down_f32, down_dgrad, gu_dgrad, gu_dgrad_f32, router_dx_f32;
   WgradKernel wgrad_down, wgrad_gate_up, wgrad_down_f32, wgrad_gate_up_f32, wgrad_router_f32;
   size_t lds_row, lds_wgrad;
+  RowKernel down_dgrad_lo;   // bf16 only
 };
 
-#define MOE_KERNEL_TABLE(T, TN, BM, BN)                                                                 \
+#define MOE_KERNEL_TABLE(T, TN, BM, BN, LOK)                                                            \
   KernelSet{moe_gemm_gate_up_swiglu_##TN##_##BM##x##BN, moe_gemm_down_##TN##_##BM##x##BN,               \
             moe_gemm_down_f32out_##TN##_##BM##x##BN, moe_gemm_down_dgrad_swiglu_##TN##_##BM##x##BN,     \
-            moe_gemm_gate_up_dgrad_##TN##_##BM##x##BN, moe_gemm_router_dx_f32out_##TN##_##BM##x##BN,       \
+            moe_gemm_gate_up_dgrad_##TN##_##BM##x##BN, moe_gemm_gate_up_dgrad_f32out_##TN##_##BM##x##BN,     \
+            moe_gemm_router_dx_f32out_##TN##_##BM##x##BN,                                                   \
             moe_wgrad_down_##TN##_##BM##x##BN, moe_wgrad_gate_up_##TN##_##BM##x##BN,                      \
             moe_wgrad_down_f32out_##TN##_##BM##x##BN, moe_wgrad_gate_up_f32out_##TN##_##BM##x##BN,        \
             moe_wgrad_router_f32out_##TN##_##BM##x##BN, smem_for<T, BM, BN, false>(),                  \
-            smem_for<T, BM, BN, true>()}
+            smem_for<T, BM, BN, true>(), LOK}
 
-#define MOE_ROW_TABLE(T, TN, BM, BN)                                                                    \
+#define MOE_ROW_TABLE_PP(T, TN, LOK)                                                                    \
+  KernelSet{moe_gemm_gate_up_swiglu_##TN##_256x256pp, moe_gemm_down_##TN##_256x256pp,                   \
+            moe_gemm_down_f32out_##TN##_256x256pp, moe_gemm_down_dgrad_swiglu_##TN##_256x256pp,         \
+            moe_gemm_gate_up_dgrad_##TN##_256x256pp, moe_gemm_gate_up_dgrad_f32out_##TN##_256x256pp,         \
+            moe_gemm_router_dx_f32out_##TN##_256x256pp,                                                     \
+            moe_wgrad_down_##TN##_256x256pp, moe_wgrad_gate_up_##TN##_256x256pp,                              \
+            moe_wgrad_down_f32out_##TN##_256x256pp, moe_wgrad_gate_up_f32out_##TN##_256x256pp,                \
+            moe_wgrad_router_f32out_##TN##_256x256pp, smem_for<T, 256, 256, false, true>(),                 \
+            smem_for<T, 256, 256, true, true>(), LOK}
+
+#define MOE_ROW_TABLE(T, TN, BM, BN, LOK)                                                               \
   KernelSet{moe_gemm_gate_up_swiglu_##TN##_##BM##x##BN, moe_gemm_down_##TN##_##BM##x##BN,               \
             moe_gemm_down_f32out_##TN##_##BM##x##BN, moe_gemm_down_dgrad_swiglu_##TN##_##BM##x##BN,     \
-            moe_gemm_gate_up_dgrad_##TN##_##BM##x##BN, moe_gemm_router_dx_f32out_##TN##_##BM##x##BN,       \
-            nullptr, nullptr, nullptr, nullptr, nullptr, smem_for<T, BM, BN, false>(), 0}
+            moe_gemm_gate_up_dgrad_##TN##_##BM##x##BN, moe_gemm_gate_up_dgrad_f32out_##TN##_##BM##x##BN,     \
+            moe_gemm_router_dx_f32out_##TN##_##BM##x##BN,                                                   \
+            nullptr, nullptr, nullptr, nullptr, nullptr, smem_for<T, BM, BN, false>(), 0, LOK}
 
 const KernelSet* kernel_set(int dt, int tile) {
-  static const KernelSet bf16_256 = MOE_KERNEL_TABLE(__bf16, bf16, 256, 256);
-  static const KernelSet bf16_128 = MOE_KERNEL_TABLE(__bf16, bf16, 128, 128);
-  static const KernelSet bf16_128x256 = MOE_ROW_TABLE(__bf16, bf16, 128, 256);
-  static const KernelSet f16_256 = MOE_KERNEL_TABLE(_Float16, f16, 256, 256);
-  static const KernelSet f16_128 = MOE_KERNEL_TABLE(_Float16, f16, 128, 128);
-  static const KernelSet f16_128x256 = MOE_ROW_TABLE(_Float16, f16, 128, 256);
-  static const KernelSet f32_128 = MOE_KERNEL_TABLE(float, f32, 128, 128);
+  static const KernelSet bf16_256 = MOE_KERNEL_TABLE(__bf16, bf16, 256, 256, moe_gemm_down_dgrad_swiglu_lo_bf16_256x256);
+  static const KernelSet bf16_128 = MOE_KERNEL_TABLE(__bf16, bf16, 128, 128, moe_gemm_down_dgrad_swiglu_lo_bf16_128x128);
+  static const KernelSet bf16_128x256 =
+      MOE_ROW_TABLE(__bf16, bf16, 128, 256, moe_gemm_down_dgrad_swiglu_lo_bf16_128x256);
+  static const KernelSet f16_256 = MOE_KERNEL_TABLE(_Float16, f16, 256, 256, nullptr);
+  static const KernelSet f16_128 = MOE_KERNEL_TABLE(_Float16, f16, 128, 128, nullptr);
+  static const KernelSet f16_128x256 = MOE_ROW_TABLE(_Float16, f16, 128, 256, nullptr);
+  static const KernelSet f32_128 = MOE_KERNEL_TABLE(float, f32, 128, 128, nullptr);
+  static const KernelSet bf16_pp = MOE_ROW_TABLE_PP(__bf16, bf16, moe_gemm_down_dgrad_swiglu_lo_bf16_256x256pp);
+  static const KernelSet f16_pp = MOE_ROW_TABLE_PP(_Float16, f16, nullptr);
+  if (tile == TILE_256PP) return dt == DT_BF16 ? &bf16_pp : (dt == DT_F16 ? &f16_pp : nullptr);
   if (dt == DT_BF16) return tile == TILE_256 ? &bf16_256 : (tile == TILE_128x256 ? &bf16_128x256 : &bf16_128);
   if (dt == DT_F16) return tile == TILE_256 ? &f16_256 : (tile == TILE_128x256 ? &f16_128x256 : &f16_128);
   if (dt == DT_F32 && tile == 128) return &f32_128;
@@ -1494,10 +1973,10 @@ const KernelSet* kernel_set(int dt, int tile) {
     constexpr size_t mx_lds = 2 * (128 + 128) * MX_DKB + 2 * (128 + 128) * 4 + 64;
     static const KernelSet mx_128{moe_mx_gemm_gate_up_swiglu_128x128, moe_mx_gemm_down_128x128,
                                   moe_mx_gemm_down_f32out_128x128, moe_mx_gemm_down_dgrad_swiglu_128x128,
-                                  moe_mx_gemm_gate_up_dgrad_128x128, nullptr,
+                                  moe_mx_gemm_gate_up_dgrad_128x128, nullptr, nullptr,
                                   moe_mx_wgrad_down_128x128, moe_mx_wgrad_gate_up_128x128,
                                   moe_mx_wgrad_down_f32out_128x128, moe_mx_wgrad_gate_up_f32out_128x128,
-                                  nullptr, mx_lds, mx_lds};
+                                  nullptr, mx_lds, mx_lds, nullptr};
     return &mx_128;
   }
   return nullptr;
@@ -1523,12 +2002,15 @@ hipError_t launch_row_gemm(int dt, int op, int epi, int tile, const RowGemmArgs&
   switch (op) {
     case OP_GU_FWD: k = set->gu; break;
     case OP_DOWN_FWD: k = (epi == EPI_STORE_F32) ? set->down_f32 : set->down; break;
-    case OP_DOWN_DGRAD: k = set->down_dgrad; break;
-    case OP_GU_DGRAD: k = set->gu_dgrad; break;
+    case OP_DOWN_DGRAD: k = a.C_lo ? set->down_dgrad_lo : set->down_dgrad; break;
+    case OP_GU_DGRAD: k = (epi == EPI_STORE_F32) ? set->gu_dgrad_f32 : set->gu_dgrad; break;
     case OP_ROUTER_DX: k = set->router_dx_f32; break;
     default: return hipErrorInvalidValue;
   }
   if (!k) return hipErrorInvalidValue;
+  if (a.C_lo && (op != OP_DOWN_DGRAD || !a.C2 || !a.C2_lo)) return hipErrorInvalidValue;
+  // the f16 and MX-fp8 down dgrads write no w H rows
+  if (op == OP_DOWN_DGRAD && a.C2 && (dt == DT_F16 || dt == DT_MXFP8)) return hipErrorInvalidValue;
   if (dt == DT_MXFP8 && (a.ldp % 128 || a.ldq % 128 || a.q_group_stride % 32 || !a.Ps || !a.Qs))
     return hipErrorInvalidValue;
   if (dt == DT_F32 && tile != TILE_128) return hipErrorInvalidValue;
@@ -1545,7 +2027,7 @@ hipError_t launch_row_gemm(int dt, int op, int epi, int tile, const RowGemmArgs&
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipError_t e = prepare((const void*)k, set->lds_row);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(tile == TILE_256 ? 512 : 256),
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3((tile == TILE_256 || tile == TILE_256PP) ? 512 : 256),
                      set->lds_row, s, a);
   return hipGetLastError();
 }
@@ -1560,17 +2042,19 @@ hipError_t launch_wgrad(int dt, int op, int tile, const WgradArgs& a, hipStream_
     case WG_ROUTER: k = set->wgrad_router_f32; break;
     default: return hipErrorInvalidValue;
   }
-  if (!k || (op == WG_ROUTER && !a.out_f32) || (tile != TILE_128 && tile != TILE_256)) return hipErrorInvalidValue;
+  if (!k || (op == WG_ROUTER && !a.out_f32) || (tile != TILE_128 && tile != TILE_256 && tile != TILE_256PP))
+    return hipErrorInvalidValue;
   if (dt == DT_MXFP8 && (a.ldp % 128 || a.ldq % 128 || !a.offsets || !a.Ps || !a.Qs)) return hipErrorInvalidValue;
-  if (a.M % tile || a.N % tile) return hipErrorInvalidValue;
-  const int64_t chunk8 = 8 * (int64_t)(a.N / tile);   // whole rounds of XCD chunks (xcd_chunked)
-  int64_t grid = (int64_t)a.G * a.splits * (a.M / tile) * (a.N / tile);
+  const int bt = tile_rows(tile);                     // square tiles: 128 or 256
+  if (a.M % bt || a.N % bt) return hipErrorInvalidValue;
+  const int64_t chunk8 = 8 * (int64_t)(a.N / bt);     // whole rounds of XCD chunks (xcd_chunked)
+  int64_t grid = (int64_t)a.G * a.splits * (a.M / bt) * (a.N / bt);
   grid = (grid + chunk8 - 1) / chunk8 * chunk8;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipError_t e = prepare((const void*)k, set->lds_wgrad);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(tile == 256 ? 512 : 256),
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(tile == TILE_128 ? 256 : 512),
                      set->lds_wgrad, s, a);
   return hipGetLastError();
 }

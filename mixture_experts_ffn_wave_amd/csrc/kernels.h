@@ -65,7 +65,9 @@ struct RowGemmArgs {
   int K;                           // contraction length
   int sub;                         // width of one shared expert (= I for routed experts)
   void* C; int64_t ldc;            // main output
-  void* C2; int64_t ldc2;          // second output (H for OP_GU_FWD)
+  void* C2; int64_t ldc2;          // second output: H (SwiGLU forward); for the SwiGLU backward of
+                                   // routed experts, optional wrow[r] H[r] rounded once (the down
+                                   // weight gradient's operand), H in f32 from the saved G, U
   const void* aux; int64_t ldaux;  // saved GU (SwiGLU backward epilogue)
   // DT_MXFP8 only: scale bytes of P ([rows][K/32], row stride ldp/32) and of
   // Q ([rows][K/32], row stride ldq/32, group stride q_group_stride/32)
@@ -75,15 +77,35 @@ struct RowGemmArgs {
   // [rows][ldc2], Hs [rows][ldc2/32].  Backward: [dG | dU] into Hq
   // [rows][ldc], Hs [rows][ldc/32].
   uint8_t* Hq; uint8_t* Hs;
-  // DT_MXFP8, optional: token-side row r is row gather[r] of P (and of Ps),
-  // P holding p_rows rows (p_rows * ldp < 2^31); nullptr reads row r itself
+  // Optional: token-side row r is row gather[r] of P (and of Ps for MX), P
+  // holding p_rows rows (p_rows * ldp * element bytes < 2^31); nullptr reads
+  // row r itself
   const int32_t* gather; int64_t p_rows;
+  // EPI_SWIGLU_BWD of the routed experts of a 16-bit or f32 layer (nullptr
+  // otherwise): wrow [rows] f32 routing weight of each row, dH = wrow[r] *
+  // (P Q)[r]; gpart [rows][gparts] f32, the partial row sums of
+  // (P Q)[r][n] * H[r][n] (H = silu(G) U from the saved G, U, in f32) over
+  // each wave's BN / WN columns, written at index n0 / (BN / WN) + wave column
+  const float* wrow; float* gpart; int gparts;
+  // EPI_SWIGLU_BWD, 16-bit layers, optional: the rounding remainders
+  // v - round(v) of [dG | dU] (C_lo, layout of C) and of the C2 values
+  // (C2_lo, layout of C2), rounded to the layer's dtype; the weight
+  // gradients add their products to those of the rounded values
+  void* C_lo = nullptr; void* C2_lo = nullptr;
 };
+// Intermediates a bf16 layer with bf16 experts keeps in f32 (the saved gate/up
+// pre-activations [G | U], the expert output rows Y_perm and the input-gradient
+// rows dX_perm and dx_shared): rounded to bf16 they alone move y, dx and the
+// router gradient by up to 2-3 % of their RMS.  MX-fp8 experts keep [G | U]
+// and dX_perm in bf16 and Y_perm in f32; f16 and f32 layers keep all of them
+// in their own dtype.
+inline bool f32_intermediates(int dt, bool mx) { return dt == DT_BF16 && !mx; }
 // Output tile shapes (rows x columns): TILE_128 = 128 x 128 (every dtype),
-// TILE_256 = 256 x 256 and TILE_128x256 = 128 x 256 (16-bit types; the latter
-// for the row GEMMs only).  The plan chooses one per GEMM.
-enum TileShape { TILE_128 = 128, TILE_256 = 256, TILE_128x256 = 384 };
-inline int tile_rows(int t) { return t == TILE_256 ? 256 : 128; }
+// TILE_256 = 256 x 256, TILE_128x256 = 128 x 256 and TILE_256PP = 256 x 256
+// with the ping-pong main loop (16-bit types; the last two for the row GEMMs
+// only).  The plan chooses one per GEMM.
+enum TileShape { TILE_128 = 128, TILE_256 = 256, TILE_128x256 = 384, TILE_256PP = 512 };
+inline int tile_rows(int t) { return (t == TILE_256 || t == TILE_256PP) ? 256 : 128; }
 inline int tile_cols(int t) { return t == TILE_128 ? 128 : 256; }
 hipError_t launch_row_gemm(int dt, int op, int epi, int tile, const RowGemmArgs& a, hipStream_t s);
 
@@ -150,21 +172,26 @@ hipError_t launch_mx_single_segment(int32_t* seg_pad, int64_t T, int align, hipS
 
 // ------------------------------------------------------ element-wise --
 struct CombineArgs {
-  const float* y_perm; const int32_t* inv; const float* wts; const void* y_shared; void* y;
+  const void* y_perm;   // [T*k, d]: f32 when y_f32, else the activation dtype
+  const int32_t* inv; const float* wts; const void* y_shared; void* y;
   int64_t T; int d, k;
+  int y_f32;
 };
 hipError_t launch_combine(int dt, const CombineArgs& a, hipStream_t s);
 
 struct CombineBwdArgs {
   const void* dy; const float* y_perm; const int32_t* inv; const float* wts;
-  void* dy_perm;  // [T*k, d]
-  float* g;       // [T, k]
+  void* dy_perm;  // [T*k, d]: row inv[t, j] = wts[t, j] dy[t], or dy[t] itself when `copy`
+  float* g;       // [T, k]: g = <dy, y_perm row> (y_perm f32, MX-fp8 experts), or nullptr
   int64_t T; int d, k;
+  // without g: the routing weight of each expert-sorted row, wsorted[inv[t, j]] = wts[t, j]
+  float* wsorted = nullptr;
   // MX-fp8 experts (16-bit layer): dY_perm also quantised along its rows
   // (blocks of 32) into q [T*k, d] and qs [T*k, d/32]; nullptr skips it
   uint8_t* q = nullptr; uint8_t* qs = nullptr;
   // and dY itself (the shared experts' output gradient) into dq [T, d], dqs [T, d/32]
   uint8_t* dq = nullptr; uint8_t* dqs = nullptr;
+  int copy = 0;   // 1: dy_perm rows are plain copies of dy rows (no routing weight)
 };
 hipError_t launch_combine_bwd(int dt, const CombineBwdArgs& a, hipStream_t s);
 
@@ -176,6 +203,9 @@ struct RouterDzArgs {
   // balancing statistic over real tokens: mask [T] (0 = filler) and the real
   // tokens' counts [E] plus their number at [E]; nullptr = every token
   const int32_t* mask = nullptr; const int32_t* rcounts = nullptr;
+  // g from partial sums instead of g [T, k]: g[t, j] = sum over p < gparts of
+  // gpart[inv[t, j] * gparts + p], in that order
+  const float* gpart = nullptr; const int32_t* inv = nullptr; int gparts = 0;
 };
 int router_dz_blocks(int64_t T);
 hipError_t launch_router_dz(int dt, const RouterDzArgs& a, hipStream_t s);
@@ -197,6 +227,7 @@ struct RouterBwdSmallArgs {
   float* dbias_part;      // [nblk, E]
   int64_t T; int E, Ep, d, k, renorm; float aux_coef;
   const int32_t* mask = nullptr; const int32_t* rcounts = nullptr;   // as in RouterDzArgs
+  const float* gpart = nullptr; const int32_t* inv = nullptr; int gparts = 0;  // as in RouterDzArgs
 };
 int router_small_blocks(int64_t T);
 hipError_t launch_router_bwd_small(int dt, const RouterBwdSmallArgs& a, hipStream_t s);
@@ -228,6 +259,7 @@ struct UnpermuteArgs {
   const void* w_router;    // [E, d]
   void* dx;                // [T, d]
   int64_t T; int d, k, E, Ep;
+  int src_f32 = 0;         // dx_perm and dx_shared rows are f32 (else the activation dtype)
 };
 hipError_t launch_unpermute(int dt, const UnpermuteArgs& a, hipStream_t s);
 constexpr int kRouterDxVectorMaxE = 32;   // up to this many experts the router part of dx is computed inline

@@ -24,20 +24,22 @@ class MoELayer:
         self.offsets = z(E + 1, dtype=torch.int32)
         self.perm_token = z(A, dtype=torch.int32)
         # MX experts: the gate/up GEMM and its weight gradient gather x's rows
-        # by perm_token instead of reading x_perm (False: the x_perm path)
-        self.mx_gather = plan.mx
+        # by perm_token instead of reading x_perm (False: the x_perm path);
+        # the gather addresses x with 32-bit offsets
+        self.mx_gather = plan.mx and T * d < 2 ** 31
         # x_perm is written only when something reads it: the non-MX experts,
-        # the x_perm path, or a caller that inspects it (write_x_perm = True)
+        # the x_perm path, or a caller that inspects it (write_x_perm = True);
+        # on the gather path it is allocated on first use
         self.write_x_perm = False
         self.inv_perm = z(T, k, dtype=torch.int32)
-        self.x_perm = z(A, d)
-        self.gu = z(A, 2 * I)
+        self._x_perm = None if self.mx_gather else z(A, d)
+        self.gu = z(A, 2 * I, dtype=p.gu_dtype)
         self.h = z(A, I)
-        self.y_perm = z(A, d, dtype=torch.float32)
+        self.y_perm = z(A, d, dtype=p.y_perm_dtype)
         self.y = z(T, d)
         if p.Ns > 0:
             NI = p.Ns * p.Is
-            self.gu_shared = z(T, 2 * NI)
+            self.gu_shared = z(T, 2 * NI, dtype=p.gu_dtype)
             self.h_shared = z(T, NI)
             self.y_shared = z(T, d)
         else:
@@ -60,6 +62,13 @@ class MoELayer:
         self.balance_gamma = 0.0
         self.real_mask = None     # statistic over real tokens only: set by set_real_mask()
         self.real_counts = None
+
+    @property
+    def x_perm(self):
+        if self._x_perm is None:
+            p = self.plan
+            self._x_perm = torch.empty(p.T * p.k, p.d, dtype=p.dtype, device=self.probs.device)
+        return self._x_perm
 
     def set_real_mask(self, mask):
         """Compute the balancing statistic (and its gradient) over the tokens
@@ -100,7 +109,7 @@ class MoELayer:
         xp = self.x_perm if (self.write_x_perm or not self.mx_gather) else None
         L.moe_permute(self.plan, self.topk_idx, q["x"], self.counts, self.offsets, self.perm_token,
                       self.inv_perm, xp, self.ws, stream)
-        L.moe_expert_ffn(self.plan, self.x_perm, self.offsets, q["w_gate_up"], q["w_down"], self.gu,
+        L.moe_expert_ffn(self.plan, xp, self.offsets, q["w_gate_up"], q["w_down"], self.gu,
                          self.h, self.y_perm, q["x"], q["ws_gate_up"], q["ws_down"], self.gu_shared,
                          self.h_shared, self.y_shared, self.ws, stream,
                          perm_token=self.perm_token if self.mx_gather else None)
@@ -114,12 +123,15 @@ class MoELayer:
     # ------------------------------------------------------------- backward
     def saved(self):
         q = self.params
+        # perm_token: the down dgrad of 16-bit / f32 experts gathers dy by it,
+        # and MX experts on the gather path read x's rows through it
         return dict(x=q["x"], w_router=q["w_router"], probs=self.probs, topk_idx=self.topk_idx,
                     topk_w=self.topk_w, counts=self.counts, offsets=self.offsets, inv_perm=self.inv_perm,
-                    x_perm=self.x_perm, gu=self.gu, h=self.h, y_perm=self.y_perm, w_gate_up=q["w_gate_up"],
-                    w_down=q["w_down"], ws_gate_up=q["ws_gate_up"], ws_down=q["ws_down"],
-                    gu_shared=self.gu_shared, h_shared=self.h_shared, real_mask=self.real_mask,
-                    real_counts=self.real_counts, perm_token=self.perm_token if self.mx_gather else None)
+                    x_perm=None if self.mx_gather else self._x_perm, gu=self.gu, h=self.h,
+                    y_perm=self.y_perm, w_gate_up=q["w_gate_up"], w_down=q["w_down"],
+                    ws_gate_up=q["ws_gate_up"], ws_down=q["ws_down"], gu_shared=self.gu_shared,
+                    h_shared=self.h_shared, real_mask=self.real_mask, real_counts=self.real_counts,
+                    perm_token=self.perm_token if (self.mx_gather or not self.plan.mx) else None)
 
     def backward(self, dy, stream=None):
         L.moe_backward(self.plan, self.saved(), dy, self.grads, self.ws, stream)
@@ -127,13 +139,18 @@ class MoELayer:
 
     def backward_intermediate(self, name):
         """View of an intermediate the last backward left in the workspace
-        ("dy_perm", "dgu", "dx_perm", "dgu_shared", "dx_shared")."""
+        ("dy_perm", "dgu", "dx_perm", "dgu_shared", "dx_shared"; bf16 and f32
+        experts also "wh", the w H rows of the down weight gradient; bf16
+        plans with few rows per expert also "dgu_lo", "wh_lo", the rounding
+        remainders)."""
         p = self.plan
         A, NI = p.T * p.k, p.Ns * p.Is
         shape = {"dy_perm": (A, p.d), "dgu": (A, 2 * p.I), "dx_perm": (A, p.d),
-                 "dgu_shared": (p.T, 2 * NI), "dx_shared": (p.T, p.d)}[name]
+                 "dgu_shared": (p.T, 2 * NI), "dx_shared": (p.T, p.d), "wh": (A, p.I),
+                 "dgu_lo": (A, 2 * p.I), "wh_lo": (A, p.I)}[name]
         off, nb = L.workspace_region(p, name)
-        return self.ws[off:off + nb].view(p.dtype).view(*shape)
+        dt = p.dx_rows_dtype if name in ("dx_perm", "dx_shared") else p.dtype
+        return self.ws[off:off + nb].view(dt).view(*shape)
 
     def aux_stats(self, stream=None):
         if self.real_mask is not None:

@@ -65,7 +65,8 @@ WORKLOADS = {
 }
 
 TINY = "t512_d256_e8k2_i128_f32"
-BENCH = "t16384_d512_e8k2_i768_bf16"
+BENCH = "t16384_d512_e8k2_i768_bf16"                 # the small bf16 workload (full-size parity case)
+LARGEST = "t32768_d1536_e4k2_i3072_s1x3072_f16"      # the largest single-GPU workload: the benchmark's default
 
 
 def zipf_bias(E, s):

@@ -1,33 +1,27 @@
 """Shared helpers of the GPU parity tests: run the HIP path through the C ABI,
 run the fp64 oracle on the same seeded inputs, compare.
 
-Reference.  f32 and f16 layers are compared with the exact fp64 oracle.  A
-bf16 layer is compared with the fp64 oracle run with its storage rounding
-(``store``: G, U, H, dY_perm, [dG | dU], dX_perm and the shared experts'
-values rounded to bf16 where the layer keeps them, Y_perm and dz to f32): a
-bf16 layer that keeps those values in bf16 lands up to ~0.2 x RMS away from
-the exact layer on the weight gradients of experts that see a handful of
-tokens, whatever its kernels do, so the exact oracle cannot tell a faithful
-kernel from a wrong one there.  The distance of the GPU result from the exact
-oracle is printed as well.
+Reference.  f32, f16 and bf16 layers are compared with the exact fp64 oracle
+(no rounding anywhere in it).  The fp64 oracle run with the layer's storage
+rounding (``store``) is printed beside it as a diagnostic only.
 
 Tolerances, per output matrix and element (each expert's weight gradient is
 its own matrix, as each expert is a separate parameter, with its RMS floored
 at the RMS of the whole stacked gradient):
   |gpu - oracle| <= c * RMS(oracle tensor) + ulp(value) / 2
-  (one ulp for values the bf16 reference itself rounds to storage: G, U, H,
-  Y_perm (an f32 ulp), the shared experts' G, U, H, Y)
   with c = 2e-2 for bf16 / f16 storage (the layer's stated bar) and c = 1e-4
   for f32 storage (f32 MFMA products, f32 intermediates).  The half-ulp term
   is the rounding of the result into its storage dtype, which no
   implementation that returns that dtype can avoid: for bf16 it alone reaches
   2^-8 of an element just above a power of two, i.e. about 2.2% of the RMS at
-  the largest elements of these tensors.  The raw max|err|/RMS is reported
-  too.  Router probabilities and
+  the largest elements of these tensors.  The raw max|err|/RMS and the excess
+  over the half ulp are reported too.  Router probabilities and
   routing weights within 1e-6 absolute; routing indices, counts, offsets,
   permutation and inverse permutation bit-exact, except tokens whose oracle
   logits tie within 1e-5 (set or slot order), whose GPU choice must only be a
   valid top-k within that margin.
+
+MX-fp8 experts (KohakUwULLM README, "Key features"): see full_parity.
 """
 
 import sys
@@ -53,6 +47,33 @@ def rel_tol(wl):
     return 1e-4 if wl.dtype == "f32" else 2e-2
 
 
+# MX-fp8 layers.  Step-wise: every GEMM step of the oracle run on the inputs
+# the GPU step received (quantised by the oracle from the GPU's stored
+# values, which the bit-exact code tests show the GPU quantises identically),
+# so only f32 against fp64 accumulation separates the two.
+MX_STEP_TOL = 2e-3
+# End to end against the oracle's whole MX layer (bf16 storage, no GPU value
+# in it): a stored value one bf16 ulp away from the oracle's (f32 against fp64
+# accumulation) lands on a neighbouring e4m3 code now and then, and at a
+# block's largest value moves the block's scale, so single elements can
+# differ by a code step; the criterion is on the bulk of the tensor:
+# relative Frobenius distance <= MX_E2E_FRO and the 99.9th percentile of
+# (|err| - ulp/2) <= MX_E2E_P999 x RMS.
+MX_E2E_FRO = 2e-2
+MX_E2E_P999 = 6e-2
+
+
+def gu_dtype(wl):
+    """Storage of the saved [G | U] (include/moe.h, moe_ffn_args)."""
+    if wl.expert_dtype == "mxfp8":
+        return "bf16"
+    return "f32" if wl.dtype == "bf16" else wl.dtype
+
+
+def y_perm_dtype(wl):
+    return "f32" if wl.expert_dtype == "mxfp8" or wl.dtype == "bf16" else wl.dtype
+
+
 def plan_for(wl, has_bias):
     from mixture_experts_ffn_wave_amd import Plan
     return Plan(wl.T, wl.d, wl.E, wl.k, wl.I, n_shared=wl.n_shared, d_ff_shared=wl.I_shared,
@@ -69,13 +90,15 @@ def to_np(t):
     return t.to(torch.float64).numpy()
 
 
-def gpu_run(wl, inp, routing=None, intermediates=False, sel_bias=None, mask=None):
+def gpu_run(wl, inp, routing=None, intermediates=False, sel_bias=None, mask=None, extra=()):
     """One fwd+bwd step on cuda:0.  ``routing`` (probs, idx, w as numpy) replaces
     the router's outputs when given (then moe_route is not called).
     ``intermediates`` also returns what the backward left in the workspace
     (dy_perm, dgu, dx_perm and, with shared experts, dgu_shared, dx_shared).
     ``sel_bias`` (numpy [E]) routes with aux-loss-free balancing; ``mask``
-    (numpy [T], 0 = filler) takes the balancing statistic over real tokens."""
+    (numpy [T], 0 = filler) takes the balancing statistic over real tokens.
+    ``extra`` names further workspace intermediates to return ("wh",
+    "dgu_lo", "wh_lo")."""
     from mixture_experts_ffn_wave_amd import MoELayer, decode_aux
     b = inp.get("bias")
     plan = plan_for(wl, b is not None)
@@ -112,7 +135,7 @@ def gpu_run(wl, inp, routing=None, intermediates=False, sel_bias=None, mask=None
     if mask is not None:
         out["real_counts"] = to_np(layer.real_counts)
     if intermediates:
-        names = ["dy_perm", "dgu", "dx_perm"] + (["dgu_shared", "dx_shared"] if wl.n_shared else [])
+        names = ["dy_perm", "dgu", "dx_perm"] + (["dgu_shared", "dx_shared"] if wl.n_shared else []) + list(extra)
         for n in names:
             out[n] = to_np(layer.backward_intermediate(n))
     return out
@@ -173,7 +196,7 @@ def check_close(name, got, ref, c, dtype="f32", ulps=0.5, rms_floor=0.0):
     excess = diff - 2.0 * ulps * half_ulp(np.maximum(np.abs(got), np.abs(ref)), dtype)
     err = float(diff.max())
     worst = float(excess.max())
-    REPORT.append((name, err / rms if rms > 0 else 0.0))
+    REPORT.append((name, err / rms if rms > 0 else 0.0, worst / rms if rms > 0 else 0.0))
     if not STRICT[0]:
         return err, rms
     assert worst <= c * rms + 1e-30, (f"{name}: max(|err| - ulp/2) {worst:.3e} > {c:g} x RMS {rms:.3e} "
@@ -237,18 +260,19 @@ def compare_downstream(wl, gpu, fwd, bwd, st, rounded=False):
     half an ulp of rounding, so they are allowed one ulp."""
     c = rel_tol(wl)
     dt = wl.dtype
+    gdt, ydt = gu_dtype(wl), y_perm_dtype(wl)
     ku = 1.0 if rounded else 0.5
     compare_dispatch(gpu, fwd)
     inter = wl.I
-    check_close("G", gpu["gu"][:, :inter], fwd["g"], c, dt, ku)
-    check_close("U", gpu["gu"][:, inter:], fwd["u"], c, dt, ku)
+    check_close("G", gpu["gu"][:, :inter], fwd["g"], c, gdt, ku)
+    check_close("U", gpu["gu"][:, inter:], fwd["u"], c, gdt, ku)
     check_close("H", gpu["h"], fwd["h"], c, dt, ku)
-    check_close("Y_perm", gpu["y_perm"], fwd["y_perm"], c, "f32", ku)
+    check_close("Y_perm", gpu["y_perm"], fwd["y_perm"], c, ydt, ku)
     if wl.n_shared:
         Is = wl.I_shared
         for s, (gs, us, hs) in enumerate(fwd["shared"]):
-            check_close(f"G_shared[{s}]", gpu["gu_shared"][:, 2 * s * Is:2 * s * Is + Is], gs, c, dt, ku)
-            check_close(f"U_shared[{s}]", gpu["gu_shared"][:, 2 * s * Is + Is:2 * (s + 1) * Is], us, c, dt, ku)
+            check_close(f"G_shared[{s}]", gpu["gu_shared"][:, 2 * s * Is:2 * s * Is + Is], gs, c, gdt, ku)
+            check_close(f"U_shared[{s}]", gpu["gu_shared"][:, 2 * s * Is + Is:2 * (s + 1) * Is], us, c, gdt, ku)
             check_close(f"H_shared[{s}]", gpu["h_shared"][:, s * Is:(s + 1) * Is], hs, c, dt, ku)
         check_close("Y_shared", gpu["y_shared"], fwd["y_shared"], c, dt, ku)
     check_close("y", gpu["y"], fwd["y"], c, dt)
@@ -283,7 +307,7 @@ def compare_mx_stepwise(wl, gpu, fwd, f64, st):
     checked on the inputs the GPU step received: the oracle's step function
     runs on the GPU's stored G, U, H, Y_perm, dY_perm, [dG | dU], dX_perm
     (and the shared experts' counterparts), quantising them itself."""
-    c = rel_tol(wl)
+    c = MX_STEP_TOL
     dt = wl.dtype
     q = O.mx_fake_quant
     sr = storage_rounding(wl)
@@ -373,27 +397,83 @@ def compare_mx_stepwise(wl, gpu, fwd, f64, st):
     compare_stats(gpu, st)
 
 
+def compare_mx_end_to_end(wl, gpu, fwd, bwd):
+    """An MX layer against the oracle's whole MX layer (bf16 storage; no GPU
+    value enters it): the MX_E2E_* criterion on every stored intermediate and
+    every output."""
+    dt = wl.dtype
+    pairs = [("G", gpu["gu"][:, :wl.I], fwd["g"], dt), ("U", gpu["gu"][:, wl.I:], fwd["u"], dt),
+             ("H", gpu["h"], fwd["h"], dt), ("Y_perm", gpu["y_perm"], fwd["y_perm"], "f32"),
+             ("y", gpu["y"], fwd["y"], dt), ("dx", gpu["dx"], bwd["dx"], dt),
+             ("dW_router", gpu["dw_router"], bwd["dw_router"], dt), ("dbias", gpu["dbias"], bwd["dbias"], "f32"),
+             ("dW_gate_up", gpu["dw_gate_up"], bwd["dw_gate_up"], dt), ("dW_down", gpu["dw_down"], bwd["dw_down"], dt)]
+    if wl.n_shared:
+        pairs += [("Y_shared", gpu["y_shared"], fwd["y_shared"], dt),
+                  ("dWs_gate_up", gpu["dws_gate_up"], bwd["dws_gate_up"], dt),
+                  ("dWs_down", gpu["dws_down"], bwd["dws_down"], dt)]
+    out = {}
+    for name, got, ref, sdt in pairs:
+        got = np.asarray(got, dtype=np.float64)
+        ref = np.asarray(ref, dtype=np.float64)
+        assert got.shape == ref.shape and np.all(np.isfinite(got)), name
+        if ref.size == 0:
+            continue
+        rms = float(np.sqrt(np.mean(ref * ref)))
+        fro = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+        exc = np.abs(got - ref) - half_ulp(np.maximum(np.abs(got), np.abs(ref)), sdt)
+        p999 = float(np.quantile(exc, 0.999)) / max(rms, 1e-300)
+        out[name] = (fro, p999)
+        assert fro <= MX_E2E_FRO and p999 <= MX_E2E_P999, (
+            f"{name}: relative Frobenius {fro:.4f} (bar {MX_E2E_FRO}), 99.9th percentile {p999:.4f} x RMS "
+            f"(bar {MX_E2E_P999}) against the oracle's MX layer")
+    return out
+
+
+def _report(wl, tag):
+    worst = {}
+    for n, r, e in REPORT:
+        key = n.split("[")[0]
+        a = worst.get(key, (0.0, 0.0))
+        worst[key] = (max(a[0], r), max(a[1], e))
+    say(f"[parity] {wl.name}: {tag}, max|err|/RMS raw/excess " +
+        " ".join(f"{n}={r:.4f}/{e:.4f}" for n, (r, e) in worst.items()))
+
+
+def _diagnostic(fn):
+    """Run a comparison without asserting (it fills REPORT)."""
+    REPORT.clear()
+    STRICT[0] = False
+    try:
+        fn()
+    finally:
+        STRICT[0] = True
+
+
 def full_parity(wl, inp=None, mx_diagnostic=True, sel_bias=None, mask=None):
     """The whole chain on the GPU against the oracle.  When a near-tie made
     the GPU pick a different (valid) routing, the downstream calls are run a
     second time from the oracle's routing so every later tensor is compared
     on identical assignments.
 
-    A layer with MX-fp8 experts is compared with the oracle's layer that
-    quantises the same GEMM operands to MX-fp8 (the method's own step), with
-    bf16 storage of what it keeps between steps, one GEMM step at a time
-    (compare_mx_stepwise); ``mx_diagnostic`` also prints its distance from
-    that whole oracle layer and from the unquantised layer, for the record."""
+    f32 / f16 / bf16 experts: every tensor against the exact fp64 oracle
+    (compare_downstream, asserted); for bf16 the oracle with the layer's
+    storage rounding is printed beside it.
+
+    MX-fp8 experts: (1) one GEMM step at a time (compare_mx_stepwise, at
+    MX_STEP_TOL) against the oracle's MX-quantised steps on the inputs the
+    GPU step received, (2) end to end against the oracle's whole MX layer
+    (compare_mx_end_to_end, the MX_E2E_* criterion); ``mx_diagnostic`` also
+    prints the distance from the exact, unquantised layer, which the method
+    itself does not come within 6e-2 x RMS of (tests/golden
+    mx_method_distance)."""
     if inp is None:
         inp = MI.make_inputs(wl)
     f64 = oracle_inputs(inp)
     say(f"[parity] {wl.name}: {MI.describe(wl)} -- GPU chain")
     mx = wl.expert_dtype == "mxfp8"
     gpu = gpu_run(wl, inp, intermediates=mx, sel_bias=sel_bias, mask=mask)
-    rounded = wl.dtype == "bf16" or mx
-    say(f"[parity] {wl.name}: oracle" + (" (bf16 storage rounding)" if rounded else "") +
-        (" (MX-quantised expert GEMM operands)" if mx else ""))
-    fwd, bwd, st = oracle_run(wl, f64, storage_rounding(wl) if rounded else None,
+    say(f"[parity] {wl.name}: oracle" + (" (MX-quantised expert GEMM operands, bf16 storage)" if mx else " (exact)"))
+    fwd, bwd, st = oracle_run(wl, f64, storage_rounding(wl) if mx else None,
                               quant=O.mx_fake_quant if mx else None, sel_bias=sel_bias, mask=mask)
     identical = compare_routing(wl, gpu, fwd)
     if not identical:
@@ -403,39 +483,19 @@ def full_parity(wl, inp=None, mx_diagnostic=True, sel_bias=None, mask=None):
     REPORT.clear()
     if mx:
         compare_mx_stepwise(wl, gpu, fwd, f64, st)
+        _report(wl, "MX step-wise")
+        e2e = compare_mx_end_to_end(wl, gpu, fwd, bwd)
+        say(f"[parity] {wl.name}: vs the whole MX oracle layer, relative Frobenius / p99.9 excess " +
+            " ".join(f"{n}={a:.4f}/{b:.4f}" for n, (a, b) in e2e.items()))
+        if mx_diagnostic:
+            xf, xb, xs = oracle_run(wl, f64, sel_bias=sel_bias, mask=mask)
+            _diagnostic(lambda: compare_downstream(wl, gpu, xf, xb, xs))
+            _report(wl, "vs exact (unquantised) oracle, not asserted")
     else:
-        compare_downstream(wl, gpu, fwd, bwd, st, rounded=rounded)
-    worst = {}
-    for n, r in REPORT:
-        key = n.split("[")[0]
-        worst[key] = max(worst.get(key, 0.0), r)
-    say(f"[parity] {wl.name}: raw max|err|/RMS " + " ".join(f"{n}={r:.4f}" for n, r in worst.items()))
-    if mx and mx_diagnostic:
-        # distance from the oracle's whole MX layer, for the record (not asserted)
-        REPORT.clear()
-        STRICT[0] = False
-        try:
-            compare_downstream(wl, gpu, fwd, bwd, st, rounded=True)
-        finally:
-            STRICT[0] = True
-        ex = {}
-        for n, r in REPORT:
-            key = n.split("[")[0]
-            ex[key] = max(ex.get(key, 0.0), r)
-        say(f"[parity] {wl.name}: vs the whole MX oracle layer, raw max|err|/RMS " +
-            " ".join(f"{n}={r:.4f}" for n, r in ex.items()))
-    if rounded and (mx_diagnostic or not mx):
-        # distance from the exact layer, for the record (not asserted)
-        xf, xb, xs = oracle_run(wl, f64, sel_bias=sel_bias, mask=mask)
-        REPORT.clear()
-        STRICT[0] = False
-        try:
-            compare_downstream(wl, gpu, xf, xb, xs)
-        finally:
-            STRICT[0] = True
-        ex = {}
-        for n, r in REPORT:
-            key = n.split("[")[0]
-            ex[key] = max(ex.get(key, 0.0), r)
-        say(f"[parity] {wl.name}: vs exact oracle, raw max|err|/RMS " + " ".join(f"{n}={r:.4f}" for n, r in ex.items()))
+        compare_downstream(wl, gpu, fwd, bwd, st)
+        _report(wl, "vs exact oracle")
+        if wl.dtype == "bf16" and mx_diagnostic:
+            rf, rb, rs = oracle_run(wl, f64, storage_rounding(wl), sel_bias=sel_bias, mask=mask)
+            _diagnostic(lambda: compare_downstream(wl, gpu, rf, rb, rs, rounded=True))
+            _report(wl, "vs storage-rounded oracle, not asserted")
     return gpu, fwd, bwd, st

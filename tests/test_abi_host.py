@@ -229,8 +229,9 @@ def test_workspace_regions_lie_inside_the_workspace_and_do_not_overlap():
     T, d, E, k, I, Ns, Is = 300, 256, 8, 2, 128, 2, 128
     p = L.Plan(T, d, E, k, I, n_shared=Ns, d_ff_shared=Is)
     ws = p.workspace_bytes()
-    expect = {"dy_perm": T * k * d * 2, "dgu": T * k * 2 * I * 2, "dx_perm": T * k * d * 2,
-              "dgu_shared": T * 2 * Ns * Is * 2, "dx_shared": T * d * 2}
+    # a bf16 layer keeps the experts' input-gradient rows in f32
+    expect = {"dy_perm": T * k * d * 2, "dgu": T * k * 2 * I * 2, "dx_perm": T * k * d * 4,
+              "dgu_shared": T * 2 * Ns * Is * 2, "dx_shared": T * d * 4}
     spans = []
     for name, nbytes in expect.items():
         off, nb = L.workspace_region(p, name)
@@ -248,3 +249,44 @@ def test_workspace_regions_lie_inside_the_workspace_and_do_not_overlap():
     assert lib.moe_workspace_region(q.handle, b"dgu_shared", ctypes.byref(off), ctypes.byref(nb)) == MOE_ERR_INVALID
     assert lib.moe_workspace_region(q.handle, b"dgu", ctypes.byref(off), ctypes.byref(nb)) == MOE_OK
     q.close()
+
+
+def test_mx_code_regions_have_their_stated_sizes_and_do_not_overlap():
+    lib = L.lib()
+    T, d, E, k, I, Ns, Is = 300, 256, 8, 2, 128, 2, 128
+    A, NI = T * k, Ns * Is
+    p = L.Plan(T, d, E, k, I, n_shared=Ns, d_ff_shared=Is, expert_dtype="mxfp8")
+    ws = p.workspace_bytes()
+    Apad = L.workspace_region(p, "mx_dyt")[1] // d
+    Tpad = (T + 127) // 128 * 128
+    assert Apad % 128 == 0 and Apad >= A + 127 * E
+    rows = {"mx_xq": (A, d), "mx_hq": (A, I), "mx_dyq": (A, d), "mx_dguq": (A, 2 * I), "mx_wgu": (E * 2 * I, d),
+            "mx_wd": (E * d, I), "mx_wdt": (I, E * d), "mx_wgut": (d, E * 2 * I), "mx_dyt": (d, Apad),
+            "mx_ht": (I, Apad), "mx_dgut": (2 * I, Apad), "mx_xt": (d, Apad), "mx_sxq": (T, d), "mx_shq": (T, NI),
+            "mx_sdyq": (T, d), "mx_sdguq": (T, 2 * NI), "mx_swgu": (2 * NI, d), "mx_swd": (d, NI),
+            "mx_swdt": (NI, d), "mx_swgut": (d, 2 * NI), "mx_sdyt": (d, Tpad), "mx_sht": (NI, Tpad),
+            "mx_sdgut": (2 * NI, Tpad), "mx_sxt": (d, Tpad)}
+    spans = []
+    for name, (R, K) in rows.items():
+        off, nb = L.workspace_region(p, name)
+        assert nb == R * K, name
+        so, sb = L.workspace_region(p, name + ".scales")
+        assert sb == R * (K // 32), name
+        for o, b in ((off, nb), (so, sb)):
+            assert o % 256 == 0 and o + b <= ws, name
+            spans.append((o, o + b))
+    off, nb = L.workspace_region(p, "mx_pad")
+    assert nb == (E + 1) * 4
+    spans.append((off, off + nb))
+    spans.sort()
+    assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:])), "regions overlap"
+    o, n = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.moe_workspace_region(p.handle, b"mx_nope", ctypes.byref(o), ctypes.byref(n)) == MOE_ERR_INVALID
+    p.close()
+    q = L.Plan(T, d, E, k, I)                                  # not an MX plan: no code regions
+    assert lib.moe_workspace_region(q.handle, b"mx_hq", ctypes.byref(o), ctypes.byref(n)) == MOE_ERR_INVALID
+    q.close()
+    r = L.Plan(T, d, E, k, I, expert_dtype="mxfp8")            # no shared experts: no shared regions
+    assert lib.moe_workspace_region(r.handle, b"mx_sxq", ctypes.byref(o), ctypes.byref(n)) == MOE_ERR_INVALID
+    assert lib.moe_workspace_region(r.handle, b"mx_hq.scales", ctypes.byref(o), ctypes.byref(n)) == MOE_OK
+    r.close()
