@@ -63,7 +63,8 @@ typedef enum {
   MOE_ERR_INVALID = -2,     /* a size or flag is out of range */
   MOE_ERR_UNSUPPORTED = -3, /* valid but not implemented (dtype pair, alignment) */
   MOE_ERR_WORKSPACE = -4,   /* workspace missing or smaller than moe_workspace_bytes() */
-  MOE_ERR_HIP = -5          /* the HIP runtime reported an error */
+  MOE_ERR_HIP = -5,         /* the HIP runtime reported an error */
+  MOE_ERR_SCRATCH = -6      /* an allocation-free call needs more than its fixed scratch */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_F16 = 1, MOE_BF16 = 2, MOE_MXFP8_E4M3 = 3 } moe_dtype;
@@ -162,6 +163,22 @@ moe_status moe_balance_update(moe_plan plan, const int32_t* counts, float* sel_b
 moe_status moe_permute(moe_plan plan, const int32_t* topk_idx, const void* x, int32_t* counts,
                        int32_t* offsets, int32_t* perm_token, int32_t* inv_perm, void* x_perm,
                        void* ws, size_t ws_bytes, void* stream);
+
+/* moe_permute without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results and error checks as
+ * moe_permute; its scratch (2 * ceil(T / 256) * E int32, each half rounded up
+ * to 256 bytes) lives in a fixed 1 MiB device array inside the library, one
+ * per GPU, held until the process ends; a plan needing more returns
+ * MOE_ERR_SCRATCH before anything is launched (e.g. T <= 65536 with E <= 256
+ * fits).  Nothing in the scratch has to start at zero (every call writes what
+ * it reads).  The first call on a device looks up the array's address
+ * (hipGetSymbolAddress); no call allocates.  All calls on one GPU share the
+ * array: calls that overlap in time on one GPU (concurrent streams, or
+ * threads) race and must be ordered by the caller. */
+moe_status moe_permute_noalloc(moe_plan plan, const int32_t* topk_idx, const void* x, int32_t* counts,
+                               int32_t* offsets, int32_t* perm_token, int32_t* inv_perm, void* x_perm,
+                               void* stream);
 
 /* Pointers of the expert FFN (shared-expert fields are ignored when n_shared == 0). */
 typedef struct {

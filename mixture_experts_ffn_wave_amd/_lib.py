@@ -15,6 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_F32, MOE_F16, MOE_BF16, MOE_MXFP8_E4M3 = 0, 1, 2, 3
+MOE_ERR_SCRATCH = -6
 _DTYPE_CODE = {torch.float32: MOE_F32, torch.float16: MOE_F16, torch.bfloat16: MOE_BF16}
 
 c_int32, c_int64, c_float, c_void_p, c_size_t = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
@@ -65,6 +66,7 @@ SIGNATURES = {
     "moe_route_balanced": (c_int32, [c_void_p] * 9),
     "moe_balance_update": (c_int32, [c_void_p, c_void_p, c_void_p, c_float, c_void_p]),
     "moe_permute": (c_int32, [c_void_p] * 9 + [c_size_t, c_void_p]),
+    "moe_permute_noalloc": (c_int32, [c_void_p] * 9),
     "moe_expert_ffn": (c_int32, [c_void_p, ctypes.POINTER(MoeFfnArgs), c_void_p, c_size_t, c_void_p]),
     "moe_combine": (c_int32, [c_void_p] * 7),
     "moe_backward": (c_int32, [c_void_p, ctypes.POINTER(MoeSaved), c_void_p, ctypes.POINTER(MoeGrads),
@@ -231,6 +233,19 @@ def moe_permute(plan, topk_idx, x, counts, offsets, perm_token, inv_perm, x_perm
                            _ptr(perm_token), _ptr(inv_perm), _ptr(x_perm), _ptr(ws), ws.numel(),
                            _stream(stream))
     _check("moe_permute", st)
+
+
+def moe_permute_noalloc(plan, topk_idx, x, counts, offsets, perm_token, inv_perm, x_perm, stream=None):
+    """moe_permute with its scratch in the library's fixed device array (no workspace)."""
+    T, d, E, k, dt = plan.T, plan.d, plan.E, plan.k, plan.dtype
+    _need(topk_idx, "topk_idx", (T, k), torch.int32); _need(x, "x", (T, d), dt)
+    _need(counts, "counts", (E,), torch.int32); _need(offsets, "offsets", (E + 1,), torch.int32)
+    _need(perm_token, "perm_token", (T * k,), torch.int32); _need(inv_perm, "inv_perm", (T, k), torch.int32)
+    if x_perm is not None:
+        _need(x_perm, "x_perm", (T * k, d), dt)
+    st = lib().moe_permute_noalloc(plan.handle, _ptr(topk_idx), _ptr(x), _ptr(counts), _ptr(offsets),
+                                   _ptr(perm_token), _ptr(inv_perm), _ptr(x_perm), _stream(stream))
+    _check("moe_permute_noalloc", st)
 
 
 def moe_expert_ffn(plan, x_perm, offsets, w_gate_up, w_down, gu, h, y_perm, x=None, ws_gate_up=None,

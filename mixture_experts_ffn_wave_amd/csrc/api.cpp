@@ -221,6 +221,7 @@ const char* moe_status_string(moe_status s) {
     case MOE_ERR_UNSUPPORTED: return "valid but unsupported configuration (dtype or alignment)";
     case MOE_ERR_WORKSPACE: return "workspace missing or smaller than moe_workspace_bytes()";
     case MOE_ERR_HIP: return "the HIP runtime reported an error";
+    case MOE_ERR_SCRATCH: return "the call needs more scratch than the fixed device array of an allocation-free call";
   }
   return "unknown status";
 }
@@ -619,6 +620,36 @@ moe_status moe_permute(moe_plan p, const int32_t* topk_idx, const void* x, int32
   PermuteArgs a{topk_idx, x, counts, offsets, perm_token, inv_perm, x_perm,
                 reinterpret_cast<int32_t*>(wsp(ws, p->o_block_counts)),
                 reinterpret_cast<int32_t*>(wsp(ws, p->o_block_base)), p->T, p->d, p->E, p->k};
+  {
+    Probe pr(p, "permute_hist", s);
+    MOE_TRY(launch_permute_hist(a, s));
+  }
+  {
+    Probe pr(p, "permute_scan", s);
+    MOE_TRY(launch_permute_scan(a, s));
+  }
+  {
+    Probe pr(p, "permute_scatter", s);
+    MOE_TRY(launch_permute_scatter(p->dt, a, s));
+  }
+  return MOE_OK;
+}
+
+// Scratch bytes moe_permute needs: [blocks x E] counts, then [blocks x E] first rows.
+static size_t permute_scratch_bytes(moe_plan p) { return 2 * align_up((size_t)p->nblk_hist * p->E * 4); }
+
+moe_status moe_permute_noalloc(moe_plan p, const int32_t* topk_idx, const void* x, int32_t* counts, int32_t* offsets,
+                               int32_t* perm_token, int32_t* inv_perm, void* x_perm, void* stream) {
+  if (!p) return MOE_ERR_NULL;
+  if (!counts || !offsets) return MOE_ERR_NULL;
+  if (p->T > 0 && (!topk_idx || !perm_token || !inv_perm || (x_perm && !x))) return MOE_ERR_NULL;
+  if (permute_scratch_bytes(p) > kPermuteScratchBytes) return MOE_ERR_SCRATCH;
+  void* scr = nullptr;
+  MOE_TRY(permute_scratch(&scr));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* bc = static_cast<int32_t*>(scr);
+  int32_t* bb = reinterpret_cast<int32_t*>(static_cast<char*>(scr) + permute_scratch_bytes(p) / 2);
+  PermuteArgs a{topk_idx, x, counts, offsets, perm_token, inv_perm, x_perm, bc, bb, p->T, p->d, p->E, p->k};
   {
     Probe pr(p, "permute_hist", s);
     MOE_TRY(launch_permute_hist(a, s));

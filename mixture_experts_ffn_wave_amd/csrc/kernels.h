@@ -45,6 +45,11 @@ struct PermuteArgs {
   int d, E, k;
 };
 hipError_t launch_permute_hist(const PermuteArgs& a, hipStream_t s);
+// Fixed device scratch of the allocation-free permute (moe_permute_noalloc):
+// its size, and its address on the current device (looked up once per device).
+constexpr size_t kPermuteScratchBytes = (size_t)1 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t permute_scratch(void** ptr);
 hipError_t launch_permute_scan(const PermuteArgs& a, hipStream_t s);
 hipError_t launch_permute_scatter(int dt, const PermuteArgs& a, hipStream_t s);
 

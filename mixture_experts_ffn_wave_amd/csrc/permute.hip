@@ -16,11 +16,20 @@
 //      perm_token, reads the token's row of x once and writes it k times
 //      (every access a full 16-byte vector, rows contiguous).
 
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 namespace {
+
+// Scratch of moe_permute_noalloc: the [blocks x E] counts and first rows that
+// moe_permute keeps in the caller's workspace, in a fixed device array (each
+// GPU the library runs on holds its own copy until the process ends).  Host
+// code reaches it only through the address hipGetSymbolAddress returns for
+// the current device (permute_scratch below), never through its name.
+static __device__ __align__(256) uint8_t scratch[kPermuteScratchBytes];
 
 constexpr int NT = 256;
 constexpr int WORDS = kHistTokens / 32;   // 32-bit mask words per expert per block
@@ -196,6 +205,25 @@ hipError_t launch_permute_scatter_tw(int dt, const PermuteArgs& a, hipStream_t s
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t permute_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* per_device[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!per_device[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));    // the array's address on the current device
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_permute_scatter(int dt, const PermuteArgs& a, hipStream_t s) {

@@ -290,3 +290,16 @@ def test_mx_code_regions_have_their_stated_sizes_and_do_not_overlap():
     assert lib.moe_workspace_region(r.handle, b"mx_sxq", ctypes.byref(o), ctypes.byref(n)) == MOE_ERR_INVALID
     assert lib.moe_workspace_region(r.handle, b"mx_hq.scales", ctypes.byref(o), ctypes.byref(n)) == MOE_OK
     r.close()
+
+
+def test_permute_noalloc_refuses_plans_beyond_its_fixed_scratch():
+    """moe_permute_noalloc keeps its [blocks x E] scratch in a 1 MiB device
+    array: 2^20 tokens (4096 blocks) x 256 experts need 8 MiB, refused with
+    MOE_ERR_SCRATCH before anything is launched; null pointers first."""
+    lib = L.lib()
+    fake = ctypes.c_void_p(0x1000)
+    big = L.Plan(1 << 20, 128, 256, 2, 128, dtype=L.torch.bfloat16)
+    assert lib.moe_permute_noalloc(big.handle, fake, fake, fake, fake, fake, fake, None, None) == L.MOE_ERR_SCRATCH
+    assert lib.moe_permute_noalloc(big.handle, None, fake, fake, fake, fake, fake, None, None) == MOE_ERR_NULL
+    assert lib.moe_permute_noalloc(None, fake, fake, fake, fake, fake, fake, None, None) == MOE_ERR_NULL
+    assert b"scratch" in lib.moe_status_string(L.MOE_ERR_SCRATCH)
