@@ -485,6 +485,120 @@ __global__ void __launch_bounds__(256) route_esplit_kernel(RouteArgs a) {
   route_epilogue_wide<NSUB>(red, t0, wave, lane, a, s_bias, s_sel, s_wts);
 }
 
+// Many experts, more tokens per workgroup: 64 tokens and eight waves (two
+// token halves by four expert quarters).  Each K chunk of W_r staged in LDS
+// then serves 64 tokens instead of 32: x still streams once from HBM, and
+// W_r (re-read from L2 by every workgroup, four times the bytes of x's rows
+// at 128 experts with 32 tokens) is read half as often.  One workgroup per
+// CU at 16384 tokens.  The two halves finish their tokens as above, four
+// waves each.
+template <typename T, int NSUB>
+__global__ void __launch_bounds__(512) route_esplit64_kernel(RouteArgs a) {
+  constexpr int ES = sizeof(T);
+  constexpr int BK = KB / ES;
+  constexpr int EP = 32 * NSUB;
+  constexpr int NW = 8, SPW = NSUB / 4;            // expert subtiles per wave
+  constexpr int NTH = 64 * NW;
+  constexpr int WPT = EP * 8 / NTH;                // 16-byte chunks of the W tile per thread
+  constexpr int TILES = (64 + EP) * LROW;
+  constexpr int RED = 2 * NSUB * 16 * 64 * 4;      // logits of both halves
+  constexpr int LDSB = TILES > RED ? TILES : RED;
+  static_assert(NSUB % 4 == 0 && 64 * 8 == NTH && WPT >= 1 && WPT * NTH == EP * 8, "tile split");
+  __shared__ __attribute__((aligned(16))) char lds[LDSB];
+  __shared__ float s_bias[EP], s_sel[EP];
+  __shared__ float s_wts[2 * kWtsLds];
+  stage_bias<NSUB>(s_bias, s_sel, a);              // visible after the K loop's first barrier
+  char* lx = lds;
+  char* lw = lds + 64 * LROW;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int th = wave & 1, eg = wave >> 1;         // token half, expert quarter
+  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  const char* xb = static_cast<const char*>(a.x);
+  const char* wb = static_cast<const char*>(a.w);
+  auto load = [&](int kc, u32x4& rx, u32x4* rw) {
+    {
+      const int r = tid >> 3, cc = tid & 7;
+      rx = (t0 + r < a.T) ? ld16(xb + ((t0 + r) * a.d + kc) * ES + cc * 16) : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int s = 0; s < WPT; ++s) {
+      const int c = tid + NTH * s, r = c >> 3, cc = c & 7;
+      rw[s] = (r < a.E) ? ld16(wb + ((int64_t)r * a.d + kc) * ES + cc * 16) : (u32x4){0u, 0u, 0u, 0u};
+    }
+  };
+  auto stage = [&](const u32x4& rx, const u32x4* rw) {
+    st16(lx + (tid >> 3) * LROW + (tid & 7) * 16, rx);
+#pragma unroll
+    for (int s = 0; s < WPT; ++s) {
+      const int c = tid + NTH * s;
+      st16(lw + (c >> 3) * LROW + (c & 7) * 16, rw[s]);
+    }
+  };
+
+  f32x16 acc[SPW];
+#pragma unroll
+  for (int s = 0; s < SPW; ++s)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[s][r] = 0.0f;
+
+  constexpr int CH = Mma32<T>::kChunks;
+  constexpr int PF = 3;
+  const int nk = a.d / BK;
+  u32x4 rx[PF], rw[PF][WPT];
+#pragma unroll
+  for (int q = 0; q < PF; ++q)
+    if (q < nk) load(q * BK, rx[q], rw[q]);
+  for (int kc0 = 0; kc0 < nk; kc0 += PF) {
+#pragma unroll
+    for (int q = 0; q < PF; ++q) {
+      const int kc = kc0 + q;
+      if (kc < nk) {
+        stage(rx[q], rw[q]);
+        __syncthreads();
+        if (kc + PF < nk) load((kc + PF) * BK, rx[q], rw[q]);
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+          const int kb = ks * 16 * ES + (lane >> 5) * 8 * ES;
+          u32x4 fb[CH];
+          const char* xrow = lx + (th * 32 + (lane & 31)) * LROW + kb;
+#pragma unroll
+          for (int ch = 0; ch < CH; ++ch) fb[ch] = ld16(xrow + ch * 16);
+#pragma unroll
+          for (int s = 0; s < SPW; ++s) {
+            u32x4 fa[CH];
+            const char* wrow = lw + ((eg + 4 * s) * 32 + (lane & 31)) * LROW + kb;
+#pragma unroll
+            for (int ch = 0; ch < CH; ++ch) fa[ch] = ld16(wrow + ch * 16);
+            Mma32<T>::run(acc[s], fa, fb);
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+
+  // logits -> LDS: [token half][subtile][r][lane] (the accumulator layout)
+  float* red = reinterpret_cast<float*>(lds);
+  __syncthreads();                                 // (also covers an empty K loop)
+#pragma unroll
+  for (int s = 0; s < SPW; ++s)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[((th * NSUB + eg + 4 * s) * 16 + r) * 64 + lane] = acc[s][r];
+  __syncthreads();
+  const int half = wave >> 2;                      // waves 0-3 finish tokens 0-31, waves 4-7 tokens 32-63
+  route_epilogue_wide<NSUB>(red + half * NSUB * 16 * 64, t0 + 32 * half, wave & 3, lane, a, s_bias, s_sel,
+                            s_wts + half * kWtsLds);
+}
+
+template <typename T, int NSUB>
+hipError_t launch_route_esplit64(const RouteArgs& a, hipStream_t s) {
+  const int64_t grid = (a.T + 63) / 64;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((route_esplit64_kernel<T, NSUB>), dim3((unsigned)grid), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
 template <typename T, int NSUB>
 hipError_t launch_route_esplit(const RouteArgs& a, hipStream_t s) {
   const int64_t grid = (a.T + 31) / 32;
@@ -506,7 +620,7 @@ hipError_t launch_route_dt(const RouteArgs& a, hipStream_t s) {
   const int nsub = (a.E + 31) / 32;
   if (nsub <= 1) return launch_route_ksplit<T, 1, 4>(a, s);
   if (nsub <= 2) return launch_route_ksplit<T, 2, 4>(a, s);
-  if (nsub <= 4) return launch_route_esplit<T, 4>(a, s);
+  if (nsub <= 4) return launch_route_esplit64<T, 4>(a, s);
   return launch_route_esplit<T, 8>(a, s);
 }
 

@@ -19,6 +19,8 @@ Configurations (everything not named is computed exactly in fp64 here):
                 routing-weight gradient g = <dy W_d, H> from f32 G, U, and
                 the down weight gradient from dy's own rows and bf16(w H)
                 with H in f32
+  [G | U] bf16  as library, the saved pre-activations rounded to bf16 (the
+                SwiGLU backward and the routing-weight gradient read them)
   Y_perm bf16   as library, Y_perm rounded to bf16
   dX_perm bf16  as library, dX_perm rounded to bf16
   dW_down from bf16(w dy), bf16(H)
@@ -48,7 +50,7 @@ import moe_inputs as MI  # noqa: E402
 import oracle as O  # noqa: E402
 
 WORKLOAD = "t16384_d2048_e128k8_i768_zipf_bf16"
-CONFIGS = {"library": set(), "Y_perm bf16": {"Y"}, "dX_perm bf16": {"dXp"},
+CONFIGS = {"library": set(), "[G | U] bf16": {"GU"}, "Y_perm bf16": {"Y"}, "dX_perm bf16": {"dXp"},
            "dW_down from bf16(w dy), bf16(H)": {"wgH"},
            "all bf16": {"GU", "gH", "dXp", "dYw", "wgH"}}
 
@@ -88,13 +90,14 @@ def variant(wl, f, xf, xb, flags):
         Yp = Hb @ Wd[e].T
         np.add.at(y, perm[r0:r1], wr[r0:r1, None] * (R(Yp) if "Y" in flags else Yp))
         dyr = dy[perm[r0:r1]]
-        g[r0:r1] = (dyr * Yp).sum(1) if "gH" in flags else (dyr * (Hx @ Wd[e].T)).sum(1)
+        Gs, Us = (R(G), R(U)) if "GU" in flags else (G, U)   # the saved pre-activations
+        Hs = O.silu(Gs) * Us                                  # H as the backward forms it
+        g[r0:r1] = (dyr * Yp).sum(1) if "gH" in flags else (dyr * (Hs @ Wd[e].T)).sum(1)
         dYw = R(wr[r0:r1, None] * dyr)
         dH = dYw @ Wd[e] if "dYw" in flags else wr[r0:r1, None] * (dyr @ Wd[e])
-        Gs, Us = (R(G), R(U)) if "GU" in flags else (G, U)
         sg = 1.0 / (1.0 + np.exp(-Gs))
         dGU = R(np.concatenate([dH * Us * sg * (1 + Gs * (1 - sg)), dH * Gs * sg], 1))   # operand
-        dwd[e] = dYw.T @ Hb if "wgH" in flags else dyr.T @ R(wr[r0:r1, None] * Hx)
+        dwd[e] = dYw.T @ Hb if "wgH" in flags else dyr.T @ R(wr[r0:r1, None] * Hs)
         dwgu[e] = dGU.T @ X
         dX = dGU @ Wgu[e]
         np.add.at(dx, perm[r0:r1], R(dX) if "dXp" in flags else dX)
