@@ -22,6 +22,8 @@ from .moe_oracle import (  # noqa: F401
     topk_select,
     gate_weights,
     balanced_selection_scores,
+    sinkhorn_column_scales,
+    sinkhorn_selection_scores,
     balance_bias_update,
     near_tie_tokens,
     expert_permutation,

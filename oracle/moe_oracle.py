@@ -25,6 +25,10 @@ Readings where the pages are silent (each is also listed in the design notes):
     with aux-loss-free load balancing, no rule given) follows the published
     method: top-k on probability + per-expert selection bias, weights from the
     unbiased probabilities, bias += gamma * sign(mean load - load) per step;
+  * the Sinkhorn router (KohakUwULLM README, "Key features": named, no rule)
+    follows the published Sinkhorn-Knopp balancing: a fixed number of
+    alternating row / column scalings of the batch's probability matrix,
+    top-k on the column-scaled probabilities, weights from the unscaled ones;
   * f_e = count_e / (T * k), P_e = mean over all T tokens of the full softmax,
     aux = E * sum_e f_e * P_e (equals 1 at perfect balance; E = 4 gives the
     model card's "4 * sum");
@@ -88,6 +92,35 @@ def balanced_selection_scores(p, sel_bias):
     still taken from the unbiased probabilities).  Rank with topk_select;
     weights with gate_weights on the unbiased ``p``."""
     return p + np.asarray(sel_bias, dtype=np.float64)[None, :]
+
+
+def sinkhorn_column_scales(p, n_iter):
+    """Column scales b [E] of the Sinkhorn router.  KohakUwULLM README, "Key
+    features", names Sinkhorn routers beside the default one and gives no
+    rule; the reading taken is the published Sinkhorn-Knopp balancing of the
+    batch's [T, E] routing-probability matrix toward equal row sums (1/T,
+    every token routed) and equal column sums (1/E, every expert equally
+    loaded): starting from b = 1, ``n_iter`` times
+        a_t = (1/T) / sum_e p_te b_e,   then   b_e = (1/E) / sum_t p_te a_t.
+    A fixed number of rounds (no convergence test) keeps the layer free of
+    host synchronisation."""
+    p = np.asarray(p, dtype=np.float64)
+    T, E = p.shape
+    b = np.ones(E)
+    for _ in range(int(n_iter)):
+        a = (1.0 / T) / (p @ b)
+        b = (1.0 / E) / (p.T @ a)
+    return b
+
+
+def sinkhorn_selection_scores(p, b):
+    """Scores the Sinkhorn router ranks for top-k: the balanced matrix
+    a_t p_te b_e of one token, without its row scale a_t (common to the
+    token's experts, so it does not change the ranking).  Rank with
+    topk_select; the gate weights stay the unscaled probabilities of the
+    chosen experts (gate_weights on ``p``), so the selection carries no
+    gradient."""
+    return np.asarray(p, dtype=np.float64) * np.asarray(b, dtype=np.float64)[None, :]
 
 
 def balance_bias_update(sel_bias, counts, T, top_k, gamma):
@@ -277,12 +310,15 @@ def expert_down_step(h, w_down_e, quant=None):
 
 
 def layer_forward(x, w_router, w_gate_up, w_down, *, top_k, renorm=True, bias=None,
-                  ws_gate_up=None, ws_down=None, quant=None, store=None, sel_bias=None):
+                  ws_gate_up=None, ws_down=None, quant=None, store=None, sel_bias=None,
+                  sinkhorn_iters=None):
     """Full forward pass.  Returns a dict of every intermediate.
 
     ``sel_bias`` (aux-loss-free balancing) moves the choice of experts to
     balanced_selection_scores(p, sel_bias); the weights stay the unbiased
-    probabilities of the chosen experts.
+    probabilities of the chosen experts.  ``sinkhorn_iters`` (the Sinkhorn
+    router) moves it to sinkhorn_selection_scores(p, b) with b =
+    sinkhorn_column_scales(p, sinkhorn_iters), returned as "sinkhorn_b".
 
     ``quant``, if given, is applied to each operand of each expert GEMM as
     quant(array, axis) with ``axis`` the contraction axis of that GEMM (the MX
@@ -302,7 +338,12 @@ def layer_forward(x, w_router, w_gate_up, w_down, *, top_k, renorm=True, bias=No
     E = w_router.shape[0]
     z = router_logits(x, w_router, bias)
     p = softmax_rows(z)
-    idx = topk_select(z if sel_bias is None else balanced_selection_scores(p, sel_bias), top_k)
+    sk_b = None
+    if sinkhorn_iters is not None:
+        sk_b = sinkhorn_column_scales(p, sinkhorn_iters) if T > 0 else np.ones(E)
+        idx = topk_select(sinkhorn_selection_scores(p, sk_b), top_k)
+    else:
+        idx = topk_select(z if sel_bias is None else balanced_selection_scores(p, sel_bias), top_k)
     w = gate_weights(p, idx, renorm)
     counts, offsets, perm_token, inv = expert_permutation(idx, E)
     x_perm = x[perm_token]
@@ -331,7 +372,7 @@ def layer_forward(x, w_router, w_gate_up, w_down, *, top_k, renorm=True, bias=No
                 y_perm=y_perm, y_shared=y_shared, shared=shared, y=y,
                 x=x, w_router=w_router, w_gate_up=w_gate_up, w_down=w_down,
                 ws_gate_up=ws_gate_up, ws_down=ws_down, top_k=top_k,
-                renorm=renorm, bias=bias, store=store, sel_bias=sel_bias)
+                renorm=renorm, bias=bias, store=store, sel_bias=sel_bias, sinkhorn_b=sk_b)
 
 
 def expert_down_backward_step(dy_rows, g, u, h, w_down_e, quant=None, store=None):
