@@ -140,6 +140,25 @@ moe_status moe_route_balanced(moe_plan plan, const void* x, const void* w_router
                               const float* sel_bias, float* probs, int32_t* topk_idx, float* topk_w,
                               void* stream);
 
+/* Sinkhorn router (KohakUwULLM README, "Key features": Sinkhorn routers
+ * beside the default; the pages give no rule, so this library follows the
+ * published Sinkhorn-Knopp balancing of the batch's routing probabilities).
+ * probs as moe_route; then n_iter rounds of
+ *   a_t = (1/T) / sum_e probs[t, e] b_e,   b_e = (1/E) / sum_t probs[t, e] a_t
+ * from b = 1 (f32, every sum in a fixed order), and each token's k experts
+ * are the largest probs[t, e] * b_e (descending; on equal values the lower
+ * expert index first).  topk_w holds the chosen probabilities themselves
+ * (divided by their sum when cfg.renorm): the selection carries no gradient
+ * and moe_backward runs as for moe_route.  No host synchronisation: the
+ * rounds are a fixed count of launches.
+ *   n_iter    rounds, 1 .. 1000 (MOE_ERR_INVALID otherwise)
+ *   col_scale [E] f32 out: b after the last round
+ *   ws        the plan's workspace (moe_workspace_bytes); E <= 256
+ *   other arguments as for moe_route. */
+moe_status moe_route_sinkhorn(moe_plan plan, const void* x, const void* w_router, const float* bias,
+                              int32_t n_iter, float* probs, int32_t* topk_idx, float* topk_w, float* col_scale,
+                              void* ws, size_t ws_bytes, void* stream);
+
 /* The step-end update of the selection bias (same reading as above):
  * sel_bias[e] += gamma * sign(T k - E counts[e]), i.e. a fixed step down for
  * experts above the mean load T k / E and up for those below; the sign is

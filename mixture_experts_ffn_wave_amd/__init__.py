@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     lib,
     moe_route,
     moe_route_balanced,
+    moe_route_sinkhorn,
     moe_balance_update,
     moe_permute,
     moe_expert_ffn,

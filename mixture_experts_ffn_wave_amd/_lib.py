@@ -64,6 +64,7 @@ SIGNATURES = {
     "moe_version": (ctypes.c_char_p, []),
     "moe_route": (c_int32, [c_void_p] * 8),
     "moe_route_balanced": (c_int32, [c_void_p] * 9),
+    "moe_route_sinkhorn": (c_int32, [c_void_p] * 4 + [c_int32] + [c_void_p] * 5 + [c_size_t, c_void_p]),
     "moe_balance_update": (c_int32, [c_void_p, c_void_p, c_void_p, c_float, c_void_p]),
     "moe_permute": (c_int32, [c_void_p] * 9 + [c_size_t, c_void_p]),
     "moe_permute_noalloc": (c_int32, [c_void_p] * 9),
@@ -214,6 +215,20 @@ def moe_route_balanced(plan, x, w_router, bias, sel_bias, probs, topk_idx, topk_
     st = lib().moe_route_balanced(plan.handle, _ptr(x), _ptr(w_router), _ptr(bias) if plan.has_bias else None,
                                   _ptr(sel_bias), _ptr(probs), _ptr(topk_idx), _ptr(topk_w), _stream(stream))
     _check("moe_route_balanced", st)
+
+
+def moe_route_sinkhorn(plan, x, w_router, bias, n_iter, probs, topk_idx, topk_w, col_scale, ws, stream=None):
+    T, d, E, k, dt = plan.T, plan.d, plan.E, plan.k, plan.dtype
+    _need(x, "x", (T, d), dt); _need(w_router, "w_router", (E, d), dt)
+    _need(probs, "probs", (T, E), torch.float32)
+    _need(topk_idx, "topk_idx", (T, k), torch.int32); _need(topk_w, "topk_w", (T, k), torch.float32)
+    _need(col_scale, "col_scale", (E,), torch.float32)
+    if plan.has_bias:
+        _need(bias, "bias", (E,), torch.float32)
+    st = lib().moe_route_sinkhorn(plan.handle, _ptr(x), _ptr(w_router), _ptr(bias) if plan.has_bias else None,
+                                  int(n_iter), _ptr(probs), _ptr(topk_idx), _ptr(topk_w), _ptr(col_scale),
+                                  _ptr(ws), ws.numel(), _stream(stream))
+    _check("moe_route_sinkhorn", st)
 
 
 def moe_balance_update(plan, counts, sel_bias, gamma, stream=None):

@@ -28,7 +28,7 @@ const char* kKernelNames =
     "gemm_down_dgrad_swiglu,gemm_wgrad_down,gemm_gate_up_dgrad,gemm_wgrad_gate_up,"
     "gemm_down_dgrad_swiglu_shared,gemm_wgrad_down_shared,gemm_wgrad_gate_up_shared,"
     "gemm_gate_up_dgrad_shared,stack_router,gemm_router_dx,unpermute,gemm_wgrad_router,router_reduce,aux,"
-    "wgrad_reduce,mx_quantize,router_bwd_small,balance_update";
+    "wgrad_reduce,mx_quantize,router_bwd_small,balance_update,sinkhorn_rows,sinkhorn_cols,sinkhorn_select";
 
 }  // namespace
 
@@ -46,7 +46,7 @@ struct moe_plan_s {
   // workspace regions (byte offsets)
   size_t o_block_counts, o_block_base, o_dy_perm, o_g, o_dzhl, o_w2, o_dgu, o_dx_perm, o_dgu_s,
       o_dxs, o_dxr, o_dwr_part, o_dbias_part, o_aux_part, o_wg_part, o_wsorted, o_gpart, o_wh, o_dgu_lo,
-      o_wh_lo, ws_total;
+      o_wh_lo, o_sk_part, ws_total;
   // bf16 experts seeing few tokens each: the expert weight gradients add the
   // products of the rounding remainders of [dG | dU] and of w H (see run_wgrad)
   bool comp = false;
@@ -125,6 +125,8 @@ constexpr int kCUs = 256;
 // mean rows per expert below which a bf16 plan adds the remainder terms to
 // the expert weight gradients (moe_plan_s::comp)
 constexpr int kCompTokens = 128;
+// largest number of Sinkhorn rounds one moe_route_sinkhorn call accepts
+constexpr int kSinkhornMaxIters = 1000;
 
 // Tile override for tuning and tests: MOE_ROW_TILE = 128, 256, 128x256 or
 // 256pp, MOE_WGRAD_TILE = 128, 256 or 256pp, read once per plan; any other
@@ -413,6 +415,8 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
     if (v && p->dt == DT_BF16 && !p->mx) p->comp = std::atoi(v) != 0;
   }
   p->o_dgu_lo = take(p->comp ? (size_t)A * 2 * p->I * es : 0);
+  // Sinkhorn router: column partials of its token blocks
+  p->o_sk_part = take((size_t)((p->T + kSinkhornTokens - 1) / kSinkhornTokens) * p->E * 4);
   p->o_wh_lo = take(p->comp ? (size_t)A * p->I * es : 0);
   // input-gradient rows of the experts, f32 in a bf16 layer (f32_intermediates)
   const size_t xs = f32_intermediates(p->dt, p->mx) ? 4 : es;
@@ -598,6 +602,38 @@ moe_status moe_route_balanced(moe_plan p, const void* x, const void* w_router, c
               p->T, p->d, p->E, p->k, p->cfg.renorm, sel_bias};
   Probe pr(p, "route", s);
   return hip_status(launch_route(p->dt, a, s));
+}
+
+moe_status moe_route_sinkhorn(moe_plan p, const void* x, const void* w_router, const float* bias, int32_t n_iter,
+                              float* probs, int32_t* topk_idx, float* topk_w, float* col_scale, void* ws,
+                              size_t ws_bytes, void* stream) {
+  if (!p) return MOE_ERR_NULL;
+  if (n_iter < 1 || n_iter > kSinkhornMaxIters) return MOE_ERR_INVALID;
+  if (p->T == 0) return MOE_OK;
+  if (!x || !w_router || !probs || !topk_idx || !topk_w || !col_scale) return MOE_ERR_NULL;
+  if (p->cfg.has_router_bias && !bias) return MOE_ERR_NULL;
+  moe_status st = check_ws(p, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  {
+    // the probabilities (the plain router's choice is overwritten below)
+    RouteArgs a{x, w_router, p->cfg.has_router_bias ? bias : nullptr, probs, topk_idx, topk_w,
+                p->T, p->d, p->E, p->k, p->cfg.renorm};
+    Probe pr(p, "route", s);
+    MOE_TRY(launch_route(p->dt, a, s));
+  }
+  SinkhornArgs a{probs, col_scale, reinterpret_cast<float*>(wsp(ws, p->o_sk_part)), topk_idx, topk_w,
+                 p->T, p->E, p->k, p->cfg.renorm};
+  for (int it = 0; it < n_iter; ++it) {
+    {
+      Probe pr(p, "sinkhorn_rows", s);
+      MOE_TRY(launch_sinkhorn_rows(a, it == 0, s));
+    }
+    Probe pr(p, "sinkhorn_cols", s);
+    MOE_TRY(launch_sinkhorn_cols(a, s));
+  }
+  Probe pr(p, "sinkhorn_select", s);
+  return hip_status(launch_sinkhorn_select(a, s));
 }
 
 moe_status moe_balance_update(moe_plan p, const int32_t* counts, float* sel_bias, float gamma, void* stream) {

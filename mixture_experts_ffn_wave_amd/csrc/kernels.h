@@ -25,6 +25,23 @@ struct RouteArgs {
   const float* sel_bias = nullptr;  // [E] or nullptr: experts chosen on probs + sel_bias (weights unbiased)
 };
 hipError_t launch_route(int dt, const RouteArgs& a, hipStream_t s);
+
+// Sinkhorn router over the saved probabilities [T, E] (E <= 256): rounds of
+// a_t = (1/T) / sum_e p_te b_e and b_e = (1/E) / sum_t p_te a_t (column sums
+// from per-block partials in block order), then top-k of p_te b_e per token.
+constexpr int kSinkhornTokens = 32;   // tokens per workgroup
+struct SinkhornArgs {
+  const float* probs;   // [T, E]
+  float* b;             // [E] column scales (out; read by later rounds)
+  float* part;          // [ceil(T / kSinkhornTokens), E] column partials (workspace)
+  int32_t* idx;         // [T, k] out (select)
+  float* wts;           // [T, k] out (select)
+  int64_t T;
+  int E, k, renorm;
+};
+hipError_t launch_sinkhorn_rows(const SinkhornArgs& a, bool first, hipStream_t s);
+hipError_t launch_sinkhorn_cols(const SinkhornArgs& a, hipStream_t s);
+hipError_t launch_sinkhorn_select(const SinkhornArgs& a, hipStream_t s);
 // sel_bias[e] += gamma * sign(T k - E counts[e]) (aux-loss-free balancing update), E <= 256
 hipError_t launch_balance_update(const int32_t* counts, float* sel_bias, int64_t T, int E, int k, float gamma,
                                  hipStream_t s);

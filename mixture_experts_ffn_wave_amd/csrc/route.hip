@@ -635,12 +635,142 @@ __global__ void __launch_bounds__(256) balance_update_kernel(const int32_t* coun
   sel_bias[e] = sel_bias[e] + gamma * sgn;
 }
 
+// ---- Sinkhorn router (KohakUwULLM README, "Key features": Sinkhorn routers
+// beside the default; the published Sinkhorn-Knopp balancing of the batch's
+// probability matrix).  The probabilities come from the plain router pass.
+constexpr int SKT = kSinkhornTokens;
+constexpr int SK_EMAX = 256;
+
+// One block of 32 tokens of one round: a_t = (1/T) / sum_e p_te b_e (b = 1
+// in the first round; eight lanes per token, each summing every eighth
+// expert, then a fixed butterfly), and the block's column partials
+// sum_t p_te a_t over its tokens in order.
+__global__ void __launch_bounds__(256) sinkhorn_rows_kernel(SinkhornArgs a, int first) {
+  __shared__ float s_p[SKT * (SK_EMAX + 1)];
+  __shared__ float s_b[SK_EMAX], s_a[SKT];
+  const int tid = threadIdx.x, E = a.E, ld = E + 1;
+  const int64_t t0 = (int64_t)blockIdx.x * SKT;
+  const int nt = (a.T - t0) < SKT ? (int)(a.T - t0) : SKT;
+  for (int e = tid; e < E; e += 256) s_b[e] = first ? 1.0f : a.b[e];
+  for (int i = tid; i < nt * E; i += 256) {
+    const int t = i / E, e = i - t * E;
+    s_p[t * ld + e] = a.probs[(t0 + t) * E + e];
+  }
+  __syncthreads();
+  {
+    const int t = tid >> 3, g = tid & 7;
+    float sum = 0.0f;
+    if (t < nt)
+      for (int e = g; e < E; e += 8) sum = fmaf(s_p[t * ld + e], s_b[e], sum);
+    sum += __shfl_xor(sum, 1, 64);
+    sum += __shfl_xor(sum, 2, 64);
+    sum += __shfl_xor(sum, 4, 64);
+    if (g == 0 && t < nt) s_a[t] = 1.0f / ((float)a.T * sum);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {
+    float c = 0.0f;
+    for (int t = 0; t < nt; ++t) c = fmaf(s_p[t * ld + e], s_a[t], c);
+    a.part[(int64_t)blockIdx.x * E + e] = c;
+  }
+}
+
+// b_e = (1/E) / (sum over blocks of the column partials, in block order).
+__global__ void __launch_bounds__(256) sinkhorn_cols_kernel(SinkhornArgs a) {
+  const int64_t nblk = (a.T + SKT - 1) / SKT;
+  for (int e = threadIdx.x; e < a.E; e += 256) {
+    float c = 0.0f;
+    for (int64_t b = 0; b < nblk; ++b) c += a.part[b * a.E + e];
+    a.b[e] = 1.0f / ((float)a.E * c);
+  }
+}
+
+// Top-k of p_te b_e per token (k rounds: largest remaining score, lower
+// expert index on ties, slots in that order); weights = the chosen p_te,
+// divided by their sum (in slot order) when renormalising.  Eight lanes per
+// token, lane g owning experts g, g + 8, ...; rounds are butterflies over
+// the eight lanes.
+__global__ void __launch_bounds__(256) sinkhorn_select_kernel(SinkhornArgs a) {
+  constexpr int EPL = SK_EMAX / 8;
+  __shared__ float s_b[SK_EMAX];
+  const int tid = threadIdx.x, E = a.E;
+  for (int e = tid; e < E; e += 256) s_b[e] = a.b[e];
+  __syncthreads();
+  const int t_l = tid >> 3, g = tid & 7;
+  const int64_t t = (int64_t)blockIdx.x * SKT + t_l;
+  const bool tv = t < a.T;
+  float p[EPL], v[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = g + 8 * i;
+    const bool ok = tv && e < E;
+    p[i] = ok ? a.probs[t * E + e] : 0.0f;
+    v[i] = ok ? p[i] * s_b[e] : -INFINITY;
+  }
+  uint32_t taken = 0u;
+  float psum = 0.0f;
+  for (int j = 0; j < a.k; ++j) {
+    float bv = -INFINITY, bp = 0.0f;
+    int be = -1;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = g + 8 * i;
+      if (e < E && !((taken >> i) & 1u) && (be < 0 || v[i] > bv)) {
+        bv = v[i];
+        bp = p[i];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      const float ov = __shfl_xor(bv, o, 64), op = __shfl_xor(bp, o, 64);
+      const int oe = __shfl_xor(be, o, 64);
+      if (be < 0 || (oe >= 0 && (ov > bv || (ov == bv && oe < be)))) {
+        bv = ov;
+        bp = op;
+        be = oe;
+      }
+    }
+    if (be >= 0 && (be & 7) == g) taken |= 1u << (be >> 3);
+    psum += bp;
+    if (tv && g == 0) {
+      a.idx[t * a.k + j] = be;
+      a.wts[t * a.k + j] = bp;                     // divided by the sum below when renormalising
+    }
+  }
+  if (a.renorm && tv && g == 0)
+    for (int j = 0; j < a.k; ++j) a.wts[t * a.k + j] = a.wts[t * a.k + j] / psum;
+}
+
 }  // namespace
 
 hipError_t launch_balance_update(const int32_t* counts, float* sel_bias, int64_t T, int E, int k, float gamma,
                                  hipStream_t s) {
   if (E < 1 || E > 256) return hipErrorInvalidValue;
   hipLaunchKernelGGL(balance_update_kernel, dim3(1), dim3(256), 0, s, counts, sel_bias, T, E, k, gamma);
+  return hipGetLastError();
+}
+
+hipError_t launch_sinkhorn_rows(const SinkhornArgs& a, bool first, hipStream_t s) {
+  const int64_t grid = (a.T + SKT - 1) / SKT;
+  if (grid == 0) return hipSuccess;
+  if (a.E < 1 || a.E > SK_EMAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sinkhorn_rows_kernel, dim3((unsigned)grid), dim3(256), 0, s, a, first ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_sinkhorn_cols(const SinkhornArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  if (a.E < 1 || a.E > SK_EMAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sinkhorn_cols_kernel, dim3(1), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sinkhorn_select(const SinkhornArgs& a, hipStream_t s) {
+  const int64_t grid = (a.T + SKT - 1) / SKT;
+  if (grid == 0) return hipSuccess;
+  if (a.E < 1 || a.E > SK_EMAX || a.k < 1 || a.k > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sinkhorn_select_kernel, dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -60,6 +60,8 @@ class MoELayer:
         self.params = None
         self.sel_bias = None      # aux-loss-free balancing: set by enable_balancing()
         self.balance_gamma = 0.0
+        self.sinkhorn_iters = 0   # Sinkhorn router: set by enable_sinkhorn()
+        self.sinkhorn_b = None
         self.real_mask = None     # statistic over real tokens only: set by set_real_mask()
         self.real_counts = None
 
@@ -86,6 +88,12 @@ class MoELayer:
                                                                           device=self.probs.device)
         self.balance_gamma = float(gamma)
 
+    def enable_sinkhorn(self, n_iter):
+        """Route with the Sinkhorn router (n_iter balancing rounds); the
+        column scales of the last route call land in self.sinkhorn_b."""
+        self.sinkhorn_iters = int(n_iter)
+        self.sinkhorn_b = torch.empty(self.plan.E, dtype=torch.float32, device=self.probs.device)
+
     def update_balance(self, gamma, stream=None):
         """Step-end update of the selection bias from this step's counts."""
         L.moe_balance_update(self.plan, self.counts, self.sel_bias, gamma, stream)
@@ -97,7 +105,10 @@ class MoELayer:
 
     def route(self, stream=None):
         q = self.params
-        if self.sel_bias is not None:
+        if self.sinkhorn_iters > 0:
+            L.moe_route_sinkhorn(self.plan, q["x"], q["w_router"], q["bias"], self.sinkhorn_iters, self.probs,
+                                 self.topk_idx, self.topk_w, self.sinkhorn_b, self.ws, stream)
+        elif self.sel_bias is not None:
             L.moe_route_balanced(self.plan, q["x"], q["w_router"], q["bias"], self.sel_bias, self.probs,
                                  self.topk_idx, self.topk_w, stream)
         else:

@@ -34,6 +34,10 @@ import oracle as O
 
 TIE_EPS = 1e-5
 PROB_ATOL = 1e-6
+# Sinkhorn router: ties are judged on ln(p_te b_e); the GPU's column scales
+# carry f32 rounding of T-term sums over several rounds (measured under 5e-7 relative)
+SINKHORN_TIE_EPS = 5e-5
+SINKHORN_B_RTOL = 1e-5
 
 
 def say(msg):
@@ -90,7 +94,7 @@ def to_np(t):
     return t.to(torch.float64).numpy()
 
 
-def gpu_run(wl, inp, routing=None, intermediates=False, sel_bias=None, mask=None, extra=()):
+def gpu_run(wl, inp, routing=None, intermediates=False, sel_bias=None, mask=None, extra=(), sinkhorn=None):
     """One fwd+bwd step on cuda:0.  ``routing`` (probs, idx, w as numpy) replaces
     the router's outputs when given (then moe_route is not called).
     ``intermediates`` also returns what the backward left in the workspace
@@ -98,7 +102,8 @@ def gpu_run(wl, inp, routing=None, intermediates=False, sel_bias=None, mask=None
     ``sel_bias`` (numpy [E]) routes with aux-loss-free balancing; ``mask``
     (numpy [T], 0 = filler) takes the balancing statistic over real tokens.
     ``extra`` names further workspace intermediates to return ("wh",
-    "dgu_lo", "wh_lo")."""
+    "dgu_lo", "wh_lo").  ``sinkhorn`` (rounds) routes with the Sinkhorn
+    router."""
     from mixture_experts_ffn_wave_amd import MoELayer, decode_aux
     b = inp.get("bias")
     plan = plan_for(wl, b is not None)
@@ -110,6 +115,8 @@ def gpu_run(wl, inp, routing=None, intermediates=False, sel_bias=None, mask=None
                      ws_gate_up=dev.get("ws_gate_up"), ws_down=dev.get("ws_down"))
     if sel_bias is not None:
         layer.enable_balancing(torch.from_numpy(np.asarray(sel_bias, dtype=np.float32)).cuda())
+    if sinkhorn is not None:
+        layer.enable_sinkhorn(sinkhorn)
     if mask is not None:
         layer.set_real_mask(torch.from_numpy(np.asarray(mask, dtype=np.int32)).cuda())
     if routing is None:
@@ -132,6 +139,8 @@ def gpu_run(wl, inp, routing=None, intermediates=False, sel_bias=None, mask=None
     for n, t in layer.grads.items():
         out[n] = to_np(t)
     out["aux"] = decode_aux(layer.aux_out)
+    if sinkhorn is not None and routing is None:
+        out["sinkhorn_b"] = to_np(layer.sinkhorn_b)
     if mask is not None:
         out["real_counts"] = to_np(layer.real_counts)
     if intermediates:
@@ -150,12 +159,13 @@ def storage_rounding(wl):
     return lambda a, kind: O.round_to_format(a, "f32" if kind == "f32" else wl.dtype)
 
 
-def oracle_run(wl, f64, store=None, quant=None, sel_bias=None, mask=None):
+def oracle_run(wl, f64, store=None, quant=None, sel_bias=None, mask=None, sinkhorn=None):
     b = f64.get("bias")
     fwd = O.layer_forward(f64["x"], f64["w_router"], f64["w_gate_up"], f64["w_down"], top_k=wl.k,
                           renorm=wl.renorm, bias=b, ws_gate_up=f64.get("ws_gate_up"),
                           ws_down=f64.get("ws_down"), store=store, quant=quant,
-                          sel_bias=None if sel_bias is None else np.asarray(sel_bias, dtype=np.float64))
+                          sel_bias=None if sel_bias is None else np.asarray(sel_bias, dtype=np.float64),
+                          sinkhorn_iters=sinkhorn)
     bwd = O.layer_backward(fwd, f64["dy"], aux_coef=wl.aux_coef, quant=quant, mask=mask)
     if mask is None:
         st = O.aux_statistics(fwd["p"], fwd["counts"], wl.k)
@@ -208,22 +218,32 @@ def compare_routing(wl, gpu, fwd):
     """Returns True when the GPU chose exactly the oracle's routing for every
     token; asserts that any difference is an allowed near-tie.  The ranked
     values are the logits, or probability + selection bias when balancing."""
-    z = fwd["z"] if fwd.get("sel_bias") is None else O.balanced_selection_scores(fwd["p"], fwd["sel_bias"])
+    eps = TIE_EPS
+    if fwd.get("sinkhorn_b") is not None:
+        # Sinkhorn router: scales first, then ranks on ln(p b)
+        if "sinkhorn_b" in gpu:
+            b_ref = fwd["sinkhorn_b"]
+            rel = np.max(np.abs(gpu["sinkhorn_b"] - b_ref) / np.abs(b_ref))
+            assert rel <= SINKHORN_B_RTOL, f"Sinkhorn column scales: max relative error {rel:.3e}"
+        z = np.log(O.sinkhorn_selection_scores(fwd["p"], fwd["sinkhorn_b"]))
+        eps = SINKHORN_TIE_EPS
+    else:
+        z = fwd["z"] if fwd.get("sel_bias") is None else O.balanced_selection_scores(fwd["p"], fwd["sel_bias"])
     k, E = wl.k, wl.E
     assert np.max(np.abs(gpu["probs"] - fwd["p"])) <= PROB_ATOL, "router probabilities"
     gi = gpu["topk_idx"]
     same = np.all(gi == fwd["idx"], axis=1)
-    set_tie, order_tie = O.near_tie_tokens(z, k, TIE_EPS)
+    set_tie, order_tie = O.near_tie_tokens(z, k, eps)
     bad = ~same & ~(set_tie | order_tie)
     assert not bad.any(), f"routing differs on {int(bad.sum())} non-tied tokens, e.g. {np.where(bad)[0][:5]}"
     for t in np.where(~same)[0]:
         sel = gi[t]
         assert len(set(sel.tolist())) == k and sel.min() >= 0 and sel.max() < E
         zs = z[t, sel]
-        assert np.all(np.diff(zs) <= TIE_EPS), f"token {t}: slot order not descending"
+        assert np.all(np.diff(zs) <= eps), f"token {t}: slot order not descending"
         rest = np.setdiff1d(np.arange(E), sel)
         if rest.size:
-            assert zs.min() >= z[t, rest].max() - TIE_EPS, f"token {t}: not a top-k"
+            assert zs.min() >= z[t, rest].max() - eps, f"token {t}: not a top-k"
     if same.any():
         assert np.max(np.abs(gpu["topk_w"][same] - fwd["w"][same])) <= PROB_ATOL, "routing weights"
     return bool(same.all())
@@ -449,7 +469,7 @@ def _diagnostic(fn):
         STRICT[0] = True
 
 
-def full_parity(wl, inp=None, mx_diagnostic=True, sel_bias=None, mask=None):
+def full_parity(wl, inp=None, mx_diagnostic=True, sel_bias=None, mask=None, sinkhorn=None):
     """The whole chain on the GPU against the oracle.  When a near-tie made
     the GPU pick a different (valid) routing, the downstream calls are run a
     second time from the oracle's routing so every later tensor is compared
@@ -471,10 +491,11 @@ def full_parity(wl, inp=None, mx_diagnostic=True, sel_bias=None, mask=None):
     f64 = oracle_inputs(inp)
     say(f"[parity] {wl.name}: {MI.describe(wl)} -- GPU chain")
     mx = wl.expert_dtype == "mxfp8"
-    gpu = gpu_run(wl, inp, intermediates=mx, sel_bias=sel_bias, mask=mask)
+    gpu = gpu_run(wl, inp, intermediates=mx, sel_bias=sel_bias, mask=mask, sinkhorn=sinkhorn)
     say(f"[parity] {wl.name}: oracle" + (" (MX-quantised expert GEMM operands, bf16 storage)" if mx else " (exact)"))
     fwd, bwd, st = oracle_run(wl, f64, storage_rounding(wl) if mx else None,
-                              quant=O.mx_fake_quant if mx else None, sel_bias=sel_bias, mask=mask)
+                              quant=O.mx_fake_quant if mx else None, sel_bias=sel_bias, mask=mask,
+                              sinkhorn=sinkhorn)
     identical = compare_routing(wl, gpu, fwd)
     if not identical:
         say(f"[parity] {wl.name}: near-tie routing differs; rerunning downstream from the oracle routing")
@@ -495,7 +516,8 @@ def full_parity(wl, inp=None, mx_diagnostic=True, sel_bias=None, mask=None):
         compare_downstream(wl, gpu, fwd, bwd, st)
         _report(wl, "vs exact oracle")
         if wl.dtype == "bf16" and mx_diagnostic:
-            rf, rb, rs = oracle_run(wl, f64, storage_rounding(wl), sel_bias=sel_bias, mask=mask)
+            rf, rb, rs = oracle_run(wl, f64, storage_rounding(wl), sel_bias=sel_bias, mask=mask,
+                                    sinkhorn=sinkhorn)
             _diagnostic(lambda: compare_downstream(wl, gpu, rf, rb, rs, rounded=True))
             _report(wl, "vs storage-rounded oracle, not asserted")
     return gpu, fwd, bwd, st

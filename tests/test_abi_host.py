@@ -303,3 +303,19 @@ def test_permute_noalloc_refuses_plans_beyond_its_fixed_scratch():
     assert lib.moe_permute_noalloc(big.handle, None, fake, fake, fake, fake, fake, None, None) == MOE_ERR_NULL
     assert lib.moe_permute_noalloc(None, fake, fake, fake, fake, fake, fake, None, None) == MOE_ERR_NULL
     assert b"scratch" in lib.moe_status_string(L.MOE_ERR_SCRATCH)
+
+
+def test_route_sinkhorn_validates_before_any_launch():
+    """moe_route_sinkhorn: rounds outside 1 .. 1000 are refused, T = 0 is a
+    no-op, and missing pointers or workspace are reported, all on the host."""
+    lib = L.lib()
+    fake = ctypes.c_void_p(0x1000)
+    p = L.Plan(512, 128, 8, 2, 128, dtype=L.torch.bfloat16)
+    wsb = p.workspace_bytes()
+    args = lambda n, cs=fake, ws=fake, nb=wsb: (p.handle, fake, fake, None, n, fake, fake, fake, cs, ws, nb, None)
+    assert lib.moe_route_sinkhorn(*args(0)) == MOE_ERR_INVALID
+    assert lib.moe_route_sinkhorn(*args(1001)) == MOE_ERR_INVALID
+    assert lib.moe_route_sinkhorn(*args(8, cs=None)) == MOE_ERR_NULL
+    assert lib.moe_route_sinkhorn(*args(8, nb=wsb - 1)) == MOE_ERR_WORKSPACE
+    empty = L.Plan(0, 128, 8, 2, 128, dtype=L.torch.bfloat16)
+    assert lib.moe_route_sinkhorn(empty.handle, None, None, None, 4, None, None, None, None, None, 0, None) == MOE_OK
