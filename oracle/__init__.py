@@ -24,6 +24,9 @@ from .moe_oracle import (  # noqa: F401
     balanced_selection_scores,
     sinkhorn_column_scales,
     sinkhorn_selection_scores,
+    relu_gates,
+    relu_select,
+    relu_gate_weights,
     balance_bias_update,
     near_tie_tokens,
     expert_permutation,

@@ -123,6 +123,33 @@ def sinkhorn_selection_scores(p, b):
     return np.asarray(p, dtype=np.float64) * np.asarray(b, dtype=np.float64)[None, :]
 
 
+def relu_gates(z):
+    """Gates of the ReLU router: g_te = max(z_te, 0), no softmax.  KohakUwULLM
+    README, "Key features", names ReLU routers and gives no rule; the reading
+    taken is the published ReLU routing (ReMoE): a token uses every expert
+    whose gate is positive, weighted by the gate itself, and the gates take
+    the place of the probabilities everywhere else, so the layer's balancing
+    statistic E sum_e f_e mean_t g_te is the published load-balanced L1 term
+    on the gates.  Here at most ``top_k`` experts per token (relu_select)."""
+    return np.maximum(np.asarray(z, dtype=np.float64), 0.0)
+
+
+def relu_select(z, k):
+    """The ReLU router's choice: the token's k largest logits that are
+    positive (descending, lower index first on equal logits); slots past the
+    token's positive logits hold -1 (no expert)."""
+    idx = topk_select(z, k)
+    zs = np.take_along_axis(z, idx, axis=1)
+    return np.where(zs > 0, idx, -1)
+
+
+def relu_gate_weights(g, idx):
+    """Weights of the ReLU router's slots: the gate of the chosen expert, 0
+    for an empty slot (no renormalisation)."""
+    sel = np.take_along_axis(g, np.maximum(idx, 0), axis=1)
+    return np.where(idx >= 0, sel, 0.0)
+
+
 def balance_bias_update(sel_bias, counts, T, top_k, gamma):
     """One update of the selection bias after a step: b_e += gamma * sign(mean
     load - count_e), mean load = T k / E, so overloaded experts lose and
@@ -169,16 +196,20 @@ def expert_permutation(idx, n_experts):
     perm_token[r]  token of the r-th row of the expert-sorted order, the order
                    being (expert ascending, token ascending)
     inv[t, j]      row r at which assignment (t, j) sits in that order
+    A slot holding -1 (no expert: the ReLU router) is no assignment: it gets
+    no row and inv -1, and perm_token covers the offsets[E] real rows.
     """
     T, k = idx.shape
     flat = idx.reshape(-1)
-    counts = np.bincount(flat, minlength=n_experts).astype(np.int64)
+    real = flat >= 0
+    counts = np.bincount(flat[real], minlength=n_experts).astype(np.int64)
     offsets = np.zeros(n_experts + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(counts)
-    order = np.argsort(flat, kind="stable")          # flat position f = t*k + j
+    pos = np.nonzero(real)[0]                        # flat positions f = t*k + j of real slots
+    order = pos[np.argsort(flat[real], kind="stable")]
     perm_token = (order // k).astype(np.int64)
-    inv = np.empty(T * k, dtype=np.int64)
-    inv[order] = np.arange(T * k, dtype=np.int64)
+    inv = np.full(T * k, -1, dtype=np.int64)
+    inv[order] = np.arange(order.size, dtype=np.int64)
     return counts, offsets, perm_token, inv.reshape(T, k)
 
 
@@ -220,8 +251,10 @@ def shared_experts_forward(x, ws_gate_up, ws_down):
 
 
 def combine(y_perm, inv, w, y_shared=None):
-    """y_t = sum_j w_tj * Y_perm[inv[t, j]] (+ shared output)."""
-    y = np.einsum("tj,tjd->td", w, y_perm[inv])
+    """y_t = sum_j w_tj * Y_perm[inv[t, j]] (+ shared output); slots with
+    inv -1 (no expert) add nothing."""
+    rows = np.where((inv >= 0)[:, :, None], y_perm[np.maximum(inv, 0)], 0.0)
+    y = np.einsum("tj,tjd->td", w, rows)
     if y_shared is not None:
         y = y + y_shared
     return y
@@ -233,8 +266,8 @@ def real_token_counts(idx, mask, n_experts):
     """Assignments per expert among the real tokens (mask 1) only, and the
     number of real tokens."""
     m = np.asarray(mask, dtype=np.int64)
-    sel = idx[m != 0]
-    return np.bincount(sel.ravel(), minlength=n_experts).astype(np.int64), int(m.sum())
+    sel = idx[m != 0].ravel()
+    return np.bincount(sel[sel >= 0], minlength=n_experts).astype(np.int64), int(m.sum())
 
 
 def aux_statistics(p, counts, top_k, mask=None):
@@ -311,7 +344,7 @@ def expert_down_step(h, w_down_e, quant=None):
 
 def layer_forward(x, w_router, w_gate_up, w_down, *, top_k, renorm=True, bias=None,
                   ws_gate_up=None, ws_down=None, quant=None, store=None, sel_bias=None,
-                  sinkhorn_iters=None):
+                  sinkhorn_iters=None, router="softmax"):
     """Full forward pass.  Returns a dict of every intermediate.
 
     ``sel_bias`` (aux-loss-free balancing) moves the choice of experts to
@@ -319,6 +352,9 @@ def layer_forward(x, w_router, w_gate_up, w_down, *, top_k, renorm=True, bias=No
     probabilities of the chosen experts.  ``sinkhorn_iters`` (the Sinkhorn
     router) moves it to sinkhorn_selection_scores(p, b) with b =
     sinkhorn_column_scales(p, sinkhorn_iters), returned as "sinkhorn_b".
+    ``router="relu"`` (the ReLU router) replaces the probabilities by the
+    gates relu_gates(z) (returned as "p"), the choice by relu_select and the
+    weights by relu_gate_weights (no renormalisation: renorm must be False).
 
     ``quant``, if given, is applied to each operand of each expert GEMM as
     quant(array, axis) with ``axis`` the contraction axis of that GEMM (the MX
@@ -337,18 +373,23 @@ def layer_forward(x, w_router, w_gate_up, w_down, *, top_k, renorm=True, bias=No
     T, d = x.shape
     E = w_router.shape[0]
     z = router_logits(x, w_router, bias)
-    p = softmax_rows(z)
+    relu = router == "relu"
+    if relu:
+        assert not renorm and sel_bias is None and sinkhorn_iters is None, "the ReLU router does not renormalise"
+    p = relu_gates(z) if relu else softmax_rows(z)
     sk_b = None
-    if sinkhorn_iters is not None:
+    if relu:
+        idx = relu_select(z, top_k)
+    elif sinkhorn_iters is not None:
         sk_b = sinkhorn_column_scales(p, sinkhorn_iters) if T > 0 else np.ones(E)
         idx = topk_select(sinkhorn_selection_scores(p, sk_b), top_k)
     else:
         idx = topk_select(z if sel_bias is None else balanced_selection_scores(p, sel_bias), top_k)
-    w = gate_weights(p, idx, renorm)
+    w = relu_gate_weights(p, idx) if relu else gate_weights(p, idx, renorm)
     counts, offsets, perm_token, inv = expert_permutation(idx, E)
     x_perm = x[perm_token]
     inter = w_down.shape[2]
-    A = T * top_k
+    A = int(offsets[-1])                            # real rows (T k unless slots are empty)
     g = np.zeros((A, inter)); u = np.zeros((A, inter)); h = np.zeros((A, inter))
     y_perm = np.zeros((A, d))
     for e in range(E):
@@ -372,7 +413,7 @@ def layer_forward(x, w_router, w_gate_up, w_down, *, top_k, renorm=True, bias=No
                 y_perm=y_perm, y_shared=y_shared, shared=shared, y=y,
                 x=x, w_router=w_router, w_gate_up=w_gate_up, w_down=w_down,
                 ws_gate_up=ws_gate_up, ws_down=ws_down, top_k=top_k,
-                renorm=renorm, bias=bias, store=store, sel_bias=sel_bias, sinkhorn_b=sk_b)
+                renorm=renorm, bias=bias, store=store, sel_bias=sel_bias, sinkhorn_b=sk_b, router=router)
 
 
 def expert_down_backward_step(dy_rows, g, u, h, w_down_e, quant=None, store=None):
@@ -398,7 +439,8 @@ def expert_gate_up_backward_step(dgu, rows, w_gate_up_e, quant=None):
     return q(dgu, 1) @ q(w_gate_up_e, 0), q(dgu, 0).T @ q(rows, 0)
 
 
-def router_backward(dy, y_perm, inv, p, idx, w, renorm, counts, aux_coef=0.0, store=None, mask=None):
+def router_backward(dy, y_perm, inv, p, idx, w, renorm, counts, aux_coef=0.0, store=None, mask=None,
+                    router="softmax"):
     """Gradient of L = <dy, y> + aux_coef * aux with respect to the router
     logits, given the expert output rows Y_perm the combine weighted.
 
@@ -409,11 +451,31 @@ def router_backward(dy, y_perm, inv, p, idx, w, renorm, counts, aux_coef=0.0, st
     With ``mask`` the statistic covers the real tokens only (aux_statistics):
     ``counts`` are theirs, T is their number, and only real tokens' p_te get
     the balancing term.
+    ``router="relu"``: ``p`` holds the gates max(z, 0), which are the weights
+    themselves, so dL/dg of a slot is g_tj, the balancing term is added the
+    same way, and dz = dp where z > 0 (g > 0), 0 elsewhere; slots with idx -1
+    carry nothing.
     Returns (g [T, k], dz [T, E] as stored, kind "f32")."""
     st = store or _no_store
     T, E = p.shape
     k = idx.shape[1]
-    gsc = np.einsum("td,tjd->tj", dy, y_perm[inv])
+    real = inv >= 0
+    gsc = np.where(real, np.einsum("td,tjd->tj", dy, y_perm[np.maximum(inv, 0)]), 0.0)
+    if router == "relu":
+        dp = np.zeros_like(p)
+        for j in range(k):
+            t = np.nonzero(idx[:, j] >= 0)[0]
+            dp[t, idx[t, j]] += gsc[t, j]
+        if aux_coef != 0.0:
+            if mask is None:
+                dp = dp + aux_coef * E * (np.asarray(counts, dtype=np.float64) / (T * k))[None, :] / T
+            else:
+                m = np.asarray(mask, dtype=np.float64)
+                Tr = float(m.sum())
+                if Tr > 0:
+                    f = np.asarray(counts, dtype=np.float64) / (Tr * k)
+                    dp = dp + m[:, None] * (aux_coef * E * f[None, :] / Tr)
+        return gsc, st(np.where(p > 0, dp, 0.0), "f32")
     p_sel = np.take_along_axis(p, idx, axis=1)
     if renorm:
         S = p_sel.sum(axis=1, keepdims=True)
@@ -459,11 +521,12 @@ def layer_backward(fwd, dy, *, aux_coef=0.0, quant=None, mask=None):
 
     # combine: y_t = sum_j w_tj Y_perm[inv_tj]  ->  dY_perm rows w_tj dy_t
     dy_perm = np.zeros_like(fwd["y_perm"])
-    dy_perm[inv.reshape(-1)] = st((w[:, :, None] * dy[:, None, :]).reshape(-1, d), "act")
+    realf = inv.reshape(-1) >= 0
+    dy_perm[inv.reshape(-1)[realf]] = st((w[:, :, None] * dy[:, None, :]).reshape(-1, d)[realf], "act")
 
     dw_gate_up = np.zeros_like(w_gate_up)
     dw_down = np.zeros_like(w_down)
-    dx_perm = np.zeros((T * k, d))
+    dx_perm = np.zeros((int(offsets[-1]), d))
     for e in range(E):
         r0, r1 = offsets[e], offsets[e + 1]
         if r1 == r0:
@@ -475,7 +538,8 @@ def layer_backward(fwd, dy, *, aux_coef=0.0, quant=None, mask=None):
 
     dx = np.zeros((T, d))
     for j in range(k):
-        dx += dx_perm[inv[:, j]]
+        t = np.nonzero(inv[:, j] >= 0)[0]
+        dx[t] += dx_perm[inv[t, j]]
 
     grads = {"dw_gate_up": dw_gate_up, "dw_down": dw_down}
     if fwd["ws_gate_up"] is not None and fwd["ws_gate_up"].shape[0] > 0:
@@ -493,7 +557,8 @@ def layer_backward(fwd, dy, *, aux_coef=0.0, quant=None, mask=None):
     # router (the balancing statistic over the real tokens when masked)
     if mask is not None:
         counts, _ = real_token_counts(idx, mask, E)
-    gsc, dz = router_backward(dy, fwd["y_perm"], inv, p, idx, w, fwd["renorm"], counts, aux_coef, st, mask)
+    gsc, dz = router_backward(dy, fwd["y_perm"], inv, p, idx, w, fwd["renorm"], counts, aux_coef, st, mask,
+                              fwd.get("router", "softmax"))
     grads["dw_router"] = dz.T @ x
     grads["dbias"] = dz.sum(axis=0)
     dx += dz @ w_r

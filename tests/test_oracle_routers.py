@@ -134,3 +134,91 @@ def test_sinkhorn_layer_gradient_matches_central_differences(renorm):
             arr[pos] = orig
             fd = (lp - lm) / (2 * h)
             assert abs(fd - g[gname][pos]) <= 1e-6 * max(1.0, abs(g[gname][pos])), (pname, pos)
+
+
+# --------------------------------------------------------------------- ReLU
+
+def _brute_relu_select(z, k):
+    out = []
+    for row in z.tolist():
+        pos = [(v, e) for e, v in enumerate(row) if v > 0]
+        pos.sort(key=lambda ve: (-ve[0], ve[1]))        # value descending, lower index on ties
+        sel = [e for _, e in pos[:k]]
+        out.append(sel + [-1] * (k - len(sel)))
+    return np.array(out)
+
+
+def test_relu_select_by_brute_force():
+    rng = np.random.default_rng(8)
+    z = np.round(rng.standard_normal((60, 7)), 1)         # ties and zeros on purpose
+    z[3] = -1.0                                           # a token with no positive logit
+    z[4] = 0.0                                            # zero is not positive
+    for k in (1, 3, 7):
+        assert np.array_equal(O.relu_select(z, k), _brute_relu_select(z, k))
+    idx = O.relu_select(z, 3)
+    w = O.relu_gate_weights(O.relu_gates(z), idx)
+    for t in range(60):
+        for j in range(3):
+            assert w[t, j] == (z[t, idx[t, j]] if idx[t, j] >= 0 else 0.0)
+    assert np.all(idx[3] == -1) and np.all(idx[4] == -1)
+
+
+def test_permutation_with_empty_slots_by_brute_force():
+    idx = np.array([[2, -1], [0, 2], [-1, -1], [2, 1], [1, -1]])
+    counts, offsets, perm, inv = O.expert_permutation(idx, 3)
+    assert counts.tolist() == [1, 2, 3] and offsets.tolist() == [0, 1, 3, 6]
+    assert perm.tolist() == [1, 3, 4, 0, 1, 3]            # expert ascending, then token ascending
+    assert inv.tolist() == [[3, -1], [0, 4], [-1, -1], [5, 1], [2, -1]]
+
+
+def test_relu_layer_with_every_expert_active_is_the_gate_weighted_sum():
+    # all logits positive and k = E: y_t = sum_e relu(z_te) SwiGLU_e(x_t)
+    L = rand_layer(T=9, d=12, E=4, k=4, inter=8, seed=11)
+    bias = np.full(4, 5.0)
+    fwd = O.layer_forward(L["x"], L["w_router"], L["w_gate_up"], L["w_down"], top_k=4, renorm=False, bias=bias,
+                          router="relu")
+    z = O.router_logits(L["x"], L["w_router"], bias)
+    assert np.all(z > 0)
+    y = np.zeros_like(L["x"])
+    for e in range(4):
+        y += z[:, e:e + 1] * O.swiglu_rows(L["x"], L["w_gate_up"][e], L["w_down"][e])[3]
+    assert np.allclose(fwd["y"], y, rtol=1e-13, atol=1e-13)
+
+
+def _relu_fwd(L, k, bias):
+    return O.layer_forward(L["x"], L["w_router"], L["w_gate_up"], L["w_down"], top_k=k, renorm=False, bias=bias,
+                           ws_gate_up=L["ws_gate_up"], ws_down=L["ws_down"], router="relu")
+
+
+@pytest.mark.parametrize("n_shared", [0, 1])
+def test_relu_layer_gradient_matches_central_differences(n_shared):
+    k, aux_coef = 2, 0.4
+    bias = np.array([0.2, -0.1, 0.0, 0.1, -0.2])
+    for sd in range(300, 600):
+        L = rand_layer(T=10, d=12, E=5, k=k, inter=8, n_shared=n_shared, inter_s=8, seed=sd, wscale=0.3)
+        z = O.router_logits(L["x"], L["w_router"], bias)
+        srt = -np.sort(-z, axis=1)
+        # away from every kink: no logit near 0, the k-th and (k+1)-th apart,
+        # and some tokens with fewer than k positive logits
+        if np.min(np.abs(z)) > 1e-3 and np.min(srt[:, k - 1] - srt[:, k]) > 1e-3 and (srt[:, k - 1] < 0).any():
+            break
+    fwd = _relu_fwd(L, k, bias)
+    assert (fwd["idx"] == -1).any()
+    g = O.layer_backward(fwd, L["dy"], aux_coef=aux_coef)
+    names = {"x": "dx", "w_router": "dw_router", "w_gate_up": "dw_gate_up", "w_down": "dw_down"}
+    if n_shared:
+        names.update({"ws_gate_up": "dws_gate_up"})
+    rng = np.random.default_rng(3)
+    h = 1e-6
+    for pname, gname in names.items():
+        arr = L[pname]
+        for fi in rng.choice(arr.size, size=min(arr.size, 30), replace=False):
+            pos = np.unravel_index(fi, arr.shape)
+            orig = arr[pos]
+            arr[pos] = orig + h
+            lp = O.layer_loss(_relu_fwd(L, k, bias), L["dy"], aux_coef)
+            arr[pos] = orig - h
+            lm = O.layer_loss(_relu_fwd(L, k, bias), L["dy"], aux_coef)
+            arr[pos] = orig
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - g[gname][pos]) <= 1e-6 * max(1.0, abs(g[gname][pos])), (pname, pos)
