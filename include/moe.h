@@ -94,7 +94,24 @@ typedef struct {
   int32_t act_dtype;      /* moe_dtype */
   int32_t expert_dtype;   /* moe_dtype of the expert GEMM operands */
   float aux_coef;         /* alpha: coefficient of the balancing statistic in the loss */
+  int32_t router;         /* moe_router: how moe_route chooses and weights the experts */
 } moe_config;
+
+/* Router kinds (moe_config.router).
+ * MOE_ROUTER_SOFTMAX: f32 softmax over the experts, top-k (spark-gpt README,
+ *   feature list); moe_route_balanced and moe_route_sinkhorn are its variants.
+ * MOE_ROUTER_RELU: the ReLU router (KohakUwULLM README, "Key features": ReLU
+ *   routers beside the default; the pages give no rule, so this library
+ *   follows the published ReLU routing): gates g = max(z, 0) with z the
+ *   logits (+ bias), no softmax; each token takes its experts with a positive
+ *   logit, at most top_k of them (the largest, descending, lower index first
+ *   on ties); the remaining slots hold index -1 and weight 0 and are no
+ *   assignment (moe_permute skips them, so offsets[E] <= T*k); the weights
+ *   are the gates themselves (cfg.renorm must be 0); probs holds the gates,
+ *   so the balancing statistic E sum_e f_e mean_t g_te is the published
+ *   load-balanced L1 term on them; moe_backward applies dz = dg where the
+ *   gate is positive, 0 elsewhere. */
+typedef enum { MOE_ROUTER_SOFTMAX = 0, MOE_ROUTER_RELU = 1 } moe_router;
 
 typedef struct moe_plan_s* moe_plan;
 

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_F32, MOE_F16, MOE_BF16, MOE_MXFP8_E4M3 = 0, 1, 2, 3
 MOE_ERR_SCRATCH = -6
+ROUTER_KINDS = {"softmax": 0, "relu": 1}
 _DTYPE_CODE = {torch.float32: MOE_F32, torch.float16: MOE_F16, torch.bfloat16: MOE_BF16}
 
 c_int32, c_int64, c_float, c_void_p, c_size_t = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
@@ -26,7 +27,7 @@ class MoeConfig(ctypes.Structure):
     _fields_ = [("T", c_int64), ("d_model", c_int32), ("n_experts", c_int32), ("top_k", c_int32),
                 ("d_ff", c_int32), ("n_shared", c_int32), ("d_ff_shared", c_int32),
                 ("renorm", c_int32), ("has_router_bias", c_int32), ("act_dtype", c_int32),
-                ("expert_dtype", c_int32), ("aux_coef", c_float)]
+                ("expert_dtype", c_int32), ("aux_coef", c_float), ("router", c_int32)]
 
 
 _FFN_FIELDS = ["x_perm", "offsets", "w_gate_up", "w_down", "gu", "h", "y_perm", "x", "ws_gate_up",
@@ -143,7 +144,7 @@ class Plan:
     without a GPU."""
 
     def __init__(self, T, d_model, n_experts, top_k, d_ff, n_shared=0, d_ff_shared=0, renorm=True,
-                 has_router_bias=False, dtype=torch.bfloat16, aux_coef=0.01, expert_dtype=None):
+                 has_router_bias=False, dtype=torch.bfloat16, aux_coef=0.01, expert_dtype=None, router="softmax"):
         if dtype not in _DTYPE_CODE:
             raise ValueError(f"unsupported activation dtype {dtype}")
         code = _DTYPE_CODE[dtype]
@@ -153,8 +154,11 @@ class Plan:
             ecode = MOE_MXFP8_E4M3
         else:
             ecode = expert_dtype
+        if router not in ROUTER_KINDS:
+            raise ValueError(f"unknown router {router!r}")
         self.cfg = MoeConfig(T, d_model, n_experts, top_k, d_ff, n_shared, d_ff_shared, int(renorm),
-                             int(has_router_bias), code, ecode, aux_coef)
+                             int(has_router_bias), code, ecode, aux_coef, ROUTER_KINDS[router])
+        self.router = router
         self.dtype = dtype
         self.mx = ecode == MOE_MXFP8_E4M3                  # MX-fp8 experts
         self.T, self.d, self.E, self.k, self.I = T, d_model, n_experts, top_k, d_ff

@@ -307,6 +307,8 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
   if (c.act_dtype < MOE_F32 || c.act_dtype > MOE_MXFP8_E4M3) return MOE_ERR_INVALID;
   if (c.expert_dtype < MOE_F32 || c.expert_dtype > MOE_MXFP8_E4M3) return MOE_ERR_INVALID;
   if (!(c.aux_coef == c.aux_coef)) return MOE_ERR_INVALID;  // NaN
+  if (c.router != MOE_ROUTER_SOFTMAX && c.router != MOE_ROUTER_RELU) return MOE_ERR_INVALID;
+  if (c.router == MOE_ROUTER_RELU && c.renorm) return MOE_ERR_INVALID;   // ReLU gates are the weights
   if (c.act_dtype == MOE_MXFP8_E4M3) return MOE_ERR_UNSUPPORTED;
   const bool mx = c.expert_dtype == MOE_MXFP8_E4M3;
   if (mx && c.act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;   // MX GEMMs write bf16
@@ -587,6 +589,7 @@ moe_status moe_route(moe_plan p, const void* x, const void* w_router, const floa
   hipStream_t s = static_cast<hipStream_t>(stream);
   RouteArgs a{x, w_router, p->cfg.has_router_bias ? bias : nullptr, probs, topk_idx, topk_w,
               p->T, p->d, p->E, p->k, p->cfg.renorm};
+  a.relu = p->cfg.router == MOE_ROUTER_RELU;
   Probe pr(p, "route", s);
   return hip_status(launch_route(p->dt, a, s));
 }
@@ -594,6 +597,7 @@ moe_status moe_route(moe_plan p, const void* x, const void* w_router, const floa
 moe_status moe_route_balanced(moe_plan p, const void* x, const void* w_router, const float* bias,
                               const float* sel_bias, float* probs, int32_t* topk_idx, float* topk_w, void* stream) {
   if (!p) return MOE_ERR_NULL;
+  if (p->cfg.router != MOE_ROUTER_SOFTMAX) return MOE_ERR_INVALID;   // ranks on probabilities
   if (p->T == 0) return MOE_OK;
   if (!x || !w_router || !sel_bias || !probs || !topk_idx || !topk_w) return MOE_ERR_NULL;
   if (p->cfg.has_router_bias && !bias) return MOE_ERR_NULL;
@@ -609,6 +613,7 @@ moe_status moe_route_sinkhorn(moe_plan p, const void* x, const void* w_router, c
                               size_t ws_bytes, void* stream) {
   if (!p) return MOE_ERR_NULL;
   if (n_iter < 1 || n_iter > kSinkhornMaxIters) return MOE_ERR_INVALID;
+  if (p->cfg.router != MOE_ROUTER_SOFTMAX) return MOE_ERR_INVALID;   // balances probabilities
   if (p->T == 0) return MOE_OK;
   if (!x || !w_router || !probs || !topk_idx || !topk_w || !col_scale) return MOE_ERR_NULL;
   if (p->cfg.has_router_bias && !bias) return MOE_ERR_NULL;
@@ -1040,13 +1045,13 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
     if (p->router_small) {
       RouterBwdSmallArgs a{g, sv->topk_w, sv->topk_idx, sv->probs, sv->counts, sv->x, dzhl, dwr_part, dbias_part,
                            p->T, E, Ep, d, k, p->cfg.renorm, p->cfg.aux_coef, sv->real_mask, sv->real_counts};
-      a.gpart = gp; a.inv = sv->inv_perm; a.gparts = p->gparts;
+      a.gpart = gp; a.inv = sv->inv_perm; a.gparts = p->gparts; a.relu = p->cfg.router == MOE_ROUTER_RELU;
       Probe pr(p, "router_bwd_small", s);
       MOE_TRY(launch_router_bwd_small(p->dt, a, s));
     } else {
       RouterDzArgs a{g, sv->topk_w, sv->topk_idx, sv->probs, sv->counts, dzhl, dbias_part,
                      p->T, E, Ep, k, p->cfg.renorm, p->cfg.aux_coef, sv->real_mask, sv->real_counts};
-      a.gpart = gp; a.inv = sv->inv_perm; a.gparts = p->gparts;
+      a.gpart = gp; a.inv = sv->inv_perm; a.gparts = p->gparts; a.relu = p->cfg.router == MOE_ROUTER_RELU;
       Probe pr(p, "router_dz", s);
       MOE_TRY(launch_router_dz(p->dt, a, s));
     }

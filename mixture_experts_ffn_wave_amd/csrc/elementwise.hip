@@ -196,7 +196,9 @@ __global__ void __launch_bounds__(NT) combine_bwd_kernel(CombineBwdArgs a) {
 __device__ __forceinline__ float slot_g(const float* g, const float* gpart, const int32_t* inv, int gparts,
                                         int64_t tj) {
   if (!gpart) return g[tj];
-  const float* p = gpart + (int64_t)inv[tj] * gparts;
+  const int r = inv[tj];
+  if (r < 0) return 0.0f;                         // an empty slot (no expert)
+  const float* p = gpart + (int64_t)r * gparts;
   float s = 0.0f;
   for (int i = 0; i < gparts; ++i) s += p[i];
   return s;
@@ -247,9 +249,11 @@ __global__ void __launch_bounds__(NT) router_dz_kernel(RouterDzArgs a) {
     int ej = -1;
     if (lane < a.k) {
       ej = a.idx[t * a.k + lane];
-      gj = slot_g(a.g, a.gpart, a.inv, a.gparts, t * a.k + lane);
-      wj = a.wts[t * a.k + lane];
       if ((unsigned)ej >= (unsigned)a.E) ej = -1;
+      if (ej >= 0) {                                   // an empty slot carries nothing
+        gj = slot_g(a.g, a.gpart, a.inv, a.gparts, t * a.k + lane);
+        wj = a.wts[t * a.k + lane];
+      }
     }
     // p of this slot's expert, from the lane that holds it
     float pj = 0.0f;
@@ -282,7 +286,8 @@ __global__ void __launch_bounds__(NT) router_dz_kernel(RouterDzArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = lane + 64 * q;
-      const float v = (e < a.E) ? p[q] * (dp[q] - dot) : 0.0f;
+      // softmax Jacobian, or (ReLU gates) the gate's derivative 1[gate > 0]
+      const float v = (e < a.E) ? (a.relu ? (p[q] > 0.0f ? dp[q] : 0.0f) : p[q] * (dp[q] - dot)) : 0.0f;
       if (e < a.Ep) {
         const T hi = from_f32<T>(v);
         const T lo = from_f32<T>(v - to_f32<T>(hi));
@@ -334,6 +339,7 @@ __global__ void __launch_bounds__(NT) router_bwd_small_kernel(RouterBwdSmallArgs
       float S = 0.0f, wg = 0.0f;
       for (int j = 0; j < a.k; ++j) {
         const int ej = a.idx[t * a.k + j];
+        if (ej < 0) continue;                          // an empty slot carries nothing
         float pj = 0.0f;
 #pragma unroll
         for (int e = 0; e < EM; ++e) pj = (e == ej) ? p[e] : pj;
@@ -342,6 +348,7 @@ __global__ void __launch_bounds__(NT) router_bwd_small_kernel(RouterBwdSmallArgs
       }
       for (int j = 0; j < a.k; ++j) {
         const int ej = a.idx[t * a.k + j];
+        if (ej < 0) continue;
         const float gj = slot_g(a.g, a.gpart, a.inv, a.gparts, t * a.k + j);
         const float dps = a.renorm ? (gj - wg) / S : gj;
 #pragma unroll
@@ -354,7 +361,7 @@ __global__ void __launch_bounds__(NT) router_bwd_small_kernel(RouterBwdSmallArgs
 #pragma unroll
       for (int e = 0; e < EM; ++e) {
         if (e < E) {
-          const float v = p[e] * (dp[e] - dot);
+          const float v = a.relu ? (p[e] > 0.0f ? dp[e] : 0.0f) : p[e] * (dp[e] - dot);
           dzv[e] = v;
           const T hi = from_f32<T>(v);
           dz[e] = hi;

@@ -23,6 +23,7 @@ struct RouteArgs {
   int64_t T;
   int d, E, k, renorm;
   const float* sel_bias = nullptr;  // [E] or nullptr: experts chosen on probs + sel_bias (weights unbiased)
+  int relu = 0;                      // 1: ReLU router (gates max(z, 0) in probs, positive logits only)
 };
 hipError_t launch_route(int dt, const RouteArgs& a, hipStream_t s);
 
@@ -228,6 +229,7 @@ struct RouterDzArgs {
   // g from partial sums instead of g [T, k]: g[t, j] = sum over p < gparts of
   // gpart[inv[t, j] * gparts + p], in that order
   const float* gpart = nullptr; const int32_t* inv = nullptr; int gparts = 0;
+  int relu = 0;         // 1: probs hold ReLU gates; dz = dp where the gate is positive, else 0
 };
 int router_dz_blocks(int64_t T);
 hipError_t launch_router_dz(int dt, const RouterDzArgs& a, hipStream_t s);
@@ -250,6 +252,7 @@ struct RouterBwdSmallArgs {
   int64_t T; int E, Ep, d, k, renorm; float aux_coef;
   const int32_t* mask = nullptr; const int32_t* rcounts = nullptr;   // as in RouterDzArgs
   const float* gpart = nullptr; const int32_t* inv = nullptr; int gparts = 0;  // as in RouterDzArgs
+  int relu = 0;                                                                 // as in RouterDzArgs
 };
 int router_small_blocks(int64_t T);
 hipError_t launch_router_bwd_small(int dt, const RouterBwdSmallArgs& a, hipStream_t s);

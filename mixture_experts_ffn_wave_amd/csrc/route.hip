@@ -194,10 +194,13 @@ __device__ __forceinline__ void route_epilogue_wide(const float* red, int64_t tb
     if (g * EPL + i < E) sum += expf(z[i] - m);
 #pragma unroll
   for (int o = 1; o < 8; o <<= 1) sum += __shfl_xor(sum, o, 64);
-  // probabilities (kept in z when a selection bias ranks on them)
+  // probabilities (kept in z when a selection bias ranks on them); the ReLU
+  // router stores its gates max(z, 0) in their place
+  const bool relu = a.relu != 0;
   float p[EPL];
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) p[i] = (g * EPL + i < E) ? expf(z[i] - m) / sum : 0.0f;
+  for (int i = 0; i < EPL; ++i)
+    p[i] = (g * EPL + i < E) ? (relu ? fmaxf(z[i], 0.0f) : expf(z[i] - m) / sum) : 0.0f;
   if (tv) {
     float* prow = a.probs + t * E + g * EPL;
     if ((E & 3) == 0) {
@@ -211,7 +214,9 @@ __device__ __forceinline__ void route_epilogue_wide(const float* red, int64_t tb
         if (g * EPL + i < E) prow[i] = p[i];
     }
   }
-  // top-k: k rounds of (largest remaining ranking value, lower index on ties)
+  // top-k: k rounds of (largest remaining ranking value, lower index on ties);
+  // the ReLU router only takes positive logits, a round without one leaves
+  // the slot empty (index -1, weight 0)
   uint32_t taken = 0u;
   float psum = 0.0f;
   for (int j = 0; j < a.k; ++j) {
@@ -220,7 +225,7 @@ __device__ __forceinline__ void route_epilogue_wide(const float* red, int64_t tb
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = g * EPL + i;
-      if (e < E && !((taken >> i) & 1u)) {
+      if (e < E && !((taken >> i) & 1u) && (!relu || z[i] > 0.0f)) {
         const float v = sel ? p[i] + s_sel[e] : z[i];
         if (be < 0 || v > bv) {
           bv = v;
@@ -243,7 +248,7 @@ __device__ __forceinline__ void route_epilogue_wide(const float* red, int64_t tb
       }
     }
     if (be >= 0 && be / EPL == g) taken |= 1u << (be - g * EPL);
-    const float pj = sel ? bp : expf(bz - m) / sum;
+    const float pj = be < 0 ? 0.0f : (relu ? bz : (sel ? bp : expf(bz - m) / sum));
     psum += pj;
     if (tv && g == 0) {
       a.idx[t * a.k + j] = be;

@@ -36,6 +36,7 @@ class Workload:
     zipf_s: float = 0.0          # > 0: constant router bias ln(pi_e), pi_e ~ (e+1)^-s
     aux_coef: float = 0.01
     seed: int = 0
+    router: str = "softmax"      # "softmax" or "relu" (the ReLU router)
 
     @property
     def torch_dtype(self):
@@ -137,5 +138,6 @@ def to_f64(t):
 def describe(wl: Workload):
     ed = wl.expert_dtype or wl.dtype
     return (f"T={wl.T} d={wl.d} E={wl.E} k={wl.k} I={wl.I} shared={wl.n_shared}x{wl.I_shared} "
-            f"renorm={wl.renorm} dtype={wl.dtype} experts={ed} zipf={wl.zipf_s}")
+            f"renorm={wl.renorm} dtype={wl.dtype} experts={ed} zipf={wl.zipf_s}" +
+            (f" router={wl.router}" if wl.router != "softmax" else ""))
 

@@ -82,7 +82,7 @@ def plan_for(wl, has_bias):
     from mixture_experts_ffn_wave_amd import Plan
     return Plan(wl.T, wl.d, wl.E, wl.k, wl.I, n_shared=wl.n_shared, d_ff_shared=wl.I_shared,
                 renorm=wl.renorm, has_router_bias=has_bias, dtype=wl.torch_dtype, aux_coef=wl.aux_coef,
-                expert_dtype=wl.expert_dtype or None)
+                expert_dtype=wl.expert_dtype or None, router=wl.router)
 
 
 def to_np(t):
@@ -165,7 +165,7 @@ def oracle_run(wl, f64, store=None, quant=None, sel_bias=None, mask=None, sinkho
                           renorm=wl.renorm, bias=b, ws_gate_up=f64.get("ws_gate_up"),
                           ws_down=f64.get("ws_down"), store=store, quant=quant,
                           sel_bias=None if sel_bias is None else np.asarray(sel_bias, dtype=np.float64),
-                          sinkhorn_iters=sinkhorn)
+                          sinkhorn_iters=sinkhorn, router=wl.router)
     bwd = O.layer_backward(fwd, f64["dy"], aux_coef=wl.aux_coef, quant=quant, mask=mask)
     if mask is None:
         st = O.aux_statistics(fwd["p"], fwd["counts"], wl.k)
@@ -219,6 +219,8 @@ def compare_routing(wl, gpu, fwd):
     token; asserts that any difference is an allowed near-tie.  The ranked
     values are the logits, or probability + selection bias when balancing."""
     eps = TIE_EPS
+    if wl.router == "relu":
+        return _compare_relu_routing(wl, gpu, fwd)
     if fwd.get("sinkhorn_b") is not None:
         # Sinkhorn router: scales first, then ranks on ln(p b)
         if "sinkhorn_b" in gpu:
@@ -249,22 +251,59 @@ def compare_routing(wl, gpu, fwd):
     return bool(same.all())
 
 
+RELU_ATOL = 1e-5      # gates are f32 logits (f32 accumulation over d): relative to max(1, |gate|)
+
+
+def _compare_relu_routing(wl, gpu, fwd):
+    """The ReLU router: gates max(z, 0) against the oracle's, and the choice
+    (the k largest positive logits, -1 past them) bit-exact except tokens
+    whose choice a near-tie decides: the k-th and (k+1)-th logits within
+    TIE_EPS, or a logit within TIE_EPS of zero (its sign decides whether it
+    may be chosen); those must hold a valid choice within that margin."""
+    z, k, E = fwd["z"], wl.k, wl.E
+    g_ref = fwd["p"]
+    assert np.max(np.abs(gpu["probs"] - g_ref) / np.maximum(1.0, np.abs(g_ref))) <= RELU_ATOL, "ReLU gates"
+    gi = gpu["topk_idx"]
+    same = np.all(gi == fwd["idx"], axis=1)
+    set_tie, order_tie = O.near_tie_tokens(z, k, TIE_EPS)
+    tie = set_tie | order_tie | (np.abs(z) < TIE_EPS).any(axis=1)
+    bad = ~same & ~tie
+    assert not bad.any(), f"ReLU routing differs on {int(bad.sum())} non-tied tokens, e.g. {np.where(bad)[0][:5]}"
+    for t in np.where(~same)[0]:
+        sel = gi[t][gi[t] >= 0]
+        assert np.all(gi[t][len(sel):] == -1), f"token {t}: empty slots not last"
+        assert len(set(sel.tolist())) == len(sel) and (sel.size == 0 or sel.max() < E)
+        zs = z[t, sel]
+        assert np.all(zs > -TIE_EPS) and np.all(np.diff(zs) <= TIE_EPS), f"token {t}: not positive / descending"
+        rest = np.setdiff1d(np.arange(E), sel)
+        bound = zs.min() if len(sel) == k else 0.0
+        if rest.size:
+            assert z[t, rest].max() <= bound + TIE_EPS, f"token {t}: a larger positive logit left out"
+    if same.any():
+        w = fwd["w"][same]
+        assert np.max(np.abs(gpu["topk_w"][same] - w) / np.maximum(1.0, np.abs(w))) <= RELU_ATOL, "ReLU weights"
+    return bool(same.all())
+
+
 def compare_dispatch(gpu, fwd):
-    """Integer work and the gather: bit-exact."""
+    """Integer work and the gather: bit-exact (over the offsets[E] real rows:
+    the ReLU router's empty slots are no assignment)."""
+    n = int(fwd["offsets"][-1])
     assert np.array_equal(gpu["counts"], fwd["counts"]), "counts"
     assert np.array_equal(gpu["offsets"], fwd["offsets"]), "offsets"
-    assert np.array_equal(gpu["perm_token"], fwd["perm_token"]), "perm_token"
+    assert np.array_equal(gpu["perm_token"][:n], fwd["perm_token"]), "perm_token"
     assert np.array_equal(gpu["inv_perm"], fwd["inv"]), "inv_perm"
-    assert np.array_equal(gpu["x_perm"], fwd["x_perm"]), "x_perm is a pure copy"
+    assert np.array_equal(gpu["x_perm"][:n], fwd["x_perm"]), "x_perm is a pure copy"
 
 
-def compare_stats(gpu, st):
+def compare_stats(gpu, st, p_atol=PROB_ATOL):
     """Balancing statistic and router metrics (and, over real tokens, their
-    counts: integers, bit-exact)."""
+    counts: integers, bit-exact).  ``p_atol``: of the mean probability (the
+    ReLU router's mean gate: relative to max(1, value))."""
     if "real_counts" in st:
         assert np.array_equal(gpu["real_counts"], st["real_counts"]), "real-token counts"
     assert np.allclose(gpu["f"], st["f"], rtol=1e-6, atol=0), "f"
-    assert np.max(np.abs(gpu["p_mean"] - st["p_mean"])) <= PROB_ATOL, "p_mean"
+    assert np.max(np.abs(gpu["p_mean"] - st["p_mean"]) / np.maximum(1.0, np.abs(st["p_mean"]))) <= p_atol, "p_mean"
     a = gpu["aux"]
     assert abs(a["aux"] - st["aux"]) <= 1e-5 * max(1.0, abs(st["aux"])), ("aux", a["aux"], st["aux"])
     assert abs(a["aux_raw"] - st["aux_raw"]) <= 1e-5 * max(1.0, abs(st["aux_raw"]))
@@ -284,10 +323,11 @@ def compare_downstream(wl, gpu, fwd, bwd, st, rounded=False):
     ku = 1.0 if rounded else 0.5
     compare_dispatch(gpu, fwd)
     inter = wl.I
-    check_close("G", gpu["gu"][:, :inter], fwd["g"], c, gdt, ku)
-    check_close("U", gpu["gu"][:, inter:], fwd["u"], c, gdt, ku)
-    check_close("H", gpu["h"], fwd["h"], c, dt, ku)
-    check_close("Y_perm", gpu["y_perm"], fwd["y_perm"], c, ydt, ku)
+    n = int(fwd["offsets"][-1])                     # real rows
+    check_close("G", gpu["gu"][:n, :inter], fwd["g"], c, gdt, ku)
+    check_close("U", gpu["gu"][:n, inter:], fwd["u"], c, gdt, ku)
+    check_close("H", gpu["h"][:n], fwd["h"], c, dt, ku)
+    check_close("Y_perm", gpu["y_perm"][:n], fwd["y_perm"], c, ydt, ku)
     if wl.n_shared:
         Is = wl.I_shared
         for s, (gs, us, hs) in enumerate(fwd["shared"]):
@@ -315,7 +355,7 @@ def compare_downstream(wl, gpu, fwd, bwd, st, rounded=False):
         for s_ in range(wl.n_shared):
             check_close(f"dWs_gate_up[{s_}]", gpu["dws_gate_up"][s_], bwd["dws_gate_up"][s_], c, dt)
             check_close(f"dWs_down[{s_}]", gpu["dws_down"][s_], bwd["dws_down"][s_], c, dt)
-    compare_stats(gpu, st)
+    compare_stats(gpu, st, RELU_ATOL if wl.router == "relu" else PROB_ATOL)
 
 
 def compare_mx_stepwise(wl, gpu, fwd, f64, st):

@@ -103,6 +103,9 @@ def _create(**kw):
     (dict(act_dtype=L.MOE_F16, expert_dtype=L.MOE_MXFP8_E4M3), MOE_ERR_UNSUPPORTED),  # MX GEMMs write bf16
     (dict(act_dtype=L.MOE_F32, expert_dtype=L.MOE_MXFP8_E4M3), MOE_ERR_UNSUPPORTED),
     (dict(expert_dtype=L.MOE_MXFP8_E4M3, n_shared=2, d_ff_shared=256), MOE_OK),
+    (dict(router=1, renorm=0), MOE_OK),                     # ReLU router
+    (dict(router=1, renorm=1), MOE_ERR_INVALID),            # its gates are the weights
+    (dict(router=2, renorm=0), MOE_ERR_INVALID),
 ])
 def test_plan_validation(kw, status):
     st, h = _create(**kw)
@@ -319,3 +322,12 @@ def test_route_sinkhorn_validates_before_any_launch():
     assert lib.moe_route_sinkhorn(*args(8, nb=wsb - 1)) == MOE_ERR_WORKSPACE
     empty = L.Plan(0, 128, 8, 2, 128, dtype=L.torch.bfloat16)
     assert lib.moe_route_sinkhorn(empty.handle, None, None, None, 4, None, None, None, None, None, 0, None) == MOE_OK
+
+
+def test_probability_router_variants_refuse_a_relu_plan():
+    lib = L.lib()
+    fake = ctypes.c_void_p(0x1000)
+    p = L.Plan(512, 128, 8, 2, 128, dtype=L.torch.bfloat16, renorm=False, router="relu")
+    assert lib.moe_route_balanced(p.handle, fake, fake, None, fake, fake, fake, fake, None) == MOE_ERR_INVALID
+    assert lib.moe_route_sinkhorn(p.handle, fake, fake, None, 4, fake, fake, fake, fake, fake,
+                                  p.workspace_bytes(), None) == MOE_ERR_INVALID

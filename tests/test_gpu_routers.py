@@ -7,7 +7,9 @@ Sinkhorn router: the column scales within SINKHORN_B_RTOL of the oracle's
 except near-ties of ln(p b), the weights within 1e-6, on every router engine
 (4, 8, 64, 128 and 256 experts; f32, f16, bf16; with and without renorm and
 logit bias) and for 1 to 30 rounds; then the whole layer routed this way
-against the exact oracle layer."""
+against the exact oracle layer.
+
+ReLU router: the whole layer against the exact oracle (see RELU below)."""
 
 import numpy as np
 import pytest
@@ -66,3 +68,29 @@ def test_sinkhorn_layer_matches_oracle():
     plain = np.bincount(O.topk_select(fwd["z"], wl.k).ravel(), minlength=wl.E)
     # the Sinkhorn choice spreads the skewed router's load
     assert counts.std() < 0.5 * plain.std(), (counts.std(), plain.std())
+
+
+# ReLU router (moe_config.router = MOE_ROUTER_RELU): gates max(z, 0), the k
+# largest positive logits per token, empty slots -1; the whole layer against
+# the exact oracle on the router engines of 4, 8, 64 and 128 experts.  A
+# constant logit bias falling from hi to lo over the experts makes some tokens
+# have fewer than k (or no) positive logits.
+RELU = [
+    (W("t1000_d256_e8k2_i128_bf16_relu", T=1000, d=256, E=8, k=2, I=128, renorm=False, router="relu"), (0.1, -0.3)),
+    (W("t777_d128_e4k2_i256_f16_relu_shared1", T=777, d=128, E=4, k=2, I=256, renorm=False, router="relu",
+       n_shared=1, I_shared=128, dtype="f16"), (0.1, -0.3)),
+    (W("t513_d128_e64k6_i128_f32_relu", T=513, d=128, E=64, k=6, I=128, renorm=False, router="relu", dtype="f32"),
+     (0.0, -1.0)),
+    (W("t1200_d256_e128k8_i128_bf16_relu", T=1200, d=256, E=128, k=8, I=128, renorm=False, router="relu"),
+     (0.1, -2.0)),
+]
+
+
+@pytest.mark.parametrize("wl,bias", RELU, ids=[w.name for w, _ in RELU])
+def test_relu_router_layer_matches_oracle(wl, bias):
+    inp = MI.make_inputs(wl)
+    inp["bias"] = torch.linspace(bias[0], bias[1], wl.E, dtype=torch.float32)
+    gpu, fwd, _, _ = PT.full_parity(wl, inp)
+    empty = int((fwd["idx"] < 0).sum())
+    PT.say(f"[relu] {wl.name}: {empty} empty slots of {wl.T * wl.k}, {int(fwd['offsets'][-1])} rows")
+    assert empty > 0                                 # the case of fewer than k positive logits is exercised
