@@ -27,6 +27,7 @@ from .moe_oracle import (  # noqa: F401
     relu_gates,
     relu_select,
     relu_gate_weights,
+    expert_choice_select,
     balance_bias_update,
     near_tie_tokens,
     expert_permutation,

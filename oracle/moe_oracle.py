@@ -144,10 +144,29 @@ def relu_select(z, k):
 
 
 def relu_gate_weights(g, idx):
-    """Weights of the ReLU router's slots: the gate of the chosen expert, 0
-    for an empty slot (no renormalisation)."""
+    """Weights of the slots of the ReLU and expert-choice routers: the gate
+    (or probability) of the slot's expert, 0 for an empty slot (no
+    renormalisation)."""
     sel = np.take_along_axis(g, np.maximum(idx, 0), axis=1)
     return np.where(idx >= 0, sel, 0.0)
+
+
+def expert_choice_select(p, capacity):
+    """Expert-choice routing.  KohakUwULLM README, "Key features", names
+    expert-choice routers and gives no rule; the reading taken is the
+    published method: every expert takes the ``capacity`` tokens with the
+    largest routing probability p_te (lower token index first on equal
+    probabilities), C = T k / E rounded down with k the average number of
+    experts per token, so a token is taken by any number of experts (0 to E)
+    and every expert by exactly C tokens.  Returns idx [T, E]: idx[t, e] = e
+    when expert e took token t, else -1 (slot e belongs to expert e)."""
+    p = np.asarray(p, dtype=np.float64)
+    T, E = p.shape
+    idx = np.full((T, E), -1, dtype=np.int64)
+    for e in range(E):
+        taken = np.argsort(-p[:, e], kind="stable")[:capacity]
+        idx[taken, e] = e
+    return idx
 
 
 def balance_bias_update(sel_bias, counts, T, top_k, gamma):
@@ -352,6 +371,10 @@ def layer_forward(x, w_router, w_gate_up, w_down, *, top_k, renorm=True, bias=No
     probabilities of the chosen experts.  ``sinkhorn_iters`` (the Sinkhorn
     router) moves it to sinkhorn_selection_scores(p, b) with b =
     sinkhorn_column_scales(p, sinkhorn_iters), returned as "sinkhorn_b".
+    ``router="expert_choice"``: idx = expert_choice_select(p, T top_k // E)
+    ([T, E] slots, -1 where the expert did not take the token), weights the
+    probabilities of the taken slots (no renormalisation: renorm must be
+    False).
     ``router="relu"`` (the ReLU router) replaces the probabilities by the
     gates relu_gates(z) (returned as "p"), the choice by relu_select and the
     weights by relu_gate_weights (no renormalisation: renorm must be False).
@@ -374,18 +397,21 @@ def layer_forward(x, w_router, w_gate_up, w_down, *, top_k, renorm=True, bias=No
     E = w_router.shape[0]
     z = router_logits(x, w_router, bias)
     relu = router == "relu"
-    if relu:
-        assert not renorm and sel_bias is None and sinkhorn_iters is None, "the ReLU router does not renormalise"
+    ec = router == "expert_choice"
+    if relu or ec:
+        assert not renorm and sel_bias is None and sinkhorn_iters is None, "no renormalisation for this router"
     p = relu_gates(z) if relu else softmax_rows(z)
     sk_b = None
     if relu:
         idx = relu_select(z, top_k)
+    elif ec:
+        idx = expert_choice_select(p, (T * top_k) // E)
     elif sinkhorn_iters is not None:
         sk_b = sinkhorn_column_scales(p, sinkhorn_iters) if T > 0 else np.ones(E)
         idx = topk_select(sinkhorn_selection_scores(p, sk_b), top_k)
     else:
         idx = topk_select(z if sel_bias is None else balanced_selection_scores(p, sel_bias), top_k)
-    w = relu_gate_weights(p, idx) if relu else gate_weights(p, idx, renorm)
+    w = relu_gate_weights(p, idx) if (relu or ec) else gate_weights(p, idx, renorm)
     counts, offsets, perm_token, inv = expert_permutation(idx, E)
     x_perm = x[perm_token]
     inter = w_down.shape[2]
@@ -537,7 +563,7 @@ def layer_backward(fwd, dy, *, aux_coef=0.0, quant=None, mask=None):
         dx_perm[r0:r1] = st(dxe, "act")
 
     dx = np.zeros((T, d))
-    for j in range(k):
+    for j in range(inv.shape[1]):                   # slots (E of them for expert choice)
         t = np.nonzero(inv[:, j] >= 0)[0]
         dx[t] += dx_perm[inv[t, j]]
 

@@ -222,3 +222,75 @@ def test_relu_layer_gradient_matches_central_differences(n_shared):
             arr[pos] = orig
             fd = (lp - lm) / (2 * h)
             assert abs(fd - g[gname][pos]) <= 1e-6 * max(1.0, abs(g[gname][pos])), (pname, pos)
+
+
+# ------------------------------------------------------------ expert choice
+
+def _brute_expert_choice(p, C):
+    T, E = len(p), len(p[0])
+    idx = [[-1] * E for _ in range(T)]
+    for e in range(E):
+        col = sorted(range(T), key=lambda t: (-p[t][e], t))   # probability descending, lower token on ties
+        for t in col[:C]:
+            idx[t][e] = e
+    return np.array(idx)
+
+
+def test_expert_choice_by_brute_force():
+    rng = np.random.default_rng(12)
+    p = O.softmax_rows(np.round(rng.standard_normal((37, 5)), 1))   # ties on purpose
+    for C in (0, 1, 7, 37):
+        got = O.expert_choice_select(p, C)
+        assert np.array_equal(got, _brute_expert_choice(p.tolist(), C))
+        assert np.all((got >= 0).sum(axis=0) == C)                  # every expert takes exactly C tokens
+        assert np.all((got == np.arange(5)[None, :]) | (got == -1))  # slot e is expert e's
+
+
+def test_expert_choice_at_full_capacity_is_the_soft_mixture():
+    # k = E: C = T, every expert takes every token: y_t = sum_e p_te SwiGLU_e(x_t)
+    L = rand_layer(T=9, d=12, E=4, k=4, inter=8, seed=13)
+    fwd = O.layer_forward(L["x"], L["w_router"], L["w_gate_up"], L["w_down"], top_k=4, renorm=False,
+                          router="expert_choice")
+    p = O.softmax_rows(O.router_logits(L["x"], L["w_router"]))
+    assert np.all(fwd["idx"] == np.arange(4)[None, :]) and np.array_equal(fwd["counts"], [9] * 4)
+    y = np.zeros_like(L["x"])
+    for e in range(4):
+        y += p[:, e:e + 1] * O.swiglu_rows(L["x"], L["w_gate_up"][e], L["w_down"][e])[3]
+    assert np.allclose(fwd["y"], y, rtol=1e-13, atol=1e-13)
+
+
+def _ec_fwd(L, k):
+    return O.layer_forward(L["x"], L["w_router"], L["w_gate_up"], L["w_down"], top_k=k, renorm=False,
+                           ws_gate_up=L["ws_gate_up"], ws_down=L["ws_down"], router="expert_choice")
+
+
+@pytest.mark.parametrize("n_shared", [0, 1])
+def test_expert_choice_layer_gradient_matches_central_differences(n_shared):
+    k, aux_coef = 2, 0.4
+    for sd in range(600, 900):
+        L = rand_layer(T=10, d=12, E=5, k=k, inter=8, n_shared=n_shared, inter_s=8, seed=sd, wscale=0.3)
+        p = O.softmax_rows(O.router_logits(L["x"], L["w_router"]))
+        C = (10 * k) // 5
+        srt = -np.sort(-p, axis=0)
+        if np.min(srt[C - 1] - srt[C]) > 1e-4:                      # each expert's C-th and (C+1)-th apart
+            break
+    fwd = _ec_fwd(L, k)
+    assert (fwd["idx"] < 0).any() and ((fwd["idx"] >= 0).sum(axis=1) != k).any()   # uneven tokens
+    g = O.layer_backward(fwd, L["dy"], aux_coef=aux_coef)
+    names = {"x": "dx", "w_router": "dw_router", "w_gate_up": "dw_gate_up", "w_down": "dw_down"}
+    if n_shared:
+        names.update({"ws_down": "dws_down"})
+    rng = np.random.default_rng(4)
+    h = 1e-6
+    for pname, gname in names.items():
+        arr = L[pname]
+        for fi in rng.choice(arr.size, size=min(arr.size, 30), replace=False):
+            pos = np.unravel_index(fi, arr.shape)
+            orig = arr[pos]
+            arr[pos] = orig + h
+            lp = O.layer_loss(_ec_fwd(L, k), L["dy"], aux_coef)
+            arr[pos] = orig - h
+            lm = O.layer_loss(_ec_fwd(L, k), L["dy"], aux_coef)
+            arr[pos] = orig
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - g[gname][pos]) <= 1e-6 * max(1.0, abs(g[gname][pos])), (pname, pos)
