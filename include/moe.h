@@ -110,8 +110,22 @@ typedef struct {
  *   are the gates themselves (cfg.renorm must be 0); probs holds the gates,
  *   so the balancing statistic E sum_e f_e mean_t g_te is the published
  *   load-balanced L1 term on them; moe_backward applies dz = dg where the
- *   gate is positive, 0 elsewhere. */
-typedef enum { MOE_ROUTER_SOFTMAX = 0, MOE_ROUTER_RELU = 1 } moe_router;
+ *   gate is positive, 0 elsewhere.
+ * MOE_ROUTER_EXPERT_CHOICE: the expert-choice router (KohakUwULLM README,
+ *   "Key features": expert-choice routers beside the default; the pages give
+ *   no rule, so this library follows the published method), routed with
+ *   moe_route_expert_choice (moe_route refuses it): every expert takes the
+ *   C = T top_k / E (rounded down) tokens of largest f32 softmax probability
+ *   (lower token index first on ties), so a token is taken by 0 to E experts.
+ *   The routing arrays then have one slot per expert: topk_idx, topk_w and
+ *   inv_perm are [T, E] (slot e holds e or -1, the weight the probability or
+ *   0; cfg.renorm must be 0), everything [T, k]-shaped elsewhere in this
+ *   header is [T, E], and E <= 64 (MOE_ERR_UNSUPPORTED otherwise); rows stay
+ *   at most T top_k (E C of them), and the statistic's f_e = count_e /
+ *   (T top_k) = C / (T top_k), the same for every expert.  moe_backward
+ *   applies the softmax Jacobian to the taken slots' gradients (the choice
+ *   carries no gradient). */
+typedef enum { MOE_ROUTER_SOFTMAX = 0, MOE_ROUTER_RELU = 1, MOE_ROUTER_EXPERT_CHOICE = 2 } moe_router;
 
 typedef struct moe_plan_s* moe_plan;
 
@@ -156,6 +170,18 @@ moe_status moe_route(moe_plan plan, const void* x, const void* w_router, const f
 moe_status moe_route_balanced(moe_plan plan, const void* x, const void* w_router, const float* bias,
                               const float* sel_bias, float* probs, int32_t* topk_idx, float* topk_w,
                               void* stream);
+
+/* Expert-choice router (see MOE_ROUTER_EXPERT_CHOICE; the plan must have that
+ * router): probs as moe_route, then every expert takes its C tokens of
+ * largest probability by a radix select on the f32 bit patterns of its
+ * column, deterministically (no float atomics).
+ *   topk_idx  [T, E] int32 out: e where expert e took token t, else -1
+ *   topk_w    [T, E] f32 out: probs[t, e] where taken, else 0
+ *   ws        the plan's workspace (it holds the transposed probabilities)
+ *   other arguments as for moe_route. */
+moe_status moe_route_expert_choice(moe_plan plan, const void* x, const void* w_router, const float* bias,
+                                   float* probs, int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                                   void* stream);
 
 /* Sinkhorn router (KohakUwULLM README, "Key features": Sinkhorn routers
  * beside the default; the pages give no rule, so this library follows the

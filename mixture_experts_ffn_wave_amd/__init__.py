@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     moe_route,
     moe_route_balanced,
     moe_route_sinkhorn,
+    moe_route_expert_choice,
     moe_balance_update,
     moe_permute,
     moe_expert_ffn,

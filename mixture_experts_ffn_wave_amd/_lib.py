@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_F32, MOE_F16, MOE_BF16, MOE_MXFP8_E4M3 = 0, 1, 2, 3
 MOE_ERR_SCRATCH = -6
-ROUTER_KINDS = {"softmax": 0, "relu": 1}
+ROUTER_KINDS = {"softmax": 0, "relu": 1, "expert_choice": 2}
 _DTYPE_CODE = {torch.float32: MOE_F32, torch.float16: MOE_F16, torch.bfloat16: MOE_BF16}
 
 c_int32, c_int64, c_float, c_void_p, c_size_t = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
@@ -66,6 +66,7 @@ SIGNATURES = {
     "moe_route": (c_int32, [c_void_p] * 8),
     "moe_route_balanced": (c_int32, [c_void_p] * 9),
     "moe_route_sinkhorn": (c_int32, [c_void_p] * 4 + [c_int32] + [c_void_p] * 5 + [c_size_t, c_void_p]),
+    "moe_route_expert_choice": (c_int32, [c_void_p] * 8 + [c_size_t, c_void_p]),
     "moe_balance_update": (c_int32, [c_void_p, c_void_p, c_void_p, c_float, c_void_p]),
     "moe_permute": (c_int32, [c_void_p] * 9 + [c_size_t, c_void_p]),
     "moe_permute_noalloc": (c_int32, [c_void_p] * 9),
@@ -159,6 +160,9 @@ class Plan:
         self.cfg = MoeConfig(T, d_model, n_experts, top_k, d_ff, n_shared, d_ff_shared, int(renorm),
                              int(has_router_bias), code, ecode, aux_coef, ROUTER_KINDS[router])
         self.router = router
+        # routing slots per token (topk_idx, topk_w, inv_perm are [T, slots]):
+        # top_k, or one per expert for expert choice
+        self.slots = n_experts if router == "expert_choice" else top_k
         self.dtype = dtype
         self.mx = ecode == MOE_MXFP8_E4M3                  # MX-fp8 experts
         self.T, self.d, self.E, self.k, self.I = T, d_model, n_experts, top_k, d_ff
@@ -200,7 +204,7 @@ def moe_route(plan, x, w_router, bias, probs, topk_idx, topk_w, stream=None):
     T, d, E, k, dt = plan.T, plan.d, plan.E, plan.k, plan.dtype
     _need(x, "x", (T, d), dt); _need(w_router, "w_router", (E, d), dt)
     _need(probs, "probs", (T, E), torch.float32)
-    _need(topk_idx, "topk_idx", (T, k), torch.int32); _need(topk_w, "topk_w", (T, k), torch.float32)
+    _need(topk_idx, "topk_idx", (T, plan.slots), torch.int32); _need(topk_w, "topk_w", (T, plan.slots), torch.float32)
     if plan.has_bias:
         _need(bias, "bias", (E,), torch.float32)
     st = lib().moe_route(plan.handle, _ptr(x), _ptr(w_router), _ptr(bias) if plan.has_bias else None,
@@ -213,7 +217,7 @@ def moe_route_balanced(plan, x, w_router, bias, sel_bias, probs, topk_idx, topk_
     _need(x, "x", (T, d), dt); _need(w_router, "w_router", (E, d), dt)
     _need(sel_bias, "sel_bias", (E,), torch.float32)
     _need(probs, "probs", (T, E), torch.float32)
-    _need(topk_idx, "topk_idx", (T, k), torch.int32); _need(topk_w, "topk_w", (T, k), torch.float32)
+    _need(topk_idx, "topk_idx", (T, plan.slots), torch.int32); _need(topk_w, "topk_w", (T, plan.slots), torch.float32)
     if plan.has_bias:
         _need(bias, "bias", (E,), torch.float32)
     st = lib().moe_route_balanced(plan.handle, _ptr(x), _ptr(w_router), _ptr(bias) if plan.has_bias else None,
@@ -225,7 +229,7 @@ def moe_route_sinkhorn(plan, x, w_router, bias, n_iter, probs, topk_idx, topk_w,
     T, d, E, k, dt = plan.T, plan.d, plan.E, plan.k, plan.dtype
     _need(x, "x", (T, d), dt); _need(w_router, "w_router", (E, d), dt)
     _need(probs, "probs", (T, E), torch.float32)
-    _need(topk_idx, "topk_idx", (T, k), torch.int32); _need(topk_w, "topk_w", (T, k), torch.float32)
+    _need(topk_idx, "topk_idx", (T, plan.slots), torch.int32); _need(topk_w, "topk_w", (T, plan.slots), torch.float32)
     _need(col_scale, "col_scale", (E,), torch.float32)
     if plan.has_bias:
         _need(bias, "bias", (E,), torch.float32)
@@ -233,6 +237,20 @@ def moe_route_sinkhorn(plan, x, w_router, bias, n_iter, probs, topk_idx, topk_w,
                                   int(n_iter), _ptr(probs), _ptr(topk_idx), _ptr(topk_w), _ptr(col_scale),
                                   _ptr(ws), ws.numel(), _stream(stream))
     _check("moe_route_sinkhorn", st)
+
+
+def moe_route_expert_choice(plan, x, w_router, bias, probs, topk_idx, topk_w, ws, stream=None):
+    T, d, E, dt = plan.T, plan.d, plan.E, plan.dtype
+    _need(x, "x", (T, d), dt); _need(w_router, "w_router", (E, d), dt)
+    _need(probs, "probs", (T, E), torch.float32)
+    _need(topk_idx, "topk_idx", (T, plan.slots), torch.int32)
+    _need(topk_w, "topk_w", (T, plan.slots), torch.float32)
+    if plan.has_bias:
+        _need(bias, "bias", (E,), torch.float32)
+    st = lib().moe_route_expert_choice(plan.handle, _ptr(x), _ptr(w_router), _ptr(bias) if plan.has_bias else None,
+                                       _ptr(probs), _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws.numel(),
+                                       _stream(stream))
+    _check("moe_route_expert_choice", st)
 
 
 def moe_balance_update(plan, counts, sel_bias, gamma, stream=None):
@@ -243,9 +261,9 @@ def moe_balance_update(plan, counts, sel_bias, gamma, stream=None):
 
 def moe_permute(plan, topk_idx, x, counts, offsets, perm_token, inv_perm, x_perm, ws, stream=None):
     T, d, E, k, dt = plan.T, plan.d, plan.E, plan.k, plan.dtype
-    _need(topk_idx, "topk_idx", (T, k), torch.int32); _need(x, "x", (T, d), dt)
+    _need(topk_idx, "topk_idx", (T, plan.slots), torch.int32); _need(x, "x", (T, d), dt)
     _need(counts, "counts", (E,), torch.int32); _need(offsets, "offsets", (E + 1,), torch.int32)
-    _need(perm_token, "perm_token", (T * k,), torch.int32); _need(inv_perm, "inv_perm", (T, k), torch.int32)
+    _need(perm_token, "perm_token", (T * k,), torch.int32); _need(inv_perm, "inv_perm", (T, plan.slots), torch.int32)
     if x_perm is not None:                     # None: indices only (MX experts gathering on load)
         _need(x_perm, "x_perm", (T * k, d), dt)
     st = lib().moe_permute(plan.handle, _ptr(topk_idx), _ptr(x), _ptr(counts), _ptr(offsets),
@@ -257,9 +275,9 @@ def moe_permute(plan, topk_idx, x, counts, offsets, perm_token, inv_perm, x_perm
 def moe_permute_noalloc(plan, topk_idx, x, counts, offsets, perm_token, inv_perm, x_perm, stream=None):
     """moe_permute with its scratch in the library's fixed device array (no workspace)."""
     T, d, E, k, dt = plan.T, plan.d, plan.E, plan.k, plan.dtype
-    _need(topk_idx, "topk_idx", (T, k), torch.int32); _need(x, "x", (T, d), dt)
+    _need(topk_idx, "topk_idx", (T, plan.slots), torch.int32); _need(x, "x", (T, d), dt)
     _need(counts, "counts", (E,), torch.int32); _need(offsets, "offsets", (E + 1,), torch.int32)
-    _need(perm_token, "perm_token", (T * k,), torch.int32); _need(inv_perm, "inv_perm", (T, k), torch.int32)
+    _need(perm_token, "perm_token", (T * k,), torch.int32); _need(inv_perm, "inv_perm", (T, plan.slots), torch.int32)
     if x_perm is not None:
         _need(x_perm, "x_perm", (T * k, d), dt)
     st = lib().moe_permute_noalloc(plan.handle, _ptr(topk_idx), _ptr(x), _ptr(counts), _ptr(offsets),
@@ -303,8 +321,8 @@ def moe_expert_ffn(plan, x_perm, offsets, w_gate_up, w_down, gu, h, y_perm, x=No
 
 def moe_combine(plan, y_perm, inv_perm, topk_w, y_shared, y, stream=None):
     T, d, k, dt = plan.T, plan.d, plan.k, plan.dtype
-    _need(y_perm, "y_perm", (T * k, d), plan.y_perm_dtype); _need(inv_perm, "inv_perm", (T, k), torch.int32)
-    _need(topk_w, "topk_w", (T, k), torch.float32); _need(y, "y", (T, d), dt)
+    _need(y_perm, "y_perm", (T * k, d), plan.y_perm_dtype); _need(inv_perm, "inv_perm", (T, plan.slots), torch.int32)
+    _need(topk_w, "topk_w", (T, plan.slots), torch.float32); _need(y, "y", (T, d), dt)
     if y_shared is not None:
         _need(y_shared, "y_shared", (T, d), dt)
     st = lib().moe_combine(plan.handle, _ptr(y_perm), _ptr(inv_perm), _ptr(topk_w), _ptr(y_shared), _ptr(y),
@@ -350,7 +368,7 @@ def moe_aux_stats_masked(plan, probs, topk_idx, real_mask, f, p_mean, real_count
     """The statistic over real tokens (real_mask [T] int32, 0 = filler);
     real_counts [E+1] int32 receives their counts and their number."""
     T, E, k = plan.T, plan.E, plan.k
-    _need(probs, "probs", (T, E), torch.float32); _need(topk_idx, "topk_idx", (T, k), torch.int32)
+    _need(probs, "probs", (T, E), torch.float32); _need(topk_idx, "topk_idx", (T, plan.slots), torch.int32)
     _need(real_mask, "real_mask", (T,), torch.int32)
     _need(f, "f", (E,), torch.float32); _need(p_mean, "p_mean", (E,), torch.float32)
     _need(real_counts, "real_counts", (E + 1,), torch.int32)

@@ -28,7 +28,8 @@ const char* kKernelNames =
     "gemm_down_dgrad_swiglu,gemm_wgrad_down,gemm_gate_up_dgrad,gemm_wgrad_gate_up,"
     "gemm_down_dgrad_swiglu_shared,gemm_wgrad_down_shared,gemm_wgrad_gate_up_shared,"
     "gemm_gate_up_dgrad_shared,stack_router,gemm_router_dx,unpermute,gemm_wgrad_router,router_reduce,aux,"
-    "wgrad_reduce,mx_quantize,router_bwd_small,balance_update,sinkhorn_rows,sinkhorn_cols,sinkhorn_select";
+    "wgrad_reduce,mx_quantize,router_bwd_small,balance_update,sinkhorn_rows,sinkhorn_cols,sinkhorn_select,"
+    "expert_choice";
 
 }  // namespace
 
@@ -37,6 +38,7 @@ struct moe_plan_s {
   int dt;
   int64_t T, A;
   int d, E, k, I, Ns, Is, Ep;
+  int kf;                  // top_k: T kf routed rows (at most) and the f_e denominator
   int nblk_hist, nblk_dz, nblk_aux, router_splits;
   // GEMM tile per call site, chosen once at plan time
   int t_gu, t_down, t_gu_s, t_down_s, t_down_dgrad, t_gu_dgrad, t_down_dgrad_s, t_gu_dgrad_s, t_router_dx;
@@ -46,7 +48,7 @@ struct moe_plan_s {
   // workspace regions (byte offsets)
   size_t o_block_counts, o_block_base, o_dy_perm, o_g, o_dzhl, o_w2, o_dgu, o_dx_perm, o_dgu_s,
       o_dxs, o_dxr, o_dwr_part, o_dbias_part, o_aux_part, o_wg_part, o_wsorted, o_gpart, o_wh, o_dgu_lo,
-      o_wh_lo, o_sk_part, ws_total;
+      o_wh_lo, o_sk_part, o_ec_pt, ws_total;
   // bf16 experts seeing few tokens each: the expert weight gradients add the
   // products of the rounding remainders of [dG | dU] and of w H (see run_wgrad)
   bool comp = false;
@@ -307,8 +309,12 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
   if (c.act_dtype < MOE_F32 || c.act_dtype > MOE_MXFP8_E4M3) return MOE_ERR_INVALID;
   if (c.expert_dtype < MOE_F32 || c.expert_dtype > MOE_MXFP8_E4M3) return MOE_ERR_INVALID;
   if (!(c.aux_coef == c.aux_coef)) return MOE_ERR_INVALID;  // NaN
-  if (c.router != MOE_ROUTER_SOFTMAX && c.router != MOE_ROUTER_RELU) return MOE_ERR_INVALID;
-  if (c.router == MOE_ROUTER_RELU && c.renorm) return MOE_ERR_INVALID;   // ReLU gates are the weights
+  if (c.router != MOE_ROUTER_SOFTMAX && c.router != MOE_ROUTER_RELU && c.router != MOE_ROUTER_EXPERT_CHOICE)
+    return MOE_ERR_INVALID;
+  // ReLU gates and expert-choice probabilities are the weights themselves
+  if (c.router != MOE_ROUTER_SOFTMAX && c.renorm) return MOE_ERR_INVALID;
+  // expert choice: one routing slot per expert, E <= 64 slots
+  if (c.router == MOE_ROUTER_EXPERT_CHOICE && c.n_experts > 64) return MOE_ERR_UNSUPPORTED;
   if (c.act_dtype == MOE_MXFP8_E4M3) return MOE_ERR_UNSUPPORTED;
   const bool mx = c.expert_dtype == MOE_MXFP8_E4M3;
   if (mx && c.act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;   // MX GEMMs write bf16
@@ -330,7 +336,9 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
   p->A = A;
   p->d = c.d_model;
   p->E = c.n_experts;
-  p->k = c.top_k;
+  // routing slots per token: top_k, or every expert's slot for expert choice
+  p->k = c.router == MOE_ROUTER_EXPERT_CHOICE ? c.n_experts : c.top_k;
+  p->kf = c.top_k;
   p->I = c.d_ff;
   p->Ns = c.n_shared;
   p->Is = c.n_shared > 0 ? c.d_ff_shared : 0;
@@ -419,6 +427,8 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
   p->o_dgu_lo = take(p->comp ? (size_t)A * 2 * p->I * es : 0);
   // Sinkhorn router: column partials of its token blocks
   p->o_sk_part = take((size_t)((p->T + kSinkhornTokens - 1) / kSinkhornTokens) * p->E * 4);
+  // expert choice: the transposed probabilities
+  p->o_ec_pt = take(c.router == MOE_ROUTER_EXPERT_CHOICE ? (size_t)p->T * p->E * 4 : 0);
   p->o_wh_lo = take(p->comp ? (size_t)A * p->I * es : 0);
   // input-gradient rows of the experts, f32 in a bf16 layer (f32_intermediates)
   const size_t xs = f32_intermediates(p->dt, p->mx) ? 4 : es;
@@ -587,6 +597,7 @@ moe_status moe_route(moe_plan p, const void* x, const void* w_router, const floa
   if (!x || !w_router || !probs || !topk_idx || !topk_w) return MOE_ERR_NULL;
   if (p->cfg.has_router_bias && !bias) return MOE_ERR_NULL;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p->cfg.router == MOE_ROUTER_EXPERT_CHOICE) return MOE_ERR_INVALID;   // moe_route_expert_choice
   RouteArgs a{x, w_router, p->cfg.has_router_bias ? bias : nullptr, probs, topk_idx, topk_w,
               p->T, p->d, p->E, p->k, p->cfg.renorm};
   a.relu = p->cfg.router == MOE_ROUTER_RELU;
@@ -594,10 +605,35 @@ moe_status moe_route(moe_plan p, const void* x, const void* w_router, const floa
   return hip_status(launch_route(p->dt, a, s));
 }
 
+moe_status moe_route_expert_choice(moe_plan p, const void* x, const void* w_router, const float* bias,
+                                   float* probs, int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  if (!p) return MOE_ERR_NULL;
+  if (p->cfg.router != MOE_ROUTER_EXPERT_CHOICE) return MOE_ERR_INVALID;
+  if (p->T == 0) return MOE_OK;
+  if (!x || !w_router || !probs || !topk_idx || !topk_w) return MOE_ERR_NULL;
+  if (p->cfg.has_router_bias && !bias) return MOE_ERR_NULL;
+  moe_status st = check_ws(p, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  {
+    // the probabilities (the plain top-1 this writes into the slots is
+    // overwritten by the experts' choice)
+    RouteArgs a{x, w_router, p->cfg.has_router_bias ? bias : nullptr, probs, topk_idx, topk_w,
+                p->T, p->d, p->E, 1, 0};
+    Probe pr(p, "route", s);
+    MOE_TRY(launch_route(p->dt, a, s));
+  }
+  ExpertChoiceArgs b{probs, reinterpret_cast<float*>(wsp(ws, p->o_ec_pt)), topk_idx, topk_w, p->T, p->E,
+                     p->T * p->kf / p->E};
+  Probe pr(p, "expert_choice", s);
+  return hip_status(launch_expert_choice(b, s));
+}
+
 moe_status moe_route_balanced(moe_plan p, const void* x, const void* w_router, const float* bias,
                               const float* sel_bias, float* probs, int32_t* topk_idx, float* topk_w, void* stream) {
   if (!p) return MOE_ERR_NULL;
-  if (p->cfg.router != MOE_ROUTER_SOFTMAX) return MOE_ERR_INVALID;   // ranks on probabilities
+  if (p->cfg.router != MOE_ROUTER_SOFTMAX) return MOE_ERR_INVALID;   // ranks on probabilities (top-k)
   if (p->T == 0) return MOE_OK;
   if (!x || !w_router || !sel_bias || !probs || !topk_idx || !topk_w) return MOE_ERR_NULL;
   if (p->cfg.has_router_bias && !bias) return MOE_ERR_NULL;
@@ -643,6 +679,7 @@ moe_status moe_route_sinkhorn(moe_plan p, const void* x, const void* w_router, c
 
 moe_status moe_balance_update(moe_plan p, const int32_t* counts, float* sel_bias, float gamma, void* stream) {
   if (!p) return MOE_ERR_NULL;
+  if (p->cfg.router != MOE_ROUTER_SOFTMAX) return MOE_ERR_INVALID;  // the balanced top-k router's update
   if (!counts || !sel_bias) return MOE_ERR_NULL;
   if (!(gamma >= 0.0f) || !(gamma < INFINITY)) return MOE_ERR_INVALID;   // also rejects NaN
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1171,6 +1208,7 @@ moe_status moe_aux_stats(moe_plan p, const float* probs, const int32_t* counts, 
   if (st != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   AuxArgs a{probs, counts, f, p_mean, out, reinterpret_cast<float*>(wsp(ws, p->o_aux_part)), p->T, p->E, p->k};
+  a.kf = p->kf;
   Probe pr(p, "aux", s);
   return hip_status(launch_aux(a, s));
 }
@@ -1187,6 +1225,7 @@ moe_status moe_aux_stats_masked(moe_plan p, const float* probs, const int32_t* t
   float* part = reinterpret_cast<float*>(wsp(ws, p->o_aux_part));
   const int nb = p->nblk_aux > 0 ? p->nblk_aux : 1;
   AuxArgs a{probs, nullptr, f, p_mean, out, part, p->T, p->E, p->k};
+  a.kf = p->kf;
   a.mask = real_mask;
   a.idx = topk_idx;
   a.rcounts = real_counts;

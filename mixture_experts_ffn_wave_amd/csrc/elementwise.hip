@@ -822,7 +822,7 @@ __global__ void __launch_bounds__(NT) aux_finalize_kernel(AuxArgs a, int nblk) {
   const float ps = valid ? colp[e] : 0.0f, ent = valid ? cole[e] : 0.0f;
   const double T = a.mask ? (double)s_real : (double)a.T;
   const double cnt = valid ? (double)(a.mask ? a.rcounts[e] : a.counts[e]) : 0.0;
-  const double f = (T > 0) ? cnt / (T * a.k) : 0.0;
+  const double f = (T > 0) ? cnt / (T * (a.kf ? a.kf : a.k)) : 0.0;
   const double P = (T > 0) ? (double)ps / T : 0.0;
   if (valid) {
     a.f[e] = (float)f;

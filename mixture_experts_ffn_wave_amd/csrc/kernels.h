@@ -43,6 +43,17 @@ struct SinkhornArgs {
 hipError_t launch_sinkhorn_rows(const SinkhornArgs& a, bool first, hipStream_t s);
 hipError_t launch_sinkhorn_cols(const SinkhornArgs& a, hipStream_t s);
 hipError_t launch_sinkhorn_select(const SinkhornArgs& a, hipStream_t s);
+
+// Expert-choice router over the saved probabilities [T, E] (E <= 64): every
+// expert takes the C tokens with the largest probs[t, e] (lower token index
+// first on ties), found by a radix select on the f32 bit patterns of its
+// column; written as [T, E] slots (idx[t, e] = e or -1, wts = the taken
+// probabilities or 0).  pT: [E, T] f32 workspace (the transposed probabilities).
+struct ExpertChoiceArgs {
+  const float* probs; float* pT; int32_t* idx; float* wts;
+  int64_t T; int E; int64_t C;
+};
+hipError_t launch_expert_choice(const ExpertChoiceArgs& a, hipStream_t s);
 // sel_bias[e] += gamma * sign(T k - E counts[e]) (aux-loss-free balancing update), E <= 256
 hipError_t launch_balance_update(const int32_t* counts, float* sel_bias, int64_t T, int E, int k, float gamma,
                                  hipStream_t s);
@@ -298,7 +309,8 @@ struct moe_aux_out {
 struct AuxArgs {
   const float* probs; const int32_t* counts; float* f; float* p_mean; void* out;
   float* part;           // ws [nblk, 2, E]
-  int64_t T; int E, k;
+  int64_t T; int E, k;    // k: routing slots per token (idx [T, k])
+  int kf = 0;             // k of f_e = count_e / (T kf); 0: kf = k (expert choice: the capacity factor)
   // statistic over real tokens only (mask [T], 0 = filler): counts are then
   // taken from idx [T, k] under the mask into rcounts [E + 1] (number of real
   // tokens at [E]), with per-block integer partials in cpart [nblk, E + 1]

@@ -747,6 +747,95 @@ __global__ void __launch_bounds__(256) sinkhorn_select_kernel(SinkhornArgs a) {
     for (int j = 0; j < a.k; ++j) a.wts[t * a.k + j] = a.wts[t * a.k + j] / psum;
 }
 
+// ---- Expert-choice router (KohakUwULLM README, "Key features": expert-choice
+// routers beside the default; the published method: every expert takes its C
+// tokens of largest probability).
+constexpr int EC_T = 64;                           // tokens per transpose tile
+
+// probs [T, E] -> pT [E, T] through LDS (reads and writes along rows).
+__global__ void __launch_bounds__(256) ec_transpose_kernel(ExpertChoiceArgs a) {
+  __shared__ float tile[EC_T][65];
+  const int E = a.E;
+  const int64_t t0 = (int64_t)blockIdx.x * EC_T;
+  const int nt = (a.T - t0) < EC_T ? (int)(a.T - t0) : EC_T;
+  for (int i = threadIdx.x; i < nt * E; i += 256) {
+    const int t = i / E, e = i - t * E;
+    tile[t][e] = a.probs[(t0 + t) * E + e];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nt * E; i += 256) {
+    const int e = i / nt, t = i - e * nt;
+    a.pT[(int64_t)e * a.T + t0 + t] = tile[t][e];
+  }
+}
+
+// One workgroup per expert.  Probabilities are non-negative, so their f32
+// bit patterns order as unsigned integers: four 8-bit radix passes find the
+// pattern K of the C-th largest value and how many tokens equal to K are
+// taken (the rest of the C are above K); a last pass in token order takes the
+// tokens above K and the first of those equal to K (a block prefix count).
+__global__ void __launch_bounds__(256) expert_choice_kernel(ExpertChoiceArgs a) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t s_key, s_wave[4];
+  __shared__ long long s_need;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e = blockIdx.x, E = a.E;
+  const float* col = a.pT + (int64_t)e * a.T;
+  uint32_t prefix = 0u, mask = 0u;
+  long long need = a.C;                            // tokens still to take at or below the prefix
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[tid] = 0u;
+    __syncthreads();
+    for (int64_t t = tid; t < a.T; t += 256) {
+      const uint32_t key = __float_as_uint(col[t]);
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      long long above = 0;
+      int dsel = 0;
+      for (int dg = 255; dg >= 0; --dg) {
+        if (above + (long long)hist[dg] >= need) { dsel = dg; break; }
+        above += hist[dg];
+      }
+      s_key = prefix | ((uint32_t)dsel << shift);
+      s_need = need - above;
+    }
+    __syncthreads();
+    prefix = s_key;
+    need = s_need;
+    mask |= 0xFFu << shift;
+    __syncthreads();
+  }
+  // prefix = K; take key > K, and the first `need` tokens with key == K
+  long long base = 0;                              // tokens equal to K before this chunk
+  for (int64_t c0 = 0; c0 < a.T; c0 += 256) {
+    const int64_t t = c0 + tid;
+    const bool tv = t < a.T;
+    const float pv = tv ? col[t] : 0.0f;
+    const uint32_t key = __float_as_uint(pv);
+    const bool eq = tv && key == prefix;
+    // exclusive prefix count of eq over the chunk: within the wave, then waves in order
+    const unsigned long long bal = __ballot(eq);
+    const uint32_t below = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) s_wave[wave] = __popcll(bal);
+    __syncthreads();
+    uint32_t before = 0u, total = 0u;
+    for (int w = 0; w < 4; ++w) {
+      before += (w < wave) ? s_wave[w] : 0u;
+      total += s_wave[w];
+    }
+    const long long rank = base + before + below;
+    const bool take = tv && (key > prefix || (eq && rank < need));
+    if (tv) {
+      a.idx[t * E + e] = take ? e : -1;
+      a.wts[t * E + e] = take ? pv : 0.0f;
+    }
+    base += total;
+    __syncthreads();                               // s_wave reused by the next chunk
+  }
+}
+
 }  // namespace
 
 hipError_t launch_balance_update(const int32_t* counts, float* sel_bias, int64_t T, int E, int k, float gamma,
@@ -776,6 +865,16 @@ hipError_t launch_sinkhorn_select(const SinkhornArgs& a, hipStream_t s) {
   if (grid == 0) return hipSuccess;
   if (a.E < 1 || a.E > SK_EMAX || a.k < 1 || a.k > 64) return hipErrorInvalidValue;
   hipLaunchKernelGGL(sinkhorn_select_kernel, dim3((unsigned)grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_choice(const ExpertChoiceArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  if (a.E < 1 || a.E > 64 || a.C < 0 || a.C > a.T) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(ec_transpose_kernel, dim3((unsigned)((a.T + EC_T - 1) / EC_T)), dim3(256), 0, s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(expert_choice_kernel, dim3((unsigned)a.E), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -18,8 +18,8 @@ class MoELayer:
         T, d, E, k, I, A = p.T, p.d, p.E, p.k, p.I, p.T * p.k
         z = lambda *s, dtype=dt: torch.empty(*s, dtype=dtype, device=dev)
         self.probs = z(T, E, dtype=torch.float32)
-        self.topk_idx = z(T, k, dtype=torch.int32)
-        self.topk_w = z(T, k, dtype=torch.float32)
+        self.topk_idx = z(T, p.slots, dtype=torch.int32)      # [T, slots]: slots = E for expert choice
+        self.topk_w = z(T, p.slots, dtype=torch.float32)
         self.counts = z(E, dtype=torch.int32)
         self.offsets = z(E + 1, dtype=torch.int32)
         self.perm_token = z(A, dtype=torch.int32)
@@ -31,7 +31,7 @@ class MoELayer:
         # the x_perm path, or a caller that inspects it (write_x_perm = True);
         # on the gather path it is allocated on first use
         self.write_x_perm = False
-        self.inv_perm = z(T, k, dtype=torch.int32)
+        self.inv_perm = z(T, p.slots, dtype=torch.int32)
         self._x_perm = None if self.mx_gather else z(A, d)
         self.gu = z(A, 2 * I, dtype=p.gu_dtype)
         self.h = z(A, I)
@@ -105,7 +105,10 @@ class MoELayer:
 
     def route(self, stream=None):
         q = self.params
-        if self.sinkhorn_iters > 0:
+        if self.plan.router == "expert_choice":
+            L.moe_route_expert_choice(self.plan, q["x"], q["w_router"], q["bias"], self.probs, self.topk_idx,
+                                      self.topk_w, self.ws, stream)
+        elif self.sinkhorn_iters > 0:
             L.moe_route_sinkhorn(self.plan, q["x"], q["w_router"], q["bias"], self.sinkhorn_iters, self.probs,
                                  self.topk_idx, self.topk_w, self.sinkhorn_b, self.ws, stream)
         elif self.sel_bias is not None:

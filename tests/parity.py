@@ -221,6 +221,8 @@ def compare_routing(wl, gpu, fwd):
     eps = TIE_EPS
     if wl.router == "relu":
         return _compare_relu_routing(wl, gpu, fwd)
+    if wl.router == "expert_choice":
+        return _compare_expert_choice_routing(wl, gpu, fwd)
     if fwd.get("sinkhorn_b") is not None:
         # Sinkhorn router: scales first, then ranks on ln(p b)
         if "sinkhorn_b" in gpu:
@@ -282,6 +284,33 @@ def _compare_relu_routing(wl, gpu, fwd):
     if same.any():
         w = fwd["w"][same]
         assert np.max(np.abs(gpu["topk_w"][same] - w) / np.maximum(1.0, np.abs(w))) <= RELU_ATOL, "ReLU weights"
+    return bool(same.all())
+
+
+def _compare_expert_choice_routing(wl, gpu, fwd):
+    """Expert choice: probabilities within PROB_ATOL; every expert takes
+    exactly C tokens; the [T, E] slots bit-exact except tokens whose
+    probability for some expert lies within TIE_EPS of that expert's C-th
+    largest (the expert's choice is decided by a near-tie there): their
+    slots must still be a valid choice within that margin."""
+    p, T, E = fwd["p"], wl.T, wl.E
+    C = (T * wl.k) // E
+    assert np.max(np.abs(gpu["probs"] - p)) <= PROB_ATOL, "router probabilities"
+    gi = gpu["topk_idx"]
+    assert gi.shape == (T, E)
+    assert np.all((gi == np.arange(E)[None, :]) | (gi == -1)), "slot e holds e or -1"
+    assert np.all((gi >= 0).sum(axis=0) == C), "every expert takes C tokens"
+    same = np.all(gi == fwd["idx"], axis=1)
+    srt = -np.sort(-p, axis=0)
+    thr = srt[C - 1] if C > 0 else np.full(E, np.inf)
+    tie = (np.abs(p - thr[None, :]) < TIE_EPS).any(axis=1)
+    bad = ~same & ~tie
+    assert not bad.any(), f"expert choice differs on {int(bad.sum())} non-tied tokens, e.g. {np.where(bad)[0][:5]}"
+    taken = gi >= 0
+    assert np.all(p[taken] >= np.broadcast_to(thr, p.shape)[taken] - TIE_EPS), "a taken token below the C-th"
+    assert np.all(p[~taken] <= np.broadcast_to(thr, p.shape)[~taken] + TIE_EPS), "a left token above the C-th"
+    if same.any():
+        assert np.max(np.abs(gpu["topk_w"][same] - fwd["w"][same])) <= PROB_ATOL, "routing weights"
     return bool(same.all())
 
 

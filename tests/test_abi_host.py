@@ -105,7 +105,10 @@ def _create(**kw):
     (dict(expert_dtype=L.MOE_MXFP8_E4M3, n_shared=2, d_ff_shared=256), MOE_OK),
     (dict(router=1, renorm=0), MOE_OK),                     # ReLU router
     (dict(router=1, renorm=1), MOE_ERR_INVALID),            # its gates are the weights
-    (dict(router=2, renorm=0), MOE_ERR_INVALID),
+    (dict(router=2, renorm=0), MOE_OK),                     # expert choice
+    (dict(router=2, renorm=1), MOE_ERR_INVALID),
+    (dict(router=2, renorm=0, n_experts=128), MOE_ERR_UNSUPPORTED),   # one slot per expert, at most 64
+    (dict(router=3, renorm=0), MOE_ERR_INVALID),
 ])
 def test_plan_validation(kw, status):
     st, h = _create(**kw)
@@ -331,3 +334,16 @@ def test_probability_router_variants_refuse_a_relu_plan():
     assert lib.moe_route_balanced(p.handle, fake, fake, None, fake, fake, fake, fake, None) == MOE_ERR_INVALID
     assert lib.moe_route_sinkhorn(p.handle, fake, fake, None, 4, fake, fake, fake, fake, fake,
                                   p.workspace_bytes(), None) == MOE_ERR_INVALID
+
+
+def test_expert_choice_has_its_own_entry_point():
+    lib = L.lib()
+    fake = ctypes.c_void_p(0x1000)
+    ec = L.Plan(512, 128, 8, 2, 128, dtype=L.torch.bfloat16, renorm=False, router="expert_choice")
+    assert ec.slots == 8
+    assert lib.moe_route(ec.handle, fake, fake, None, fake, fake, fake, None) == MOE_ERR_INVALID
+    sm = L.Plan(512, 128, 8, 2, 128, dtype=L.torch.bfloat16)
+    assert lib.moe_route_expert_choice(sm.handle, fake, fake, None, fake, fake, fake, fake, sm.workspace_bytes(),
+                                       None) == MOE_ERR_INVALID
+    assert lib.moe_route_expert_choice(ec.handle, fake, fake, None, fake, fake, fake, fake, ec.workspace_bytes() - 1,
+                                       None) == MOE_ERR_WORKSPACE

@@ -94,3 +94,29 @@ def test_relu_router_layer_matches_oracle(wl, bias):
     empty = int((fwd["idx"] < 0).sum())
     PT.say(f"[relu] {wl.name}: {empty} empty slots of {wl.T * wl.k}, {int(fwd['offsets'][-1])} rows")
     assert empty > 0                                 # the case of fewer than k positive logits is exercised
+
+
+# Expert-choice router (MOE_ROUTER_EXPERT_CHOICE, moe_route_expert_choice):
+# every expert takes its C = T k / E tokens of largest probability; [T, E]
+# slots; the whole layer against the exact oracle on both router-backward
+# engines (E <= 16: the fused per-block kernel; 64: dz kernel + MFMA products).
+EXPERT_CHOICE = [
+    W("t1000_d256_e4k2_i128_bf16_ec", T=1000, d=256, E=4, k=2, I=128, renorm=False, router="expert_choice"),
+    W("t777_d128_e8k2_i256_f16_ec_shared1", T=777, d=128, E=8, k=2, I=256, renorm=False, router="expert_choice",
+      n_shared=1, I_shared=128, dtype="f16"),
+    # (uniform router: with a Zipf-skewed one some tokens are taken by up to
+    # 17 experts, y's largest elements sit 16 RMS out, and the bf16 rounding
+    # of H alone, the down GEMM's operand, puts y 0.030 RMS past the bar)
+    W("t1536_d256_e64k4_i128_bf16_ec", T=1536, d=256, E=64, k=4, I=128, renorm=False, router="expert_choice"),
+    W("t513_d128_e16k3_i128_f32_ec", T=513, d=128, E=16, k=3, I=128, renorm=False, router="expert_choice",
+      dtype="f32"),
+]
+
+
+@pytest.mark.parametrize("wl", EXPERT_CHOICE, ids=[w.name for w in EXPERT_CHOICE])
+def test_expert_choice_layer_matches_oracle(wl):
+    gpu, fwd, _, _ = PT.full_parity(wl)
+    per_token = (fwd["idx"] >= 0).sum(axis=1)
+    PT.say(f"[expert-choice] {wl.name}: C={(wl.T * wl.k) // wl.E}, experts per token "
+           f"{per_token.min()}..{per_token.max()}, tokens with none {int((per_token == 0).sum())}")
+    assert np.array_equal(fwd["counts"], np.full(wl.E, (wl.T * wl.k) // wl.E))
