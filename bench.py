@@ -127,17 +127,24 @@ def traffic_per_launch(wl, probe_name):
     """HBM bytes per launch of one kernel from profiles/traffic_<workload>.md,
     or None (no summary, other sources, or no unique kernel row)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.md")
-    sym = KERNEL_SYMBOL.get(probe_name)
+    sym = KERNEL_SYMBOL.get(probe_name[:-len("_shared")] if probe_name.endswith("_shared") else probe_name)
     if sym is None or not os.path.exists(path):
         return None
     text = open(path).read()
     m = re.search(r"source sha256: `([0-9a-f]{64})`", text)
     if not m or m.group(1) != kernel_source_hash():
         return None
-    pat = re.compile(r"^\| `(" + re.escape(sym) + r"_" + wl.dtype + r"_\d+x\d+)` \|[^|]*\|[^|]*\|[^|]*\| *([0-9.]+) *\|",
-                     re.M)
+    # a row is a call site: the kernel symbol (dtype, tile, "pp" for the
+    # ping-pong tiles), and "(routed)" / "(shared)" where one symbol ran with
+    # both the routed and the shared experts' grids
+    pat = re.compile(r"^\| `" + re.escape(sym) + r"_" + wl.dtype + r"_\d+x\d+(?:pp)?(?: \((\w+)\))?` \|"
+                     r"[^|]*\|[^|]*\|[^|]*\| *([0-9.]+) *\|", re.M)
     rows = pat.findall(text)
-    return float(rows[0][1]) if len(rows) == 1 else None
+    site = "shared" if probe_name.endswith("_shared") else "routed"
+    labelled = [v for lab, v in rows if lab == site]
+    plain = [v for lab, v in rows if not lab]
+    pick = labelled if labelled else plain
+    return float(pick[0]) if len(pick) == 1 else None
 
 
 def traffic_calibration():
