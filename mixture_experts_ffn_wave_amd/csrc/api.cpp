@@ -167,41 +167,28 @@ int choose_row_tile(int dt, int ncols, int block_align, int64_t tiles256, int K,
   if (tiles256 / 2 >= kPPTileMin || (tiles256 / 2 >= kPPTileMinLongK && K >= kPPLongK)) return TILE_256PP;
   return tiles256 >= kWideTileMin ? TILE_128x256 : TILE_128;
 }
-// Weight-gradient GEMMs: 256 x 256 stages twice the FLOP per operand byte of
-// 128 x 128 but yields a quarter of the workgroups; estimated time = rounds of
-// workgroups over the CUs x the time of one tile, the smaller tile costed at
-// about 0.55 of the larger one's rate.  The 256 x 256 tile runs the ping-pong
-// main loop (measured 6-15 % faster than the 8-wave lockstep loop at the
-// large-expert and skewed workloads); the lockstep one only on request.
-int choose_wgrad_tile(int dt, double segs, int M, int N, double ktok, int override_tile) {
-  if (dt == DT_F32) return 128;
-  if (M % 256 || N % 256) return 128;
-  if (override_tile) return override_tile;
-  const double w256 = segs * (M / 256) * (N / 256), w128 = segs * (M / 128) * (N / 128);
-  const double c256 = std::ceil(w256 / kCUs) * 256.0 * 256.0 * ktok;          // whole rounds
-  const double c128 = std::ceil(w128 / kCUs) * 128.0 * 128.0 * ktok / 0.55;
-  return c256 <= c128 ? TILE_256PP : 128;
-}
-
-// Split-K factor of a weight-gradient GEMM with W = G (M/bt)(N/bt) output
-// tiles (bt = 128 or 256).  The f32 partials of a split are summed in order by
-// one extra pass; every split keeps at least 512 tokens per group.
+// Weight-gradient GEMMs: W = G (M/bt)(N/bt) output tiles of bt x bt (bt =
+// 128 or 256) over `ktok` tokens per group, optionally split s ways over the
+// tokens into f32 partials that one extra pass sums in order; every split
+// keeps at least 512 tokens per group.
 //   128 x 128 tiles (several workgroups per CU): fewer than 384 tiles leave
 //   CUs with one workgroup or none, so the token range is split until about
 //   512 workgroups run (at most 4 ways);
 //   256 x 256 tiles (one workgroup per CU): the split s (up to 8) minimises
-//   rounds(W s over the CUs) / s times the time of one unsplit tile, plus the
-//   partials' traffic (s W 256^2 f32 written and read back), the tile time
-//   taken at ~6.5 TFLOP/s per CU and the traffic at ~5 TB/s.
-// MOE_WGRAD_SPLITS (1..8) forces a value.
-int choose_wgrad_splits(int tile, int G, int M, int N, double tokens_per_group) {
-  const char* v = std::getenv("MOE_WGRAD_SPLITS");
-  if (v) {
-    const int s = std::atoi(v);
-    if (s >= 1 && s <= 8) return s;
-  }
-  const int bt = tile_rows(tile);
-  const int64_t W = (int64_t)G * (M / bt) * (N / bt);
+//   the estimated time below.
+// Estimated time = rounds of W s workgroups over the CUs x the time of one
+// tile / s, plus the partials' traffic (s W bt^2 f32 written and read back at
+// ~5 TB/s); a 256 x 256 tile taken at ~6.5 TFLOP/s per CU, the 128 x 128 one
+// at 0.55 of that.  The tile with the smaller estimate (each at its split)
+// runs; 256 x 256 uses the ping-pong main loop (measured 6-15 % faster than
+// the 8-wave lockstep loop at the large-expert and skewed workloads), the
+// lockstep one only on request.  MOE_WGRAD_SPLITS (1..8) forces a split.
+double wgrad_seconds(int bt, int64_t W, double ktok, int s) {
+  const double tile_s = 2.0 * bt * bt * ktok / (bt == 256 ? 6.5e12 : 6.5e12 * 0.55);
+  const double rounds = (double)((W * s + kCUs - 1) / kCUs);
+  return rounds * tile_s / s + (s > 1 ? 2.0 * s * (double)W * bt * bt * 4 / 5e12 : 0.0);
+}
+int best_wgrad_splits(int bt, int64_t W, double tokens_per_group) {
   if (W <= 0) return 1;
   if (bt == 128) {
     if (W >= 384) return 1;
@@ -210,16 +197,32 @@ int choose_wgrad_splits(int tile, int G, int M, int N, double tokens_per_group) 
     while (s > 1 && tokens_per_group / s < 512) --s;
     return s < 1 ? 1 : s;
   }
-  const double tile_s = 2.0 * bt * bt * tokens_per_group / 6.5e12;
   int best = 1;
   double best_t = 1e30;
   for (int s = 1; s <= 8; ++s) {
     if (s > 1 && tokens_per_group / s < 512) break;
-    const double rounds = (double)((W * s + kCUs - 1) / kCUs);
-    const double t = rounds * tile_s / s + (s > 1 ? 2.0 * s * (double)W * bt * bt * 4 / 5e12 : 0.0);
+    const double t = wgrad_seconds(bt, W, tokens_per_group, s);
     if (t < best_t) { best_t = t; best = s; }
   }
   return best;
+}
+int choose_wgrad_tile(int dt, double segs, int M, int N, double ktok, int override_tile) {
+  if (dt == DT_F32) return 128;
+  if (M % 256 || N % 256) return 128;
+  if (override_tile) return override_tile;
+  const int64_t w256 = (int64_t)segs * (M / 256) * (N / 256), w128 = (int64_t)segs * (M / 128) * (N / 128);
+  const double t256 = wgrad_seconds(256, w256, ktok, best_wgrad_splits(256, w256, ktok));
+  const double t128 = wgrad_seconds(128, w128, ktok, best_wgrad_splits(128, w128, ktok));
+  return t256 <= t128 ? TILE_256PP : 128;
+}
+int choose_wgrad_splits(int tile, int G, int M, int N, double tokens_per_group) {
+  const char* v = std::getenv("MOE_WGRAD_SPLITS");
+  if (v) {
+    const int s = std::atoi(v);
+    if (s >= 1 && s <= 8) return s;
+  }
+  const int bt = tile_rows(tile);
+  return best_wgrad_splits(bt, (int64_t)G * (M / bt) * (N / bt), tokens_per_group);
 }
 
 }  // namespace
