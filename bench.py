@@ -137,7 +137,7 @@ def traffic_per_launch(wl, probe_name):
     # a row is a call site: the kernel symbol (dtype, tile, "pp" for the
     # ping-pong tiles), and "(routed)" / "(shared)" where one symbol ran with
     # both the routed and the shared experts' grids
-    pat = re.compile(r"^\| `" + re.escape(sym) + r"_" + wl.dtype + r"_\d+x\d+(?:pp)?(?: \((\w+)\))?` \|"
+    pat = re.compile(r"^\| `" + re.escape(sym) + r"(?:_f32out)?_" + wl.dtype + r"_\d+x\d+(?:pp)?(?: \((\w+)\))?` \|"
                      r"[^|]*\|[^|]*\|[^|]*\| *([0-9.]+) *\|", re.M)
     rows = pat.findall(text)
     site = "shared" if probe_name.endswith("_shared") else "routed"
