@@ -760,7 +760,14 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
   // still three workgroups per CU); each later pass's rows are loaded while
   // the previous pass computes.
   constexpr bool GU_PRE = PERM && !GUF32 && EPI == EPI_SWIGLU_BWD && BM == 128 && BN == 128;
-  u32x4 gun[2][PERM ? SITER : 1];                           // (unused unless GU_PRE)
+  // Ping-pong tiles (one workgroup per CU, nothing else to hide a pass's
+  // G/U load behind): the first pass's rows are loaded during the last two
+  // chunks of the main loop and each later pass's rows while the previous
+  // pass computes and stores (32 more VGPRs, within the 256 that two waves
+  // per SIMD allow).
+  constexpr bool GU_PIPE = PERM && !GUF32 && EPI == EPI_SWIGLU_BWD && PP;
+  u32x4 gun[2][PERM ? SITER : 1];                           // (unused unless GU_PRE or GU_PIPE)
+  bool gu_first = false;                                    // GU_PIPE: the first pass's rows are in gun
   // The last two chunks of a ring main loop, with the first pass's G/U loads
   // issued after every chunk's loads (so a vmcnt of 2 SITER before the last
   // chunk still means that chunk has landed).
@@ -969,12 +976,30 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
     phase_barrier();
     if (grp == 1) phase_barrier();                  // one phase behind group 0
     u32x4 fa[KSTEPS][NS], fb[KSTEPS][MS];
+    // SwiGLU backward: the first epilogue pass's G/U rows are loaded in the
+    // last-but-one chunk, after the ring's last loads, so the wait for the
+    // last chunk allows those 2 SITER loads to stay in flight
+    const int gu_at = nkd >= 2 ? nkd - 2 : 0;
     for (int c = 0; c < nkd; ++c) {
       const char* buf = smem + (c % NSTG) * DSTAGE;
       read_chunk_frags<PD, QD, NS, MS, KSTEPS>(fa, fb, buf + PD::BYTES, buf, qrow, prow, lane);
       if (c + NSTG - 1 < nkd) issue_half(c + NSTG - 1);
+      if constexpr (GU_PIPE) {
+        if (c == gu_at) {
+          asm volatile("" ::: "memory");
+          load_gu_rows(gun, 0);
+          gu_first = true;
+        }
+      }
       __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0): fragments in registers, slot read
-      if (c + 1 < nkd) wait_chunk(c + 1, nkd);
+      if (c + 1 < nkd) {
+        if (GU_PIPE && c == gu_at) {
+          asm volatile("" ::: "memory");
+          wait_vmcnt<2 * SITER>();                   // chunk c + 1 = the last; only G/U after it
+        } else {
+          wait_chunk(c + 1, nkd);
+        }
+      }
       phase_barrier();
       __builtin_amdgcn_s_setprio(1);
       mfma_chunk_frags<T, NS, MS, KSTEPS>(acc, fa, fb);
@@ -1171,7 +1196,10 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
         if (a.wrow && tr_l < rows) wrow_l = a.wrow[row0 + tr_l];
       }
       if constexpr (EPI == EPI_SWIGLU_BWD && !GUF32) {
-        if constexpr (GU_PRE) {
+        if constexpr (GU_PRE || GU_PIPE) {
+          if constexpr (GU_PIPE) {
+            if (ms == 0 && !gu_first) load_gu_rows(gun, 0);
+          }
 #pragma unroll
           for (int i = 0; i < SITER; ++i) {
             const int q = tid + 64 * NW * i, sr = q / CPR, c = q % CPR;
