@@ -1183,6 +1183,28 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
       return smem + arr * SR * RB + sr * RB + ((c ^ (sr & 7)) << 4);
     };
     const int sr_l = wm * 32 + (lane & 31);                   // this lane's staged row
+    // f32 G, U of the SwiGLU backward: this lane's row pieces of column
+    // subtile ns, loaded one subtile ahead of the one being computed; in
+    // ping-pong tiles also the next pass's first subtile during this pass's
+    // last one (NS is even, so that subtile computes from gub[1] while gub[0]
+    // fills; the smaller tiles would spill the registers it keeps live)
+    constexpr bool GU_DIRECT = GUF32 && EPI == EPI_SWIGLU_BWD;
+    static_assert(!GU_DIRECT || NS % 2 == 0, "G/U double buffer alternates over an even subtile count");
+    float gub[2][GU_DIRECT ? NRUN : 1][2][RUN];
+    auto load_gu_f32 = [&](float (&dst)[GU_DIRECT ? NRUN : 1][2][RUN], int trow, int ns) {
+      if constexpr (GU_DIRECT) {
+#pragma unroll
+        for (int t = 0; t < NRUN; ++t) {
+          const int c = (qrow[ns] + RSTEP * t + RUN * h) / 8;
+          const float* gp = static_cast<const float*>(a.aux) + (row0 + (trow < rows ? trow : 0)) * a.ldaux +
+                            gcol0 + c * 8;
+          load4<float>(gp, dst[t][0]);
+          load4<float>(gp + 4, dst[t][0] + 4);
+          load4<float>(gp + a.sub, dst[t][1]);
+          load4<float>(gp + a.sub + 4, dst[t][1] + 4);
+        }
+      }
+    };
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) {
       lds_barrier();                                          // ring / previous pass no longer read
@@ -1219,25 +1241,9 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
         }
         lds_barrier();
       }
-      // f32 G, U of the SwiGLU backward: this lane's row pieces of column
-      // subtile ns, loaded one subtile ahead of the one being computed
-      constexpr bool GU_DIRECT = GUF32 && EPI == EPI_SWIGLU_BWD;
-      float gub[2][GU_DIRECT ? NRUN : 1][2][RUN];
-      auto load_gu_f32 = [&](float (&dst)[GU_DIRECT ? NRUN : 1][2][RUN], int ns) {
-        if constexpr (GU_DIRECT) {
-#pragma unroll
-          for (int t = 0; t < NRUN; ++t) {
-            const int c = (qrow[ns] + RSTEP * t + RUN * h) / 8;
-            const float* gp = static_cast<const float*>(a.aux) + (row0 + (tr_l < rows ? tr_l : 0)) * a.ldaux +
-                              gcol0 + c * 8;
-            load4<float>(gp, dst[t][0]);
-            load4<float>(gp + 4, dst[t][0] + 4);
-            load4<float>(gp + a.sub, dst[t][1]);
-            load4<float>(gp + a.sub + 4, dst[t][1] + 4);
-          }
-        }
-      };
-      if constexpr (GU_DIRECT) load_gu_f32(gub[0], 0);
+      if constexpr (GU_DIRECT) {
+        if (ms == 0 || !PP) load_gu_f32(gub[0], tr_l, 0);
+      }
       // accumulators -> staging (MFMA layout: 8 consecutive columns per run)
 #pragma unroll
       for (int ns = 0; ns < NS; ++ns) {
@@ -1249,7 +1255,8 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
           // one subtile ahead) are not hoisted above the previous subtile
           asm volatile("" ::: "memory");
           if constexpr (GU_DIRECT) {
-            if (ns + 1 < NS) load_gu_f32(gub[(ns + 1) & 1], ns + 1);
+            if (ns + 1 < NS) load_gu_f32(gub[(ns + 1) & 1], tr_l, ns + 1);
+            else if (PP && ms + 1 < MS) load_gu_f32(gub[0], prow[ms + 1] + (lane & 31), 0);
           }
         }
 #pragma unroll
