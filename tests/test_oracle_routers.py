@@ -22,9 +22,9 @@ from tests.test_oracle_pins import rand_layer
 
 def test_sinkhorn_two_by_two_by_hand():
     p = np.array([[0.9, 0.1], [0.6, 0.4]])
-    # round 1 from b = 1: a = (1/2) / [1, 1]; column sums [0.75, 0.25]; b = (1/2) / them
+    # first Sinkhorn round, from b = 1: a = (1/2) / [1, 1]; column sums [0.75, 0.25]; b = (1/2) / them
     assert np.allclose(O.sinkhorn_column_scales(p, 1), [2.0 / 3.0, 2.0], rtol=0, atol=1e-15)
-    # round 2: p b = [0.8, 1.2], a = [5/8, 5/12]; column sums [13/16, 11/48]
+    # second Sinkhorn round: p b = [0.8, 1.2], a = [5/8, 5/12]; column sums [13/16, 11/48]
     assert np.allclose(O.sinkhorn_column_scales(p, 2), [8.0 / 13.0, 24.0 / 11.0], rtol=0, atol=1e-15)
     assert np.array_equal(O.sinkhorn_column_scales(p, 0), [1.0, 1.0])
 
