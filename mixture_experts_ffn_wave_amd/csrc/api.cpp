@@ -917,6 +917,7 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
     a.offsets = sv->offsets; a.G = (int)E; a.M = A; a.N = (int)I; a.K = (int)d; a.sub = (int)I;
     a.C = dgu; a.ldc = 2 * I; a.aux = sv->gu; a.ldaux = 2 * I;
     a.Hq = dguq.pay; a.Hs = dguq.sc;                 // the epilogue also writes [dG | dU] row-wise
+    a.Tq = dgut.pay; a.Ts = dgut.sc; a.tpad = pad; a.ldt = Apad;   // and along the tokens, for dW_gu
     Probe pr(p, "gemm_down_dgrad_swiglu", s);
     MOE_TRY(launch_row_gemm(DT_MXFP8, OP_DOWN_DGRAD, EPI_SWIGLU_BWD, 128, a, s));
   }
@@ -931,8 +932,7 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
   }
   if (T > 0) {
     // dX_perm = [dG | dU] W_gu (reduction over 2I): W_gu [E][2I][d] transposed to [d][E 2I]
-    // [dG | dU]: row-wise codes from the SwiGLU-backward epilogue; token blocks for dW_gu
-    MOE_TRY_STATUS(mx_cols(p, s, dgu, 2 * I, (int)(2 * I), sv->offsets, pad, (int)E, 0, Apad / 32, 0, Apad, 0, dgut));
+    // [dG | dU]: row-wise and token-axis codes from the SwiGLU-backward epilogue
     MOE_TRY_STATUS(mx_cols(p, s, sv->w_gate_up, d, (int)d, nullptr, nullptr, (int)E, (int)(2 * I), E * 2 * I / 32, 0,
                            E * 2 * I, 0, wgut));
     RowGemmArgs a{};
@@ -974,6 +974,7 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
       a.offsets = nullptr; a.G = 1; a.M = T; a.N = (int)NI; a.K = (int)d; a.sub = (int)Is;
       a.C = dgu_s; a.ldc = 2 * NI; a.aux = sv->gu_shared; a.ldaux = 2 * NI;
       a.Hq = sdguq.pay; a.Hs = sdguq.sc;             // the epilogue also writes [dG | dU] row-wise
+      a.Tq = sdgut.pay; a.Ts = sdgut.sc; a.ldt = Tpad;   // and along the tokens (one segment), for dWs_gu
       Probe pr(p, "gemm_down_dgrad_swiglu_shared", s);
       MOE_TRY(launch_row_gemm(DT_MXFP8, OP_DOWN_DGRAD, EPI_SWIGLU_BWD, 128, a, s));
     }
@@ -987,8 +988,6 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
                                "gemm_wgrad_down_shared", s, DT_MXFP8));
     }
     {
-      MOE_TRY_STATUS(mx_cols(p, s, dgu_s, 2 * NI, (int)(2 * NI), seg_pad, seg_pad + 2, 1, 0, Tpad / 32, 0, Tpad, 0,
-                             sdgut));
       MOE_TRY_STATUS(mx_cols(p, s, sv->x, d, (int)d, seg_pad, seg_pad + 2, 1, 0, Tpad / 32, 0, Tpad, 0, sxt));
       WgradArgs a{};
       a.P = sdgut.pay; a.Ps = sdgut.sc; a.ldp = Tpad; a.Q = sxt.pay; a.Qs = sxt.sc; a.ldq = Tpad;

@@ -1183,6 +1183,15 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
       return smem + arr * SR * RB + sr * RB + ((c ^ (sr & 7)) << 4);
     };
     const int sr_l = wm * 32 + (lane & 31);                   // this lane's staged row
+    // MX SwiGLU backward: padded K position of the tile's first row in the
+    // token-axis codes of [dG | dU], and the scale bytes of this thread's
+    // column for the tile's BM / 32 blocks
+    [[maybe_unused]] const int64_t tkbase = (a.tpad ? (int64_t)a.tpad[g] : 0) + (row0 - seg0);
+    [[maybe_unused]] uint32_t tsc = 0;
+    // their LDS staging: [2 BN][BM] bytes after the staged dG, dU rows
+    constexpr int TQ_OFF = NARR * SR * RB;
+    static_assert(!(MX && EPI == EPI_SWIGLU_BWD) || TQ_OFF + 2 * BN * BM <= NSTG * (BM + BN) * DKB,
+                  "token-axis code staging fits in the ring");
     // f32 G, U of the SwiGLU backward: this lane's row pieces of column
     // subtile ns, loaded one subtile ahead of the one being computed; in
     // ping-pong tiles also the next pass's first subtile during this pass's
@@ -1440,6 +1449,56 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
               }
             }
           }
+        }
+      }
+      if constexpr (MX && EPI == EPI_SWIGLU_BWD) {
+        // [dG | dU] along the tokens for the gate/up weight gradient: thread
+        // j takes column j of the tile's [dG | dU] and quantises the pass's WM
+        // staged blocks of 32 rows (tile rows gi WTM + 32 ms ..; the tile
+        // starts a 32-block of its segment, and rows past the segment were
+        // staged as zeros, as the padding they stand for)
+        if (a.Tq) {
+          static_assert(64 * NW == 2 * BN, "one thread per column of [dG | dU]");
+          const int arr = tid / BN, col = tid % BN;
+          // the codes wait in LDS (the free half of the ring), row j = column
+          // j, 16-byte chunk q at (q ^ (j & 7)), until the tile's rows are
+          // whole; then every row leaves as one 128-byte store
+          uint8_t* crow = reinterpret_cast<uint8_t*>(smem) + TQ_OFF + tid * BM;
+#pragma unroll
+          for (int gi = 0; gi < WM; ++gi) {
+            float v[32];
+#pragma unroll
+            for (int r = 0; r < 32; ++r)
+              v[r] = to_f32<TO>(reinterpret_cast<const TO*>(sp(arr, gi * 32 + r, col / 8))[col % 8]);
+            float amax = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 32; ++r) amax = fmaxf(amax, fabsf(v[r]));
+            const int x = mx_scale_exp(amax);
+            const float sc = ldexpf(1.0f, -x);
+            u32x4 o[2];
+#pragma unroll
+            for (int w = 0; w < 8; ++w) o[w >> 2][w & 3] = e4m3x4(v[4 * w], v[4 * w + 1], v[4 * w + 2], v[4 * w + 3], sc);
+            const int tb = gi * WTM + ms * 32, q0 = tb / 16;
+            *reinterpret_cast<u32x4*>(crow + ((q0 ^ (tid & 7)) << 4)) = o[0];
+            *reinterpret_cast<u32x4*>(crow + (((q0 + 1) ^ (tid & 7)) << 4)) = o[1];
+            tsc |= (uint32_t)(x + 127) << (8 * (tb / 32));
+          }
+        }
+      }
+    }
+    if constexpr (MX && EPI == EPI_SWIGLU_BWD) {
+      if (a.Tq) {
+        static_assert(BM == 128, "four token blocks per tile: 128 code bytes and one 4-byte scale store per column");
+        const int arr = tid / BN, col = tid % BN;
+        *reinterpret_cast<uint32_t*>(a.Ts + (gcol0 + col + arr * a.sub) * (a.ldt / 32) + tkbase / 32) = tsc;
+        lds_barrier();                                        // every column's codes staged
+        const uint8_t* cst = reinterpret_cast<const uint8_t*>(smem) + TQ_OFF;
+#pragma unroll
+        for (int i = 0; i < 2 * BN * (BM / 16) / (64 * NW); ++i) {
+          const int q = tid + 64 * NW * i, j = q >> 3, ch = q & 7;
+          const int jarr = j / BN, jcol = j % BN;
+          st16(a.Tq + (gcol0 + jcol + jarr * a.sub) * a.ldt + tkbase + ch * 16,
+               *reinterpret_cast<const u32x4*>(cst + j * BM + ((ch ^ (j & 7)) << 4)));
         }
       }
     }
@@ -2047,6 +2106,10 @@ hipError_t launch_row_gemm(int dt, int op, int epi, int tile, const RowGemmArgs&
   // the f16 and MX-fp8 down dgrads write no w H rows
   if (op == OP_DOWN_DGRAD && a.C2 && (dt == DT_F16 || dt == DT_MXFP8)) return hipErrorInvalidValue;
   if (dt == DT_MXFP8 && (a.ldp % 128 || a.ldq % 128 || a.q_group_stride % 32 || !a.Ps || !a.Qs))
+    return hipErrorInvalidValue;
+  // token-axis [dG | dU] codes: the MX SwiGLU backward only, rows of ldt bytes (a multiple of 128)
+  if (a.Tq && (dt != DT_MXFP8 || op != OP_DOWN_DGRAD || epi != EPI_SWIGLU_BWD || !a.Ts || a.ldt <= 0 ||
+               a.ldt % 128 || (a.offsets && !a.tpad)))
     return hipErrorInvalidValue;
   if (dt == DT_F32 && tile != TILE_128) return hipErrorInvalidValue;
   const int bm = tile_rows(tile), bn = tile_cols(tile);

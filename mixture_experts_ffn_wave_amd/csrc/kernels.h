@@ -126,6 +126,12 @@ struct RowGemmArgs {
   // (C2_lo, layout of C2), rounded to the layer's dtype; the weight
   // gradients add their products to those of the rounded values
   void* C_lo = nullptr; void* C2_lo = nullptr;
+  // DT_MXFP8 with EPI_SWIGLU_BWD, optional: [dG | dU] also quantised along the
+  // tokens (blocks of 32 rows from each segment's start) for the gate/up
+  // weight gradient: column j of [dG | dU] is row j of Tq [2 sub-blocks][ldt]
+  // (scales Ts [..][ldt/32]), segment g's rows at K positions tpad[g] ..
+  // (tpad: [G+1] padded offsets, multiples of 128; nullptr = position = row)
+  uint8_t* Tq = nullptr; uint8_t* Ts = nullptr; const int32_t* tpad = nullptr; int64_t ldt = 0;
 };
 // Intermediates a bf16 layer with bf16 experts keeps in f32 (the saved gate/up
 // pre-activations [G | U], the expert output rows Y_perm and the input-gradient
