@@ -108,10 +108,21 @@ __device__ __forceinline__ void route_epilogue(const f32x16 (&acc)[NSUB], int64_
       }
   }
 
-  // top-k: k rounds of (largest remaining logit, lower index on ties)
-  uint32_t taken[NSUB];
+  // top-k: k rounds of (largest remaining logit, lower index on ties).  The
+  // ranking values and the candidates are fixed before the rounds, and each
+  // round's scan is made of selects, not branches.
+  float rk[NSUB][16];
+  uint32_t avail[NSUB];
 #pragma unroll
-  for (int s = 0; s < NSUB; ++s) taken[s] = 0u;
+  for (int s = 0; s < NSUB; ++s) {
+    avail[s] = 0u;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int e = s * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      rk[s][r] = sel ? z[s][r] + s_sel[e] : z[s][r];
+      if (e < E) avail[s] |= 1u << r;
+    }
+  }
   float psum = 0.0f;
   for (int j = 0; j < a.k; ++j) {
     float bv = -INFINITY, bp = 0.0f;               // best ranking value, and its probability (sel)
@@ -121,14 +132,10 @@ __device__ __forceinline__ void route_epilogue(const f32x16 (&acc)[NSUB], int64_
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int e = s * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (e < E && !((taken[s] >> r) & 1u)) {
-          const float v = sel ? z[s][r] + s_sel[e] : z[s][r];
-          if (be < 0 || v > bv) {
-            bv = v;
-            bp = z[s][r];
-            be = e;
-          }
-        }
+        const bool better = ((avail[s] >> r) & 1u) && (be < 0 || rk[s][r] > bv);
+        bv = better ? rk[s][r] : bv;
+        bp = better ? z[s][r] : bp;
+        be = better ? e : be;
       }
     const float pv = __shfl_xor(bv, 32, 64);
     const float pp = __shfl_xor(bp, 32, 64);
@@ -142,7 +149,7 @@ __device__ __forceinline__ void route_epilogue(const f32x16 (&acc)[NSUB], int64_
       const int r = ((w5 >> 3) << 2) | (w5 & 3);
 #pragma unroll
       for (int ss = 0; ss < NSUB; ++ss)
-        if (ss == s) taken[ss] |= 1u << r;
+        if (ss == s) avail[ss] &= ~(1u << r);
     }
     const float pj = sel ? wp : expf(wv - m) / sum;
     psum += pj;
@@ -154,6 +161,37 @@ __device__ __forceinline__ void route_epilogue(const f32x16 (&acc)[NSUB], int64_
   }
   if (a.renorm && tv && h == 0) {
     for (int j = 0; j < a.k; ++j) a.wts[t * a.k + j] = s_wts[(lane & 31) * kWtsStride + j] / psum;
+  }
+}
+
+// Exchange with the partner lane of butterfly stage S inside each group of
+// eight lanes, as a DPP move (a VALU operand modifier, no LDS round trip):
+// stage 0 pairs lanes i, i ^ 1 and stage 1 lanes i, i ^ 2 (quad permutes),
+// stage 2 lane i with lane 7 - i of its half-row (half mirror).  After the
+// three stages every lane of the group has combined all eight values, in the
+// same pairs as an xor-1, 2, 4 butterfly (after stage 1 each quad holds one
+// value), so maxima, sums and the ranking below come out identical.
+template <int S>
+__device__ __forceinline__ int x8(int v) {
+  static_assert(S >= 0 && S < 3, "three stages");
+  constexpr int CTRL = S == 0 ? 0xB1 : (S == 1 ? 0x4E : 0x141);   // quad_perm [1,0,3,2], [2,3,0,1]; row_half_mirror
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+template <int S>
+__device__ __forceinline__ float x8f(float v) { return __int_as_float(x8<S>(__float_as_int(v))); }
+
+// One stage of the top-k round's merge: keep the partner's candidate when it
+// ranks higher (larger value, lower expert index on equal values; -1 = none).
+template <int S>
+__device__ __forceinline__ void topk_merge(float& bv, float& bp, float& bz, int& be) {
+  const float ov = x8f<S>(bv), op = x8f<S>(bp), oz = x8f<S>(bz);
+  const int oe = x8<S>(be);
+  const bool take = (be < 0) || (oe >= 0 && (ov > bv || (ov == bv && oe < be)));
+  if (take) {
+    bv = ov;
+    bp = op;
+    bz = oz;
+    be = oe;
   }
 }
 
@@ -186,14 +224,16 @@ __device__ __forceinline__ void route_epilogue_wide(const float* red, int64_t tb
     z[i] = (e < E) ? v + s_bias[e] : -INFINITY;
     m = fmaxf(m, z[i]);
   }
-#pragma unroll
-  for (int o = 1; o < 8; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  m = fmaxf(m, x8f<0>(m));
+  m = fmaxf(m, x8f<1>(m));
+  m = fmaxf(m, x8f<2>(m));
   float sum = 0.0f;
 #pragma unroll
   for (int i = 0; i < EPL; ++i)
     if (g * EPL + i < E) sum += expf(z[i] - m);
-#pragma unroll
-  for (int o = 1; o < 8; o <<= 1) sum += __shfl_xor(sum, o, 64);
+  sum += x8f<0>(sum);
+  sum += x8f<1>(sum);
+  sum += x8f<2>(sum);
   // probabilities (kept in z when a selection bias ranks on them); the ReLU
   // router stores its gates max(z, 0) in their place
   const bool relu = a.relu != 0;
@@ -216,39 +256,36 @@ __device__ __forceinline__ void route_epilogue_wide(const float* red, int64_t tb
   }
   // top-k: k rounds of (largest remaining ranking value, lower index on ties);
   // the ReLU router only takes positive logits, a round without one leaves
-  // the slot empty (index -1, weight 0)
-  uint32_t taken = 0u;
+  // the slot empty (index -1, weight 0).  The ranking values and the
+  // candidates are fixed before the rounds, and each round's scan over the
+  // lane's experts is made of selects, not branches.
+  float rk[EPL];
+  uint32_t avail = 0u;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = g * EPL + i;
+    rk[i] = sel ? p[i] + s_sel[e < E ? e : 0] : z[i];
+    if (e < E && (!relu || z[i] > 0.0f)) avail |= 1u << i;
+  }
   float psum = 0.0f;
   for (int j = 0; j < a.k; ++j) {
     float bv = -INFINITY, bp = 0.0f, bz = -INFINITY;
-    int be = -1;
+    int bi = -1;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      const int e = g * EPL + i;
-      if (e < E && !((taken >> i) & 1u) && (!relu || z[i] > 0.0f)) {
-        const float v = sel ? p[i] + s_sel[e] : z[i];
-        if (be < 0 || v > bv) {
-          bv = v;
-          bp = p[i];
-          bz = z[i];
-          be = e;
-        }
-      }
+      const bool better = ((avail >> i) & 1u) && (bi < 0 || rk[i] > bv);
+      bv = better ? rk[i] : bv;
+      bp = better ? p[i] : bp;
+      bz = better ? z[i] : bz;
+      bi = better ? i : bi;
     }
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
-      const float ov = __shfl_xor(bv, o, 64), op = __shfl_xor(bp, o, 64), oz = __shfl_xor(bz, o, 64);
-      const int oe = __shfl_xor(be, o, 64);
-      const bool take = (be < 0) || (oe >= 0 && (ov > bv || (ov == bv && oe < be)));
-      if (take) {
-        bv = ov;
-        bp = op;
-        bz = oz;
-        be = oe;
-      }
-    }
-    if (be >= 0 && be / EPL == g) taken |= 1u << (be - g * EPL);
-    const float pj = be < 0 ? 0.0f : (relu ? bz : (sel ? bp : expf(bz - m) / sum));
+    int be = bi < 0 ? -1 : g * EPL + bi;
+    topk_merge<0>(bv, bp, bz, be);
+    topk_merge<1>(bv, bp, bz, be);
+    topk_merge<2>(bv, bp, bz, be);
+    if (be >= 0 && be / EPL == g) avail &= ~(1u << (be - g * EPL));
+    // (the chosen probability is the p of the stored row: the same expression)
+    const float pj = be < 0 ? 0.0f : (relu ? bz : bp);
     psum += pj;
     if (tv && g == 0) {
       a.idx[t * a.k + j] = be;
