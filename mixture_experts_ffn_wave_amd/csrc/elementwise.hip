@@ -200,7 +200,20 @@ __device__ __forceinline__ float slot_g(const float* g, const float* gpart, cons
   if (r < 0) return 0.0f;                         // an empty slot (no expert)
   const float* p = gpart + (int64_t)r * gparts;
   float s = 0.0f;
-  for (int i = 0; i < gparts; ++i) s += p[i];
+  if ((gparts & 3) == 0) {
+    // 16-byte loads (a row then starts 16-byte aligned), added in the same
+    // order; all of a row's loads can be in flight before the first add
+#pragma unroll 4
+    for (int i = 0; i < gparts; i += 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(p + i);
+      s += v[0];
+      s += v[1];
+      s += v[2];
+      s += v[3];
+    }
+  } else {
+    for (int i = 0; i < gparts; ++i) s += p[i];
+  }
   return s;
 }
 
@@ -468,16 +481,17 @@ __global__ void __launch_bounds__(NT) stack2_kernel(Stack2Args a) {
   }
 }
 
-// Blocks [0, nbw): block b reduces columns 64 (b % (d/64)) .. +63 of row
-// e = b / (d/64): dW_r[e][n] = sum_s part[s][e][n] (+ sum_s part[s][lo_row + e][n]).
+// Blocks [0, nbw): block b reduces columns 64 VEC (b % (d / (64 VEC))) ..
+// + 64 VEC - 1 of row e = b / (d / (64 VEC)), VEC consecutive columns per
+// lane: dW_r[e][n] = sum_s part[s][e][n] (+ sum_s part[s][lo_row + e][n]).
 // Its 16 waves each sum every 16th split (hi and lo apart), then the wave
 // partials are added in index order.  Blocks [nbw, nbw + E): dbias[e] = sum
 // over router_dz blocks of their partial.
 constexpr int kReduceThreads = 1024;
-template <typename T>
+template <typename T, int VEC>
 __global__ void __launch_bounds__(kReduceThreads) router_reduce_kernel(RouterReduceArgs a, int nbw) {
   constexpr int NWV = kReduceThreads / 64;
-  __shared__ float sh[2][NWV][64];
+  __shared__ float sh[2][NWV][64 * VEC];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if ((int)blockIdx.x >= nbw) {
     const int e = blockIdx.x - nbw;
@@ -493,34 +507,51 @@ __global__ void __launch_bounds__(kReduceThreads) router_reduce_kernel(RouterRed
     }
     return;
   }
-  const int groups = a.d / 64;
+  typedef __attribute__((__vector_size__(VEC * sizeof(float)))) float VT;   // VEC floats, one load
+  const int groups = a.d / (64 * VEC);
   const int e = blockIdx.x / groups;
-  const int col = (blockIdx.x - e * groups) * 64 + lane;
+  const int col = (blockIdx.x - e * groups) * 64 * VEC + lane * VEC;
   const int64_t sstride = (int64_t)a.rows * a.d;
   const float* ph = a.part + (int64_t)e * a.d + col;
   const float* pl = a.part + (int64_t)(a.lo_row + e) * a.d + col;
-  float hi = 0.0f, lo = 0.0f;
+  float hi[VEC], lo[VEC];
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) hi[c] = lo[c] = 0.0f;
   if (a.lo_row >= 0) {
 #pragma unroll 4
     for (int s = wave; s < a.splits; s += NWV) {
-      hi += ph[s * sstride];
-      lo += pl[s * sstride];
+      const VT h = *reinterpret_cast<const VT*>(ph + s * sstride), l = *reinterpret_cast<const VT*>(pl + s * sstride);
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) {
+        hi[c] += h[c];
+        lo[c] += l[c];
+      }
     }
   } else {
 #pragma unroll 4
-    for (int s = wave; s < a.splits; s += NWV) hi += ph[s * sstride];
+    for (int s = wave; s < a.splits; s += NWV) {
+      const VT h = *reinterpret_cast<const VT*>(ph + s * sstride);
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) hi[c] += h[c];
+    }
   }
-  sh[0][wave][lane] = hi;
-  sh[1][wave][lane] = lo;
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) {
+    sh[0][wave][lane * VEC + c] = hi[c];
+    sh[1][wave][lane * VEC + c] = lo[c];
+  }
   __syncthreads();
   if (wave == 0) {
-    float h = 0.0f, l = 0.0f;
 #pragma unroll
-    for (int w = 0; w < NWV; ++w) {
-      h += sh[0][w][lane];
-      l += sh[1][w][lane];
+    for (int c = 0; c < VEC; ++c) {
+      float h = 0.0f, l = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) {
+        h += sh[0][w][lane * VEC + c];
+        l += sh[1][w][lane * VEC + c];
+      }
+      static_cast<T*>(a.dw)[(int64_t)e * a.d + col + c] = from_f32<T>(h + l);
     }
-    static_cast<T*>(a.dw)[(int64_t)e * a.d + col] = from_f32<T>(h + l);
   }
 }
 
@@ -776,9 +807,24 @@ __global__ void __launch_bounds__(NT) aux_finalize_kernel(AuxArgs a, int nblk) {
     const int e = threadIdx.x % EP2, tl = threadIdx.x / EP2;
     float s1 = 0.0f, s2 = 0.0f;
     if (e < a.E) {
-      for (int b = tl; b < nblk; b += TL) {
-        s1 += a.part[((int64_t)b * 2 + 0) * a.E + e];
-        s2 += a.part[((int64_t)b * 2 + 1) * a.E + e];
+      // blocks tl, tl + TL, ... in that order; eight blocks' loads issued
+      // together (a chain of single loads left this one block waiting on
+      // memory for most of its time)
+      for (int b0 = tl; b0 < nblk; b0 += 8 * TL) {
+        float v1[8], v2[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int b = b0 + u * TL;
+          v1[u] = b < nblk ? a.part[((int64_t)b * 2 + 0) * a.E + e] : 0.0f;
+          v2[u] = b < nblk ? a.part[((int64_t)b * 2 + 1) * a.E + e] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (b0 + u * TL < nblk) {
+            s1 += v1[u];
+            s2 += v2[u];
+          }
+        }
       }
     }
     cp[threadIdx.x] = s1;
@@ -945,7 +991,9 @@ hipError_t launch_router_bwd_small_t(const RouterBwdSmallArgs& a, hipStream_t s)
   const int grid = router_small_blocks(a.T);
   const int nch = a.d / 8, G = NT / nch;
   const size_t shm = G > 1 ? (size_t)a.E * a.d * sizeof(float) : 0;
-  if (a.E <= 8) hipLaunchKernelGGL((router_bwd_small_kernel<T, 8>), dim3(grid), dim3(NT), shm, s, a);
+  // (EM = E rounded up: every dW_r product runs EM wide)
+  if (a.E <= 4) hipLaunchKernelGGL((router_bwd_small_kernel<T, 4>), dim3(grid), dim3(NT), shm, s, a);
+  else if (a.E <= 8) hipLaunchKernelGGL((router_bwd_small_kernel<T, 8>), dim3(grid), dim3(NT), shm, s, a);
   else hipLaunchKernelGGL((router_bwd_small_kernel<T, 16>), dim3(grid), dim3(NT), shm, s, a);
   return hipGetLastError();
 }
@@ -975,15 +1023,28 @@ hipError_t launch_stack2(int dt, const Stack2Args& a, hipStream_t s) {
 
 hipError_t launch_router_reduce(int dt, const RouterReduceArgs& a, hipStream_t s) {
   if (a.d % 64) return hipErrorInvalidValue;
-  const int64_t nbw = (int64_t)a.E * (a.d / 64);
+  // the widest loads (4 or 2 columns per lane) that still give every CU a
+  // block; with few rows, blocks of 64 single columns (many splits then
+  // spread over more blocks)
+  int vec = 1;
+  for (int v = 4; v > 1; v /= 2)
+    if (a.d % (64 * v) == 0 && (int64_t)a.E * (a.d / (64 * v)) >= 256) { vec = v; break; }
+  const int64_t nbw = (int64_t)a.E * (a.d / (64 * vec));
   const int64_t grid = nbw + (a.dbias ? a.E : 0);
   if (grid == 0) return hipSuccess;
+#define MOE_LAUNCH_RR(TY)                                                                                        \
+  do {                                                                                                           \
+    if (vec == 4) hipLaunchKernelGGL((router_reduce_kernel<TY, 4>), dim3((unsigned)grid), dim3(kReduceThreads), 0, s, a, (int)nbw); \
+    else if (vec == 2) hipLaunchKernelGGL((router_reduce_kernel<TY, 2>), dim3((unsigned)grid), dim3(kReduceThreads), 0, s, a, (int)nbw); \
+    else hipLaunchKernelGGL((router_reduce_kernel<TY, 1>), dim3((unsigned)grid), dim3(kReduceThreads), 0, s, a, (int)nbw); \
+  } while (0)
   switch (dt) {
-    case DT_BF16: hipLaunchKernelGGL(router_reduce_kernel<__bf16>, dim3((unsigned)grid), dim3(kReduceThreads), 0, s, a, (int)nbw); break;
-    case DT_F16: hipLaunchKernelGGL(router_reduce_kernel<_Float16>, dim3((unsigned)grid), dim3(kReduceThreads), 0, s, a, (int)nbw); break;
-    case DT_F32: hipLaunchKernelGGL(router_reduce_kernel<float>, dim3((unsigned)grid), dim3(kReduceThreads), 0, s, a, (int)nbw); break;
+    case DT_BF16: MOE_LAUNCH_RR(__bf16); break;
+    case DT_F16: MOE_LAUNCH_RR(_Float16); break;
+    case DT_F32: MOE_LAUNCH_RR(float); break;
     default: return hipErrorInvalidValue;
   }
+#undef MOE_LAUNCH_RR
   return hipGetLastError();
 }
 
