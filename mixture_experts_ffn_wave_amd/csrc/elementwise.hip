@@ -706,7 +706,7 @@ __global__ void __launch_bounds__(NT) unpermute_kernel(UnpermuteArgs a) {
 // ---- balancing statistic -----------------------------------------------------
 // Threads form a (token lane) x (expert) grid: EP2 = E rounded up to a power of
 // two experts per row of threads, NT / EP2 token lanes.
-constexpr int kAuxTokens = 128;
+constexpr int kAuxTokens = 64;
 
 __device__ __forceinline__ int pow2_at_least(int v) {
   int p = 1;
