@@ -385,7 +385,17 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
     p->t_wg_down = choose_wgrad_tile(p->dt, E, d, I, rps, wt);
     p->t_wg_gu = choose_wgrad_tile(p->dt, E, 2 * I, d, rps, wt);
     p->t_wg_router = 128;
-    if (p->mx) p->t_gu = p->t_down = p->t_down_dgrad = p->t_gu_dgrad = p->t_wg_down = p->t_wg_gu = 128;
+    // MX-fp8 experts: 256 x 256 tiles (8 waves, the plain ring) where the
+    // 16-bit layer would take its ping-pong tiles, for the forward GEMMs and
+    // the gate/up dgrad; the down dgrad (whose epilogue writes the token-axis
+    // codes of 128-row tiles) and the weight gradients keep 128 x 128
+    auto mx_row = [](int t) { return (t == TILE_256PP || t == TILE_256) ? TILE_256 : TILE_128; };
+    if (p->mx) {
+      p->t_gu = mx_row(p->t_gu);
+      p->t_down = mx_row(p->t_down);
+      p->t_gu_dgrad = mx_row(p->t_gu_dgrad);
+      p->t_down_dgrad = p->t_wg_down = p->t_wg_gu = 128;
+    }
     p->sp_wg_down = choose_wgrad_splits(p->t_wg_down, E, d, I, rps);
     p->sp_wg_gu = choose_wgrad_splits(p->t_wg_gu, E, 2 * I, d, rps);
     if (p->Ns > 0) {
@@ -395,7 +405,12 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
       p->t_gu_dgrad_s = choose_row_tile(p->dt, d, 256, mts * (d / 256), 2 * NI, rt);
       p->t_wg_down_s = (p->Is % 256 == 0) ? choose_wgrad_tile(p->dt, 1, d, NI, T, wt) : 128;
       p->t_wg_gu_s = choose_wgrad_tile(p->dt, 1, 2 * NI, d, T, wt);
-      if (p->mx) p->t_gu_s = p->t_down_s = p->t_down_dgrad_s = p->t_gu_dgrad_s = p->t_wg_down_s = p->t_wg_gu_s = 128;
+      if (p->mx) {
+        p->t_gu_s = mx_row(p->t_gu_s);
+        p->t_down_s = mx_row(p->t_down_s);
+        p->t_gu_dgrad_s = mx_row(p->t_gu_dgrad_s);
+        p->t_down_dgrad_s = p->t_wg_down_s = p->t_wg_gu_s = 128;
+      }
       p->sp_wg_down_s = choose_wgrad_splits(p->t_wg_down_s, 1, d, NI, T);
       p->sp_wg_gu_s = choose_wgrad_splits(p->t_wg_gu_s, 1, 2 * NI, d, T);
     } else {
@@ -839,7 +854,7 @@ moe_status mx_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, hipStream_
     a.C = f->gu; a.ldc = 2 * I; a.C2 = f->h; a.ldc2 = I;
     a.Hq = hq.pay; a.Hs = hq.sc;                     // the epilogue also quantises H row-wise
     Probe pr(p, "gemm_gate_up_swiglu", s);
-    MOE_TRY(launch_row_gemm(DT_MXFP8, OP_GU_FWD, EPI_SWIGLU_FWD, 128, a, s));
+    MOE_TRY(launch_row_gemm(DT_MXFP8, OP_GU_FWD, EPI_SWIGLU_FWD, p->t_gu, a, s));
   }
   MOE_TRY_STATUS(mx_rows(p, s, f->w_down, I, 0, (int)I, E * d, (int)I, wd));
   {
@@ -848,7 +863,7 @@ moe_status mx_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, hipStream_
     a.offsets = f->offsets; a.G = (int)E; a.M = A; a.N = (int)d; a.K = (int)I; a.sub = (int)I;
     a.C = f->y_perm; a.ldc = d;
     Probe pr(p, "gemm_down", s);
-    MOE_TRY(launch_row_gemm(DT_MXFP8, OP_DOWN_FWD, EPI_STORE_F32, 128, a, s));
+    MOE_TRY(launch_row_gemm(DT_MXFP8, OP_DOWN_FWD, EPI_STORE_F32, p->t_down, a, s));
   }
   if (p->Ns > 0) {
     const int64_t Is = p->Is, NI = p->Ns * p->Is, T = p->T;
@@ -863,7 +878,7 @@ moe_status mx_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, hipStream_
       a.C = f->gu_shared; a.ldc = 2 * NI; a.C2 = f->h_shared; a.ldc2 = NI;
       a.Hq = shq.pay; a.Hs = shq.sc;                 // the epilogue also quantises H row-wise
       Probe pr(p, "gemm_gate_up_swiglu_shared", s);
-      MOE_TRY(launch_row_gemm(DT_MXFP8, OP_GU_FWD, EPI_SWIGLU_FWD, 128, a, s));
+      MOE_TRY(launch_row_gemm(DT_MXFP8, OP_GU_FWD, EPI_SWIGLU_FWD, p->t_gu_s, a, s));
     }
     // shared down weights [Ns][d][Is] concatenated along K into [d][NI]
     MOE_TRY_STATUS(mx_rows(p, s, f->ws_down, Is, d * Is, (int)Is, d, (int)NI, swd));
@@ -873,7 +888,7 @@ moe_status mx_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, hipStream_
       a.offsets = nullptr; a.G = 1; a.M = T; a.N = (int)d; a.K = (int)NI; a.sub = (int)Is;
       a.C = f->y_shared; a.ldc = d;
       Probe pr(p, "gemm_down_shared", s);
-      MOE_TRY(launch_row_gemm(DT_MXFP8, OP_DOWN_FWD, EPI_STORE, 128, a, s));
+      MOE_TRY(launch_row_gemm(DT_MXFP8, OP_DOWN_FWD, EPI_STORE, p->t_down_s, a, s));
     }
   }
   return MOE_OK;
@@ -940,7 +955,7 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
     a.offsets = sv->offsets; a.G = (int)E; a.M = A; a.N = (int)d; a.K = (int)(2 * I); a.sub = (int)I;
     a.C = dx_perm; a.ldc = d;
     Probe pr(p, "gemm_gate_up_dgrad", s);
-    MOE_TRY(launch_row_gemm(DT_MXFP8, OP_GU_DGRAD, EPI_STORE, 128, a, s));
+    MOE_TRY(launch_row_gemm(DT_MXFP8, OP_GU_DGRAD, EPI_STORE, p->t_gu_dgrad, a, s));
   }
   {
     if (sv->perm_token)                        // x's rows gathered by perm_token (x_perm not read)
@@ -1004,7 +1019,7 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
       a.offsets = nullptr; a.G = 1; a.M = T; a.N = (int)d; a.K = (int)(2 * NI); a.sub = (int)d;
       a.C = dxs; a.ldc = d;
       Probe pr(p, "gemm_gate_up_dgrad_shared", s);
-      MOE_TRY(launch_row_gemm(DT_MXFP8, OP_GU_DGRAD, EPI_STORE, 128, a, s));
+      MOE_TRY(launch_row_gemm(DT_MXFP8, OP_GU_DGRAD, EPI_STORE, p->t_gu_dgrad_s, a, s));
     }
   }
   return MOE_OK;

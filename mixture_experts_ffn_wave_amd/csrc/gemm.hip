@@ -425,6 +425,35 @@ __device__ __forceinline__ void mfma_chunk_mx(f32x16 (&acc)[NS][MS], const char*
                                               const int (&qrow)[NS], const int (&prow)[MS], int lane) {
   constexpr int KS = MX_DKB / 64;
   const int h = lane >> 5;
+  if constexpr (NS * MS > 4) {
+    // the 256 x 256 tile's waves (8 output subtiles): one k step's fragments
+    // at a time, so the chunk's fragments and the 128 accumulators fit the
+    // register budget
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      v8i fa[NS], fb[MS];
+      int sa[NS], sb[MS];
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns) {
+        const int r = qrow[ns] + perm_row(lane & 31);
+        fa[ns] = mx_frag(lq, r, ks, h);
+        sa[ns] = sq[4 * r + 2 * ks + h];
+      }
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) {
+        const int r = prow[ms] + (lane & 31);
+        fb[ms] = mx_frag(lp, r, ks, h);
+        sb[ms] = sp[4 * r + 2 * ks + h];
+      }
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms)
+          acc[ns][ms] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[ns], fb[ms], acc[ns][ms], 0, 0, 0, sa[ns],
+                                                                          0, sb[ms]);
+    }
+    return;
+  }
   // every k step's fragments and scales first, then the MFMAs
   v8i fa[KS][NS], fb[KS][MS];
   int sa[KS][NS], sb[KS][MS];
@@ -636,8 +665,9 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
   constexpr bool GUF32 = !MX && std::is_same_v<T, __bf16>;
   using TG = std::conditional_t<GUF32, float, TO>;
   constexpr int NW = WM * WN;                                  // waves: WM along rows, WN along columns
-  static_assert(ES == 2 || NW == 4, "the register-staged path runs 4 waves");
-  static_assert(!MX || (ES == 1 && BM == 128 && BN == 128 && NW == 4), "MX tiles are 128 x 128, 4 waves");
+  static_assert(ES == 2 || MX || NW == 4, "the register-staged path runs 4 waves");
+  static_assert(!MX || (ES == 1 && ((BM == 128 && BN == 128 && NW == 4) || (BM == 256 && BN == 256 && NW == 8))),
+                "MX row tiles: 128 x 128 with 4 waves or 256 x 256 with 8");
   constexpr bool QT = !MX && (OP == OP_DOWN_DGRAD || OP == OP_GU_DGRAD || OP == OP_ROUTER_DX);
   using TOP = std::conditional_t<MX, __bf16, T>;              // (register-path operand type; unused for MX)
   using PO = Operand<TOP, BM, false>;
@@ -824,8 +854,12 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
       qoff[s2] = (uint32_t)(qsrc_row(q) * a.ldq + QD::gchunk(q, lane) * 16);
     }
     // scale rows: wave 0/1 load P rows 0-63 / 64-127, wave 2/3 Q rows 0-63 / 64-127
-    const bool sq_side = wave >= 2;
-    const int srow_t = (wave & 1) * 64 + lane;
+    // scale rows: the first BM / 64 waves load P's rows 64 w .. 64 w + 63, the
+    // others Q's
+    static_assert(64 * NW == BM + BN, "one wave per 64 scale rows");
+    const bool sq_side = wave >= BM / 64;
+    const int swave = sq_side ? wave - BM / 64 : wave;
+    const int srow_t = swave * 64 + lane;
     const uint8_t* qsb = a.Qs + (int64_t)g * (a.q_group_stride / 32);
     const rsrc_t psrs = gat ? make_rsrc(a.Ps, (uint32_t)(a.p_rows * pls))
                             : make_rsrc(a.Ps + row0 * pls, (uint32_t)(rows * pls));
@@ -837,7 +871,7 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
       const rsrc_t qrs = make_rsrc(Qb + kc, 0x7fffffffu);
 #pragma unroll
       for (int s2 = 0; s2 < QD::NI; ++s2) dma16(qrs, stage + PD::BYTES + QD::lds_off(wave, s2), qoff[s2]);
-      char* sst = smem + SC_OFF + st * SSTAGE + (sq_side ? BM * 4 : 0) + (wave & 1) * 64 * 4;
+      char* sst = smem + SC_OFF + st * SSTAGE + (sq_side ? BM * 4 : 0) + swave * 64 * 4;
       if (sq_side) dma4(make_rsrc(qsb + kc / 32, 0x7fffffffu), sst, soff);
       else dma4(psrs, sst, soff + (uint32_t)(kc / 32));
     };
@@ -1602,7 +1636,7 @@ __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
   static_assert(!PP || (ES == 2 && BM == 256 && BN == 256 && WM == 2 && WN == 4), "ping-pong tile");
   using TO = std::conditional_t<MX, __bf16, T>;
   constexpr int NW = WM * WN;
-  static_assert(ES == 2 || NW == 4, "the register-staged path runs 4 waves");
+  static_assert(ES == 2 || MX || NW == 4, "the register-staged path runs 4 waves");
   static_assert(!MX || (ES == 1 && BM == 128 && BN == 128 && NW == 4), "MX tiles are 128 x 128, 4 waves");
   using TOP = std::conditional_t<MX, __bf16, T>;
   using PO = Operand<TOP, BM, true>;
@@ -2004,6 +2038,18 @@ MOE_MX_ROW_KERNEL(moe_mx_gemm_down_128x128, OP_DOWN_FWD, EPI_STORE)
 MOE_MX_ROW_KERNEL(moe_mx_gemm_down_f32out_128x128, OP_DOWN_FWD, EPI_STORE_F32)
 MOE_MX_ROW_KERNEL(moe_mx_gemm_down_dgrad_swiglu_128x128, OP_DOWN_DGRAD, EPI_SWIGLU_BWD)
 MOE_MX_ROW_KERNEL(moe_mx_gemm_gate_up_dgrad_128x128, OP_GU_DGRAD, EPI_STORE)
+// 256 x 256 tiles, 8 waves (2 x 4), the same 2-stage ring of 128-byte chunks
+// (one workgroup per CU); not for the SwiGLU backward, whose epilogue writes
+// the token-axis codes block by block of a 128-row tile
+#define MOE_MX_ROW_KERNEL_256(NAME, OP, EPI)                                                          \
+  extern "C" __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) NAME(RowGemmArgs a) { \
+    extern __shared__ __attribute__((aligned(16))) char smem[];                                   \
+    row_gemm_body<uint8_t, 256, 256, OP, EPI, 2, 4, true>(a, smem);                               \
+  }
+MOE_MX_ROW_KERNEL_256(moe_mx_gemm_gate_up_swiglu_256x256, OP_GU_FWD, EPI_SWIGLU_FWD)
+MOE_MX_ROW_KERNEL_256(moe_mx_gemm_down_256x256, OP_DOWN_FWD, EPI_STORE)
+MOE_MX_ROW_KERNEL_256(moe_mx_gemm_down_f32out_256x256, OP_DOWN_FWD, EPI_STORE_F32)
+MOE_MX_ROW_KERNEL_256(moe_mx_gemm_gate_up_dgrad_256x256, OP_GU_DGRAD, EPI_STORE)
 MOE_MX_WGRAD_KERNEL(moe_mx_wgrad_down_128x128, 0)
 MOE_MX_WGRAD_KERNEL(moe_mx_wgrad_gate_up_128x128, 0)
 MOE_MX_WGRAD_KERNEL(moe_mx_wgrad_down_f32out_128x128, 1)
@@ -2072,6 +2118,14 @@ const KernelSet* kernel_set(int dt, int tile) {
                                   moe_mx_wgrad_down_f32out_128x128, moe_mx_wgrad_gate_up_f32out_128x128,
                                   nullptr, mx_lds, mx_lds, nullptr};
     return &mx_128;
+  }
+  if (dt == DT_MXFP8 && tile == TILE_256) {
+    constexpr size_t mx_lds = 2 * (256 + 256) * MX_DKB + 2 * (256 + 256) * 4 + 64;
+    static const KernelSet mx_256{moe_mx_gemm_gate_up_swiglu_256x256, moe_mx_gemm_down_256x256,
+                                  moe_mx_gemm_down_f32out_256x256, nullptr, moe_mx_gemm_gate_up_dgrad_256x256,
+                                  nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, mx_lds, mx_lds,
+                                  nullptr};
+    return &mx_256;
   }
   return nullptr;
 }

@@ -71,6 +71,18 @@ def test_mx_layer_matches_oracle(wl):
     PT.full_parity(wl)
 
 
+# The 256 x 256 MX tiles (8 waves) of the forward GEMMs and the gate/up
+# dgrad, forced on shapes that span several tiles with ragged and skewed
+# segments (the large workload takes them by default)
+MX_256 = [SMALL_MX[0], SMALL_MX[1], SMALL_MX[3]]
+
+
+@pytest.mark.parametrize("wl", MX_256, ids=[w.name for w in MX_256])
+def test_mx_256_tiles_match_oracle(wl, monkeypatch):
+    monkeypatch.setenv("MOE_ROW_TILE", "256")
+    PT.full_parity(wl)
+
+
 def test_mx_forced_empty_experts_write_zero_gradients():
     wl = W("t700_d256_e8k2_i256_mx_bias", T=700, d=256, E=8, k=2, I=256, n_shared=1, I_shared=128,
            expert_dtype="mxfp8")

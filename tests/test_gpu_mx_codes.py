@@ -236,6 +236,17 @@ def test_every_mx_operand_is_bit_exact(wl, gather):
         assert counts.max() > 4 * counts.mean() and (counts[counts > 0] < 32).any(), counts
 
 
+# The 256 x 256 tiles (8 waves) of the forward GEMMs and the gate/up dgrad:
+# H's row-wise codes come from the 256-wide gate/up epilogue
+@pytest.mark.parametrize("wl,gather", [CASES[0], CASES[2]], ids=["zipf-gather", "shared1-gather"])
+def test_every_mx_operand_is_bit_exact_with_256_tiles(wl, gather, monkeypatch):
+    monkeypatch.setenv("MOE_ROW_TILE", "256")
+    PT.say(f"[mx-codes] {wl.name} gather={gather} row tiles 256 x 256")
+    inp = MI.make_inputs(wl)
+    layer, dev = run_layer(wl, inp, gather)
+    check_all(wl, layer, dev, gather)
+
+
 def test_mx_codes_with_empty_experts():
     wl = W("t700_d256_e8k2_i256_s1x128_mx_empty", T=700, d=256, E=8, k=2, I=256, n_shared=1, I_shared=128,
            expert_dtype="mxfp8")
