@@ -386,15 +386,17 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
     p->t_wg_gu = choose_wgrad_tile(p->dt, E, 2 * I, d, rps, wt);
     p->t_wg_router = 128;
     // MX-fp8 experts: 256 x 256 tiles (8 waves, the plain ring) where the
-    // 16-bit layer would take its ping-pong tiles, for the forward GEMMs and
-    // the gate/up dgrad; the down dgrad (whose epilogue writes the token-axis
-    // codes of 128-row tiles) and the weight gradients keep 128 x 128
+    // 16-bit layer would take its 256 x 256 (ping-pong) tiles, for the forward
+    // GEMMs, the gate/up dgrad and the weight gradients; the down dgrad, whose
+    // epilogue writes the token-axis codes of 128-row tiles, keeps 128 x 128
     auto mx_row = [](int t) { return (t == TILE_256PP || t == TILE_256) ? TILE_256 : TILE_128; };
     if (p->mx) {
       p->t_gu = mx_row(p->t_gu);
       p->t_down = mx_row(p->t_down);
       p->t_gu_dgrad = mx_row(p->t_gu_dgrad);
-      p->t_down_dgrad = p->t_wg_down = p->t_wg_gu = 128;
+      p->t_wg_down = mx_row(p->t_wg_down);
+      p->t_wg_gu = mx_row(p->t_wg_gu);
+      p->t_down_dgrad = 128;
     }
     p->sp_wg_down = choose_wgrad_splits(p->t_wg_down, E, d, I, rps);
     p->sp_wg_gu = choose_wgrad_splits(p->t_wg_gu, E, 2 * I, d, rps);
@@ -409,7 +411,9 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
         p->t_gu_s = mx_row(p->t_gu_s);
         p->t_down_s = mx_row(p->t_down_s);
         p->t_gu_dgrad_s = mx_row(p->t_gu_dgrad_s);
-        p->t_down_dgrad_s = p->t_wg_down_s = p->t_wg_gu_s = 128;
+        p->t_wg_down_s = mx_row(p->t_wg_down_s);
+        p->t_wg_gu_s = mx_row(p->t_wg_gu_s);
+        p->t_down_dgrad_s = 128;
       }
       p->sp_wg_down_s = choose_wgrad_splits(p->t_wg_down_s, 1, d, NI, T);
       p->sp_wg_gu_s = choose_wgrad_splits(p->t_wg_gu_s, 1, 2 * NI, d, T);
@@ -942,7 +946,7 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
     WgradArgs a{};
     a.P = dyt.pay; a.Ps = dyt.sc; a.ldp = Apad; a.Q = ht.pay; a.Qs = ht.sc; a.ldq = Apad;
     a.offsets = pad; a.G = (int)E; a.Mtok = Apad; a.M = (int)d; a.N = (int)I; a.sub = (int)I;
-    MOE_TRY_STATUS(run_wgrad(p, WG_DOWN, 128, p->sp_wg_down, a, gr->dw_down, d * I, ws, "gemm_wgrad_down", s,
+    MOE_TRY_STATUS(run_wgrad(p, WG_DOWN, p->t_wg_down, p->sp_wg_down, a, gr->dw_down, d * I, ws, "gemm_wgrad_down", s,
                              DT_MXFP8));
   }
   if (T > 0) {
@@ -966,7 +970,7 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
     WgradArgs a{};
     a.P = dgut.pay; a.Ps = dgut.sc; a.ldp = Apad; a.Q = xt.pay; a.Qs = xt.sc; a.ldq = Apad;
     a.offsets = pad; a.G = (int)E; a.Mtok = Apad; a.M = (int)(2 * I); a.N = (int)d; a.sub = (int)d;
-    MOE_TRY_STATUS(run_wgrad(p, WG_GATE_UP, 128, p->sp_wg_gu, a, gr->dw_gate_up, 2 * I * d, ws,
+    MOE_TRY_STATUS(run_wgrad(p, WG_GATE_UP, p->t_wg_gu, p->sp_wg_gu, a, gr->dw_gate_up, 2 * I * d, ws,
                              "gemm_wgrad_gate_up", s, DT_MXFP8));
   }
   if (p->Ns > 0) {
@@ -999,7 +1003,7 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
       WgradArgs a{};
       a.P = sdyt.pay; a.Ps = sdyt.sc; a.ldp = Tpad; a.Q = sht.pay; a.Qs = sht.sc; a.ldq = Tpad;
       a.offsets = seg_pad + 2; a.G = 1; a.Mtok = Tpad; a.M = (int)d; a.N = (int)NI; a.sub = (int)Is;
-      MOE_TRY_STATUS(run_wgrad(p, WG_DOWN, 128, p->sp_wg_down_s, a, gr->dws_down, d * NI, ws,
+      MOE_TRY_STATUS(run_wgrad(p, WG_DOWN, p->t_wg_down_s, p->sp_wg_down_s, a, gr->dws_down, d * NI, ws,
                                "gemm_wgrad_down_shared", s, DT_MXFP8));
     }
     {
@@ -1007,7 +1011,7 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
       WgradArgs a{};
       a.P = sdgut.pay; a.Ps = sdgut.sc; a.ldp = Tpad; a.Q = sxt.pay; a.Qs = sxt.sc; a.ldq = Tpad;
       a.offsets = seg_pad + 2; a.G = 1; a.Mtok = Tpad; a.M = (int)(2 * NI); a.N = (int)d; a.sub = (int)d;
-      MOE_TRY_STATUS(run_wgrad(p, WG_GATE_UP, 128, p->sp_wg_gu_s, a, gr->dws_gate_up, 2 * NI * d, ws,
+      MOE_TRY_STATUS(run_wgrad(p, WG_GATE_UP, p->t_wg_gu_s, p->sp_wg_gu_s, a, gr->dws_gate_up, 2 * NI * d, ws,
                                "gemm_wgrad_gate_up_shared", s, DT_MXFP8));
     }
     if (T > 0) {

@@ -1637,7 +1637,8 @@ __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
   using TO = std::conditional_t<MX, __bf16, T>;
   constexpr int NW = WM * WN;
   static_assert(ES == 2 || MX || NW == 4, "the register-staged path runs 4 waves");
-  static_assert(!MX || (ES == 1 && BM == 128 && BN == 128 && NW == 4), "MX tiles are 128 x 128, 4 waves");
+  static_assert(!MX || (ES == 1 && ((BM == 128 && BN == 128 && NW == 4) || (BM == 256 && BN == 256 && NW == 8))),
+                "MX weight-gradient tiles: 128 x 128 with 4 waves or 256 x 256 with 8");
   using TOP = std::conditional_t<MX, __bf16, T>;
   using PO = Operand<TOP, BM, true>;
   using QO = Operand<TOP, BN, true>;
@@ -1726,8 +1727,11 @@ __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
       const int r = QD::row_of(wave, s2, lane);
       qoff[s2] = (uint32_t)(r * a.ldq + QD::gchunk(r, lane) * 16);
     }
-    const bool sq_side = wave >= 2;
-    const int sr = (wave & 1) * 64 + lane;
+    // scale rows: the first BM / 64 waves load P's rows 64 w .., the others Q's
+    static_assert(64 * NW == BM + BN, "one wave per 64 scale rows");
+    const bool sq_side = wave >= BM / 64;
+    const int swave = sq_side ? wave - BM / 64 : wave;
+    const int sr = swave * 64 + lane;
     const uint32_t soff = sq_side ? (uint32_t)((n0 + sr) * qls) : (uint32_t)((m0 + sr) * pls);
     const uint8_t* sbase = sq_side ? a.Qs : a.Ps;
     const int64_t ldp = a.ldp, ldq = a.ldq;
@@ -1739,7 +1743,7 @@ __device__ __forceinline__ void wgrad_body(const WgradArgs& a, char* smem) {
       for (int s2 = 0; s2 < PD::NI; ++s2) dma16(prs, stage + PD::lds_off(wave, s2), poff[s2]);
 #pragma unroll
       for (int s2 = 0; s2 < QD::NI; ++s2) dma16(qrs, stage + PD::BYTES + QD::lds_off(wave, s2), qoff[s2]);
-      char* sst = smem + SC_OFF + st * SSTAGE + (sq_side ? BM * 4 : 0) + (wave & 1) * 64 * 4;
+      char* sst = smem + SC_OFF + st * SSTAGE + (sq_side ? BM * 4 : 0) + swave * 64 * 4;
       dma4(make_rsrc(sbase + kc / 32, 0x7fffffffu), sst, soff);
     };
     constexpr int LPC = PD::NI + QD::NI + 1;
@@ -2050,6 +2054,15 @@ MOE_MX_ROW_KERNEL_256(moe_mx_gemm_gate_up_swiglu_256x256, OP_GU_FWD, EPI_SWIGLU_
 MOE_MX_ROW_KERNEL_256(moe_mx_gemm_down_256x256, OP_DOWN_FWD, EPI_STORE)
 MOE_MX_ROW_KERNEL_256(moe_mx_gemm_down_f32out_256x256, OP_DOWN_FWD, EPI_STORE_F32)
 MOE_MX_ROW_KERNEL_256(moe_mx_gemm_gate_up_dgrad_256x256, OP_GU_DGRAD, EPI_STORE)
+#define MOE_MX_WGRAD_KERNEL_256(NAME, F32)                                                            \
+  extern "C" __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) NAME(WgradArgs a) { \
+    extern __shared__ __attribute__((aligned(16))) char smem[];                                   \
+    wgrad_body<uint8_t, 256, 256, F32, 2, 4, true>(a, smem);                                      \
+  }
+MOE_MX_WGRAD_KERNEL_256(moe_mx_wgrad_down_256x256, 0)
+MOE_MX_WGRAD_KERNEL_256(moe_mx_wgrad_gate_up_256x256, 0)
+MOE_MX_WGRAD_KERNEL_256(moe_mx_wgrad_down_f32out_256x256, 1)
+MOE_MX_WGRAD_KERNEL_256(moe_mx_wgrad_gate_up_f32out_256x256, 1)
 MOE_MX_WGRAD_KERNEL(moe_mx_wgrad_down_128x128, 0)
 MOE_MX_WGRAD_KERNEL(moe_mx_wgrad_gate_up_128x128, 0)
 MOE_MX_WGRAD_KERNEL(moe_mx_wgrad_down_f32out_128x128, 1)
@@ -2123,8 +2136,10 @@ const KernelSet* kernel_set(int dt, int tile) {
     constexpr size_t mx_lds = 2 * (256 + 256) * MX_DKB + 2 * (256 + 256) * 4 + 64;
     static const KernelSet mx_256{moe_mx_gemm_gate_up_swiglu_256x256, moe_mx_gemm_down_256x256,
                                   moe_mx_gemm_down_f32out_256x256, nullptr, moe_mx_gemm_gate_up_dgrad_256x256,
-                                  nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, mx_lds, mx_lds,
-                                  nullptr};
+                                  nullptr, nullptr,
+                                  moe_mx_wgrad_down_256x256, moe_mx_wgrad_gate_up_256x256,
+                                  moe_mx_wgrad_down_f32out_256x256, moe_mx_wgrad_gate_up_f32out_256x256,
+                                  nullptr, mx_lds, mx_lds, nullptr};
     return &mx_256;
   }
   return nullptr;

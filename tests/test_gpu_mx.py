@@ -71,15 +71,17 @@ def test_mx_layer_matches_oracle(wl):
     PT.full_parity(wl)
 
 
-# The 256 x 256 MX tiles (8 waves) of the forward GEMMs and the gate/up
-# dgrad, forced on shapes that span several tiles with ragged and skewed
-# segments (the large workload takes them by default)
+# The 256 x 256 MX tiles (8 waves) of the forward GEMMs, the gate/up dgrad
+# and the weight gradients (those whose two sides are multiples of 256),
+# forced on shapes that span several tiles with ragged and skewed segments
+# (the large workload takes them by default)
 MX_256 = [SMALL_MX[0], SMALL_MX[1], SMALL_MX[3]]
 
 
 @pytest.mark.parametrize("wl", MX_256, ids=[w.name for w in MX_256])
 def test_mx_256_tiles_match_oracle(wl, monkeypatch):
     monkeypatch.setenv("MOE_ROW_TILE", "256")
+    monkeypatch.setenv("MOE_WGRAD_TILE", "256")
     PT.full_parity(wl)
 
 
