@@ -427,6 +427,8 @@ const char* moe_kernel_names(void);
  *                 average) the rounding remainders v - bf16(v) of "dgu" and
  *                 "wh", in bf16, which the expert weight gradients add
  *   "dgu"         [T*top_k, 2 d_ff]      [dG | dU] of the routed experts
+ *                 (MX-fp8 plans: only after moe_keep_intermediates(plan, 1),
+ *                 as "dgu_shared")
  *   "dx_perm"     [T*top_k, d_model]     input gradient of the expert rows
  *   "dgu_shared"  [T, 2 n_shared d_ff_shared]  [dG_s | dU_s] per shared expert
  *   "dx_shared"   [T, d_model]           input gradient of the shared experts
@@ -461,6 +463,17 @@ const char* moe_kernel_names(void);
  * unknown name or a region this plan does not have (no shared experts, not
  * an MX plan). */
 moe_status moe_workspace_region(moe_plan plan, const char* name, size_t* offset, size_t* bytes);
+
+/* MX-fp8 plans: the backward reads [dG | dU] (routed and shared) only through
+ * the two MX operands the SwiGLU-backward epilogue writes ("mx_dguq",
+ * "mx_dgut" and their shared counterparts), so by default it does not also
+ * store the act-dtype "dgu" and "dgu_shared" rows (T*top_k * 2 d_ff * 2 bytes
+ * of HBM writes saved).  keep = 1 makes later moe_backward calls on this plan
+ * store them too, for tests and debugging; keep = 0 restores the default.
+ * Other plans always store them (their next GEMMs read them): the call is
+ * accepted there and changes nothing.  Like the timing probe, it changes the
+ * plan and is not thread-safe.  MOE_ERR_NULL for a null plan. */
+moe_status moe_keep_intermediates(moe_plan plan, int keep);
 
 #ifdef __cplusplus
 }

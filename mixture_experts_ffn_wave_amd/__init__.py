@@ -26,6 +26,7 @@ from ._lib import (  # noqa: F401
     kernel_names,
     mx_quantize_rows,
     workspace_region,
+    keep_intermediates,
     LIB_PATH,
 )
 from .layer import MoELayer  # noqa: F401

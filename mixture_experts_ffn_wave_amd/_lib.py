@@ -80,6 +80,7 @@ SIGNATURES = {
     "moe_probe_read": (c_int32, [c_void_p, ctypes.POINTER(c_float), ctypes.POINTER(c_int32)]),
     "moe_kernel_names": (ctypes.c_char_p, []),
     "moe_mx_quantize_rows": (c_int32, [c_void_p, c_int32, c_int64, c_int32, c_void_p, c_void_p, c_void_p]),
+    "moe_keep_intermediates": (c_int32, [c_void_p, c_int32]),
     "moe_workspace_region": (c_int32, [c_void_p, ctypes.c_char_p, ctypes.POINTER(c_size_t),
                                        ctypes.POINTER(c_size_t)]),
 }
@@ -403,6 +404,12 @@ def workspace_region(plan, name):
     _check("moe_workspace_region", lib().moe_workspace_region(plan.handle, name.encode(), ctypes.byref(off),
                                                               ctypes.byref(nb)))
     return int(off.value), int(nb.value)
+
+
+def keep_intermediates(plan, keep=True):
+    """MX-fp8 plans: make moe_backward also store the act-dtype [dG | dU]
+    ("dgu", "dgu_shared"), which it otherwise reads only as MX operands."""
+    _check("moe_keep_intermediates", lib().moe_keep_intermediates(plan.handle, int(bool(keep))))
 
 
 def kernel_names():

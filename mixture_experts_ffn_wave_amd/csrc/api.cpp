@@ -67,6 +67,7 @@ struct moe_plan_s {
   MxBuf mx_dyq, mx_wdt, mx_dguq, mx_wgut, mx_dyt, mx_ht, mx_dgut, mx_xt;              // backward, routed
   MxBuf mx_sdyq, mx_swdt, mx_sdguq, mx_swgut, mx_sdyt, mx_sht, mx_sdgut, mx_sxt;      // backward, shared
   size_t o_mx_pad = 0, o_mx_seg1 = 0;  // padded expert offsets [E+1]; single-segment bounds [2] + pad [2]
+  bool keep_dgu = false;               // MX: also store the act-dtype [dG | dU] (moe_keep_intermediates)
   int64_t Apad = 0, Tpad = 0;          // padded token axes of the transposed operands
   // timing probe
   std::string probe_name;
@@ -934,8 +935,8 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
     RowGemmArgs a{};
     mx_pq(a, dyq, d, wdt, E * d, d);
     a.offsets = sv->offsets; a.G = (int)E; a.M = A; a.N = (int)I; a.K = (int)d; a.sub = (int)I;
-    a.C = dgu; a.ldc = 2 * I; a.aux = sv->gu; a.ldaux = 2 * I;
-    a.Hq = dguq.pay; a.Hs = dguq.sc;                 // the epilogue also writes [dG | dU] row-wise
+    a.C = p->keep_dgu ? dgu : nullptr; a.ldc = 2 * I; a.aux = sv->gu; a.ldaux = 2 * I;
+    a.Hq = dguq.pay; a.Hs = dguq.sc;                 // the epilogue writes [dG | dU] row-wise
     a.Tq = dgut.pay; a.Ts = dgut.sc; a.tpad = pad; a.ldt = Apad;   // and along the tokens, for dW_gu
     Probe pr(p, "gemm_down_dgrad_swiglu", s);
     MOE_TRY(launch_row_gemm(DT_MXFP8, OP_DOWN_DGRAD, EPI_SWIGLU_BWD, 128, a, s));
@@ -991,8 +992,8 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
       RowGemmArgs a{};
       mx_pq(a, sdyq, d, swdt, d, 0);
       a.offsets = nullptr; a.G = 1; a.M = T; a.N = (int)NI; a.K = (int)d; a.sub = (int)Is;
-      a.C = dgu_s; a.ldc = 2 * NI; a.aux = sv->gu_shared; a.ldaux = 2 * NI;
-      a.Hq = sdguq.pay; a.Hs = sdguq.sc;             // the epilogue also writes [dG | dU] row-wise
+      a.C = p->keep_dgu ? dgu_s : nullptr; a.ldc = 2 * NI; a.aux = sv->gu_shared; a.ldaux = 2 * NI;
+      a.Hq = sdguq.pay; a.Hs = sdguq.sc;             // the epilogue writes [dG | dU] row-wise
       a.Tq = sdgut.pay; a.Ts = sdgut.sc; a.ldt = Tpad;   // and along the tokens (one segment), for dWs_gu
       Probe pr(p, "gemm_down_dgrad_swiglu_shared", s);
       MOE_TRY(launch_row_gemm(DT_MXFP8, OP_DOWN_DGRAD, EPI_SWIGLU_BWD, 128, a, s));
@@ -1296,6 +1297,12 @@ moe_status moe_probe_enable(moe_plan p, const char* kernel, int max_launches) {
   }
   p->probe_name = name;
   p->probe_n = 0;
+  return MOE_OK;
+}
+
+moe_status moe_keep_intermediates(moe_plan p, int keep) {
+  if (!p) return MOE_ERR_NULL;
+  p->keep_dgu = keep != 0;
   return MOE_OK;
 }
 

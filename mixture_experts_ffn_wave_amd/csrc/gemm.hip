@@ -1454,10 +1454,13 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
             }
           }
         } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-          TO* dgu = static_cast<TO*>(a.C) + row * a.ldc + gcol0 + c * 8;
           const u32x4 dgraw = ld16(sp(0, sr, c)), duraw = ld16(sp(1, sr, c));
-          st16(dgu, dgraw);
-          st16(dgu + a.sub, duraw);
+          // (MX: the act-dtype [dG | dU] only on request, C non-null)
+          if (!MX || a.C) {
+            TO* dgu = static_cast<TO*>(a.C) + row * a.ldc + gcol0 + c * 8;
+            st16(dgu, dgraw);
+            st16(dgu + a.sub, duraw);
+          }
           if constexpr (WH_STAGED) {
             if (a.C2) st16(static_cast<TO*>(a.C2) + row * a.ldc2 + n0 + c * 8, ld16(sp(2, sr, c)));
           }
@@ -2171,6 +2174,8 @@ hipError_t launch_row_gemm(int dt, int op, int epi, int tile, const RowGemmArgs&
     default: return hipErrorInvalidValue;
   }
   if (!k) return hipErrorInvalidValue;
+  // every call writes C, except the MX SwiGLU backward, whose [dG | dU] codes are its product
+  if (!a.C && !(dt == DT_MXFP8 && op == OP_DOWN_DGRAD && a.Hq && a.Tq)) return hipErrorInvalidValue;
   if (a.C_lo && (op != OP_DOWN_DGRAD || !a.C2 || !a.C2_lo)) return hipErrorInvalidValue;
   // the f16 and MX-fp8 down dgrads write no w H rows
   if (op == OP_DOWN_DGRAD && a.C2 && (dt == DT_F16 || dt == DT_MXFP8)) return hipErrorInvalidValue;

@@ -151,6 +151,11 @@ class MoELayer:
         L.moe_backward(self.plan, self.saved(), dy, self.grads, self.ws, stream)
         return self.grads
 
+    def keep_intermediates(self, keep=True):
+        """MX-fp8 experts: let later backwards also store "dgu" and
+        "dgu_shared" (by default they exist only as MX operands)."""
+        L.keep_intermediates(self.plan, keep)
+
     def backward_intermediate(self, name):
         """View of an intermediate the last backward left in the workspace
         ("dy_perm", "dgu", "dx_perm", "dgu_shared", "dx_shared"; bf16 and f32

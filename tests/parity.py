@@ -109,6 +109,8 @@ def gpu_run(wl, inp, routing=None, intermediates=False, sel_bias=None, mask=None
     plan = plan_for(wl, b is not None)
     layer = MoELayer(plan)
     layer.write_x_perm = True                  # compared with the oracle's gather
+    if intermediates:
+        layer.keep_intermediates()             # MX plans: also store [dG | dU] in the act dtype
     dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
     layer.set_params(dev["x"], dev["w_router"], dev["w_gate_up"], dev["w_down"],
                      bias=(dev["bias"].float() if b is not None else None),

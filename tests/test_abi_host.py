@@ -254,6 +254,8 @@ def test_workspace_regions_lie_inside_the_workspace_and_do_not_overlap():
     q = L.Plan(T, d, E, k, I)                                  # no shared experts: no shared regions
     assert lib.moe_workspace_region(q.handle, b"dgu_shared", ctypes.byref(off), ctypes.byref(nb)) == MOE_ERR_INVALID
     assert lib.moe_workspace_region(q.handle, b"dgu", ctypes.byref(off), ctypes.byref(nb)) == MOE_OK
+    assert lib.moe_keep_intermediates(q.handle, 1) == MOE_OK     # accepted, no effect on a bf16 plan
+    assert lib.moe_keep_intermediates(None, 1) == MOE_ERR_NULL
     q.close()
 
 

@@ -118,6 +118,51 @@ def test_mx_two_runs_are_bitwise_identical():
             assert np.array_equal(v, b[key]), key
 
 
+def test_mx_backward_without_kept_dgu():
+    """By default an MX backward stores [dG | dU] only as its two MX operands:
+    the act-dtype "dgu" / "dgu_shared" regions keep what was there, and every
+    gradient and every MX operand is bitwise what a backward that also stores
+    them (moe_keep_intermediates) gives."""
+    wl = W("t700_d256_e8k2_i256_s1x128_mx_nodgu", T=700, d=256, E=8, k=2, I=256, n_shared=1, I_shared=128,
+           expert_dtype="mxfp8")
+    inp = MI.make_inputs(wl)
+    from mixture_experts_ffn_wave_amd import MoELayer, workspace_region
+    dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+    runs = []
+    for keep in (False, True):
+        layer = MoELayer(PT.plan_for(wl, inp.get("bias") is not None))
+        layer.write_x_perm = True
+        layer.set_params(dev["x"], dev["w_router"], dev["w_gate_up"], dev["w_down"],
+                         ws_gate_up=dev.get("ws_gate_up"), ws_down=dev.get("ws_down"))
+        if keep:
+            layer.keep_intermediates()
+        layer.forward()
+        for n in ("dgu", "dgu_shared"):
+            layer.backward_intermediate(n).fill_(7.0)
+        layer.backward(dev["dy"])
+        torch.cuda.synchronize()
+        off, nb = workspace_region(layer.plan, "mx_pad")
+        end = int(layer.ws[off:off + nb].view(torch.int32)[-1])         # padded token axis in use
+        A, I = wl.T * wl.k, wl.I
+        mx = {}
+        NI = wl.n_shared * wl.I_shared
+        for n, rows in (("mx_dguq", A), ("mx_dgut", 2 * I), ("mx_sdguq", wl.T), ("mx_sdgut", 2 * NI)):
+            for r in (n, n + ".scales"):
+                off, nb = workspace_region(layer.plan, r)
+                v = PT.to_np(layer.ws[off:off + nb]).reshape(rows, -1)
+                # the routed token axis has headroom past the last segment, never written
+                mx[r] = v[:, :end // (32 if r.endswith(".scales") else 1)] if n == "mx_dgut" else v
+        runs.append((layer, {n: PT.to_np(t) for n, t in layer.grads.items()}, mx))
+    (quiet, g0, m0), (kept, g1, m1) = runs
+    for n in ("dgu", "dgu_shared"):
+        assert bool((quiet.backward_intermediate(n) == 7.0).all()), n
+        assert not bool((kept.backward_intermediate(n) == 7.0).all()), n
+    for n in g0:
+        assert np.array_equal(g0[n], g1[n]), n
+    for n in m0:
+        assert np.array_equal(m0[n], m1[n]), n
+
+
 def test_mx_gather_on_load_equals_the_x_perm_path():
     """The gate/up GEMM reading x's codes through perm_token, and the weight
     gradient gathering x's rows, quantise the same values as the x_perm path

@@ -101,6 +101,7 @@ def run_layer(wl, inp, gather):
     layer = MoELayer(PT.plan_for(wl, b is not None))
     layer.mx_gather = gather
     layer.write_x_perm = True
+    layer.keep_intermediates()                 # the bf16 [dG | dU] the codes are checked against
     dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
     layer.set_params(dev["x"], dev["w_router"], dev["w_gate_up"], dev["w_down"],
                      bias=(dev["bias"].float() if b is not None else None),
