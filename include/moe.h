@@ -251,7 +251,7 @@ typedef struct {
   void* gu;                /* out [T*k, 2I]: [G | U] per row, saved for backward; f32 for a
                               bf16 layer with bf16 experts, bf16 for MX-fp8 experts, else act */
   void* h;                 /* out [T*k, I] act: silu(G) * U */
-  void* y_perm;            /* out [T*k, d]: H W_d^T; f32 for a bf16 layer or MX-fp8 experts, else act */
+  void* y_perm;            /* out [T*k, d]: H W_d^T; f32 for a bf16 layer with bf16 experts, else act */
   const void* x;           /* [T, d] act (shared experts' input) */
   const void* ws_gate_up;  /* [Ns, 2Is, d] act */
   const void* ws_down;     /* [Ns, d, Is] act */

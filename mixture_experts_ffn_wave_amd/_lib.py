@@ -172,7 +172,7 @@ class Plan:
         # storage of the saved [G | U], of Y_perm and of the experts' input
         # gradient rows (include/moe.h): f32 in a bf16 layer with bf16 experts
         if self.mx:
-            self.gu_dtype, self.y_perm_dtype, self.dx_rows_dtype = torch.bfloat16, torch.float32, dtype
+            self.gu_dtype = self.y_perm_dtype = self.dx_rows_dtype = dtype            # bf16
         else:
             wide = torch.float32 if dtype == torch.bfloat16 else dtype
             self.gu_dtype = self.y_perm_dtype = self.dx_rows_dtype = wide

@@ -866,9 +866,9 @@ moe_status mx_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, hipStream_
     RowGemmArgs a{};
     mx_pq(a, hq, I, wd, I, d * I);
     a.offsets = f->offsets; a.G = (int)E; a.M = A; a.N = (int)d; a.K = (int)I; a.sub = (int)I;
-    a.C = f->y_perm; a.ldc = d;
+    a.C = f->y_perm; a.ldc = d;                      // Y_perm in bf16 (the MX layer's error dwarfs its rounding)
     Probe pr(p, "gemm_down", s);
-    MOE_TRY(launch_row_gemm(DT_MXFP8, OP_DOWN_FWD, EPI_STORE_F32, p->t_down, a, s));
+    MOE_TRY(launch_row_gemm(DT_MXFP8, OP_DOWN_FWD, EPI_STORE, p->t_down, a, s));
   }
   if (p->Ns > 0) {
     const int64_t Is = p->Is, NI = p->Ns * p->Is, T = p->T;
@@ -907,7 +907,7 @@ moe_status moe_combine(moe_plan p, const void* y_perm, const int32_t* inv_perm, 
   if (!y_perm || !inv_perm || !topk_w || !y) return MOE_ERR_NULL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   CombineArgs a{y_perm, inv_perm, topk_w, y_shared, y, p->T, p->d, p->k,
-                p->mx || p->dt == DT_F32 || f32_intermediates(p->dt, p->mx)};
+                p->dt == DT_F32 || f32_intermediates(p->dt, p->mx)};
   Probe pr(p, "combine", s);
   return hip_status(launch_combine(p->dt, a, s));
 }
@@ -1076,7 +1076,7 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
       // routing-weight gradient g = <dy, Y_perm> here (their Y_perm is the
       // quantised forward's), the others the per-row weights (the down
       // dgrad forms g from dy W_d and the saved G, U)
-      CombineBwdArgs a{dy, static_cast<const float*>(sv->y_perm), sv->inv_perm, sv->topk_w, dy_perm,
+      CombineBwdArgs a{dy, sv->y_perm, sv->inv_perm, sv->topk_w, dy_perm,
                        p->mx ? g : nullptr, p->T, d, k};
       if (!p->mx) a.wsorted = wsorted;
       if (wh_rows(p)) a.copy = 1;                    // the routing weight goes on the H side

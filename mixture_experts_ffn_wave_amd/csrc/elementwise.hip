@@ -114,7 +114,7 @@ __device__ __forceinline__ void mx_row_codes(u32x4 raw, bool ok, uint8_t* q, uin
 template <typename T, int KG, bool MXQ, bool GD>
 __global__ void __launch_bounds__(NT) combine_bwd_kernel(CombineBwdArgs a) {
   constexpr int VR = 16 / sizeof(T);
-  constexpr int YC = VR / 4;
+  const T* yperm = static_cast<const T*>(a.y_perm);   // (GD) in the activation dtype
   const int lane = threadIdx.x & 63;
   const int64_t waves = (int64_t)gridDim.x * (NT / 64);
   const int64_t rowbytes = (int64_t)a.d * sizeof(T);
@@ -145,26 +145,22 @@ __global__ void __launch_bounds__(NT) combine_bwd_kernel(CombineBwdArgs a) {
         if constexpr (MXQ && sizeof(T) == 2) {
           if (a.dq && j0 == 0) mx_row_codes<T>(dv.raw, ok, a.dq + t * a.d + (int64_t)c * 8, a.dqs + t * (a.d / 32) + c / 4, c);
         }
-        f32x4 yv[KG][YC];
+        Chunk<T> yv[KG];
 #pragma unroll
         for (int u = 0; u < KG; ++u) {
           const bool use = GD && ok && j0 + u < a.k && r[u] >= 0;
-          const f32x4* src = reinterpret_cast<const f32x4*>(a.y_perm + (int64_t)r[u] * a.d + (int64_t)c * VR);
-#pragma unroll
-          for (int q = 0; q < YC; ++q) yv[u][q] = use ? src[q] : (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+          yv[u].raw = use ? ld16(yperm + (int64_t)r[u] * a.d + (int64_t)c * VR) : (u32x4){0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int u = 0; u < KG; ++u) {
           if (j0 + u < a.k && r[u] >= 0) {                  // wave-uniform
             Chunk<T> o;
 #pragma unroll
-            for (int q = 0; q < YC; ++q)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const float dd = to_f32<T>(dv.e[4 * q + i]);
-                if constexpr (GD) dot[u] = fmaf(dd, yv[u][q][i], dot[u]);
-                o.e[4 * q + i] = a.copy ? dv.e[4 * q + i] : from_f32<T>(w[u] * dd);
-              }
+            for (int i = 0; i < VR; ++i) {
+              const float dd = to_f32<T>(dv.e[i]);
+              if constexpr (GD) dot[u] = fmaf(dd, to_f32<T>(yv[u].e[i]), dot[u]);
+              o.e[i] = a.copy ? dv.e[i] : from_f32<T>(w[u] * dd);
+            }
             if (ok) st16(dyp + (int64_t)r[u] * rowbytes + (int64_t)c * 16, o.raw);
             if constexpr (MXQ && sizeof(T) == 2) {
               // MX-fp8 experts: the row-wise codes of the stored values; the
@@ -941,13 +937,13 @@ hipError_t launch_combine_bwd(int dt, const CombineBwdArgs& a, hipStream_t s) {
   int64_t grid = (a.T + 3) / 4;
   if (grid > 8192) grid = 8192;
   switch (dt) {
-    // the MX row-code writes are a separate instantiation, so the plain
-    // kernel carries none of their code
-    // g from y_perm (MX-fp8 experts) or the per-row weights (the down dgrad
-    // then forms g); the MX row-code writes are a separate instantiation
+    // g from y_perm (MX-fp8 experts; y_perm in the activation dtype) or the
+    // per-row weights (the down dgrad then forms g); the MX row-code writes
+    // are a separate instantiation, so the plain kernel carries none of their
+    // code.  A bf16 layer with bf16 experts keeps Y_perm in f32: no g here.
     case DT_BF16:
       if (a.q || a.dq) MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, __bf16, true, true);
-      else if (a.g) MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, __bf16, false, true);
+      else if (a.g) return hipErrorInvalidValue;
       else MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, __bf16, false, false);
       break;
     case DT_F16:

@@ -220,9 +220,9 @@ struct CombineArgs {
 hipError_t launch_combine(int dt, const CombineArgs& a, hipStream_t s);
 
 struct CombineBwdArgs {
-  const void* dy; const float* y_perm; const int32_t* inv; const float* wts;
+  const void* dy; const void* y_perm; const int32_t* inv; const float* wts;
   void* dy_perm;  // [T*k, d]: row inv[t, j] = wts[t, j] dy[t], or dy[t] itself when `copy`
-  float* g;       // [T, k]: g = <dy, y_perm row> (y_perm f32, MX-fp8 experts), or nullptr
+  float* g;       // [T, k]: g = <dy, y_perm row> (y_perm in the act dtype: MX-fp8 experts), or nullptr
   int64_t T; int d, k;
   // without g: the routing weight of each expert-sorted row, wsorted[inv[t, j]] = wts[t, j]
   float* wsorted = nullptr;

@@ -75,7 +75,9 @@ def gu_dtype(wl):
 
 
 def y_perm_dtype(wl):
-    return "f32" if wl.expert_dtype == "mxfp8" or wl.dtype == "bf16" else wl.dtype
+    if wl.expert_dtype == "mxfp8":
+        return "bf16"
+    return "f32" if wl.dtype == "bf16" else wl.dtype
 
 
 def plan_for(wl, has_bias):
@@ -157,7 +159,9 @@ def oracle_inputs(inp):
 
 
 def storage_rounding(wl):
-    """The ``store`` rounding of a layer whose values are kept in wl.dtype."""
+    """The ``store`` rounding of a layer whose values are kept in wl.dtype
+    (kind "f32": the router's dz and Y_perm stay in f32; an MX layer keeps
+    Y_perm in bf16, whose half-ulp rounding its comparisons allow)."""
     return lambda a, kind: O.round_to_format(a, "f32" if kind == "f32" else wl.dtype)
 
 
@@ -416,7 +420,7 @@ def compare_mx_stepwise(wl, gpu, fwd, f64, st):
         r0, r1 = off[e], off[e + 1]
         if r1 > r0:
             y_perm[r0:r1] = sr(O.expert_down_step(H[r0:r1], f64["w_down"][e], q), "f32")
-    check_close("Y_perm", gpu["y_perm"], y_perm, c, "f32", 1.0)
+    check_close("Y_perm", gpu["y_perm"], y_perm, c, y_perm_dtype(wl), 1.0)
     y_shared = None
     if wl.n_shared:
         Is = wl.I_shared
@@ -494,7 +498,7 @@ def compare_mx_end_to_end(wl, gpu, fwd, bwd):
     every output."""
     dt = wl.dtype
     pairs = [("G", gpu["gu"][:, :wl.I], fwd["g"], dt), ("U", gpu["gu"][:, wl.I:], fwd["u"], dt),
-             ("H", gpu["h"], fwd["h"], dt), ("Y_perm", gpu["y_perm"], fwd["y_perm"], "f32"),
+             ("H", gpu["h"], fwd["h"], dt), ("Y_perm", gpu["y_perm"], fwd["y_perm"], y_perm_dtype(wl)),
              ("y", gpu["y"], fwd["y"], dt), ("dx", gpu["dx"], bwd["dx"], dt),
              ("dW_router", gpu["dw_router"], bwd["dw_router"], dt), ("dbias", gpu["dbias"], bwd["dbias"], "f32"),
              ("dW_gate_up", gpu["dw_gate_up"], bwd["dw_gate_up"], dt), ("dW_down", gpu["dw_down"], bwd["dw_down"], dt)]
