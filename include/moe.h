@@ -139,6 +139,9 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out);
 void moe_plan_destroy(moe_plan plan);
 /* Bytes of device workspace the compute calls need (same for all calls). */
 size_t moe_workspace_bytes(moe_plan plan);
+/* Bytes of the optional MX-fp8 saved-codes buffer (moe_ffn_args.mx_saved);
+ * 0 for a NULL plan or a plan without MX-fp8 experts. */
+size_t moe_mx_saved_bytes(moe_plan plan);
 /* Static description of a status code. */
 const char* moe_status_string(moe_status status);
 /* Library version string, e.g. "moe-ffn-mi355x 0.1 gfx950". */
@@ -263,6 +266,15 @@ typedef struct {
    * token (x must then be set) instead of quantising the T*k rows of x_perm;
    * x_perm is not read.  NULL keeps the x_perm path.  Ignored otherwise. */
   const int32_t* perm_token;
+  /* Optional, MX-fp8 plans: a buffer of moe_mx_saved_bytes() bytes that the
+   * forward fills with operand codes the backward would otherwise make
+   * (pass it on as moe_saved.mx_saved): the weights' codes along the
+   * backward's reduction axes (W_gu along 2 d_ff, W_d along d, the shared
+   * experts' likewise), written by the same pass that reads the weights for
+   * the forward's codes, and H's codes along each expert's tokens (and the
+   * shared experts' H along the T tokens), written by the gate/up epilogue
+   * beside H.  NULL: the backward quantises them itself.  Ignored otherwise. */
+  void* mx_saved;
 } moe_ffn_args;
 
 /* Routed experts as grouped GEMMs over the expert segments of x_perm (gate/up
@@ -312,6 +324,10 @@ typedef struct {
    * gate/up projection gathers x's rows by it instead of reading x_perm
    * (which may then be NULL). */
   const int32_t* perm_token;
+  /* Optional, MX-fp8 plans: the moe_ffn_args.mx_saved buffer the forward of
+   * this step filled (the weights unchanged since).  NULL: the backward
+   * quantises the weights and H itself.  Ignored otherwise. */
+  const void* mx_saved;
 } moe_saved;
 
 /* Gradient outputs (act dtype unless noted).  Every weight gradient is fully
@@ -474,6 +490,15 @@ moe_status moe_workspace_region(moe_plan plan, const char* name, size_t* offset,
  * accepted there and changes nothing.  Like the timing probe, it changes the
  * plan and is not thread-safe.  MOE_ERR_NULL for a null plan. */
 moe_status moe_keep_intermediates(moe_plan plan, int keep);
+
+/* Byte offset and size, inside the MX-fp8 saved-codes buffer
+ * (moe_ffn_args.mx_saved), of the operands it holds, named and laid out as
+ * the workspace's MX operands of moe_workspace_region (payload, or
+ * "<name>.scales"): "mx_wdt", "mx_wgut", "mx_ht" and, with shared experts,
+ * "mx_swdt", "mx_swgut", "mx_sht".  For tests and debugging.  MOE_ERR_NULL
+ * for a null argument, MOE_ERR_INVALID for another name or a plan without
+ * MX-fp8 experts (or shared experts, for the shared names). */
+moe_status moe_mx_saved_region(moe_plan plan, const char* name, size_t* offset, size_t* bytes);
 
 #ifdef __cplusplus
 }

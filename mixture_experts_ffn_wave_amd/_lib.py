@@ -31,10 +31,10 @@ class MoeConfig(ctypes.Structure):
 
 
 _FFN_FIELDS = ["x_perm", "offsets", "w_gate_up", "w_down", "gu", "h", "y_perm", "x", "ws_gate_up",
-               "ws_down", "gu_shared", "h_shared", "y_shared", "perm_token"]
+               "ws_down", "gu_shared", "h_shared", "y_shared", "perm_token", "mx_saved"]
 _SAVED_FIELDS = ["x", "w_router", "probs", "topk_idx", "topk_w", "counts", "offsets", "inv_perm",
                  "x_perm", "gu", "h", "y_perm", "w_gate_up", "w_down", "ws_gate_up", "ws_down",
-                 "gu_shared", "h_shared", "real_mask", "real_counts", "perm_token"]
+                 "gu_shared", "h_shared", "real_mask", "real_counts", "perm_token", "mx_saved"]
 _GRAD_FIELDS = ["dx", "dw_router", "dbias", "dw_gate_up", "dw_down", "dws_gate_up", "dws_down"]
 
 
@@ -61,6 +61,7 @@ SIGNATURES = {
     "moe_plan_create": (c_int32, [ctypes.POINTER(MoeConfig), ctypes.POINTER(c_void_p)]),
     "moe_plan_destroy": (None, [c_void_p]),
     "moe_workspace_bytes": (c_size_t, [c_void_p]),
+    "moe_mx_saved_bytes": (c_size_t, [c_void_p]),
     "moe_status_string": (ctypes.c_char_p, [c_int32]),
     "moe_version": (ctypes.c_char_p, []),
     "moe_route": (c_int32, [c_void_p] * 8),
@@ -81,6 +82,8 @@ SIGNATURES = {
     "moe_kernel_names": (ctypes.c_char_p, []),
     "moe_mx_quantize_rows": (c_int32, [c_void_p, c_int32, c_int64, c_int32, c_void_p, c_void_p, c_void_p]),
     "moe_keep_intermediates": (c_int32, [c_void_p, c_int32]),
+    "moe_mx_saved_region": (c_int32, [c_void_p, ctypes.c_char_p, ctypes.POINTER(c_size_t),
+                                      ctypes.POINTER(c_size_t)]),
     "moe_workspace_region": (c_int32, [c_void_p, ctypes.c_char_p, ctypes.POINTER(c_size_t),
                                        ctypes.POINTER(c_size_t)]),
 }
@@ -187,6 +190,10 @@ class Plan:
     def workspace_bytes(self):
         return int(lib().moe_workspace_bytes(self._h))
 
+    def mx_saved_bytes(self):
+        """Bytes of the optional MX-fp8 saved-codes buffer (0 unless MX)."""
+        return int(lib().moe_mx_saved_bytes(self._h))
+
     def close(self):
         if getattr(self, "_h", None) and self._h.value:
             lib().moe_plan_destroy(self._h)
@@ -288,7 +295,7 @@ def moe_permute_noalloc(plan, topk_idx, x, counts, offsets, perm_token, inv_perm
 
 def moe_expert_ffn(plan, x_perm, offsets, w_gate_up, w_down, gu, h, y_perm, x=None, ws_gate_up=None,
                    ws_down=None, gu_shared=None, h_shared=None, y_shared=None, ws=None, stream=None,
-                   perm_token=None):
+                   perm_token=None, mx_saved=None):
     T, d, E, k, I, dt = plan.T, plan.d, plan.E, plan.k, plan.I, plan.dtype
     A = T * k
     if x_perm is not None or perm_token is None:   # x_perm may be omitted when MX experts gather on load
@@ -315,6 +322,9 @@ def moe_expert_ffn(plan, x_perm, offsets, w_gate_up, w_down, gu, h, y_perm, x=No
         _need(x, "x", (T, d), dt)
         args.perm_token = perm_token.data_ptr()
         args.x = x.data_ptr()
+    if mx_saved is not None:
+        _need(mx_saved, "mx_saved", (plan.mx_saved_bytes(),), torch.uint8)
+        args.mx_saved = mx_saved.data_ptr()
     st = lib().moe_expert_ffn(plan.handle, ctypes.byref(args), _ptr(ws), ws.numel() if ws is not None else 0,
                               _stream(stream))
     _check("moe_expert_ffn", st)
@@ -403,6 +413,15 @@ def workspace_region(plan, name):
     off, nb = c_size_t(), c_size_t()
     _check("moe_workspace_region", lib().moe_workspace_region(plan.handle, name.encode(), ctypes.byref(off),
                                                               ctypes.byref(nb)))
+    return int(off.value), int(nb.value)
+
+
+def mx_saved_region(plan, name):
+    """(byte offset, bytes) of an operand in the MX saved-codes buffer
+    (moe_mx_saved_region)."""
+    off, nb = c_size_t(), c_size_t()
+    _check("moe_mx_saved_region", lib().moe_mx_saved_region(plan.handle, name.encode(), ctypes.byref(off),
+                                                            ctypes.byref(nb)))
     return int(off.value), int(nb.value)
 
 

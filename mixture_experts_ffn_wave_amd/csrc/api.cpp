@@ -68,6 +68,10 @@ struct moe_plan_s {
   MxBuf mx_sdyq, mx_swdt, mx_sdguq, mx_swgut, mx_sdyt, mx_sht, mx_sdgut, mx_sxt;      // backward, shared
   size_t o_mx_pad = 0, o_mx_seg1 = 0;  // padded expert offsets [E+1]; single-segment bounds [2] + pad [2]
   bool keep_dgu = false;               // MX: also store the act-dtype [dG | dU] (moe_keep_intermediates)
+  // the optional saved-codes buffer (offsets into it): the weights along the
+  // backward's reduction axes and H along the tokens, routed and shared
+  MxBuf sv_wdt, sv_wgut, sv_ht, sv_swdt, sv_swgut, sv_sht;
+  size_t sv_total = 0;
   int64_t Apad = 0, Tpad = 0;          // padded token axes of the transposed operands
   // timing probe
   std::string probe_name;
@@ -509,6 +513,24 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
     p->mx_xt = mxb(d, p->Apad);
     p->o_mx_pad = take((size_t)(E + 1) * 4);
     p->o_mx_seg1 = take(4 * 4);
+    {
+      size_t so = 0;
+      auto sb = [&](int64_t rows, int64_t K) {
+        moe_plan_s::MxBuf b;
+        b.pay = so; so += ((size_t)rows * K + 255) / 256 * 256;
+        b.sc = so; so += ((size_t)rows * (K / 32) + 255) / 256 * 256;
+        return b;
+      };
+      p->sv_wdt = sb(I, E * d);
+      p->sv_wgut = sb(d, E * 2 * I);
+      p->sv_ht = sb(I, p->Apad);
+      if (NI > 0) {
+        p->sv_swdt = sb(NI, d);
+        p->sv_swgut = sb(d, 2 * NI);
+        p->sv_sht = sb(NI, p->Tpad);
+      }
+      p->sv_total = so;
+    }
     if (NI > 0) {
       p->mx_sxq = mxb(T, d);
       p->mx_shq = mxb(T, NI);
@@ -532,6 +554,7 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
 void moe_plan_destroy(moe_plan plan) { delete plan; }
 
 size_t moe_workspace_bytes(moe_plan plan) { return plan ? plan->ws_total : 0; }
+size_t moe_mx_saved_bytes(moe_plan plan) { return (plan && plan->mx) ? plan->sv_total : 0; }
 
 // Weight-gradient GEMM into `out` ([G][group_elems], act dtype), split over
 // tokens `splits` ways through f32 partials when splits > 1.
@@ -596,6 +619,11 @@ struct MxOp { uint8_t* pay; uint8_t* sc; };
 MxOp mxop(void* ws, const moe_plan_s::MxBuf& b) {
   return {reinterpret_cast<uint8_t*>(wsp(ws, b.pay)), reinterpret_cast<uint8_t*>(wsp(ws, b.sc))};
 }
+// a region of the saved-codes buffer (moe_ffn_args / moe_saved .mx_saved)
+MxOp svop(const void* saved, const moe_plan_s::MxBuf& b) {
+  uint8_t* base = static_cast<uint8_t*>(const_cast<void*>(saved));
+  return {base + b.pay, base + b.sc};
+}
 // rows operand: element (r, k) at in + (k / sub) * block_stride + r * ld_in + k % sub
 moe_status mx_rows(moe_plan p, hipStream_t s, const void* in, int64_t ld_in, int64_t block_stride, int sub,
                    int64_t R, int K, MxOp o) {
@@ -605,10 +633,13 @@ moe_status mx_rows(moe_plan p, hipStream_t s, const void* in, int64_t ld_in, int
   return MOE_OK;
 }
 // transposed operand: the token axis of in [tokens][C] becomes K
+// rq (optional): the row-wise codes of the same input too, row i at
+// rq.pay + i * rld (scales rq.sc + i * rld / 32)
 moe_status mx_cols(moe_plan p, hipStream_t s, const void* in, int64_t ld_in, int C, const int32_t* seg,
                    const int32_t* pad, int G, int seg_len, int64_t nblk, int64_t k0, int64_t Kpad, int64_t row0,
-                   MxOp o, const int32_t* gather = nullptr) {
+                   MxOp o, const int32_t* gather = nullptr, MxOp rq = {nullptr, nullptr}, int64_t rld = 0) {
   MxColsArgs a{in, ld_in, C, seg, pad, G, seg_len, nblk, k0, Kpad, row0, o.pay, o.sc, gather};
+  a.rq = rq.pay; a.rqs = rq.sc; a.rld = rld; a.rlds = rld / 32;
   Probe pr(p, "mx_quantize", s);
   MOE_TRY(launch_mx_quant_cols(p->dt, a, s));
   return MOE_OK;
@@ -850,7 +881,19 @@ moe_status mx_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, hipStream_
   const MxOp xrows = (gather && p->Ns > 0) ? mxop(ws, p->mx_sxq) : xq;
   if (gather) MOE_TRY_STATUS(mx_rows(p, s, f->x, d, 0, (int)d, p->T, (int)d, xrows));
   else MOE_TRY_STATUS(mx_rows(p, s, f->x_perm, d, 0, (int)d, A, (int)d, xq));
-  MOE_TRY_STATUS(mx_rows(p, s, f->w_gate_up, d, 0, (int)d, E * 2 * I, (int)d, wgu));
+  // with a saved-codes buffer: the weights' backward codes from the pass that
+  // makes their row-wise ones, and H's token-axis codes from the epilogue
+  const void* sv = f->mx_saved;
+  int32_t* pad = reinterpret_cast<int32_t*>(wsp(ws, p->o_mx_pad));
+  if (sv) {
+    Probe pr(p, "mx_quantize", s);
+    MOE_TRY(launch_mx_pad_offsets(f->offsets, pad, (int)E, 128, s));
+  }
+  if (sv)   // W_gu [E][2I][d]: along d (forward) and along each expert's 2I (dX = [dG | dU] W_gu)
+    MOE_TRY_STATUS(mx_cols(p, s, f->w_gate_up, d, (int)d, nullptr, nullptr, (int)E, (int)(2 * I), E * 2 * I / 32, 0,
+                           E * 2 * I, 0, svop(sv, p->sv_wgut), nullptr, wgu, d));
+  else
+    MOE_TRY_STATUS(mx_rows(p, s, f->w_gate_up, d, 0, (int)d, E * 2 * I, (int)d, wgu));
   {
     RowGemmArgs a{};
     mx_pq(a, xrows, d, wgu, d, 2 * I * d);
@@ -858,10 +901,18 @@ moe_status mx_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, hipStream_
     a.offsets = f->offsets; a.G = (int)E; a.M = A; a.N = (int)I; a.K = (int)d; a.sub = (int)I;
     a.C = f->gu; a.ldc = 2 * I; a.C2 = f->h; a.ldc2 = I;
     a.Hq = hq.pay; a.Hs = hq.sc;                     // the epilogue also quantises H row-wise
+    if (sv) {                                        // and along the tokens, for dW_d
+      const MxOp ht = svop(sv, p->sv_ht);
+      a.Tq = ht.pay; a.Ts = ht.sc; a.tpad = pad; a.ldt = p->Apad;
+    }
     Probe pr(p, "gemm_gate_up_swiglu", s);
     MOE_TRY(launch_row_gemm(DT_MXFP8, OP_GU_FWD, EPI_SWIGLU_FWD, p->t_gu, a, s));
   }
-  MOE_TRY_STATUS(mx_rows(p, s, f->w_down, I, 0, (int)I, E * d, (int)I, wd));
+  if (sv)   // W_d [E][d][I]: along I (forward) and along each expert's d (dH = dY W_d)
+    MOE_TRY_STATUS(mx_cols(p, s, f->w_down, I, (int)I, nullptr, nullptr, (int)E, (int)d, E * d / 32, 0, E * d, 0,
+                           svop(sv, p->sv_wdt), nullptr, wd, I));
+  else
+    MOE_TRY_STATUS(mx_rows(p, s, f->w_down, I, 0, (int)I, E * d, (int)I, wd));
   {
     RowGemmArgs a{};
     mx_pq(a, hq, I, wd, I, d * I);
@@ -875,18 +926,37 @@ moe_status mx_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, hipStream_
     const MxOp sxq = mxop(ws, p->mx_sxq), shq = mxop(ws, p->mx_shq), swgu = mxop(ws, p->mx_swgu),
                swd = mxop(ws, p->mx_swd);
     if (!gather) MOE_TRY_STATUS(mx_rows(p, s, f->x, d, 0, (int)d, T, (int)d, sxq));
-    MOE_TRY_STATUS(mx_rows(p, s, f->ws_gate_up, d, 0, (int)d, 2 * NI, (int)d, swgu));
+    if (sv) {   // W_sgu[s] [2Is][d]: rows s 2Is.. of [2 NI][d], and K positions s 2Is.. of [d][2 NI]
+      for (int sh = 0; sh < p->Ns; ++sh)
+        MOE_TRY_STATUS(mx_cols(p, s, static_cast<const char*>(f->ws_gate_up) + (int64_t)sh * 2 * Is * d * 2, d,
+                               (int)d, nullptr, nullptr, 1, (int)(2 * Is), 2 * Is / 32, sh * 2 * Is, 2 * NI, 0,
+                               svop(sv, p->sv_swgut), nullptr,
+                               {swgu.pay + sh * 2 * Is * d, swgu.sc + sh * 2 * Is * (d / 32)}, d));
+    } else {
+      MOE_TRY_STATUS(mx_rows(p, s, f->ws_gate_up, d, 0, (int)d, 2 * NI, (int)d, swgu));
+    }
     {
       RowGemmArgs a{};
       mx_pq(a, sxq, d, swgu, d, 0);
       a.offsets = nullptr; a.G = 1; a.M = T; a.N = (int)NI; a.K = (int)d; a.sub = (int)Is;
       a.C = f->gu_shared; a.ldc = 2 * NI; a.C2 = f->h_shared; a.ldc2 = NI;
       a.Hq = shq.pay; a.Hs = shq.sc;                 // the epilogue also quantises H row-wise
+      if (sv) {                                      // and along the T tokens, for dWs_d
+        const MxOp sht = svop(sv, p->sv_sht);
+        a.Tq = sht.pay; a.Ts = sht.sc; a.ldt = p->Tpad;
+      }
       Probe pr(p, "gemm_gate_up_swiglu_shared", s);
       MOE_TRY(launch_row_gemm(DT_MXFP8, OP_GU_FWD, EPI_SWIGLU_FWD, p->t_gu_s, a, s));
     }
     // shared down weights [Ns][d][Is] concatenated along K into [d][NI]
-    MOE_TRY_STATUS(mx_rows(p, s, f->ws_down, Is, d * Is, (int)Is, d, (int)NI, swd));
+    if (sv) {   // W_sd[s] [d][Is]: columns s Is.. of [d][NI], and rows s Is.. of [NI][d]
+      for (int sh = 0; sh < p->Ns; ++sh)
+        MOE_TRY_STATUS(mx_cols(p, s, static_cast<const char*>(f->ws_down) + (int64_t)sh * d * Is * 2, Is, (int)Is,
+                               nullptr, nullptr, 1, (int)d, d / 32, 0, d, sh * Is, svop(sv, p->sv_swdt), nullptr,
+                               {swd.pay + sh * Is, swd.sc + sh * Is / 32}, NI));
+    } else {
+      MOE_TRY_STATUS(mx_rows(p, s, f->ws_down, Is, d * Is, (int)Is, d, (int)NI, swd));
+    }
     {
       RowGemmArgs a{};
       mx_pq(a, shq, NI, swd, NI, 0);
@@ -920,9 +990,13 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
                                hipStream_t s, void* dy_perm, void* dgu, void* dx_perm, void* dgu_s, void* dxs) {
   const int64_t d = p->d, I = p->I, E = p->E, A = p->A, T = p->T, Apad = p->Apad;
   int32_t* pad = reinterpret_cast<int32_t*>(wsp(ws, p->o_mx_pad));
-  const MxOp dyq = mxop(ws, p->mx_dyq), wdt = mxop(ws, p->mx_wdt), dguq = mxop(ws, p->mx_dguq),
-             wgut = mxop(ws, p->mx_wgut), dyt = mxop(ws, p->mx_dyt), ht = mxop(ws, p->mx_ht),
-             dgut = mxop(ws, p->mx_dgut), xt = mxop(ws, p->mx_xt);
+  // the weights' and H's codes from the forward's saved-codes buffer, if given
+  const void* svb = sv->mx_saved;
+  const MxOp dyq = mxop(ws, p->mx_dyq), dguq = mxop(ws, p->mx_dguq), dyt = mxop(ws, p->mx_dyt),
+             dgut = mxop(ws, p->mx_dgut), xt = mxop(ws, p->mx_xt),
+             wdt = svb ? svop(svb, p->sv_wdt) : mxop(ws, p->mx_wdt),
+             wgut = svb ? svop(svb, p->sv_wgut) : mxop(ws, p->mx_wgut),
+             ht = svb ? svop(svb, p->sv_ht) : mxop(ws, p->mx_ht);
   {
     Probe pr(p, "mx_quantize", s);
     MOE_TRY(launch_mx_pad_offsets(sv->offsets, pad, (int)E, 128, s));
@@ -931,7 +1005,9 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
     // dH = dY_perm W_d (reduction over d): W_d [E][d][I] transposed to [I][E d]
     // dY_perm: its row-wise codes came from the combine backward; token blocks for dW_d
     MOE_TRY_STATUS(mx_cols(p, s, dy_perm, d, (int)d, sv->offsets, pad, (int)E, 0, Apad / 32, 0, Apad, 0, dyt));
-    MOE_TRY_STATUS(mx_cols(p, s, sv->w_down, I, (int)I, nullptr, nullptr, (int)E, (int)d, E * d / 32, 0, E * d, 0, wdt));
+    if (!svb)
+      MOE_TRY_STATUS(mx_cols(p, s, sv->w_down, I, (int)I, nullptr, nullptr, (int)E, (int)d, E * d / 32, 0, E * d, 0,
+                             wdt));
     RowGemmArgs a{};
     mx_pq(a, dyq, d, wdt, E * d, d);
     a.offsets = sv->offsets; a.G = (int)E; a.M = A; a.N = (int)I; a.K = (int)d; a.sub = (int)I;
@@ -943,7 +1019,7 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
   }
   {
     // dW_d[e] = dY_perm[seg]^T H[seg]: token axis blocked per segment (dY_perm's done above)
-    MOE_TRY_STATUS(mx_cols(p, s, sv->h, I, (int)I, sv->offsets, pad, (int)E, 0, Apad / 32, 0, Apad, 0, ht));
+    if (!svb) MOE_TRY_STATUS(mx_cols(p, s, sv->h, I, (int)I, sv->offsets, pad, (int)E, 0, Apad / 32, 0, Apad, 0, ht));
     WgradArgs a{};
     a.P = dyt.pay; a.Ps = dyt.sc; a.ldp = Apad; a.Q = ht.pay; a.Qs = ht.sc; a.ldq = Apad;
     a.offsets = pad; a.G = (int)E; a.Mtok = Apad; a.M = (int)d; a.N = (int)I; a.sub = (int)I;
@@ -953,8 +1029,9 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
   if (T > 0) {
     // dX_perm = [dG | dU] W_gu (reduction over 2I): W_gu [E][2I][d] transposed to [d][E 2I]
     // [dG | dU]: row-wise and token-axis codes from the SwiGLU-backward epilogue
-    MOE_TRY_STATUS(mx_cols(p, s, sv->w_gate_up, d, (int)d, nullptr, nullptr, (int)E, (int)(2 * I), E * 2 * I / 32, 0,
-                           E * 2 * I, 0, wgut));
+    if (!svb)
+      MOE_TRY_STATUS(mx_cols(p, s, sv->w_gate_up, d, (int)d, nullptr, nullptr, (int)E, (int)(2 * I), E * 2 * I / 32,
+                             0, E * 2 * I, 0, wgut));
     RowGemmArgs a{};
     mx_pq(a, dguq, 2 * I, wgut, E * 2 * I, 2 * I);
     a.offsets = sv->offsets; a.G = (int)E; a.M = A; a.N = (int)d; a.K = (int)(2 * I); a.sub = (int)I;
@@ -977,16 +1054,18 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
   if (p->Ns > 0) {
     const int64_t Is = p->Is, NI = p->Ns * p->Is, Tpad = p->Tpad;
     int32_t* seg_pad = reinterpret_cast<int32_t*>(wsp(ws, p->o_mx_seg1));   // {0, T} then {0, Tpad}
-    const MxOp sdyq = mxop(ws, p->mx_sdyq), swdt = mxop(ws, p->mx_swdt), sdguq = mxop(ws, p->mx_sdguq),
-               swgut = mxop(ws, p->mx_swgut), sdyt = mxop(ws, p->mx_sdyt), sht = mxop(ws, p->mx_sht),
-               sdgut = mxop(ws, p->mx_sdgut), sxt = mxop(ws, p->mx_sxt);
+    const MxOp sdyq = mxop(ws, p->mx_sdyq), sdguq = mxop(ws, p->mx_sdguq), sdyt = mxop(ws, p->mx_sdyt),
+               sdgut = mxop(ws, p->mx_sdgut), sxt = mxop(ws, p->mx_sxt),
+               swdt = svb ? svop(svb, p->sv_swdt) : mxop(ws, p->mx_swdt),
+               swgut = svb ? svop(svb, p->sv_swgut) : mxop(ws, p->mx_swgut),
+               sht = svb ? svop(svb, p->sv_sht) : mxop(ws, p->mx_sht);
     {
       Probe pr(p, "mx_quantize", s);
       MOE_TRY(launch_mx_single_segment(seg_pad, T, 128, s));
     }
     if (T > 0) {
       // dY's row-wise codes (sdyq) came from the combine backward
-      for (int sh = 0; sh < p->Ns; ++sh)   // W_sd[s] [d][Is] -> rows s Is.. of [NI][d]
+      for (int sh = 0; sh < p->Ns && !svb; ++sh)   // W_sd[s] [d][Is] -> rows s Is.. of [NI][d]
         MOE_TRY_STATUS(mx_cols(p, s, static_cast<const char*>(sv->ws_down) + (int64_t)sh * d * Is * 2, Is, (int)Is,
                                nullptr, nullptr, 1, (int)d, d / 32, 0, d, sh * Is, swdt));
       RowGemmArgs a{};
@@ -1000,7 +1079,9 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
     }
     {
       MOE_TRY_STATUS(mx_cols(p, s, dy, d, (int)d, seg_pad, seg_pad + 2, 1, 0, Tpad / 32, 0, Tpad, 0, sdyt));
-      MOE_TRY_STATUS(mx_cols(p, s, sv->h_shared, NI, (int)NI, seg_pad, seg_pad + 2, 1, 0, Tpad / 32, 0, Tpad, 0, sht));
+      if (!svb)
+        MOE_TRY_STATUS(mx_cols(p, s, sv->h_shared, NI, (int)NI, seg_pad, seg_pad + 2, 1, 0, Tpad / 32, 0, Tpad, 0,
+                               sht));
       WgradArgs a{};
       a.P = sdyt.pay; a.Ps = sdyt.sc; a.ldp = Tpad; a.Q = sht.pay; a.Qs = sht.sc; a.ldq = Tpad;
       a.offsets = seg_pad + 2; a.G = 1; a.Mtok = Tpad; a.M = (int)d; a.N = (int)NI; a.sub = (int)Is;
@@ -1016,7 +1097,7 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
                                "gemm_wgrad_gate_up_shared", s, DT_MXFP8));
     }
     if (T > 0) {
-      for (int sh = 0; sh < p->Ns; ++sh)   // W_sgu[s] [2Is][d] -> K positions s 2Is.. of [d][2 NI]
+      for (int sh = 0; sh < p->Ns && !svb; ++sh)   // W_sgu[s] [2Is][d] -> K positions s 2Is.. of [d][2 NI]
         MOE_TRY_STATUS(mx_cols(p, s, static_cast<const char*>(sv->ws_gate_up) + (int64_t)sh * 2 * Is * d * 2, d,
                                (int)d, nullptr, nullptr, 1, (int)(2 * Is), 2 * Is / 32, sh * 2 * Is, 2 * NI, 0, swgut));
       RowGemmArgs a{};
@@ -1298,6 +1379,29 @@ moe_status moe_probe_enable(moe_plan p, const char* kernel, int max_launches) {
   p->probe_name = name;
   p->probe_n = 0;
   return MOE_OK;
+}
+
+moe_status moe_mx_saved_region(moe_plan p, const char* name, size_t* offset, size_t* bytes) {
+  if (!p || !name || !offset || !bytes) return MOE_ERR_NULL;
+  if (!p->mx) return MOE_ERR_INVALID;
+  const std::string n(name);
+  const bool sc = n.size() > 7 && n.compare(n.size() - 7, 7, ".scales") == 0;
+  const std::string base = sc ? n.substr(0, n.size() - 7) : n;
+  const int64_t d = p->d, I = p->I, E = p->E, NI = (int64_t)p->Ns * p->Is;
+  struct Entry { const char* name; const moe_plan_s::MxBuf* buf; int64_t rows, K; bool shared; };
+  const Entry tab[] = {
+      {"mx_wdt", &p->sv_wdt, I, E * d, false},      {"mx_wgut", &p->sv_wgut, d, E * 2 * I, false},
+      {"mx_ht", &p->sv_ht, I, p->Apad, false},      {"mx_swdt", &p->sv_swdt, NI, d, true},
+      {"mx_swgut", &p->sv_swgut, d, 2 * NI, true}, {"mx_sht", &p->sv_sht, NI, p->Tpad, true},
+  };
+  for (const Entry& t : tab) {
+    if (base != t.name) continue;
+    if (t.shared && p->Ns == 0) return MOE_ERR_INVALID;
+    *offset = sc ? t.buf->sc : t.buf->pay;
+    *bytes = (size_t)t.rows * (sc ? t.K / 32 : t.K);
+    return MOE_OK;
+  }
+  return MOE_ERR_INVALID;
 }
 
 moe_status moe_keep_intermediates(moe_plan p, int keep) {

@@ -1226,6 +1226,10 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
     constexpr int TQ_OFF = NARR * SR * RB;
     static_assert(!(MX && EPI == EPI_SWIGLU_BWD) || TQ_OFF + 2 * BN * BM <= NSTG * (BM + BN) * DKB,
                   "token-axis code staging fits in the ring");
+    // (SwiGLU forward: H's, TILE_N columns of BM bytes, then their BM / 32 scale bytes each)
+    constexpr int HQ_OFF = NARR * SR * RB;
+    static_assert(!(MX && EPI == EPI_SWIGLU_FWD) || HQ_OFF + TILE_N * (BM + BM / 32) <= NSTG * (BM + BN) * DKB,
+                  "token-axis code staging fits in the ring");
     // f32 G, U of the SwiGLU backward: this lane's row pieces of column
     // subtile ns, loaded one subtile ahead of the one being computed; in
     // ping-pong tiles also the next pass's first subtile during this pass's
@@ -1488,6 +1492,41 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
           }
         }
       }
+      if constexpr (MX && EPI == EPI_SWIGLU_FWD) {
+        // H along the tokens for the down weight gradient (optional, saved
+        // beside H): thread j < WM * TILE_N takes H column j % TILE_N of the
+        // tile and the pass's staged 32-row block j / TILE_N (tile rows
+        // gi WTM + 32 ms ..).  The tile starts a 32-block of its segment and
+        // rows past the segment were staged as zeros (their P rows read as
+        // zero), as the padding they stand for.  The codes wait in LDS (after
+        // the staged rows: column j's BM bytes at HQ_OFF + j BM, 16-byte
+        // chunk q at (q ^ (j & 7)), then its BM / 32 scale bytes) until the
+        // tile is whole.
+        if (a.Tq) {
+          static_assert(64 * NW >= WM * TILE_N, "a thread per (column, row block)");
+          const int col = tid % TILE_N, gi = tid / TILE_N;
+          const int tb = gi * WTM + ms * 32;
+          if (gi < WM) {
+            float v[32];
+#pragma unroll
+            for (int r = 0; r < 32; ++r)
+              v[r] = to_f32<TO>(reinterpret_cast<const TO*>(sp(2, gi * 32 + r, col / 8))[col % 8]);
+            float amax = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 32; ++r) amax = fmaxf(amax, fabsf(v[r]));
+            const int x = mx_scale_exp(amax);
+            const float sc = ldexpf(1.0f, -x);
+            u32x4 o[2];
+#pragma unroll
+            for (int w = 0; w < 8; ++w) o[w >> 2][w & 3] = e4m3x4(v[4 * w], v[4 * w + 1], v[4 * w + 2], v[4 * w + 3], sc);
+            uint8_t* crow = reinterpret_cast<uint8_t*>(smem) + HQ_OFF + col * BM;
+            const int q0 = tb / 16;
+            *reinterpret_cast<u32x4*>(crow + ((q0 ^ (col & 7)) << 4)) = o[0];
+            *reinterpret_cast<u32x4*>(crow + (((q0 + 1) ^ (col & 7)) << 4)) = o[1];
+            reinterpret_cast<uint8_t*>(smem)[HQ_OFF + TILE_N * BM + col * (BM / 32) + tb / 32] = (uint8_t)(x + 127);
+          }
+        }
+      }
       if constexpr (MX && EPI == EPI_SWIGLU_BWD) {
         // [dG | dU] along the tokens for the gate/up weight gradient: thread
         // j takes column j of the tile's [dG | dU] and quantises the pass's WM
@@ -1520,6 +1559,31 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
             *reinterpret_cast<u32x4*>(crow + (((q0 + 1) ^ (tid & 7)) << 4)) = o[1];
             tsc |= (uint32_t)(x + 127) << (8 * (tb / 32));
           }
+        }
+      }
+    }
+    if constexpr (MX && EPI == EPI_SWIGLU_FWD) {
+      // the tile's H codes: each column's rows up to the segment's 128-padded
+      // end (the last 256-row tile of a segment stops there), 16 bytes per
+      // thread, and its scale bytes as 4-byte words
+      if (a.Tq) {
+        lds_barrier();                                        // every column's codes staged
+        const int tq_rows = (rows + 127) / 128 * 128;
+        const uint8_t* cst = reinterpret_cast<const uint8_t*>(smem) + HQ_OFF;
+        constexpr int CH = BM / 16;                           // 16-byte chunks per column
+#pragma unroll
+        for (int i = 0; i < (TILE_N * CH + 64 * NW - 1) / (64 * NW); ++i) {
+          const int q = tid + 64 * NW * i, j = q / CH, ch = q % CH;
+          if (j < TILE_N && ch * 16 < tq_rows)
+            st16(a.Tq + (int64_t)(n0 + j) * a.ldt + tkbase + ch * 16,
+                 *reinterpret_cast<const u32x4*>(cst + j * BM + ((ch ^ (j & 7)) << 4)));
+        }
+        constexpr int SW = BM / 128;                          // 4-byte scale words per column
+        if (tid < TILE_N * SW) {
+          const int j = tid / SW, w = tid % SW;
+          if (w * 128 < tq_rows)
+            *reinterpret_cast<uint32_t*>(a.Ts + (int64_t)(n0 + j) * (a.ldt / 32) + tkbase / 32 + 4 * w) =
+                *reinterpret_cast<const uint32_t*>(cst + TILE_N * BM + j * (BM / 32) + 4 * w);
         }
       }
     }
@@ -2181,9 +2245,11 @@ hipError_t launch_row_gemm(int dt, int op, int epi, int tile, const RowGemmArgs&
   if (op == OP_DOWN_DGRAD && a.C2 && (dt == DT_F16 || dt == DT_MXFP8)) return hipErrorInvalidValue;
   if (dt == DT_MXFP8 && (a.ldp % 128 || a.ldq % 128 || a.q_group_stride % 32 || !a.Ps || !a.Qs))
     return hipErrorInvalidValue;
-  // token-axis [dG | dU] codes: the MX SwiGLU backward only, rows of ldt bytes (a multiple of 128)
-  if (a.Tq && (dt != DT_MXFP8 || op != OP_DOWN_DGRAD || epi != EPI_SWIGLU_BWD || !a.Ts || a.ldt <= 0 ||
-               a.ldt % 128 || (a.offsets && !a.tpad)))
+  // token-axis codes of [dG | dU] (MX SwiGLU backward) or H (MX SwiGLU
+  // forward), rows of ldt bytes (a multiple of 128)
+  if (a.Tq && (dt != DT_MXFP8 || !((op == OP_DOWN_DGRAD && epi == EPI_SWIGLU_BWD) ||
+                                   (op == OP_GU_FWD && epi == EPI_SWIGLU_FWD)) ||
+               !a.Ts || a.ldt <= 0 || a.ldt % 128 || (a.offsets && !a.tpad)))
     return hipErrorInvalidValue;
   if (dt == DT_F32 && tile != TILE_128) return hipErrorInvalidValue;
   const int bm = tile_rows(tile), bn = tile_cols(tile);

@@ -130,7 +130,9 @@ struct RowGemmArgs {
   // tokens (blocks of 32 rows from each segment's start) for the gate/up
   // weight gradient: column j of [dG | dU] is row j of Tq [2 sub-blocks][ldt]
   // (scales Ts [..][ldt/32]), segment g's rows at K positions tpad[g] ..
-  // (tpad: [G+1] padded offsets, multiples of 128; nullptr = position = row)
+  // (tpad: [G+1] padded offsets, multiples of 128; nullptr = position = row).
+  // DT_MXFP8 with EPI_SWIGLU_FWD, optional: H so, for the down weight
+  // gradient (column j of H is row j of Tq).
   uint8_t* Tq = nullptr; uint8_t* Ts = nullptr; const int32_t* tpad = nullptr; int64_t ldt = 0;
 };
 // Intermediates a bf16 layer with bf16 experts keeps in f32 (the saved gate/up
@@ -202,6 +204,11 @@ struct MxColsArgs {
   // optional: token t of a segment is row gather[seg start + t] of in
   // (rows of x picked by perm_token instead of the rows of x_perm)
   const int32_t* gather = nullptr;
+  // optional, from the same read: the row-wise codes too (blocks of 32 along
+  // C), input row i (= seg start + t) to rq + i * rld + col, its scale bytes
+  // to rqs + i * rlds + col / 32; C a multiple of 32, no gather
+  uint8_t* rq = nullptr; uint8_t* rqs = nullptr;
+  int64_t rld = 0, rlds = 0;
 };
 hipError_t launch_mx_quant_cols(int dt, const MxColsArgs& a, hipStream_t s);
 

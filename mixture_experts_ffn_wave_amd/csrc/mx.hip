@@ -59,7 +59,11 @@ __global__ void __launch_bounds__(NT) mx_quant_rows_kernel(MxRowsArgs a) {
 // which is dead by then) so that each output row's 128-byte span (four
 // blocks) leaves as eight consecutive 16-byte stores and its four scale
 // bytes as one 4-byte store.  Tiles never straddle a segment: segment starts
-// (pad) and seg_len are multiples of 128.
+// (pad) and seg_len are multiples of 128.  With rq set, the same tile also
+// gives the row-wise codes (blocks of 32 along the columns), as the row
+// quantiser lays them out: four consecutive lanes per block, eight values
+// each (a wave reads four whole tile rows from LDS, without bank conflicts),
+// before the tile is overwritten.
 constexpr int kColsTileK = 128;
 constexpr int kColsOutRow = kColsTileK + 16;                // staged output row (padded: no bank conflicts)
 
@@ -107,6 +111,31 @@ __global__ void __launch_bounds__(NT) mx_quant_cols_kernel(MxColsArgs a) {
     *reinterpret_cast<u32x4*>(&tile[r][pc * VP]) = v;
   }
   __syncthreads();
+  // ---- row-wise blocks (optional): 128 rows x TC / 32 blocks, in order
+  if (a.rq) {
+    constexpr int PPR = TC / 8;                             // 8-value pieces per tile row
+#pragma unroll
+    for (int i = 0; i < kColsTileK * PPR / NT; ++i) {
+      const int q = threadIdx.x + NT * i, r = q / PPR, pc = q % PPR;
+      const int col = c0 + 8 * pc;
+      const int64_t t = tt0 + r;
+      float v[8];
+      unpack8<T>(*reinterpret_cast<const u32x4*>(&tile[r][8 * pc]), v);
+      float amax = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));        // the block's four lanes
+      amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+      const int x = mx_scale_exp(amax);
+      const float sc = ldexpf(1.0f, -x);
+      const u32x2 o = {e4m3x4(v[0], v[1], v[2], v[3], sc), e4m3x4(v[4], v[5], v[6], v[7], sc)};
+      if (t < n && col < a.C) {
+        const int64_t row = tstart + t;
+        st8(a.rq + row * a.rld + col, o);
+        if ((pc & 3) == 0) a.rqs[row * a.rlds + col / 32] = (uint8_t)(x + 127);
+      }
+    }
+  }
   // ---- token blocks: wave j, block j of the tile, columns lane (+ 64)
   constexpr int NCC = TC / 64;
   const int j = threadIdx.x >> 6, cl = threadIdx.x & 63;
@@ -209,7 +238,19 @@ hipError_t launch_mx_quant_cols(int dt, const MxColsArgs& a, hipStream_t s) {
   if (a.nblk <= 0) return hipSuccess;
   const int64_t tiles = (a.nblk * 32 + kColsTileK - 1) / kColsTileK;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  constexpr int tc = 64;                                    // 64-column tiles measured faster than 128
+  if (a.rq && (!a.rqs || a.gather || a.C % 32)) return hipErrorInvalidValue;
+  // 64-column tiles measured faster than 128 for the token-axis codes alone;
+  // with the row-wise codes too, 128 (whole 128-byte row pieces)
+  if (a.rq) {
+    const dim3 grid((unsigned)tiles, (unsigned)((a.C + 127) / 128));
+    switch (dt) {
+      case DT_BF16: hipLaunchKernelGGL((mx_quant_cols_kernel<__bf16, 128>), grid, dim3(NT), 0, s, a); break;
+      case DT_F16: hipLaunchKernelGGL((mx_quant_cols_kernel<_Float16, 128>), grid, dim3(NT), 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  constexpr int tc = 64;
   const dim3 grid((unsigned)tiles, (unsigned)((a.C + tc - 1) / tc));
   switch (dt) {
     case DT_BF16: hipLaunchKernelGGL((mx_quant_cols_kernel<__bf16, tc>), grid, dim3(NT), 0, s, a); break;

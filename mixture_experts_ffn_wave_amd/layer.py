@@ -57,6 +57,10 @@ class MoELayer:
         self.p_mean = z(E, dtype=torch.float32)
         self.aux_out = torch.zeros(L.ctypes.sizeof(L.MoeAuxScalars), dtype=torch.uint8, device=dev)
         self.ws = torch.empty(max(p.workspace_bytes(), 256), dtype=torch.uint8, device=dev)
+        # MX-fp8 experts: the forward saves the weights' and H's backward codes
+        # for the backward (moe_ffn_args.mx_saved); False: the backward makes them
+        self.mx_save = p.mx
+        self.mx_saved = torch.empty(p.mx_saved_bytes(), dtype=torch.uint8, device=dev) if p.mx else None
         self.params = None
         self.sel_bias = None      # aux-loss-free balancing: set by enable_balancing()
         self.balance_gamma = 0.0
@@ -126,7 +130,8 @@ class MoELayer:
         L.moe_expert_ffn(self.plan, xp, self.offsets, q["w_gate_up"], q["w_down"], self.gu,
                          self.h, self.y_perm, q["x"], q["ws_gate_up"], q["ws_down"], self.gu_shared,
                          self.h_shared, self.y_shared, self.ws, stream,
-                         perm_token=self.perm_token if self.mx_gather else None)
+                         perm_token=self.perm_token if self.mx_gather else None,
+                         mx_saved=self.mx_saved if self.mx_save else None)
         L.moe_combine(self.plan, self.y_perm, self.inv_perm, self.topk_w, self.y_shared, self.y, stream)
 
     def forward(self, stream=None):
@@ -145,7 +150,8 @@ class MoELayer:
                     y_perm=self.y_perm, w_gate_up=q["w_gate_up"], w_down=q["w_down"],
                     ws_gate_up=q["ws_gate_up"], ws_down=q["ws_down"], gu_shared=self.gu_shared,
                     h_shared=self.h_shared, real_mask=self.real_mask, real_counts=self.real_counts,
-                    perm_token=self.perm_token if (self.mx_gather or not self.plan.mx) else None)
+                    perm_token=self.perm_token if (self.mx_gather or not self.plan.mx) else None,
+                    mx_saved=self.mx_saved if self.mx_save else None)
 
     def backward(self, dy, stream=None):
         L.moe_backward(self.plan, self.saved(), dy, self.grads, self.ws, stream)

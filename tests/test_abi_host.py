@@ -48,8 +48,8 @@ def test_version_and_status_strings():
 def test_struct_sizes_match_header_layout(tmp_path):
     assert ctypes.sizeof(L.MoeConfig) == 56          # int64 + 10 int32 + float, 8-aligned
     assert ctypes.sizeof(L.MoeAuxScalars) == 32
-    assert ctypes.sizeof(L.MoeFfnArgs) == 14 * 8
-    assert ctypes.sizeof(L.MoeSaved) == 21 * 8
+    assert ctypes.sizeof(L.MoeFfnArgs) == 15 * 8
+    assert ctypes.sizeof(L.MoeSaved) == 22 * 8
     assert ctypes.sizeof(L.MoeGrads) == 7 * 8
     # and the C compiler's layout of the header itself
     import shutil
@@ -297,6 +297,41 @@ def test_mx_code_regions_have_their_stated_sizes_and_do_not_overlap():
     r = L.Plan(T, d, E, k, I, expert_dtype="mxfp8")            # no shared experts: no shared regions
     assert lib.moe_workspace_region(r.handle, b"mx_sxq", ctypes.byref(o), ctypes.byref(n)) == MOE_ERR_INVALID
     assert lib.moe_workspace_region(r.handle, b"mx_hq.scales", ctypes.byref(o), ctypes.byref(n)) == MOE_OK
+    r.close()
+
+
+def test_mx_saved_code_regions_fill_the_saved_buffer_without_overlap():
+    lib = L.lib()
+    T, d, E, k, I, Ns, Is = 300, 256, 8, 2, 128, 2, 128
+    NI = Ns * Is
+    p = L.Plan(T, d, E, k, I, n_shared=Ns, d_ff_shared=Is, expert_dtype="mxfp8")
+    total = p.mx_saved_bytes()
+    Apad = L.workspace_region(p, "mx_dyt")[1] // d
+    Tpad = (T + 127) // 128 * 128
+    rows = {"mx_wdt": (I, E * d), "mx_wgut": (d, E * 2 * I), "mx_ht": (I, Apad), "mx_swdt": (NI, d),
+            "mx_swgut": (d, 2 * NI), "mx_sht": (NI, Tpad)}
+    spans = []
+    for name, (R, K) in rows.items():
+        for r, nbytes in ((name, R * K), (name + ".scales", R * (K // 32))):
+            off, nb = L.mx_saved_region(p, r)
+            assert nb == nbytes and off % 256 == 0 and off + nb <= total, r
+            spans.append((off, off + nb))
+    spans.sort()
+    assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:])), "regions overlap"
+    assert total - spans[-1][1] < 256                            # nothing else in the buffer
+    o, n = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.moe_mx_saved_region(p.handle, b"mx_xt", ctypes.byref(o), ctypes.byref(n)) == MOE_ERR_INVALID
+    assert lib.moe_mx_saved_region(None, b"mx_ht", ctypes.byref(o), ctypes.byref(n)) == MOE_ERR_NULL
+    p.close()
+    q = L.Plan(T, d, E, k, I)                                    # not an MX plan: no saved buffer
+    assert q.mx_saved_bytes() == 0
+    assert lib.moe_mx_saved_region(q.handle, b"mx_ht", ctypes.byref(o), ctypes.byref(n)) == MOE_ERR_INVALID
+    q.close()
+    r = L.Plan(T, d, E, k, I, expert_dtype="mxfp8")              # no shared experts: no shared regions
+    assert lib.moe_mx_saved_region(r.handle, b"mx_sht", ctypes.byref(o), ctypes.byref(n)) == MOE_ERR_INVALID
+    assert r.mx_saved_bytes() == sum(-(-b // 256) * 256 for b in (I * E * d, I * E * d // 32, d * E * 2 * I,
+                                                                    d * E * 2 * I // 32, I * Apad, I * Apad // 32))
+    assert lib.moe_mx_saved_bytes(None) == 0
     r.close()
 
 

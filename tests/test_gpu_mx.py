@@ -163,6 +163,42 @@ def test_mx_backward_without_kept_dgu():
         assert np.array_equal(m0[n], m1[n]), n
 
 
+def _mx_step(wl, inp, save):
+    from mixture_experts_ffn_wave_amd import MoELayer
+    dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+    layer = MoELayer(PT.plan_for(wl, inp.get("bias") is not None))
+    layer.mx_save = save
+    b = dev.get("bias")
+    layer.set_params(dev["x"], dev["w_router"], dev["w_gate_up"], dev["w_down"],
+                     bias=(b.float() if b is not None else None),
+                     ws_gate_up=dev.get("ws_gate_up"), ws_down=dev.get("ws_down"))
+    layer.forward()
+    layer.backward(dev["dy"])
+    torch.cuda.synchronize()
+    out = {n: getattr(layer, n).clone() for n in ("gu", "h", "y_perm", "y")}
+    out.update({n: t.clone() for n, t in layer.grads.items() if t is not None})
+    return out
+
+
+SAVED_CASES = [(SMALL_MX[2], None), (SMALL_MX[3], None), (SMALL_MX[1], "256"), (SMALL_MX[3], "256")]
+
+
+@pytest.mark.parametrize("wl,tile", SAVED_CASES, ids=[f"{w.name}-{t or 'auto'}" for w, t in SAVED_CASES])
+def test_mx_saved_codes_change_nothing(wl, tile, monkeypatch):
+    """The forward's saved codes (the weights along the backward's reduction
+    axes, from the pass that makes the forward's row-wise codes; H along each
+    expert's tokens, from the gate/up epilogue) are the codes the backward
+    makes itself without them: every output and gradient is bitwise the same
+    either way, on 128 x 128 and 256 x 256 gate/up tiles."""
+    if tile:
+        monkeypatch.setenv("MOE_ROW_TILE", tile)
+    inp = MI.make_inputs(wl)
+    a, b = _mx_step(wl, inp, True), _mx_step(wl, inp, False)
+    for n in a:
+        if a[n] is not None:
+            assert torch.equal(a[n], b[n]), n
+
+
 def test_mx_gather_on_load_equals_the_x_perm_path():
     """The gate/up GEMM reading x's codes through perm_token, and the weight
     gradient gathering x's rows, quantise the same values as the x_perm path

@@ -66,19 +66,25 @@ def check_codes(name, pay, sc, vals):
     assert bad.size == 0, f"{name}: payload differs at {bad[:4].tolist()} ({got[tuple(bad[0])]} vs {q[tuple(bad[0])]})"
 
 
+SAVED = ("mx_wdt", "mx_wgut", "mx_ht", "mx_swdt", "mx_swgut", "mx_sht")
+
+
 class Regions:
-    """Reads MX buffers (payload, scales) of a layer's workspace."""
+    """Reads MX buffers (payload, scales) of a layer's workspace, or of its
+    saved-codes buffer for the operands the forward saved there."""
 
     def __init__(self, layer):
-        from mixture_experts_ffn_wave_amd._lib import workspace_region
-        self.layer, self.wr = layer, workspace_region
+        from mixture_experts_ffn_wave_amd._lib import workspace_region, mx_saved_region
+        self.layer, self.wr, self.sr = layer, workspace_region, mx_saved_region
 
     def raw(self, name, rows, K, sel=None):
-        ws = self.layer.ws
-        off, nb = self.wr(self.layer.plan, name)
+        saved = self.layer.mx_save and name in SAVED
+        ws = self.layer.mx_saved if saved else self.layer.ws
+        where = self.sr if saved else self.wr
+        off, nb = where(self.layer.plan, name)
         assert nb == rows * K, (name, nb, rows, K)
         pay = ws[off:off + nb].view(rows, K)
-        off, nb = self.wr(self.layer.plan, name + ".scales")
+        off, nb = where(self.layer.plan, name + ".scales")
         assert nb == rows * (K // 32), (name, nb)
         sc = ws[off:off + nb].view(rows, K // 32)
         if sel is not None:
@@ -95,11 +101,14 @@ def f64(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def run_layer(wl, inp, gather):
+def run_layer(wl, inp, gather, save=True):
+    """``save``: the forward writes the weights' and H's backward codes into
+    the saved-codes buffer (else the backward quantises them itself)."""
     from mixture_experts_ffn_wave_amd import MoELayer
     b = inp.get("bias")
     layer = MoELayer(PT.plan_for(wl, b is not None))
     layer.mx_gather = gather
+    layer.mx_save = save
     layer.write_x_perm = True
     layer.keep_intermediates()                 # the bf16 [dG | dU] the codes are checked against
     dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
@@ -235,6 +244,16 @@ def test_every_mx_operand_is_bit_exact(wl, gather):
     counts = check_all(wl, layer, dev, gather)
     if wl.zipf_s:
         assert counts.max() > 4 * counts.mean() and (counts[counts > 0] < 32).any(), counts
+
+
+# Without the saved-codes buffer the backward quantises the weights along its
+# reduction axes and H along the tokens itself (the transposing quantiser)
+@pytest.mark.parametrize("wl,gather", [CASES[1], CASES[3]], ids=["zipf-xperm", "shared2-xperm"])
+def test_every_mx_operand_is_bit_exact_without_saved_codes(wl, gather):
+    PT.say(f"[mx-codes] {wl.name} gather={gather} no saved codes")
+    inp = MI.make_inputs(wl)
+    layer, dev = run_layer(wl, inp, gather, save=False)
+    check_all(wl, layer, dev, gather)
 
 
 # The 256 x 256 tiles (8 waves) of the forward GEMMs and the gate/up dgrad:
