@@ -444,7 +444,8 @@ const char* moe_kernel_names(void);
  *                 "wh", in bf16, which the expert weight gradients add
  *   "dgu"         [T*top_k, 2 d_ff]      [dG | dU] of the routed experts
  *                 (MX-fp8 plans: only after moe_keep_intermediates(plan, 1),
- *                 as "dgu_shared")
+ *                 as "dgu_shared", and "dy_perm" when the backward was given
+ *                 perm_token)
  *   "dx_perm"     [T*top_k, d_model]     input gradient of the expert rows
  *   "dgu_shared"  [T, 2 n_shared d_ff_shared]  [dG_s | dU_s] per shared expert
  *   "dx_shared"   [T, d_model]           input gradient of the shared experts
@@ -484,8 +485,12 @@ moe_status moe_workspace_region(moe_plan plan, const char* name, size_t* offset,
  * the two MX operands the SwiGLU-backward epilogue writes ("mx_dguq",
  * "mx_dgut" and their shared counterparts), so by default it does not also
  * store the act-dtype "dgu" and "dgu_shared" rows (T*top_k * 2 d_ff * 2 bytes
- * of HBM writes saved).  keep = 1 makes later moe_backward calls on this plan
- * store them too, for tests and debugging; keep = 0 restores the default.
+ * of HBM writes saved); given moe_saved.perm_token, the same holds for the
+ * "dy_perm" rows (their row-wise codes come from the combine backward, their
+ * token-axis codes from dy's rows gathered by perm_token and scaled by the
+ * routing weight as the rows would be).  keep = 1 makes later moe_backward
+ * calls on this plan store them too, for tests and debugging; keep = 0
+ * restores the default.
  * Other plans always store them (their next GEMMs read them): the call is
  * accepted there and changes nothing.  Like the timing probe, it changes the
  * plan and is not thread-safe.  MOE_ERR_NULL for a null plan. */

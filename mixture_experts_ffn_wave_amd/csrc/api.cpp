@@ -67,7 +67,7 @@ struct moe_plan_s {
   MxBuf mx_dyq, mx_wdt, mx_dguq, mx_wgut, mx_dyt, mx_ht, mx_dgut, mx_xt;              // backward, routed
   MxBuf mx_sdyq, mx_swdt, mx_sdguq, mx_swgut, mx_sdyt, mx_sht, mx_sdgut, mx_sxt;      // backward, shared
   size_t o_mx_pad = 0, o_mx_seg1 = 0;  // padded expert offsets [E+1]; single-segment bounds [2] + pad [2]
-  bool keep_dgu = false;               // MX: also store the act-dtype [dG | dU] (moe_keep_intermediates)
+  bool keep_inter = false;             // MX: also store [dG | dU] and dY_perm rows (moe_keep_intermediates)
   // the optional saved-codes buffer (offsets into it): the weights along the
   // backward's reduction axes and H along the tokens, routed and shared
   MxBuf sv_wdt, sv_wgut, sv_ht, sv_swdt, sv_swgut, sv_sht;
@@ -443,7 +443,7 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
     const int wcols = p->t_down_dgrad == TILE_128x256 ? 128 : 64;   // 128 x 128, 256 x 256, 256 x 256 pp: 64
     p->gparts = p->I / wcols;
   }
-  p->o_wsorted = take(p->mx ? 0 : (size_t)A * 4);
+  p->o_wsorted = take((size_t)A * 4);
   p->o_gpart = take(p->mx ? 0 : (size_t)A * p->gparts * 4);
   p->o_dzhl = take((size_t)p->T * 2 * p->Ep * es);
   p->o_w2 = take(p->router_dx_gemm ? (size_t)2 * p->Ep * p->d * es : 0);
@@ -637,9 +637,10 @@ moe_status mx_rows(moe_plan p, hipStream_t s, const void* in, int64_t ld_in, int
 // rq.pay + i * rld (scales rq.sc + i * rld / 32)
 moe_status mx_cols(moe_plan p, hipStream_t s, const void* in, int64_t ld_in, int C, const int32_t* seg,
                    const int32_t* pad, int G, int seg_len, int64_t nblk, int64_t k0, int64_t Kpad, int64_t row0,
-                   MxOp o, const int32_t* gather = nullptr, MxOp rq = {nullptr, nullptr}, int64_t rld = 0) {
+                   MxOp o, const int32_t* gather = nullptr, MxOp rq = {nullptr, nullptr}, int64_t rld = 0,
+                   const float* wrow = nullptr) {
   MxColsArgs a{in, ld_in, C, seg, pad, G, seg_len, nblk, k0, Kpad, row0, o.pay, o.sc, gather};
-  a.rq = rq.pay; a.rqs = rq.sc; a.rld = rld; a.rlds = rld / 32;
+  a.rq = rq.pay; a.rqs = rq.sc; a.rld = rld; a.rlds = rld / 32; a.wrow = wrow;
   Probe pr(p, "mx_quantize", s);
   MOE_TRY(launch_mx_quant_cols(p->dt, a, s));
   return MOE_OK;
@@ -1003,15 +1004,22 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
   }
   if (T > 0) {
     // dH = dY_perm W_d (reduction over d): W_d [E][d][I] transposed to [I][E d]
-    // dY_perm: its row-wise codes came from the combine backward; token blocks for dW_d
-    MOE_TRY_STATUS(mx_cols(p, s, dy_perm, d, (int)d, sv->offsets, pad, (int)E, 0, Apad / 32, 0, Apad, 0, dyt));
+    // dY_perm: its row-wise codes came from the combine backward; token blocks for dW_d,
+    // from dy's rows gathered by perm_token and scaled by their routing weights
+    // (the combine backward wrote those, not the rows), else from the stored rows
+    if (sv->perm_token)
+      MOE_TRY_STATUS(mx_cols(p, s, dy, d, (int)d, sv->offsets, pad, (int)E, 0, Apad / 32, 0, Apad, 0, dyt,
+                             sv->perm_token, {nullptr, nullptr}, 0,
+                             reinterpret_cast<const float*>(wsp(ws, p->o_wsorted))));
+    else
+      MOE_TRY_STATUS(mx_cols(p, s, dy_perm, d, (int)d, sv->offsets, pad, (int)E, 0, Apad / 32, 0, Apad, 0, dyt));
     if (!svb)
       MOE_TRY_STATUS(mx_cols(p, s, sv->w_down, I, (int)I, nullptr, nullptr, (int)E, (int)d, E * d / 32, 0, E * d, 0,
                              wdt));
     RowGemmArgs a{};
     mx_pq(a, dyq, d, wdt, E * d, d);
     a.offsets = sv->offsets; a.G = (int)E; a.M = A; a.N = (int)I; a.K = (int)d; a.sub = (int)I;
-    a.C = p->keep_dgu ? dgu : nullptr; a.ldc = 2 * I; a.aux = sv->gu; a.ldaux = 2 * I;
+    a.C = p->keep_inter ? dgu : nullptr; a.ldc = 2 * I; a.aux = sv->gu; a.ldaux = 2 * I;
     a.Hq = dguq.pay; a.Hs = dguq.sc;                 // the epilogue writes [dG | dU] row-wise
     a.Tq = dgut.pay; a.Ts = dgut.sc; a.tpad = pad; a.ldt = Apad;   // and along the tokens, for dW_gu
     Probe pr(p, "gemm_down_dgrad_swiglu", s);
@@ -1071,7 +1079,7 @@ moe_status mx_backward_experts(moe_plan p, const moe_saved* sv, const void* dy, 
       RowGemmArgs a{};
       mx_pq(a, sdyq, d, swdt, d, 0);
       a.offsets = nullptr; a.G = 1; a.M = T; a.N = (int)NI; a.K = (int)d; a.sub = (int)Is;
-      a.C = p->keep_dgu ? dgu_s : nullptr; a.ldc = 2 * NI; a.aux = sv->gu_shared; a.ldaux = 2 * NI;
+      a.C = p->keep_inter ? dgu_s : nullptr; a.ldc = 2 * NI; a.aux = sv->gu_shared; a.ldaux = 2 * NI;
       a.Hq = sdguq.pay; a.Hs = sdguq.sc;             // the epilogue writes [dG | dU] row-wise
       a.Tq = sdgut.pay; a.Ts = sdgut.sc; a.ldt = Tpad;   // and along the tokens (one segment), for dWs_gu
       Probe pr(p, "gemm_down_dgrad_swiglu_shared", s);
@@ -1160,6 +1168,10 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
       CombineBwdArgs a{dy, sv->y_perm, sv->inv_perm, sv->topk_w, dy_perm,
                        p->mx ? g : nullptr, p->T, d, k};
       if (!p->mx) a.wsorted = wsorted;
+      if (p->mx && sv->perm_token) {                 // MX: dY_perm's token-axis codes gather dy (see there)
+        a.wsorted = wsorted;
+        a.no_rows = p->keep_inter ? 0 : 1;
+      }
       if (wh_rows(p)) a.copy = 1;                    // the routing weight goes on the H side
       if (p->mx) {                                   // MX experts: dY_perm's row-wise codes too
         const MxOp dyq = mxop(ws, p->mx_dyq);
@@ -1406,7 +1418,7 @@ moe_status moe_mx_saved_region(moe_plan p, const char* name, size_t* offset, siz
 
 moe_status moe_keep_intermediates(moe_plan p, int keep) {
   if (!p) return MOE_ERR_NULL;
-  p->keep_dgu = keep != 0;
+  p->keep_inter = keep != 0;
   return MOE_OK;
 }
 

@@ -161,7 +161,7 @@ __global__ void __launch_bounds__(NT) combine_bwd_kernel(CombineBwdArgs a) {
               if constexpr (GD) dot[u] = fmaf(dd, to_f32<T>(yv[u].e[i]), dot[u]);
               o.e[i] = a.copy ? dv.e[i] : from_f32<T>(w[u] * dd);
             }
-            if (ok) st16(dyp + (int64_t)r[u] * rowbytes + (int64_t)c * 16, o.raw);
+            if (ok && !a.no_rows) st16(dyp + (int64_t)r[u] * rowbytes + (int64_t)c * 16, o.raw);
             if constexpr (MXQ && sizeof(T) == 2) {
               // MX-fp8 experts: the row-wise codes of the stored values; the
               // four lanes of chunks 4b .. 4b+3 hold one 32-value block
@@ -178,6 +178,7 @@ __global__ void __launch_bounds__(NT) combine_bwd_kernel(CombineBwdArgs a) {
           if constexpr (GD) {
             const float ds = wave_sum(dot[u]);
             if (lane == 0) a.g[t * a.k + j0 + u] = ds;
+            if (a.wsorted && lane == 0 && r[u] >= 0) a.wsorted[r[u]] = w[u];
           } else {
             if (lane == 0 && r[u] >= 0) a.wsorted[r[u]] = w[u];
           }

@@ -209,6 +209,10 @@ struct MxColsArgs {
   // to rqs + i * rlds + col / 32; C a multiple of 32, no gather
   uint8_t* rq = nullptr; uint8_t* rqs = nullptr;
   int64_t rld = 0, rlds = 0;
+  // optional, with gather: input row i scaled by wrow[seg start + t] and
+  // rounded to the input dtype first (the w dy rows of dY_perm, formed as the
+  // combine backward forms them)
+  const float* wrow = nullptr;
 };
 hipError_t launch_mx_quant_cols(int dt, const MxColsArgs& a, hipStream_t s);
 
@@ -239,6 +243,7 @@ struct CombineBwdArgs {
   // and dY itself (the shared experts' output gradient) into dq [T, d], dqs [T, d/32]
   uint8_t* dq = nullptr; uint8_t* dqs = nullptr;
   int copy = 0;   // 1: dy_perm rows are plain copies of dy rows (no routing weight)
+  int no_rows = 0;  // 1 (MX, with q): the dy_perm rows themselves are not stored, only their codes
 };
 hipError_t launch_combine_bwd(int dt, const CombineBwdArgs& a, hipStream_t s);
 

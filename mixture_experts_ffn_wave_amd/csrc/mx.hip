@@ -107,7 +107,17 @@ __global__ void __launch_bounds__(NT) mx_quant_cols_kernel(MxColsArgs a) {
     const int col = c0 + pc * VP;
     const int64_t t = tt0 + r;
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (t < n && col < a.C) v = ld16(in + (a.gather ? (int64_t)a.gather[tstart + t] : t) * a.ld_in + col);
+    if (t < n && col < a.C) {
+      v = ld16(in + (a.gather ? (int64_t)a.gather[tstart + t] : t) * a.ld_in + col);
+      if (a.wrow) {                                         // w x, rounded as the stored rows would be
+        const float w = a.wrow[tstart + t];
+        Chunk<T> ch;
+        ch.raw = v;
+#pragma unroll
+        for (int u = 0; u < VP; ++u) ch.e[u] = from_f32<T>(w * to_f32<T>(ch.e[u]));
+        v = ch.raw;
+      }
+    }
     *reinterpret_cast<u32x4*>(&tile[r][pc * VP]) = v;
   }
   __syncthreads();
@@ -239,6 +249,7 @@ hipError_t launch_mx_quant_cols(int dt, const MxColsArgs& a, hipStream_t s) {
   const int64_t tiles = (a.nblk * 32 + kColsTileK - 1) / kColsTileK;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
   if (a.rq && (!a.rqs || a.gather || a.C % 32)) return hipErrorInvalidValue;
+  if (a.wrow && !a.gather) return hipErrorInvalidValue;
   // 64-column tiles measured faster than 128 for the token-axis codes alone;
   // with the row-wise codes too, 128 (whole 128-byte row pieces)
   if (a.rq) {

@@ -119,10 +119,12 @@ def test_mx_two_runs_are_bitwise_identical():
 
 
 def test_mx_backward_without_kept_dgu():
-    """By default an MX backward stores [dG | dU] only as its two MX operands:
-    the act-dtype "dgu" / "dgu_shared" regions keep what was there, and every
-    gradient and every MX operand is bitwise what a backward that also stores
-    them (moe_keep_intermediates) gives."""
+    """By default an MX backward stores [dG | dU] and dY_perm only as their MX
+    operands (dY_perm's token-axis codes from dy's rows gathered by
+    perm_token and scaled by the routing weight): the act-dtype "dgu",
+    "dgu_shared" and "dy_perm" regions keep what was there, and every gradient
+    and every MX operand is bitwise what a backward that also stores them
+    (moe_keep_intermediates) gives."""
     wl = W("t700_d256_e8k2_i256_s1x128_mx_nodgu", T=700, d=256, E=8, k=2, I=256, n_shared=1, I_shared=128,
            expert_dtype="mxfp8")
     inp = MI.make_inputs(wl)
@@ -137,7 +139,8 @@ def test_mx_backward_without_kept_dgu():
         if keep:
             layer.keep_intermediates()
         layer.forward()
-        for n in ("dgu", "dgu_shared"):
+        assert layer.mx_gather                   # the backward gets perm_token
+        for n in ("dgu", "dgu_shared", "dy_perm"):
             layer.backward_intermediate(n).fill_(7.0)
         layer.backward(dev["dy"])
         torch.cuda.synchronize()
@@ -146,15 +149,17 @@ def test_mx_backward_without_kept_dgu():
         A, I = wl.T * wl.k, wl.I
         mx = {}
         NI = wl.n_shared * wl.I_shared
-        for n, rows in (("mx_dguq", A), ("mx_dgut", 2 * I), ("mx_sdguq", wl.T), ("mx_sdgut", 2 * NI)):
+        for n, rows in (("mx_dguq", A), ("mx_dgut", 2 * I), ("mx_sdguq", wl.T), ("mx_sdgut", 2 * NI),
+                        ("mx_dyq", A), ("mx_dyt", wl.d)):
             for r in (n, n + ".scales"):
                 off, nb = workspace_region(layer.plan, r)
                 v = PT.to_np(layer.ws[off:off + nb]).reshape(rows, -1)
                 # the routed token axis has headroom past the last segment, never written
-                mx[r] = v[:, :end // (32 if r.endswith(".scales") else 1)] if n == "mx_dgut" else v
+                tok = n in ("mx_dgut", "mx_dyt")
+                mx[r] = v[:, :end // (32 if r.endswith(".scales") else 1)] if tok else v
         runs.append((layer, {n: PT.to_np(t) for n, t in layer.grads.items()}, mx))
     (quiet, g0, m0), (kept, g1, m1) = runs
-    for n in ("dgu", "dgu_shared"):
+    for n in ("dgu", "dgu_shared", "dy_perm"):
         assert bool((quiet.backward_intermediate(n) == 7.0).all()), n
         assert not bool((kept.backward_intermediate(n) == 7.0).all()), n
     for n in g0:
