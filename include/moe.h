@@ -253,13 +253,14 @@ typedef struct {
   const void* w_down;      /* [E, d, I] act */
   void* gu;                /* out [T*k, 2I]: [G | U] per row, saved for backward; f32 for a
                               bf16 layer with bf16 experts, bf16 for MX-fp8 experts, else act */
-  void* h;                 /* out [T*k, I] act: silu(G) * U */
+  void* h;                 /* out [T*k, I] act: silu(G) * U (MX-fp8 plans given mx_saved: may be
+                              NULL, H then exists only as its two MX codes) */
   void* y_perm;            /* out [T*k, d]: H W_d^T; f32 for a bf16 layer with bf16 experts, else act */
   const void* x;           /* [T, d] act (shared experts' input) */
   const void* ws_gate_up;  /* [Ns, 2Is, d] act */
   const void* ws_down;     /* [Ns, d, Is] act */
   void* gu_shared;         /* out [T, 2 Ns Is], dtype as gu: expert s in columns [2 s Is, 2 (s+1) Is) as [G_s | U_s] */
-  void* h_shared;          /* out [T, Ns Is] act: expert s in columns [s Is, (s+1) Is) */
+  void* h_shared;          /* out [T, Ns Is] act: expert s in columns [s Is, (s+1) Is) (NULL as h) */
   void* y_shared;          /* out [T, d] act: sum over shared experts */
   /* Optional, MX-fp8 plans: perm_token [T*k] from moe_permute.  Given it,
    * the gate/up GEMM gathers its rows on load from x quantised once per
@@ -305,14 +306,14 @@ typedef struct {
   const int32_t* inv_perm;  /* [T, k] */
   const void* x_perm;       /* [T*k, d] */
   const void* gu;           /* [T*k, 2I], dtype as in moe_ffn_args */
-  const void* h;            /* [T*k, I] */
+  const void* h;            /* [T*k, I] (not read, may be NULL, with mx_saved) */
   const void* y_perm;       /* [T*k, d], dtype as in moe_ffn_args (read for MX-fp8 experts only) */
   const void* w_gate_up;    /* [E, 2I, d] */
   const void* w_down;       /* [E, d, I] */
   const void* ws_gate_up;   /* [Ns, 2Is, d] (n_shared > 0) */
   const void* ws_down;      /* [Ns, d, Is] */
   const void* gu_shared;    /* [T, 2 Ns Is] */
-  const void* h_shared;     /* [T, Ns Is] */
+  const void* h_shared;     /* [T, Ns Is] (not read, may be NULL, with mx_saved) */
   /* Balancing statistic over real tokens only (spark-gpt MoE paragraph):
    * real_mask [T] int32 (0 = filler) and real_counts [E+1] from
    * moe_aux_stats_masked of the same step; NULL real_mask = every token. */

@@ -302,7 +302,9 @@ def moe_expert_ffn(plan, x_perm, offsets, w_gate_up, w_down, gu, h, y_perm, x=No
         _need(x_perm, "x_perm", (A, d), dt)
     _need(offsets, "offsets", (E + 1,), torch.int32)
     _need(w_gate_up, "w_gate_up", (E, 2 * I, d), dt); _need(w_down, "w_down", (E, d, I), dt)
-    _need(gu, "gu", (A, 2 * I), plan.gu_dtype); _need(h, "h", (A, I), dt)
+    _need(gu, "gu", (A, 2 * I), plan.gu_dtype)
+    if h is not None or mx_saved is None:            # H may be omitted when MX experts save their codes
+        _need(h, "h", (A, I), dt)
     _need(y_perm, "y_perm", (A, d), plan.y_perm_dtype)
     args = MoeFfnArgs(*[None] * len(_FFN_FIELDS))
     for n, t in [("x_perm", x_perm), ("offsets", offsets), ("w_gate_up", w_gate_up), ("w_down", w_down),
@@ -312,11 +314,13 @@ def moe_expert_ffn(plan, x_perm, offsets, w_gate_up, w_down, gu, h, y_perm, x=No
         Ns, Is = plan.Ns, plan.Is
         _need(x, "x", (T, d), dt); _need(ws_gate_up, "ws_gate_up", (Ns, 2 * Is, d), dt)
         _need(ws_down, "ws_down", (Ns, d, Is), dt)
-        _need(gu_shared, "gu_shared", (T, 2 * Ns * Is), plan.gu_dtype); _need(h_shared, "h_shared", (T, Ns * Is), dt)
+        _need(gu_shared, "gu_shared", (T, 2 * Ns * Is), plan.gu_dtype)
+        if h_shared is not None or mx_saved is None:
+            _need(h_shared, "h_shared", (T, Ns * Is), dt)
         _need(y_shared, "y_shared", (T, d), dt)
         for n, t in [("x", x), ("ws_gate_up", ws_gate_up), ("ws_down", ws_down), ("gu_shared", gu_shared),
                      ("h_shared", h_shared), ("y_shared", y_shared)]:
-            setattr(args, n, t.data_ptr())
+            setattr(args, n, t.data_ptr() if t is not None else None)
     if perm_token is not None:
         _need(perm_token, "perm_token", (A,), torch.int32)
         _need(x, "x", (T, d), dt)

@@ -815,11 +815,15 @@ moe_status moe_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, size_t ws
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p->T == 0) return MOE_OK;
   const bool gather = p->mx && f->perm_token;       // MX: token rows gathered from x on load
-  if ((!gather && !f->x_perm) || !f->offsets || !f->w_gate_up || !f->w_down || !f->gu || !f->h || !f->y_perm)
+  // (H may be NULL for MX experts given a saved-codes buffer: it then exists only as its codes)
+  const bool h_opt = p->mx && f->mx_saved;
+  if ((!gather && !f->x_perm) || !f->offsets || !f->w_gate_up || !f->w_down || !f->gu || (!f->h && !h_opt) ||
+      !f->y_perm)
     return MOE_ERR_NULL;
   if (gather && !f->x) return MOE_ERR_NULL;
   if (gather && p->T * p->d >= (int64_t)1 << 31) return MOE_ERR_INVALID;   // 32-bit gather offsets
-  if (p->Ns > 0 && (!f->x || !f->ws_gate_up || !f->ws_down || !f->gu_shared || !f->h_shared || !f->y_shared))
+  if (p->Ns > 0 && (!f->x || !f->ws_gate_up || !f->ws_down || !f->gu_shared || (!f->h_shared && !h_opt) ||
+                    !f->y_shared))
     return MOE_ERR_NULL;
   if (p->mx) {
     moe_status st = check_ws(p, ws, ws_bytes);
@@ -1127,12 +1131,14 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
   if (p->Ns > 0 && (!gr->dws_gate_up || !gr->dws_down)) return MOE_ERR_NULL;
   if (p->T > 0) {
     if (!dy || !gr->dx || !sv->x || !sv->w_router || !sv->probs || !sv->topk_idx || !sv->topk_w ||
-        !sv->counts || !sv->inv_perm || (!sv->x_perm && !(p->mx && sv->perm_token)) || !sv->gu || !sv->h ||
+        !sv->counts || !sv->inv_perm || (!sv->x_perm && !(p->mx && sv->perm_token)) || !sv->gu ||
+        (!sv->h && !(p->mx && sv->mx_saved)) ||
         (!p->mx && !sv->perm_token) ||
         !sv->y_perm ||
         !sv->w_gate_up || !sv->w_down)
       return MOE_ERR_NULL;
-    if (p->Ns > 0 && (!sv->ws_gate_up || !sv->ws_down || !sv->gu_shared || !sv->h_shared))
+    if (p->Ns > 0 &&
+        (!sv->ws_gate_up || !sv->ws_down || !sv->gu_shared || (!sv->h_shared && !(p->mx && sv->mx_saved))))
       return MOE_ERR_NULL;
     if (sv->real_mask && !sv->real_counts) return MOE_ERR_NULL;
   } else if (!sv->w_router || !sv->w_gate_up || !sv->w_down) {

@@ -1437,7 +1437,8 @@ __device__ __forceinline__ void row_gemm_body(const RowGemmArgs& a, char* smem) 
             st16(gu + a.sub, ld16(sp(1, sr, c)));
           }
           const u32x4 hraw = ld16(sp(2, sr, c));
-          st16(static_cast<TO*>(a.C2) + row * a.ldc2 + n0 + c * 8, hraw);
+          // (MX with H's token-axis codes: the act-dtype H rows only if C2 is given)
+          if (!MX || a.C2) st16(static_cast<TO*>(a.C2) + row * a.ldc2 + n0 + c * 8, hraw);
           if constexpr (MX) {
             // the stored H row-wise in MX-fp8 for the down projection: the
             // four lanes of chunks 4b .. 4b+3 (one row, consecutive lanes)
@@ -2238,8 +2239,10 @@ hipError_t launch_row_gemm(int dt, int op, int epi, int tile, const RowGemmArgs&
     default: return hipErrorInvalidValue;
   }
   if (!k) return hipErrorInvalidValue;
-  // every call writes C, except the MX SwiGLU backward, whose [dG | dU] codes are its product
+  // every call writes C, except the MX SwiGLU backward, whose [dG | dU] codes are its product;
+  // the SwiGLU forward writes H (C2), except with MX when both its codes are written
   if (!a.C && !(dt == DT_MXFP8 && op == OP_DOWN_DGRAD && a.Hq && a.Tq)) return hipErrorInvalidValue;
+  if (op == OP_GU_FWD && !a.C2 && !(dt == DT_MXFP8 && a.Hq && a.Tq)) return hipErrorInvalidValue;
   if (a.C_lo && (op != OP_DOWN_DGRAD || !a.C2 || !a.C2_lo)) return hipErrorInvalidValue;
   // the f16 and MX-fp8 down dgrads write no w H rows
   if (op == OP_DOWN_DGRAD && a.C2 && (dt == DT_F16 || dt == DT_MXFP8)) return hipErrorInvalidValue;

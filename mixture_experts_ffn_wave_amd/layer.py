@@ -61,6 +61,9 @@ class MoELayer:
         # for the backward (moe_ffn_args.mx_saved); False: the backward makes them
         self.mx_save = p.mx
         self.mx_saved = torch.empty(p.mx_saved_bytes(), dtype=torch.uint8, device=dev) if p.mx else None
+        # with saved codes the MX layer needs H only as codes: store_h = True
+        # also writes the act-dtype H (self.h, self.h_shared)
+        self.store_h = not p.mx
         self.params = None
         self.sel_bias = None      # aux-loss-free balancing: set by enable_balancing()
         self.balance_gamma = 0.0
@@ -127,9 +130,11 @@ class MoELayer:
         xp = self.x_perm if (self.write_x_perm or not self.mx_gather) else None
         L.moe_permute(self.plan, self.topk_idx, q["x"], self.counts, self.offsets, self.perm_token,
                       self.inv_perm, xp, self.ws, stream)
+        h = self.h if (self.store_h or not self.mx_save) else None
+        hs = self.h_shared if h is not None else None
         L.moe_expert_ffn(self.plan, xp, self.offsets, q["w_gate_up"], q["w_down"], self.gu,
-                         self.h, self.y_perm, q["x"], q["ws_gate_up"], q["ws_down"], self.gu_shared,
-                         self.h_shared, self.y_shared, self.ws, stream,
+                         h, self.y_perm, q["x"], q["ws_gate_up"], q["ws_down"], self.gu_shared,
+                         hs, self.y_shared, self.ws, stream,
                          perm_token=self.perm_token if self.mx_gather else None,
                          mx_saved=self.mx_saved if self.mx_save else None)
         L.moe_combine(self.plan, self.y_perm, self.inv_perm, self.topk_w, self.y_shared, self.y, stream)

@@ -111,6 +111,7 @@ def gpu_run(wl, inp, routing=None, intermediates=False, sel_bias=None, mask=None
     plan = plan_for(wl, b is not None)
     layer = MoELayer(plan)
     layer.write_x_perm = True                  # compared with the oracle's gather
+    layer.store_h = True                       # (MX layers keep H only as codes otherwise)
     if intermediates:
         layer.keep_intermediates()             # MX plans: also store [dG | dU] in the act dtype
     dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}

@@ -168,11 +168,12 @@ def test_mx_backward_without_kept_dgu():
         assert np.array_equal(m0[n], m1[n]), n
 
 
-def _mx_step(wl, inp, save):
+def _mx_step(wl, inp, save, store_h=True):
     from mixture_experts_ffn_wave_amd import MoELayer
     dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
     layer = MoELayer(PT.plan_for(wl, inp.get("bias") is not None))
     layer.mx_save = save
+    layer.store_h = store_h
     b = dev.get("bias")
     layer.set_params(dev["x"], dev["w_router"], dev["w_gate_up"], dev["w_down"],
                      bias=(b.float() if b is not None else None),
@@ -180,7 +181,7 @@ def _mx_step(wl, inp, save):
     layer.forward()
     layer.backward(dev["dy"])
     torch.cuda.synchronize()
-    out = {n: getattr(layer, n).clone() for n in ("gu", "h", "y_perm", "y")}
+    out = {n: getattr(layer, n).clone() for n in (("gu", "h", "y_perm", "y") if store_h else ("gu", "y_perm", "y"))}
     out.update({n: t.clone() for n, t in layer.grads.items() if t is not None})
     return out
 
@@ -194,14 +195,17 @@ def test_mx_saved_codes_change_nothing(wl, tile, monkeypatch):
     axes, from the pass that makes the forward's row-wise codes; H along each
     expert's tokens, from the gate/up epilogue) are the codes the backward
     makes itself without them: every output and gradient is bitwise the same
-    either way, on 128 x 128 and 256 x 256 gate/up tiles."""
+    either way, on 128 x 128 and 256 x 256 gate/up tiles, and also when the
+    forward then keeps H only as its codes (h = NULL)."""
     if tile:
         monkeypatch.setenv("MOE_ROW_TILE", tile)
     inp = MI.make_inputs(wl)
     a, b = _mx_step(wl, inp, True), _mx_step(wl, inp, False)
     for n in a:
-        if a[n] is not None:
-            assert torch.equal(a[n], b[n]), n
+        assert torch.equal(a[n], b[n]), n
+    c = _mx_step(wl, inp, True, store_h=False)
+    for n in c:
+        assert torch.equal(a[n], c[n]), n
 
 
 def test_mx_gather_on_load_equals_the_x_perm_path():
@@ -217,6 +221,7 @@ def test_mx_gather_on_load_equals_the_x_perm_path():
     for gather in (True, False):
         layer = MoELayer(PT.plan_for(wl, inp.get("bias") is not None))
         layer.mx_gather = gather
+        layer.store_h = True
         layer.set_params(dev["x"], dev["w_router"], dev["w_gate_up"], dev["w_down"],
                          bias=(dev["bias"].float() if inp.get("bias") is not None else None),
                          ws_gate_up=dev.get("ws_gate_up"), ws_down=dev.get("ws_down"))

@@ -109,6 +109,7 @@ def run_layer(wl, inp, gather, save=True):
     layer = MoELayer(PT.plan_for(wl, b is not None))
     layer.mx_gather = gather
     layer.mx_save = save
+    layer.store_h = True                       # the bf16 H its codes are checked against
     layer.write_x_perm = True
     layer.keep_intermediates()                 # the bf16 [dG | dU] the codes are checked against
     dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
