@@ -238,3 +238,16 @@ def test_mx_gather_on_load_equals_the_x_perm_path():
 @pytest.mark.timeout(900)
 def test_mx_workload_full_size():
     PT.full_parity(MI.WORKLOADS["t16384_d2048_e64k6_i1408_s2x1408_mxfp8"], mx_diagnostic=False)
+
+
+def test_mx_workload_full_size_default_path_is_the_checked_one():
+    """At the full MX workload the layer's default path (saved codes, H kept
+    only as codes, [dG | dU] and dY_perm not stored) gives bitwise the
+    outputs and gradients of the path the parity tests check (no saved codes,
+    H stored): the default adds no arithmetic of its own."""
+    wl = MI.WORKLOADS["t16384_d2048_e64k6_i1408_s2x1408_mxfp8"]
+    inp = MI.make_inputs(wl)
+    a = _mx_step(wl, inp, True, store_h=False)
+    b = _mx_step(wl, inp, False)
+    for n in a:
+        assert torch.equal(a[n], b[n]), n
