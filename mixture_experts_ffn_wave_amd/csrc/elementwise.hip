@@ -112,7 +112,7 @@ __device__ __forceinline__ void mx_row_codes(u32x4 raw, bool ok, uint8_t* q, uin
 }
 
 template <typename T, int KG, bool MXQ, bool GD>
-__global__ void __launch_bounds__(NT) combine_bwd_kernel(CombineBwdArgs a) {
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) combine_bwd_kernel(CombineBwdArgs a) {
   constexpr int VR = 16 / sizeof(T);
   const T* yperm = static_cast<const T*>(a.y_perm);   // (GD) in the activation dtype
   const int lane = threadIdx.x & 63;
@@ -943,7 +943,14 @@ hipError_t launch_combine_bwd(int dt, const CombineBwdArgs& a, hipStream_t s) {
     // are a separate instantiation, so the plain kernel carries none of their
     // code.  A bf16 layer with bf16 experts keeps Y_perm in f32: no g here.
     case DT_BF16:
-      if (a.q || a.dq) MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, __bf16, true, true);
+      // (the MX instantiation in batches of at most four slots: within four
+      // waves per SIMD's registers; the slots' results do not depend on it)
+      if (a.q || a.dq) {
+        if (a.k <= 2)
+          hipLaunchKernelGGL((combine_bwd_kernel<__bf16, 2, true, true>), dim3((unsigned)grid), dim3(NT), 0, s, a);
+        else
+          hipLaunchKernelGGL((combine_bwd_kernel<__bf16, 4, true, true>), dim3((unsigned)grid), dim3(NT), 0, s, a);
+      }
       else if (a.g) return hipErrorInvalidValue;
       else MOE_LAUNCH_SLOT_BATCH(combine_bwd_kernel, __bf16, false, false);
       break;
