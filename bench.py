@@ -83,14 +83,26 @@ def expert_flops(wl):
     return 18.0 * wl.d * (wl.T * wl.k * wl.I + wl.T * wl.n_shared * wl.I_shared)
 
 
-def make_layer(wl, device="cuda"):
+def make_layer(wl, device="cuda", mx_path="fused"):
+    """mx_path (MX-fp8 experts): "fused" = a fused-only plan (x gathered on
+    load, the forward's saved codes, H and the backward's [dG | dU] and
+    dY_perm kept only as codes, the smaller workspace); "unfused" = x_perm
+    formed and quantised, every act-dtype intermediate stored, the backward
+    quantising the weights and H itself."""
     from mixture_experts_ffn_wave_amd import MoELayer, Plan
     inp = MI.make_inputs(wl)
     dev = {k: (v.to(device) if v is not None else None) for k, v in inp.items()}
+    mx = wl.expert_dtype == "mxfp8"
     plan = Plan(wl.T, wl.d, wl.E, wl.k, wl.I, n_shared=wl.n_shared, d_ff_shared=wl.I_shared,
                 renorm=wl.renorm, has_router_bias=dev["bias"] is not None, dtype=wl.torch_dtype,
-                aux_coef=wl.aux_coef, expert_dtype=wl.expert_dtype or None)
+                aux_coef=wl.aux_coef, expert_dtype=wl.expert_dtype or None,
+                mx_fused=mx and mx_path == "fused")
     layer = MoELayer(plan, device)
+    if mx and mx_path == "unfused":
+        layer.mx_gather = False
+        layer.mx_save = False
+        layer.store_h = True
+        layer.keep_intermediates()
     layer.set_params(dev["x"], dev["w_router"], dev["w_gate_up"], dev["w_down"], bias=dev["bias"],
                      ws_gate_up=dev.get("ws_gate_up"), ws_down=dev.get("ws_down"))
     return layer, dev
@@ -254,6 +266,8 @@ def main():
     ap.add_argument("--balance-gamma", type=float, default=0.0,
                     help="route with aux-loss-free balancing, the selection bias updated by this step "
                          "size at the end of every step (0 = the plain router)")
+    ap.add_argument("--mx-path", choices=("fused", "unfused"), default="fused",
+                    help="MX-fp8 workloads: the fused path (default) or every intermediate formed, for comparison")
     ap.add_argument("--filler-frac", type=float, default=0.0,
                     help="mark about this share of the tokens as fillers (seeded runs) and take the balancing "
                          "statistic over the real tokens only (0 = every token real)")
@@ -267,7 +281,7 @@ def main():
         return
     wl = MI.WORKLOADS[args.workload]
     torch.cuda.init()
-    layer, dev = make_layer(wl)
+    layer, dev = make_layer(wl, mx_path=args.mx_path)
     if args.balance_gamma > 0:
         layer.enable_balancing(gamma=args.balance_gamma)
     if args.filler_frac > 0:
@@ -279,6 +293,9 @@ def main():
     for _ in range(max(args.warmup, 1)):
         layer.step(dy)
     torch.cuda.synchronize()
+    # device memory the inputs, the layer's buffers and its workspace took at
+    # their peak (torch's allocator), before the cache-flush buffer below
+    peak_alloc = torch.cuda.max_memory_allocated()
 
     from mixture_experts_ffn_wave_amd import kernel_names, probe_enable, probe_read
     breakdown = {}
@@ -352,6 +369,9 @@ def main():
                                   "frac_of_peak": (expert_flops(wl) / (gemm_ms * 1e-3) / 1e12) / peak
                                   if gemm_ms else None,
                                   "gemm_ms_per_step": gemm_ms}
+    result["memory"] = {"peak_alloc_gb": peak_alloc / 2 ** 30,
+                        "workspace_gb": layer.plan.workspace_bytes() / 2 ** 30,
+                        **({"mx_path": args.mx_path} if wl.expert_dtype == "mxfp8" else {})}
     warm = step_distribution(layer, dy, args.steps)
     result["step_ms"] = {"flushed": flushed, "warm": warm, "timed_region_s": el,
                          "warm_tokens_per_s": wl.T / (warm["median"] * 1e-3)}

@@ -95,6 +95,15 @@ typedef struct {
   int32_t expert_dtype;   /* moe_dtype of the expert GEMM operands */
   float aux_coef;         /* alpha: coefficient of the balancing statistic in the loss */
   int32_t router;         /* moe_router: how moe_route chooses and weights the experts */
+  int32_t mx_fused;       /* MX-fp8 plans, 1: only the fused path (KohakUwULLM README, "Key
+                             features": fused MXFP8 experts without the (tokens x top_k, hidden)
+                             intermediates): the workspace then holds neither the act-dtype
+                             dY_perm and [dG | dU] rows nor the backward's own codes of the
+                             weights and H, and the x codes only for the T rows; every
+                             moe_expert_ffn / moe_backward call must then pass perm_token and
+                             mx_saved (MOE_ERR_NULL otherwise), and moe_keep_intermediates is
+                             refused (MOE_ERR_UNSUPPORTED).  Needs T * d_model < 2^31.  0: both
+                             paths (the default).  Must be 0 for other plans. */
 } moe_config;
 
 /* Router kinds (moe_config.router).

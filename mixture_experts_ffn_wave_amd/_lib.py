@@ -27,7 +27,7 @@ class MoeConfig(ctypes.Structure):
     _fields_ = [("T", c_int64), ("d_model", c_int32), ("n_experts", c_int32), ("top_k", c_int32),
                 ("d_ff", c_int32), ("n_shared", c_int32), ("d_ff_shared", c_int32),
                 ("renorm", c_int32), ("has_router_bias", c_int32), ("act_dtype", c_int32),
-                ("expert_dtype", c_int32), ("aux_coef", c_float), ("router", c_int32)]
+                ("expert_dtype", c_int32), ("aux_coef", c_float), ("router", c_int32), ("mx_fused", c_int32)]
 
 
 _FFN_FIELDS = ["x_perm", "offsets", "w_gate_up", "w_down", "gu", "h", "y_perm", "x", "ws_gate_up",
@@ -149,7 +149,8 @@ class Plan:
     without a GPU."""
 
     def __init__(self, T, d_model, n_experts, top_k, d_ff, n_shared=0, d_ff_shared=0, renorm=True,
-                 has_router_bias=False, dtype=torch.bfloat16, aux_coef=0.01, expert_dtype=None, router="softmax"):
+                 has_router_bias=False, dtype=torch.bfloat16, aux_coef=0.01, expert_dtype=None, router="softmax",
+                 mx_fused=False):
         if dtype not in _DTYPE_CODE:
             raise ValueError(f"unsupported activation dtype {dtype}")
         code = _DTYPE_CODE[dtype]
@@ -162,7 +163,8 @@ class Plan:
         if router not in ROUTER_KINDS:
             raise ValueError(f"unknown router {router!r}")
         self.cfg = MoeConfig(T, d_model, n_experts, top_k, d_ff, n_shared, d_ff_shared, int(renorm),
-                             int(has_router_bias), code, ecode, aux_coef, ROUTER_KINDS[router])
+                             int(has_router_bias), code, ecode, aux_coef, ROUTER_KINDS[router], int(mx_fused))
+        self.mx_fused = bool(mx_fused)                     # MX: the fused path only (smaller workspace)
         self.router = router
         # routing slots per token (topk_idx, topk_w, inv_perm are [T, slots]):
         # top_k, or one per expert for expert choice

@@ -68,6 +68,7 @@ struct moe_plan_s {
   MxBuf mx_sdyq, mx_swdt, mx_sdguq, mx_swgut, mx_sdyt, mx_sht, mx_sdgut, mx_sxt;      // backward, shared
   size_t o_mx_pad = 0, o_mx_seg1 = 0;  // padded expert offsets [E+1]; single-segment bounds [2] + pad [2]
   bool keep_inter = false;             // MX: also store [dG | dU] and dY_perm rows (moe_keep_intermediates)
+  bool fused = false;                  // MX: the fused path only (moe_config.mx_fused): fewer regions
   // the optional saved-codes buffer (offsets into it): the weights along the
   // backward's reduction axes and H along the tokens, routed and shared
   MxBuf sv_wdt, sv_wgut, sv_ht, sv_swdt, sv_swgut, sv_sht;
@@ -256,6 +257,8 @@ moe_status moe_workspace_region(moe_plan p, const char* name, size_t* offset, si
   const size_t es = dtype_bytes(p->dt);
   const std::string n(name);
   size_t o = 0, b = 0;
+  // a fused MX plan has no act-dtype dY_perm / [dG | dU] rows
+  if (p->fused && (n == "dy_perm" || n == "dgu" || n == "dgu_shared")) return MOE_ERR_INVALID;
   if (n == "dy_perm") {
     o = p->o_dy_perm; b = (size_t)p->A * p->d * es;
   } else if (n == "dgu") {
@@ -280,8 +283,10 @@ moe_status moe_workspace_region(moe_plan p, const char* name, size_t* offset, si
     const std::string base = sc ? n.substr(0, n.size() - 7) : n;
     const int64_t A = p->A, T = p->T, d = p->d, I = p->I, E = p->E, NI = (int64_t)p->Ns * p->Is;
     struct Entry { const char* name; const moe_plan_s::MxBuf* buf; int64_t rows, K; bool shared; };
+    // (a fused plan: x's codes for its T rows only, and none of the backward's
+    // own weight and H codes, which the saved-codes buffer holds)
     const Entry tab[] = {
-        {"mx_xq", &p->mx_xq, A, d, false},       {"mx_hq", &p->mx_hq, A, I, false},
+        {"mx_xq", &p->mx_xq, p->fused ? T : A, d, false}, {"mx_hq", &p->mx_hq, A, I, false},
         {"mx_wgu", &p->mx_wgu, E * 2 * I, d, false}, {"mx_wd", &p->mx_wd, E * d, I, false},
         {"mx_dyq", &p->mx_dyq, A, d, false},     {"mx_wdt", &p->mx_wdt, I, E * d, false},
         {"mx_dguq", &p->mx_dguq, A, 2 * I, false}, {"mx_wgut", &p->mx_wgut, d, E * 2 * I, false},
@@ -298,6 +303,10 @@ moe_status moe_workspace_region(moe_plan p, const char* name, size_t* offset, si
     for (const Entry& t : tab)
       if (base == t.name) hit = &t;
     if (!hit || (hit->shared && p->Ns == 0)) return MOE_ERR_INVALID;
+    if (p->fused) {
+      for (const char* own : {"mx_wdt", "mx_wgut", "mx_ht", "mx_swdt", "mx_swgut", "mx_sht"})
+        if (base == own) return MOE_ERR_INVALID;
+    }
     o = sc ? hit->buf->sc : hit->buf->pay;
     b = (size_t)hit->rows * (sc ? hit->K / 32 : hit->K);
   } else {
@@ -334,6 +343,9 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
   const bool mx = c.expert_dtype == MOE_MXFP8_E4M3;
   if (mx && c.act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;   // MX GEMMs write bf16
   if (!mx && c.expert_dtype != c.act_dtype) return MOE_ERR_UNSUPPORTED;
+  if (c.mx_fused != 0 && c.mx_fused != 1) return MOE_ERR_INVALID;
+  if (c.mx_fused && !mx) return MOE_ERR_INVALID;
+  if (c.mx_fused && c.T * c.d_model >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;   // the x-row gather
   if (c.d_model % 128 || c.d_ff % 128) return MOE_ERR_UNSUPPORTED;
   if (c.n_shared > 0 && c.d_ff_shared % 128) return MOE_ERR_UNSUPPORTED;
   const int64_t A = c.T * c.top_k;
@@ -347,6 +359,7 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
   p->cfg = c;
   p->dt = c.act_dtype == MOE_F32 ? DT_F32 : (c.act_dtype == MOE_F16 ? DT_F16 : DT_BF16);
   p->mx = mx;
+  p->fused = mx && c.mx_fused;
   p->T = c.T;
   p->A = A;
   p->d = c.d_model;
@@ -436,7 +449,7 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
   };
   p->o_block_counts = take((size_t)p->nblk_hist * p->E * 4);
   p->o_block_base = take((size_t)p->nblk_hist * p->E * 4);
-  p->o_dy_perm = take((size_t)A * p->d * es);
+  p->o_dy_perm = take(p->fused ? 0 : (size_t)A * p->d * es);
   p->o_g = take(p->mx ? (size_t)A * 4 : 0);
   if (!p->mx) {
     // waves along the columns of the down dgrad's tile: BN / WN columns each
@@ -447,7 +460,7 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
   p->o_gpart = take(p->mx ? 0 : (size_t)A * p->gparts * 4);
   p->o_dzhl = take((size_t)p->T * 2 * p->Ep * es);
   p->o_w2 = take(p->router_dx_gemm ? (size_t)2 * p->Ep * p->d * es : 0);
-  p->o_dgu = take((size_t)A * 2 * p->I * es);
+  p->o_dgu = take(p->fused ? 0 : (size_t)A * 2 * p->I * es);
   // w H rows, the down weight gradient's operand (bf16 and f32 experts)
   p->o_wh = take(wh_rows(p) ? (size_t)A * p->I * es : 0);
   {
@@ -467,7 +480,7 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
   // input-gradient rows of the experts, f32 in a bf16 layer (f32_intermediates)
   const size_t xs = f32_intermediates(p->dt, p->mx) ? 4 : es;
   p->o_dx_perm = take((size_t)A * p->d * xs);
-  p->o_dgu_s = take((size_t)p->T * 2 * p->Ns * p->Is * es);
+  p->o_dgu_s = take(p->fused ? 0 : (size_t)p->T * 2 * p->Ns * p->Is * es);
   p->o_dxs = take(p->Ns > 0 ? (size_t)p->T * p->d * xs : 0);
   p->o_dxr = take(p->router_dx_gemm ? (size_t)p->T * p->d * 4 : 0);
   p->o_dwr_part = take(p->router_small ? (size_t)p->nblk_small * p->E * p->d * 4
@@ -499,16 +512,17 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
     const int64_t A = p->A, T = p->T, d = p->d, I = p->I, E = p->E, NI = (int64_t)p->Ns * p->Is;
     p->Apad = (A + 128 * E + 127) / 128 * 128;     // >= sum over experts of their counts rounded up to 128
     p->Tpad = (T + 127) / 128 * 128;
-    p->mx_xq = mxb(A, d);
+    p->mx_xq = mxb(p->fused ? T : A, d);             // (fused: x's T rows, gathered on load)
     p->mx_hq = mxb(A, I);
     p->mx_wgu = mxb(E * 2 * I, d);
     p->mx_wd = mxb(E * d, I);
     p->mx_dyq = mxb(A, d);
-    p->mx_wdt = mxb(I, E * d);
+    const bool own = !p->fused;                      // the backward's own weight and H codes
+    p->mx_wdt = mxb(own ? I : 0, E * d);
     p->mx_dguq = mxb(A, 2 * I);
-    p->mx_wgut = mxb(d, E * 2 * I);
+    p->mx_wgut = mxb(own ? d : 0, E * 2 * I);
     p->mx_dyt = mxb(d, p->Apad);
-    p->mx_ht = mxb(I, p->Apad);
+    p->mx_ht = mxb(own ? I : 0, p->Apad);
     p->mx_dgut = mxb(2 * I, p->Apad);
     p->mx_xt = mxb(d, p->Apad);
     p->o_mx_pad = take((size_t)(E + 1) * 4);
@@ -537,11 +551,11 @@ moe_status moe_plan_create(const moe_config* cfg, moe_plan* out) {
       p->mx_swgu = mxb(2 * NI, d);
       p->mx_swd = mxb(d, NI);
       p->mx_sdyq = mxb(T, d);
-      p->mx_swdt = mxb(NI, d);
+      p->mx_swdt = mxb(own ? NI : 0, d);
       p->mx_sdguq = mxb(T, 2 * NI);
-      p->mx_swgut = mxb(d, 2 * NI);
+      p->mx_swgut = mxb(own ? d : 0, 2 * NI);
       p->mx_sdyt = mxb(d, p->Tpad);
-      p->mx_sht = mxb(NI, p->Tpad);
+      p->mx_sht = mxb(own ? NI : 0, p->Tpad);
       p->mx_sdgut = mxb(2 * NI, p->Tpad);
       p->mx_sxt = mxb(d, p->Tpad);
     }
@@ -817,6 +831,7 @@ moe_status moe_expert_ffn(moe_plan p, const moe_ffn_args* f, void* ws, size_t ws
   const bool gather = p->mx && f->perm_token;       // MX: token rows gathered from x on load
   // (H may be NULL for MX experts given a saved-codes buffer: it then exists only as its codes)
   const bool h_opt = p->mx && f->mx_saved;
+  if (p->fused && (!f->perm_token || !f->mx_saved)) return MOE_ERR_NULL;   // the fused path only
   if ((!gather && !f->x_perm) || !f->offsets || !f->w_gate_up || !f->w_down || !f->gu || (!f->h && !h_opt) ||
       !f->y_perm)
     return MOE_ERR_NULL;
@@ -1141,6 +1156,7 @@ moe_status moe_backward(moe_plan p, const moe_saved* sv, const void* dy, const m
         (!sv->ws_gate_up || !sv->ws_down || !sv->gu_shared || (!sv->h_shared && !(p->mx && sv->mx_saved))))
       return MOE_ERR_NULL;
     if (sv->real_mask && !sv->real_counts) return MOE_ERR_NULL;
+    if (p->fused && (!sv->perm_token || !sv->mx_saved)) return MOE_ERR_NULL;   // the fused path only
   } else if (!sv->w_router || !sv->w_gate_up || !sv->w_down) {
     return MOE_ERR_NULL;
   }
@@ -1424,6 +1440,7 @@ moe_status moe_mx_saved_region(moe_plan p, const char* name, size_t* offset, siz
 
 moe_status moe_keep_intermediates(moe_plan p, int keep) {
   if (!p) return MOE_ERR_NULL;
+  if (p->fused && keep) return MOE_ERR_UNSUPPORTED;        // no room for the rows in its workspace
   p->keep_inter = keep != 0;
   return MOE_OK;
 }

@@ -34,16 +34,17 @@ class MoELayer:
         self.inv_perm = z(T, p.slots, dtype=torch.int32)
         self._x_perm = None if self.mx_gather else z(A, d)
         self.gu = z(A, 2 * I, dtype=p.gu_dtype)
-        self.h = z(A, I)
+        # H: MX experts keep it only as codes unless store_h (allocated on first use)
+        self._h = None if p.mx else z(A, I)
         self.y_perm = z(A, d, dtype=p.y_perm_dtype)
         self.y = z(T, d)
         if p.Ns > 0:
             NI = p.Ns * p.Is
             self.gu_shared = z(T, 2 * NI, dtype=p.gu_dtype)
-            self.h_shared = z(T, NI)
+            self._h_shared = None if p.mx else z(T, NI)
             self.y_shared = z(T, d)
         else:
-            self.gu_shared = self.h_shared = self.y_shared = None
+            self.gu_shared = self._h_shared = self.y_shared = None
         self.grads = {
             "dx": z(T, d),
             "dw_router": z(E, d),
@@ -71,6 +72,20 @@ class MoELayer:
         self.sinkhorn_b = None
         self.real_mask = None     # statistic over real tokens only: set by set_real_mask()
         self.real_counts = None
+
+    @property
+    def h(self):
+        if self._h is None:
+            p = self.plan
+            self._h = torch.empty(p.T * p.k, p.I, dtype=p.dtype, device=self.probs.device)
+        return self._h
+
+    @property
+    def h_shared(self):
+        p = self.plan
+        if self._h_shared is None and p.Ns > 0:
+            self._h_shared = torch.empty(p.T, p.Ns * p.Is, dtype=p.dtype, device=self.probs.device)
+        return self._h_shared
 
     @property
     def x_perm(self):
@@ -151,10 +166,10 @@ class MoELayer:
         # and MX experts on the gather path read x's rows through it
         return dict(x=q["x"], w_router=q["w_router"], probs=self.probs, topk_idx=self.topk_idx,
                     topk_w=self.topk_w, counts=self.counts, offsets=self.offsets, inv_perm=self.inv_perm,
-                    x_perm=None if self.mx_gather else self._x_perm, gu=self.gu, h=self.h,
+                    x_perm=None if self.mx_gather else self._x_perm, gu=self.gu, h=self._h,
                     y_perm=self.y_perm, w_gate_up=q["w_gate_up"], w_down=q["w_down"],
                     ws_gate_up=q["ws_gate_up"], ws_down=q["ws_down"], gu_shared=self.gu_shared,
-                    h_shared=self.h_shared, real_mask=self.real_mask, real_counts=self.real_counts,
+                    h_shared=self._h_shared, real_mask=self.real_mask, real_counts=self.real_counts,
                     perm_token=self.perm_token if (self.mx_gather or not self.plan.mx) else None,
                     mx_saved=self.mx_saved if self.mx_save else None)
 

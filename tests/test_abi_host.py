@@ -46,7 +46,7 @@ def test_version_and_status_strings():
 
 
 def test_struct_sizes_match_header_layout(tmp_path):
-    assert ctypes.sizeof(L.MoeConfig) == 56          # int64 + 10 int32 + float, 8-aligned
+    assert ctypes.sizeof(L.MoeConfig) == 64          # int64 + 12 int32 + float, 8-aligned
     assert ctypes.sizeof(L.MoeAuxScalars) == 32
     assert ctypes.sizeof(L.MoeFfnArgs) == 15 * 8
     assert ctypes.sizeof(L.MoeSaved) == 22 * 8
@@ -384,3 +384,54 @@ def test_expert_choice_has_its_own_entry_point():
                                        None) == MOE_ERR_INVALID
     assert lib.moe_route_expert_choice(ec.handle, fake, fake, None, fake, fake, fake, fake, ec.workspace_bytes() - 1,
                                        None) == MOE_ERR_WORKSPACE
+
+
+def test_fused_mx_plan_has_the_smaller_workspace_and_its_contract():
+    lib = L.lib()
+    T, d, E, k, I, Ns, Is = 300, 256, 8, 2, 128, 1, 128
+    full = L.Plan(T, d, E, k, I, n_shared=Ns, d_ff_shared=Is, expert_dtype="mxfp8")
+    fused = L.Plan(T, d, E, k, I, n_shared=Ns, d_ff_shared=Is, expert_dtype="mxfp8", mx_fused=True)
+    A = T * k
+    # no dY_perm, [dG | dU] (routed and shared) rows, no own weight / H codes, x codes for T rows
+    saved = sum(L.workspace_region(full, n)[1] for n in ("dy_perm", "dgu", "dgu_shared"))
+    for n in ("mx_wdt", "mx_wgut", "mx_ht", "mx_swdt", "mx_swgut", "mx_sht"):
+        saved += L.workspace_region(full, n)[1] + L.workspace_region(full, n + ".scales")[1]
+    saved += (A - T) * d + (A - T) * d // 32
+    assert full.workspace_bytes() - fused.workspace_bytes() >= saved - 64 * 256   # (region alignment)
+    assert fused.mx_saved_bytes() == full.mx_saved_bytes()
+    o, n = ctypes.c_size_t(), ctypes.c_size_t()
+    for name in (b"dy_perm", b"dgu", b"dgu_shared", b"mx_wdt", b"mx_ht.scales", b"mx_swgut"):
+        assert lib.moe_workspace_region(fused.handle, name, ctypes.byref(o), ctypes.byref(n)) == MOE_ERR_INVALID
+    assert L.workspace_region(fused, "mx_xq")[1] == T * d
+    assert L.workspace_region(fused, "dx_perm")[1] > 0
+    assert lib.moe_keep_intermediates(fused.handle, 1) == MOE_ERR_UNSUPPORTED
+    assert lib.moe_keep_intermediates(fused.handle, 0) == MOE_OK
+    # every call must bring perm_token and the saved-codes buffer (checked before any launch)
+    fake = 0x1000
+    args = L.MoeFfnArgs(*[fake] * len(L._FFN_FIELDS))
+    args.perm_token = None
+    assert lib.moe_expert_ffn(fused.handle, ctypes.byref(args), ctypes.c_void_p(fake), 1 << 40, None) == MOE_ERR_NULL
+    args.perm_token = fake
+    args.mx_saved = None
+    assert lib.moe_expert_ffn(fused.handle, ctypes.byref(args), ctypes.c_void_p(fake), 1 << 40, None) == MOE_ERR_NULL
+    sv = L.MoeSaved(*[fake] * len(L._SAVED_FIELDS))
+    sv.real_mask = None
+    sv.mx_saved = None
+    gr = L.MoeGrads(*[fake] * len(L._GRAD_FIELDS))
+    assert lib.moe_backward(fused.handle, ctypes.byref(sv), ctypes.c_void_p(fake), ctypes.byref(gr),
+                            ctypes.c_void_p(fake), 1 << 40, None) == MOE_ERR_NULL
+    full.close()
+    fused.close()
+    # only MX plans can be fused-only, and within the gather's 32-bit offsets
+    cfg = L.MoeConfig(T=512, d_model=256, n_experts=8, top_k=2, d_ff=128, n_shared=0, d_ff_shared=0, renorm=1,
+                      has_router_bias=0, act_dtype=L.MOE_BF16, expert_dtype=L.MOE_BF16, aux_coef=0.0, router=0,
+                      mx_fused=1)
+    h = ctypes.c_void_p()
+    assert lib.moe_plan_create(ctypes.byref(cfg), ctypes.byref(h)) == MOE_ERR_INVALID
+    cfg.expert_dtype = L.MOE_MXFP8_E4M3
+    cfg.mx_fused = 2
+    assert lib.moe_plan_create(ctypes.byref(cfg), ctypes.byref(h)) == MOE_ERR_INVALID
+    cfg.mx_fused = 1
+    cfg.T = 1 << 22
+    cfg.d_model = 1024
+    assert lib.moe_plan_create(ctypes.byref(cfg), ctypes.byref(h)) == MOE_ERR_UNSUPPORTED

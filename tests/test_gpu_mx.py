@@ -168,10 +168,16 @@ def test_mx_backward_without_kept_dgu():
         assert np.array_equal(m0[n], m1[n]), n
 
 
-def _mx_step(wl, inp, save, store_h=True):
-    from mixture_experts_ffn_wave_amd import MoELayer
+def _mx_step(wl, inp, save, store_h=True, fused=False):
+    from mixture_experts_ffn_wave_amd import MoELayer, Plan
     dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
-    layer = MoELayer(PT.plan_for(wl, inp.get("bias") is not None))
+    if fused:                                   # a fused-only plan (smaller workspace)
+        plan = Plan(wl.T, wl.d, wl.E, wl.k, wl.I, n_shared=wl.n_shared, d_ff_shared=wl.I_shared,
+                    renorm=wl.renorm, has_router_bias=inp.get("bias") is not None, dtype=wl.torch_dtype,
+                    aux_coef=wl.aux_coef, expert_dtype="mxfp8", router=wl.router, mx_fused=True)
+    else:
+        plan = PT.plan_for(wl, inp.get("bias") is not None)
+    layer = MoELayer(plan)
     layer.mx_save = save
     layer.store_h = store_h
     b = dev.get("bias")
@@ -206,6 +212,9 @@ def test_mx_saved_codes_change_nothing(wl, tile, monkeypatch):
     c = _mx_step(wl, inp, True, store_h=False)
     for n in c:
         assert torch.equal(a[n], c[n]), n
+    f = _mx_step(wl, inp, True, store_h=False, fused=True)    # the fused-only plan
+    for n in f:
+        assert torch.equal(a[n], f[n]), n
 
 
 def test_mx_gather_on_load_equals_the_x_perm_path():
@@ -241,13 +250,13 @@ def test_mx_workload_full_size():
 
 
 def test_mx_workload_full_size_default_path_is_the_checked_one():
-    """At the full MX workload the layer's default path (saved codes, H kept
-    only as codes, [dG | dU] and dY_perm not stored) gives bitwise the
-    outputs and gradients of the path the parity tests check (no saved codes,
-    H stored): the default adds no arithmetic of its own."""
+    """At the full MX workload the fused-only plan the benchmark runs (saved
+    codes, H kept only as codes, [dG | dU] and dY_perm not stored, the smaller
+    workspace) gives bitwise the outputs and gradients of the path the parity
+    tests check (no saved codes, H stored): it adds no arithmetic of its own."""
     wl = MI.WORKLOADS["t16384_d2048_e64k6_i1408_s2x1408_mxfp8"]
     inp = MI.make_inputs(wl)
-    a = _mx_step(wl, inp, True, store_h=False)
+    a = _mx_step(wl, inp, True, store_h=False, fused=True)
     b = _mx_step(wl, inp, False)
     for n in a:
         assert torch.equal(a[n], b[n]), n
