@@ -488,7 +488,9 @@ const char* moe_kernel_names(void);
  * For tests and debugging, e.g. to check each GEMM of the backward on its
  * own inputs.  MOE_ERR_NULL for a null argument, MOE_ERR_INVALID for an
  * unknown name or a region this plan does not have (no shared experts, not
- * an MX plan). */
+ * an MX plan; a fused-only plan has no "dy_perm", "dgu", "dgu_shared" and
+ * none of "mx_wdt", "mx_wgut", "mx_ht" and their shared counterparts, which
+ * its saved-codes buffer holds, and its "mx_xq" has T rows). */
 moe_status moe_workspace_region(moe_plan plan, const char* name, size_t* offset, size_t* bytes);
 
 /* MX-fp8 plans: the backward reads [dG | dU] (routed and shared) only through
@@ -503,7 +505,9 @@ moe_status moe_workspace_region(moe_plan plan, const char* name, size_t* offset,
  * restores the default.
  * Other plans always store them (their next GEMMs read them): the call is
  * accepted there and changes nothing.  Like the timing probe, it changes the
- * plan and is not thread-safe.  MOE_ERR_NULL for a null plan. */
+ * plan and is not thread-safe.  MOE_ERR_NULL for a null plan;
+ * MOE_ERR_UNSUPPORTED for keep = 1 on a fused-only plan (moe_config.mx_fused),
+ * whose workspace has no room for the rows. */
 moe_status moe_keep_intermediates(moe_plan plan, int keep);
 
 /* Byte offset and size, inside the MX-fp8 saved-codes buffer
