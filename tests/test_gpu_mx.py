@@ -107,6 +107,15 @@ def test_mx_empty_batch():
         assert not np.any(gpu[key]), key
 
 
+def test_mx_empty_batch_fused_plan():
+    """A fused-only plan with no tokens: every weight gradient written as zeros."""
+    wl = W("t0_d256_e4k2_i128_mx_shared1_fused", T=0, d=256, E=4, k=2, I=128, n_shared=1, I_shared=128,
+           expert_dtype="mxfp8")
+    out = _mx_step(wl, MI.make_inputs(wl), True, store_h=False, fused=True)
+    for key in ("dw_router", "dw_gate_up", "dw_down", "dws_gate_up", "dws_down"):
+        assert not bool(out[key].any()), key
+
+
 def test_mx_two_runs_are_bitwise_identical():
     wl = W("t900_d256_e16k4_i384_s2x128_mx_det", T=900, d=256, E=16, k=4, I=384, n_shared=2, I_shared=128,
            expert_dtype="mxfp8")
